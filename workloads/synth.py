@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs with the shapes and value distributions of the
+Scute paper's workloads (arXiv 2611.01089: §6.1 "Setup" for the
+Llama-3.1-8B projection shapes, the appendix "Training" for ranks, block
+size and which projections each method adapts, "Amplified adapters" for
+vectors pulled away from the identity).
+
+Every array is float32 holding a value already rounded to the layer's
+storage type (f32, f16 or bf16), so the oracle (which upcasts to float64)
+and the HIP path see exactly the same numbers.
+
+Layouts: the base weight ``W`` is stored like an nn.Linear weight,
+[d_out, d_in] (the oracle uses its transpose, the paper's math layout);
+adapter parameters are in the paper's math layout, A [d_in, r],
+B [r, d_out], Q [d_in / b, b, b].
+
+Distributions (one reading of the workload descriptions, used everywhere):
+  W ~ N(0, 1/d_in); x ~ N(0, 1); LoRA and DoRA A ~ N(0, 1/d_in),
+  B ~ N(0, 1/r), c = 2 (alpha 32 over rank 16); DoRA magnitude
+  m = ‖Wᵀ + cAB‖_c · (1 + 0.1 z); (IA)3 l = 1 + 0.3 z; VeRA shared
+  A ~ N(0, 1/d_in), B ~ N(0, 1/r_v), d, e = 1 + 0.3 z, c = 1; OFT skew Q
+  with upper entries 0.1 z, blocks of 32.
+
+The DoRA magnitude is an input recipe: it is formed here once from the
+rounded W, A, B, so that the adapter's scale is 1 + 0.1 z; both sides then
+receive m and compute the scale from it on their own.
+"""
+import numpy as np
+
+# Llama-3.1-8B projection shapes (d_in, d_out), §6.1.
+LLAMA8B_PROJECTIONS = (
+    ("q", 4096, 4096),
+    ("k", 4096, 1024),
+    ("v", 4096, 1024),
+    ("o", 4096, 4096),
+    ("gate", 4096, 14336),
+    ("up", 4096, 14336),
+    ("down", 14336, 4096),
+)
+
+
+def round_to(a, dtype):
+    """Round float data to the storage type and return it as float32."""
+    a = np.asarray(a, dtype=np.float64)
+    if dtype == "f32":
+        return a.astype(np.float32)
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = a.astype(np.float32).view(np.uint32).astype(np.uint64)
+        bias = ((u >> 16) & 1) + 0x7FFF
+        r = ((u + bias) >> 16) << 16
+        return r.astype(np.uint32).view(np.float32)
+    raise ValueError(dtype)
+
+
+def _normal(rng, shape, std):
+    return rng.standard_normal(shape) * std
+
+
+def _lora(rng, d_in, d_out, r, dtype, c=2.0):
+    A = round_to(_normal(rng, (d_in, r), 1.0 / np.sqrt(d_in)), dtype)
+    B = round_to(_normal(rng, (r, d_out), 1.0 / np.sqrt(r)), dtype)
+    return {"method": "lora", "A": A, "B": B, "c": float(c)}
+
+
+def _dora(rng, W, r, dtype, c=2.0):
+    d_out, d_in = W.shape
+    rec = _lora(rng, d_in, d_out, r, dtype, c)
+    Wp = W.T.astype(np.float64) + c * (rec["A"].astype(np.float64) @ rec["B"].astype(np.float64))
+    col = np.sqrt(np.sum(Wp * Wp, axis=0))
+    g = 1.0 + 0.1 * rng.standard_normal(d_out)
+    rec["method"] = "dora"
+    rec["m"] = (col * g).astype(np.float32)
+    return rec
+
+
+def _ia3(rng, d_out):
+    return {"method": "ia3", "l": (1.0 + 0.3 * rng.standard_normal(d_out)).astype(np.float32)}
+
+
+def _vera(rng, r_v, d_out, c=1.0):
+    return {"method": "vera",
+            "d": (1.0 + 0.3 * rng.standard_normal(r_v)).astype(np.float32),
+            "e": (1.0 + 0.3 * rng.standard_normal(d_out)).astype(np.float32),
+            "c": float(c)}
+
+
+def _oft(rng, d_in, block=32, std=0.1):
+    nb = d_in // block
+    Q = np.zeros((nb, block, block))
+    iu = np.triu_indices(block, 1)
+    for j in range(nb):
+        v = std * rng.standard_normal(len(iu[0]))
+        Q[j][iu] = v
+        Q[j][(iu[1], iu[0])] = -v
+    return {"method": "oft", "Q": Q.astype(np.float32), "block": block}
+
+
+def _vera_shared(rng, d_in, d_out, r_v, dtype):
+    return {"A": round_to(_normal(rng, (d_in, r_v), 1.0 / np.sqrt(d_in)), dtype),
+            "B": round_to(_normal(rng, (r_v, d_out), 1.0 / np.sqrt(r_v)), dtype)}
+
+
+def make_projection(rng, name, d_in, d_out, dtype, n):
+    """Base weight and input rows of one projection."""
+    W = round_to(_normal(rng, (d_out, d_in), 1.0 / np.sqrt(d_in)), dtype)
+    x = round_to(rng.standard_normal((n, d_in)), dtype)
+    return {"name": name, "d_in": d_in, "d_out": d_out, "dtype": dtype,
+            "W": W, "x": x, "shared": None, "adapters": {}}
+
+
+def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False):
+    """Tiny single layer: W [256 x 256], n rows assigned uniformly at random
+    to five tenants, one per method (LoRA r8, DoRA r8, (IA)3, VeRA with a
+    shared rank-32 pair, OFT with blocks of 32).  Slots 1..5 in that order;
+    with_identity also draws rows onto slot 0 (base only)."""
+    rng = np.random.default_rng(seed)
+    p = make_projection(rng, "tiny", d, d, dtype, n)
+    p["shared"] = _vera_shared(rng, d, d, 32, dtype)
+    p["adapters"] = {
+        1: _lora(rng, d, d, 8, dtype),
+        2: _dora(rng, p["W"], 8, dtype),
+        3: _ia3(rng, d),
+        4: _vera(rng, 32, d),
+        5: _oft(rng, d, 32),
+    }
+    lo = 0 if with_identity else 1
+    slot_of_row = rng.integers(lo, 6, size=n).astype(np.int32)
+    return {"name": "tiny_mixed", "dtype": dtype, "n": n,
+            "slot_of_row": slot_of_row, "projections": [p]}
+
+
+def prefill_lora_dora(seed=1000, n=1024, d=4096, r=16, dtype="f16", tenants=16):
+    """q_proj 4096 -> 4096, n prefill rows in `tenants` contiguous segments
+    of n / tenants rows; even segments LoRA, odd segments DoRA, rank r."""
+    rng = np.random.default_rng(seed)
+    p = make_projection(rng, "q", d, d, dtype, n)
+    for t in range(tenants):
+        p["adapters"][t + 1] = (_lora(rng, d, d, r, dtype) if t % 2 == 0
+                                else _dora(rng, p["W"], r, dtype))
+    seg = n // tenants
+    slot_of_row = (np.arange(n) // seg + 1).astype(np.int32)
+    return {"name": "prefill_lora_dora", "dtype": dtype, "n": n,
+            "slot_of_row": slot_of_row, "projections": [p]}
+
+
+def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=256,
+                        oft_block=32, shapes=LLAMA8B_PROJECTIONS, pure_lora=False):
+    """One decoder layer's seven projections with 5 * per_method tenants:
+    LoRA r16 and DoRA r16 on all seven, (IA)3 on k, v and up, VeRA (shared
+    rank-256 pair) on all seven, OFT (blocks of 32) on q, k and v.  Tenant t
+    has slot t + 1 in every projection; where its method does not adapt a
+    projection the slot holds the identity.  Row j belongs to tenant
+    j mod (5 * per_method), then the rows are shuffled so segments are not
+    contiguous.  Inputs per projection are independent N(0, 1) rows.
+
+    pure_lora: the same rows and slots, every tenant a rank-r LoRA (the
+    equal-size pure-LoRA batch)."""
+    rng = np.random.default_rng(seed)
+    T = 5 * per_method
+    order = ["lora", "dora", "ia3", "vera", "oft"]
+    methods = [order[t // per_method] for t in range(T)]
+    projs = []
+    for name, d_in, d_out in shapes:
+        p = make_projection(rng, name, d_in, d_out, dtype, n)
+        if not pure_lora:
+            p["shared"] = _vera_shared(rng, d_in, d_out, r_v, dtype)
+        for t, m in enumerate(methods):
+            slot = t + 1
+            if pure_lora or m == "lora":
+                p["adapters"][slot] = _lora(rng, d_in, d_out, r, dtype)
+            elif m == "dora":
+                p["adapters"][slot] = _dora(rng, p["W"], r, dtype)
+            elif m == "ia3":
+                p["adapters"][slot] = (_ia3(rng, d_out) if name in ("k", "v", "up")
+                                       else {"method": "identity"})
+            elif m == "vera":
+                p["adapters"][slot] = _vera(rng, r_v, d_out)
+            elif m == "oft":
+                p["adapters"][slot] = (_oft(rng, d_in, oft_block) if name in ("q", "k", "v")
+                                       else {"method": "identity"})
+        projs.append(p)
+    slot_of_row = (np.arange(n) % T + 1).astype(np.int32)
+    slot_of_row = slot_of_row[rng.permutation(n)]
+    return {"name": "decoder_layer_mixed" + ("_pure_lora" if pure_lora else ""),
+            "dtype": dtype, "n": n, "slot_of_row": slot_of_row, "projections": projs}
+
+
+def vera_sweep(seed=3000, n=256, d_in=4096, d_out=4096, tenants=16, r_v=256, dtype="f16",
+               as_lora=False):
+    """VeRA tenant sweep: n rows drawn uniformly over `tenants` VeRA tenants
+    sharing one rank-r_v pair.  as_lora: the same tenants stored as their
+    exact rank-r_v LoRA conversion, A_a = A diag(c d_a), B_a = B diag(e_a)
+    (§4.2; the factors are rounded to the storage type after scaling)."""
+    rng = np.random.default_rng(seed)
+    p = make_projection(rng, "vera_%dx%d" % (d_in, d_out), d_in, d_out, dtype, n)
+    shared = _vera_shared(rng, d_in, d_out, r_v, dtype)
+    p["shared"] = shared
+    for t in range(tenants):
+        rec = _vera(rng, r_v, d_out)
+        if as_lora:
+            A = round_to(shared["A"].astype(np.float64) * (rec["c"] * rec["d"].astype(np.float64))[None, :], dtype)
+            B = round_to(shared["B"].astype(np.float64) * rec["e"].astype(np.float64)[None, :], dtype)
+            rec = {"method": "lora", "A": A, "B": B, "c": 1.0}
+        p["adapters"][t + 1] = rec
+    if as_lora:
+        p["shared"] = None
+    slot_of_row = rng.integers(1, tenants + 1, size=n).astype(np.int32)
+    return {"name": "vera_sweep", "dtype": dtype, "n": n, "slot_of_row": slot_of_row,
+            "projections": [p]}
