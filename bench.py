@@ -1,0 +1,280 @@
+"""Benchmark of the batched multi-adapter layer on one MI355X.
+
+Workload (default): one Llama-3.1-8B decoder layer's seven adapted
+projections (q, k, v, o, gate, up, down) in fp16, 64 decode rows over 20
+tenants -- 4 each of LoRA r16, DoRA r16, (IA)3 on k/v/up, VeRA with a shared
+rank-256 pair, OFT with blocks of 32 on q/k/v -- rows shuffled so segments
+are not contiguous.  Inputs are seeded synthetic data of those shapes.
+
+A step is one forward of all seven projections (plan, OFT rotate, base GEMM,
+shrink, expand for each), captured in one HIP graph.  `value` is adapted-
+layer rows/s: rows through one adapted projection per second, i.e.
+7 · n / t_step.
+
+Prints one JSON line.  `python bench.py --gpus N` with N > 1 exits: this
+build measures one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "adapted-layer rows/s, mixed 5-method batch; adapter-path HBM GB/s vs byte model"
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+MFMA_F16_PEAK = 2.5e15     # flop/s, dense fp16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pure-lora", action="store_true", help="skip the pure-LoRA comparison batch")
+    ap.add_argument("--stage-reps", type=int, default=30)
+    ap.add_argument("--cpu-rows", type=int, default=8, help="rows in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def build_step(wl, torch):
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    n = wl["n"]
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    layers, xs, outs, wss = [], [], [], []
+    for p in wl["projections"]:
+        W = torch.tensor(p["W"]).half().cuda()
+        L = AdaptedLayer(W, max_slots=32, max_rank=256)
+        if p["shared"] is not None:
+            L.set_vera_shared(p["shared"]["A"], p["shared"]["B"])
+        for slot in sorted(p["adapters"]):
+            assert L.load(p["adapters"][slot]) == slot
+        layers.append(L)
+        xs.append(torch.tensor(p["x"]).half().cuda())
+        outs.append(torch.empty((n, p["d_out"]), dtype=torch.float16, device="cuda"))
+        wss.append(L.workspace(n))
+
+    def step():
+        for L, x, o, w in zip(layers, xs, outs, wss):
+            L.forward(x, sor, out=o, ws=w)
+    return layers, step
+
+
+def capture(step, torch):
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, steps, warmup, torch):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def stage_times(layers, step, reps, torch):
+    """Per projection and stage durations (µs) from events the library
+    records on its own stream around each kernel, inside a captured graph."""
+    from tenant_peft_adapter_amd import binding as B
+    evs = []
+    for L in layers:
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for x in e:
+            x.record()
+        torch.cuda.synchronize()
+        B.tpa_layer_set_stage_events(L.handle, [x.cuda_event for x in e])
+        evs.append(e)
+    g = capture(step, torch)
+    acc = [[0.0] * 5 for _ in layers]
+    for _ in range(reps):
+        g.replay()
+        torch.cuda.synchronize()
+        for i, e in enumerate(evs):
+            for k in range(5):
+                acc[i][k] += e[k].elapsed_time(e[k + 1]) * 1e3
+    for L in layers:
+        B.tpa_layer_set_stage_events(L.handle, None)
+    return [[v / reps for v in row] for row in acc]
+
+
+def calibrate(torch):
+    """β_HBM: a 2 GiB device copy (larger than the 256 MB MALL); λ: 200 chained
+    one-block kernels in one graph (appendix "Constants")."""
+    from tenant_peft_adapter_amd import binding as B
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    reps = 10
+    for _ in range(reps):
+        B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
+    e1.record()
+    torch.cuda.synchronize()
+    beta = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            B.tpa_probe_empty(200, s.cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    lam = (time.perf_counter() - t0) / 20 / 200
+    return beta, lam
+
+
+def cpu_baseline(wl, rows):
+    """The oracle, untuned, on a bounded sample: `rows` rows of the batch
+    through all seven projections."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    sel = np.arange(rows)
+    t0 = time.perf_counter()
+    for p in wl["projections"]:
+        x = p["x"][sel].astype(np.float64)
+        oracle.layer_forward(x, p["W"].astype(np.float64).T, wl["slot_of_row"][sel], p["adapters"], p["shared"])
+    dt = time.perf_counter() - t0
+    return {"value": rows * len(wl["projections"]) / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of the %d rows through all %d projections (%.1f s)" % (rows, wl["n"],
+                                                                             len(wl["projections"]), dt)}
+
+
+def main():
+    args = parse()
+    ws = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or ws != 1:
+        print("bench.py measures one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from tenant_peft_adapter_amd import bytemodel as bm
+    from workloads import synth
+
+    torch.cuda.set_device(0)
+    wl = synth.decoder_layer_mixed()
+    n = wl["n"]
+    layers, step = build_step(wl, torch)
+    g = capture(step, torch)
+    t_step = time_graph(g, args.steps, args.warmup, torch)
+
+    # Eager (no graph) for reference.
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / 20
+
+    stages = stage_times(layers, step, args.stage_reps, torch)
+    beta, lam = calibrate(torch)
+
+    # Byte model per projection.
+    names = [p["name"] for p in wl["projections"]]
+    shapes = [bm.shape_of(n, p["d_in"], p["d_out"], wl["slot_of_row"], p["adapters"], q=2, r_v=256)
+              for p in wl["projections"]]
+    kb = [bm.kernel_bytes(s) for s in shapes]
+    # Dominant kernel: the skinny base GEMM with 64-column blocks (q, o, gate,
+    # up, down: the projections with d_out >= 4096).
+    dom = [i for i, p in enumerate(wl["projections"]) if p["d_out"] >= 4096]
+    dom_bytes = sum(kb[i]["gemm"]["bytes"] for i in dom) / len(dom)
+    dom_time = sum(stages[i][2] for i in dom) / len(dom) * 1e-6
+    gemm_bytes_all = sum(k["gemm"]["bytes"] for k in kb)
+    gemm_time_all = sum(st[2] for st in stages) * 1e-6
+    adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes)
+    adapter_time = sum(st[0] + st[1] + st[3] + st[4] for st in stages) * 1e-6
+    adapter_launches = sum(k["plan"]["launches"] + k["oft"]["launches"] + k["shrink"]["launches"]
+                           + k["expand"]["launches"] for k in kb)
+    base_only_time = gemm_time_all
+    predicted = bm.predict_time(base_only_time, adapter_bytes, adapter_launches, beta, lam)
+
+    ratio = None
+    if not args.no_pure_lora:
+        wl_pure = synth.decoder_layer_mixed(pure_lora=True)
+        for L in layers:
+            L.close()
+        del g
+        torch.cuda.empty_cache()
+        layers_p, step_p = build_step(wl_pure, torch)
+        gp = capture(step_p, torch)
+        t_pure = time_graph(gp, args.steps, args.warmup, torch)
+        ratio = t_step / t_pure
+        for L in layers_p:
+            L.close()
+        del gp
+
+    out = {
+        "metric": METRIC,
+        "value": 7 * n / t_step,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; Llama-3.1-8B projection shapes, random-init weights and adapters)",
+        "config": {"workload": "decoder_layer_mixed: one Llama-3.1-8B decoder layer, 7 adapted projections, "
+                               "n=64 decode rows, 20 tenants (4 each LoRA r16, DoRA r16, (IA)3 k/v/up, "
+                               "VeRA shared r256, OFT b32 q/k/v), rows shuffled",
+                   "n": n, "projections": names, "graph": True},
+        "us_per_adapted_layer": t_step * 1e6 / 7,
+        "decoder_layer_rows_per_s": n / t_step,
+        "eager_ms_per_step": t_eager * 1e3,
+        "mixed_over_pure_lora": ratio,
+        "roofline": {
+            "kernel": "gemm_skinny_kernel<f16,4,4> (base GEMM of q, o, gate, up, down)",
+            "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+            "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": None,
+            "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
+        },
+        "base_gemm": {"bytes_per_step": gemm_bytes_all, "us_per_step": gemm_time_all * 1e6,
+                      "GBps": gemm_bytes_all / gemm_time_all / 1e9},
+        "adapter_path": {"bytes_per_step": adapter_bytes, "us_per_step": adapter_time * 1e6,
+                         "GBps": adapter_bytes / adapter_time / 1e9, "launches": adapter_launches,
+                         "predicted_step_us": predicted * 1e6},
+        "calibration": {"beta_hbm_GBps": beta / 1e9, "lambda_us": lam * 1e6},
+        "stages_us": {nm: dict(zip(("plan", "oft", "gemm", "shrink", "expand"), [round(v, 2) for v in st]))
+                      for nm, st in zip(names, stages)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

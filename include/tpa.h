@@ -1,0 +1,242 @@
+/*
+ * tpa.h -- C ABI of the batched multi-adapter layer in normal form, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One `tpa_layer` is one adapted projection: a shared base weight W and a
+ * table of slots, each holding one tenant's adapter in normal form
+ * (Scute paper, arXiv 2611.01089, §3.1 eq. (1)):
+ *
+ *   F_a(x) = ((x R) W) ⊙ s + b + Σ_k c_k (((x A_k) ⊙ d_k) B_k ⊙ e_k)
+ *
+ * `tpa_layer_forward` evaluates F_{a(i)} for every row i of one batch whose
+ * rows belong to many tenants (slot_of_row[i] = the row's slot), following
+ * §2 "The LoRA schedule" and the three routes of §4.1: the output scale s
+ * (and shift b) is applied inside the expand, VeRA's shared-factor term
+ * runs over row tiles whatever their tenant, and OFT's rotation R runs in a
+ * pass of its own before the shared GEMM.
+ *
+ * Conventions
+ *   - Layer element type (`dtype`): TPA_F32, TPA_F16 or TPA_BF16.  x, W and
+ *     out use it; accumulation is always fp32.
+ *   - W is row-major [d_out][d_in] (an nn.Linear weight; the paper's math W
+ *     is its transpose).  x is row-major [n][d_in]; out is [n][d_out].
+ *   - Raw adapter parameters are float32 host arrays in the paper's math
+ *     layout: A [d_in][r], B [r][d_out], Q [d_in / b][b][b].
+ *   - All device work is enqueued on the caller's stream; nothing here
+ *     synchronizes except where a function says so.  A `tpa_layer` is not
+ *     thread-safe: serialize calls on one layer.
+ *   - Errors: every function returns a tpa_status; on failure a message for
+ *     the calling thread is available from tpa_last_error().
+ */
+#ifndef TPA_H
+#define TPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tpa_status;
+#define TPA_OK 0
+#define TPA_ERR_INVALID (-1)      /* bad argument or shape */
+#define TPA_ERR_METHOD (-2)       /* unknown method */
+#define TPA_ERR_NO_SLOT (-3)      /* every slot is in use */
+#define TPA_ERR_UNKNOWN_SLOT (-4) /* slot not loaded (or slot 0) */
+#define TPA_ERR_VALUE (-5)        /* non-skew Q, non-finite or zero-norm input */
+#define TPA_ERR_WORKSPACE (-6)    /* workspace too small */
+#define TPA_ERR_HIP (-7)          /* HIP runtime error */
+
+typedef struct tpa_layer tpa_layer;
+typedef void* tpa_stream; /* a hipStream_t; NULL = the null stream */
+
+enum tpa_dtype { TPA_F32 = 0, TPA_F16 = 1, TPA_BF16 = 2 };
+
+/* Methods of Table 1 (§3.1).  TPA_IDENTITY loads a slot that leaves its rows
+ * unchanged, so a tenant that does not adapt this projection can keep the
+ * same slot id in every layer. */
+enum tpa_method {
+  TPA_IDENTITY = 0,
+  TPA_LORA = 1,
+  TPA_DORA = 2,
+  TPA_IA3 = 3,
+  TPA_VERA = 4,
+  TPA_OFT = 5,
+  TPA_SSF = 6
+};
+
+/* Raw parameters of one adapter (host memory, float32, copied before
+ * tpa_adapter_load returns).  Fields a method does not use are ignored.
+ *   LoRA : A [d_in][rank], B [rank][d_out], c
+ *   DoRA : A, B, c as LoRA, m [d_out] magnitude (§5.1: s = m ⊘ ‖W + cAB‖_c)
+ *   (IA)3: l [d_out]
+ *   VeRA : d [r_v], e [d_out], c; the shared pair is set per layer with
+ *          tpa_vera_shared_set; rank must be 0 or r_v
+ *   OFT  : Q [d_in / oft_block][oft_block][oft_block], skew-symmetric
+ *   SSF  : s [d_out], b [d_out]                                           */
+typedef struct {
+  int32_t method;
+  int32_t rank;
+  int32_t oft_block;
+  float c;
+  const float* A;
+  const float* B;
+  const float* m;
+  const float* l;
+  const float* d;
+  const float* e;
+  const float* Q;
+  const float* s;
+  const float* b;
+} tpa_adapter_desc;
+
+/* Merged-slot metadata (Table 1 and the fold rule of §3.2).
+ *   live_mask: which slots stay live   S=1, B(shift)=2, R=4, D=8, E=16
+ *   fold_mask: which folds were made   C->A=1, E->B=2, C->D=4, D->A=8
+ *   term_kind: 0 no term, 1 term on owned factors, 2 term on shared factors */
+#define TPA_LIVE_S 1
+#define TPA_LIVE_B 2
+#define TPA_LIVE_R 4
+#define TPA_LIVE_D 8
+#define TPA_LIVE_E 16
+#define TPA_FOLD_C_A 1
+#define TPA_FOLD_E_B 2
+#define TPA_FOLD_C_D 4
+#define TPA_FOLD_D_A 8
+typedef struct {
+  int32_t method;
+  int32_t live_mask;
+  int32_t fold_mask;
+  int32_t term_kind;
+  int32_t rank;
+  int32_t oft_block;
+} tpa_adapter_info;
+
+/* Metadata a method gets by the fold rule (appendix "Folds": c folds into
+ * the first owned neighbour among A, d, B, e; d into an owned A or B; e into
+ * an owned B; s, b, R never fold).  Host only; needs no GPU. */
+tpa_status tpa_method_info(int32_t method, tpa_adapter_info* out);
+
+/* Create one adapted projection on `device`.
+ *   W_dev: device pointer to W [d_out][d_in] in `dtype`; borrowed, must
+ *          outlive the layer and not change while adapters are loaded
+ *          (DoRA's scale is computed from it at load).
+ *   max_slots: slots 0..max_slots-1; slot 0 is the permanent identity.
+ *   max_rank : largest rank of any term (owned rank or VeRA r_v); sizes the
+ *              workspace.
+ * Requires d_in a multiple of 64, d_out a multiple of 128, 2 <= max_slots <= 16384,
+ * 1 <= max_rank <= 512. */
+tpa_status tpa_layer_create(int32_t device, int32_t d_in, int32_t d_out, int32_t dtype,
+                            const void* W_dev, int32_t max_slots, int32_t max_rank,
+                            tpa_layer** out);
+tpa_status tpa_layer_destroy(tpa_layer* layer);
+
+/* Set VeRA's frozen pair shared by every VeRA slot of this layer
+ * (§2 "The methods", §3.2): A [d_in][r_v], B [r_v][d_out], float32 host.
+ * Stored once; r_v a multiple of 16, <= max_rank.  Must precede any VeRA
+ * load and cannot change while VeRA slots are loaded. */
+tpa_status tpa_vera_shared_set(tpa_layer* layer, int32_t r_v, const float* A, const float* B,
+                               tpa_stream stream);
+
+/* Admit one adapter (§5.1): validate, convert to normal form and fold what
+ * the fold rule allows, upload to the device, and return its slot (the
+ * lowest free slot >= 1).  Runs on `stream` and synchronizes it before
+ * returning; host arrays may be reused when the call returns.  Folds: LoRA and DoRA c -> A; DoRA
+ * s = m ⊘ ‖W + cAB‖_c computed on the device from W, then e = s -> B;
+ * VeRA c -> d; OFT blocks R_j = (I + Q_j)(I - Q_j)^-1 computed in float64 on
+ * the host.  Errors: -1 shapes/rank, -2 method, -3 no free slot, -5 Q not
+ * skew-symmetric, a non-finite value, or a zero column norm. */
+tpa_status tpa_adapter_load(tpa_layer* layer, const tpa_adapter_desc* desc, int32_t* slot_out,
+                            tpa_stream stream);
+
+/* Free a slot.  Synchronizes `stream` before releasing device memory, so
+ * forwards enqueued on it earlier still see the adapter.  -4 if the slot is
+ * not loaded. */
+tpa_status tpa_adapter_unload(tpa_layer* layer, int32_t slot, tpa_stream stream);
+
+tpa_status tpa_adapter_info_get(const tpa_layer* layer, int32_t slot, tpa_adapter_info* out);
+
+/* Bytes of device workspace a forward of any n <= n_max rows needs under
+ * the layer's current options; n_max <= 8192. */
+tpa_status tpa_workspace_size(const tpa_layer* layer, int32_t n_max, size_t* bytes);
+
+/* out[i] = F_{slot_of_row[i]}(x[i]) for i < n (eq. (1)).
+ *   x_dev [n][d_in], out_dev [n][d_out] in the layer dtype (out may not
+ *   alias x); slot_of_row_dev int32 [n] on the device; ws_dev of at least
+ *   tpa_workspace_size(n) bytes, 256-byte aligned, not shared by forwards
+ *   that may run concurrently.
+ * n <= 8192.  A row whose slot is out of range or not loaded is computed as
+ * the identity
+ * and raises the layer's sticky error flag (tpa_error_flag).  n = 0 is a
+ * no-op.  No host synchronization; capturable in a HIP graph. */
+tpa_status tpa_layer_forward(tpa_layer* layer, const void* x_dev, const int32_t* slot_of_row_dev,
+                             int32_t n, void* out_dev, void* ws_dev, size_t ws_bytes,
+                             tpa_stream stream);
+
+/* Read (and optionally clear) the layer's sticky invalid-slot flag.
+ * Synchronizes `stream`. */
+tpa_status tpa_error_flag(tpa_layer* layer, int32_t* flag_host, int32_t clear, tpa_stream stream);
+
+/* The row plan a forward of these rows uses, copied to host arrays
+ * (synchronizes `stream`).  Rows are ordered by (term class of the slot,
+ * slot, row), class 0 = term on owned factors, 1 = shared-factor term,
+ * 2 = no term.  Arrays (each may be NULL):
+ *   perm[n], row_slot[n], seg_ptr[n+1], seg_slot[n], class_ptr[4],
+ *   tiles[4 * max_tiles] as (p0, p1, kind, slot), oft_tiles[4 * max_tiles]
+ *   as (p0, p1, slot, 0), counts[4] = (n_seg, n_tiles, n_oft_tiles, invalid),
+ * with max_tiles from tpa_plan_max_tiles. */
+typedef struct {
+  int32_t* perm;
+  int32_t* row_slot;
+  int32_t* seg_ptr;
+  int32_t* seg_slot;
+  int32_t* class_ptr;
+  int32_t* tiles;
+  int32_t* oft_tiles;
+  int32_t* counts;
+} tpa_plan_host;
+tpa_status tpa_plan_max_tiles(const tpa_layer* layer, int32_t n, int32_t* max_tiles,
+                              int32_t* tile_rows);
+tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int32_t n,
+                          void* ws_dev, size_t ws_bytes, tpa_plan_host* out, tpa_stream stream);
+
+/* Kernel configuration pins, for tests and tuning.  value < 0 restores the
+ * automatic choice.
+ *   TPA_OPT_GEMM_SPLIT   : split-K factor of the base GEMM
+ *   TPA_OPT_SHRINK_SPLIT : split-K factor of the shrink
+ *   TPA_OPT_TILE_ROWS    : rows per tile of the plan (16 or 64)
+ *   TPA_OPT_GEMM_PATH    : 0 skinny (n <= 64) kernel, 1 LDS-tiled kernel
+ *   TPA_OPT_SCALE_ROUTE  : where s (and b) are applied (§4.3, appendix
+ *                          "Routes"): 0 inside the expand (route one),
+ *                          1 side kernel writing h⊙s before the expand,
+ *                          2 gathered scale pass after the expand,
+ *                          3 index scale: write s per row, then multiply */
+#define TPA_OPT_GEMM_SPLIT 1
+#define TPA_OPT_SHRINK_SPLIT 2
+#define TPA_OPT_TILE_ROWS 3
+#define TPA_OPT_GEMM_PATH 4
+#define TPA_OPT_SCALE_ROUTE 5
+tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
+
+/* Stage timing: when `events` is non-null, each forward records events[0]
+ * before its first kernel and events[1..5] after the plan, the OFT rotate,
+ * the base GEMM, the shrink and the expand (with any separate scale pass)
+ * on its stream.  `events` are hipEvent_t handles owned by the caller;
+ * count must be 6 (or 0 with null to stop).  For profiling only. */
+tpa_status tpa_layer_set_stage_events(tpa_layer* layer, void* const* events, int32_t count);
+
+/* Calibration probes (appendix "Constants"): a plain device copy of `bytes`
+ * (a multiple of 16, 16-byte aligned pointers) by a streaming kernel, and
+ * `count` chained one-block empty kernels for the launch cost. */
+tpa_status tpa_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, tpa_stream stream);
+tpa_status tpa_probe_empty(int32_t count, tpa_stream stream);
+
+/* Message of the last error on this thread ("" if none). */
+const char* tpa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPA_H */

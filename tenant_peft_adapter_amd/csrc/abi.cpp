@@ -1,0 +1,883 @@
+// The C ABI of include/tpa.h: layer and slot management, the admission
+// converter (normal form and folds), workspace layout and the forward's
+// launch sequence.  Kernels live in the .hip files next to this one.
+//
+// Scute paper (arXiv 2611.01089): §3.1 eq. (1) and Table 1 (the normal form
+// and its members), §3.2 and the appendix "Folds" (the fold rule), §5.1
+// (admission: DoRA's s at load, VeRA as d, e plus a reference to the shared
+// pair, OFT as explicit blocks), §5.2 (per-layer slot buffers set to the
+// identity; the forward's steps).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "tpa.h"
+
+using tpa::SlotDev;
+
+namespace {
+
+thread_local std::string g_err;
+
+tpa_status fail(tpa_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define TPA_HIP(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(TPA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+struct HostSlot {
+  bool used = false;
+  tpa_adapter_info info{};
+  void* mem = nullptr;
+};
+
+inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool finite_all(const float* p, size_t n) {
+  for (size_t i = 0; i < n; ++i)
+    if (!std::isfinite(p[i])) return false;
+  return true;
+}
+
+// The fold rule (appendix "Folds"): c folds into the first owned neighbour
+// among A, d, B, e; d into an owned A or B; e into an owned B; s, b and R
+// never fold.  `owned` and `present` use the bits below.
+enum { OWN_A = 1, OWN_B = 2, OWN_D = 4, OWN_E = 8, OWN_R = 16 };
+enum { PR_S = 1, PR_B = 2, PR_R = 4, PR_C = 8, PR_D = 16, PR_E = 32 };
+
+void fold_rule(int owned, int present, int* fold_mask, int* live_mask) {
+  int fm = 0, lm = 0;
+  if (present & PR_S) lm |= TPA_LIVE_S;
+  if (present & PR_B) lm |= TPA_LIVE_B;
+  if (present & PR_R) lm |= TPA_LIVE_R;
+  if (present & PR_C) {
+    if (owned & OWN_A)
+      fm |= TPA_FOLD_C_A;
+    else if (owned & OWN_D)
+      fm |= TPA_FOLD_C_D;
+    // c next to only shared tensors would stay live; no member of Table 1
+    // has such a term.
+  }
+  if (present & PR_D) {
+    if (owned & (OWN_A | OWN_B))
+      fm |= TPA_FOLD_D_A;
+    else
+      lm |= TPA_LIVE_D;
+  }
+  if (present & PR_E) {
+    if (owned & OWN_B)
+      fm |= TPA_FOLD_E_B;
+    else
+      lm |= TPA_LIVE_E;
+  }
+  *fold_mask = fm;
+  *live_mask = lm;
+}
+
+// Ownership and non-identity slots of each method (Table 1, §2, §5.1).
+bool method_shape(int method, int* owned, int* present, int* term) {
+  switch (method) {
+    case TPA_IDENTITY: *owned = 0; *present = 0; *term = 0; return true;
+    case TPA_LORA: *owned = OWN_A | OWN_B; *present = PR_C; *term = 1; return true;
+    case TPA_DORA: *owned = OWN_A | OWN_B; *present = PR_S | PR_C | PR_E; *term = 1; return true;
+    case TPA_IA3: *owned = 0; *present = PR_S; *term = 0; return true;
+    case TPA_VERA: *owned = OWN_D | OWN_E; *present = PR_C | PR_D | PR_E; *term = 2; return true;
+    case TPA_OFT: *owned = OWN_R; *present = PR_R; *term = 0; return true;
+    case TPA_SSF: *owned = 0; *present = PR_S | PR_B; *term = 0; return true;
+  }
+  return false;
+}
+
+// R_jᵀ = (I + Q)^-1 (I - Q) for the Cayley rotation R_j = (I + Q)(I - Q)^-1
+// of a skew-symmetric Q (the two factors commute and (I ± Q)ᵀ = I ∓ Q), by
+// Gaussian elimination with partial pivoting in float64.  Writes the b x b
+// block row-major, which is the transposed storage the rotate kernel reads.
+void cayley_transposed(const float* Q, int b, float* out) {
+  std::vector<double> M((size_t)b * 2 * b);
+  for (int i = 0; i < b; ++i)
+    for (int j = 0; j < b; ++j) {
+      const double q = Q[(size_t)i * b + j];
+      M[(size_t)i * 2 * b + j] = (i == j ? 1.0 : 0.0) + q;
+      M[(size_t)i * 2 * b + b + j] = (i == j ? 1.0 : 0.0) - q;
+    }
+  for (int c = 0; c < b; ++c) {
+    int piv = c;
+    for (int r = c + 1; r < b; ++r)
+      if (std::fabs(M[(size_t)r * 2 * b + c]) > std::fabs(M[(size_t)piv * 2 * b + c])) piv = r;
+    if (piv != c)
+      for (int j = 0; j < 2 * b; ++j) std::swap(M[(size_t)c * 2 * b + j], M[(size_t)piv * 2 * b + j]);
+    const double inv = 1.0 / M[(size_t)c * 2 * b + c];
+    for (int j = 0; j < 2 * b; ++j) M[(size_t)c * 2 * b + j] *= inv;
+    for (int r = 0; r < b; ++r) {
+      if (r == c) continue;
+      const double f = M[(size_t)r * 2 * b + c];
+      if (f == 0.0) continue;
+      for (int j = 0; j < 2 * b; ++j) M[(size_t)r * 2 * b + j] -= f * M[(size_t)c * 2 * b + j];
+    }
+  }
+  for (int i = 0; i < b; ++i)
+    for (int j = 0; j < b; ++j) out[(size_t)i * b + j] = (float)M[(size_t)i * 2 * b + b + j];
+}
+
+struct Config {
+  int tile_rows;
+  int gemm_path;  // 0 skinny, 1 tiled
+  int gemm_nb;
+  int gemm_split, gemm_kc;
+  int shrink_split, shrink_kc;
+  int scale_route;
+};
+
+struct Layout {
+  size_t perm, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
+  size_t x_rot, hpart, vpart, srow;
+  size_t total;
+  int max_tiles;
+};
+
+}  // namespace
+
+struct tpa_layer {
+  int device = 0;
+  int d_in = 0, d_out = 0, dtype = 0, max_slots = 0, max_rank = 0, kmax = 0;
+  const void* W = nullptr;
+  SlotDev* slots_dev = nullptr;
+  std::vector<SlotDev> slots_host;
+  std::vector<HostSlot> hs;
+  int32_t* flag_dev = nullptr;
+  void* vera_mem = nullptr;
+  const void* vera_At = nullptr;
+  const void* vera_Bt = nullptr;
+  int r_v = 0;
+  int n_owned = 0, n_vera = 0, n_dora = 0;
+  int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
+  int opt[6] = {-1, -1, -1, -1, -1, 0};
+  hipEvent_t stage_ev[6] = {};
+  bool stage_on = false;
+};
+
+namespace {
+
+int oft_bs_index(int bs) { return bs == 16 ? 0 : bs == 32 ? 1 : bs == 64 ? 2 : -1; }
+
+Config choose_config(const tpa_layer* L, int n) {
+  Config c{};
+  c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : (n <= 256 ? 16 : 64);
+  c.gemm_path = (n > 64) ? 1 : (L->opt[TPA_OPT_GEMM_PATH] >= 0 ? L->opt[TPA_OPT_GEMM_PATH] : 0);
+  if (c.gemm_path == 0) {
+    c.gemm_nb = (L->d_out / 64 >= 64) ? 4 : 1;
+    const int col_tiles = L->d_out / (16 * c.gemm_nb);
+    int split = L->opt[TPA_OPT_GEMM_SPLIT];
+    if (split <= 0) split = std::max(1, std::min(L->d_in / 256, (256 + col_tiles - 1) / col_tiles));
+    split = std::min(split, L->d_in / 32);
+    c.gemm_kc = round_up((L->d_in + split - 1) / split, 32);
+    c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
+  } else {
+    c.gemm_nb = 4;
+    const int tiles = ((n + 127) / 128) * (L->d_out / 128);
+    int split = L->opt[TPA_OPT_GEMM_SPLIT];
+    if (split <= 0) split = std::max(1, std::min(L->d_in / 512, (256 + tiles - 1) / tiles));
+    split = std::min(split, L->d_in / 64);
+    c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
+    c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
+  }
+  int ssplit = L->opt[TPA_OPT_SHRINK_SPLIT];
+  if (ssplit <= 0) ssplit = n <= 1024 ? std::max(1, L->d_in / 512) : std::max(1, L->d_in / 2048);
+  ssplit = std::min(ssplit, L->d_in / 32);
+  c.shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
+  c.shrink_split = (L->d_in + c.shrink_kc - 1) / c.shrink_kc;
+  c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];
+  return c;
+}
+
+int max_tiles_for(const tpa_layer* L, int n, int tile_rows) {
+  return (n + tile_rows - 1) / tile_rows + std::min(n, L->max_slots) + 2;
+}
+
+Layout make_layout(const tpa_layer* L, int n, const Config& c) {
+  Layout y{};
+  const size_t esz = tpa::dtype_size(L->dtype);
+  y.max_tiles = max_tiles_for(L, n, c.tile_rows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  y.perm = take(4 * (size_t)n);
+  y.row_slot = take(4 * (size_t)n);
+  y.rot_pos = take(4 * (size_t)n);
+  y.seg_ptr = take(4 * (size_t)(n + 1));
+  y.seg_slot = take(4 * (size_t)n);
+  y.tiles = take(16 * (size_t)y.max_tiles);
+  y.oft_tiles = take(16 * (size_t)y.max_tiles);
+  y.counts = take(4 * tpa::CNT_WORDS);
+  y.x_rot = take((size_t)n * L->d_in * esz);
+  const bool need_hpart = c.gemm_path == 0 || c.gemm_split > 1;
+  y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
+  y.vpart = take((size_t)c.shrink_split * n * L->kmax * 4);
+  y.srow = take(c.scale_route == 3 ? (size_t)n * L->d_out * 4 : 0);
+  y.total = off;
+  return y;
+}
+
+tpa::PlanArgs plan_args(tpa_layer* L, const int32_t* sor, int n, char* ws, const Layout& y,
+                        const Config& c) {
+  tpa::PlanArgs p{};
+  p.slot_of_row = sor;
+  p.slots = L->slots_dev;
+  p.n = n;
+  p.max_slots = L->max_slots;
+  p.tile_rows = c.tile_rows;
+  p.perm = reinterpret_cast<int32_t*>(ws + y.perm);
+  p.row_slot = reinterpret_cast<int32_t*>(ws + y.row_slot);
+  p.rot_pos = reinterpret_cast<int32_t*>(ws + y.rot_pos);
+  p.seg_ptr = reinterpret_cast<int32_t*>(ws + y.seg_ptr);
+  p.seg_slot = reinterpret_cast<int32_t*>(ws + y.seg_slot);
+  p.tiles = reinterpret_cast<int32_t*>(ws + y.tiles);
+  p.oft_tiles = reinterpret_cast<int32_t*>(ws + y.oft_tiles);
+  p.counts = reinterpret_cast<int32_t*>(ws + y.counts);
+  p.flag = L->flag_dev;
+  return p;
+}
+
+tpa_status stage(tpa_layer* L, int i, hipStream_t s) {
+  if (L->stage_on) TPA_HIP(hipEventRecord(L->stage_ev[i], s));
+  return TPA_OK;
+}
+
+tpa_status check_layer(const tpa_layer* L) {
+  if (!L) return fail(TPA_ERR_INVALID, "null layer");
+  return TPA_OK;
+}
+
+tpa_status upload_slot(tpa_layer* L, int slot, hipStream_t s) {
+  TPA_HIP(hipMemcpyAsync(L->slots_dev + slot, &L->slots_host[slot], sizeof(SlotDev), hipMemcpyHostToDevice, s));
+  TPA_HIP(hipStreamSynchronize(s));
+  return TPA_OK;
+}
+
+// A device float32 staging copy of a host array.
+struct Staging {
+  std::vector<void*> bufs;
+  ~Staging() {
+    for (void* p : bufs) (void)hipFree(p);
+  }
+  tpa_status put(const float* host, size_t count, float** dev) {
+    void* p = nullptr;
+    TPA_HIP(hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(float)));
+    bufs.push_back(p);
+    if (count) TPA_HIP(hipMemcpy(p, host, count * sizeof(float), hipMemcpyHostToDevice));
+    *dev = static_cast<float*>(p);
+    return TPA_OK;
+  }
+  tpa_status alloc(size_t count, float** dev) {
+    void* p = nullptr;
+    TPA_HIP(hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(float)));
+    bufs.push_back(p);
+    *dev = static_cast<float*>(p);
+    return TPA_OK;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* tpa_last_error(void) { return g_err.c_str(); }
+
+tpa_status tpa_method_info(int32_t method, tpa_adapter_info* out) {
+  if (!out) return fail(TPA_ERR_INVALID, "null output");
+  int owned, present, term;
+  if (!method_shape(method, &owned, &present, &term)) return fail(TPA_ERR_METHOD, "unknown method %d", method);
+  std::memset(out, 0, sizeof *out);
+  out->method = method;
+  out->term_kind = term;
+  fold_rule(owned, present, &out->fold_mask, &out->live_mask);
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_create(int32_t device, int32_t d_in, int32_t d_out, int32_t dtype, const void* W_dev,
+                            int32_t max_slots, int32_t max_rank, tpa_layer** out) {
+  if (!out) return fail(TPA_ERR_INVALID, "null output");
+  *out = nullptr;
+  if (d_in <= 0 || d_out <= 0 || d_in % 64 || d_out % 128)
+    return fail(TPA_ERR_INVALID, "d_in must be a positive multiple of 64 and d_out of 128 (got %d, %d)", d_in, d_out);
+  if (dtype < TPA_F32 || dtype > TPA_BF16) return fail(TPA_ERR_INVALID, "unknown dtype %d", dtype);
+  if (!W_dev) return fail(TPA_ERR_INVALID, "null W");
+  if (max_slots < 2 || max_slots > 16384) return fail(TPA_ERR_INVALID, "max_slots must be in [2, 16384]");
+  if (max_rank < 1 || max_rank > 512) return fail(TPA_ERR_INVALID, "max_rank must be in [1, 512]");
+  int ndev = 0;
+  TPA_HIP(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return fail(TPA_ERR_INVALID, "no device %d", device);
+  DeviceGuard guard(device);
+  tpa_layer* L = new tpa_layer();
+  L->device = device;
+  L->d_in = d_in;
+  L->d_out = d_out;
+  L->dtype = dtype;
+  L->W = W_dev;
+  L->max_slots = max_slots;
+  L->max_rank = max_rank;
+  L->kmax = round_up(max_rank, 16);
+  L->slots_host.assign(max_slots, SlotDev{});
+  for (auto& s : L->slots_host) s.cls = -1;
+  L->slots_host[0].cls = tpa::CLS_NONE;  // slot 0: the identity
+  L->hs.assign(max_slots, HostSlot{});
+  L->hs[0].used = true;
+  L->hs[0].info.method = TPA_IDENTITY;
+  hipError_t e = hipMalloc(&L->slots_dev, sizeof(SlotDev) * max_slots);
+  if (e == hipSuccess) e = hipMemcpy(L->slots_dev, L->slots_host.data(), sizeof(SlotDev) * max_slots, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMalloc(&L->flag_dev, sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(L->flag_dev, 0, sizeof(int32_t));
+  if (e != hipSuccess) {
+    if (L->slots_dev) (void)hipFree(L->slots_dev);
+    if (L->flag_dev) (void)hipFree(L->flag_dev);
+    delete L;
+    return fail(TPA_ERR_HIP, "layer allocation: %s", hipGetErrorString(e));
+  }
+  *out = L;
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_destroy(tpa_layer* L) {
+  if (!L) return TPA_OK;
+  DeviceGuard guard(L->device);
+  (void)hipDeviceSynchronize();
+  for (auto& h : L->hs)
+    if (h.mem) (void)hipFree(h.mem);
+  if (L->vera_mem) (void)hipFree(L->vera_mem);
+  if (L->slots_dev) (void)hipFree(L->slots_dev);
+  if (L->flag_dev) (void)hipFree(L->flag_dev);
+  delete L;
+  return TPA_OK;
+}
+
+tpa_status tpa_vera_shared_set(tpa_layer* L, int32_t r_v, const float* A, const float* B, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!A || !B) return fail(TPA_ERR_INVALID, "null VeRA factor");
+  if (r_v <= 0 || r_v % 16 || r_v > L->max_rank)
+    return fail(TPA_ERR_INVALID, "r_v must be a positive multiple of 16 and <= max_rank (got %d)", r_v);
+  if (L->n_vera > 0) return fail(TPA_ERR_INVALID, "VeRA slots are loaded; unload them first");
+  if (!finite_all(A, (size_t)L->d_in * r_v) || !finite_all(B, (size_t)r_v * L->d_out))
+    return fail(TPA_ERR_VALUE, "non-finite VeRA factor");
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TPA_HIP(hipStreamSynchronize(s));
+  if (L->vera_mem) {
+    TPA_HIP(hipFree(L->vera_mem));
+    L->vera_mem = nullptr;
+  }
+  const size_t esz = tpa::dtype_size(L->dtype);
+  const size_t at_bytes = align256((size_t)r_v * L->d_in * esz);
+  const size_t bt_bytes = align256((size_t)L->d_out * r_v * esz);
+  TPA_HIP(hipMalloc(&L->vera_mem, at_bytes + bt_bytes));
+  char* base = static_cast<char*>(L->vera_mem);
+  Staging st;
+  float *a32, *b32;
+  if (tpa_status e = st.put(A, (size_t)L->d_in * r_v, &a32)) return e;
+  if (tpa_status e = st.put(B, (size_t)r_v * L->d_out, &b32)) return e;
+  // A [d_in][r_v] -> [r_v][d_in];  B [r_v][d_out] -> [d_out][r_v].
+  TPA_HIP(tpa::launch_pack_transpose(L->dtype, a32, L->d_in, r_v, 1.f, nullptr, base, r_v, L->d_in, s));
+  TPA_HIP(tpa::launch_pack_transpose(L->dtype, b32, r_v, L->d_out, 1.f, nullptr, base + at_bytes, L->d_out, r_v, s));
+  TPA_HIP(hipStreamSynchronize(s));
+  L->vera_At = base;
+  L->vera_Bt = base + at_bytes;
+  L->r_v = r_v;
+  return TPA_OK;
+}
+
+tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* slot_out, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!d || !slot_out) return fail(TPA_ERR_INVALID, "null argument");
+  int owned, present, term;
+  if (!method_shape(d->method, &owned, &present, &term)) return fail(TPA_ERR_METHOD, "unknown method %d", d->method);
+  const int d_in = L->d_in, d_out = L->d_out;
+  const int m = d->method;
+  // Validation.
+  if (m == TPA_LORA || m == TPA_DORA) {
+    if (d->rank < 1 || d->rank > L->max_rank)
+      return fail(TPA_ERR_INVALID, "rank %d outside [1, max_rank=%d]", d->rank, L->max_rank);
+    if (!d->A || !d->B) return fail(TPA_ERR_INVALID, "null A or B");
+    if (!std::isfinite(d->c) || !finite_all(d->A, (size_t)d_in * d->rank) || !finite_all(d->B, (size_t)d->rank * d_out))
+      return fail(TPA_ERR_VALUE, "non-finite LoRA/DoRA factor");
+    if (m == TPA_DORA && (!d->m || !finite_all(d->m, d_out))) return fail(TPA_ERR_VALUE, "missing or non-finite DoRA m");
+  } else if (m == TPA_IA3) {
+    if (!d->l) return fail(TPA_ERR_INVALID, "null l");
+    if (!finite_all(d->l, d_out)) return fail(TPA_ERR_VALUE, "non-finite l");
+  } else if (m == TPA_SSF) {
+    if (!d->s || !d->b) return fail(TPA_ERR_INVALID, "null s or b");
+    if (!finite_all(d->s, d_out) || !finite_all(d->b, d_out)) return fail(TPA_ERR_VALUE, "non-finite s or b");
+  } else if (m == TPA_VERA) {
+    if (L->r_v == 0) return fail(TPA_ERR_INVALID, "VeRA shared pair not set");
+    if (d->rank != 0 && d->rank != L->r_v) return fail(TPA_ERR_INVALID, "VeRA rank %d != shared rank %d", d->rank, L->r_v);
+    if (!d->d || !d->e) return fail(TPA_ERR_INVALID, "null d or e");
+    if (!std::isfinite(d->c) || !finite_all(d->d, L->r_v) || !finite_all(d->e, d_out))
+      return fail(TPA_ERR_VALUE, "non-finite VeRA vector");
+  } else if (m == TPA_OFT) {
+    const int bs = d->oft_block;
+    if (oft_bs_index(bs) < 0 || d_in % bs) return fail(TPA_ERR_INVALID, "OFT block %d must be 16, 32 or 64 and divide d_in", bs);
+    if (!d->Q) return fail(TPA_ERR_INVALID, "null Q");
+    const size_t cnt = (size_t)d_in * bs;
+    if (!finite_all(d->Q, cnt)) return fail(TPA_ERR_VALUE, "non-finite Q");
+    for (int j = 0; j < d_in / bs; ++j) {
+      const float* q = d->Q + (size_t)j * bs * bs;
+      float mx = 0.f;
+      for (int i = 0; i < bs * bs; ++i) mx = std::max(mx, std::fabs(q[i]));
+      for (int r = 0; r < bs; ++r)
+        for (int c = 0; c <= r; ++c)
+          if (std::fabs(q[r * bs + c] + q[c * bs + r]) > 1e-6f * (1.f + mx))
+            return fail(TPA_ERR_VALUE, "Q block %d is not skew-symmetric at (%d, %d)", j, r, c);
+    }
+  }
+  int slot = -1;
+  for (int i = 1; i < L->max_slots; ++i)
+    if (!L->hs[i].used) {
+      slot = i;
+      break;
+    }
+  if (slot < 0) return fail(TPA_ERR_NO_SLOT, "all %d slots in use", L->max_slots);
+
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = tpa::dtype_size(L->dtype);
+  const bool post_scale = L->opt[TPA_OPT_SCALE_ROUTE] >= 2;  // s applied after the expand
+  SlotDev sd{};
+  sd.cls = term == 1 ? tpa::CLS_OWNED : term == 2 ? tpa::CLS_SHARED : tpa::CLS_NONE;
+  const int r_pad = (m == TPA_LORA || m == TPA_DORA) ? round_up(d->rank, 16) : 0;
+  // One device block per adapter: factors, vectors, blocks.
+  size_t off = 0;
+  size_t o_At = 0, o_Bt = 0, o_s = 0, o_b = 0, o_d = 0, o_e = 0, o_R = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  if (r_pad) {
+    o_At = take((size_t)r_pad * d_in * esz);
+    o_Bt = take((size_t)d_out * r_pad * esz);
+  }
+  if (m == TPA_DORA || m == TPA_IA3 || m == TPA_SSF) o_s = take((size_t)d_out * 4);
+  if (m == TPA_SSF) o_b = take((size_t)d_out * 4);
+  if (m == TPA_VERA) {
+    o_d = take((size_t)L->r_v * 4);
+    o_e = take((size_t)d_out * 4);
+  }
+  if (m == TPA_OFT) o_R = take((size_t)d_in * d->oft_block * esz);
+  void* mem = nullptr;
+  if (off) TPA_HIP(hipMalloc(&mem, off));
+  char* base = static_cast<char*>(mem);
+  Staging st;
+  int32_t* status_dev = nullptr;
+  // Conversion to normal form; TPA_HIP returns from this lambda on error.
+  auto convert = [&]() -> tpa_status {
+    if (m == TPA_LORA || m == TPA_DORA) {
+      float *a32, *b32, *at32;
+      if (tpa_status e = st.put(d->A, (size_t)d_in * d->rank, &a32)) return e;
+      if (tpa_status e = st.put(d->B, (size_t)d->rank * d_out, &b32)) return e;
+      // A' = c·A stored [r_pad][d_in] (fold c -> A).
+      if (tpa_status e = st.alloc((size_t)r_pad * d_in, &at32)) return e;
+      TPA_HIP(tpa::launch_pack_transpose(0, a32, d_in, d->rank, d->c, nullptr, at32, r_pad, d_in, s));
+      TPA_HIP(tpa::launch_convert(L->dtype, at32, base + o_At, (size_t)r_pad * d_in, 1.f, s));
+      sd.A = base + o_At;
+      sd.Bt = base + o_Bt;
+      sd.rank = r_pad;
+      if (m == TPA_LORA || post_scale)  // B stored [d_out][r_pad]
+        TPA_HIP(tpa::launch_pack_transpose(L->dtype, b32, d->rank, d_out, 1.f, nullptr, base + o_Bt, d_out, r_pad, s));
+      if (m == TPA_DORA) {
+        float* m32;
+        if (tpa_status e = st.put(d->m, d_out, &m32)) return e;
+        TPA_HIP(hipMalloc(&status_dev, sizeof(int32_t)));
+        TPA_HIP(hipMemsetAsync(status_dev, 0, sizeof(int32_t), s));
+        // s = m ⊘ ‖W + cAB‖_c on the device from W; e = s folds into B
+        // unless s is applied after the expand.
+        tpa::DoraArgs da{};
+        da.W = L->W;
+        da.At = at32;
+        da.B = b32;
+        da.m = m32;
+        da.d_in = d_in;
+        da.d_out = d_out;
+        da.r = d->rank;
+        da.r_pad = r_pad;
+        da.s = reinterpret_cast<float*>(base + o_s);
+        da.Bt = base + o_Bt;
+        da.fold_e = post_scale ? 0 : 1;
+        da.status = status_dev;
+        TPA_HIP(tpa::launch_dora_norm(L->dtype, da, s));
+        sd.s = da.s;
+      }
+    } else if (m == TPA_IA3 || m == TPA_SSF) {
+      const float* sv = m == TPA_IA3 ? d->l : d->s;
+      TPA_HIP(hipMemcpyAsync(base + o_s, sv, (size_t)d_out * 4, hipMemcpyHostToDevice, s));
+      sd.s = reinterpret_cast<float*>(base + o_s);
+      if (m == TPA_SSF) {
+        TPA_HIP(hipMemcpyAsync(base + o_b, d->b, (size_t)d_out * 4, hipMemcpyHostToDevice, s));
+        sd.b = reinterpret_cast<float*>(base + o_b);
+      }
+      TPA_HIP(hipStreamSynchronize(s));
+    } else if (m == TPA_VERA) {
+      // d' = c·d (fold c -> d); e stays live.
+      std::vector<float> dd(L->r_v);
+      for (int k = 0; k < L->r_v; ++k) dd[k] = d->c * d->d[k];
+      TPA_HIP(hipMemcpyAsync(base + o_d, dd.data(), (size_t)L->r_v * 4, hipMemcpyHostToDevice, s));
+      TPA_HIP(hipMemcpyAsync(base + o_e, d->e, (size_t)d_out * 4, hipMemcpyHostToDevice, s));
+      TPA_HIP(hipStreamSynchronize(s));
+      sd.d = reinterpret_cast<float*>(base + o_d);
+      sd.e = reinterpret_cast<float*>(base + o_e);
+      sd.rank = L->r_v;
+    } else if (m == TPA_OFT) {
+      const int bs = d->oft_block;
+      const size_t cnt = (size_t)d_in * bs;
+      std::vector<float> rt(cnt);
+      for (int j = 0; j < d_in / bs; ++j)
+        cayley_transposed(d->Q + (size_t)j * bs * bs, bs, rt.data() + (size_t)j * bs * bs);
+      float* r32;
+      if (tpa_status e = st.put(rt.data(), cnt, &r32)) return e;
+      TPA_HIP(tpa::launch_convert(L->dtype, r32, base + o_R, cnt, 1.f, s));
+      sd.Rt = base + o_R;
+      sd.has_R = 1;
+      sd.oft_block = bs;
+    }
+    TPA_HIP(hipStreamSynchronize(s));
+    if (status_dev) {
+      int32_t status = 0;
+      TPA_HIP(hipMemcpy(&status, status_dev, sizeof status, hipMemcpyDeviceToHost));
+      if (status) return fail(TPA_ERR_VALUE, "DoRA: zero or non-finite column norm");
+    }
+    return TPA_OK;
+  };
+  tpa_status err = convert();
+  if (status_dev) (void)hipFree(status_dev);
+  if (err) {
+    if (mem) (void)hipFree(mem);
+    return err;
+  }
+  L->slots_host[slot] = sd;
+  if ((err = upload_slot(L, slot, s))) {
+    L->slots_host[slot] = SlotDev{};
+    L->slots_host[slot].cls = -1;
+    if (mem) (void)hipFree(mem);
+    return err;
+  }
+  HostSlot& h = L->hs[slot];
+  h.used = true;
+  h.mem = mem;
+  h.info = tpa_adapter_info{};
+  h.info.method = m;
+  h.info.term_kind = term;
+  int pres = present;
+  if (m == TPA_DORA && post_scale) pres &= ~PR_E;  // e rides with s in the post-expand pass
+  fold_rule(owned, pres, &h.info.fold_mask, &h.info.live_mask);
+  h.info.rank = (m == TPA_LORA || m == TPA_DORA) ? d->rank : (m == TPA_VERA ? L->r_v : 0);
+  h.info.oft_block = m == TPA_OFT ? d->oft_block : 0;
+  if (term == 1) ++L->n_owned;
+  if (term == 2) ++L->n_vera;
+  if (m == TPA_DORA) ++L->n_dora;
+  if (m == TPA_OFT) ++L->n_oft_bs[oft_bs_index(d->oft_block)];
+  *slot_out = slot;
+  return TPA_OK;
+}
+
+tpa_status tpa_adapter_unload(tpa_layer* L, int32_t slot, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (slot <= 0 || slot >= L->max_slots || !L->hs[slot].used) return fail(TPA_ERR_UNKNOWN_SLOT, "slot %d is not loaded", slot);
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TPA_HIP(hipStreamSynchronize(s));
+  const tpa_adapter_info info = L->hs[slot].info;
+  L->slots_host[slot] = SlotDev{};
+  L->slots_host[slot].cls = -1;
+  if (tpa_status e = upload_slot(L, slot, s)) return e;
+  if (L->hs[slot].mem) TPA_HIP(hipFree(L->hs[slot].mem));
+  L->hs[slot] = HostSlot{};
+  if (info.term_kind == 1) --L->n_owned;
+  if (info.term_kind == 2) --L->n_vera;
+  if (info.method == TPA_DORA) --L->n_dora;
+  if (info.method == TPA_OFT) --L->n_oft_bs[oft_bs_index(info.oft_block)];
+  return TPA_OK;
+}
+
+tpa_status tpa_adapter_info_get(const tpa_layer* L, int32_t slot, tpa_adapter_info* out) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!out) return fail(TPA_ERR_INVALID, "null output");
+  if (slot < 0 || slot >= L->max_slots || !L->hs[slot].used) return fail(TPA_ERR_UNKNOWN_SLOT, "slot %d is not loaded", slot);
+  *out = L->hs[slot].info;
+  return TPA_OK;
+}
+
+tpa_status tpa_workspace_size(const tpa_layer* L, int32_t n_max, size_t* bytes) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!bytes || n_max < 0 || n_max > tpa::PLAN_MAX_ROWS)
+    return fail(TPA_ERR_INVALID, "n_max must be in [0, %d]", tpa::PLAN_MAX_ROWS);
+  if (n_max == 0) {
+    *bytes = 0;
+    return TPA_OK;
+  }
+  // Split and tile choices depend on n, so take the largest layout of any
+  // batch size up to n_max.
+  size_t best = 0;
+  for (int n = 1; n <= n_max; ++n) best = std::max(best, make_layout(L, n, choose_config(L, n)).total);
+  *bytes = best;
+  return TPA_OK;
+}
+
+tpa_status tpa_plan_max_tiles(const tpa_layer* L, int32_t n, int32_t* max_tiles, int32_t* tile_rows) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "bad n");
+  const Config c = choose_config(L, std::max(n, 1));
+  if (max_tiles) *max_tiles = max_tiles_for(L, n, c.tile_rows);
+  if (tile_rows) *tile_rows = c.tile_rows;
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, int32_t n, void* out, void* ws,
+                             size_t ws_bytes, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "n=%d outside [0, %d]", n, tpa::PLAN_MAX_ROWS);
+  if (n == 0) return TPA_OK;
+  if (!x || !sor || !out || !ws) return fail(TPA_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TPA_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (x == out) return fail(TPA_ERR_INVALID, "out may not alias x");
+  const Config c = choose_config(L, n);
+  const Layout y = make_layout(L, n, c);
+  if (ws_bytes < y.total) return fail(TPA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const tpa::PlanArgs p = plan_args(L, sor, n, w, y, c);
+  if (tpa_status st = stage(L, 0, s)) return st;
+  TPA_HIP(tpa::launch_plan(p, s));
+  if (tpa_status st = stage(L, 1, s)) return st;
+
+  const bool any_oft = L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
+  if (any_oft) {
+    tpa::OftArgs o{};
+    o.x = x;
+    o.perm = p.perm;
+    o.oft_tiles = p.oft_tiles;
+    o.counts = p.counts;
+    o.slots = L->slots_dev;
+    o.x_rot = w + y.x_rot;
+    o.d_in = L->d_in;
+    o.max_tiles = y.max_tiles;
+    static const int kBs[3] = {16, 32, 64};
+    for (int i = 0; i < 3; ++i) {
+      if (!L->n_oft_bs[i]) continue;
+      o.block = kBs[i];
+      TPA_HIP(tpa::launch_oft(L->dtype, c.tile_rows, o, s));
+    }
+  }
+
+  if (tpa_status st = stage(L, 2, s)) return st;
+  tpa::BaseGemmArgs g{};
+  g.x = x;
+  g.x_rot = any_oft ? w + y.x_rot : nullptr;
+  g.rot_pos = any_oft ? p.rot_pos : nullptr;
+  g.W = L->W;
+  g.n = n;
+  g.d_in = L->d_in;
+  g.d_out = L->d_out;
+  g.split = c.gemm_split;
+  g.kc = c.gemm_kc;
+  g.part = reinterpret_cast<float*>(w + y.hpart);
+  g.out = out;
+  if (c.gemm_path == 0)
+    TPA_HIP(tpa::launch_gemm_skinny(L->dtype, c.gemm_nb, g, s));
+  else
+    TPA_HIP(tpa::launch_gemm_tiled(L->dtype, g, s));
+  const bool hsplit = c.gemm_path == 0 || c.gemm_split > 1;
+  if (tpa_status st = stage(L, 3, s)) return st;
+
+  const bool any_term = L->n_owned > 0 || L->n_vera > 0;
+  if (any_term) {
+    tpa::ShrinkArgs sh{};
+    sh.x = x;
+    sh.perm = p.perm;
+    sh.row_slot = p.row_slot;
+    sh.tiles = p.tiles;
+    sh.counts = p.counts;
+    sh.slots = L->slots_dev;
+    sh.vera_At = L->vera_At;
+    sh.r_v = L->r_v;
+    sh.n = n;
+    sh.d_in = L->d_in;
+    sh.kmax = L->kmax;
+    sh.max_tiles = y.max_tiles;
+    sh.nblk = (L->kmax + 63) / 64;
+    sh.split = c.shrink_split;
+    sh.kc = c.shrink_kc;
+    sh.part = reinterpret_cast<float*>(w + y.vpart);
+    TPA_HIP(tpa::launch_shrink(L->dtype, c.tile_rows, sh, s));
+  }
+
+  if (tpa_status st = stage(L, 4, s)) return st;
+  tpa::ScaleArgs sc{};
+  sc.y = out;
+  sc.hpart = hsplit ? reinterpret_cast<const float*>(w + y.hpart) : nullptr;
+  sc.hsplit = c.gemm_split;
+  sc.row_slot = p.row_slot;
+  sc.slots = L->slots_dev;
+  sc.srow = reinterpret_cast<float*>(w + y.srow);
+  sc.n = n;
+  sc.d_out = L->d_out;
+  bool h_in_out = !hsplit;
+  if (c.scale_route == 1) {  // side kernel: h ⊙ s + b written before the expand
+    TPA_HIP(tpa::launch_scale_pass(L->dtype, 1, sc, s));
+    h_in_out = true;
+  }
+  tpa::ExpandArgs e{};
+  e.out = out;
+  e.hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(w + y.hpart);
+  e.hsplit = c.gemm_split;
+  e.perm = p.perm;
+  e.row_slot = p.row_slot;
+  e.tiles = p.tiles;
+  e.counts = p.counts;
+  e.slots = L->slots_dev;
+  e.vera_Bt = L->vera_Bt;
+  e.r_v = L->r_v;
+  e.vpart = reinterpret_cast<const float*>(w + y.vpart);
+  e.vsplit = c.shrink_split;
+  e.kmax = L->kmax;
+  e.n = n;
+  e.d_out = L->d_out;
+  e.max_tiles = y.max_tiles;
+  e.apply_scale = c.scale_route == 0;
+  TPA_HIP(tpa::launch_expand(L->dtype, c.tile_rows, e, s));
+  sc.hpart = nullptr;
+  if (c.scale_route == 2) TPA_HIP(tpa::launch_scale_pass(L->dtype, 2, sc, s));
+  if (c.scale_route == 3) {
+    TPA_HIP(tpa::launch_scale_pass(L->dtype, 3, sc, s));
+    TPA_HIP(tpa::launch_scale_pass(L->dtype, 4, sc, s));
+  }
+  return stage(L, 5, s);
+}
+
+tpa_status tpa_error_flag(tpa_layer* L, int32_t* flag_host, int32_t clear, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!flag_host) return fail(TPA_ERR_INVALID, "null output");
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TPA_HIP(hipStreamSynchronize(s));
+  TPA_HIP(hipMemcpy(flag_host, L->flag_dev, sizeof(int32_t), hipMemcpyDeviceToHost));
+  if (clear) {
+    const int32_t zero = 0;
+    TPA_HIP(hipMemcpy(L->flag_dev, &zero, sizeof zero, hipMemcpyHostToDevice));
+  }
+  return TPA_OK;
+}
+
+tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws, size_t ws_bytes, tpa_plan_host* o,
+                          tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!o || n < 0 || n > tpa::PLAN_MAX_ROWS || (n > 0 && (!sor || !ws))) return fail(TPA_ERR_INVALID, "bad argument");
+  const Config c = choose_config(L, std::max(n, 1));
+  const Layout y = make_layout(L, n, c);
+  if (ws_bytes < y.total) return fail(TPA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (n == 0) {
+    if (o->counts) std::memset(o->counts, 0, 4 * sizeof(int32_t));
+    if (o->class_ptr) std::memset(o->class_ptr, 0, 4 * sizeof(int32_t));
+    if (o->seg_ptr) o->seg_ptr[0] = 0;
+    return TPA_OK;
+  }
+  const tpa::PlanArgs p = plan_args(L, sor, n, w, y, c);
+  TPA_HIP(tpa::launch_plan(p, s));
+  TPA_HIP(hipStreamSynchronize(s));
+  int32_t cnt[tpa::CNT_WORDS];
+  TPA_HIP(hipMemcpy(cnt, p.counts, sizeof cnt, hipMemcpyDeviceToHost));
+  const int nseg = cnt[tpa::CNT_NSEG], nt = cnt[tpa::CNT_NTILES], no = cnt[tpa::CNT_NOFT];
+  if (o->perm) TPA_HIP(hipMemcpy(o->perm, p.perm, 4 * (size_t)n, hipMemcpyDeviceToHost));
+  if (o->row_slot) TPA_HIP(hipMemcpy(o->row_slot, p.row_slot, 4 * (size_t)n, hipMemcpyDeviceToHost));
+  if (o->seg_ptr) TPA_HIP(hipMemcpy(o->seg_ptr, p.seg_ptr, 4 * (size_t)(nseg + 1), hipMemcpyDeviceToHost));
+  if (o->seg_slot) TPA_HIP(hipMemcpy(o->seg_slot, p.seg_slot, 4 * (size_t)nseg, hipMemcpyDeviceToHost));
+  if (o->tiles) TPA_HIP(hipMemcpy(o->tiles, p.tiles, 16 * (size_t)nt, hipMemcpyDeviceToHost));
+  if (o->oft_tiles) TPA_HIP(hipMemcpy(o->oft_tiles, p.oft_tiles, 16 * (size_t)no, hipMemcpyDeviceToHost));
+  if (o->class_ptr) std::memcpy(o->class_ptr, cnt + tpa::CNT_CLASS0, 4 * sizeof(int32_t));
+  if (o->counts) {
+    o->counts[0] = nseg;
+    o->counts[1] = nt;
+    o->counts[2] = no;
+    o->counts[3] = cnt[tpa::CNT_INVALID];
+  }
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_SCALE_ROUTE) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_TILE_ROWS && value > 0 && value != 16 && value != 64)
+    return fail(TPA_ERR_INVALID, "tile rows must be 16 or 64");
+  if (key == TPA_OPT_GEMM_PATH && value > 1) return fail(TPA_ERR_INVALID, "gemm path must be 0 or 1");
+  if (key == TPA_OPT_SCALE_ROUTE) {
+    if (value < 0) value = 0;
+    if (value > 3) return fail(TPA_ERR_INVALID, "scale route must be 0..3");
+    const bool was_post = L->opt[TPA_OPT_SCALE_ROUTE] >= 2, post = value >= 2;
+    if (was_post != post && L->n_dora > 0)
+      return fail(TPA_ERR_INVALID, "DoRA slots are folded for the current route; unload them first");
+  }
+  L->opt[key] = value;
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_set_stage_events(tpa_layer* L, void* const* events, int32_t count) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!events) {
+    L->stage_on = false;
+    return TPA_OK;
+  }
+  if (count != 6) return fail(TPA_ERR_INVALID, "stage events: count must be 6");
+  for (int i = 0; i < 6; ++i) {
+    if (!events[i]) return fail(TPA_ERR_INVALID, "stage events: null event %d", i);
+    L->stage_ev[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  L->stage_on = true;
+  return TPA_OK;
+}
+
+tpa_status tpa_probe_copy(void* dst, const void* src, size_t bytes, tpa_stream stream) {
+  if (!dst || !src || (bytes & 15) || (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+    return fail(TPA_ERR_INVALID, "copy needs 16-byte aligned pointers and a multiple of 16 bytes");
+  TPA_HIP(tpa::launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+  return TPA_OK;
+}
+
+tpa_status tpa_probe_empty(int32_t count, tpa_stream stream) {
+  if (count < 0) return fail(TPA_ERR_INVALID, "negative count");
+  TPA_HIP(tpa::launch_empty(count, static_cast<hipStream_t>(stream)));
+  return TPA_OK;
+}
+
+}  // extern "C"

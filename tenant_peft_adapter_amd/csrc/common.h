@@ -1,0 +1,125 @@
+// Shared device helpers for the gfx950 kernels: element types, 8-element
+// operand fragments and the 16x16 MFMA step.
+//
+// Fragment convention (used by every MFMA kernel here).  One
+// v_mfma_f32_16x16x32 step multiplies a 16x32 operand "a" by a 32x16 operand
+// "b".  Lane l holds row (l % 16) of a and column (l % 16) of b, each as 8
+// consecutive k values starting at k = 8 * (l / 16).  Both operands use the
+// same k order, so any fixed permutation of k inside a step is harmless.
+// The 4 fp32 results of lane l are D[4 * (l / 16) + v][l % 16], v = 0..3.
+//
+// Kernels compute D = W_tile · X_tileᵀ (a = weight rows = output columns,
+// b = input rows), so a lane ends up holding output columns of one input
+// row.  With NB column blocks per wave, block b's a-row i is mapped to the
+// output column 4·NB·(i / 4) + 4·b + (i % 4): lane l then holds the 4·NB
+// consecutive columns [4·NB·(l / 16), 4·NB·(l / 16 + 1)) of row l % 16, so
+// epilogues load and store contiguous runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpa {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T>
+struct Frag;
+template <>
+struct Frag<f16> {
+  typedef f16x8 V;
+};
+template <>
+struct Frag<bf16> {
+  typedef bf16x8 V;
+};
+template <>
+struct Frag<float> {
+  typedef f32x8 V;
+};
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::V load_frag(const T* p) {
+  return *reinterpret_cast<const typename Frag<T>::V*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::V zero_frag() {
+  typename Frag<T>::V v = {};
+  return v;
+}
+
+__device__ __forceinline__ f32x4 mma(f32x4 acc, f16x8 a, f16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 acc, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 acc, f32x8 a, f32x8 b) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], b[t], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename T>
+__device__ __forceinline__ T to_t(float v);
+template <>
+__device__ __forceinline__ f16 to_t<f16>(float v) {
+  return (f16)v;
+}
+template <>
+__device__ __forceinline__ bf16 to_t<bf16>(float v) {
+  return (bf16)v;
+}
+template <>
+__device__ __forceinline__ float to_t<float>(float v) {
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f(T v) {
+  return (float)v;
+}
+
+// Output column, within a wave's group of 16*NB columns, of a-row i of
+// column block b (see the file comment).
+template <int NB>
+__device__ __forceinline__ int perm_col(int i, int b) {
+  return 4 * NB * (i >> 2) + 4 * b + (i & 3);
+}
+
+// Term class of a slot, as ordered by the row plan.
+enum { CLS_OWNED = 0, CLS_SHARED = 1, CLS_NONE = 2 };
+
+// Per-slot device record: what a row of this slot needs in the hot path.
+// cls < 0 marks a slot that is not loaded.
+struct SlotDev {
+  int32_t cls;        // CLS_OWNED / CLS_SHARED / CLS_NONE, or -1
+  int32_t rank;       // rank of the owned term (CLS_OWNED)
+  int32_t has_R;      // OFT rotation present
+  int32_t oft_block;  // block size of R
+  const void* A;      // owned: c·A as [rank][d_in]
+  const void* Bt;     // owned: B diag(e) as [d_out][rank]
+  const float* s;     // output scale [d_out] or null
+  const float* b;     // output shift [d_out] or null
+  const float* d;     // VeRA inner vector c·d [r_v] or null
+  const float* e;     // VeRA outer vector [d_out] or null
+  const void* Rt;     // OFT blocks, each stored transposed: [d_in / bs][bs][bs]
+};
+
+// Workspace counters written by the plan kernel.
+enum {
+  CNT_NSEG = 0,
+  CNT_NTILES = 1,
+  CNT_NOFT = 2,
+  CNT_INVALID = 3,
+  CNT_CLASS0 = 4,  // class_ptr[0..3] at 4..7
+  CNT_WORDS = 16
+};
+
+}  // namespace tpa

@@ -1,0 +1,301 @@
+// The expand: one pass over every output tile that finishes the layer.
+//
+// Scute paper (arXiv 2611.01089):
+//   * §2 "The LoRA schedule": the expand reads h, adds V B and writes the
+//     result, one tile of rows (one segment) at a time.
+//   * §4.1 route one and §5.2: the output scale s is applied inside the
+//     expand as each tile finishes, so a live s costs one extra read of the
+//     adapter's vector per tile (the shift b rides along the same way).
+//   * §4.1 route two, second GEMM: for VeRA rows, U · B_v over tiles of rows
+//     whatever their tenant, each row multiplied by its tenant's e before it
+//     is added; B_v is read once per tile, not once per tenant.
+//
+// Work-group = one plan tile (up to 16·MB rows in plan order) x 256 output
+// columns; each wave owns 64 columns.  The tile's V (or U) rows are summed
+// over the shrink's split-K partials in a fixed order and staged in LDS in
+// the layer type; the term is an MFMA product with the factor stored
+// [d_out][rank], computed transposed so each lane holds 16 consecutive
+// output columns of one row.  The epilogue reads h (from `out`, or summed
+// from the base GEMM's split partials in a fixed order), applies s and b of
+// the row's slot, adds the term and writes the row segment once.
+#include "internal.h"
+
+namespace tpa {
+
+namespace {
+
+constexpr int THREADS = 256;
+
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::V lds_frag(const T* p) {
+  return *reinterpret_cast<const typename Frag<T>::V*>(p);
+}
+template <>
+__device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <typename T>
+__device__ __forceinline__ void load_run16(const T* src, float* v) {
+  typename Frag<T>::V lo = *reinterpret_cast<const typename Frag<T>::V*>(src);
+  typename Frag<T>::V hi = *reinterpret_cast<const typename Frag<T>::V*>(src + 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = to_f<T>(lo[j]);
+    v[8 + j] = to_f<T>(hi[j]);
+  }
+}
+template <>
+__device__ __forceinline__ void load_run16<float>(const float* src, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * q);
+    v[4 * q] = x[0];
+    v[4 * q + 1] = x[1];
+    v[4 * q + 2] = x[2];
+    v[4 * q + 3] = x[3];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_run16(T* dst, const float* v) {
+  typename Frag<T>::V lo, hi;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    lo[j] = to_t<T>(v[j]);
+    hi[j] = to_t<T>(v[8 + j]);
+  }
+  *reinterpret_cast<typename Frag<T>::V*>(dst) = lo;
+  *reinterpret_cast<typename Frag<T>::V*>(dst + 8) = hi;
+}
+template <>
+__device__ __forceinline__ void store_run16<float>(float* dst, const float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(dst + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+
+// h of one row segment of 16 columns: from the split partials (summed in
+// split order) or from the layer-type buffer.
+__device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size_t split_stride,
+                                            float* v) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = 0.f;
+  for (int s = 0; s < hsplit; ++s) {
+    const float* src = hpart + (size_t)s * split_stride;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * q);
+      v[4 * q] += x[0];
+      v[4 * q + 1] += x[1];
+      v[4 * q + 2] += x[2];
+      v[4 * q + 3] += x[3];
+    }
+  }
+}
+
+template <typename T, int MB, bool HPART>
+__global__ __launch_bounds__(THREADS) void expand_kernel(ExpandArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* vl = reinterpret_cast<T*>(smem);
+  constexpr int TM = 16 * MB;
+  const int LDV = a.kmax + 16 / (int)sizeof(T);
+  const int t = blockIdx.x;
+  if (t >= a.counts[CNT_NTILES]) return;
+  const int* tile = a.tiles + 4 * t;
+  const int p0 = tile[0], p1 = tile[1], kind = tile[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.y * 256 + 64 * wave;
+  const bool wact = n0 < a.d_out;
+
+  int K = 0;
+  const T* Bt = nullptr;
+  if (kind == CLS_OWNED) {
+    const SlotDev& sd = a.slots[tile[3]];
+    K = sd.rank;
+    Bt = static_cast<const T*>(sd.Bt);
+  } else if (kind == CLS_SHARED) {
+    K = a.r_v;
+    Bt = static_cast<const T*>(a.vera_Bt);
+  }
+
+  f32x4 acc[4][MB];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (K > 0) {
+    // Stage the tile's V rows: sum of the shrink's split partials.
+    const int rows = p1 - p0;
+    const int k4 = K / 4;
+    const size_t sstride = (size_t)a.n * a.kmax;
+    for (int idx = tid; idx < TM * k4; idx += THREADS) {
+      const int r = idx / k4, c = 4 * (idx % k4);
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (r < rows) {
+        const float* src = a.vpart + (size_t)(p0 + r) * a.kmax + c;
+        for (int s = 0; s < a.vsplit; ++s) v += *reinterpret_cast<const f32x4*>(src + s * sstride);
+      }
+      T* dst = vl + r * LDV + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(v[q]);
+    }
+    __syncthreads();
+    if (wact) {
+      for (int k0 = 0; k0 < K; k0 += 32) {
+        const bool kok = k0 + 8 * g < K;
+        typename Frag<T>::V af[4], bf[MB];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          af[b] = kok ? load_frag<T>(Bt + (size_t)(n0 + perm_col<4>(i16, b)) * K + k0 + 8 * g)
+                      : zero_frag<T>();
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          bf[m] = kok ? lds_frag<T>(vl + (16 * m + i16) * LDV + k0 + 8 * g) : zero_frag<T>();
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+      }
+    }
+  }
+  if (!wact) return;
+
+  T* out = static_cast<T*>(a.out);
+  const int col = n0 + 16 * g;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int p = p0 + 16 * m + i16;
+    if (p >= p1) continue;
+    const int row = a.perm[p];
+    const SlotDev& sd = a.slots[a.row_slot[row]];
+    float v[16];
+    T* orow = out + (size_t)row * a.d_out + col;
+    if (HPART)
+      sum_parts16(a.hpart + (size_t)row * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
+    else
+      load_run16<T>(orow, v);
+    if (a.apply_scale) {
+      if (sd.s) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(sd.s + col + 4 * q);
+          v[4 * q] *= s4[0];
+          v[4 * q + 1] *= s4[1];
+          v[4 * q + 2] *= s4[2];
+          v[4 * q + 3] *= s4[3];
+        }
+      }
+      if (sd.b) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(sd.b + col + 4 * q);
+          v[4 * q] += b4[0];
+          v[4 * q + 1] += b4[1];
+          v[4 * q + 2] += b4[2];
+          v[4 * q + 3] += b4[3];
+        }
+      }
+    }
+    if (K > 0) {
+      if (kind == CLS_SHARED) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const f32x4 e4 = *reinterpret_cast<const f32x4*>(sd.e + col + 4 * b);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[4 * b + q] += acc[b][m][q] * e4[q];
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[4 * b + q] += acc[b][m][q];
+      }
+    }
+    store_run16<T>(orow, v);
+  }
+}
+
+// Separate scale passes (route comparison).  One thread per 16 columns.
+template <typename T>
+__global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mode) {
+  const size_t idx = (size_t)blockIdx.x * THREADS + threadIdx.x;
+  const int runs = a.d_out / 16;
+  if (idx >= (size_t)a.n * runs) return;
+  const int row = (int)(idx / runs);
+  const int col = 16 * (int)(idx % runs);
+  const SlotDev& sd = a.slots[a.row_slot[row]];
+  T* y = static_cast<T*>(a.y) + (size_t)row * a.d_out + col;
+  float v[16];
+  if (mode == 3) {  // index scale, step one: a per-row copy of the scale
+    float* sr = a.srow + (size_t)row * a.d_out + col;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sr[j] = sd.s ? sd.s[col + j] : 1.f;
+    return;
+  }
+  if (mode == 1 && a.hpart)
+    sum_parts16(a.hpart + (size_t)row * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
+  else
+    load_run16<T>(y, v);
+  if (mode == 4) {  // index scale, step two: multiply by the per-row copy
+    const float* sr = a.srow + (size_t)row * a.d_out + col;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] *= sr[j];
+  } else if (sd.s) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] *= sd.s[col + j];
+  }
+  if (sd.b) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] += sd.b[col + j];
+  }
+  store_run16<T>(y, v);
+}
+
+template <typename T, int MB>
+hipError_t expand_launch(const ExpandArgs& a, hipStream_t s) {
+  dim3 grid(a.max_tiles, (a.d_out + 255) / 256);
+  const size_t lds = (size_t)(16 * MB) * (a.kmax + 16 / sizeof(T)) * sizeof(T);
+  if (a.hpart)
+    hipLaunchKernelGGL((expand_kernel<T, MB, true>), grid, dim3(THREADS), lds, s, a);
+  else
+    hipLaunchKernelGGL((expand_kernel<T, MB, false>), grid, dim3(THREADS), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t expand_tm(int tile_rows, const ExpandArgs& a, hipStream_t s) {
+  if (tile_rows == 16) return expand_launch<T, 1>(a, s);
+  if (tile_rows == 64) return expand_launch<T, 4>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case 0: return expand_tm<float>(tile_rows, a, s);
+    case 1: return expand_tm<f16>(tile_rows, a, s);
+    case 2: return expand_tm<bf16>(tile_rows, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scale_pass(int dtype, int mode, const ScaleArgs& a, hipStream_t s) {
+  const size_t work = (size_t)a.n * (a.d_out / 16);
+  dim3 grid((unsigned)((work + THREADS - 1) / THREADS));
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(scale_pass_kernel<float>, grid, dim3(THREADS), 0, s, a, mode); break;
+    case 1: hipLaunchKernelGGL(scale_pass_kernel<f16>, grid, dim3(THREADS), 0, s, a, mode); break;
+    case 2: hipLaunchKernelGGL(scale_pass_kernel<bf16>, grid, dim3(THREADS), 0, s, a, mode); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpa

@@ -1,0 +1,157 @@
+// Internal interface between the C ABI (abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace tpa {
+
+// ---------------------------------------------------------------- plan ----
+struct PlanArgs {
+  const int32_t* slot_of_row;
+  const SlotDev* slots;
+  int32_t n;
+  int32_t max_slots;
+  int32_t tile_rows;
+  int32_t* perm;       // [n]
+  int32_t* row_slot;   // [n]
+  int32_t* rot_pos;    // [n]
+  int32_t* seg_ptr;    // [n + 1]
+  int32_t* seg_slot;   // [n]
+  int32_t* tiles;      // [4 * max_tiles]
+  int32_t* oft_tiles;  // [4 * max_tiles]
+  int32_t* counts;     // [CNT_WORDS]
+  int32_t* flag;       // layer's sticky invalid-slot flag
+};
+constexpr int PLAN_MAX_ROWS = 8192;
+hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------- OFT rotate ----
+struct OftArgs {
+  const void* x;           // [n][d_in]
+  const int32_t* perm;
+  const int32_t* oft_tiles;
+  const int32_t* counts;
+  const SlotDev* slots;
+  void* x_rot;             // [n][d_in], row p = rotated row perm[p]
+  int32_t d_in;
+  int32_t block;           // OFT block size of this launch (16, 32 or 64)
+  int32_t max_tiles;
+};
+hipError_t launch_oft(int dtype, int tile_rows, const OftArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMMs ---
+// Base GEMM h = X_sel Wᵀ for all n rows, where row i of X_sel is x[i] or,
+// for an OFT row, x_rot[rot_pos[i]].
+struct BaseGemmArgs {
+  const void* x;
+  const void* x_rot;       // may be null when no row has R
+  const int32_t* rot_pos;  // may be null when no row has R
+  const void* W;           // [d_out][d_in]
+  int32_t n, d_in, d_out;
+  int32_t split;           // split-K factor
+  int32_t kc;              // k range per split (multiple of 32)
+  float* part;             // [split][n][d_out] fp32 partials (split path)
+  void* out;               // [n][d_out] in the layer type (split == 1, tiled)
+};
+// Skinny kernel: n <= 64 rows, weights streamed straight into registers.
+hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, hipStream_t stream);
+// LDS-tiled 128x128 kernel; writes `out` when split == 1, else `part`.
+hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t stream);
+
+// Shrink over the plan's tiles: owned-term tiles V[p] = x[perm[p]] A'ᵀ,
+// shared-term tiles U[p] = (x[perm[p]] A_vᵀ) ⊙ d'[slot].  Writes fp32
+// partials [split][n][kmax] indexed by plan position p.
+struct ShrinkArgs {
+  const void* x;
+  const int32_t* perm;
+  const int32_t* row_slot;
+  const int32_t* tiles;
+  const int32_t* counts;
+  const SlotDev* slots;
+  const void* vera_At;     // [r_v][d_in] or null
+  int32_t r_v;
+  int32_t n, d_in;
+  int32_t kmax;            // row stride of the partials
+  int32_t max_tiles;
+  int32_t nblk;            // column blocks of 64 per tile item
+  int32_t split, kc;
+  float* part;
+};
+hipError_t launch_shrink(int dtype, int tile_rows, const ShrinkArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- expand --
+// out[row] = h[row] ⊙ s + b + V[p] B'ᵀ (owned tile) or (U[p] B_vᵀ) ⊙ e
+// (shared tile), for row = perm[p].  h is read from `out` (in place, layer
+// type) or summed from `hpart` (fp32 split-K partials, fixed order).
+struct ExpandArgs {
+  void* out;
+  const float* hpart;      // null: read h from out
+  int32_t hsplit;
+  const int32_t* perm;
+  const int32_t* row_slot;
+  const int32_t* tiles;
+  const int32_t* counts;
+  const SlotDev* slots;
+  const void* vera_Bt;     // [d_out][r_v]
+  int32_t r_v;
+  const float* vpart;      // shrink partials [vsplit][n][kmax]
+  int32_t vsplit, kmax;
+  int32_t n, d_out;
+  int32_t max_tiles;
+  int32_t apply_scale;     // 0: leave s and b to a separate pass
+};
+hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs& a, hipStream_t stream);
+
+// Separate scale passes, for the route comparison of the appendix "Routes".
+//   mode 1 side kernel:  h ← h ⊙ s + b        (before the expand)
+//   mode 2 gathered:     out ← out ⊙ s + b    (after the expand)
+//   mode 3 index scale, step one:  srow[i] ← s[slot(i)]
+//   mode 4 index scale, step two:  out ← out ⊙ srow + b
+struct ScaleArgs {
+  void* y;                 // [n][d_out] layer type
+  const float* hpart;      // side kernel on split partials: sum them into y
+  int32_t hsplit;
+  const int32_t* row_slot;
+  const SlotDev* slots;
+  float* srow;             // index scale buffers [n][d_out]
+  int32_t n, d_out;
+};
+hipError_t launch_scale_pass(int dtype, int mode, const ScaleArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------ load time ---
+// DoRA: norm[j] = ‖W[j,:] + c·(A B)[:, j]‖ over d_in; s[j] = m[j] / norm[j];
+// Bt[j][k] = B[k][j]·s[j] (k < r), 0 for r <= k < r_pad.  status |= 1 for a
+// zero or non-finite norm.
+struct DoraArgs {
+  const void* W;           // [d_out][d_in]
+  const float* At;         // c·A as fp32 [r][d_in]
+  const float* B;          // [r][d_out]
+  const float* m;          // [d_out]
+  int32_t d_in, d_out, r, r_pad;
+  float* s;                // [d_out]
+  void* Bt;                // [d_out][r_pad], written when fold_e
+  int32_t fold_e;
+  int32_t* status;
+};
+hipError_t launch_dora_norm(int dtype, const DoraArgs& a, hipStream_t stream);
+// dst[i] = (T)(alpha * src[i]) for i < count.
+hipError_t launch_convert(int dtype, const float* src, void* dst, size_t count, float alpha,
+                          hipStream_t stream);
+// dst[c][r] = (T)(alpha * src[r][c] * colscale[c]) for a [rows][cols] source;
+// dst is [cols_pad][ld] with rows < ld; rows >= `rows` and cols >= `cols`
+// are zero.  colscale may be null.
+hipError_t launch_pack_transpose(int dtype, const float* src, int rows, int cols, float alpha,
+                                 const float* colscale, void* dst, int cols_pad, int ld,
+                                 hipStream_t stream);
+
+// -------------------------------------------------------------- probes ----
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+hipError_t launch_empty(int count, hipStream_t stream);
+
+size_t dtype_size(int dtype);
+
+}  // namespace tpa

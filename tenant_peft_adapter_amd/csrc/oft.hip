@@ -1,0 +1,115 @@
+// OFT's input transform in a pass of its own (Scute paper, arXiv
+// 2611.01089, §4.1 route three, and the appendix "Propositions A2-A4"): each
+// OFT row is multiplied by its tenant's block-diagonal R before the shared
+// GEMM, which then sees the rotated row.  The pass reads and writes
+// [rows, d_in] once plus each tenant's d_in / b blocks of b x b.
+//
+// Work-group = one OFT tile of the plan (rows of one tenant, so each R
+// block is read once per tile) x 16 consecutive blocks (4 per wave).  A
+// block is an MFMA product with K = b: D = Rᵀ · x_blockᵀ, so each lane ends
+// with 4·(b/16) consecutive columns of one row.  R blocks are stored
+// transposed ([c][t] = R[t][c]).  The rotated row p (plan order) is written
+// to x_rot[p].
+#include "internal.h"
+
+namespace tpa {
+
+namespace {
+
+constexpr int THREADS = 256;
+constexpr int BLOCKS_PER_WG = 16;
+
+template <typename T, int MB, int BS>
+__global__ __launch_bounds__(THREADS) void oft_kernel(OftArgs a) {
+  constexpr int NB = BS / 16;
+  const int t = blockIdx.x;
+  if (t >= a.counts[CNT_NOFT]) return;
+  const int* tile = a.oft_tiles + 4 * t;
+  const int p0 = tile[0], p1 = tile[1];
+  const SlotDev& sd = a.slots[tile[2]];
+  if (sd.oft_block != BS) return;
+  const T* Rt = static_cast<const T*>(sd.Rt);
+  const T* X = static_cast<const T*>(a.x);
+  T* XR = static_cast<T*>(a.x_rot);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int nblocks = a.d_in / BS;
+
+  const T* xp[MB];
+  bool xv[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int p = p0 + 16 * m + i16;
+    xv[m] = p < p1;
+    xp[m] = X + (size_t)(xv[m] ? a.perm[p] : 0) * a.d_in + 8 * g;
+  }
+
+  for (int j = 0; j < BLOCKS_PER_WG / 4; ++j) {
+    const int kb = blockIdx.y * BLOCKS_PER_WG + 4 * j + wave;
+    if (kb >= nblocks) break;
+    f32x4 acc[NB][MB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < BS; k0 += 32) {
+      const bool kok = k0 + 8 * g < BS;
+      typename Frag<T>::V af[NB], bf[MB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        af[b] = kok ? load_frag<T>(Rt + ((size_t)kb * BS + perm_col<NB>(i16, b)) * BS + k0 + 8 * g)
+                    : zero_frag<T>();
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        bf[m] = (kok && xv[m]) ? load_frag<T>(xp[m] + kb * BS + k0) : zero_frag<T>();
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int p = p0 + 16 * m + i16;
+      if (p >= p1) continue;
+      T* dst = XR + (size_t)p * a.d_in + kb * BS + 4 * NB * g;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[4 * b + q] = to_t<T>(acc[b][m][q]);
+    }
+  }
+}
+
+template <typename T, int MB>
+hipError_t oft_bs(const OftArgs& a, hipStream_t s) {
+  const int nblocks = a.d_in / a.block;
+  dim3 grid(a.max_tiles, (nblocks + BLOCKS_PER_WG - 1) / BLOCKS_PER_WG);
+  switch (a.block) {
+    case 16: hipLaunchKernelGGL((oft_kernel<T, MB, 16>), grid, dim3(THREADS), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((oft_kernel<T, MB, 32>), grid, dim3(THREADS), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((oft_kernel<T, MB, 64>), grid, dim3(THREADS), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t oft_tm(int tile_rows, const OftArgs& a, hipStream_t s) {
+  if (tile_rows == 16) return oft_bs<T, 1>(a, s);
+  if (tile_rows == 64) return oft_bs<T, 4>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_oft(int dtype, int tile_rows, const OftArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case 0: return oft_tm<float>(tile_rows, a, s);
+    case 1: return oft_tm<f16>(tile_rows, a, s);
+    case 2: return oft_tm<bf16>(tile_rows, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpa

@@ -1,0 +1,101 @@
+"""A thin object wrapper over the C ABI for one adapted projection.
+
+PyTorch supplies device memory (weights, inputs, outputs, workspace) and
+the stream; every step of the computation runs in libtpa.so's kernels.
+"""
+import numpy as np
+import torch
+
+from . import binding as B
+
+TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+_TPA_OF_TORCH = {torch.float32: B.TPA_F32, torch.float16: B.TPA_F16, torch.bfloat16: B.TPA_BF16}
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+class AdaptedLayer:
+    """One projection y = F_{slot_of_row[i]}(x[i]) over a shared weight W
+    ([d_out, d_in], an nn.Linear weight on the GPU)."""
+
+    def __init__(self, W, max_slots=64, max_rank=256):
+        if not W.is_cuda or W.dim() != 2:
+            raise ValueError("W must be a 2-D CUDA tensor [d_out, d_in]")
+        self.W = W.contiguous()
+        self.d_out, self.d_in = self.W.shape
+        self.dtype = _TPA_OF_TORCH[self.W.dtype]
+        self.device = self.W.device.index or 0
+        self.handle = B.tpa_layer_create(self.device, self.d_in, self.d_out, self.dtype, self.W.data_ptr(),
+                                         max_slots, max_rank)
+        self._ws = None
+        self._ws_n = 0
+
+    def close(self):
+        if self.handle:
+            B.tpa_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_vera_shared(self, A, Bm):
+        A = np.asarray(A, np.float32)
+        B.tpa_vera_shared_set(self.handle, A.shape[1], A, Bm, _stream())
+
+    def load(self, rec):
+        """Admit an adapter given as a raw-parameter record (method name and
+        numpy arrays in the paper's math layout); returns its slot."""
+        meth = rec["method"]
+        kw = {}
+        if meth in ("lora", "dora"):
+            kw = dict(rank=rec["A"].shape[1], c=rec["c"], A=rec["A"], B=rec["B"], m=rec.get("m"))
+        elif meth == "ia3":
+            kw = dict(l=rec["l"])
+        elif meth == "ssf":
+            kw = dict(s=rec["s"], b=rec["b"])
+        elif meth == "vera":
+            kw = dict(c=rec.get("c", 1.0), d=rec["d"], e=rec["e"])
+        elif meth == "oft":
+            kw = dict(oft_block=rec["Q"].shape[1], Q=rec["Q"])
+        return B.tpa_adapter_load(self.handle, meth, stream=_stream(), **kw)
+
+    def unload(self, slot):
+        B.tpa_adapter_unload(self.handle, slot, _stream())
+
+    def info(self, slot):
+        return B.tpa_adapter_info_get(self.handle, slot)
+
+    def set_option(self, key, value):
+        B.tpa_layer_set_option(self.handle, key, value)
+        self._ws = None
+
+    def workspace(self, n):
+        if self._ws is None or self._ws_n < n:
+            size = B.tpa_workspace_size(self.handle, n)
+            self._ws = torch.empty(max(size, 256), dtype=torch.uint8, device=self.W.device)
+            self._ws_n = n
+        return self._ws
+
+    def forward(self, x, slot_of_row, out=None, ws=None):
+        n = x.shape[0]
+        if out is None:
+            out = torch.empty((n, self.d_out), dtype=self.W.dtype, device=self.W.device)
+        if n == 0:
+            return out
+        ws = self.workspace(n) if ws is None else ws
+        B.tpa_layer_forward(self.handle, x.data_ptr(), slot_of_row.data_ptr(), n, out.data_ptr(), ws.data_ptr(),
+                            ws.numel(), _stream())
+        return out
+
+    def plan(self, slot_of_row):
+        n = slot_of_row.numel()
+        ws = self.workspace(max(n, 1))
+        return B.tpa_plan_debug(self.handle, slot_of_row.data_ptr(), n, ws.data_ptr(), ws.numel(), _stream())
+
+    def error_flag(self, clear=False):
+        return B.tpa_error_flag(self.handle, clear, _stream())

@@ -1,0 +1,75 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and its host-only logic (method metadata, argument validation
+before any device call) behaves as documented."""
+import ctypes
+import json
+import os
+
+import pytest
+
+from tenant_peft_adapter_amd import binding as B
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "table1_members.json")))["methods"]
+
+
+def test_library_exports_every_header_symbol():
+    names = B.header_symbols()
+    assert len(names) >= 15
+    lib = B.library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _decode(info):
+    live = []
+    for bit, name in ((B.LIVE_S, "s"), (B.LIVE_B, "b"), (B.LIVE_R, "R"), (B.LIVE_D, "d"), (B.LIVE_E, "e")):
+        if info["live_mask"] & bit:
+            live.append(name)
+    folds = []
+    for bit, name in ((B.FOLD_C_A, "c->A"), (B.FOLD_E_B, "e->B"), (B.FOLD_C_D, "c->d"), (B.FOLD_D_A, "d->A")):
+        if info["fold_mask"] & bit:
+            folds.append(name)
+    return sorted(folds), sorted(live)
+
+
+@pytest.mark.parametrize("meth", sorted(GOLD))
+def test_method_info_is_table1(meth):
+    info = B.tpa_method_info(meth)
+    folds, live = _decode(info)
+    assert folds == sorted(GOLD[meth]["folds"])
+    assert live == sorted(GOLD[meth]["live"])
+    want_term = {"lora": 1, "dora": 1, "vera": 2}.get(meth, 0)
+    assert info["term_kind"] == want_term
+
+
+def test_method_info_identity_and_unknown():
+    info = B.tpa_method_info("identity")
+    assert info["live_mask"] == 0 and info["fold_mask"] == 0 and info["term_kind"] == 0
+    with pytest.raises(B.TpaError) as e:
+        B.tpa_method_info(99)
+    assert e.value.code == -2
+    assert "unknown method" in B.tpa_last_error()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 100, 128, 1, 1, 8, 16), -1),      # d_in not a multiple of 64
+    ((0, 128, 100, 1, 1, 8, 16), -1),      # d_out not a multiple of 128
+    ((0, 128, 128, 7, 1, 8, 16), -1),      # unknown dtype
+    ((0, 128, 128, 1, None, 8, 16), -1),   # null W
+    ((0, 128, 128, 1, 1, 1, 16), -1),      # max_slots < 2
+    ((0, 128, 128, 1, 1, 8, 0), -1),       # max_rank < 1
+    ((0, 128, 128, 1, 1, 8, 513), -1),     # max_rank > 512
+])
+def test_layer_create_validates_before_touching_a_device(args, code):
+    with pytest.raises(B.TpaError) as e:
+        B.tpa_layer_create(*args)
+    assert e.value.code == code
+
+
+def test_null_layer_calls_fail_cleanly():
+    lib = B.library()
+    assert lib.tpa_layer_forward(None, None, None, 1, None, None, 0, None) == -1
+    assert lib.tpa_adapter_unload(None, 1, None) == -1
+    assert lib.tpa_layer_destroy(None) == 0
+    out = ctypes.c_size_t()
+    assert lib.tpa_workspace_size(None, 4, ctypes.byref(out)) == -1

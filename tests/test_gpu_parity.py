@@ -1,0 +1,110 @@
+"""GPU parity: the HIP path through the C ABI against the CPU float64 oracle,
+element by element, on the seeded workloads.
+
+Tolerance (written here, from the target the layer is held to): for fp16 and
+bf16 layers with fp32 accumulation, the mean over rows of
+‖y_gpu,i − y_ref,i‖ / ‖y_ref,i − x_i W‖ is at most 1%, and the largest
+elementwise error is at most 2e-3 · max|h| with h = (x R_a) W the oracle's
+base output.  fp32 layers are held to 1e-4 and 2e-5.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_util import check, make_layer, reference, run, say
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = dict(mean_tol=1e-4, max_tol=2e-5)
+
+
+@pytest.mark.parametrize("with_identity", [False, True])
+def test_tiny_mixed_fp32(with_identity):
+    wl = synth.tiny_mixed(seed=0, with_identity=with_identity)
+    p = wl["projections"][0]
+    say("tiny_mixed fp32 identity=%s n=%d" % (with_identity, wl["n"]))
+    L = make_layer(p, max_slots=8, max_rank=32)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f32")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="tiny f32", **F32_TOL)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tiny_mixed_half(dtype):
+    wl = synth.tiny_mixed(seed=1, dtype=dtype, with_identity=True)
+    p = wl["projections"][0]
+    say("tiny_mixed", dtype)
+    L = make_layer(p, max_slots=8, max_rank=32)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    # bf16 keeps 8 bits of mantissa: the output rounding alone is 2^-9
+    # relative, so the max bound is scaled by the type's unit roundoff.
+    max_tol = 2e-3 if dtype == "f16" else 1.6e-2
+    check(y_gpu, y, h, xw, max_tol=max_tol, mean_tol=0.01 if dtype == "f16" else 0.05, label="tiny " + dtype)
+
+
+@pytest.mark.parametrize("n", [1, 5, 16, 17, 63, 64, 65, 100, 129, 300])
+def test_ragged_batch_sizes(n):
+    """Sizes that span several tiles with a ragged tail, on both GEMM paths
+    (n <= 64 takes the skinny kernel, larger n the tiled one)."""
+    wl = synth.tiny_mixed(seed=10 + n, n=n, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    say("ragged n=%d" % n)
+    L = make_layer(p, max_slots=8, max_rank=32)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="ragged n=%d" % n)
+
+
+def test_prefill_lora_dora_q_proj():
+    """q_proj 4096 -> 4096, 1024 rows in 16 segments of 64, 8 LoRA + 8 DoRA
+    rank 16: every row checked."""
+    wl = synth.prefill_lora_dora()
+    p = wl["projections"][0]
+    say("prefill_lora_dora n=1024 4096x4096")
+    L = make_layer(p, max_slots=32, max_rank=16)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="prefill q")
+
+
+def test_decoder_layer_mixed_all_projections():
+    """One Llama-3.1-8B decoder layer (7 projections), 64 decode rows over 20
+    tenants of 5 methods, rows shuffled: every row of every projection."""
+    wl = synth.decoder_layer_mixed()
+    for p in wl["projections"]:
+        say("decoder_layer_mixed", p["name"], p["d_in"], p["d_out"])
+        L = make_layer(p, max_slots=32, max_rank=256)
+        y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+        y, h, xw = reference(p, wl["slot_of_row"])
+        check(y_gpu, y, h, xw, label="decoder " + p["name"])
+        L.close()
+
+
+@pytest.mark.parametrize("tenants,d_out", [(1, 4096), (16, 4096), (64, 14336)])
+def test_vera_sweep_and_lora_arm(tenants, d_out):
+    """VeRA tenants through the shared-factor path, and the same tenants as
+    their exact rank-256 LoRA conversion through the segmented path; both
+    against the oracle, and against each other."""
+    wl = synth.vera_sweep(tenants=tenants, d_out=d_out)
+    arm = synth.vera_sweep(tenants=tenants, d_out=d_out, as_lora=True)
+    p, pa = wl["projections"][0], arm["projections"][0]
+    say("vera sweep T=%d d_out=%d" % (tenants, d_out))
+    rows = np.arange(0, 256, 3)
+    y, h, xw = reference(p, wl["slot_of_row"], rows)
+    L = make_layer(p, max_slots=tenants + 2, max_rank=256)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    check(y_gpu[rows], y, h, xw, label="vera shared")
+    L.close()
+    La = make_layer(pa, max_slots=tenants + 2, max_rank=256)
+    ya_gpu = run(La, pa["x"], arm["slot_of_row"], "f16")
+    ya, ha, xwa = reference(pa, arm["slot_of_row"], rows)
+    check(ya_gpu[rows], ya, ha, xwa, label="vera as lora")
+    # The two GPU paths compute the same layer, up to the conversion's
+    # rounding of A diag(d) and B diag(e) to fp16.
+    base = p["x"].astype(np.float64) @ p["W"].astype(np.float64).T
+    m = oracle.parity_metrics(ya_gpu, y_gpu, base, base)
+    say("shared vs arm", m)
+    assert m["mean_rel"] <= 0.02 and m["max_abs"] <= 4e-3 * m["max_h"]

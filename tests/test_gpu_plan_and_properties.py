@@ -1,0 +1,249 @@
+"""GPU tests of the row plan, the merged-slot metadata, and properties the
+layer must have beyond parity: identity rows equal the base-only output bit
+for bit, a row's output does not depend on the rest of the batch, one
+tenant's weights never reach another tenant's rows, invalid slots raise the
+sticky flag and compute as the identity, runs are deterministic, a captured
+HIP graph replays correctly, and the error paths return their codes."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TORCH, check, make_layer, reference, run, say, slot_classes
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "table1_members.json")))["methods"]
+
+
+def _tiny(seed=3, n=64, dtype="f16"):
+    wl = synth.tiny_mixed(seed=seed, n=n, dtype=dtype, with_identity=True)
+    return wl, wl["projections"][0]
+
+
+# ------------------------------------------------------------------ plan ---
+
+@pytest.mark.parametrize("n,tile_rows", [(1, 16), (64, 16), (300, 16), (1000, 64), (4096, 64), (8192, 64)])
+def test_plan_bit_exact_against_oracle(n, tile_rows):
+    wl, p = _tiny()
+    L = make_layer(p, max_slots=8, max_rank=32, options={3: tile_rows})
+    rng = np.random.default_rng(n)
+    sor = rng.integers(-1, 9, size=n).astype(np.int32)     # includes invalid ids
+    say("plan n=%d tile_rows=%d" % (n, tile_rows))
+    got = L.plan(torch.tensor(sor).cuda())
+    cls, has_R = slot_classes(p, 8)
+    want = oracle.plan(sor.tolist(), cls, tile_rows, has_R)
+    for k in ("perm", "row_slot", "seg_ptr", "seg_slot", "class_ptr", "tiles", "oft_tiles", "invalid"):
+        assert got[k] == (list(want[k]) if isinstance(want[k], list) else want[k]), k
+
+
+def test_plan_empty_and_single_class():
+    wl, p = _tiny()
+    L = make_layer(p, max_slots=8, max_rank=32)
+    got = L.plan(torch.zeros(0, dtype=torch.int32).cuda())
+    assert got["perm"] == [] and got["tiles"] == [] and got["invalid"] == 0
+    sor = np.full(40, 4, np.int32)                            # all VeRA
+    got = L.plan(torch.tensor(sor).cuda())
+    cls, has_R = slot_classes(p, 8)
+    want = oracle.plan(sor.tolist(), cls, 16, has_R)
+    assert got["tiles"] == want["tiles"] and got["class_ptr"] == want["class_ptr"]
+
+
+def test_metadata_matches_table1():
+    wl, p = _tiny()
+    L = make_layer(p, max_slots=8, max_rank=32)
+    names = {1: "lora", 2: "dora", 3: "ia3", 4: "vera", 5: "oft"}
+    from tenant_peft_adapter_amd import binding as B
+    for slot, meth in names.items():
+        info = L.info(slot)
+        assert info == {**B.tpa_method_info(meth), "rank": info["rank"], "oft_block": info["oft_block"]}
+        assert info["rank"] == {"lora": 8, "dora": 8, "vera": 32}.get(meth, 0)
+        assert info["oft_block"] == (32 if meth == "oft" else 0)
+    assert L.info(0)["method"] == 0
+
+
+# ------------------------------------------------------------ properties ---
+
+def test_identity_rows_equal_base_only_output_bitwise():
+    wl, p = _tiny(seed=4)
+    sor = wl["slot_of_row"]
+    L = make_layer(p, max_slots=8, max_rank=32)
+    y_mixed = run(L, p["x"], sor, "f16")
+    base = make_layer({**p, "adapters": {}, "shared": None}, max_slots=8, max_rank=32)
+    y_base = run(base, p["x"], np.zeros_like(sor), "f16")
+    ident = sor == 0
+    assert ident.sum() > 0
+    assert np.array_equal(y_mixed[ident], y_base[ident])
+
+
+@pytest.mark.parametrize("n", [20, 64, 200])
+def test_batch_invariance_row_alone_vs_in_batch(n):
+    """With the kernel configuration pinned, a row computed alone equals the
+    same row inside a batch of other tenants, bit for bit."""
+    wl, p = _tiny(seed=5, n=n)
+    opts = {1: 2, 2: 2, 3: 16, 4: 0 if n <= 64 else 1}
+    L = make_layer(p, max_slots=8, max_rank=32, options=opts)
+    sor = wl["slot_of_row"]
+    y_all = run(L, p["x"], sor, "f16")
+    for i in [0, n // 2, n - 1]:
+        y_one = run(L, p["x"][i:i + 1], sor[i:i + 1], "f16")
+        assert np.array_equal(y_one[0], y_all[i]), i
+
+
+def test_isolation_canary_tenant():
+    """A canary adapter with a huge update changes only its own rows."""
+    wl, p = _tiny(seed=6)
+    sor = wl["slot_of_row"].copy()
+    d_in, d_out = p["d_in"], p["d_out"]
+    canary = {"method": "lora", "A": np.ones((d_in, 8), np.float32) * 0.5,
+              "B": np.ones((8, d_out), np.float32) * 0.5, "c": 8.0}
+    with_canary = {**p, "adapters": {**p["adapters"], 6: canary}}
+    without = {**p, "adapters": {**p["adapters"], 6: {"method": "identity"}}}
+    sor[::7] = 6
+    La = make_layer(with_canary, max_slots=8, max_rank=32)
+    Lb = make_layer(without, max_slots=8, max_rank=32)
+    ya = run(La, p["x"], sor, "f16")
+    yb = run(Lb, p["x"], sor, "f16")
+    other = sor != 6
+    assert np.array_equal(ya[other], yb[other])
+    assert np.all(np.abs(ya[~other] - yb[~other]).max(axis=1) > 1.0)
+
+
+def test_invalid_slots_compute_identity_and_flag():
+    wl, p = _tiny(seed=7)
+    sor = wl["slot_of_row"].copy()
+    L = make_layer(p, max_slots=8, max_rank=32)
+    assert L.error_flag(clear=True) == 0
+    y_ok = run(L, p["x"], sor, "f16")
+    assert L.error_flag() == 0
+    bad = sor.copy()
+    bad[3], bad[10], bad[20] = 99, -4, 7          # out of range, negative, not loaded
+    y_bad = run(L, p["x"], bad, "f16")
+    assert L.error_flag(clear=True) == 1
+    assert L.error_flag() == 0
+    base = make_layer({**p, "adapters": {}, "shared": None}, max_slots=8, max_rank=32)
+    y_base = run(base, p["x"], np.zeros_like(sor), "f16")
+    for i in (3, 10, 20):
+        assert np.array_equal(y_bad[i], y_base[i])
+    keep = np.ones(len(sor), bool)
+    keep[[3, 10, 20]] = False
+    assert np.array_equal(y_bad[keep], y_ok[keep])
+
+
+def test_deterministic_runs():
+    wl = synth.decoder_layer_mixed(shapes=(("q", 4096, 4096),))
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=32, max_rank=256)
+    a = run(L, p["x"], wl["slot_of_row"], "f16")
+    b = run(L, p["x"], wl["slot_of_row"], "f16")
+    assert np.array_equal(a, b)
+
+
+def test_graph_capture_replays_match_eager():
+    wl = synth.decoder_layer_mixed(shapes=(("k", 4096, 1024),))
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=32, max_rank=256)
+    x = torch.tensor(p["x"]).half().cuda()
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    out = torch.empty((x.shape[0], p["d_out"]), dtype=torch.float16, device="cuda")
+    ws = L.workspace(x.shape[0])
+    L.forward(x, sor, out=out, ws=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            L.forward(x, sor, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        # eager work between replays
+        L.forward(x, sor)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("route", [1, 2, 3])
+def test_scale_routes_outside_the_expand(route):
+    """The comparison routes (side kernel, gathered scale, index scale) give
+    the same layer as the fused route, within the parity tolerance."""
+    wl = synth.prefill_lora_dora(n=256, tenants=4)
+    p = wl["projections"][0]
+    say("route", route)
+    L = make_layer(p, max_slots=8, max_rank=16, options={5: route})
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    rows = np.arange(0, 256, 5)
+    y, h, xw = reference(p, wl["slot_of_row"], rows)
+    check(y_gpu[rows], y, h, xw, label="route %d" % route)
+
+
+def test_unload_and_reload():
+    wl, p = _tiny(seed=8)
+    L = make_layer(p, max_slots=8, max_rank=32)
+    sor = wl["slot_of_row"]
+    y0 = run(L, p["x"], sor, "f16")
+    L.unload(1)
+    assert L.load(p["adapters"][1]) == 1              # lowest free slot again
+    y1 = run(L, p["x"], sor, "f16")
+    assert np.array_equal(y0, y1)
+    L.error_flag(clear=True)
+
+
+def test_error_codes():
+    from tenant_peft_adapter_amd import binding as B
+    wl, p = _tiny(seed=9)
+    L = make_layer(p, max_slots=7, max_rank=32)       # slots 1..5 used, 6 free
+    d_in, d_out = p["d_in"], p["d_out"]
+
+    def code(fn):
+        with pytest.raises(B.TpaError) as e:
+            fn()
+        return e.value.code
+
+    Q = np.zeros((d_in // 32, 32, 32), np.float32)
+    Q[0, 0, 1] = 0.3                                   # not skew
+    assert code(lambda: L.load({"method": "oft", "Q": Q})) == -5
+    big = {"method": "lora", "A": np.zeros((d_in, 64), np.float32), "B": np.zeros((64, d_out), np.float32), "c": 1.0}
+    assert code(lambda: L.load(big)) == -1              # rank > max_rank
+    nan = {"method": "ia3", "l": np.full(d_out, np.nan, np.float32)}
+    assert code(lambda: L.load(nan)) == -5
+    assert code(lambda: B.tpa_adapter_load(L.handle, 42)) == -2
+    zero_dora = {"method": "dora", "A": np.zeros((d_in, 8), np.float32), "B": np.zeros((8, d_out), np.float32),
+                 "c": 1.0, "m": np.ones(d_out, np.float32)}
+    W0 = torch.zeros((d_out, d_in), dtype=torch.float16, device="cuda")
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    Lz = AdaptedLayer(W0, max_slots=4, max_rank=16)
+    assert code(lambda: Lz.load(zero_dora)) == -5       # zero column norm
+    assert L.load({"method": "identity"}) == 6
+    assert code(lambda: L.load({"method": "identity"})) == -3
+    assert code(lambda: L.unload(6 + 1)) == -4
+    assert code(lambda: L.unload(0)) == -4
+    Lv = make_layer({**p, "adapters": {}, "shared": None}, max_slots=4, max_rank=32)
+    assert code(lambda: Lv.load(p["adapters"][4])) == -1   # VeRA without the shared pair
+    x = torch.zeros((64, d_in), dtype=torch.float16, device="cuda")
+    sor = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = torch.empty((64, d_out), dtype=torch.float16, device="cuda")
+    ws = L.workspace(64)
+    assert code(lambda: B.tpa_layer_forward(L.handle, x.data_ptr(), sor.data_ptr(), 64, out.data_ptr(),
+                                            ws.data_ptr(), 16, 0)) == -6
+    assert code(lambda: B.tpa_layer_forward(L.handle, x.data_ptr(), sor.data_ptr(), 9000, out.data_ptr(),
+                                            ws.data_ptr(), ws.numel(), 0)) == -1
+    L.forward(x[:0], sor[:0])                            # n = 0 is a no-op
+
+
+def test_probes_copy_and_launch():
+    from tenant_peft_adapter_amd import binding as B
+    src = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), src.numel(), torch.cuda.current_stream().cuda_stream)
+    B.tpa_probe_empty(8, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
