@@ -28,6 +28,11 @@ HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 MFMA_F16_PEAK = 2.5e15     # flop/s, dense fp16
 
 
+def log(msg):
+    """Progress line on stderr (the JSON result is the only stdout line)."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -36,7 +41,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pure-lora", action="store_true", help="skip the pure-LoRA comparison batch")
     ap.add_argument("--stage-reps", type=int, default=30)
-    ap.add_argument("--cpu-rows", type=int, default=8, help="rows in the oracle's timed sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
     return ap.parse_args()
 
 
@@ -89,27 +94,37 @@ def time_graph(g, steps, warmup, torch):
 
 
 def stage_times(layers, step, reps, torch):
-    """Per projection and stage durations (µs) from events the library
-    records on its own stream around each kernel, inside a captured graph."""
+    """Per projection and stage durations (µs) from HIP events the library
+    records on the forward's stream around each kernel.  Events recorded
+    while a graph is captured do not time anything, so the step runs
+    eagerly, queued behind ~2 ms of copies: the host has enqueued every
+    launch before the GPU reaches the first event, so each event pair
+    brackets only GPU work."""
     from tenant_peft_adapter_amd import binding as B
     evs = []
     for L in layers:
         e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         for x in e:
-            x.record()
+            x.record()  # torch creates the HIP event on first record
         torch.cuda.synchronize()
         B.tpa_layer_set_stage_events(L.handle, [x.cuda_event for x in e])
         evs.append(e)
-    g = capture(step, torch)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream().cuda_stream
     acc = [[0.0] * 5 for _ in layers]
     for _ in range(reps):
-        g.replay()
+        for _ in range(4):
+            B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
+        step()
         torch.cuda.synchronize()
         for i, e in enumerate(evs):
             for k in range(5):
                 acc[i][k] += e[k].elapsed_time(e[k + 1]) * 1e3
     for L in layers:
         B.tpa_layer_set_stage_events(L.handle, None)
+    del src, dst
     return [[v / reps for v in row] for row in acc]
 
 
@@ -148,9 +163,10 @@ def calibrate(torch):
     return beta, lam
 
 
-def cpu_baseline(wl, rows):
-    """The oracle, untuned, on a bounded sample: `rows` rows of the batch
-    through all seven projections."""
+def cpu_baseline(wl, min_seconds=10.0, chunk=4):
+    """The oracle, untuned, on a bounded sample of the same batch: chunks of
+    `chunk` rows (in batch order) through all seven projections until at
+    least `min_seconds` have passed."""
     import numpy as np
     import oracle
     try:
@@ -158,15 +174,21 @@ def cpu_baseline(wl, rows):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    sel = np.arange(rows)
+    rows = 0
     t0 = time.perf_counter()
-    for p in wl["projections"]:
-        x = p["x"][sel].astype(np.float64)
-        oracle.layer_forward(x, p["W"].astype(np.float64).T, wl["slot_of_row"][sel], p["adapters"], p["shared"])
+    while rows < wl["n"]:
+        sel = np.arange(rows, min(rows + chunk, wl["n"]))
+        for p in wl["projections"]:
+            x = p["x"][sel].astype(np.float64)
+            oracle.layer_forward(x, p["W"].astype(np.float64).T, wl["slot_of_row"][sel], p["adapters"],
+                                 p["shared"])
+        rows += len(sel)
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
     return {"value": rows * len(wl["projections"]) / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of the %d rows through all %d projections (%.1f s)" % (rows, wl["n"],
-                                                                             len(wl["projections"]), dt)}
+            "sample": "first %d of the %d rows, in calls of %d rows, through all %d projections (%.1f s)"
+                      % (rows, wl["n"], chunk, len(wl["projections"]), dt)}
 
 
 def main():
@@ -182,11 +204,15 @@ def main():
     from workloads import synth
 
     torch.cuda.set_device(0)
+    log("generating the mixed decoder-layer workload")
     wl = synth.decoder_layer_mixed()
     n = wl["n"]
+    log("loading 20 tenants into 7 projections")
     layers, step = build_step(wl, torch)
     g = capture(step, torch)
+    log("timing %d graph-replayed steps" % args.steps)
     t_step = time_graph(g, args.steps, args.warmup, torch)
+    log("%.1f us per step" % (t_step * 1e6))
 
     # Eager (no graph) for reference.
     for _ in range(3):
@@ -198,7 +224,9 @@ def main():
     torch.cuda.synchronize()
     t_eager = (time.perf_counter() - t0) / 20
 
+    log("per-stage event timing")
     stages = stage_times(layers, step, args.stage_reps, torch)
+    log("calibration")
     beta, lam = calibrate(torch)
 
     # Byte model per projection.
@@ -222,6 +250,7 @@ def main():
 
     ratio = None
     if not args.no_pure_lora:
+        log("pure-LoRA batch")
         wl_pure = synth.decoder_layer_mixed(pure_lora=True)
         for L in layers:
             L.close()
@@ -272,7 +301,8 @@ def main():
                       for nm, st in zip(names, stages)},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+        log("oracle on the CPU")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

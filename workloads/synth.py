@@ -39,8 +39,11 @@ LLAMA8B_PROJECTIONS = (
 
 
 def round_to(a, dtype):
-    """Round float data to the storage type and return it as float32."""
-    a = np.asarray(a, dtype=np.float64)
+    """Round float data to the storage type (once, to nearest even) and
+    return it as float32."""
+    a = np.asarray(a)
+    if a.dtype not in (np.float32, np.float64):
+        a = a.astype(np.float64)
     if dtype == "f32":
         return a.astype(np.float32)
     if dtype == "f16":
@@ -54,7 +57,10 @@ def round_to(a, dtype):
 
 
 def _normal(rng, shape, std):
-    return rng.standard_normal(shape) * std
+    """float32 draws of N(0, std^2)."""
+    a = rng.standard_normal(shape, dtype=np.float32)
+    a *= np.float32(std)
+    return a
 
 
 def _lora(rng, d_in, d_out, r, dtype, c=2.0):
@@ -63,11 +69,30 @@ def _lora(rng, d_in, d_out, r, dtype, c=2.0):
     return {"method": "lora", "A": A, "B": B, "c": float(c)}
 
 
-def _dora(rng, W, r, dtype, c=2.0):
+class _BaseStats:
+    """float64 copy of a base weight and its squared row norms, formed once
+    per projection for the DoRA magnitude recipe below."""
+
+    def __init__(self, W):
+        self.W64 = W.astype(np.float64)
+        self.sq = np.einsum("ij,ij->i", self.W64, self.W64)
+
+
+def _dora(rng, W, r, dtype, c=2.0, stats=None):
+    """DoRA tenant whose magnitude follows the workload recipe
+    m = ‖Wᵀ + cAB‖_c · (1 + 0.1 z).  The column norm is expanded over the
+    rank-r term, ‖w_j‖² + 2c·w_j·(A b_j) + c²·b_jᵀ(AᵀA)b_j, so the recipe
+    costs one [d_out x d_in] x [d_in x r] product per tenant."""
     d_out, d_in = W.shape
     rec = _lora(rng, d_in, d_out, r, dtype, c)
-    Wp = W.T.astype(np.float64) + c * (rec["A"].astype(np.float64) @ rec["B"].astype(np.float64))
-    col = np.sqrt(np.sum(Wp * Wp, axis=0))
+    st = stats if stats is not None else _BaseStats(W)
+    A = rec["A"].astype(np.float64)
+    B = rec["B"].astype(np.float64)
+    WA = st.W64 @ A                                   # [d_out, r]
+    cross = np.einsum("jk,kj->j", WA, B)
+    G = A.T @ A                                       # [r, r]
+    quad = np.einsum("kj,kl,lj->j", B, G, B)
+    col = np.sqrt(st.sq + 2.0 * c * cross + c * c * quad)
     g = 1.0 + 0.1 * rng.standard_normal(d_out)
     rec["method"] = "dora"
     rec["m"] = (col * g).astype(np.float32)
@@ -135,9 +160,10 @@ def prefill_lora_dora(seed=1000, n=1024, d=4096, r=16, dtype="f16", tenants=16):
     of n / tenants rows; even segments LoRA, odd segments DoRA, rank r."""
     rng = np.random.default_rng(seed)
     p = make_projection(rng, "q", d, d, dtype, n)
+    stats = _BaseStats(p["W"])
     for t in range(tenants):
         p["adapters"][t + 1] = (_lora(rng, d, d, r, dtype) if t % 2 == 0
-                                else _dora(rng, p["W"], r, dtype))
+                                else _dora(rng, p["W"], r, dtype, stats=stats))
     seg = n // tenants
     slot_of_row = (np.arange(n) // seg + 1).astype(np.int32)
     return {"name": "prefill_lora_dora", "dtype": dtype, "n": n,
@@ -163,14 +189,16 @@ def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=25
     projs = []
     for name, d_in, d_out in shapes:
         p = make_projection(rng, name, d_in, d_out, dtype, n)
+        stats = None
         if not pure_lora:
             p["shared"] = _vera_shared(rng, d_in, d_out, r_v, dtype)
+            stats = _BaseStats(p["W"])
         for t, m in enumerate(methods):
             slot = t + 1
             if pure_lora or m == "lora":
                 p["adapters"][slot] = _lora(rng, d_in, d_out, r, dtype)
             elif m == "dora":
-                p["adapters"][slot] = _dora(rng, p["W"], r, dtype)
+                p["adapters"][slot] = _dora(rng, p["W"], r, dtype, stats=stats)
             elif m == "ia3":
                 p["adapters"][slot] = (_ia3(rng, d_out) if name in ("k", "v", "up")
                                        else {"method": "identity"})
