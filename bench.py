@@ -234,9 +234,17 @@ def main():
     shapes = [bm.shape_of(n, p["d_in"], p["d_out"], wl["slot_of_row"], p["adapters"], q=2, r_v=256)
               for p in wl["projections"]]
     kb = [bm.kernel_bytes(s) for s in shapes]
-    # Dominant kernel: the skinny base GEMM with 64-column blocks (q, o, gate,
-    # up, down: the projections with d_out >= 4096).
-    dom = [i for i, p in enumerate(wl["projections"]) if p["d_out"] >= 4096]
+    # Dominant kernel: the base-GEMM instance with the most algorithmic bytes
+    # per step.  Projections share an instance when the library picks the
+    # same path and 64-column blocks per work-group for them.
+    cfgs = [L.config(n) for L in layers]
+    mb = 1 if n <= 16 else 2 if n <= 32 else 4
+    groups = {}
+    for i, c in enumerate(cfgs):
+        key = ("gemm_skinny_kernel<f16,%d,%d,2>" % (mb, c["gemm_nb"]) if c["gemm_path"] == 0
+               else "gemm_tiled_kernel<f16>")
+        groups.setdefault(key, []).append(i)
+    dom_name, dom = max(groups.items(), key=lambda kv: sum(kb[i]["gemm"]["bytes"] for i in kv[1]))
     dom_bytes = sum(kb[i]["gemm"]["bytes"] for i in dom) / len(dom)
     dom_time = sum(stages[i][2] for i in dom) / len(dom) * 1e-6
     gemm_bytes_all = sum(k["gemm"]["bytes"] for k in kb)
@@ -286,7 +294,7 @@ def main():
         "eager_ms_per_step": t_eager * 1e3,
         "mixed_over_pure_lora": ratio,
         "roofline": {
-            "kernel": "gemm_skinny_kernel<f16,4,4> (base GEMM of q, o, gate, up, down)",
+            "kernel": "%s (base GEMM of %s)" % (dom_name, ", ".join(names[i] for i in dom)),
             "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
             "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": None,
             "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
@@ -297,7 +305,8 @@ def main():
                          "GBps": adapter_bytes / adapter_time / 1e9, "launches": adapter_launches,
                          "predicted_step_us": predicted * 1e6},
         "calibration": {"beta_hbm_GBps": beta / 1e9, "lambda_us": lam * 1e6},
-        "stages_us": {nm: dict(zip(("plan", "oft", "gemm", "shrink", "expand"), [round(v, 2) for v in st]))
+        "stages_us": {nm: dict(zip(("plan", "shrink+oft", "gemm+reduce", "pre-expand", "expand"),
+                                   [round(v, 2) for v in st]))
                       for nm, st in zip(names, stages)},
     }
     if not args.no_cpu_baseline:

@@ -219,11 +219,23 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_SCALE_ROUTE 5
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
+/* The kernel configuration a forward of n rows would use (host only, no
+ * device work): plan tile rows, base GEMM path (0 decode kernel with x
+ * staged in LDS, 1 LDS-tiled kernel), its 64-column blocks per work-group
+ * (nb), split-K factor and k range, the shrink's split and k range, and the
+ * scale route.  For tests and measurement. */
+typedef struct {
+  int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route;
+} tpa_config;
+tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
+
 /* Stage timing: when `events` is non-null, each forward records events[0]
- * before its first kernel and events[1..5] after the plan, the OFT rotate,
- * the base GEMM, the shrink and the expand (with any separate scale pass)
- * on its stream.  `events` are hipEvent_t handles owned by the caller;
- * count must be 6 (or 0 with null to stop).  For profiling only. */
+ * before its first kernel and events[1..5] after the plan, the launch of the
+ * shrink with OFT's rotation, the base GEMM (which also carries the shrink's
+ * split reduction on the decode path), any scale pass that runs before the
+ * expand, and the expand (with any scale pass after it), all on its stream.
+ * `events` are hipEvent_t handles owned by the caller; count must be 6 (or 0
+ * with null to stop).  For profiling only. */
 tpa_status tpa_layer_set_stage_events(tpa_layer* layer, void* const* events, int32_t count);
 
 /* Calibration probes (appendix "Constants"): a plain device copy of `bytes`

@@ -49,6 +49,11 @@ class tpa_adapter_info(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in ("method", "live_mask", "fold_mask", "term_kind", "rank", "oft_block")]
 
 
+class tpa_config(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("tile_rows", "gemm_path", "gemm_nb", "gemm_split", "gemm_kc",
+                                              "shrink_split", "shrink_kc", "scale_route")]
+
+
 class tpa_plan_host(ctypes.Structure):
     _fields_ = [(k, ctypes.c_void_p) for k in ("perm", "row_slot", "seg_ptr", "seg_slot", "class_ptr", "tiles",
                                                "oft_tiles", "counts")]
@@ -75,6 +80,7 @@ def _load():
         "tpa_plan_max_tiles": [vp, i32, P(i32), P(i32)],
         "tpa_plan_debug": [vp, vp, i32, vp, sz, P(tpa_plan_host), vp],
         "tpa_layer_set_option": [vp, i32, i32],
+        "tpa_layer_config": [vp, i32, P(tpa_config)],
         "tpa_layer_set_stage_events": [vp, P(vp), i32],
         "tpa_probe_copy": [vp, vp, sz, vp],
         "tpa_probe_empty": [i32, vp],
@@ -208,6 +214,12 @@ def tpa_plan_debug(layer, slot_of_row_ptr, n, ws_ptr, ws_bytes, stream=0):
 
 def tpa_layer_set_option(layer, key, value):
     _check(_lib.tpa_layer_set_option(layer, key, value))
+
+
+def tpa_layer_config(layer, n):
+    out = tpa_config()
+    _check(_lib.tpa_layer_config(layer, n, ctypes.byref(out)))
+    return {k: getattr(out, k) for k, _ in tpa_config._fields_}
 
 
 def tpa_layer_set_stage_events(layer, events):

@@ -159,7 +159,7 @@ struct Config {
 
 struct Layout {
   size_t perm, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
-  size_t x_rot, hpart, vpart, srow;
+  size_t x_rot, hpart, vpart, v, srow;
   size_t total;
   int max_tiles;
 };
@@ -194,12 +194,23 @@ Config choose_config(const tpa_layer* L, int n) {
   c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : (n <= 256 ? 16 : 64);
   c.gemm_path = (n > 64) ? 1 : (L->opt[TPA_OPT_GEMM_PATH] >= 0 ? L->opt[TPA_OPT_GEMM_PATH] : 0);
   if (c.gemm_path == 0) {
-    c.gemm_nb = (L->d_out / 64 >= 64) ? 4 : 1;
-    const int col_tiles = L->d_out / (16 * c.gemm_nb);
-    int split = L->opt[TPA_OPT_GEMM_SPLIT];
-    if (split <= 0) split = std::max(1, std::min(L->d_in / 256, (256 + col_tiles - 1) / col_tiles));
-    split = std::min(split, L->d_in / 32);
-    c.gemm_kc = round_up((L->d_in + split - 1) / split, 32);
+    // 64·nb columns per work-group; the largest k range (1024, 512 or 256)
+    // that still gives ~200 work-groups and whose staged x fits in LDS.
+    c.gemm_nb = (L->d_out >= 8192 && L->d_out % 256 == 0) ? 4 : (L->d_out >= 2048 ? 2 : 1);
+    const int col_tiles = L->d_out / (64 * c.gemm_nb);
+    int kc = 0;
+    const int split_opt = L->opt[TPA_OPT_GEMM_SPLIT];
+    if (split_opt > 0) {
+      kc = round_up((L->d_in + split_opt - 1) / split_opt, 64);
+      while (kc > 64 && tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, kc) > tpa::GEMM_SKINNY_MAX_LDS) kc -= 64;
+    } else {
+      for (int cand : {1024, 512, 256, 128, 64}) {
+        if (tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
+        kc = cand;
+        if ((long)col_tiles * ((L->d_in + cand - 1) / cand) >= 200) break;
+      }
+    }
+    c.gemm_kc = std::min(kc, round_up(L->d_in, 64));
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
   } else {
     c.gemm_nb = 4;
@@ -210,8 +221,9 @@ Config choose_config(const tpa_layer* L, int n) {
     c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
   }
+  // Shrink: one wave per (tile, 16 factor columns, k range of ~256-512).
   int ssplit = L->opt[TPA_OPT_SHRINK_SPLIT];
-  if (ssplit <= 0) ssplit = n <= 1024 ? std::max(1, L->d_in / 512) : std::max(1, L->d_in / 2048);
+  if (ssplit <= 0) ssplit = std::max(1, std::min(28, L->d_in / 256));
   ssplit = std::min(ssplit, L->d_in / 32);
   c.shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
   c.shrink_split = (L->d_in + c.shrink_kc - 1) / c.shrink_kc;
@@ -245,6 +257,7 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   const bool need_hpart = c.gemm_path == 0 || c.gemm_split > 1;
   y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
   y.vpart = take((size_t)c.shrink_split * n * L->kmax * 4);
+  y.v = take((size_t)n * L->kmax * esz);
   y.srow = take(c.scale_route == 3 ? (size_t)n * L->d_out * 4 : 0);
   y.total = off;
   return y;
@@ -679,48 +692,12 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
   TPA_HIP(tpa::launch_plan(p, s));
   if (tpa_status st = stage(L, 1, s)) return st;
 
+  // 2. One launch for the shrink and OFT's rotation (the first block size
+  //    present; any other block size gets a launch of its own).
   const bool any_oft = L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
-  if (any_oft) {
-    tpa::OftArgs o{};
-    o.x = x;
-    o.perm = p.perm;
-    o.oft_tiles = p.oft_tiles;
-    o.counts = p.counts;
-    o.slots = L->slots_dev;
-    o.x_rot = w + y.x_rot;
-    o.d_in = L->d_in;
-    o.max_tiles = y.max_tiles;
-    static const int kBs[3] = {16, 32, 64};
-    for (int i = 0; i < 3; ++i) {
-      if (!L->n_oft_bs[i]) continue;
-      o.block = kBs[i];
-      TPA_HIP(tpa::launch_oft(L->dtype, c.tile_rows, o, s));
-    }
-  }
-
-  if (tpa_status st = stage(L, 2, s)) return st;
-  tpa::BaseGemmArgs g{};
-  g.x = x;
-  g.x_rot = any_oft ? w + y.x_rot : nullptr;
-  g.rot_pos = any_oft ? p.rot_pos : nullptr;
-  g.W = L->W;
-  g.n = n;
-  g.d_in = L->d_in;
-  g.d_out = L->d_out;
-  g.split = c.gemm_split;
-  g.kc = c.gemm_kc;
-  g.part = reinterpret_cast<float*>(w + y.hpart);
-  g.out = out;
-  if (c.gemm_path == 0)
-    TPA_HIP(tpa::launch_gemm_skinny(L->dtype, c.gemm_nb, g, s));
-  else
-    TPA_HIP(tpa::launch_gemm_tiled(L->dtype, g, s));
-  const bool hsplit = c.gemm_path == 0 || c.gemm_split > 1;
-  if (tpa_status st = stage(L, 3, s)) return st;
-
   const bool any_term = L->n_owned > 0 || L->n_vera > 0;
+  tpa::ShrinkArgs sh{};
   if (any_term) {
-    tpa::ShrinkArgs sh{};
     sh.x = x;
     sh.perm = p.perm;
     sh.row_slot = p.row_slot;
@@ -733,14 +710,55 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
     sh.d_in = L->d_in;
     sh.kmax = L->kmax;
     sh.max_tiles = y.max_tiles;
-    sh.nblk = (L->kmax + 63) / 64;
+    sh.nblk = L->kmax / 16;
     sh.split = c.shrink_split;
     sh.kc = c.shrink_kc;
     sh.part = reinterpret_cast<float*>(w + y.vpart);
-    TPA_HIP(tpa::launch_shrink(L->dtype, c.tile_rows, sh, s));
+    sh.v = w + y.v;
   }
+  tpa::OftArgs o{};
+  o.x = x;
+  o.perm = p.perm;
+  o.oft_tiles = p.oft_tiles;
+  o.counts = p.counts;
+  o.slots = L->slots_dev;
+  o.x_rot = w + y.x_rot;
+  o.d_in = L->d_in;
+  o.max_tiles = y.max_tiles;
+  static const int kBs[3] = {16, 32, 64};
+  bool fused_oft = false;
+  for (int i = 0; i < 3; ++i) {
+    if (!L->n_oft_bs[i]) continue;
+    o.block = kBs[i];
+    TPA_HIP(tpa::launch_pre(L->dtype, c.tile_rows, fused_oft || !any_term ? nullptr : &sh, &o, s));
+    fused_oft = true;
+  }
+  if (any_term && !fused_oft) TPA_HIP(tpa::launch_pre(L->dtype, c.tile_rows, &sh, nullptr, s));
+  if (tpa_status st = stage(L, 2, s)) return st;
 
-  if (tpa_status st = stage(L, 4, s)) return st;
+  // 3. Base GEMM; on the decode path the shrink's split reduction rides in
+  //    the same grid.
+  tpa::BaseGemmArgs g{};
+  g.x = x;
+  g.x_rot = any_oft ? w + y.x_rot : nullptr;
+  g.rot_pos = any_oft ? p.rot_pos : nullptr;
+  g.W = L->W;
+  g.n = n;
+  g.d_in = L->d_in;
+  g.d_out = L->d_out;
+  g.split = c.gemm_split;
+  g.kc = c.gemm_kc;
+  g.part = reinterpret_cast<float*>(w + y.hpart);
+  g.out = out;
+  if (c.gemm_path == 0) {
+    TPA_HIP(tpa::launch_gemm_skinny(L->dtype, c.gemm_nb, g, any_term ? &sh : nullptr, s));
+  } else {
+    TPA_HIP(tpa::launch_gemm_tiled(L->dtype, g, s));
+    if (any_term) TPA_HIP(tpa::launch_shrink_reduce(L->dtype, sh, s));
+  }
+  const bool hsplit = c.gemm_path == 0 || c.gemm_split > 1;
+  if (tpa_status st = stage(L, 3, s)) return st;
+
   tpa::ScaleArgs sc{};
   sc.y = out;
   sc.hpart = hsplit ? reinterpret_cast<const float*>(w + y.hpart) : nullptr;
@@ -755,6 +773,7 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
     TPA_HIP(tpa::launch_scale_pass(L->dtype, 1, sc, s));
     h_in_out = true;
   }
+  if (tpa_status st = stage(L, 4, s)) return st;
   tpa::ExpandArgs e{};
   e.out = out;
   e.hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(w + y.hpart);
@@ -766,8 +785,7 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
   e.slots = L->slots_dev;
   e.vera_Bt = L->vera_Bt;
   e.r_v = L->r_v;
-  e.vpart = reinterpret_cast<const float*>(w + y.vpart);
-  e.vsplit = c.shrink_split;
+  e.v = w + y.v;
   e.kmax = L->kmax;
   e.n = n;
   e.d_out = L->d_out;
@@ -849,6 +867,21 @@ tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
       return fail(TPA_ERR_INVALID, "DoRA slots are folded for the current route; unload them first");
   }
   L->opt[key] = value;
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!out || n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "bad argument");
+  const Config c = choose_config(L, std::max(n, 1));
+  out->tile_rows = c.tile_rows;
+  out->gemm_path = c.gemm_path;
+  out->gemm_nb = c.gemm_nb;
+  out->gemm_split = c.gemm_split;
+  out->gemm_kc = c.gemm_kc;
+  out->shrink_split = c.shrink_split;
+  out->shrink_kc = c.shrink_kc;
+  out->scale_route = c.scale_route;
   return TPA_OK;
 }
 

@@ -10,14 +10,14 @@
 //     whatever their tenant, each row multiplied by its tenant's e before it
 //     is added; B_v is read once per tile, not once per tenant.
 //
-// Work-group = one plan tile (up to 16·MB rows in plan order) x 256 output
-// columns; each wave owns 64 columns.  The tile's V (or U) rows are summed
-// over the shrink's split-K partials in a fixed order and staged in LDS in
-// the layer type; the term is an MFMA product with the factor stored
-// [d_out][rank], computed transposed so each lane holds 16 consecutive
-// output columns of one row.  The epilogue reads h (from `out`, or summed
-// from the base GEMM's split partials in a fixed order), applies s and b of
-// the row's slot, adds the term and writes the row segment once.
+// Work-group = one wave = one plan tile (up to 16·MB rows in plan order) x
+// 64 output columns.  The term is an MFMA product of the factor stored
+// [d_out][rank] (a operand: output columns) with the tile's V (or U) rows
+// as the shrink left them ([n][kmax], layer type), computed transposed so
+// each lane holds 16 consecutive output columns of one row.  The epilogue
+// reads h (from `out`, or summed from the base GEMM's split partials in a
+// fixed order), applies s and b of the row's slot, adds the term (times e
+// for shared-term rows) and writes the row segment once.
 #include "internal.h"
 
 namespace tpa {
@@ -25,17 +25,6 @@ namespace tpa {
 namespace {
 
 constexpr int THREADS = 256;
-
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::V lds_frag(const T* p) {
-  return *reinterpret_cast<const typename Frag<T>::V*>(p);
-}
-template <>
-__device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
-  f32x4 lo = *reinterpret_cast<const f32x4*>(p);
-  f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
-  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
 
 template <typename T>
 __device__ __forceinline__ void load_run16(const T* src, float* v) {
@@ -97,20 +86,17 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
 }
 
 template <typename T, int MB, bool HPART>
-__global__ __launch_bounds__(THREADS) void expand_kernel(ExpandArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* vl = reinterpret_cast<T*>(smem);
-  constexpr int TM = 16 * MB;
-  const int LDV = a.kmax + 16 / (int)sizeof(T);
+__global__ __launch_bounds__(64) void expand_kernel(ExpandArgs a) {
+  typedef typename Frag<T>::V Vt;
+  // k steps whose loads are issued together (fewer for wide fragments)
+  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
   const int t = blockIdx.x;
   if (t >= a.counts[CNT_NTILES]) return;
   const int* tile = a.tiles + 4 * t;
   const int p0 = tile[0], p1 = tile[1], kind = tile[2];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int i16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.y * 256 + 64 * wave;
-  const bool wact = n0 < a.d_out;
+  const int n0 = blockIdx.y * 64;
 
   int K = 0;
   const T* Bt = nullptr;
@@ -130,42 +116,43 @@ __global__ __launch_bounds__(THREADS) void expand_kernel(ExpandArgs a) {
     for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (K > 0) {
-    // Stage the tile's V rows: sum of the shrink's split partials.
-    const int rows = p1 - p0;
-    const int k4 = K / 4;
-    const size_t sstride = (size_t)a.n * a.kmax;
-    for (int idx = tid; idx < TM * k4; idx += THREADS) {
-      const int r = idx / k4, c = 4 * (idx % k4);
-      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (r < rows) {
-        const float* src = a.vpart + (size_t)(p0 + r) * a.kmax + c;
-        for (int s = 0; s < a.vsplit; ++s) v += *reinterpret_cast<const f32x4*>(src + s * sstride);
-      }
-      T* dst = vl + r * LDV + c;
+    // term = V[p] · B'ᵀ over this wave's 64 columns: a = B' rows (output
+    // columns), b = V rows of the tile (plan positions).
+    const T* V = static_cast<const T*>(a.v);
+    const T* bp[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(v[q]);
+    for (int b = 0; b < 4; ++b) bp[b] = Bt + (size_t)(n0 + perm_col<4>(i16, b)) * K + 8 * g;
+    const T* vp[MB];
+    bool vv[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int p = p0 + 16 * m + i16;
+      vv[m] = p < p1;
+      vp[m] = V + (size_t)(vv[m] ? p : 0) * a.kmax + 8 * g;
     }
-    __syncthreads();
-    if (wact) {
-      for (int k0 = 0; k0 < K; k0 += 32) {
-        const bool kok = k0 + 8 * g < K;
-        typename Frag<T>::V af[4], bf[MB];
+    for (int k = 0; k < K; k += 32 * U) {
+      Vt af[U][4], bf[U][MB];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = k + 32 * u;
+        const bool ok = kk + 8 * g < K;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) af[u][b] = ok ? load_frag<T>(bp[b] + kk) : zero_frag<T>();
+#pragma unroll
+        for (int m = 0; m < MB; ++m) bf[u][m] = (ok && vv[m]) ? load_frag<T>(vp[m] + kk) : zero_frag<T>();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k + 32 * u >= K) break;
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          af[b] = kok ? load_frag<T>(Bt + (size_t)(n0 + perm_col<4>(i16, b)) * K + k0 + 8 * g)
-                      : zero_frag<T>();
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-          bf[m] = kok ? lds_frag<T>(vl + (16 * m + i16) * LDV + k0 + 8 * g) : zero_frag<T>();
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+          for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[u][b], bf[u][m]);
       }
     }
   }
-  if (!wact) return;
 
+  // Epilogue: lane holds 16 consecutive columns of one row of the tile.
   T* out = static_cast<T*>(a.out);
   const int col = n0 + 16 * g;
 #pragma unroll
@@ -259,12 +246,11 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
 
 template <typename T, int MB>
 hipError_t expand_launch(const ExpandArgs& a, hipStream_t s) {
-  dim3 grid(a.max_tiles, (a.d_out + 255) / 256);
-  const size_t lds = (size_t)(16 * MB) * (a.kmax + 16 / sizeof(T)) * sizeof(T);
+  dim3 grid(a.max_tiles, a.d_out / 64);
   if (a.hpart)
-    hipLaunchKernelGGL((expand_kernel<T, MB, true>), grid, dim3(THREADS), lds, s, a);
+    hipLaunchKernelGGL((expand_kernel<T, MB, true>), grid, dim3(64), 0, s, a);
   else
-    hipLaunchKernelGGL((expand_kernel<T, MB, false>), grid, dim3(THREADS), lds, s, a);
+    hipLaunchKernelGGL((expand_kernel<T, MB, false>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

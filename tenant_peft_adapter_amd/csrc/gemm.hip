@@ -8,148 +8,21 @@
 //
 // Two kernels:
 //   gemm_skinny  -- n <= 64 rows (decode).  The layer is bound by reading W
-//     once from HBM.  Each work-group owns 16·NB output columns and one k
-//     range (split-K); its 4 waves take interleaved 32-wide k steps, so the
-//     group reads whole 128-element runs of each weight row, and operands go
-//     straight from memory into MFMA registers.  The 4 wave partials are
-//     summed in LDS in a fixed order and written as fp32 split partials;
-//     the expand sums the splits in a fixed order, so results do not depend
-//     on scheduling.
+//     once from HBM.  Each work-group owns 64·NB output columns and one k
+//     range (split-K): x for that range sits in LDS, W streams straight
+//     from memory into MFMA registers; partial sums are combined in a fixed
+//     order (k-groups in LDS, splits in the expand), so results do not
+//     depend on scheduling.
 //   gemm_tiled   -- larger n (prefill).  128x128 output tiles, 128-byte k
 //     slices staged through double-buffered LDS, 2x2 waves of 64x64.
-// The shrink uses the skinny structure over the plan's tiles.
 #include "internal.h"
+#include "shrink_impl.h"
 
 namespace tpa {
 
 namespace {
 
 constexpr int THREADS = 256;
-
-// Sum the four waves' accumulators of a skinny work-group into wave 0, in
-// the fixed order (w0 + w2) + (w1 + w3).  red holds 2 x (NB*MB*4) x 64.
-template <int NB, int MB>
-__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NB][MB], float* red, int wave, int lane) {
-  constexpr int E = NB * MB * 4;
-  auto at = [&](int half, int b, int m, int q) -> float& {
-    return red[(half * E + (b * MB + m) * 4 + q) * 64 + lane];
-  };
-  if (wave >= 2) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) at(wave - 2, b, m, q) = acc[b][m][q];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[b][m][q] += at(wave, b, m, q);
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) at(0, b, m, q) = acc[b][m][q];
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int m = 0; m < MB; ++m)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[b][m][q] += at(0, b, m, q);
-  }
-}
-
-// Main loop shared by the skinny GEMM and the shrink: acc[b][m] +=
-// W-rows(b) · X-rows(m) over k in [kbeg, kend), waves interleaved by 32.
-template <typename T, int MB, int NB>
-__device__ __forceinline__ void skinny_loop(f32x4 (&acc)[NB][MB], const T* const* wp, const bool* wv,
-                                            const T* const* xp, const bool* xv, int kbeg, int kend,
-                                            int wave) {
-  typedef typename Frag<T>::V V;
-  constexpr int U = 4;
-  for (int k = kbeg + 32 * wave; k < kend; k += 128 * U) {
-    V wf[U][NB], xf[U][MB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int kk = k + 128 * u;
-      const bool ok = kk < kend;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) wf[u][b] = (ok && wv[b]) ? load_frag<T>(wp[b] + kk) : zero_frag<T>();
-#pragma unroll
-      for (int m = 0; m < MB; ++m) xf[u][m] = (ok && xv[m]) ? load_frag<T>(xp[m] + kk) : zero_frag<T>();
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], wf[u][b], xf[u][m]);
-  }
-}
-
-template <typename T, int MB, int NB>
-__global__ __launch_bounds__(THREADS) void gemm_skinny_kernel(BaseGemmArgs a) {
-  __shared__ float red[2 * NB * MB * 4 * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, g = lane >> 4;
-  const int col0 = blockIdx.x * (16 * NB);
-  const int ks = blockIdx.y;
-  const int kbeg = ks * a.kc;
-  const int kend = min(a.d_in, kbeg + a.kc);
-  const T* X = static_cast<const T*>(a.x);
-  const T* XR = static_cast<const T*>(a.x_rot);
-  const T* W = static_cast<const T*>(a.W);
-
-  const T* xp[MB];
-  bool xv[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int r = 16 * m + i16;
-    xv[m] = r < a.n;
-    const int rp = (xv[m] && a.rot_pos) ? a.rot_pos[r] : -1;
-    const T* base = rp >= 0 ? XR + (size_t)rp * a.d_in : X + (size_t)(xv[m] ? r : 0) * a.d_in;
-    xp[m] = base + 8 * g;
-  }
-  const T* wp[NB];
-  bool wv[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int c = col0 + perm_col<NB>(i16, b);
-    wv[b] = true;
-    wp[b] = W + (size_t)c * a.d_in + 8 * g;
-  }
-  f32x4 acc[NB][MB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  skinny_loop<T, MB, NB>(acc, wp, wv, xp, xv, kbeg, kend, wave);
-  reduce_waves<NB, MB>(acc, red, wave, lane);
-  if (wave != 0) return;
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int row = 16 * m + i16;
-    if (row >= a.n) continue;
-    float* dst = a.part + ((size_t)ks * a.n + row) * a.d_out + col0 + 4 * NB * g;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = acc[b][m];
-  }
-}
-
-// --------------------------------------------------------------- tiled ----
 
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::V lds_frag(const T* p) {
@@ -161,6 +34,158 @@ __device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
   f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+
+// Decode base GEMM (n <= 64 rows).  Work-group = 4·G waves; its tile is
+// BN = 64·NB output columns (wave slice w % 4 owns 16·NB of them) by one k
+// range of kc (split-K).  The work-group's x rows for that range are staged
+// in LDS once (rows >= n zero), so each x byte serves BN columns; k-group
+// w / 4 streams its share of the range of W straight into MFMA registers,
+// U k steps of loads issued together, with x fragments read from LDS.  The
+// k-groups are added in LDS in group order and the sum is the split's fp32
+// partial [split][n][d_out]; the expand adds the splits in split order.
+//
+// The first n_side work-groups of the grid do another job instead: the
+// shrink's split reduction (one thread per 4 columns of one plan position),
+// which the previous launch made ready and which is hidden under the GEMM.
+template <typename T, int MB, int NB, int G>
+__global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(BaseGemmArgs a, ShrinkArgs side, int n_side) {
+  typedef typename Frag<T>::V Vt;
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int U = sizeof(T) == 4 ? 2 : 8 / NB;  // k steps per register stage
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* xs = reinterpret_cast<T*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if ((int)blockIdx.x < n_side) {
+    shrink_impl::shrink_reduce_item<T>(side, (int)blockIdx.x * (256 * G) + tid);
+    return;
+  }
+  const int gid = (int)blockIdx.x - n_side;
+  const int col_tiles = a.d_out / (64 * NB);
+  const int slice = wave & 3, grp = wave >> 2;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int col0 = (gid % col_tiles) * (64 * NB) + slice * (16 * NB);
+  const int ks = gid / col_tiles;
+  const int kbeg = ks * a.kc;
+  const int klen = min(a.d_in - kbeg, a.kc);  // a multiple of 32
+  const int ldx = a.kc + EPC;                 // LDS row stride in elements
+  const T* X = static_cast<const T*>(a.x);
+  const T* XR = static_cast<const T*>(a.x_rot);
+  const T* W = static_cast<const T*>(a.W);
+
+  // 1. Stage the x rows of this k range.
+  const int cpr = klen / EPC;
+  for (int i = tid; i < 16 * MB * cpr; i += 256 * G) {
+    const int r = i / cpr, c = (i % cpr) * EPC;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < a.n) {
+      const int rp = a.rot_pos ? a.rot_pos[r] : -1;
+      const T* src = rp >= 0 ? XR + (size_t)rp * a.d_in : X + (size_t)r * a.d_in;
+      v = *reinterpret_cast<const uint4*>(src + kbeg + c);
+    }
+    *reinterpret_cast<uint4*>(xs + r * ldx + c) = v;
+  }
+  __syncthreads();
+
+  // 2. This k-group's k steps [s_lo, s_hi) of 32.
+  const int steps = klen / 32;
+  const int per = (steps + G - 1) / G;
+  const int s_lo = min(steps, grp * per), s_hi = min(steps, s_lo + per);
+  const T* wp[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) wp[b] = W + (size_t)(col0 + perm_col<NB>(i16, b)) * a.d_in + kbeg + 8 * g;
+  const T* xl = xs + i16 * ldx + 8 * g;
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Two register stages of U k steps: the loads of batch i + 1 are in
+  // flight while batch i is multiplied.  Scheduling barriers keep the
+  // compiler from interleaving (and so serializing) loads and MFMAs.
+  Vt wa[U][NB], wb[U][NB];
+  auto load = [&](Vt(&w)[U][NB], int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) w[u][b] = load_frag<T>(wp[b] + 32 * (s0 + u));
+  };
+  auto comp = [&](Vt(&w)[U][NB], int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      Vt xf[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) xf[m] = lds_frag<T>(xl + 16 * m * ldx + 32 * (s0 + u));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], w[u][b], xf[m]);
+    }
+  };
+  const int nfull = (s_hi - s_lo) / U;
+  int st = s_lo;
+  if (nfull > 0) load(wa, st);
+  int i = 0;
+  for (; i + 2 <= nfull; i += 2) {
+    load(wb, st + U);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wa, st);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < nfull) load(wa, st + 2 * U);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wb, st + U);
+    __builtin_amdgcn_sched_barrier(0);
+    st += 2 * U;
+  }
+  if (i < nfull) {
+    comp(wa, st);
+    st += U;
+  }
+  for (; st < s_hi; ++st) {
+    Vt wf[NB], xf[MB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) wf[b] = load_frag<T>(wp[b] + 32 * st);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) xf[m] = lds_frag<T>(xl + 16 * m * ldx + 32 * st);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], wf[b], xf[m]);
+  }
+
+  // 3. Add the k-groups in group order (group 0 keeps the sum).
+  if (G > 1) {
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    __syncthreads();  // every wave is done with the staged x
+    for (int q = 1; q < G; ++q) {
+      if (grp == q) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) red[((slice * NB + b) * MB + m) * 64 + lane] = acc[b][m];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) acc[b][m] += red[((slice * NB + b) * MB + m) * 64 + lane];
+      }
+      __syncthreads();
+    }
+    if (grp != 0) return;
+  }
+  // Lane holds columns col0 + 4·NB·g + [0, 4·NB) of row 16m + i16.
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int row = 16 * m + i16;
+    if (row >= a.n) continue;
+    float* dst = a.part + ((size_t)ks * a.n + row) * a.d_out + col0 + 4 * NB * g;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = acc[b][m];
+  }
+}
+
+// --------------------------------------------------------------- tiled ----
 
 template <typename T>
 __device__ __forceinline__ void store_run16(T* dst, const float* v);
@@ -286,108 +311,48 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
   }
 }
 
-// -------------------------------------------------------------- shrink ----
-
-template <typename T, int MB>
-__global__ __launch_bounds__(THREADS) void shrink_kernel(ShrinkArgs a) {
-  constexpr int NB = 4;
-  __shared__ float red[2 * NB * MB * 4 * 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, g = lane >> 4;
-  const int t = blockIdx.x / a.nblk;
-  const int nb = blockIdx.x % a.nblk;
-  if (t >= a.counts[CNT_NTILES]) return;
-  const int* tile = a.tiles + 4 * t;
-  const int kind = tile[2];
-  if (kind == CLS_NONE) return;
-  const int p0 = tile[0], p1 = tile[1];
-  const T* Bm;
-  int N;
-  if (kind == CLS_OWNED) {
-    const SlotDev& sd = a.slots[tile[3]];
-    Bm = static_cast<const T*>(sd.A);
-    N = sd.rank;
-  } else {
-    Bm = static_cast<const T*>(a.vera_At);
-    N = a.r_v;
+template <typename T, int G>
+hipError_t skinny_dispatch(int nb, const BaseGemmArgs& a, const ShrinkArgs* side, hipStream_t s) {
+  const int mb = a.n <= 16 ? 1 : a.n <= 32 ? 2 : 4;
+  ShrinkArgs sv{};
+  int n_side = 0;
+  if (side) {
+    sv = *side;
+    n_side = (int)(((long)side->n * (side->kmax / 4) + 256 * G - 1) / (256 * G));
   }
-  const int col0 = nb * 64;
-  if (col0 >= N) return;
-  const int ks = blockIdx.y;
-  const int kbeg = ks * a.kc;
-  const int kend = min(a.d_in, kbeg + a.kc);
-  const T* X = static_cast<const T*>(a.x);
-
-  const T* xp[MB];
-  bool xv[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    xv[m] = p < p1;
-    xp[m] = X + (size_t)(xv[m] ? a.perm[p] : 0) * a.d_in + 8 * g;
+  const dim3 grid((unsigned)(n_side + (a.d_out / (64 * nb)) * a.split));
+  const size_t stage = (size_t)16 * mb * (a.kc + 16 / sizeof(T)) * sizeof(T);
+  const size_t red = G > 1 ? (size_t)4 * nb * mb * 64 * 16 : 0;
+  const size_t lds = stage > red ? stage : red;
+#define TPA_SK(MBV, NBV)                                                                       \
+  if (mb == MBV && nb == NBV) {                                                               \
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, MBV, NBV, G>), grid, dim3(256 * G), lds, s, a, sv, n_side); \
+    return hipGetLastError();                                                                 \
   }
-  const T* wp[NB];
-  bool wv[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int c = col0 + perm_col<NB>(i16, b);
-    wv[b] = c < N;
-    wp[b] = Bm + (size_t)(wv[b] ? c : 0) * a.d_in + 8 * g;
-  }
-  f32x4 acc[NB][MB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  skinny_loop<T, MB, NB>(acc, wp, wv, xp, xv, kbeg, kend, wave);
-  reduce_waves<NB, MB>(acc, red, wave, lane);
-  if (wave != 0) return;
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    if (p >= p1) continue;
-    const float* dv = nullptr;
-    if (kind == CLS_SHARED) dv = a.slots[a.row_slot[a.perm[p]]].d;
-    float* dst = a.part + ((size_t)ks * a.n + p) * a.kmax;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int col = col0 + 4 * NB * g + 4 * b;
-      if (col >= N) continue;
-      f32x4 v = acc[b][m];
-      if (dv) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dv + col);
-        v = v * d4;
-      }
-      *reinterpret_cast<f32x4*>(dst + col) = v;
-    }
-  }
-}
-
-template <typename T>
-hipError_t skinny_dispatch(int nb, const BaseGemmArgs& a, hipStream_t s) {
-  const int mb = (a.n + 15) / 16;
-  dim3 grid(a.d_out / (16 * nb), a.split);
-#define TPA_SK(MBV, NBV)                                                                        \
-  if (mb == MBV && nb == NBV) {                                                                \
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, MBV, NBV>), grid, dim3(THREADS), 0, s, a);        \
-    return hipGetLastError();                                                                  \
-  }
-  TPA_SK(1, 1) TPA_SK(2, 1) TPA_SK(3, 1) TPA_SK(4, 1)
-  TPA_SK(1, 2) TPA_SK(2, 2) TPA_SK(3, 2) TPA_SK(4, 2)
-  TPA_SK(1, 4) TPA_SK(2, 4) TPA_SK(3, 4) TPA_SK(4, 4)
+  TPA_SK(1, 1) TPA_SK(2, 1) TPA_SK(4, 1)
+  TPA_SK(1, 2) TPA_SK(2, 2) TPA_SK(4, 2)
+  TPA_SK(1, 4) TPA_SK(2, 4) TPA_SK(4, 4)
 #undef TPA_SK
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, hipStream_t s) {
-  if (a.n <= 0 || a.n > 64) return hipErrorInvalidValue;
+size_t gemm_skinny_lds(int dtype, int n, int nb, int kc) {
+  const int mb = n <= 16 ? 1 : n <= 32 ? 2 : 4;
+  const size_t esz = dtype == 0 ? 4 : 2;
+  const size_t stage = (size_t)16 * mb * (kc + 16 / esz) * esz;
+  const size_t red = dtype == 0 ? 0 : (size_t)4 * nb * mb * 64 * 16;
+  return stage > red ? stage : red;
+}
+
+hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, const ShrinkArgs* side, hipStream_t s) {
+  if (a.n <= 0 || a.n > 64 || a.kc % 64 || a.d_out % (64 * nb)) return hipErrorInvalidValue;
+  if (gemm_skinny_lds(dtype, a.n, nb, a.kc) > GEMM_SKINNY_MAX_LDS) return hipErrorInvalidValue;
   switch (dtype) {
-    case 0: return skinny_dispatch<float>(nb, a, s);
-    case 1: return skinny_dispatch<f16>(nb, a, s);
-    case 2: return skinny_dispatch<bf16>(nb, a, s);
+    case 0: return skinny_dispatch<float, 1>(nb, a, side, s);
+    case 1: return skinny_dispatch<f16, 2>(nb, a, side, s);
+    case 2: return skinny_dispatch<bf16, 2>(nb, a, side, s);
   }
   return hipErrorInvalidValue;
 }
@@ -400,30 +365,6 @@ hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t s) {
     case 2: hipLaunchKernelGGL(gemm_tiled_kernel<bf16>, grid, dim3(THREADS), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_shrink(int dtype, int tile_rows, const ShrinkArgs& a, hipStream_t s) {
-  dim3 grid(a.max_tiles * a.nblk, a.split);
-#define TPA_SH(TT, MBV) hipLaunchKernelGGL((shrink_kernel<TT, MBV>), grid, dim3(THREADS), 0, s, a)
-  if (tile_rows == 16) {
-    switch (dtype) {
-      case 0: TPA_SH(float, 1); break;
-      case 1: TPA_SH(f16, 1); break;
-      case 2: TPA_SH(bf16, 1); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else if (tile_rows == 64) {
-    switch (dtype) {
-      case 0: TPA_SH(float, 4); break;
-      case 1: TPA_SH(f16, 4); break;
-      case 2: TPA_SH(bf16, 4); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    return hipErrorInvalidValue;
-  }
-#undef TPA_SH
   return hipGetLastError();
 }
 

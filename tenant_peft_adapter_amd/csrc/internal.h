@@ -41,7 +41,6 @@ struct OftArgs {
   int32_t block;           // OFT block size of this launch (16, 32 or 64)
   int32_t max_tiles;
 };
-hipError_t launch_oft(int dtype, int tile_rows, const OftArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMMs ---
 // Base GEMM h = X_sel Wᵀ for all n rows, where row i of X_sel is x[i] or,
@@ -57,14 +56,23 @@ struct BaseGemmArgs {
   float* part;             // [split][n][d_out] fp32 partials (split path)
   void* out;               // [n][d_out] in the layer type (split == 1, tiled)
 };
-// Skinny kernel: n <= 64 rows, weights streamed straight into registers.
-hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, hipStream_t stream);
+struct ShrinkArgs;
+// Skinny kernel: n <= 64 rows; 64·nb output columns per work-group (nb = 1,
+// 2 or 4; d_out % (64·nb) == 0), kc a multiple of 64 whose staged x fits
+// GEMM_SKINNY_MAX_LDS; writes `part`.  With `side`, extra work-groups of the
+// same grid run the shrink's split reduction.
+constexpr size_t GEMM_SKINNY_MAX_LDS = 144 * 1024;
+size_t gemm_skinny_lds(int dtype, int n, int nb, int kc);
+hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, const ShrinkArgs* side,
+                              hipStream_t stream);
 // LDS-tiled 128x128 kernel; writes `out` when split == 1, else `part`.
 hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t stream);
 
 // Shrink over the plan's tiles: owned-term tiles V[p] = x[perm[p]] A'ᵀ,
-// shared-term tiles U[p] = (x[perm[p]] A_vᵀ) ⊙ d'[slot].  Writes fp32
-// partials [split][n][kmax] indexed by plan position p.
+// shared-term tiles U[p] = (x[perm[p]] A_vᵀ) ⊙ d'[slot].  One wave per
+// (tile, 16 factor columns, k range of kc); the split partials go to `part`
+// ([split][n][kmax] fp32) and a second launch adds them in split order into
+// `v` ([n][kmax], layer type) by plan position p.
 struct ShrinkArgs {
   const void* x;
   const int32_t* perm;
@@ -75,13 +83,18 @@ struct ShrinkArgs {
   const void* vera_At;     // [r_v][d_in] or null
   int32_t r_v;
   int32_t n, d_in;
-  int32_t kmax;            // row stride of the partials
+  int32_t kmax;            // row stride of part and v
   int32_t max_tiles;
-  int32_t nblk;            // column blocks of 64 per tile item
-  int32_t split, kc;
+  int32_t nblk;            // 16-column blocks per tile: kmax / 16
+  int32_t split, kc;       // k ranges (kc a multiple of 32)
   float* part;
+  void* v;
 };
-hipError_t launch_shrink(int dtype, int tile_rows, const ShrinkArgs& a, hipStream_t stream);
+// One launch for the shrink's items (sh) and OFT's rotation of its tiles for
+// one block size (of); either may be null.
+hipError_t launch_pre(int dtype, int tile_rows, const ShrinkArgs* sh, const OftArgs* of, hipStream_t stream);
+// The shrink's split reduction on its own (when the GEMM cannot carry it).
+hipError_t launch_shrink_reduce(int dtype, const ShrinkArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- expand --
 // out[row] = h[row] ⊙ s + b + V[p] B'ᵀ (owned tile) or (U[p] B_vᵀ) ⊙ e
@@ -98,8 +111,8 @@ struct ExpandArgs {
   const SlotDev* slots;
   const void* vera_Bt;     // [d_out][r_v]
   int32_t r_v;
-  const float* vpart;      // shrink partials [vsplit][n][kmax]
-  int32_t vsplit, kmax;
+  const void* v;           // shrink output [n][kmax], layer type, by plan position
+  int32_t kmax;
   int32_t n, d_out;
   int32_t max_tiles;
   int32_t apply_scale;     // 0: leave s and b to a separate pass

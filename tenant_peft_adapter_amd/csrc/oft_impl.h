@@ -1,4 +1,4 @@
-// OFT's input transform in a pass of its own (Scute paper, arXiv
+// Device code of OFT's input transform in a pass of its own (Scute paper, arXiv
 // 2611.01089, §4.1 route three, and the appendix "Propositions A2-A4"): each
 // OFT row is multiplied by its tenant's block-diagonal R before the shared
 // GEMM, which then sees the rotated row.  The pass reads and writes
@@ -10,19 +10,18 @@
 // with 4·(b/16) consecutive columns of one row.  R blocks are stored
 // transposed ([c][t] = R[t][c]).  The rotated row p (plan order) is written
 // to x_rot[p].
+#pragma once
+
 #include "internal.h"
 
 namespace tpa {
+namespace oft_impl {
 
-namespace {
-
-constexpr int THREADS = 256;
-constexpr int BLOCKS_PER_WG = 16;
-
+// Work-group part `bg` (16 consecutive blocks, 4 per wave) of OFT tile t.
 template <typename T, int MB, int BS>
-__global__ __launch_bounds__(THREADS) void oft_kernel(OftArgs a) {
+__device__ __forceinline__ void oft_part(const OftArgs& a, int t, int bg, int wave, int lane) {
   constexpr int NB = BS / 16;
-  const int t = blockIdx.x;
+  constexpr int BLOCKS_PER_WG = 16;
   if (t >= a.counts[CNT_NOFT]) return;
   const int* tile = a.oft_tiles + 4 * t;
   const int p0 = tile[0], p1 = tile[1];
@@ -31,7 +30,6 @@ __global__ __launch_bounds__(THREADS) void oft_kernel(OftArgs a) {
   const T* Rt = static_cast<const T*>(sd.Rt);
   const T* X = static_cast<const T*>(a.x);
   T* XR = static_cast<T*>(a.x_rot);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int nblocks = a.d_in / BS;
 
@@ -45,7 +43,7 @@ __global__ __launch_bounds__(THREADS) void oft_kernel(OftArgs a) {
   }
 
   for (int j = 0; j < BLOCKS_PER_WG / 4; ++j) {
-    const int kb = blockIdx.y * BLOCKS_PER_WG + 4 * j + wave;
+    const int kb = bg * BLOCKS_PER_WG + 4 * j + wave;
     if (kb >= nblocks) break;
     f32x4 acc[NB][MB];
 #pragma unroll
@@ -81,35 +79,5 @@ __global__ __launch_bounds__(THREADS) void oft_kernel(OftArgs a) {
   }
 }
 
-template <typename T, int MB>
-hipError_t oft_bs(const OftArgs& a, hipStream_t s) {
-  const int nblocks = a.d_in / a.block;
-  dim3 grid(a.max_tiles, (nblocks + BLOCKS_PER_WG - 1) / BLOCKS_PER_WG);
-  switch (a.block) {
-    case 16: hipLaunchKernelGGL((oft_kernel<T, MB, 16>), grid, dim3(THREADS), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((oft_kernel<T, MB, 32>), grid, dim3(THREADS), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((oft_kernel<T, MB, 64>), grid, dim3(THREADS), 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t oft_tm(int tile_rows, const OftArgs& a, hipStream_t s) {
-  if (tile_rows == 16) return oft_bs<T, 1>(a, s);
-  if (tile_rows == 64) return oft_bs<T, 4>(a, s);
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
-
-hipError_t launch_oft(int dtype, int tile_rows, const OftArgs& a, hipStream_t s) {
-  switch (dtype) {
-    case 0: return oft_tm<float>(tile_rows, a, s);
-    case 1: return oft_tm<f16>(tile_rows, a, s);
-    case 2: return oft_tm<bf16>(tile_rows, a, s);
-  }
-  return hipErrorInvalidValue;
-}
-
+}  // namespace oft_impl
 }  // namespace tpa

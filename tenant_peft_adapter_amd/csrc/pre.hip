@@ -1,0 +1,97 @@
+// The launch that precedes the base GEMM: the shrink (V = x A' for owned-
+// term tiles, U = (x A_v) ⊙ d' for shared-term tiles) and OFT's rotation of
+// its rows (x_rot = x R) in one grid.  Both only read x and the row plan,
+// and neither needs the other, so one launch runs them side by side.
+//
+// Scute paper (arXiv 2611.01089): §2 "The LoRA schedule" (shrink per
+// segment), §4.1 route two (shared-factor term over row tiles) and route
+// three (input transform in a pass of its own before the shared GEMM).
+//
+// Grid: first the shrink's work-groups (4 independent waves each, one item
+// per wave), then OFT's (one OFT tile x 16 blocks per work-group).
+#include "oft_impl.h"
+#include "shrink_impl.h"
+
+namespace tpa {
+
+namespace {
+
+constexpr int THREADS = 256;
+constexpr int OFT_BLOCKS_PER_WG = 16;
+
+template <typename T, int MB, int BS>
+__global__ __launch_bounds__(THREADS) void pre_kernel(ShrinkArgs sh, OftArgs of, int n_shrink_wg, int oft_bg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < n_shrink_wg) {
+    shrink_impl::shrink_item<T, MB>(sh, (int)blockIdx.x * (THREADS / 64) + wave, lane);
+    return;
+  }
+  if (BS != 0) {
+    const int o = (int)blockIdx.x - n_shrink_wg;
+    oft_impl::oft_part<T, MB, (BS == 0 ? 16 : BS)>(of, o / oft_bg, o % oft_bg, wave, lane);
+  }
+}
+
+template <typename T, int MB>
+hipError_t pre_bs(const ShrinkArgs* sh, const OftArgs* of, hipStream_t s) {
+  ShrinkArgs shv{};
+  OftArgs ofv{};
+  int n_shrink_wg = 0, n_oft_wg = 0, oft_bg = 1, bs = 0;
+  if (sh) {
+    shv = *sh;
+    const long items = (long)sh->max_tiles * sh->nblk * sh->split;
+    n_shrink_wg = (int)((items + THREADS / 64 - 1) / (THREADS / 64));
+  }
+  if (of) {
+    ofv = *of;
+    bs = of->block;
+    oft_bg = (of->d_in / bs + OFT_BLOCKS_PER_WG - 1) / OFT_BLOCKS_PER_WG;
+    n_oft_wg = of->max_tiles * oft_bg;
+  }
+  const dim3 grid((unsigned)(n_shrink_wg + n_oft_wg));
+  if (grid.x == 0) return hipSuccess;
+  switch (bs) {
+    case 0: hipLaunchKernelGGL((pre_kernel<T, MB, 0>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
+    case 16: hipLaunchKernelGGL((pre_kernel<T, MB, 16>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
+    case 32: hipLaunchKernelGGL((pre_kernel<T, MB, 32>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
+    case 64: hipLaunchKernelGGL((pre_kernel<T, MB, 64>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t pre_tm(int tile_rows, const ShrinkArgs* sh, const OftArgs* of, hipStream_t s) {
+  if (tile_rows == 16) return pre_bs<T, 1>(sh, of, s);
+  if (tile_rows == 64) return pre_bs<T, 4>(sh, of, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+__global__ __launch_bounds__(THREADS) void shrink_reduce_kernel(ShrinkArgs a) {
+  shrink_impl::shrink_reduce_item<T>(a, (int)(blockIdx.x * THREADS + threadIdx.x));
+}
+
+}  // namespace
+
+hipError_t launch_pre(int dtype, int tile_rows, const ShrinkArgs* sh, const OftArgs* of, hipStream_t s) {
+  switch (dtype) {
+    case 0: return pre_tm<float>(tile_rows, sh, of, s);
+    case 1: return pre_tm<f16>(tile_rows, sh, of, s);
+    case 2: return pre_tm<bf16>(tile_rows, sh, of, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_shrink_reduce(int dtype, const ShrinkArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(((long)a.n * (a.kmax / 4) + THREADS - 1) / THREADS));
+  switch (dtype) {
+    case 0: hipLaunchKernelGGL(shrink_reduce_kernel<float>, grid, dim3(THREADS), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(shrink_reduce_kernel<f16>, grid, dim3(THREADS), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(shrink_reduce_kernel<bf16>, grid, dim3(THREADS), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpa

@@ -1,0 +1,117 @@
+// Device code of the shrink (included by the kernels that run it).
+//
+// Scute paper (arXiv 2611.01089), §2 "The LoRA schedule": the shrink computes
+// V = x A per segment of rows of one adapter; §4.1 route two, first GEMM:
+// for rows whose adapter's term sits on the shared factors (VeRA), U = (x A)
+// ⊙ d over tiles of rows whatever their adapter, so the shared A is read once
+// per tile rather than once per tenant.
+#pragma once
+
+#include "internal.h"
+
+namespace tpa {
+namespace shrink_impl {
+
+// // One wave per work item (plan tile, 16 factor columns, k range): factor
+// rows and the tile's x rows stream straight into MFMA registers (8 k steps
+// of loads issued together), no LDS and no barriers, so the whole GPU takes
+// part even when one tile (VeRA's shared factor) holds most of the work.
+// Each item writes its fp32 partial [split][n][kmax] by plan position; the
+// reduce pass below adds the splits in split order.
+
+template <typename T, int MB>
+__device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int lane) {
+  typedef typename Frag<T>::V Vt;
+  // k steps whose loads are issued together (fp32 fragments are twice as
+  // wide, so fewer fit in registers)
+  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
+  const int i16 = lane & 15, g = lane >> 4;
+  const int ks = item % a.split;
+  const int rest = item / a.split;
+  const int cb = rest % a.nblk;
+  const int t = rest / a.nblk;
+  if (t >= a.max_tiles || t >= a.counts[CNT_NTILES]) return;
+  const int* tile = a.tiles + 4 * t;
+  const int kind = tile[2];
+  if (kind == CLS_NONE) return;
+  const int p0 = tile[0], p1 = tile[1];
+  const T* F;
+  int N;
+  if (kind == CLS_OWNED) {
+    const SlotDev& sd = a.slots[tile[3]];
+    F = static_cast<const T*>(sd.A);
+    N = sd.rank;
+  } else {
+    F = static_cast<const T*>(a.vera_At);
+    N = a.r_v;
+  }
+  const int c0 = 16 * cb;
+  if (c0 >= N) return;
+  const int kbeg = ks * a.kc;
+  const int kend = min(a.d_in, kbeg + a.kc);
+  const T* X = static_cast<const T*>(a.x);
+
+  const T* xp[MB];
+  bool xv[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int p = p0 + 16 * m + i16;
+    xv[m] = p < p1;
+    xp[m] = X + (size_t)(xv[m] ? a.perm[p] : 0) * a.d_in + 8 * g;
+  }
+  const T* fp = F + (size_t)(c0 + i16) * a.d_in + 8 * g;
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = kbeg; k < kend; k += 32 * U) {
+    Vt ff[U], xf[U][MB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + 32 * u;
+      const bool ok = kk < kend;
+      ff[u] = ok ? load_frag<T>(fp + kk) : zero_frag<T>();
+#pragma unroll
+      for (int m = 0; m < MB; ++m) xf[u][m] = (ok && xv[m]) ? load_frag<T>(xp[m] + kk) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k + 32 * u >= kend) break;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) acc[m] = mma(acc[m], ff[u], xf[u][m]);
+    }
+  }
+  // Lane holds V[p0 + 16m + i16][c0 + 4g + v], v = 0..3.
+  const int col = c0 + 4 * g;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int p = p0 + 16 * m + i16;
+    if (p < p1) *reinterpret_cast<f32x4*>(a.part + ((size_t)ks * a.n + p) * a.kmax + col) = acc[m];
+  }
+}
+
+// Reduce pass: V[p][c] = Σ_s part[s][p][c] in split order (times d'[c] for
+// a shared-term row), stored in the layer type; one thread per 4 columns of
+// one plan position, only for columns below the row's rank.
+template <typename T>
+__device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx) {
+  const int q4 = a.kmax / 4;
+  if (idx >= a.n * q4) return;
+  const int p = idx / q4;
+  const int col = 4 * (idx % q4);
+  const SlotDev& sd = a.slots[a.row_slot[a.perm[p]]];
+  const int cls = sd.cls;
+  if (cls != CLS_OWNED && cls != CLS_SHARED) return;
+  const int N = cls == CLS_OWNED ? sd.rank : a.r_v;
+  if (col >= N) return;
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.split; ++s)
+    v += *reinterpret_cast<const f32x4*>(a.part + ((size_t)s * a.n + p) * a.kmax + col);
+  if (cls == CLS_SHARED) v = v * *reinterpret_cast<const f32x4*>(sd.d + col);
+  T* dst = static_cast<T*>(a.v) + (size_t)p * a.kmax + col;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(v[q]);
+}
+
+}  // namespace shrink_impl
+}  // namespace tpa

@@ -74,6 +74,9 @@ class AdaptedLayer:
         B.tpa_layer_set_option(self.handle, key, value)
         self._ws = None
 
+    def config(self, n):
+        return B.tpa_layer_config(self.handle, n)
+
     def workspace(self, n):
         if self._ws is None or self._ws_n < n:
             size = B.tpa_workspace_size(self.handle, n)
