@@ -6,8 +6,11 @@ tenants -- 4 each of LoRA r16, DoRA r16, (IA)3 on k/v/up, VeRA with a shared
 rank-256 pair, OFT with blocks of 32 on q/k/v -- rows shuffled so segments
 are not contiguous.  Inputs are seeded synthetic data of those shapes.
 
-A step is one forward of all seven projections (plan, OFT rotate, base GEMM,
-shrink, expand for each), captured in one HIP graph.  `value` is adapted-
+A step is one forward of all seven projections, captured in one HIP graph:
+the row plan of the batch (built once per group of projections whose slot
+classes agree: q, k, v and o, gate, up, down), then for each projection the
+shrink with OFT's rotation, the base GEMM (carrying the shrink's split
+reduction) and the expand.  `value` is adapted-
 layer rows/s: rows through one adapted projection per second, i.e.
 7 · n / t_step.
 
@@ -62,9 +65,20 @@ def build_step(wl, torch):
         outs.append(torch.empty((n, p["d_out"]), dtype=torch.float16, device="cuda"))
         wss.append(L.workspace(n))
 
+    # Projections whose slot classes agree share one row plan per step (q, k
+    # and v here; o, gate, up and down), built by the first of them.
+    from tenant_peft_adapter_amd.layer import RowPlan
+    groups = {}
+    for i, L in enumerate(layers):
+        groups.setdefault(L.plan_signature(), []).append(i)
+    plans = [(RowPlan(layers[idx[0]], n), idx) for idx in groups.values()]
+
     def step():
-        for L, x, o, w in zip(layers, xs, outs, wss):
-            L.forward(x, sor, out=o, ws=w)
+        for plan, idx in plans:
+            plan.build(layers[idx[0]], sor)
+            for i in idx:
+                layers[i].forward_planned(plan, xs[i], out=outs[i], ws=wss[i])
+    step.plans = plans
     return layers, step
 
 

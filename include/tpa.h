@@ -174,6 +174,35 @@ tpa_status tpa_layer_forward(tpa_layer* layer, const void* x_dev, const int32_t*
                              int32_t n, void* out_dev, void* ws_dev, size_t ws_bytes,
                              tpa_stream stream);
 
+/* Shared row plans.  The plan of a batch (rows grouped by term class and
+ * slot, tiles, OFT tiles; §2 "The LoRA schedule") depends only on
+ * slot_of_row and on each slot's term class and whether it holds an OFT
+ * rotation, so projections whose slot tables agree on those (for example
+ * q, k and v of one decoder layer) can group the batch once:
+ *   tpa_plan_size(layer, n_max, &bytes): device bytes of a plan buffer;
+ *   tpa_plan_build(plan, layer, slot_of_row_dev, n, plan_dev, bytes, s):
+ *     enqueue the plan kernel on s into plan_dev (caller-owned, 256-byte
+ *     aligned, must stay allocated and unmodified while forwards use it) and
+ *     record layer's slot-class signature; raises layer's sticky flag for
+ *     invalid slots;
+ *   tpa_layer_forward_planned(layer, plan, x, out, ws, ws_bytes, s): as
+ *     tpa_layer_forward for the plan's rows, without the plan kernel; -1 if
+ *     layer's slot classes, slot count or tiling differ from the building
+ *     layer's (any load or unload changes them).  ws as for
+ *     tpa_layer_forward.
+ * The tpa_plan handle is host memory (create/destroy); it holds no device
+ * memory. */
+typedef struct tpa_plan tpa_plan;
+/* Layers whose signatures are equal can share a plan of the same rows. */
+tpa_status tpa_layer_plan_signature(const tpa_layer* layer, uint64_t* sig);
+tpa_status tpa_plan_create(tpa_plan** out);
+tpa_status tpa_plan_destroy(tpa_plan* plan);
+tpa_status tpa_plan_size(const tpa_layer* layer, int32_t n_max, size_t* bytes);
+tpa_status tpa_plan_build(tpa_plan* plan, tpa_layer* layer, const int32_t* slot_of_row_dev, int32_t n,
+                          void* plan_dev, size_t plan_bytes, tpa_stream stream);
+tpa_status tpa_layer_forward_planned(tpa_layer* layer, const tpa_plan* plan, const void* x_dev,
+                                     void* out_dev, void* ws_dev, size_t ws_bytes, tpa_stream stream);
+
 /* Read (and optionally clear) the layer's sticky invalid-slot flag.
  * Synchronizes `stream`. */
 tpa_status tpa_error_flag(tpa_layer* layer, int32_t* flag_host, int32_t clear, tpa_stream stream);
@@ -211,12 +240,18 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          "Routes"): 0 inside the expand (route one),
  *                          1 side kernel writing h⊙s before the expand,
  *                          2 gathered scale pass after the expand,
- *                          3 index scale: write s per row, then multiply */
+ *                          3 index scale: write s per row, then multiply
+ *   TPA_OPT_GEMM_NB      : decode GEMM, 64-column blocks per work-group (1,
+ *                          2 or 4)
+ *   TPA_OPT_GEMM_GROUPS  : decode GEMM, k-groups of 4 waves per work-group
+ *                          (1 or 2; fp32 layers always use 1) */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
 #define TPA_OPT_GEMM_PATH 4
 #define TPA_OPT_SCALE_ROUTE 5
+#define TPA_OPT_GEMM_NB 6
+#define TPA_OPT_GEMM_GROUPS 7
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no
@@ -225,7 +260,8 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
  * (nb), split-K factor and k range, the shrink's split and k range, and the
  * scale route.  For tests and measurement. */
 typedef struct {
-  int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route;
+  int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
+      gemm_groups;
 } tpa_config;
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
 

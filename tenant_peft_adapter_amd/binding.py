@@ -27,7 +27,8 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tpa.h")
 TPA_F32, TPA_F16, TPA_BF16 = 0, 1, 2
 DTYPES = {"f32": TPA_F32, "f16": TPA_F16, "bf16": TPA_BF16}
 METHODS = {"identity": 0, "lora": 1, "dora": 2, "ia3": 3, "vera": 4, "oft": 5, "ssf": 6}
-TPA_OPT_GEMM_SPLIT, TPA_OPT_SHRINK_SPLIT, TPA_OPT_TILE_ROWS, TPA_OPT_GEMM_PATH, TPA_OPT_SCALE_ROUTE = 1, 2, 3, 4, 5
+(TPA_OPT_GEMM_SPLIT, TPA_OPT_SHRINK_SPLIT, TPA_OPT_TILE_ROWS, TPA_OPT_GEMM_PATH, TPA_OPT_SCALE_ROUTE,
+ TPA_OPT_GEMM_NB, TPA_OPT_GEMM_GROUPS) = 1, 2, 3, 4, 5, 6, 7
 LIVE_S, LIVE_B, LIVE_R, LIVE_D, LIVE_E = 1, 2, 4, 8, 16
 FOLD_C_A, FOLD_E_B, FOLD_C_D, FOLD_D_A = 1, 2, 4, 8
 STATUS = {0: "OK", -1: "INVALID", -2: "METHOD", -3: "NO_SLOT", -4: "UNKNOWN_SLOT",
@@ -51,7 +52,7 @@ class tpa_adapter_info(ctypes.Structure):
 
 class tpa_config(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in ("tile_rows", "gemm_path", "gemm_nb", "gemm_split", "gemm_kc",
-                                              "shrink_split", "shrink_kc", "scale_route")]
+                                              "shrink_split", "shrink_kc", "scale_route", "gemm_groups")]
 
 
 class tpa_plan_host(ctypes.Structure):
@@ -81,6 +82,12 @@ def _load():
         "tpa_plan_debug": [vp, vp, i32, vp, sz, P(tpa_plan_host), vp],
         "tpa_layer_set_option": [vp, i32, i32],
         "tpa_layer_config": [vp, i32, P(tpa_config)],
+        "tpa_layer_plan_signature": [vp, P(ctypes.c_uint64)],
+        "tpa_plan_create": [P(vp)],
+        "tpa_plan_destroy": [vp],
+        "tpa_plan_size": [vp, i32, P(sz)],
+        "tpa_plan_build": [vp, vp, vp, i32, vp, sz, vp],
+        "tpa_layer_forward_planned": [vp, vp, vp, vp, vp, sz, vp],
         "tpa_layer_set_stage_events": [vp, P(vp), i32],
         "tpa_probe_copy": [vp, vp, sz, vp],
         "tpa_probe_empty": [i32, vp],
@@ -181,6 +188,36 @@ def tpa_workspace_size(layer, n_max):
 
 def tpa_layer_forward(layer, x_ptr, slot_of_row_ptr, n, out_ptr, ws_ptr, ws_bytes, stream=0):
     _check(_lib.tpa_layer_forward(layer, x_ptr, slot_of_row_ptr, n, out_ptr, ws_ptr, ws_bytes, stream))
+
+
+def tpa_layer_plan_signature(layer):
+    out = ctypes.c_uint64()
+    _check(_lib.tpa_layer_plan_signature(layer, ctypes.byref(out)))
+    return out.value
+
+
+def tpa_plan_create():
+    h = ctypes.c_void_p()
+    _check(_lib.tpa_plan_create(ctypes.byref(h)))
+    return h.value
+
+
+def tpa_plan_destroy(plan):
+    _check(_lib.tpa_plan_destroy(plan))
+
+
+def tpa_plan_size(layer, n_max):
+    out = ctypes.c_size_t()
+    _check(_lib.tpa_plan_size(layer, n_max, ctypes.byref(out)))
+    return out.value
+
+
+def tpa_plan_build(plan, layer, slot_of_row_ptr, n, plan_ptr, plan_bytes, stream=0):
+    _check(_lib.tpa_plan_build(plan, layer, slot_of_row_ptr, n, plan_ptr, plan_bytes, stream))
+
+
+def tpa_layer_forward_planned(layer, plan, x_ptr, out_ptr, ws_ptr, ws_bytes, stream=0):
+    _check(_lib.tpa_layer_forward_planned(layer, plan, x_ptr, out_ptr, ws_ptr, ws_bytes, stream))
 
 
 def tpa_error_flag(layer, clear=False, stream=0):

@@ -151,7 +151,7 @@ void cayley_transposed(const float* Q, int b, float* out) {
 struct Config {
   int tile_rows;
   int gemm_path;  // 0 skinny, 1 tiled
-  int gemm_nb;
+  int gemm_nb, gemm_groups;
   int gemm_split, gemm_kc;
   int shrink_split, shrink_kc;
   int scale_route;
@@ -159,6 +159,7 @@ struct Config {
 
 struct Layout {
   size_t perm, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
+  size_t plan_end;  // the plan arrays come first; a shared plan buffer holds [0, plan_end)
   size_t x_rot, hpart, vpart, v, srow;
   size_t total;
   int max_tiles;
@@ -180,9 +181,20 @@ struct tpa_layer {
   int r_v = 0;
   int n_owned = 0, n_vera = 0, n_dora = 0;
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
-  int opt[6] = {-1, -1, -1, -1, -1, 0};
+  int opt[8] = {-1, -1, -1, -1, -1, 0, -1, -1};
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
+  uint64_t plan_sig = 0;  // hash of every slot's (term class, has R): what a row plan depends on
+};
+
+// A row plan built by one layer and shared by the layers whose slot classes
+// match (same signature), so a batch is grouped once for all of them.
+struct tpa_plan {
+  uint64_t sig = 0;
+  int max_slots = 0, n = 0, tile_rows = 0;
+  const char* dev = nullptr;
+  size_t bytes = 0;
+  bool built = false;
 };
 
 namespace {
@@ -197,15 +209,17 @@ Config choose_config(const tpa_layer* L, int n) {
     // 64·nb columns per work-group; the largest k range (1024, 512 or 256)
     // that still gives ~200 work-groups and whose staged x fits in LDS.
     c.gemm_nb = (L->d_out >= 8192 && L->d_out % 256 == 0) ? 4 : (L->d_out >= 2048 ? 2 : 1);
+    if (L->opt[TPA_OPT_GEMM_NB] > 0 && L->d_out % (64 * L->opt[TPA_OPT_GEMM_NB]) == 0) c.gemm_nb = L->opt[TPA_OPT_GEMM_NB];
+    c.gemm_groups = L->dtype == TPA_F32 ? 1 : (L->opt[TPA_OPT_GEMM_GROUPS] > 0 ? L->opt[TPA_OPT_GEMM_GROUPS] : 2);
     const int col_tiles = L->d_out / (64 * c.gemm_nb);
     int kc = 0;
     const int split_opt = L->opt[TPA_OPT_GEMM_SPLIT];
     if (split_opt > 0) {
       kc = round_up((L->d_in + split_opt - 1) / split_opt, 64);
-      while (kc > 64 && tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, kc) > tpa::GEMM_SKINNY_MAX_LDS) kc -= 64;
+      while (kc > 64 && tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, kc) > tpa::GEMM_SKINNY_MAX_LDS) kc -= 64;
     } else {
       for (int cand : {1024, 512, 256, 128, 64}) {
-        if (tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
+        if (tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
         kc = cand;
         if ((long)col_tiles * ((L->d_in + cand - 1) / cand) >= 200) break;
       }
@@ -253,6 +267,7 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.tiles = take(16 * (size_t)y.max_tiles);
   y.oft_tiles = take(16 * (size_t)y.max_tiles);
   y.counts = take(4 * tpa::CNT_WORDS);
+  y.plan_end = off;
   y.x_rot = take((size_t)n * L->d_in * esz);
   const bool need_hpart = c.gemm_path == 0 || c.gemm_split > 1;
   y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
@@ -297,6 +312,21 @@ tpa_status upload_slot(tpa_layer* L, int slot, hipStream_t s) {
   TPA_HIP(hipMemcpyAsync(L->slots_dev + slot, &L->slots_host[slot], sizeof(SlotDev), hipMemcpyHostToDevice, s));
   TPA_HIP(hipStreamSynchronize(s));
   return TPA_OK;
+}
+
+// FNV-1a over every slot's (term class, has R): the plan depends on nothing
+// else of the slot table.
+void update_plan_sig(tpa_layer* L) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](uint64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (v >> (8 * i)) & 0xFF;
+      h *= 1099511628211ull;
+    }
+  };
+  mix((uint64_t)L->max_slots);
+  for (const SlotDev& sd : L->slots_host) mix((uint64_t)(uint32_t)sd.cls | ((uint64_t)sd.has_R << 32));
+  L->plan_sig = h;
 }
 
 // A device float32 staging copy of a host array.
@@ -378,6 +408,7 @@ tpa_status tpa_layer_create(int32_t device, int32_t d_in, int32_t d_out, int32_t
     delete L;
     return fail(TPA_ERR_HIP, "layer allocation: %s", hipGetErrorString(e));
   }
+  update_plan_sig(L);
   *out = L;
   return TPA_OK;
 }
@@ -617,6 +648,7 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
   if (term == 2) ++L->n_vera;
   if (m == TPA_DORA) ++L->n_dora;
   if (m == TPA_OFT) ++L->n_oft_bs[oft_bs_index(d->oft_block)];
+  update_plan_sig(L);
   *slot_out = slot;
   return TPA_OK;
 }
@@ -637,6 +669,7 @@ tpa_status tpa_adapter_unload(tpa_layer* L, int32_t slot, tpa_stream stream) {
   if (info.term_kind == 2) --L->n_vera;
   if (info.method == TPA_DORA) --L->n_dora;
   if (info.method == TPA_OFT) --L->n_oft_bs[oft_bs_index(info.oft_block)];
+  update_plan_sig(L);
   return TPA_OK;
 }
 
@@ -673,25 +706,14 @@ tpa_status tpa_plan_max_tiles(const tpa_layer* L, int32_t n, int32_t* max_tiles,
   return TPA_OK;
 }
 
-tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, int32_t n, void* out, void* ws,
-                             size_t ws_bytes, tpa_stream stream) {
-  if (tpa_status st = check_layer(L)) return st;
-  if (n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "n=%d outside [0, %d]", n, tpa::PLAN_MAX_ROWS);
-  if (n == 0) return TPA_OK;
-  if (!x || !sor || !out || !ws) return fail(TPA_ERR_INVALID, "null pointer");
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TPA_ERR_INVALID, "workspace must be 256-byte aligned");
-  if (x == out) return fail(TPA_ERR_INVALID, "out may not alias x");
-  const Config c = choose_config(L, n);
-  const Layout y = make_layout(L, n, c);
-  if (ws_bytes < y.total) return fail(TPA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
-  DeviceGuard guard(L->device);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  const tpa::PlanArgs p = plan_args(L, sor, n, w, y, c);
-  if (tpa_status st = stage(L, 0, s)) return st;
-  TPA_HIP(tpa::launch_plan(p, s));
-  if (tpa_status st = stage(L, 1, s)) return st;
+}  // extern "C"
 
+namespace {
+
+// Everything after the plan: shrink with OFT's rotation, base GEMM (with the
+// shrink's split reduction), expand (and any separate scale pass).
+tpa_status forward_after_plan(tpa_layer* L, const tpa::PlanArgs& p, const void* x, int n, void* out, char* w,
+                              const Layout& y, const Config& c, hipStream_t s) {
   // 2. One launch for the shrink and OFT's rotation (the first block size
   //    present; any other block size gets a launch of its own).
   const bool any_oft = L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
@@ -751,7 +773,7 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
   g.part = reinterpret_cast<float*>(w + y.hpart);
   g.out = out;
   if (c.gemm_path == 0) {
-    TPA_HIP(tpa::launch_gemm_skinny(L->dtype, c.gemm_nb, g, any_term ? &sh : nullptr, s));
+    TPA_HIP(tpa::launch_gemm_skinny(L->dtype, c.gemm_nb, c.gemm_groups, g, any_term ? &sh : nullptr, s));
   } else {
     TPA_HIP(tpa::launch_gemm_tiled(L->dtype, g, s));
     if (any_term) TPA_HIP(tpa::launch_shrink_reduce(L->dtype, sh, s));
@@ -799,6 +821,110 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
     TPA_HIP(tpa::launch_scale_pass(L->dtype, 4, sc, s));
   }
   return stage(L, 5, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, int32_t n, void* out, void* ws,
+                             size_t ws_bytes, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "n=%d outside [0, %d]", n, tpa::PLAN_MAX_ROWS);
+  if (n == 0) return TPA_OK;
+  if (!x || !sor || !out || !ws) return fail(TPA_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TPA_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (x == out) return fail(TPA_ERR_INVALID, "out may not alias x");
+  const Config c = choose_config(L, n);
+  const Layout y = make_layout(L, n, c);
+  if (ws_bytes < y.total) return fail(TPA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const tpa::PlanArgs p = plan_args(L, sor, n, w, y, c);
+  if (tpa_status st = stage(L, 0, s)) return st;
+  TPA_HIP(tpa::launch_plan(p, s));
+  if (tpa_status st = stage(L, 1, s)) return st;
+  return forward_after_plan(L, p, x, n, out, w, y, c, s);
+}
+
+tpa_status tpa_layer_plan_signature(const tpa_layer* L, uint64_t* sig) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!sig) return fail(TPA_ERR_INVALID, "null output");
+  *sig = L->plan_sig;
+  return TPA_OK;
+}
+
+tpa_status tpa_plan_create(tpa_plan** out) {
+  if (!out) return fail(TPA_ERR_INVALID, "null output");
+  *out = new tpa_plan();
+  return TPA_OK;
+}
+
+tpa_status tpa_plan_destroy(tpa_plan* plan) {
+  delete plan;
+  return TPA_OK;
+}
+
+tpa_status tpa_plan_size(const tpa_layer* L, int32_t n_max, size_t* bytes) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!bytes || n_max < 0 || n_max > tpa::PLAN_MAX_ROWS)
+    return fail(TPA_ERR_INVALID, "n_max must be in [0, %d]", tpa::PLAN_MAX_ROWS);
+  size_t best = 0;
+  for (int n = 1; n <= n_max; ++n) best = std::max(best, make_layout(L, n, choose_config(L, n)).plan_end);
+  *bytes = best;
+  return TPA_OK;
+}
+
+tpa_status tpa_plan_build(tpa_plan* plan, tpa_layer* L, const int32_t* sor, int32_t n, void* plan_dev,
+                          size_t plan_bytes, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!plan) return fail(TPA_ERR_INVALID, "null plan");
+  if (n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "n=%d outside [0, %d]", n, tpa::PLAN_MAX_ROWS);
+  if (n > 0 && (!sor || !plan_dev)) return fail(TPA_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(plan_dev) & 255) return fail(TPA_ERR_INVALID, "plan buffer must be 256-byte aligned");
+  const Config c = choose_config(L, std::max(n, 1));
+  const Layout y = make_layout(L, n, c);
+  if (plan_bytes < y.plan_end) return fail(TPA_ERR_WORKSPACE, "plan buffer %zu < %zu bytes", plan_bytes, y.plan_end);
+  plan->built = false;
+  if (n > 0) {
+    DeviceGuard guard(L->device);
+    const tpa::PlanArgs p = plan_args(L, sor, n, static_cast<char*>(plan_dev), y, c);
+    TPA_HIP(tpa::launch_plan(p, static_cast<hipStream_t>(stream)));
+  }
+  plan->sig = L->plan_sig;
+  plan->max_slots = L->max_slots;
+  plan->n = n;
+  plan->tile_rows = c.tile_rows;
+  plan->dev = static_cast<const char*>(plan_dev);
+  plan->bytes = plan_bytes;
+  plan->built = true;
+  return TPA_OK;
+}
+
+tpa_status tpa_layer_forward_planned(tpa_layer* L, const tpa_plan* plan, const void* x, void* out, void* ws,
+                                     size_t ws_bytes, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!plan || !plan->built) return fail(TPA_ERR_INVALID, "plan is not built");
+  const int n = plan->n;
+  if (n == 0) return TPA_OK;
+  if (!x || !out || !ws) return fail(TPA_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TPA_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (x == out) return fail(TPA_ERR_INVALID, "out may not alias x");
+  const Config c = choose_config(L, n);
+  if (plan->sig != L->plan_sig || plan->max_slots != L->max_slots || plan->tile_rows != c.tile_rows)
+    return fail(TPA_ERR_INVALID, "plan was built for a layer with other slot classes or tiling");
+  const Layout y = make_layout(L, n, c);
+  if (ws_bytes < y.total) return fail(TPA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
+  if (plan->bytes < y.plan_end) return fail(TPA_ERR_WORKSPACE, "plan buffer too small");
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The plan arrays come from the shared buffer (same offsets as a
+  // workspace's head); the rest of the workspace is this forward's.
+  const tpa::PlanArgs p = plan_args(L, nullptr, n, const_cast<char*>(plan->dev), y, c);
+  if (tpa_status st = stage(L, 0, s)) return st;
+  if (tpa_status st = stage(L, 1, s)) return st;
+  return forward_after_plan(L, p, x, n, out, static_cast<char*>(ws), y, c, s);
 }
 
 tpa_status tpa_error_flag(tpa_layer* L, int32_t* flag_host, int32_t clear, tpa_stream stream) {
@@ -855,7 +981,10 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
-  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_SCALE_ROUTE) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_GEMM_GROUPS) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_GEMM_NB && value > 0 && value != 1 && value != 2 && value != 4)
+    return fail(TPA_ERR_INVALID, "gemm nb must be 1, 2 or 4");
+  if (key == TPA_OPT_GEMM_GROUPS && value > 2) return fail(TPA_ERR_INVALID, "gemm groups must be 1 or 2");
   if (key == TPA_OPT_TILE_ROWS && value > 0 && value != 16 && value != 64)
     return fail(TPA_ERR_INVALID, "tile rows must be 16 or 64");
   if (key == TPA_OPT_GEMM_PATH && value > 1) return fail(TPA_ERR_INVALID, "gemm path must be 0 or 1");
@@ -882,6 +1011,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   out->shrink_split = c.shrink_split;
   out->shrink_kc = c.shrink_kc;
   out->scale_route = c.scale_route;
+  out->gemm_groups = c.gemm_groups;
   return TPA_OK;
 }
 

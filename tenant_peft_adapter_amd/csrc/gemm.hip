@@ -338,22 +338,22 @@ hipError_t skinny_dispatch(int nb, const BaseGemmArgs& a, const ShrinkArgs* side
 
 }  // namespace
 
-size_t gemm_skinny_lds(int dtype, int n, int nb, int kc) {
+size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc) {
   const int mb = n <= 16 ? 1 : n <= 32 ? 2 : 4;
   const size_t esz = dtype == 0 ? 4 : 2;
   const size_t stage = (size_t)16 * mb * (kc + 16 / esz) * esz;
-  const size_t red = dtype == 0 ? 0 : (size_t)4 * nb * mb * 64 * 16;
+  const size_t red = groups > 1 ? (size_t)4 * nb * mb * 64 * 16 : 0;
   return stage > red ? stage : red;
 }
 
-hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, const ShrinkArgs* side, hipStream_t s) {
+hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const BaseGemmArgs& a, const ShrinkArgs* side,
+                              hipStream_t s) {
   if (a.n <= 0 || a.n > 64 || a.kc % 64 || a.d_out % (64 * nb)) return hipErrorInvalidValue;
-  if (gemm_skinny_lds(dtype, a.n, nb, a.kc) > GEMM_SKINNY_MAX_LDS) return hipErrorInvalidValue;
-  switch (dtype) {
-    case 0: return skinny_dispatch<float, 1>(nb, a, side, s);
-    case 1: return skinny_dispatch<f16, 2>(nb, a, side, s);
-    case 2: return skinny_dispatch<bf16, 2>(nb, a, side, s);
-  }
+  if (gemm_skinny_lds(dtype, a.n, nb, dtype == 0 ? 1 : groups, a.kc) > GEMM_SKINNY_MAX_LDS)
+    return hipErrorInvalidValue;
+  if (dtype == 0) return skinny_dispatch<float, 1>(nb, a, side, s);
+  if (dtype == 1) return groups == 1 ? skinny_dispatch<f16, 1>(nb, a, side, s) : skinny_dispatch<f16, 2>(nb, a, side, s);
+  if (dtype == 2) return groups == 1 ? skinny_dispatch<bf16, 1>(nb, a, side, s) : skinny_dispatch<bf16, 2>(nb, a, side, s);
   return hipErrorInvalidValue;
 }
 

@@ -60,10 +60,11 @@ struct ShrinkArgs;
 // Skinny kernel: n <= 64 rows; 64·nb output columns per work-group (nb = 1,
 // 2 or 4; d_out % (64·nb) == 0), kc a multiple of 64 whose staged x fits
 // GEMM_SKINNY_MAX_LDS; writes `part`.  With `side`, extra work-groups of the
-// same grid run the shrink's split reduction.
+// same grid run the shrink's split reduction.  groups: k-groups of 4 waves
+// per work-group (1 or 2; fp32 uses 1).
 constexpr size_t GEMM_SKINNY_MAX_LDS = 144 * 1024;
-size_t gemm_skinny_lds(int dtype, int n, int nb, int kc);
-hipError_t launch_gemm_skinny(int dtype, int nb, const BaseGemmArgs& a, const ShrinkArgs* side,
+size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc);
+hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const BaseGemmArgs& a, const ShrinkArgs* side,
                               hipStream_t stream);
 // LDS-tiled 128x128 kernel; writes `out` when split == 1, else `part`.
 hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t stream);

@@ -95,6 +95,23 @@ class AdaptedLayer:
                             ws.numel(), _stream())
         return out
 
+    def plan_signature(self):
+        """Layers with equal signatures can share a RowPlan."""
+        return B.tpa_layer_plan_signature(self.handle)
+
+    def forward_planned(self, plan, x, out=None, ws=None):
+        """Forward of the rows of a RowPlan built by a layer with the same
+        slot classes (the plan kernel is not run again)."""
+        n = plan.n
+        if out is None:
+            out = torch.empty((n, self.d_out), dtype=self.W.dtype, device=self.W.device)
+        if n == 0:
+            return out
+        ws = self.workspace(n) if ws is None else ws
+        B.tpa_layer_forward_planned(self.handle, plan.handle, x.data_ptr(), out.data_ptr(), ws.data_ptr(),
+                                    ws.numel(), _stream())
+        return out
+
     def plan(self, slot_of_row):
         n = slot_of_row.numel()
         ws = self.workspace(max(n, 1))
@@ -102,3 +119,31 @@ class AdaptedLayer:
 
     def error_flag(self, clear=False):
         return B.tpa_error_flag(self.handle, clear, _stream())
+
+
+class RowPlan:
+    """A row plan built once by one layer and reused by every layer with the
+    same slot classes (tpa_plan_build / tpa_layer_forward_planned)."""
+
+    def __init__(self, layer, n_max):
+        self.handle = B.tpa_plan_create()
+        size = B.tpa_plan_size(layer.handle, n_max)
+        self.buf = torch.empty(max(size, 256), dtype=torch.uint8, device=layer.W.device)
+        self.n = 0
+
+    def build(self, layer, slot_of_row):
+        self.n = slot_of_row.numel()
+        B.tpa_plan_build(self.handle, layer.handle, slot_of_row.data_ptr(), self.n, self.buf.data_ptr(),
+                         self.buf.numel(), _stream())
+        return self
+
+    def close(self):
+        if self.handle:
+            B.tpa_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -247,3 +247,36 @@ def test_probes_copy_and_launch():
     B.tpa_probe_empty(8, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_shared_plan_forward_matches_plain_forward():
+    """A row plan built by one projection and reused by another with the same
+    slot classes gives the same output, bit for bit, as each projection's own
+    forward; a projection with other slot classes, or one whose slot table
+    changed after the build, is refused."""
+    from tenant_peft_adapter_amd import binding as B
+    from tenant_peft_adapter_amd.layer import RowPlan
+    wl = synth.decoder_layer_mixed(shapes=(("q", 4096, 4096), ("k", 4096, 1024), ("o", 4096, 4096)))
+    pq, pk, po = wl["projections"]
+    Ls = [make_layer(p, max_slots=32, max_rank=256) for p in (pq, pk, po)]
+    Lq, Lk, Lo = Ls
+    assert Lq.plan_signature() == Lk.plan_signature()      # OFT on both, (IA)3 is a no-term class
+    assert Lq.plan_signature() != Lo.plan_signature()      # OFT tenants are the identity on o
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    n = sor.numel()
+    plan = RowPlan(Lq, n).build(Lq, sor)
+    for L, p in ((Lq, pq), (Lk, pk)):
+        x = torch.tensor(p["x"]).half().cuda()
+        want = L.forward(x, sor).clone()
+        got = L.forward_planned(plan, x)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), p["name"]
+    xo = torch.tensor(po["x"]).half().cuda()
+    with pytest.raises(B.TpaError) as e:
+        Lo.forward_planned(plan, xo)
+    assert e.value.code == -1
+    Lk.unload(1)
+    with pytest.raises(B.TpaError) as e:
+        Lk.forward_planned(plan, torch.tensor(pk["x"]).half().cuda())
+    assert e.value.code == -1
+    plan.close()
