@@ -158,7 +158,7 @@ struct Config {
 };
 
 struct Layout {
-  size_t perm, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
+  size_t perm, pinfo, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
   size_t plan_end;  // the plan arrays come first; a shared plan buffer holds [0, plan_end)
   size_t x_rot, hpart, vpart, v, srow;
   size_t total;
@@ -260,6 +260,7 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
     return at;
   };
   y.perm = take(4 * (size_t)n);
+  y.pinfo = take(4 * (size_t)n);
   y.row_slot = take(4 * (size_t)n);
   y.rot_pos = take(4 * (size_t)n);
   y.seg_ptr = take(4 * (size_t)(n + 1));
@@ -287,6 +288,8 @@ tpa::PlanArgs plan_args(tpa_layer* L, const int32_t* sor, int n, char* ws, const
   p.max_slots = L->max_slots;
   p.tile_rows = c.tile_rows;
   p.perm = reinterpret_cast<int32_t*>(ws + y.perm);
+  p.pinfo = reinterpret_cast<int32_t*>(ws + y.pinfo);
+  p.max_tiles = y.max_tiles;
   p.row_slot = reinterpret_cast<int32_t*>(ws + y.row_slot);
   p.rot_pos = reinterpret_cast<int32_t*>(ws + y.rot_pos);
   p.seg_ptr = reinterpret_cast<int32_t*>(ws + y.seg_ptr);
@@ -721,10 +724,8 @@ tpa_status forward_after_plan(tpa_layer* L, const tpa::PlanArgs& p, const void* 
   tpa::ShrinkArgs sh{};
   if (any_term) {
     sh.x = x;
-    sh.perm = p.perm;
-    sh.row_slot = p.row_slot;
+    sh.pinfo = p.pinfo;
     sh.tiles = p.tiles;
-    sh.counts = p.counts;
     sh.slots = L->slots_dev;
     sh.vera_At = L->vera_At;
     sh.r_v = L->r_v;
@@ -742,7 +743,6 @@ tpa_status forward_after_plan(tpa_layer* L, const tpa::PlanArgs& p, const void* 
   o.x = x;
   o.perm = p.perm;
   o.oft_tiles = p.oft_tiles;
-  o.counts = p.counts;
   o.slots = L->slots_dev;
   o.x_rot = w + y.x_rot;
   o.d_in = L->d_in;
@@ -800,10 +800,8 @@ tpa_status forward_after_plan(tpa_layer* L, const tpa::PlanArgs& p, const void* 
   e.out = out;
   e.hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(w + y.hpart);
   e.hsplit = c.gemm_split;
-  e.perm = p.perm;
-  e.row_slot = p.row_slot;
+  e.pinfo = p.pinfo;
   e.tiles = p.tiles;
-  e.counts = p.counts;
   e.slots = L->slots_dev;
   e.vera_Bt = L->vera_Bt;
   e.r_v = L->r_v;

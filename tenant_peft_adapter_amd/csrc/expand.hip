@@ -66,13 +66,31 @@ __device__ __forceinline__ void store_run16<float>(float* dst, const float* v) {
     *reinterpret_cast<f32x4*>(dst + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
-// h of one row segment of 16 columns: from the split partials (summed in
-// split order) or from the layer-type buffer.
+// h of one row segment of 16 columns: the split partials added in split
+// order, their loads issued 4 splits (16 loads) at a time.
 __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size_t split_stride,
                                             float* v) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = 0.f;
-  for (int s = 0; s < hsplit; ++s) {
+  int s = 0;
+  for (; s + 4 <= hsplit; s += 4) {
+    f32x4 x[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        x[u][q] = *reinterpret_cast<const f32x4*>(hpart + (size_t)(s + u) * split_stride + 4 * q);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[4 * q] += x[u][q][0];
+        v[4 * q + 1] += x[u][q][1];
+        v[4 * q + 2] += x[u][q][2];
+        v[4 * q + 3] += x[u][q][3];
+      }
+  }
+  for (; s < hsplit; ++s) {
     const float* src = hpart + (size_t)s * split_stride;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -90,20 +108,31 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs a) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fewer for wide fragments)
   constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
-  const int t = blockIdx.x;
-  if (t >= a.counts[CNT_NTILES]) return;
-  const int* tile = a.tiles + 4 * t;
-  const int p0 = tile[0], p1 = tile[1], kind = tile[2];
+  const int4 tl = *reinterpret_cast<const int4*>(a.tiles + 4 * blockIdx.x);
+  const int p0 = tl.x, p1 = tl.y, kind = tl.z;
+  if (kind < 0) return;  // padding past the plan's last tile
   const int lane = threadIdx.x;
   const int i16 = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.y * 64;
+  const int col = n0 + 16 * g;
+
+  // Row and slot of each of this lane's positions, and the slot record that
+  // carries s, b and e (a tile of owned-term rows has one slot).
+  int row[MB];
+  const SlotDev* rsd[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int p = p0 + 16 * m + i16;
+    const int pi = p < p1 ? a.pinfo[p] : 0;
+    row[m] = p < p1 ? (pi & 0xFFFF) : -1;
+    rsd[m] = a.slots + (kind == CLS_OWNED ? tl.w : (pi >> 16));
+  }
 
   int K = 0;
   const T* Bt = nullptr;
   if (kind == CLS_OWNED) {
-    const SlotDev& sd = a.slots[tile[3]];
-    K = sd.rank;
-    Bt = static_cast<const T*>(sd.Bt);
+    K = a.slots[tl.w].rank;
+    Bt = static_cast<const T*>(a.slots[tl.w].Bt);
   } else if (kind == CLS_SHARED) {
     K = a.r_v;
     Bt = static_cast<const T*>(a.vera_Bt);
@@ -154,17 +183,14 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandArgs a) {
 
   // Epilogue: lane holds 16 consecutive columns of one row of the tile.
   T* out = static_cast<T*>(a.out);
-  const int col = n0 + 16 * g;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    if (p >= p1) continue;
-    const int row = a.perm[p];
-    const SlotDev& sd = a.slots[a.row_slot[row]];
+    if (row[m] < 0) continue;
+    const SlotDev& sd = *rsd[m];
     float v[16];
-    T* orow = out + (size_t)row * a.d_out + col;
+    T* orow = out + (size_t)row[m] * a.d_out + col;
     if (HPART)
-      sum_parts16(a.hpart + (size_t)row * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
+      sum_parts16(a.hpart + (size_t)row[m] * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
     else
       load_run16<T>(orow, v);
     if (a.apply_scale) {

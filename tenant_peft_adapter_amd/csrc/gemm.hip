@@ -44,23 +44,25 @@ __device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
 // k-groups are added in LDS in group order and the sum is the split's fp32
 // partial [split][n][d_out]; the expand adds the splits in split order.
 //
-// The first n_side work-groups of the grid do another job instead: the
+// Work-groups past the GEMM's own (when `side` is given) do another job: the
 // shrink's split reduction (one thread per 4 columns of one plan position),
-// which the previous launch made ready and which is hidden under the GEMM.
+// which the previous launch made ready; placed after the GEMM's work-groups
+// they take CUs the GEMM leaves free and are hidden under it.
 template <typename T, int MB, int NB, int G>
-__global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(BaseGemmArgs a, ShrinkArgs side, int n_side) {
+__global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(BaseGemmArgs a, ShrinkArgs side) {
   typedef typename Frag<T>::V Vt;
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int U = sizeof(T) == 4 ? 2 : 8 / NB;  // k steps per register stage
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* xs = reinterpret_cast<T*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if ((int)blockIdx.x < n_side) {
-    shrink_impl::shrink_reduce_item<T>(side, (int)blockIdx.x * (256 * G) + tid);
+  const int col_tiles = a.d_out / (64 * NB);
+  const int n_gemm = col_tiles * a.split;
+  if ((int)blockIdx.x >= n_gemm) {
+    shrink_impl::shrink_reduce_item<T>(side, ((int)blockIdx.x - n_gemm) * (256 * G) + tid);
     return;
   }
-  const int gid = (int)blockIdx.x - n_side;
-  const int col_tiles = a.d_out / (64 * NB);
+  const int gid = (int)blockIdx.x;
   const int slice = wave & 3, grp = wave >> 2;
   const int i16 = lane & 15, g = lane >> 4;
   const int col0 = (gid % col_tiles) * (64 * NB) + slice * (16 * NB);
@@ -326,7 +328,7 @@ hipError_t skinny_dispatch(int nb, const BaseGemmArgs& a, const ShrinkArgs* side
   const size_t lds = stage > red ? stage : red;
 #define TPA_SK(MBV, NBV)                                                                       \
   if (mb == MBV && nb == NBV) {                                                               \
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, MBV, NBV, G>), grid, dim3(256 * G), lds, s, a, sv, n_side); \
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, MBV, NBV, G>), grid, dim3(256 * G), lds, s, a, sv); \
     return hipGetLastError();                                                                 \
   }
   TPA_SK(1, 1) TPA_SK(2, 1) TPA_SK(4, 1)

@@ -25,6 +25,8 @@ struct PlanArgs {
   int32_t* oft_tiles;  // [4 * max_tiles]
   int32_t* counts;     // [CNT_WORDS]
   int32_t* flag;       // layer's sticky invalid-slot flag
+  int32_t* pinfo;      // [n]: (slot << 16) | row of plan position p
+  int32_t max_tiles;   // tile lists are padded to this length with kind / slot -1
 };
 constexpr int PLAN_MAX_ROWS = 8192;
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
@@ -33,8 +35,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 struct OftArgs {
   const void* x;           // [n][d_in]
   const int32_t* perm;
-  const int32_t* oft_tiles;
-  const int32_t* counts;
+  const int32_t* oft_tiles;  // padded with slot -1 to max_tiles
   const SlotDev* slots;
   void* x_rot;             // [n][d_in], row p = rotated row perm[p]
   int32_t d_in;
@@ -76,10 +77,8 @@ hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t strea
 // `v` ([n][kmax], layer type) by plan position p.
 struct ShrinkArgs {
   const void* x;
-  const int32_t* perm;
-  const int32_t* row_slot;
-  const int32_t* tiles;
-  const int32_t* counts;
+  const int32_t* pinfo;    // (slot << 16) | row by plan position
+  const int32_t* tiles;    // padded with kind -1 to max_tiles
   const SlotDev* slots;
   const void* vera_At;     // [r_v][d_in] or null
   int32_t r_v;
@@ -105,10 +104,8 @@ struct ExpandArgs {
   void* out;
   const float* hpart;      // null: read h from out
   int32_t hsplit;
-  const int32_t* perm;
-  const int32_t* row_slot;
-  const int32_t* tiles;
-  const int32_t* counts;
+  const int32_t* pinfo;    // (slot << 16) | row by plan position
+  const int32_t* tiles;    // padded with kind -1 to max_tiles
   const SlotDev* slots;
   const void* vera_Bt;     // [d_out][r_v]
   int32_t r_v;

@@ -22,8 +22,8 @@ template <typename T, int MB, int BS>
 __device__ __forceinline__ void oft_part(const OftArgs& a, int t, int bg, int wave, int lane) {
   constexpr int NB = BS / 16;
   constexpr int BLOCKS_PER_WG = 16;
-  if (t >= a.counts[CNT_NOFT]) return;
   const int* tile = a.oft_tiles + 4 * t;
+  if (tile[2] < 0) return;
   const int p0 = tile[0], p1 = tile[1];
   const SlotDev& sd = a.slots[tile[2]];
   if (sd.oft_block != BS) return;

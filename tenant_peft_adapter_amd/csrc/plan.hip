@@ -10,8 +10,10 @@
 //
 // Order: rows sorted by (term class, slot, row), with class 0 = term on
 // owned factors, 1 = shared-factor term, 2 = no term.  Outputs, in the
-// workspace: perm, row_slot, rot_pos (position of a row's rotated copy, or
-// -1), segments, tiles and OFT tiles, counters.
+// workspace: perm, pinfo ((slot << 16) | row per position, so later kernels
+// get both with one load), row_slot, rot_pos (position of a row's rotated
+// copy, or -1), segments, tiles and OFT tiles (padded to max_tiles with
+// kind / slot -1, so later kernels need no counter), counters.
 //
 // One work-group does the whole plan with everything in LDS: the only global
 // reads are slot_of_row and the slot records it points to, the rest are
@@ -142,6 +144,7 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
     const int s = key_slot(k);
     const int cls = key_cls(k);
     a.perm[p] = row;
+    a.pinfo[p] = (s << 16) | row;
     a.rot_pos[row] = key_rot(k) ? p : -1;
     if (p == 0 || key_slot(skeys[p - 1]) != s) {
       seg_start[seg] = (uint16_t)p;
@@ -213,6 +216,21 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
       t[3] = -1;
     }
     nt += cnt;
+  }
+  // Pad both tile lists to max_tiles so later kernels need no counter.
+  for (int q = nt + tid; q < a.max_tiles; q += T) {
+    int* t = a.tiles + 4 * q;
+    t[0] = 0;
+    t[1] = 0;
+    t[2] = -1;
+    t[3] = -1;
+  }
+  for (int q = oft_total + tid; q < a.max_tiles; q += T) {
+    int* t = a.oft_tiles + 4 * q;
+    t[0] = 0;
+    t[1] = 0;
+    t[2] = -1;
+    t[3] = 0;
   }
   if (tid == 0) {
     a.counts[CNT_NSEG] = nseg;

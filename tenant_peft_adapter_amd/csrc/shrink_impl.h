@@ -30,10 +30,10 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
   const int rest = item / a.split;
   const int cb = rest % a.nblk;
   const int t = rest / a.nblk;
-  if (t >= a.max_tiles || t >= a.counts[CNT_NTILES]) return;
+  if (t >= a.max_tiles) return;
   const int* tile = a.tiles + 4 * t;
   const int kind = tile[2];
-  if (kind == CLS_NONE) return;
+  if (kind != CLS_OWNED && kind != CLS_SHARED) return;
   const int p0 = tile[0], p1 = tile[1];
   const T* F;
   int N;
@@ -57,7 +57,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
   for (int m = 0; m < MB; ++m) {
     const int p = p0 + 16 * m + i16;
     xv[m] = p < p1;
-    xp[m] = X + (size_t)(xv[m] ? a.perm[p] : 0) * a.d_in + 8 * g;
+    xp[m] = X + (size_t)(xv[m] ? (a.pinfo[p] & 0xFFFF) : 0) * a.d_in + 8 * g;
   }
   const T* fp = F + (size_t)(c0 + i16) * a.d_in + 8 * g;
 
@@ -99,14 +99,24 @@ __device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx)
   if (idx >= a.n * q4) return;
   const int p = idx / q4;
   const int col = 4 * (idx % q4);
-  const SlotDev& sd = a.slots[a.row_slot[a.perm[p]]];
+  const SlotDev& sd = a.slots[a.pinfo[p] >> 16];
   const int cls = sd.cls;
   if (cls != CLS_OWNED && cls != CLS_SHARED) return;
   const int N = cls == CLS_OWNED ? sd.rank : a.r_v;
   if (col >= N) return;
+  // Splits added in order; their loads go out 8 at a time.
+  const float* src = a.part + (size_t)p * a.kmax + col;
+  const size_t stride = (size_t)a.n * a.kmax;
   f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.split; ++s)
-    v += *reinterpret_cast<const f32x4*>(a.part + ((size_t)s * a.n + p) * a.kmax + col);
+  int s = 0;
+  for (; s + 8 <= a.split; s += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(s + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += t[u];
+  }
+  for (; s < a.split; ++s) v += *reinterpret_cast<const f32x4*>(src + (size_t)s * stride);
   if (cls == CLS_SHARED) v = v * *reinterpret_cast<const f32x4*>(sd.d + col);
   T* dst = static_cast<T*>(a.v) + (size_t)p * a.kmax + col;
 #pragma unroll
