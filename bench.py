@@ -109,19 +109,19 @@ def time_graph(g, steps, warmup, torch):
 
 def stage_times(layers, step, reps, torch):
     """Per projection and stage durations (µs) from HIP events the library
-    records on the forward's stream around each kernel.  Events recorded
-    while a graph is captured do not time anything, so the step runs
-    eagerly, queued behind ~2 ms of copies: the host has enqueued every
-    launch before the GPU reaches the first event, so each event pair
-    brackets only GPU work."""
+    records on the forward's stream around each kernel.  The events are the
+    library's timing events (no system-scope fence on record, so a pair
+    around one kernel measures that kernel).  Events recorded while a graph
+    is captured do not time anything, so the step runs eagerly, queued behind
+    ~7 ms of copies: the host has enqueued every launch before the GPU
+    reaches the first event, so each event pair brackets only GPU work.
+    Stage 3 (between the base GEMM and the expand) holds no kernel on this
+    path: its interval is the cost of an event pair itself."""
     from tenant_peft_adapter_amd import binding as B
     evs = []
     for L in layers:
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        for x in e:
-            x.record()  # torch creates the HIP event on first record
-        torch.cuda.synchronize()
-        B.tpa_layer_set_stage_events(L.handle, [x.cuda_event for x in e])
+        e = [B.tpa_timing_event_create() for _ in range(6)]
+        B.tpa_layer_set_stage_events(L.handle, e)
         evs.append(e)
     nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -129,15 +129,17 @@ def stage_times(layers, step, reps, torch):
     st = torch.cuda.current_stream().cuda_stream
     acc = [[0.0] * 5 for _ in layers]
     for _ in range(reps):
-        for _ in range(4):
+        for _ in range(16):
             B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
         step()
         torch.cuda.synchronize()
         for i, e in enumerate(evs):
             for k in range(5):
-                acc[i][k] += e[k].elapsed_time(e[k + 1]) * 1e3
-    for L in layers:
+                acc[i][k] += B.tpa_timing_event_elapsed(e[k], e[k + 1]) * 1e3
+    for L, e in zip(layers, evs):
         B.tpa_layer_set_stage_events(L.handle, None)
+        for x in e:
+            B.tpa_timing_event_destroy(x)
     del src, dst
     return [[v / reps for v in row] for row in acc]
 
@@ -175,6 +177,33 @@ def calibrate(torch):
     torch.cuda.synchronize()
     lam = (time.perf_counter() - t0) / 20 / 200
     return beta, lam
+
+
+PROFILE = os.path.join(ROOT, "profiles", "gemm_skinny_decoder_layer_mixed.md")
+
+
+def profiled_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
+    summary, or None when the summary covers another kernel or the kernel's
+    sources changed since the counters were taken (sha256 over the files it
+    lists)."""
+    import hashlib
+    import re
+    try:
+        text = open(PROFILE).read()
+    except OSError:
+        return None
+    k = re.search(r"^kernel: (\S+)", text, re.M)
+    sha = re.search(r"^source_sha256: (\w+)", text, re.M)
+    files = re.search(r"^\(sha256 over ([^;]+);", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
+    if not (k and sha and files and val) or k.group(1) != kernel:
+        return None
+    h = hashlib.sha256()
+    for f in files.group(1).split(", "):
+        with open(os.path.join(ROOT, f.strip()), "rb") as fh:
+            h.update(fh.read())
+    return int(val.group(1)) if h.hexdigest()[:16] == sha.group(1) else None
 
 
 def cpu_baseline(wl, min_seconds=10.0, chunk=4):
@@ -260,7 +289,11 @@ def main():
         groups.setdefault(key, []).append(i)
     dom_name, dom = max(groups.items(), key=lambda kv: sum(kb[i]["gemm"]["bytes"] for i in kv[1]))
     dom_bytes = sum(kb[i]["gemm"]["bytes"] for i in dom) / len(dom)
-    dom_time = sum(stages[i][2] for i in dom) / len(dom) * 1e-6
+    # An event pair with no kernel between (stage 3 on this path) measures the
+    # pairs' own cost; it is taken off the dominant kernel's interval.
+    pair_cost = sum(st[3] for st in stages) / len(stages) * 1e-6
+    dom_time_raw = sum(stages[i][2] for i in dom) / len(dom) * 1e-6
+    dom_time = dom_time_raw - pair_cost
     gemm_bytes_all = sum(k["gemm"]["bytes"] for k in kb)
     gemm_time_all = sum(st[2] for st in stages) * 1e-6
     adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes)
@@ -310,8 +343,9 @@ def main():
         "roofline": {
             "kernel": "%s (base GEMM of %s)" % (dom_name, ", ".join(names[i] for i in dom)),
             "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-            "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": None,
+            "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": profiled_traffic(dom_name),
             "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
+            "us_per_launch_raw_events": dom_time_raw * 1e6, "us_event_pair_cost": pair_cost * 1e6,
         },
         "base_gemm": {"bytes_per_step": gemm_bytes_all, "us_per_step": gemm_time_all * 1e6,
                       "GBps": gemm_bytes_all / gemm_time_all / 1e9},

@@ -274,6 +274,15 @@ tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
  * with null to stop).  For profiling only. */
 tpa_status tpa_layer_set_stage_events(tpa_layer* layer, void* const* events, int32_t count);
 
+/* Events for tpa_layer_set_stage_events.  A default HIP event performs a
+ * system-scope fence (cache write-back and invalidate) when it is recorded,
+ * which costs microseconds and lands inside the interval being timed; these
+ * are created without it, so an event pair around one kernel measures that
+ * kernel.  elapsed waits for `end` and returns milliseconds. */
+tpa_status tpa_timing_event_create(void** event);
+tpa_status tpa_timing_event_destroy(void* event);
+tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms);
+
 /* Calibration probes (appendix "Constants"): a plain device copy of `bytes`
  * (a multiple of 16, 16-byte aligned pointers) by a streaming kernel, and
  * `count` chained one-block empty kernels for the launch cost. */

@@ -89,6 +89,9 @@ def _load():
         "tpa_plan_build": [vp, vp, vp, i32, vp, sz, vp],
         "tpa_layer_forward_planned": [vp, vp, vp, vp, vp, sz, vp],
         "tpa_layer_set_stage_events": [vp, P(vp), i32],
+        "tpa_timing_event_create": [P(vp)],
+        "tpa_timing_event_destroy": [vp],
+        "tpa_timing_event_elapsed": [vp, vp, P(ctypes.c_float)],
         "tpa_probe_copy": [vp, vp, sz, vp],
         "tpa_probe_empty": [i32, vp],
     }
@@ -266,6 +269,22 @@ def tpa_layer_set_stage_events(layer, events):
         return
     arr = (ctypes.c_void_p * len(events))(*events)
     _check(_lib.tpa_layer_set_stage_events(layer, arr, len(events)))
+
+
+def tpa_timing_event_create():
+    h = ctypes.c_void_p()
+    _check(_lib.tpa_timing_event_create(ctypes.byref(h)))
+    return h.value
+
+
+def tpa_timing_event_destroy(event):
+    _check(_lib.tpa_timing_event_destroy(event))
+
+
+def tpa_timing_event_elapsed(start, end):
+    ms = ctypes.c_float()
+    _check(_lib.tpa_timing_event_elapsed(start, end, ctypes.byref(ms)))
+    return ms.value
 
 
 def tpa_probe_copy(dst_ptr, src_ptr, nbytes, stream=0):

@@ -1028,6 +1028,26 @@ tpa_status tpa_layer_set_stage_events(tpa_layer* L, void* const* events, int32_t
   return TPA_OK;
 }
 
+tpa_status tpa_timing_event_create(void** event) {
+  if (!event) return fail(TPA_ERR_INVALID, "null output");
+  hipEvent_t e = nullptr;
+  TPA_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
+  *event = e;
+  return TPA_OK;
+}
+
+tpa_status tpa_timing_event_destroy(void* event) {
+  if (event) TPA_HIP(hipEventDestroy(static_cast<hipEvent_t>(event)));
+  return TPA_OK;
+}
+
+tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms) {
+  if (!start || !end || !ms) return fail(TPA_ERR_INVALID, "null argument");
+  TPA_HIP(hipEventSynchronize(static_cast<hipEvent_t>(end)));
+  TPA_HIP(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(end)));
+  return TPA_OK;
+}
+
 tpa_status tpa_probe_copy(void* dst, const void* src, size_t bytes, tpa_stream stream) {
   if (!dst || !src || (bytes & 15) || (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
     return fail(TPA_ERR_INVALID, "copy needs 16-byte aligned pointers and a multiple of 16 bytes");
