@@ -66,20 +66,43 @@ def build_step(wl, torch):
         wss.append(L.workspace(n))
 
     # Projections whose slot classes agree share one row plan per step (q, k
-    # and v here; o, gate, up and down), built by the first of them.
-    from tenant_peft_adapter_amd.layer import RowPlan
-    groups = {}
+    # and v here; o, gate, up and down), built by the first of them.  The
+    # projections of one fused layer -- q, k, v and gate, up, which read the
+    # same input in the model -- run as one group (one launch per kernel);
+    # o and down depend on earlier results in the model and run alone.
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    names = [p["name"] for p in wl["projections"]]
+    fused = [("q", "k", "v"), ("gate", "up")]
+    sig_groups = {}
     for i, L in enumerate(layers):
-        groups.setdefault(L.plan_signature(), []).append(i)
-    plans = [(RowPlan(layers[idx[0]], n), idx) for idx in groups.values()]
+        sig_groups.setdefault(L.plan_signature(), []).append(i)
+    plans = []
+    for idx in sig_groups.values():
+        launch_groups, seen = [], set()
+        for i in idx:
+            if i in seen:
+                continue
+            members = [i]
+            for f in fused:
+                if names[i] in f:
+                    members = [j for j in idx if names[j] in f]
+            seen.update(members)
+            launch_groups.append((members, LayerGroup([layers[j] for j in members], n) if len(members) > 1
+                                  else None))
+        plans.append((RowPlan(layers[idx[0]], n), idx, launch_groups))
 
     def step():
-        for plan, idx in plans:
+        for plan, idx, launch_groups in plans:
             plan.build(layers[idx[0]], sor)
-            for i in idx:
-                layers[i].forward_planned(plan, xs[i], out=outs[i], ws=wss[i])
+            for members, grp in launch_groups:
+                if grp is None:
+                    layers[members[0]].forward_planned(plan, xs[members[0]], out=outs[members[0]],
+                                                       ws=wss[members[0]])
+                else:
+                    grp.forward(plan, [xs[j] for j in members], [outs[j] for j in members])
     step.plans = plans
-    return layers, step
+    units = [members for _, _, lg in plans for members, _ in lg]
+    return layers, step, units
 
 
 def capture(step, torch):
@@ -251,7 +274,7 @@ def main():
     wl = synth.decoder_layer_mixed()
     n = wl["n"]
     log("loading 20 tenants into 7 projections")
-    layers, step = build_step(wl, torch)
+    layers, step, units = build_step(wl, torch)
     g = capture(step, torch)
     log("timing %d graph-replayed steps" % args.steps)
     t_step = time_graph(g, args.steps, args.warmup, torch)
@@ -268,40 +291,39 @@ def main():
     t_eager = (time.perf_counter() - t0) / 20
 
     log("per-stage event timing")
-    stages = stage_times(layers, step, args.stage_reps, torch)
+    stages = stage_times([layers[m[0]] for m in units], step, args.stage_reps, torch)
     log("calibration")
     beta, lam = calibrate(torch)
 
-    # Byte model per projection.
+    # Byte model per projection; measured times per launch unit (a fused
+    # group or a single projection), each kernel one launch per unit.
     names = [p["name"] for p in wl["projections"]]
+    unit_names = ["+".join(names[i] for i in m) for m in units]
     shapes = [bm.shape_of(n, p["d_in"], p["d_out"], wl["slot_of_row"], p["adapters"], q=2, r_v=256)
               for p in wl["projections"]]
     kb = [bm.kernel_bytes(s) for s in shapes]
-    # Dominant kernel: the base-GEMM instance with the most algorithmic bytes
-    # per step.  Projections share an instance when the library picks the
-    # same path and 64-column blocks per work-group for them.
-    cfgs = [L.config(n) for L in layers]
-    mb = 1 if n <= 16 else 2 if n <= 32 else 4
-    groups = {}
-    for i, c in enumerate(cfgs):
-        key = ("gemm_skinny_kernel<f16,%d,%d,2>" % (mb, c["gemm_nb"]) if c["gemm_path"] == 0
-               else "gemm_tiled_kernel<f16>")
-        groups.setdefault(key, []).append(i)
-    dom_name, dom = max(groups.items(), key=lambda kv: sum(kb[i]["gemm"]["bytes"] for i in kv[1]))
-    dom_bytes = sum(kb[i]["gemm"]["bytes"] for i in dom) / len(dom)
     # An event pair with no kernel between (stage 3 on this path) measures the
-    # pairs' own cost; it is taken off the dominant kernel's interval.
+    # pairs' own cost; it is taken off each kernel's interval.
     pair_cost = sum(st[3] for st in stages) / len(stages) * 1e-6
-    dom_time_raw = sum(stages[i][2] for i in dom) / len(dom) * 1e-6
-    dom_time = dom_time_raw - pair_cost
-    gemm_bytes_all = sum(k["gemm"]["bytes"] for k in kb)
-    gemm_time_all = sum(st[2] for st in stages) * 1e-6
+    gemm_t = [max(st[2] * 1e-6 - pair_cost, 1e-9) for st in stages]
+    # Dominant kernel: the base-GEMM launch with the most algorithmic bytes.
+    # A unit's decode GEMM instance takes the column-block width of its
+    # widest projection.
+    mb = 1 if n <= 16 else 2 if n <= 32 else 4
+    gemm_bytes = [sum(kb[i]["gemm"]["bytes"] for i in m) for m in units]
+    du = max(range(len(units)), key=lambda u: gemm_bytes[u])
+    widest = max(units[du], key=lambda i: wl["projections"][i]["d_out"])
+    cfg = layers[widest].config(n)
+    dom_name = ("gemm_skinny_kernel<f16,%d,%d,2>" % (mb, cfg["gemm_nb"]) if cfg["gemm_path"] == 0
+                else "gemm_tiled_kernel<f16>")
+    dom_bytes, dom_time = gemm_bytes[du], gemm_t[du]
+    dom_time_raw = stages[du][2] * 1e-6
+    gemm_bytes_all = sum(gemm_bytes)
+    gemm_time_all = sum(gemm_t)
     adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes)
-    adapter_time = sum(st[0] + st[1] + st[3] + st[4] for st in stages) * 1e-6
-    adapter_launches = sum(k["plan"]["launches"] + k["oft"]["launches"] + k["shrink"]["launches"]
-                           + k["expand"]["launches"] for k in kb)
-    base_only_time = gemm_time_all
-    predicted = bm.predict_time(base_only_time, adapter_bytes, adapter_launches, beta, lam)
+    adapter_time = sum(st[1] + st[4] for st in stages) * 1e-6 - 2 * pair_cost * len(stages)
+    adapter_launches = len(step.plans) + 2 * len(units)
+    predicted = bm.predict_time(gemm_time_all, adapter_bytes, adapter_launches, beta, lam)
 
     ratio = None
     if not args.no_pure_lora:
@@ -311,7 +333,7 @@ def main():
             L.close()
         del g
         torch.cuda.empty_cache()
-        layers_p, step_p = build_step(wl_pure, torch)
+        layers_p, step_p, _ = build_step(wl_pure, torch)
         gp = capture(step_p, torch)
         t_pure = time_graph(gp, args.steps, args.warmup, torch)
         ratio = t_step / t_pure
@@ -341,7 +363,7 @@ def main():
         "eager_ms_per_step": t_eager * 1e3,
         "mixed_over_pure_lora": ratio,
         "roofline": {
-            "kernel": "%s (base GEMM of %s)" % (dom_name, ", ".join(names[i] for i in dom)),
+            "kernel": "%s (base GEMM of %s in one launch)" % (dom_name, ", ".join(names[i] for i in units[du])),
             "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
             "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": profiled_traffic(dom_name),
             "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
@@ -349,13 +371,13 @@ def main():
         },
         "base_gemm": {"bytes_per_step": gemm_bytes_all, "us_per_step": gemm_time_all * 1e6,
                       "GBps": gemm_bytes_all / gemm_time_all / 1e9},
-        "adapter_path": {"bytes_per_step": adapter_bytes, "us_per_step": adapter_time * 1e6,
+        "adapter_path": {"bytes_per_step": adapter_bytes, "us_per_step_shrink_oft_expand": adapter_time * 1e6,
                          "GBps": adapter_bytes / adapter_time / 1e9, "launches": adapter_launches,
                          "predicted_step_us": predicted * 1e6},
         "calibration": {"beta_hbm_GBps": beta / 1e9, "lambda_us": lam * 1e6},
-        "stages_us": {nm: dict(zip(("plan", "shrink+oft", "gemm+reduce", "pre-expand", "expand"),
-                                   [round(v, 2) for v in st]))
-                      for nm, st in zip(names, stages)},
+        "stages_us_raw_events": {nm: dict(zip(("plan", "shrink+oft", "gemm+reduce", "pre-expand", "expand"),
+                                              [round(v, 2) for v in st]))
+                                 for nm, st in zip(unit_names, stages)},
     }
     if not args.no_cpu_baseline:
         log("oracle on the CPU")

@@ -203,6 +203,21 @@ tpa_status tpa_plan_build(tpa_plan* plan, tpa_layer* layer, const int32_t* slot_
 tpa_status tpa_layer_forward_planned(tpa_layer* layer, const tpa_plan* plan, const void* x_dev,
                                      void* out_dev, void* ws_dev, size_t ws_bytes, tpa_stream stream);
 
+/* Projections of one fused layer (q, k and v; gate and up) forwarded in one
+ * launch per kernel (P1 §5.2: one launch covers all slices of a layer), with
+ * a plan built for their common slot classes.  count <= 4; layers[i] with
+ * x[i] [n][d_in_i], out[i] [n][d_out_i], ws[i] of ws_bytes[i] bytes (at least
+ * tpa_group_workspace_size's bytes[i] for this group; 256-byte aligned).  All
+ * layers must have the plan's signature, one dtype and one device.  On the
+ * decode path (n <= 64) the group shares one base-GEMM configuration (column
+ * blocks per work-group and k range), so results may differ from separate
+ * forwards by the rounding of a different split-K order.  Stage events are
+ * those of layers[0]. */
+tpa_status tpa_group_workspace_size(tpa_layer* const* layers, int32_t count, int32_t n_max, size_t* bytes);
+tpa_status tpa_group_forward_planned(tpa_layer* const* layers, int32_t count, const tpa_plan* plan,
+                                     const void* const* x_dev, void* const* out_dev, void* const* ws_dev,
+                                     const size_t* ws_bytes, tpa_stream stream);
+
 /* Read (and optionally clear) the layer's sticky invalid-slot flag.
  * Synchronizes `stream`. */
 tpa_status tpa_error_flag(tpa_layer* layer, int32_t* flag_host, int32_t clear, tpa_stream stream);

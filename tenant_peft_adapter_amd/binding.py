@@ -88,6 +88,8 @@ def _load():
         "tpa_plan_size": [vp, i32, P(sz)],
         "tpa_plan_build": [vp, vp, vp, i32, vp, sz, vp],
         "tpa_layer_forward_planned": [vp, vp, vp, vp, vp, sz, vp],
+        "tpa_group_workspace_size": [P(vp), i32, i32, P(sz)],
+        "tpa_group_forward_planned": [P(vp), i32, vp, P(vp), P(vp), P(vp), P(sz), vp],
         "tpa_layer_set_stage_events": [vp, P(vp), i32],
         "tpa_timing_event_create": [P(vp)],
         "tpa_timing_event_destroy": [vp],
@@ -221,6 +223,21 @@ def tpa_plan_build(plan, layer, slot_of_row_ptr, n, plan_ptr, plan_bytes, stream
 
 def tpa_layer_forward_planned(layer, plan, x_ptr, out_ptr, ws_ptr, ws_bytes, stream=0):
     _check(_lib.tpa_layer_forward_planned(layer, plan, x_ptr, out_ptr, ws_ptr, ws_bytes, stream))
+
+
+def tpa_group_workspace_size(layers, n_max):
+    k = len(layers)
+    arr = (ctypes.c_void_p * k)(*layers)
+    out = (ctypes.c_size_t * k)()
+    _check(_lib.tpa_group_workspace_size(arr, k, n_max, out))
+    return list(out)
+
+
+def tpa_group_forward_planned(layers, plan, x_ptrs, out_ptrs, ws_ptrs, ws_bytes, stream=0):
+    k = len(layers)
+    V = ctypes.c_void_p * k
+    _check(_lib.tpa_group_forward_planned(V(*layers), k, plan, V(*x_ptrs), V(*out_ptrs), V(*ws_ptrs),
+                                          (ctypes.c_size_t * k)(*ws_bytes), stream))
 
 
 def tpa_error_flag(layer, clear=False, stream=0):

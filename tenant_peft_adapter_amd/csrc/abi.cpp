@@ -713,112 +713,223 @@ tpa_status tpa_plan_max_tiles(const tpa_layer* L, int32_t n, int32_t* max_tiles,
 
 namespace {
 
-// Everything after the plan: shrink with OFT's rotation, base GEMM (with the
-// shrink's split reduction), expand (and any separate scale pass).
+// One projection of a forward: its layer, input, output, workspace and the
+// kernel configuration and workspace layout it runs with.
+struct SliceCtx {
+  tpa_layer* L;
+  const void* x;
+  void* out;
+  char* w;
+  Layout y;
+  Config c;
+};
+
+// Configurations of projections forwarded together with one plan: on the
+// decode path their base GEMMs share one launch, so they take one column-block
+// width (that of the widest projection, when it divides every d_out) and one
+// k range, the largest whose staged x fits and whose combined grid still has
+// ~200 work-groups.
+void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
+  for (int i = 0; i < count; ++i) cs[i] = choose_config(Ls[i], n);
+  if (count < 2) return;
+  for (int i = 0; i < count; ++i)
+    if (cs[i].gemm_path != 0) return;
+  int ref = 0;
+  for (int i = 1; i < count; ++i)
+    if (Ls[i]->d_out > Ls[ref]->d_out) ref = i;
+  int nb = cs[ref].gemm_nb;
+  for (int i = 0; i < count; ++i)
+    if (Ls[i]->d_out % (64 * nb)) nb = 1;
+  const int G = cs[0].gemm_groups;
+  int kc = 64;
+  for (int cand : {1024, 512, 256, 128, 64}) {
+    if (tpa::gemm_skinny_lds(Ls[0]->dtype, n, nb, G, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
+    kc = cand;
+    long wgs = 0;
+    for (int i = 0; i < count; ++i) wgs += (long)(Ls[i]->d_out / (64 * nb)) * ((Ls[i]->d_in + cand - 1) / cand);
+    if (wgs >= 200) break;
+  }
+  for (int i = 0; i < count; ++i) {
+    cs[i].gemm_nb = nb;
+    cs[i].gemm_groups = G;
+    cs[i].gemm_kc = std::min(kc, round_up(Ls[i]->d_in, 64));
+    cs[i].gemm_split = (Ls[i]->d_in + cs[i].gemm_kc - 1) / cs[i].gemm_kc;
+  }
+}
+
+// Everything after the plan, for `count` projections that share it: the
+// shrink with OFT's rotation, the base GEMM (with the shrink's split
+// reduction), the expand (and any separate scale pass).  Each kernel is one
+// launch over all projections whose configurations allow it.  Stage events
+// are those of the first projection's layer.
+tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs& p, int n, hipStream_t s) {
+  tpa_layer* L0 = sl[0].L;
+  const int dtype = L0->dtype;
+  const int tile_rows = sl[0].c.tile_rows;
+  tpa::ShrinkArgs sh[tpa::MAX_SLICES];
+  tpa::OftArgs of[tpa::MAX_SLICES];
+  bool term[tpa::MAX_SLICES], oft[tpa::MAX_SLICES];
+  bool any_term_all = false;
+  for (int i = 0; i < count; ++i) {
+    tpa_layer* L = sl[i].L;
+    const Layout& y = sl[i].y;
+    const Config& c = sl[i].c;
+    term[i] = L->n_owned > 0 || L->n_vera > 0;
+    oft[i] = L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
+    any_term_all = any_term_all || term[i];
+    sh[i] = tpa::ShrinkArgs{};
+    if (term[i]) {
+      sh[i].x = sl[i].x;
+      sh[i].pinfo = p.pinfo;
+      sh[i].tiles = p.tiles;
+      sh[i].slots = L->slots_dev;
+      sh[i].vera_At = L->vera_At;
+      sh[i].r_v = L->r_v;
+      sh[i].n = n;
+      sh[i].d_in = L->d_in;
+      sh[i].kmax = L->kmax;
+      sh[i].max_tiles = y.max_tiles;
+      sh[i].nblk = L->kmax / 16;
+      sh[i].split = c.shrink_split;
+      sh[i].kc = c.shrink_kc;
+      sh[i].part = reinterpret_cast<float*>(sl[i].w + y.vpart);
+      sh[i].v = sl[i].w + y.v;
+    }
+    of[i] = tpa::OftArgs{};
+    of[i].x = sl[i].x;
+    of[i].perm = p.perm;
+    of[i].oft_tiles = p.oft_tiles;
+    of[i].slots = L->slots_dev;
+    of[i].x_rot = sl[i].w + y.x_rot;
+    of[i].d_in = L->d_in;
+    of[i].max_tiles = y.max_tiles;
+  }
+
+  // 2. The shrink and OFT's rotation: one launch per OFT block size present
+  //    (the shrink rides in the first), or one for the shrink alone.
+  static const int kBs[3] = {16, 32, 64};
+  tpa::PreSlice ps[tpa::MAX_SLICES];
+  bool sh_done = false;
+  for (int b = 0; b < 3; ++b) {
+    bool any = false;
+    for (int i = 0; i < count; ++i) any = any || sl[i].L->n_oft_bs[b] > 0;
+    if (!any) continue;
+    for (int i = 0; i < count; ++i) {
+      of[i].block = kBs[b];
+      ps[i] = tpa::make_pre_slice(!sh_done && term[i] ? &sh[i] : nullptr,
+                                  sl[i].L->n_oft_bs[b] ? &of[i] : nullptr);
+    }
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, kBs[b], ps, count, s));
+    sh_done = true;
+  }
+  if (!sh_done && any_term_all) {
+    for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr);
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, s));
+  }
+  if (tpa_status st = stage(L0, 2, s)) return st;
+
+  // 3. Base GEMM.  Decode path: one launch over the projections (they share
+  //    the column-block width and k-groups), the shrink's split reduction
+  //    riding in the same grid; otherwise the LDS-tiled kernel per projection.
+  tpa::GemmSlice gs[tpa::MAX_SLICES];
+  bool one_launch = true;
+  for (int i = 0; i < count; ++i) {
+    const Config& c = sl[i].c;
+    tpa_layer* L = sl[i].L;
+    tpa::BaseGemmArgs& g = gs[i].g;
+    g = tpa::BaseGemmArgs{};
+    g.x = sl[i].x;
+    g.x_rot = oft[i] ? sl[i].w + sl[i].y.x_rot : nullptr;
+    g.rot_pos = oft[i] ? p.rot_pos : nullptr;
+    g.W = L->W;
+    g.n = n;
+    g.d_in = L->d_in;
+    g.d_out = L->d_out;
+    g.split = c.gemm_split;
+    g.kc = c.gemm_kc;
+    g.part = reinterpret_cast<float*>(sl[i].w + sl[i].y.hpart);
+    g.out = sl[i].out;
+    gs[i].side = sh[i];
+    gs[i].has_side = term[i] ? 1 : 0;
+    if (c.gemm_path != 0 || c.gemm_nb != sl[0].c.gemm_nb || c.gemm_groups != sl[0].c.gemm_groups ||
+        sl[0].c.gemm_path != 0)
+      one_launch = false;
+  }
+  if (one_launch) {
+    TPA_HIP(tpa::launch_gemm_skinny(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, gs, count, s));
+  } else {
+    for (int i = 0; i < count; ++i) {
+      const Config& c = sl[i].c;
+      if (c.gemm_path == 0) {
+        TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
+      } else {
+        TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
+        if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
+      }
+    }
+  }
+  if (tpa_status st = stage(L0, 3, s)) return st;
+
+  // 4. Expand (with the comparison routes' separate scale passes).
+  tpa::ExpandArgs e[tpa::MAX_SLICES];
+  tpa::ScaleArgs sc[tpa::MAX_SLICES];
+  for (int i = 0; i < count; ++i) {
+    tpa_layer* L = sl[i].L;
+    const Config& c = sl[i].c;
+    const bool hsplit = c.gemm_path == 0 || c.gemm_split > 1;
+    sc[i] = tpa::ScaleArgs{};
+    sc[i].y = sl[i].out;
+    sc[i].hpart = hsplit ? reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart) : nullptr;
+    sc[i].hsplit = c.gemm_split;
+    sc[i].row_slot = p.row_slot;
+    sc[i].slots = L->slots_dev;
+    sc[i].srow = reinterpret_cast<float*>(sl[i].w + sl[i].y.srow);
+    sc[i].n = n;
+    sc[i].d_out = L->d_out;
+    bool h_in_out = !hsplit;
+    if (c.scale_route == 1) {  // side kernel: h ⊙ s + b written before the expand
+      TPA_HIP(tpa::launch_scale_pass(dtype, 1, sc[i], s));
+      h_in_out = true;
+    }
+    e[i] = tpa::ExpandArgs{};
+    e[i].out = sl[i].out;
+    e[i].hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart);
+    e[i].hsplit = c.gemm_split;
+    e[i].pinfo = p.pinfo;
+    e[i].tiles = p.tiles;
+    e[i].slots = L->slots_dev;
+    e[i].vera_Bt = L->vera_Bt;
+    e[i].r_v = L->r_v;
+    e[i].v = sl[i].w + sl[i].y.v;
+    e[i].kmax = L->kmax;
+    e[i].n = n;
+    e[i].d_out = L->d_out;
+    e[i].max_tiles = sl[i].y.max_tiles;
+    e[i].apply_scale = c.scale_route == 0;
+  }
+  if (tpa_status st = stage(L0, 4, s)) return st;
+  bool same_h = true;
+  for (int i = 0; i < count; ++i) same_h = same_h && ((e[i].hpart != nullptr) == (e[0].hpart != nullptr));
+  if (same_h) {
+    TPA_HIP(tpa::launch_expand(dtype, tile_rows, e, count, s));
+  } else {
+    for (int i = 0; i < count; ++i) TPA_HIP(tpa::launch_expand(dtype, tile_rows, &e[i], 1, s));
+  }
+  for (int i = 0; i < count; ++i) {
+    sc[i].hpart = nullptr;
+    if (sl[i].c.scale_route == 2) TPA_HIP(tpa::launch_scale_pass(dtype, 2, sc[i], s));
+    if (sl[i].c.scale_route == 3) {
+      TPA_HIP(tpa::launch_scale_pass(dtype, 3, sc[i], s));
+      TPA_HIP(tpa::launch_scale_pass(dtype, 4, sc[i], s));
+    }
+  }
+  return stage(L0, 5, s);
+}
+
 tpa_status forward_after_plan(tpa_layer* L, const tpa::PlanArgs& p, const void* x, int n, void* out, char* w,
                               const Layout& y, const Config& c, hipStream_t s) {
-  // 2. One launch for the shrink and OFT's rotation (the first block size
-  //    present; any other block size gets a launch of its own).
-  const bool any_oft = L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
-  const bool any_term = L->n_owned > 0 || L->n_vera > 0;
-  tpa::ShrinkArgs sh{};
-  if (any_term) {
-    sh.x = x;
-    sh.pinfo = p.pinfo;
-    sh.tiles = p.tiles;
-    sh.slots = L->slots_dev;
-    sh.vera_At = L->vera_At;
-    sh.r_v = L->r_v;
-    sh.n = n;
-    sh.d_in = L->d_in;
-    sh.kmax = L->kmax;
-    sh.max_tiles = y.max_tiles;
-    sh.nblk = L->kmax / 16;
-    sh.split = c.shrink_split;
-    sh.kc = c.shrink_kc;
-    sh.part = reinterpret_cast<float*>(w + y.vpart);
-    sh.v = w + y.v;
-  }
-  tpa::OftArgs o{};
-  o.x = x;
-  o.perm = p.perm;
-  o.oft_tiles = p.oft_tiles;
-  o.slots = L->slots_dev;
-  o.x_rot = w + y.x_rot;
-  o.d_in = L->d_in;
-  o.max_tiles = y.max_tiles;
-  static const int kBs[3] = {16, 32, 64};
-  bool fused_oft = false;
-  for (int i = 0; i < 3; ++i) {
-    if (!L->n_oft_bs[i]) continue;
-    o.block = kBs[i];
-    TPA_HIP(tpa::launch_pre(L->dtype, c.tile_rows, fused_oft || !any_term ? nullptr : &sh, &o, s));
-    fused_oft = true;
-  }
-  if (any_term && !fused_oft) TPA_HIP(tpa::launch_pre(L->dtype, c.tile_rows, &sh, nullptr, s));
-  if (tpa_status st = stage(L, 2, s)) return st;
-
-  // 3. Base GEMM; on the decode path the shrink's split reduction rides in
-  //    the same grid.
-  tpa::BaseGemmArgs g{};
-  g.x = x;
-  g.x_rot = any_oft ? w + y.x_rot : nullptr;
-  g.rot_pos = any_oft ? p.rot_pos : nullptr;
-  g.W = L->W;
-  g.n = n;
-  g.d_in = L->d_in;
-  g.d_out = L->d_out;
-  g.split = c.gemm_split;
-  g.kc = c.gemm_kc;
-  g.part = reinterpret_cast<float*>(w + y.hpart);
-  g.out = out;
-  if (c.gemm_path == 0) {
-    TPA_HIP(tpa::launch_gemm_skinny(L->dtype, c.gemm_nb, c.gemm_groups, g, any_term ? &sh : nullptr, s));
-  } else {
-    TPA_HIP(tpa::launch_gemm_tiled(L->dtype, g, s));
-    if (any_term) TPA_HIP(tpa::launch_shrink_reduce(L->dtype, sh, s));
-  }
-  const bool hsplit = c.gemm_path == 0 || c.gemm_split > 1;
-  if (tpa_status st = stage(L, 3, s)) return st;
-
-  tpa::ScaleArgs sc{};
-  sc.y = out;
-  sc.hpart = hsplit ? reinterpret_cast<const float*>(w + y.hpart) : nullptr;
-  sc.hsplit = c.gemm_split;
-  sc.row_slot = p.row_slot;
-  sc.slots = L->slots_dev;
-  sc.srow = reinterpret_cast<float*>(w + y.srow);
-  sc.n = n;
-  sc.d_out = L->d_out;
-  bool h_in_out = !hsplit;
-  if (c.scale_route == 1) {  // side kernel: h ⊙ s + b written before the expand
-    TPA_HIP(tpa::launch_scale_pass(L->dtype, 1, sc, s));
-    h_in_out = true;
-  }
-  if (tpa_status st = stage(L, 4, s)) return st;
-  tpa::ExpandArgs e{};
-  e.out = out;
-  e.hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(w + y.hpart);
-  e.hsplit = c.gemm_split;
-  e.pinfo = p.pinfo;
-  e.tiles = p.tiles;
-  e.slots = L->slots_dev;
-  e.vera_Bt = L->vera_Bt;
-  e.r_v = L->r_v;
-  e.v = w + y.v;
-  e.kmax = L->kmax;
-  e.n = n;
-  e.d_out = L->d_out;
-  e.max_tiles = y.max_tiles;
-  e.apply_scale = c.scale_route == 0;
-  TPA_HIP(tpa::launch_expand(L->dtype, c.tile_rows, e, s));
-  sc.hpart = nullptr;
-  if (c.scale_route == 2) TPA_HIP(tpa::launch_scale_pass(L->dtype, 2, sc, s));
-  if (c.scale_route == 3) {
-    TPA_HIP(tpa::launch_scale_pass(L->dtype, 3, sc, s));
-    TPA_HIP(tpa::launch_scale_pass(L->dtype, 4, sc, s));
-  }
-  return stage(L, 5, s);
+  SliceCtx one{L, x, out, w, y, c};
+  return forward_group_after_plan(&one, 1, p, n, s);
 }
 
 }  // namespace
@@ -923,6 +1034,57 @@ tpa_status tpa_layer_forward_planned(tpa_layer* L, const tpa_plan* plan, const v
   if (tpa_status st = stage(L, 0, s)) return st;
   if (tpa_status st = stage(L, 1, s)) return st;
   return forward_after_plan(L, p, x, n, out, static_cast<char*>(ws), y, c, s);
+}
+
+tpa_status tpa_group_workspace_size(tpa_layer* const* layers, int32_t count, int32_t n_max, size_t* bytes) {
+  if (!layers || !bytes || count < 1 || count > tpa::MAX_SLICES) return fail(TPA_ERR_INVALID, "bad group");
+  if (n_max < 0 || n_max > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "n_max must be in [0, %d]", tpa::PLAN_MAX_ROWS);
+  for (int i = 0; i < count; ++i) {
+    if (tpa_status st = check_layer(layers[i])) return st;
+    bytes[i] = 0;
+  }
+  Config cs[tpa::MAX_SLICES];
+  for (int n = 1; n <= n_max; ++n) {
+    group_configs(layers, count, n, cs);
+    for (int i = 0; i < count; ++i) bytes[i] = std::max(bytes[i], make_layout(layers[i], n, cs[i]).total);
+  }
+  return TPA_OK;
+}
+
+tpa_status tpa_group_forward_planned(tpa_layer* const* layers, int32_t count, const tpa_plan* plan,
+                                     const void* const* x, void* const* out, void* const* ws, const size_t* ws_bytes,
+                                     tpa_stream stream) {
+  if (!layers || !x || !out || !ws || !ws_bytes || count < 1 || count > tpa::MAX_SLICES)
+    return fail(TPA_ERR_INVALID, "bad group");
+  if (!plan || !plan->built) return fail(TPA_ERR_INVALID, "plan is not built");
+  for (int i = 0; i < count; ++i) {
+    tpa_layer* L = layers[i];
+    if (tpa_status st = check_layer(L)) return st;
+    if (L->dtype != layers[0]->dtype || L->device != layers[0]->device)
+      return fail(TPA_ERR_INVALID, "group layers differ in dtype or device");
+    if (plan->sig != L->plan_sig || plan->max_slots != L->max_slots)
+      return fail(TPA_ERR_INVALID, "plan was built for a layer with other slot classes");
+  }
+  const int n = plan->n;
+  if (n == 0) return TPA_OK;
+  Config cs[tpa::MAX_SLICES];
+  group_configs(layers, count, n, cs);
+  SliceCtx sl[tpa::MAX_SLICES];
+  for (int i = 0; i < count; ++i) {
+    if (!x[i] || !out[i] || !ws[i]) return fail(TPA_ERR_INVALID, "null pointer");
+    if (reinterpret_cast<uintptr_t>(ws[i]) & 255) return fail(TPA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (x[i] == out[i]) return fail(TPA_ERR_INVALID, "out may not alias x");
+    if (cs[i].tile_rows != plan->tile_rows) return fail(TPA_ERR_INVALID, "plan was built with other tiling");
+    sl[i] = SliceCtx{layers[i], x[i], out[i], static_cast<char*>(ws[i]), make_layout(layers[i], n, cs[i]), cs[i]};
+    if (ws_bytes[i] < sl[i].y.total) return fail(TPA_ERR_WORKSPACE, "workspace %d: %zu < %zu bytes", i, ws_bytes[i], sl[i].y.total);
+    if (plan->bytes < sl[i].y.plan_end) return fail(TPA_ERR_WORKSPACE, "plan buffer too small");
+  }
+  DeviceGuard guard(layers[0]->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const tpa::PlanArgs p = plan_args(layers[0], nullptr, n, const_cast<char*>(plan->dev), sl[0].y, cs[0]);
+  if (tpa_status st = stage(layers[0], 0, s)) return st;
+  if (tpa_status st = stage(layers[0], 1, s)) return st;
+  return forward_group_after_plan(sl, count, p, n, s);
 }
 
 tpa_status tpa_error_flag(tpa_layer* L, int32_t* flag_host, int32_t clear, tpa_stream stream) {

@@ -104,16 +104,20 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
 }
 
 template <typename T, int MB, bool HPART>
-__global__ __launch_bounds__(64) void expand_kernel(ExpandArgs a) {
+__global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fewer for wide fragments)
   constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
-  const int4 tl = *reinterpret_cast<const int4*>(a.tiles + 4 * blockIdx.x);
+  const int si = slice_of(t, (int)blockIdx.x);
+  const ExpandArgs& a = t.s[si];
+  const int local = (int)blockIdx.x - t.first[si];
+  const int ncb = a.d_out / 64;
+  const int4 tl = *reinterpret_cast<const int4*>(a.tiles + 4 * (local / ncb));
   const int p0 = tl.x, p1 = tl.y, kind = tl.z;
   if (kind < 0) return;  // padding past the plan's last tile
   const int lane = threadIdx.x;
   const int i16 = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.y * 64;
+  const int n0 = (local % ncb) * 64;
   const int col = n0 + 16 * g;
 
   // Row and slot of each of this lane's positions, and the slot record that
@@ -271,29 +275,40 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
 }
 
 template <typename T, int MB>
-hipError_t expand_launch(const ExpandArgs& a, hipStream_t s) {
-  dim3 grid(a.max_tiles, a.d_out / 64);
-  if (a.hpart)
-    hipLaunchKernelGGL((expand_kernel<T, MB, true>), grid, dim3(64), 0, s, a);
+hipError_t expand_launch(const Slices<ExpandArgs>& t, hipStream_t s) {
+  const dim3 grid((unsigned)t.first[t.count]);
+  if (t.s[0].hpart)
+    hipLaunchKernelGGL((expand_kernel<T, MB, true>), grid, dim3(64), 0, s, t);
   else
-    hipLaunchKernelGGL((expand_kernel<T, MB, false>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((expand_kernel<T, MB, false>), grid, dim3(64), 0, s, t);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t expand_tm(int tile_rows, const ExpandArgs& a, hipStream_t s) {
-  if (tile_rows == 16) return expand_launch<T, 1>(a, s);
-  if (tile_rows == 64) return expand_launch<T, 4>(a, s);
+hipError_t expand_tm(int tile_rows, const Slices<ExpandArgs>& t, hipStream_t s) {
+  if (tile_rows == 16) return expand_launch<T, 1>(t, s);
+  if (tile_rows == 64) return expand_launch<T, 4>(t, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs& a, hipStream_t s) {
+hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int count, hipStream_t s) {
+  if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
+  Slices<ExpandArgs> t{};
+  t.count = count;
+  t.first[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    if ((slices[i].hpart != nullptr) != (slices[0].hpart != nullptr) || slices[i].d_out % 64)
+      return hipErrorInvalidValue;
+    t.s[i] = slices[i];
+    t.first[i + 1] = t.first[i] + slices[i].max_tiles * (slices[i].d_out / 64);
+  }
+  for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
   switch (dtype) {
-    case 0: return expand_tm<float>(tile_rows, a, s);
-    case 1: return expand_tm<f16>(tile_rows, a, s);
-    case 2: return expand_tm<bf16>(tile_rows, a, s);
+    case 0: return expand_tm<float>(tile_rows, t, s);
+    case 1: return expand_tm<f16>(tile_rows, t, s);
+    case 2: return expand_tm<bf16>(tile_rows, t, s);
   }
   return hipErrorInvalidValue;
 }

@@ -15,6 +15,8 @@
 //     depend on scheduling.
 //   gemm_tiled   -- larger n (prefill).  128x128 output tiles, 128-byte k
 //     slices staged through double-buffered LDS, 2x2 waves of 64x64.
+#include <algorithm>
+
 #include "internal.h"
 #include "shrink_impl.h"
 
@@ -49,20 +51,23 @@ __device__ __forceinline__ f32x8 lds_frag<float>(const float* p) {
 // which the previous launch made ready; placed after the GEMM's work-groups
 // they take CUs the GEMM leaves free and are hidden under it.
 template <typename T, int MB, int NB, int G>
-__global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(BaseGemmArgs a, ShrinkArgs side) {
+__global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(Slices<GemmSlice> t) {
   typedef typename Frag<T>::V Vt;
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int U = sizeof(T) == 4 ? 2 : 8 / NB;  // k steps per register stage
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* xs = reinterpret_cast<T*>(smem);
+  const int si = slice_of(t, (int)blockIdx.x);
+  const BaseGemmArgs& a = t.s[si].g;
+  const int local = (int)blockIdx.x - t.first[si];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col_tiles = a.d_out / (64 * NB);
   const int n_gemm = col_tiles * a.split;
-  if ((int)blockIdx.x >= n_gemm) {
-    shrink_impl::shrink_reduce_item<T>(side, ((int)blockIdx.x - n_gemm) * (256 * G) + tid);
+  if (local >= n_gemm) {
+    shrink_impl::shrink_reduce_item<T>(t.s[si].side, (local - n_gemm) * (256 * G) + tid);
     return;
   }
-  const int gid = (int)blockIdx.x;
+  const int gid = local;
   const int slice = wave & 3, grp = wave >> 2;
   const int i16 = lane & 15, g = lane >> 4;
   const int col0 = (gid % col_tiles) * (64 * NB) + slice * (16 * NB);
@@ -314,22 +319,30 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
 }
 
 template <typename T, int G>
-hipError_t skinny_dispatch(int nb, const BaseGemmArgs& a, const ShrinkArgs* side, hipStream_t s) {
-  const int mb = a.n <= 16 ? 1 : a.n <= 32 ? 2 : 4;
-  ShrinkArgs sv{};
-  int n_side = 0;
-  if (side) {
-    sv = *side;
-    n_side = (int)(((long)side->n * (side->kmax / 4) + 256 * G - 1) / (256 * G));
+hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
+  const int mb = sl[0].g.n <= 16 ? 1 : sl[0].g.n <= 32 ? 2 : 4;
+  Slices<GemmSlice> t{};
+  t.count = count;
+  t.first[0] = 0;
+  size_t lds = 0;
+  for (int i = 0; i < count; ++i) {
+    const BaseGemmArgs& a = sl[i].g;
+    t.s[i] = sl[i];
+    const int n_gemm = (a.d_out / (64 * nb)) * a.split;
+    const int n_side = sl[i].has_side
+                           ? (int)(((long)sl[i].side.n * (sl[i].side.kmax / 4) + 256 * G - 1) / (256 * G))
+                           : 0;
+    t.first[i + 1] = t.first[i] + n_gemm + n_side;
+    const size_t stage = (size_t)16 * mb * (a.kc + 16 / sizeof(T)) * sizeof(T);
+    const size_t red = G > 1 ? (size_t)4 * nb * mb * 64 * 16 : 0;
+    lds = std::max(lds, std::max(stage, red));
   }
-  const dim3 grid((unsigned)(n_side + (a.d_out / (64 * nb)) * a.split));
-  const size_t stage = (size_t)16 * mb * (a.kc + 16 / sizeof(T)) * sizeof(T);
-  const size_t red = G > 1 ? (size_t)4 * nb * mb * 64 * 16 : 0;
-  const size_t lds = stage > red ? stage : red;
-#define TPA_SK(MBV, NBV)                                                                       \
-  if (mb == MBV && nb == NBV) {                                                               \
-    hipLaunchKernelGGL((gemm_skinny_kernel<T, MBV, NBV, G>), grid, dim3(256 * G), lds, s, a, sv); \
-    return hipGetLastError();                                                                 \
+  for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
+  const dim3 grid((unsigned)t.first[count]);
+#define TPA_SK(MBV, NBV)                                                                    \
+  if (mb == MBV && nb == NBV) {                                                            \
+    hipLaunchKernelGGL((gemm_skinny_kernel<T, MBV, NBV, G>), grid, dim3(256 * G), lds, s, t); \
+    return hipGetLastError();                                                              \
   }
   TPA_SK(1, 1) TPA_SK(2, 1) TPA_SK(4, 1)
   TPA_SK(1, 2) TPA_SK(2, 2) TPA_SK(4, 2)
@@ -348,14 +361,21 @@ size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc) {
   return stage > red ? stage : red;
 }
 
-hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const BaseGemmArgs& a, const ShrinkArgs* side,
-                              hipStream_t s) {
-  if (a.n <= 0 || a.n > 64 || a.kc % 64 || a.d_out % (64 * nb)) return hipErrorInvalidValue;
-  if (gemm_skinny_lds(dtype, a.n, nb, dtype == 0 ? 1 : groups, a.kc) > GEMM_SKINNY_MAX_LDS)
-    return hipErrorInvalidValue;
-  if (dtype == 0) return skinny_dispatch<float, 1>(nb, a, side, s);
-  if (dtype == 1) return groups == 1 ? skinny_dispatch<f16, 1>(nb, a, side, s) : skinny_dispatch<f16, 2>(nb, a, side, s);
-  if (dtype == 2) return groups == 1 ? skinny_dispatch<bf16, 1>(nb, a, side, s) : skinny_dispatch<bf16, 2>(nb, a, side, s);
+hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* slices, int count, hipStream_t s) {
+  if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
+  for (int i = 0; i < count; ++i) {
+    const BaseGemmArgs& a = slices[i].g;
+    if (a.n <= 0 || a.n > 64 || a.n != slices[0].g.n || a.kc % 64 || a.d_out % (64 * nb))
+      return hipErrorInvalidValue;
+    if (gemm_skinny_lds(dtype, a.n, nb, dtype == 0 ? 1 : groups, a.kc) > GEMM_SKINNY_MAX_LDS)
+      return hipErrorInvalidValue;
+  }
+  if (dtype == 0) return skinny_dispatch<float, 1>(nb, slices, count, s);
+  if (dtype == 1)
+    return groups == 1 ? skinny_dispatch<f16, 1>(nb, slices, count, s) : skinny_dispatch<f16, 2>(nb, slices, count, s);
+  if (dtype == 2)
+    return groups == 1 ? skinny_dispatch<bf16, 1>(nb, slices, count, s)
+                       : skinny_dispatch<bf16, 2>(nb, slices, count, s);
   return hipErrorInvalidValue;
 }
 

@@ -9,6 +9,26 @@
 
 namespace tpa {
 
+// ------------------------------------------------------------- slices ----
+// One launch can cover up to MAX_SLICES projections of a fused layer (q, k,
+// v; gate, up) that share one row plan: the kernel argument holds one record
+// per slice and the work-group ranges [first[i], first[i + 1]) of each.
+constexpr int MAX_SLICES = 4;
+template <typename A>
+struct Slices {
+  A s[MAX_SLICES];
+  int32_t first[MAX_SLICES + 1];
+  int32_t count;
+};
+template <typename A>
+__device__ __forceinline__ int slice_of(const Slices<A>& t, int bid) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < MAX_SLICES; ++j)
+    if (j < t.count && bid >= t.first[j]) i = j;
+  return i;
+}
+
 // ---------------------------------------------------------------- plan ----
 struct PlanArgs {
   const int32_t* slot_of_row;
@@ -57,16 +77,12 @@ struct BaseGemmArgs {
   float* part;             // [split][n][d_out] fp32 partials (split path)
   void* out;               // [n][d_out] in the layer type (split == 1, tiled)
 };
-struct ShrinkArgs;
 // Skinny kernel: n <= 64 rows; 64·nb output columns per work-group (nb = 1,
 // 2 or 4; d_out % (64·nb) == 0), kc a multiple of 64 whose staged x fits
-// GEMM_SKINNY_MAX_LDS; writes `part`.  With `side`, extra work-groups of the
-// same grid run the shrink's split reduction.  groups: k-groups of 4 waves
-// per work-group (1 or 2; fp32 uses 1).
+// GEMM_SKINNY_MAX_LDS; writes `part`.  groups: k-groups of 4 waves per
+// work-group (1 or 2; fp32 uses 1).  Declared with the shrink below.
 constexpr size_t GEMM_SKINNY_MAX_LDS = 144 * 1024;
 size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc);
-hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const BaseGemmArgs& a, const ShrinkArgs* side,
-                              hipStream_t stream);
 // LDS-tiled 128x128 kernel; writes `out` when split == 1, else `part`.
 hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t stream);
 
@@ -90,9 +106,27 @@ struct ShrinkArgs {
   float* part;
   void* v;
 };
-// One launch for the shrink's items (sh) and OFT's rotation of its tiles for
-// one block size (of); either may be null.
-hipError_t launch_pre(int dtype, int tile_rows, const ShrinkArgs* sh, const OftArgs* of, hipStream_t stream);
+// One slice of the launch before the base GEMM: the shrink's items and/or
+// OFT's rotation of its tiles for the launch's block size.
+struct PreSlice {
+  ShrinkArgs sh;
+  OftArgs of;
+  int32_t n_shrink_wg, n_oft_wg, oft_bg;
+};
+// Fills a PreSlice; sh / of may be null (that part gets no work-groups).
+PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of);
+// bs: OFT block size of the slices' OFT parts (0 when no slice has one).
+hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t stream);
+
+// One slice of a decode base-GEMM launch; with has_side, work-groups after
+// the slice's GEMM work-groups run the shrink's split reduction.
+struct GemmSlice {
+  BaseGemmArgs g;
+  ShrinkArgs side;
+  int32_t has_side;
+};
+hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* slices, int count,
+                              hipStream_t stream);
 // The shrink's split reduction on its own (when the GEMM cannot carry it).
 hipError_t launch_shrink_reduce(int dtype, const ShrinkArgs& a, hipStream_t stream);
 
@@ -115,7 +149,8 @@ struct ExpandArgs {
   int32_t max_tiles;
   int32_t apply_scale;     // 0: leave s and b to a separate pass
 };
-hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs& a, hipStream_t stream);
+// Every slice must have hpart set, or every slice must have it null.
+hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int count, hipStream_t stream);
 
 // Separate scale passes, for the route comparison of the appendix "Routes".
 //   mode 1 side kernel:  h ← h ⊙ s + b        (before the expand)

@@ -20,50 +20,39 @@ constexpr int THREADS = 256;
 constexpr int OFT_BLOCKS_PER_WG = 16;
 
 template <typename T, int MB, int BS>
-__global__ __launch_bounds__(THREADS) void pre_kernel(ShrinkArgs sh, OftArgs of, int n_shrink_wg, int oft_bg) {
+__global__ __launch_bounds__(THREADS) void pre_kernel(Slices<PreSlice> t) {
+  const int si = slice_of(t, (int)blockIdx.x);
+  const PreSlice& ps = t.s[si];
+  const int local = (int)blockIdx.x - t.first[si];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if ((int)blockIdx.x < n_shrink_wg) {
-    shrink_impl::shrink_item<T, MB>(sh, (int)blockIdx.x * (THREADS / 64) + wave, lane);
+  if (local < ps.n_shrink_wg) {
+    shrink_impl::shrink_item<T, MB>(ps.sh, local * (THREADS / 64) + wave, lane);
     return;
   }
   if (BS != 0) {
-    const int o = (int)blockIdx.x - n_shrink_wg;
-    oft_impl::oft_part<T, MB, (BS == 0 ? 16 : BS)>(of, o / oft_bg, o % oft_bg, wave, lane);
+    const int o = local - ps.n_shrink_wg;
+    oft_impl::oft_part<T, MB, (BS == 0 ? 16 : BS)>(ps.of, o / ps.oft_bg, o % ps.oft_bg, wave, lane);
   }
 }
 
 template <typename T, int MB>
-hipError_t pre_bs(const ShrinkArgs* sh, const OftArgs* of, hipStream_t s) {
-  ShrinkArgs shv{};
-  OftArgs ofv{};
-  int n_shrink_wg = 0, n_oft_wg = 0, oft_bg = 1, bs = 0;
-  if (sh) {
-    shv = *sh;
-    const long items = (long)sh->max_tiles * sh->nblk * sh->split;
-    n_shrink_wg = (int)((items + THREADS / 64 - 1) / (THREADS / 64));
-  }
-  if (of) {
-    ofv = *of;
-    bs = of->block;
-    oft_bg = (of->d_in / bs + OFT_BLOCKS_PER_WG - 1) / OFT_BLOCKS_PER_WG;
-    n_oft_wg = of->max_tiles * oft_bg;
-  }
-  const dim3 grid((unsigned)(n_shrink_wg + n_oft_wg));
+hipError_t pre_bs(int bs, const Slices<PreSlice>& t, hipStream_t s) {
+  const dim3 grid((unsigned)t.first[t.count]);
   if (grid.x == 0) return hipSuccess;
   switch (bs) {
-    case 0: hipLaunchKernelGGL((pre_kernel<T, MB, 0>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
-    case 16: hipLaunchKernelGGL((pre_kernel<T, MB, 16>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
-    case 32: hipLaunchKernelGGL((pre_kernel<T, MB, 32>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
-    case 64: hipLaunchKernelGGL((pre_kernel<T, MB, 64>), grid, dim3(THREADS), 0, s, shv, ofv, n_shrink_wg, oft_bg); break;
+    case 0: hipLaunchKernelGGL((pre_kernel<T, MB, 0>), grid, dim3(THREADS), 0, s, t); break;
+    case 16: hipLaunchKernelGGL((pre_kernel<T, MB, 16>), grid, dim3(THREADS), 0, s, t); break;
+    case 32: hipLaunchKernelGGL((pre_kernel<T, MB, 32>), grid, dim3(THREADS), 0, s, t); break;
+    case 64: hipLaunchKernelGGL((pre_kernel<T, MB, 64>), grid, dim3(THREADS), 0, s, t); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t pre_tm(int tile_rows, const ShrinkArgs* sh, const OftArgs* of, hipStream_t s) {
-  if (tile_rows == 16) return pre_bs<T, 1>(sh, of, s);
-  if (tile_rows == 64) return pre_bs<T, 4>(sh, of, s);
+hipError_t pre_tm(int tile_rows, int bs, const Slices<PreSlice>& t, hipStream_t s) {
+  if (tile_rows == 16) return pre_bs<T, 1>(bs, t, s);
+  if (tile_rows == 64) return pre_bs<T, 4>(bs, t, s);
   return hipErrorInvalidValue;
 }
 
@@ -74,11 +63,36 @@ __global__ __launch_bounds__(THREADS) void shrink_reduce_kernel(ShrinkArgs a) {
 
 }  // namespace
 
-hipError_t launch_pre(int dtype, int tile_rows, const ShrinkArgs* sh, const OftArgs* of, hipStream_t s) {
+PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of) {
+  PreSlice ps{};
+  ps.oft_bg = 1;
+  if (sh) {
+    ps.sh = *sh;
+    const long items = (long)sh->max_tiles * sh->nblk * sh->split;
+    ps.n_shrink_wg = (int)((items + THREADS / 64 - 1) / (THREADS / 64));
+  }
+  if (of) {
+    ps.of = *of;
+    ps.oft_bg = (of->d_in / of->block + OFT_BLOCKS_PER_WG - 1) / OFT_BLOCKS_PER_WG;
+    ps.n_oft_wg = of->max_tiles * ps.oft_bg;
+  }
+  return ps;
+}
+
+hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t s) {
+  if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
+  Slices<PreSlice> t{};
+  t.count = count;
+  t.first[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    t.s[i] = slices[i];
+    t.first[i + 1] = t.first[i] + slices[i].n_shrink_wg + slices[i].n_oft_wg;
+  }
+  for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
   switch (dtype) {
-    case 0: return pre_tm<float>(tile_rows, sh, of, s);
-    case 1: return pre_tm<f16>(tile_rows, sh, of, s);
-    case 2: return pre_tm<bf16>(tile_rows, sh, of, s);
+    case 0: return pre_tm<float>(tile_rows, bs, t, s);
+    case 1: return pre_tm<f16>(tile_rows, bs, t, s);
+    case 2: return pre_tm<bf16>(tile_rows, bs, t, s);
   }
   return hipErrorInvalidValue;
 }

@@ -147,3 +147,22 @@ class RowPlan:
             self.close()
         except Exception:
             pass
+
+
+class LayerGroup:
+    """Projections of one fused layer (q, k, v or gate, up) that share a row
+    plan, forwarded with one launch per kernel (tpa_group_forward_planned)."""
+
+    def __init__(self, layers, n_max):
+        self.layers = list(layers)
+        sizes = B.tpa_group_workspace_size([L.handle for L in self.layers], n_max)
+        self.ws = [torch.empty(max(sz, 256), dtype=torch.uint8, device=L.W.device)
+                   for L, sz in zip(self.layers, sizes)]
+
+    def forward(self, plan, xs, outs=None):
+        if outs is None:
+            outs = [torch.empty((plan.n, L.d_out), dtype=L.W.dtype, device=L.W.device) for L in self.layers]
+        B.tpa_group_forward_planned([L.handle for L in self.layers], plan.handle, [x.data_ptr() for x in xs],
+                                    [o.data_ptr() for o in outs], [w.data_ptr() for w in self.ws],
+                                    [w.numel() for w in self.ws], _stream())
+        return outs

@@ -9,6 +9,7 @@ base output.  fp32 layers are held to 1e-4 and 2e-5.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
 
@@ -108,3 +109,55 @@ def test_vera_sweep_and_lora_arm(tenants, d_out):
     m = oracle.parity_metrics(ya_gpu, y_gpu, base, base)
     say("shared vs arm", m)
     assert m["mean_rel"] <= 0.02 and m["max_abs"] <= 4e-3 * m["max_h"]
+
+
+def test_group_forward_qkv_against_oracle():
+    """q, k and v of the decoder-layer workload forwarded as one group (one
+    launch per kernel, a shared plan): every row of every projection against
+    the oracle."""
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    wl = synth.decoder_layer_mixed(shapes=(("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024)))
+    projs = wl["projections"]
+    Ls = [make_layer(p, max_slots=32, max_rank=256) for p in projs]
+    say("group q+k+v n=%d" % wl["n"])
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    plan = RowPlan(Ls[0], wl["n"]).build(Ls[0], sor)
+    grp = LayerGroup(Ls, wl["n"])
+    xs = [torch.tensor(p["x"]).half().cuda() for p in projs]
+    outs = grp.forward(plan, xs)
+    torch.cuda.synchronize()
+    for p, o in zip(projs, outs):
+        y, h, xw = reference(p, wl["slot_of_row"])
+        check(o.float().cpu().numpy().astype(np.float64), y, h, xw, label="group " + p["name"])
+    plan.close()
+
+
+def test_group_forward_gate_up_matches_separate_forwards():
+    """gate and up as one group give the separate forwards' outputs up to the
+    rounding of the shared split-K configuration."""
+    from tenant_peft_adapter_amd import binding as B
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    wl = synth.decoder_layer_mixed(shapes=(("gate", 4096, 14336), ("up", 4096, 14336), ("o", 4096, 4096)))
+    pg, pu, po = wl["projections"]
+    Lg, Lu, Lo = [make_layer(p, max_slots=32, max_rank=256) for p in (pg, pu, po)]
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    xs = [torch.tensor(p["x"]).half().cuda() for p in (pg, pu)]
+    sep = [Lg.forward(xs[0], sor).float(), Lu.forward(xs[1], sor).float()]
+    plan = RowPlan(Lg, wl["n"]).build(Lg, sor)
+    outs = LayerGroup([Lg, Lu], wl["n"]).forward(plan, xs)
+    torch.cuda.synchronize()
+    for a, b, nm in zip(outs, sep, ("gate", "up")):
+        err = (a.float() - b).abs().max().item()
+        scale = b.abs().max().item()
+        say("group vs separate", nm, err, scale)
+        assert err <= 2e-3 * scale, nm
+    # o has the same slot classes as gate and up in this workload (OFT and
+    # (IA)3 tenants are no-term classes there), so it may join the group; a
+    # layer with other slot classes may not.
+    Lq = make_layer(synth.decoder_layer_mixed(shapes=(("q", 4096, 4096),))["projections"][0],
+                    max_slots=32, max_rank=256)
+    with pytest.raises(B.TpaError) as e:
+        LayerGroup([Lg, Lq], wl["n"]).forward(plan, [xs[0], torch.zeros(wl["n"], 4096, dtype=torch.half,
+                                                                         device="cuda")])
+    assert e.value.code == -1
+    plan.close()
