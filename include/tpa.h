@@ -250,7 +250,11 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *   TPA_OPT_GEMM_SPLIT   : split-K factor of the base GEMM
  *   TPA_OPT_SHRINK_SPLIT : split-K factor of the shrink
  *   TPA_OPT_TILE_ROWS    : rows per tile of the plan (16 or 64)
- *   TPA_OPT_GEMM_PATH    : 0 skinny (n <= 64) kernel, 1 LDS-tiled kernel
+ *   TPA_OPT_GEMM_PATH    : n <= 64: 0 register-fed decode kernel, 2 decode
+ *                          kernel fed by direct global-to-LDS loads (f16 /
+ *                          bf16 with d_in % 64 == 0, else 0; the default
+ *                          where it applies); 1 LDS-tiled kernel (always
+ *                          used for n > 64)
  *   TPA_OPT_SCALE_ROUTE  : where s (and b) are applied (§4.3, appendix
  *                          "Routes"): 0 inside the expand (route one),
  *                          1 side kernel writing h⊙s before the expand,
@@ -258,8 +262,8 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          3 index scale: write s per row, then multiply
  *   TPA_OPT_GEMM_NB      : decode GEMM, 64-column blocks per work-group (1,
  *                          2 or 4)
- *   TPA_OPT_GEMM_GROUPS  : decode GEMM, k-groups of 4 waves per work-group
- *                          (1 or 2; fp32 layers always use 1) */
+ *   TPA_OPT_GEMM_GROUPS  : register-fed decode GEMM, k-groups of 4 waves per
+ *                          work-group (1 or 2; fp32 layers always use 1) */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -300,9 +304,14 @@ tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms);
 
 /* Calibration probes (appendix "Constants"): a plain device copy of `bytes`
  * (a multiple of 16, 16-byte aligned pointers) by a streaming kernel, and
- * `count` chained one-block empty kernels for the launch cost. */
+ * `count` chained one-block empty kernels for the launch cost.
+ * tpa_probe_delay enqueues one wave that idles for `microseconds` (0 .. 1e6)
+ * of the device's constant-rate clock and touches no memory: work queued
+ * behind it on the stream starts back to back once it ends, so host launch
+ * gaps drop out of event timings. */
 tpa_status tpa_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, tpa_stream stream);
 tpa_status tpa_probe_empty(int32_t count, tpa_stream stream);
+tpa_status tpa_probe_delay(int32_t microseconds, tpa_stream stream);
 
 /* Message of the last error on this thread ("" if none). */
 const char* tpa_last_error(void);

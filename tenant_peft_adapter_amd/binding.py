@@ -96,6 +96,7 @@ def _load():
         "tpa_timing_event_elapsed": [vp, vp, P(ctypes.c_float)],
         "tpa_probe_copy": [vp, vp, sz, vp],
         "tpa_probe_empty": [i32, vp],
+        "tpa_probe_delay": [i32, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -310,3 +311,7 @@ def tpa_probe_copy(dst_ptr, src_ptr, nbytes, stream=0):
 
 def tpa_probe_empty(count, stream=0):
     _check(_lib.tpa_probe_empty(count, stream))
+
+
+def tpa_probe_delay(microseconds, stream=0):
+    _check(_lib.tpa_probe_delay(microseconds, stream))

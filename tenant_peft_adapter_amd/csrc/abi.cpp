@@ -150,7 +150,7 @@ void cayley_transposed(const float* Q, int b, float* out) {
 
 struct Config {
   int tile_rows;
-  int gemm_path;  // 0 skinny, 1 tiled
+  int gemm_path;  // 0 skinny, 1 tiled, 2 stream
   int gemm_nb, gemm_groups;
   int gemm_split, gemm_kc;
   int shrink_split, shrink_kc;
@@ -204,24 +204,37 @@ int oft_bs_index(int bs) { return bs == 16 ? 0 : bs == 32 ? 1 : bs == 64 ? 2 : -
 Config choose_config(const tpa_layer* L, int n) {
   Config c{};
   c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : (n <= 256 ? 16 : 64);
-  c.gemm_path = (n > 64) ? 1 : (L->opt[TPA_OPT_GEMM_PATH] >= 0 ? L->opt[TPA_OPT_GEMM_PATH] : 0);
-  if (c.gemm_path == 0) {
-    // 64·nb columns per work-group; the largest k range (1024, 512 or 256)
-    // that still gives ~200 work-groups and whose staged x fits in LDS.
-    c.gemm_nb = (L->d_out >= 8192 && L->d_out % 256 == 0) ? 4 : (L->d_out >= 2048 ? 2 : 1);
+  // Decode (n <= 64): the LDS-streamed kernel for f16 / bf16 with d_in a
+  // multiple of 64, else the register-fed one; larger batches: tiled.
+  const bool stream_ok = L->dtype != TPA_F32 && L->d_in % 64 == 0;
+  c.gemm_path = (n > 64) ? 1 : (L->opt[TPA_OPT_GEMM_PATH] >= 0 ? L->opt[TPA_OPT_GEMM_PATH] : (stream_ok ? 2 : 0));
+  if (c.gemm_path == 2 && !stream_ok) c.gemm_path = 0;
+  if (c.gemm_path == 0 || c.gemm_path == 2) {
+    // 64·nb columns per work-group; the largest k range (1024 ... 64) that
+    // still gives enough work-groups: ~200 for the register-fed kernel (whose
+    // staged x must also fit in LDS), 256 for the streamed one (two resident
+    // per CU at nb = 2).
+    if (c.gemm_path == 2)
+      c.gemm_nb = (L->d_out >= 2048 && L->d_out % 128 == 0) ? 2 : 1;
+    else
+      c.gemm_nb = (L->d_out >= 8192 && L->d_out % 256 == 0) ? 4 : (L->d_out >= 2048 ? 2 : 1);
     if (L->opt[TPA_OPT_GEMM_NB] > 0 && L->d_out % (64 * L->opt[TPA_OPT_GEMM_NB]) == 0) c.gemm_nb = L->opt[TPA_OPT_GEMM_NB];
     c.gemm_groups = L->dtype == TPA_F32 ? 1 : (L->opt[TPA_OPT_GEMM_GROUPS] > 0 ? L->opt[TPA_OPT_GEMM_GROUPS] : 2);
+    if (c.gemm_path == 2) c.gemm_groups = 1;
+    auto fits = [&](int kc) {
+      return c.gemm_path == 2 || tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, kc) <= tpa::GEMM_SKINNY_MAX_LDS;
+    };
     const int col_tiles = L->d_out / (64 * c.gemm_nb);
     int kc = 0;
     const int split_opt = L->opt[TPA_OPT_GEMM_SPLIT];
     if (split_opt > 0) {
       kc = round_up((L->d_in + split_opt - 1) / split_opt, 64);
-      while (kc > 64 && tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, kc) > tpa::GEMM_SKINNY_MAX_LDS) kc -= 64;
+      while (kc > 64 && !fits(kc)) kc -= 64;
     } else {
       for (int cand : {1024, 512, 256, 128, 64}) {
-        if (tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
+        if (!fits(cand)) continue;
         kc = cand;
-        if ((long)col_tiles * ((L->d_in + cand - 1) / cand) >= 200) break;
+        if ((long)col_tiles * ((L->d_in + cand - 1) / cand) >= (c.gemm_path == 2 ? 256 : 200)) break;
       }
     }
     c.gemm_kc = std::min(kc, round_up(L->d_in, 64));
@@ -270,7 +283,7 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.counts = take(4 * tpa::CNT_WORDS);
   y.plan_end = off;
   y.x_rot = take((size_t)n * L->d_in * esz);
-  const bool need_hpart = c.gemm_path == 0 || c.gemm_split > 1;
+  const bool need_hpart = c.gemm_path != 1 || c.gemm_split > 1;
   y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
   y.vpart = take((size_t)c.shrink_split * n * L->kmax * 4);
   y.v = take((size_t)n * L->kmax * esz);
@@ -733,7 +746,8 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
   for (int i = 0; i < count; ++i) cs[i] = choose_config(Ls[i], n);
   if (count < 2) return;
   for (int i = 0; i < count; ++i)
-    if (cs[i].gemm_path != 0) return;
+    if (cs[i].gemm_path != cs[0].gemm_path || cs[i].gemm_path == 1) return;
+  const bool stream = cs[0].gemm_path == 2;
   int ref = 0;
   for (int i = 1; i < count; ++i)
     if (Ls[i]->d_out > Ls[ref]->d_out) ref = i;
@@ -743,11 +757,11 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
   const int G = cs[0].gemm_groups;
   int kc = 64;
   for (int cand : {1024, 512, 256, 128, 64}) {
-    if (tpa::gemm_skinny_lds(Ls[0]->dtype, n, nb, G, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
+    if (!stream && tpa::gemm_skinny_lds(Ls[0]->dtype, n, nb, G, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
     kc = cand;
     long wgs = 0;
     for (int i = 0; i < count; ++i) wgs += (long)(Ls[i]->d_out / (64 * nb)) * ((Ls[i]->d_in + cand - 1) / cand);
-    if (wgs >= 200) break;
+    if (wgs >= (stream ? 256 : 200)) break;
   }
   for (int i = 0; i < count; ++i) {
     cs[i].gemm_nb = nb;
@@ -851,16 +865,21 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     g.out = sl[i].out;
     gs[i].side = sh[i];
     gs[i].has_side = term[i] ? 1 : 0;
-    if (c.gemm_path != 0 || c.gemm_nb != sl[0].c.gemm_nb || c.gemm_groups != sl[0].c.gemm_groups ||
-        sl[0].c.gemm_path != 0)
+    if (c.gemm_path != sl[0].c.gemm_path || c.gemm_path == 1 || c.gemm_nb != sl[0].c.gemm_nb ||
+        c.gemm_groups != sl[0].c.gemm_groups)
       one_launch = false;
   }
   if (one_launch) {
-    TPA_HIP(tpa::launch_gemm_skinny(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, gs, count, s));
+    if (sl[0].c.gemm_path == 2)
+      TPA_HIP(tpa::launch_gemm_stream(dtype, sl[0].c.gemm_nb, gs, count, s));
+    else
+      TPA_HIP(tpa::launch_gemm_skinny(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, gs, count, s));
   } else {
     for (int i = 0; i < count; ++i) {
       const Config& c = sl[i].c;
-      if (c.gemm_path == 0) {
+      if (c.gemm_path == 2) {
+        TPA_HIP(tpa::launch_gemm_stream(dtype, c.gemm_nb, &gs[i], 1, s));
+      } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
         TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
@@ -876,7 +895,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   for (int i = 0; i < count; ++i) {
     tpa_layer* L = sl[i].L;
     const Config& c = sl[i].c;
-    const bool hsplit = c.gemm_path == 0 || c.gemm_split > 1;
+    const bool hsplit = c.gemm_path != 1 || c.gemm_split > 1;
     sc[i] = tpa::ScaleArgs{};
     sc[i].y = sl[i].out;
     sc[i].hpart = hsplit ? reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart) : nullptr;
@@ -1147,7 +1166,7 @@ tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (key == TPA_OPT_GEMM_GROUPS && value > 2) return fail(TPA_ERR_INVALID, "gemm groups must be 1 or 2");
   if (key == TPA_OPT_TILE_ROWS && value > 0 && value != 16 && value != 64)
     return fail(TPA_ERR_INVALID, "tile rows must be 16 or 64");
-  if (key == TPA_OPT_GEMM_PATH && value > 1) return fail(TPA_ERR_INVALID, "gemm path must be 0 or 1");
+  if (key == TPA_OPT_GEMM_PATH && value > 2) return fail(TPA_ERR_INVALID, "gemm path must be 0, 1 or 2");
   if (key == TPA_OPT_SCALE_ROUTE) {
     if (value < 0) value = 0;
     if (value > 3) return fail(TPA_ERR_INVALID, "scale route must be 0..3");
@@ -1220,6 +1239,12 @@ tpa_status tpa_probe_copy(void* dst, const void* src, size_t bytes, tpa_stream s
 tpa_status tpa_probe_empty(int32_t count, tpa_stream stream) {
   if (count < 0) return fail(TPA_ERR_INVALID, "negative count");
   TPA_HIP(tpa::launch_empty(count, static_cast<hipStream_t>(stream)));
+  return TPA_OK;
+}
+
+tpa_status tpa_probe_delay(int32_t microseconds, tpa_stream stream) {
+  if (microseconds < 0 || microseconds > 1000000) return fail(TPA_ERR_INVALID, "delay must be 0 .. 1e6 us");
+  TPA_HIP(tpa::launch_delay(microseconds, static_cast<hipStream_t>(stream)));
   return TPA_OK;
 }
 

@@ -26,6 +26,11 @@ namespace {
 
 constexpr int THREADS = 256;
 
+// s_waitcnt operand that waits for vmcnt <= n and nothing else (gfx9 layout:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at
+// their maxima).
+constexpr unsigned waitcnt_vm(int n) { return (unsigned)((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14)); }
+
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::V lds_frag(const T* p) {
   return *reinterpret_cast<const typename Frag<T>::V*>(p);
@@ -192,6 +197,175 @@ __global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(Slices<GemmSlice> 
   }
 }
 
+// ------------------------------------------------------------- stream ----
+//
+// Decode base GEMM (n <= 64 rows, f16/bf16) fed by gfx950's direct global-
+// to-LDS loads.  Work-group = 4 waves; its tile is 64·NB output columns (wave
+// w owns 16·NB) by one k range of kc (split-K).  The range is walked in
+// 64-element slices: each slice of W (64·NB rows x 128 B) and of x (16·MB
+// rows x 128 B) is loaded straight into one of S LDS buffers, 8 rows x 128 B
+// (whole cache lines) per wave instruction, with no registers held while the
+// loads are in flight; S - 1 slices are in flight while one is multiplied.
+// Synchronization per slice: each wave waits for its own loads of the slice
+// (vmcnt), then a work-group barrier; the loads write LDS directly, so no
+// fence is needed.  Partials, the slice table and the side reduction are as
+// in gemm_skinny_kernel.
+//
+// Within a 128-byte LDS row the eight 16-byte chunks are permuted, chunk c
+// stored at c ^ swz(row), so that the fragment reads (16 rows, one chunk
+// each) hit distinct bank groups: with l = row & 3 and h = bits SH, SH+1 of
+// the row (the lane's i >> 2 under perm_col), swz mixes l and h so that any
+// 8 lanes differ in (row * 128 + 16 * chunk) mod 128 and any 16 lanes in
+// that mod 256.
+constexpr int STREAM_STAGES = 3;
+
+template <int SH>
+__device__ __forceinline__ int swz(int r) {
+  const int l = r & 3, h = (r >> SH) & 3;
+  return ((l >> 1) & 1) | ((h & 1) << 1) | ((((h >> 1) ^ l) & 1) << 2);
+}
+
+template <int NB>
+constexpr int log2_nb() {
+  return NB == 1 ? 0 : NB == 2 ? 1 : 2;
+}
+
+template <int MB, int NB>
+constexpr size_t stream_stage_bytes() {
+  return (size_t)(64 * NB + 16 * MB) * 128;
+}
+
+template <typename T, int MB, int NB>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
+  typedef typename Frag<T>::V Vt;
+  constexpr int S = STREAM_STAGES;
+  constexpr int WROWS = 64 * NB;             // W rows (output columns) per work-group
+  constexpr int W_INSTR = WROWS / 32;        // W loads per wave per slice (8 rows each)
+  constexpr int X_INSTR = 2 * MB;            // x loads per slice, whole work-group
+  constexpr int XJ = (X_INSTR + 3) / 4;      // x loads per slice a wave may issue
+  constexpr int SHW = 2 + log2_nb<NB>();     // swz shift of the W rows
+  constexpr int STAGE = (int)stream_stage_bytes<MB, NB>();
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int si = slice_of(t, (int)blockIdx.x);
+  const BaseGemmArgs& a = t.s[si].g;
+  const int local = (int)blockIdx.x - t.first[si];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col_tiles = a.d_out / WROWS;
+  const int n_gemm = col_tiles * a.split;
+  if (local >= n_gemm) {
+    shrink_impl::shrink_reduce_item<T>(t.s[si].side, (local - n_gemm) * 256 + tid);
+    return;
+  }
+  const int col0 = (local % col_tiles) * WROWS;
+  const int ks = local / col_tiles;
+  const int kbeg = ks * a.kc;
+  const int nst = min(a.d_in - kbeg, a.kc) / 64;  // slices of 64 elements
+  const T* W = static_cast<const T*>(a.W);
+  const T* X = static_cast<const T*>(a.x);
+  const T* XR = static_cast<const T*>(a.x_rot);
+
+  // Global source of each of this lane's loads (the same for every slice
+  // but for the k offset): lane = 8 · (row within the instruction) + LDS chunk.
+  const int lr = lane >> 3, lc = lane & 7;
+  const T* wsrc[W_INSTR];
+#pragma unroll
+  for (int j = 0; j < W_INSTR; ++j) {
+    const int r = (wave * W_INSTR + j) * 8 + lr;
+    wsrc[j] = W + (size_t)(col0 + r) * a.d_in + kbeg + 8 * (lc ^ swz<SHW>(r));
+  }
+  const T* xsrc[XJ];
+  bool xmine[XJ];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) {
+    const int ji = wave * XJ + j;  // x instruction index
+    xmine[j] = ji < X_INSTR;
+    const int rr = (xmine[j] ? ji : 0) * 8 + lr;  // row of the x tile
+    const T* base = X;                             // rows >= n read row 0, unused
+    if (rr < a.n) {
+      base = X + (size_t)rr * a.d_in;
+      if (a.rot_pos) {
+        const int rp = a.rot_pos[rr];
+        if (rp >= 0) base = XR + (size_t)rp * a.d_in;
+      }
+    }
+    xsrc[j] = base + kbeg + 8 * (lc ^ swz<2>(rr));
+  }
+  auto issue = [&](int st) {
+    unsigned char* buf = smem + (size_t)(st % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < W_INSTR; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(wsrc[j] + 64 * st),
+          (__attribute__((address_space(3))) void*)(buf + (size_t)(wave * W_INSTR + j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < XJ; ++j)
+      if (xmine[j])
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(xsrc[j] + 64 * st),
+            (__attribute__((address_space(3))) void*)(buf + (size_t)WROWS * 128 + (size_t)(wave * XJ + j) * 1024),
+            16, 0, 0);
+  };
+
+  // LDS byte offsets (within a stage) of this lane's fragment rows.
+  const int i16 = lane & 15, g = lane >> 4;
+  int arow[NB], brow[MB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) arow[b] = wave * 16 * NB + perm_col<NB>(i16, b);
+#pragma unroll
+  for (int m = 0; m < MB; ++m) brow[m] = 16 * m + i16;
+
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nst) issue(st);
+  for (int it = 0; it < nst; ++it) {
+    // This wave's loads of slice `it` are done once no more than (slices
+    // issued after it) x W_INSTR are outstanding (a wave issues at least
+    // W_INSTR per slice; loads complete in order); every wave's, after the
+    // barrier.
+    const int younger = min(S - 2, nst - 1 - it);
+    __builtin_amdgcn_sched_barrier(0);
+    if (younger >= 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(W_INSTR));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + S - 1 < nst) issue(it + S - 1);
+    const unsigned char* buf = smem + (size_t)(it % S) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int q = 4 * kk + g;  // 16-byte chunk of the row: k = 8q .. 8q + 7
+      Vt af[NB], bf[MB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        af[b] = *reinterpret_cast<const Vt*>(buf + arow[b] * 128 + 16 * (q ^ swz<SHW>(arow[b])));
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        bf[m] = *reinterpret_cast<const Vt*>(buf + WROWS * 128 + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+    }
+  }
+
+  // The lane holds columns col0 + 16·NB·wave + 4·NB·g + [0, 4·NB) of row 16m + i16.
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int row = 16 * m + i16;
+    if (row >= a.n) continue;
+    float* dst = a.part + ((size_t)ks * a.n + row) * a.d_out + col0 + 16 * NB * wave + 4 * NB * g;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = acc[b][m];
+  }
+}
+
 // --------------------------------------------------------------- tiled ----
 
 template <typename T>
@@ -351,6 +525,35 @@ hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+template <typename T>
+hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
+  const int mb = sl[0].g.n <= 16 ? 1 : sl[0].g.n <= 32 ? 2 : 4;
+  Slices<GemmSlice> t{};
+  t.count = count;
+  t.first[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    const BaseGemmArgs& a = sl[i].g;
+    t.s[i] = sl[i];
+    const int n_gemm = (a.d_out / (64 * nb)) * a.split;
+    const int n_side =
+        sl[i].has_side ? (int)(((long)sl[i].side.n * (sl[i].side.kmax / 4) + 255) / 256) : 0;
+    t.first[i + 1] = t.first[i] + n_gemm + n_side;
+  }
+  for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
+  const dim3 grid((unsigned)t.first[count]);
+#define TPA_ST(MBV, NBV)                                                                       \
+  if (mb == MBV && nb == NBV) {                                                               \
+    const size_t lds = STREAM_STAGES * stream_stage_bytes<MBV, NBV>();                        \
+    hipLaunchKernelGGL((gemm_stream_kernel<T, MBV, NBV>), grid, dim3(256), lds, s, t);        \
+    return hipGetLastError();                                                                 \
+  }
+  TPA_ST(1, 1) TPA_ST(2, 1) TPA_ST(4, 1)
+  TPA_ST(1, 2) TPA_ST(2, 2) TPA_ST(4, 2)
+  TPA_ST(1, 4) TPA_ST(2, 4) TPA_ST(4, 4)
+#undef TPA_ST
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc) {
@@ -376,6 +579,21 @@ hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* sl
   if (dtype == 2)
     return groups == 1 ? skinny_dispatch<bf16, 1>(nb, slices, count, s)
                        : skinny_dispatch<bf16, 2>(nb, slices, count, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_stream(int dtype, int nb, const GemmSlice* slices, int count, hipStream_t s) {
+  if (count < 1 || count > MAX_SLICES || (nb != 1 && nb != 2 && nb != 4)) return hipErrorInvalidValue;
+  for (int i = 0; i < count; ++i) {
+    const BaseGemmArgs& a = slices[i].g;
+    // Whole 64-element slices in every k range, whole column tiles, rows
+    // 64-byte aligned for the 16-byte loads.
+    if (a.n <= 0 || a.n > 64 || a.n != slices[0].g.n || a.kc <= 0 || a.kc % 64 || a.d_in % 64 ||
+        a.d_out % (64 * nb) || (long)a.split * a.kc < a.d_in)
+      return hipErrorInvalidValue;
+  }
+  if (dtype == 1) return stream_dispatch<f16>(nb, slices, count, s);
+  if (dtype == 2) return stream_dispatch<bf16>(nb, slices, count, s);
   return hipErrorInvalidValue;
 }
 

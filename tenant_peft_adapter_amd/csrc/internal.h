@@ -127,6 +127,9 @@ struct GemmSlice {
 };
 hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* slices, int count,
                               hipStream_t stream);
+// The same GEMM with W and x streamed into LDS by direct loads (f16 / bf16;
+// d_in and kc multiples of 64).
+hipError_t launch_gemm_stream(int dtype, int nb, const GemmSlice* slices, int count, hipStream_t stream);
 // The shrink's split reduction on its own (when the GEMM cannot carry it).
 hipError_t launch_shrink_reduce(int dtype, const ShrinkArgs& a, hipStream_t stream);
 
@@ -197,6 +200,7 @@ hipError_t launch_pack_transpose(int dtype, const float* src, int rows, int cols
 // -------------------------------------------------------------- probes ----
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_empty(int count, hipStream_t stream);
+hipError_t launch_delay(int microseconds, hipStream_t stream);
 
 size_t dtype_size(int dtype);
 

@@ -80,6 +80,16 @@ __global__ __launch_bounds__(THREADS) void copy_kernel(uint4* dst, const uint4* 
 
 __global__ void empty_kernel() {}
 
+// One wave that idles for `ticks` of the constant-rate device clock; the
+// iteration cap (each iteration sleeps) bounds it even if the clock stalls.
+__global__ void delay_kernel(unsigned long long ticks, unsigned long long max_iters) {
+  const unsigned long long t0 = wall_clock64();
+  for (unsigned long long i = 0; i < max_iters; ++i) {
+    if (wall_clock64() - t0 >= ticks) break;
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 unsigned grid_for(size_t work) {
   size_t g = (work + THREADS - 1) / THREADS;
   if (g > 65536) g = 65536;
@@ -146,6 +156,17 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
 
 hipError_t launch_empty(int count, hipStream_t s) {
   for (int i = 0; i < count; ++i) hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_delay(int microseconds, hipStream_t s) {
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return e;
+  if (khz <= 0) return hipErrorInvalidValue;
+  const unsigned long long ticks = (unsigned long long)microseconds * (unsigned long long)khz / 1000ull;
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, s, ticks, ticks + 1);
   return hipGetLastError();
 }
 

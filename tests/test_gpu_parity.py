@@ -71,17 +71,51 @@ def test_prefill_lora_dora_q_proj():
     check(y_gpu, y, h, xw, label="prefill q")
 
 
-def test_decoder_layer_mixed_all_projections():
+_DECODER = {}
+
+
+def _decoder_layer():
+    """The decoder-layer workload and its oracle outputs, computed once."""
+    if not _DECODER:
+        wl = synth.decoder_layer_mixed()
+        _DECODER["wl"] = wl
+        _DECODER["ref"] = {p["name"]: reference(p, wl["slot_of_row"]) for p in wl["projections"]}
+    return _DECODER["wl"], _DECODER["ref"]
+
+
+@pytest.mark.parametrize("path", [0, 2])
+def test_decoder_layer_mixed_all_projections(path):
     """One Llama-3.1-8B decoder layer (7 projections), 64 decode rows over 20
-    tenants of 5 methods, rows shuffled: every row of every projection."""
-    wl = synth.decoder_layer_mixed()
+    tenants of 5 methods, rows shuffled: every row of every projection, with
+    the register-fed (0) and the LDS-streamed (2) decode GEMM."""
+    wl, ref = _decoder_layer()
     for p in wl["projections"]:
-        say("decoder_layer_mixed", p["name"], p["d_in"], p["d_out"])
-        L = make_layer(p, max_slots=32, max_rank=256)
+        say("decoder_layer_mixed path=%d" % path, p["name"], p["d_in"], p["d_out"])
+        L = make_layer(p, max_slots=32, max_rank=256, options={4: path})
         y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
-        y, h, xw = reference(p, wl["slot_of_row"])
+        y, h, xw = ref[p["name"]]
         check(y_gpu, y, h, xw, label="decoder " + p["name"])
         L.close()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n", [1, 16, 17, 40, 64])
+@pytest.mark.parametrize("nb,split", [(1, 1), (2, 4), (4, 2)])
+def test_stream_gemm_tiny(dtype, n, nb, split):
+    """The LDS-streamed decode GEMM over each row-block count (n up to 16,
+    32, 64, ragged), each column-block width and several k ranges (one
+    64-element slice up to the whole 256)."""
+    wl = synth.tiny_mixed(seed=400 + n, n=n, d=256, dtype=dtype, with_identity=True)
+    p = wl["projections"][0]
+    say("stream tiny", dtype, "n=%d nb=%d split=%d" % (n, nb, split))
+    L = make_layer(p, max_slots=8, max_rank=32, options={4: 2, 6: nb, 1: split})
+    cfg = L.config(n)
+    assert (cfg["gemm_path"], cfg["gemm_nb"], cfg["gemm_split"]) == (2, nb, split), cfg
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    max_tol = 2e-3 if dtype == "f16" else 1.6e-2
+    check(y_gpu, y, h, xw, max_tol=max_tol, mean_tol=0.01 if dtype == "f16" else 0.05,
+          label="stream " + dtype)
 
 
 @pytest.mark.parametrize("tenants,d_out", [(1, 4096), (16, 4096), (64, 14336)])
@@ -111,15 +145,16 @@ def test_vera_sweep_and_lora_arm(tenants, d_out):
     assert m["mean_rel"] <= 0.02 and m["max_abs"] <= 4e-3 * m["max_h"]
 
 
-def test_group_forward_qkv_against_oracle():
+@pytest.mark.parametrize("path", [0, 2])
+def test_group_forward_qkv_against_oracle(path):
     """q, k and v of the decoder-layer workload forwarded as one group (one
     launch per kernel, a shared plan): every row of every projection against
     the oracle."""
     from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
     wl = synth.decoder_layer_mixed(shapes=(("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024)))
     projs = wl["projections"]
-    Ls = [make_layer(p, max_slots=32, max_rank=256) for p in projs]
-    say("group q+k+v n=%d" % wl["n"])
+    Ls = [make_layer(p, max_slots=32, max_rank=256, options={4: path}) for p in projs]
+    say("group q+k+v n=%d path=%d" % (wl["n"], path))
     sor = torch.tensor(wl["slot_of_row"]).cuda()
     plan = RowPlan(Ls[0], wl["n"]).build(Ls[0], sor)
     grp = LayerGroup(Ls, wl["n"])

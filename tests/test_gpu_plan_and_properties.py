@@ -80,12 +80,12 @@ def test_identity_rows_equal_base_only_output_bitwise():
     assert np.array_equal(y_mixed[ident], y_base[ident])
 
 
-@pytest.mark.parametrize("n", [20, 64, 200])
-def test_batch_invariance_row_alone_vs_in_batch(n):
+@pytest.mark.parametrize("n,path", [(20, 0), (20, 2), (64, 0), (64, 2), (200, 1)])
+def test_batch_invariance_row_alone_vs_in_batch(n, path):
     """With the kernel configuration pinned, a row computed alone equals the
     same row inside a batch of other tenants, bit for bit."""
     wl, p = _tiny(seed=5, n=n)
-    opts = {1: 2, 2: 2, 3: 16, 4: 0 if n <= 64 else 1}
+    opts = {1: 2, 2: 2, 3: 16, 4: path}
     L = make_layer(p, max_slots=8, max_rank=32, options=opts)
     sor = wl["slot_of_row"]
     y_all = run(L, p["x"], sor, "f16")
@@ -247,6 +247,14 @@ def test_probes_copy_and_launch():
     B.tpa_probe_empty(8, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+    # The delay probe idles for about the time asked.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    B.tpa_probe_delay(2000, torch.cuda.current_stream().cuda_stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert 1.9 <= ms <= 50.0, ms
 
 
 def test_shared_plan_forward_matches_plain_forward():
