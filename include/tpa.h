@@ -262,8 +262,11 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          3 index scale: write s per row, then multiply
  *   TPA_OPT_GEMM_NB      : decode GEMM, 64-column blocks per work-group (1,
  *                          2 or 4)
- *   TPA_OPT_GEMM_GROUPS  : register-fed decode GEMM, k-groups of 4 waves per
- *                          work-group (1 or 2; fp32 layers always use 1) */
+ *   TPA_OPT_GEMM_GROUPS  : decode GEMM, k-groups of 4 waves per work-group
+ *                          (1 or 2; fp32 layers always use 1; the streamed
+ *                          kernel takes 2 only with 3 stages)
+ *   TPA_OPT_GEMM_STAGES  : streamed decode GEMM, LDS buffers per k-group
+ *                          (3, 4 or 6; fewer where they do not fit) */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -271,16 +274,19 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_SCALE_ROUTE 5
 #define TPA_OPT_GEMM_NB 6
 #define TPA_OPT_GEMM_GROUPS 7
+#define TPA_OPT_GEMM_STAGES 8
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no
- * device work): plan tile rows, base GEMM path (0 decode kernel with x
- * staged in LDS, 1 LDS-tiled kernel), its 64-column blocks per work-group
- * (nb), split-K factor and k range, the shrink's split and k range, and the
- * scale route.  For tests and measurement. */
+ * device work): plan tile rows, base GEMM path (0 register-fed decode
+ * kernel, 1 LDS-tiled kernel, 2 streamed decode kernel), its 64-column
+ * blocks per work-group (nb), split-K factor and k range, the shrink's split
+ * and k range, the scale route, the decode GEMM's k-groups per work-group
+ * and (streamed kernel, else 0) its LDS buffers per k-group.  For tests and
+ * measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
-      gemm_groups;
+      gemm_groups, gemm_stages;
 } tpa_config;
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
 

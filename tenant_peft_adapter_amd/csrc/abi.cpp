@@ -151,7 +151,7 @@ void cayley_transposed(const float* Q, int b, float* out) {
 struct Config {
   int tile_rows;
   int gemm_path;  // 0 skinny, 1 tiled, 2 stream
-  int gemm_nb, gemm_groups;
+  int gemm_nb, gemm_groups, gemm_stages;
   int gemm_split, gemm_kc;
   int shrink_split, shrink_kc;
   int scale_route;
@@ -163,6 +163,8 @@ struct Layout {
   size_t x_rot, hpart, vpart, v, srow;
   size_t total;
   int max_tiles;
+  size_t sh_tiles;
+  int max_sh_tiles;
 };
 
 }  // namespace
@@ -180,8 +182,9 @@ struct tpa_layer {
   const void* vera_Bt = nullptr;
   int r_v = 0;
   int n_owned = 0, n_vera = 0, n_dora = 0;
+  int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
-  int opt[8] = {-1, -1, -1, -1, -1, 0, -1, -1};
+  int opt[9] = {-1, -1, -1, -1, -1, 0, -1, -1, -1};
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
   uint64_t plan_sig = 0;  // hash of every slot's (term class, has R): what a row plan depends on
@@ -201,6 +204,58 @@ namespace {
 
 int oft_bs_index(int bs) { return bs == 16 ? 0 : bs == 32 ? 1 : bs == 64 ? 2 : -1; }
 
+// k range of the streamed decode GEMM for a grid of `col_tiles` column tiles
+// (summed over the projections of one launch) over d_in: the largest power
+// of two with at most 16 slices of 64 per k-group and >= 192 work-groups.
+int stream_kc(long col_tiles, int d_in, int groups) {
+  int kc = 64 * groups;
+  for (int cand = 4096; cand >= 64 * groups; cand /= 2) {
+    if (cand > 1024 * groups) continue;
+    if (col_tiles * ((d_in + cand - 1) / cand) >= 192) return cand;
+  }
+  return kc;
+}
+
+// k-groups and k range of one streamed decode-GEMM launch over `count`
+// projections (sharing d_in) at column-block width nb: two k-groups (half
+// the partials) unless their larger work-groups (one per CU) would take an
+// extra round of the grid, counting the work-groups that carry the shrink's
+// split reduction.
+void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stages, int g_opt, int* groups,
+                 int* kc_out) {
+  long col_tiles = 0;
+  int d_in = 0;
+  for (int i = 0; i < count; ++i) {
+    col_tiles += Ls[i]->d_out / (64 * nb);
+    d_in = std::max(d_in, Ls[i]->d_in);
+  }
+  long best_rounds = 0;
+  *groups = 0;
+  for (int G : {2, 1}) {
+    if (g_opt > 0 && G != g_opt) continue;
+    if (G > 1 && stages != 3) continue;
+    const size_t lds = tpa::gemm_stream_lds(n, nb, G, stages);
+    if (lds > tpa::GEMM_STREAM_MAX_LDS) continue;
+    const int kc = stream_kc(col_tiles, d_in, G);
+    long total = 0;
+    for (int i = 0; i < count; ++i) {
+      total += (long)(Ls[i]->d_out / (64 * nb)) * ((Ls[i]->d_in + kc - 1) / kc);
+      if (Ls[i]->n_owned > 0 || Ls[i]->n_vera > 0) total += ((long)n * (Ls[i]->kmax / 4) + 256 * G - 1) / (256 * G);
+    }
+    const long slots = 256L * (long)(tpa::GEMM_STREAM_MAX_LDS / lds);
+    const long rounds = (total + slots - 1) / slots;
+    if (*groups == 0 || rounds < best_rounds) {
+      *groups = G;
+      *kc_out = kc;
+      best_rounds = rounds;
+    }
+  }
+  if (*groups == 0) {  // nothing fits the options: one group, three stages
+    *groups = 1;
+    *kc_out = stream_kc(col_tiles, d_in, 1);
+  }
+}
+
 Config choose_config(const tpa_layer* L, int n) {
   Config c{};
   c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : (n <= 256 ? 16 : 64);
@@ -209,20 +264,27 @@ Config choose_config(const tpa_layer* L, int n) {
   const bool stream_ok = L->dtype != TPA_F32 && L->d_in % 64 == 0;
   c.gemm_path = (n > 64) ? 1 : (L->opt[TPA_OPT_GEMM_PATH] >= 0 ? L->opt[TPA_OPT_GEMM_PATH] : (stream_ok ? 2 : 0));
   if (c.gemm_path == 2 && !stream_ok) c.gemm_path = 0;
-  if (c.gemm_path == 0 || c.gemm_path == 2) {
+  if (c.gemm_path == 2) {
+    // 64·nb columns per work-group; k-groups and k range from stream_pick.
+    c.gemm_nb = (L->d_out >= 2048 && L->d_out % 128 == 0) ? 2 : 1;
+    if (L->opt[TPA_OPT_GEMM_NB] > 0 && L->d_out % (64 * L->opt[TPA_OPT_GEMM_NB]) == 0) c.gemm_nb = L->opt[TPA_OPT_GEMM_NB];
+    c.gemm_stages = L->opt[TPA_OPT_GEMM_STAGES] > 0 ? L->opt[TPA_OPT_GEMM_STAGES] : 3;
+    while (c.gemm_stages > 3 && tpa::gemm_stream_lds(n, c.gemm_nb, 1, c.gemm_stages) > tpa::GEMM_STREAM_MAX_LDS)
+      c.gemm_stages = c.gemm_stages == 6 ? 4 : 3;
+    int kc;
+    stream_pick(&L, 1, n, c.gemm_nb, c.gemm_stages, L->opt[TPA_OPT_GEMM_GROUPS], &c.gemm_groups, &kc);
+    const int split_opt = L->opt[TPA_OPT_GEMM_SPLIT];
+    if (split_opt > 0) kc = round_up((L->d_in + split_opt - 1) / split_opt, 64 * c.gemm_groups);
+    c.gemm_kc = std::min(kc, round_up(L->d_in, 64 * c.gemm_groups));
+    c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
+  } else if (c.gemm_path == 0) {
     // 64·nb columns per work-group; the largest k range (1024 ... 64) that
-    // still gives enough work-groups: ~200 for the register-fed kernel (whose
-    // staged x must also fit in LDS), 256 for the streamed one (two resident
-    // per CU at nb = 2).
-    if (c.gemm_path == 2)
-      c.gemm_nb = (L->d_out >= 2048 && L->d_out % 128 == 0) ? 2 : 1;
-    else
-      c.gemm_nb = (L->d_out >= 8192 && L->d_out % 256 == 0) ? 4 : (L->d_out >= 2048 ? 2 : 1);
+    // still gives ~200 work-groups and whose staged x fits in LDS.
+    c.gemm_nb = (L->d_out >= 8192 && L->d_out % 256 == 0) ? 4 : (L->d_out >= 2048 ? 2 : 1);
     if (L->opt[TPA_OPT_GEMM_NB] > 0 && L->d_out % (64 * L->opt[TPA_OPT_GEMM_NB]) == 0) c.gemm_nb = L->opt[TPA_OPT_GEMM_NB];
     c.gemm_groups = L->dtype == TPA_F32 ? 1 : (L->opt[TPA_OPT_GEMM_GROUPS] > 0 ? L->opt[TPA_OPT_GEMM_GROUPS] : 2);
-    if (c.gemm_path == 2) c.gemm_groups = 1;
     auto fits = [&](int kc) {
-      return c.gemm_path == 2 || tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, kc) <= tpa::GEMM_SKINNY_MAX_LDS;
+      return tpa::gemm_skinny_lds(L->dtype, n, c.gemm_nb, c.gemm_groups, kc) <= tpa::GEMM_SKINNY_MAX_LDS;
     };
     const int col_tiles = L->d_out / (64 * c.gemm_nb);
     int kc = 0;
@@ -234,7 +296,7 @@ Config choose_config(const tpa_layer* L, int n) {
       for (int cand : {1024, 512, 256, 128, 64}) {
         if (!fits(cand)) continue;
         kc = cand;
-        if ((long)col_tiles * ((L->d_in + cand - 1) / cand) >= (c.gemm_path == 2 ? 256 : 200)) break;
+        if ((long)col_tiles * ((L->d_in + cand - 1) / cand) >= 200) break;
       }
     }
     c.gemm_kc = std::min(kc, round_up(L->d_in, 64));
@@ -280,6 +342,8 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.seg_slot = take(4 * (size_t)n);
   y.tiles = take(16 * (size_t)y.max_tiles);
   y.oft_tiles = take(16 * (size_t)y.max_tiles);
+  y.max_sh_tiles = (n + c.tile_rows - 1) / c.tile_rows;
+  y.sh_tiles = take(16 * (size_t)y.max_sh_tiles);
   y.counts = take(4 * tpa::CNT_WORDS);
   y.plan_end = off;
   y.x_rot = take((size_t)n * L->d_in * esz);
@@ -309,6 +373,8 @@ tpa::PlanArgs plan_args(tpa_layer* L, const int32_t* sor, int n, char* ws, const
   p.seg_slot = reinterpret_cast<int32_t*>(ws + y.seg_slot);
   p.tiles = reinterpret_cast<int32_t*>(ws + y.tiles);
   p.oft_tiles = reinterpret_cast<int32_t*>(ws + y.oft_tiles);
+  p.sh_tiles = reinterpret_cast<int32_t*>(ws + y.sh_tiles);
+  p.max_sh_tiles = y.max_sh_tiles;
   p.counts = reinterpret_cast<int32_t*>(ws + y.counts);
   p.flag = L->flag_dev;
   return p;
@@ -341,8 +407,30 @@ void update_plan_sig(tpa_layer* L) {
     }
   };
   mix((uint64_t)L->max_slots);
-  for (const SlotDev& sd : L->slots_host) mix((uint64_t)(uint32_t)sd.cls | ((uint64_t)sd.has_R << 32));
+  int rmax = 0;
+  for (const SlotDev& sd : L->slots_host) {
+    mix((uint64_t)(uint32_t)sd.cls | ((uint64_t)sd.has_R << 32));
+    if (sd.cls == tpa::CLS_OWNED) rmax = std::max(rmax, (int)sd.rank);
+  }
   L->plan_sig = h;
+  L->max_owned_rank = rmax;
+}
+
+// Bounds on what a plan of n rows holds for this layer's loaded slots (the
+// kernels' grids; the plan pads its lists past the real counts).  Owned-term
+// tiles: each owned segment is cut into tiles of tile_rows, so at most
+// ceil(n / tile_rows) + (owned segments); the shared-term and no-term ranges
+// add at most one partial tile each.  OFT tiles likewise per rotated slot.
+int owned_tile_bound(const tpa_layer* L, int n, int tr, int max_tiles) {
+  if (L->n_owned == 0) return 0;
+  return std::min(max_tiles, (n + tr - 1) / tr + std::min(n, L->n_owned));
+}
+int all_tile_bound(const tpa_layer* L, int n, int tr, int max_tiles) {
+  return std::min(max_tiles, (n + tr - 1) / tr + std::min(n, L->n_owned) + 2);
+}
+int oft_tile_bound(const tpa_layer* L, int n, int tr, int max_tiles) {
+  const int n_rot = L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2];
+  return std::min(max_tiles, (n + tr - 1) / tr + std::min(n, n_rot));
 }
 
 // A device float32 staging copy of a host array.
@@ -739,9 +827,9 @@ struct SliceCtx {
 
 // Configurations of projections forwarded together with one plan: on the
 // decode path their base GEMMs share one launch, so they take one column-block
-// width (that of the widest projection, when it divides every d_out) and one
-// k range, the largest whose staged x fits and whose combined grid still has
-// ~200 work-groups.
+// width (that of the widest projection, when it divides every d_out), one
+// k-group count and one k range, chosen as for one projection but over the
+// combined grid (a split pinned on the first projection is kept).
 void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
   for (int i = 0; i < count; ++i) cs[i] = choose_config(Ls[i], n);
   if (count < 2) return;
@@ -754,19 +842,31 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
   int nb = cs[ref].gemm_nb;
   for (int i = 0; i < count; ++i)
     if (Ls[i]->d_out % (64 * nb)) nb = 1;
-  const int G = cs[0].gemm_groups;
+  int G = cs[0].gemm_groups, S = cs[0].gemm_stages;
   int kc = 64;
-  for (int cand : {1024, 512, 256, 128, 64}) {
-    if (!stream && tpa::gemm_skinny_lds(Ls[0]->dtype, n, nb, G, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
-    kc = cand;
-    long wgs = 0;
-    for (int i = 0; i < count; ++i) wgs += (long)(Ls[i]->d_out / (64 * nb)) * ((Ls[i]->d_in + cand - 1) / cand);
-    if (wgs >= (stream ? 256 : 200)) break;
+  if (stream) {
+    while (S > 3 && tpa::gemm_stream_lds(n, nb, 1, S) > tpa::GEMM_STREAM_MAX_LDS) S = S == 6 ? 4 : 3;
+    stream_pick(Ls, count, n, nb, S, Ls[0]->opt[TPA_OPT_GEMM_GROUPS], &G, &kc);
+  }
+  if (Ls[0]->opt[TPA_OPT_GEMM_SPLIT] > 0) {
+    kc = round_up((Ls[0]->d_in + Ls[0]->opt[TPA_OPT_GEMM_SPLIT] - 1) / Ls[0]->opt[TPA_OPT_GEMM_SPLIT],
+                  64 * (stream ? G : 1));
+    if (!stream)
+      while (kc > 64 && tpa::gemm_skinny_lds(Ls[0]->dtype, n, nb, G, kc) > tpa::GEMM_SKINNY_MAX_LDS) kc -= 64;
+  } else if (!stream) {
+    for (int cand : {1024, 512, 256, 128, 64}) {
+      if (tpa::gemm_skinny_lds(Ls[0]->dtype, n, nb, G, cand) > tpa::GEMM_SKINNY_MAX_LDS) continue;
+      kc = cand;
+      long wgs = 0;
+      for (int i = 0; i < count; ++i) wgs += (long)(Ls[i]->d_out / (64 * nb)) * ((Ls[i]->d_in + cand - 1) / cand);
+      if (wgs >= 200) break;
+    }
   }
   for (int i = 0; i < count; ++i) {
     cs[i].gemm_nb = nb;
     cs[i].gemm_groups = G;
-    cs[i].gemm_kc = std::min(kc, round_up(Ls[i]->d_in, 64));
+    cs[i].gemm_stages = S;
+    cs[i].gemm_kc = std::min(kc, round_up(Ls[i]->d_in, 64 * (stream ? G : 1)));
     cs[i].gemm_split = (Ls[i]->d_in + cs[i].gemm_kc - 1) / cs[i].gemm_kc;
   }
 }
@@ -802,8 +902,11 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       sh[i].n = n;
       sh[i].d_in = L->d_in;
       sh[i].kmax = L->kmax;
-      sh[i].max_tiles = y.max_tiles;
-      sh[i].nblk = L->kmax / 16;
+      sh[i].sh_tiles = p.sh_tiles;
+      sh[i].own_tiles = owned_tile_bound(L, n, tile_rows, y.max_tiles);
+      sh[i].own_nblk = std::max(1, (L->max_owned_rank + 15) / 16);
+      sh[i].sh_ntiles = L->n_vera > 0 ? y.max_sh_tiles : 0;
+      sh[i].sh_nblk = std::max(1, L->r_v / 16);
       sh[i].split = c.shrink_split;
       sh[i].kc = c.shrink_kc;
       sh[i].part = reinterpret_cast<float*>(sl[i].w + y.vpart);
@@ -816,7 +919,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     of[i].slots = L->slots_dev;
     of[i].x_rot = sl[i].w + y.x_rot;
     of[i].d_in = L->d_in;
-    of[i].max_tiles = y.max_tiles;
+    of[i].max_tiles = oft_tile_bound(L, n, tile_rows, y.max_tiles);
   }
 
   // 2. The shrink and OFT's rotation: one launch per OFT block size present
@@ -866,19 +969,19 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     gs[i].side = sh[i];
     gs[i].has_side = term[i] ? 1 : 0;
     if (c.gemm_path != sl[0].c.gemm_path || c.gemm_path == 1 || c.gemm_nb != sl[0].c.gemm_nb ||
-        c.gemm_groups != sl[0].c.gemm_groups)
+        c.gemm_groups != sl[0].c.gemm_groups || (c.gemm_path == 2 && c.gemm_stages != sl[0].c.gemm_stages))
       one_launch = false;
   }
   if (one_launch) {
     if (sl[0].c.gemm_path == 2)
-      TPA_HIP(tpa::launch_gemm_stream(dtype, sl[0].c.gemm_nb, gs, count, s));
+      TPA_HIP(tpa::launch_gemm_stream(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, sl[0].c.gemm_stages, gs, count, s));
     else
       TPA_HIP(tpa::launch_gemm_skinny(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, gs, count, s));
   } else {
     for (int i = 0; i < count; ++i) {
       const Config& c = sl[i].c;
       if (c.gemm_path == 2) {
-        TPA_HIP(tpa::launch_gemm_stream(dtype, c.gemm_nb, &gs[i], 1, s));
+        TPA_HIP(tpa::launch_gemm_stream(dtype, c.gemm_nb, c.gemm_groups, c.gemm_stages, &gs[i], 1, s));
       } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
@@ -923,7 +1026,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     e[i].kmax = L->kmax;
     e[i].n = n;
     e[i].d_out = L->d_out;
-    e[i].max_tiles = sl[i].y.max_tiles;
+    e[i].max_tiles = all_tile_bound(L, n, tile_rows, sl[i].y.max_tiles);
     e[i].apply_scale = c.scale_route == 0;
   }
   if (tpa_status st = stage(L0, 4, s)) return st;
@@ -1160,7 +1263,9 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
-  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_GEMM_GROUPS) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_GEMM_STAGES) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_GEMM_STAGES && value > 0 && value != 3 && value != 4 && value != 6)
+    return fail(TPA_ERR_INVALID, "gemm stages must be 3, 4 or 6");
   if (key == TPA_OPT_GEMM_NB && value > 0 && value != 1 && value != 2 && value != 4)
     return fail(TPA_ERR_INVALID, "gemm nb must be 1, 2 or 4");
   if (key == TPA_OPT_GEMM_GROUPS && value > 2) return fail(TPA_ERR_INVALID, "gemm groups must be 1 or 2");
@@ -1191,6 +1296,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   out->shrink_kc = c.shrink_kc;
   out->scale_route = c.scale_route;
   out->gemm_groups = c.gemm_groups;
+  out->gemm_stages = c.gemm_path == 2 ? c.gemm_stages : 0;
   return TPA_OK;
 }
 

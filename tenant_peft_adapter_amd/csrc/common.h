@@ -43,9 +43,20 @@ struct Frag<float> {
   typedef f32x8 V;
 };
 
+// Loads through a global-address-space pointer.  Pointers read from device
+// memory (the slot records' fields) are generic to the compiler, which then
+// emits flat loads; those count against both the vector-memory and the LDS /
+// scalar counters, so every wait on them drains both.  All operands loaded
+// this way live in device global memory.
+#define TPA_GLOBAL __attribute__((address_space(1)))
+template <typename V, typename T>
+__device__ __forceinline__ V gload(const T* p) {
+  return *(const TPA_GLOBAL V*)(p);
+}
+
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::V load_frag(const T* p) {
-  return *reinterpret_cast<const typename Frag<T>::V*>(p);
+  return gload<typename Frag<T>::V>(p);
 }
 
 template <typename T>

@@ -79,7 +79,7 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        x[u][q] = *reinterpret_cast<const f32x4*>(hpart + (size_t)(s + u) * split_stride + 4 * q);
+        x[u][q] = gload<f32x4>(hpart + (size_t)(s + u) * split_stride + 4 * q);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -94,7 +94,7 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
     const float* src = hpart + (size_t)s * split_stride;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * q);
+      f32x4 x = gload<f32x4>(src + 4 * q);
       v[4 * q] += x[0];
       v[4 * q + 1] += x[1];
       v[4 * q + 2] += x[2];
@@ -107,7 +107,7 @@ template <typename T, int MB, bool HPART>
 __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fewer for wide fragments)
-  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
+  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 2 : 1) : (MB == 1 ? 4 : 2);
   const int si = slice_of(t, (int)blockIdx.x);
   const ExpandArgs& a = t.s[si];
   const int local = (int)blockIdx.x - t.first[si];
@@ -130,6 +130,34 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
     const int pi = p < p1 ? a.pinfo[p] : 0;
     row[m] = p < p1 ? (pi & 0xFFFF) : -1;
     rsd[m] = a.slots + (kind == CLS_OWNED ? tl.w : (pi >> 16));
+  }
+
+  // The rows' s, b and e pointers, then h of each row: their loads (h's the
+  // largest) go out as soon as the rows are known, ahead of the term's.
+  const float* sp[MB];
+  const float* bq[MB];
+  const float* ep[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    sp[m] = nullptr;
+    bq[m] = nullptr;
+    ep[m] = nullptr;
+    if (row[m] < 0) continue;
+    if (a.apply_scale) {
+      sp[m] = gload<const float*>(&rsd[m]->s);
+      bq[m] = gload<const float*>(&rsd[m]->b);
+    }
+    if (kind == CLS_SHARED) ep[m] = gload<const float*>(&rsd[m]->e);
+  }
+  T* out = static_cast<T*>(a.out);
+  float v[MB][16];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (row[m] < 0) continue;
+    if (HPART)
+      sum_parts16(a.hpart + (size_t)row[m] * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v[m]);
+    else
+      load_run16<T>(out + (size_t)row[m] * a.d_out + col, v[m]);
   }
 
   int K = 0;
@@ -186,55 +214,26 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   }
 
   // Epilogue: lane holds 16 consecutive columns of one row of the tile.
-  T* out = static_cast<T*>(a.out);
+  // The s, b and e values of all rows are loaded together, then combined.
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     if (row[m] < 0) continue;
-    const SlotDev& sd = *rsd[m];
-    float v[16];
-    T* orow = out + (size_t)row[m] * a.d_out + col;
-    if (HPART)
-      sum_parts16(a.hpart + (size_t)row[m] * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
-    else
-      load_run16<T>(orow, v);
-    if (a.apply_scale) {
-      if (sd.s) {
+    f32x4 s4[4], b4[4], e4[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = *reinterpret_cast<const f32x4*>(sd.s + col + 4 * q);
-          v[4 * q] *= s4[0];
-          v[4 * q + 1] *= s4[1];
-          v[4 * q + 2] *= s4[2];
-          v[4 * q + 3] *= s4[3];
-        }
-      }
-      if (sd.b) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 b4 = *reinterpret_cast<const f32x4*>(sd.b + col + 4 * q);
-          v[4 * q] += b4[0];
-          v[4 * q + 1] += b4[1];
-          v[4 * q + 2] += b4[2];
-          v[4 * q + 3] += b4[3];
-        }
-      }
+    for (int q = 0; q < 4; ++q) {
+      s4[q] = sp[m] ? gload<f32x4>(sp[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+      b4[q] = bq[m] ? gload<f32x4>(bq[m] + col + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+      e4[q] = ep[m] ? gload<f32x4>(ep[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
     }
-    if (K > 0) {
-      if (kind == CLS_SHARED) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f32x4 e4 = *reinterpret_cast<const f32x4*>(sd.e + col + 4 * b);
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[4 * b + q] += acc[b][m][q] * e4[q];
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[4 * b + q] += acc[b][m][q];
+      for (int j = 0; j < 4; ++j) {
+        float h = v[m][4 * q + j] * s4[q][j] + b4[q][j];
+        if (K > 0) h += acc[q][m][j] * e4[q][j];
+        v[m][4 * q + j] = h;
       }
-    }
-    store_run16<T>(orow, v);
+    store_run16<T>(out + (size_t)row[m] * a.d_out + col, v[m]);
   }
 }
 

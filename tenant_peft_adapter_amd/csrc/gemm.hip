@@ -200,16 +200,21 @@ __global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(Slices<GemmSlice> 
 // ------------------------------------------------------------- stream ----
 //
 // Decode base GEMM (n <= 64 rows, f16/bf16) fed by gfx950's direct global-
-// to-LDS loads.  Work-group = 4 waves; its tile is 64·NB output columns (wave
-// w owns 16·NB) by one k range of kc (split-K).  The range is walked in
-// 64-element slices: each slice of W (64·NB rows x 128 B) and of x (16·MB
-// rows x 128 B) is loaded straight into one of S LDS buffers, 8 rows x 128 B
-// (whole cache lines) per wave instruction, with no registers held while the
-// loads are in flight; S - 1 slices are in flight while one is multiplied.
-// Synchronization per slice: each wave waits for its own loads of the slice
-// (vmcnt), then a work-group barrier; the loads write LDS directly, so no
-// fence is needed.  Partials, the slice table and the side reduction are as
-// in gemm_skinny_kernel.
+// to-LDS loads.  Work-group = G k-groups of 4 waves; its tile is 64·NB output
+// columns (wave w of a group owns 16·NB) by one k range of kc (split-K),
+// which the groups share out by 64-element slices (group g takes the g-th
+// run of ceil(slices / G)).  Each group walks its run: each slice of W
+// (64·NB rows x 128 B) and of x (16·MB rows x 128 B) is loaded straight into
+// one of the group's S LDS buffers, 8 rows x 128 B (whole cache lines) per
+// wave instruction, with no registers held while the loads are in flight;
+// S - 1 slices are in flight while one is multiplied.  Per slice, each wave
+// waits for its own loads (vmcnt), then the work-group meets at a barrier
+// (every wave runs the same number of iterations); the loads write LDS
+// directly, so no fence is needed.  The groups' sums are added in LDS in
+// group order and the total is the split's fp32 partial [split][n][d_out];
+// k-groups keep as many bytes in flight per CU as separate work-groups would
+// while halving the partials written and read back.  Work-groups past the
+// GEMM's own run the shrink's split reduction, as in gemm_skinny_kernel.
 //
 // Within a 128-byte LDS row the eight 16-byte chunks are permuted, chunk c
 // stored at c ^ swz(row), so that the fragment reads (16 rows, one chunk
@@ -217,8 +222,6 @@ __global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(Slices<GemmSlice> 
 // the row (the lane's i >> 2 under perm_col), swz mixes l and h so that any
 // 8 lanes differ in (row * 128 + 16 * chunk) mod 128 and any 16 lanes in
 // that mod 256.
-constexpr int STREAM_STAGES = 3;
-
 template <int SH>
 __device__ __forceinline__ int swz(int r) {
   const int l = r & 3, h = (r >> SH) & 3;
@@ -235,13 +238,12 @@ constexpr size_t stream_stage_bytes() {
   return (size_t)(64 * NB + 16 * MB) * 128;
 }
 
-template <typename T, int MB, int NB>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
+template <typename T, int MB, int NB, int G, int S>
+__global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> t) {
   typedef typename Frag<T>::V Vt;
-  constexpr int S = STREAM_STAGES;
   constexpr int WROWS = 64 * NB;             // W rows (output columns) per work-group
   constexpr int W_INSTR = WROWS / 32;        // W loads per wave per slice (8 rows each)
-  constexpr int X_INSTR = 2 * MB;            // x loads per slice, whole work-group
+  constexpr int X_INSTR = 2 * MB;            // x loads per slice, whole group
   constexpr int XJ = (X_INSTR + 3) / 4;      // x loads per slice a wave may issue
   constexpr int SHW = 2 + log2_nb<NB>();     // swz shift of the W rows
   constexpr int STAGE = (int)stream_stage_bytes<MB, NB>();
@@ -249,20 +251,25 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
   const int si = slice_of(t, (int)blockIdx.x);
   const BaseGemmArgs& a = t.s[si].g;
   const int local = (int)blockIdx.x - t.first[si];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid >> 8, wave = (tid >> 6) & 3;
   const int col_tiles = a.d_out / WROWS;
   const int n_gemm = col_tiles * a.split;
   if (local >= n_gemm) {
-    shrink_impl::shrink_reduce_item<T>(t.s[si].side, (local - n_gemm) * 256 + tid);
+    shrink_impl::shrink_reduce_item<T>(t.s[si].side, (local - n_gemm) * 256 * G + tid);
     return;
   }
   const int col0 = (local % col_tiles) * WROWS;
   const int ks = local / col_tiles;
-  const int kbeg = ks * a.kc;
-  const int nst = min(a.d_in - kbeg, a.kc) / 64;  // slices of 64 elements
+  const int ns = max(0, min(a.d_in - ks * a.kc, a.kc)) / 64;  // slices of the range
+  const int per = (ns + G - 1) / G;                              // iterations, every wave
+  const int s_lo = min(ns, grp * per);
+  const int nst = min(ns, s_lo + per) - s_lo;                    // this group's slices
+  const int kbeg = ks * a.kc + 64 * s_lo;
   const T* W = static_cast<const T*>(a.W);
   const T* X = static_cast<const T*>(a.x);
   const T* XR = static_cast<const T*>(a.x_rot);
+  unsigned char* ring = smem + (size_t)grp * S * STAGE;
 
   // Global source of each of this lane's loads (the same for every slice
   // but for the k offset): lane = 8 · (row within the instruction) + LDS chunk.
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
     xsrc[j] = base + kbeg + 8 * (lc ^ swz<2>(rr));
   }
   auto issue = [&](int st) {
-    unsigned char* buf = smem + (size_t)(st % S) * STAGE;
+    unsigned char* buf = ring + (size_t)(st % S) * STAGE;
 #pragma unroll
     for (int j = 0; j < W_INSTR; ++j)
       __builtin_amdgcn_global_load_lds(
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
             16, 0, 0);
   };
 
-  // LDS byte offsets (within a stage) of this lane's fragment rows.
+  // LDS rows of this lane's fragments.
   const int i16 = lane & 15, g = lane >> 4;
   int arow[NB], brow[MB];
 #pragma unroll
@@ -323,11 +330,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
 #pragma unroll
   for (int st = 0; st < S - 1; ++st)
     if (st < nst) issue(st);
-  for (int it = 0; it < nst; ++it) {
+  for (int it = 0; it < per; ++it) {
     // This wave's loads of slice `it` are done once no more than (slices
     // issued after it) x W_INSTR are outstanding (a wave issues at least
     // W_INSTR per slice; loads complete in order); every wave's, after the
-    // barrier.
+    // barrier.  A group past its run only meets the barrier.
     const int younger = min(S - 2, nst - 1 - it);
     __builtin_amdgcn_sched_barrier(0);
     if (younger >= 1)
@@ -336,8 +343,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if (it >= nst) continue;
     if (it + S - 1 < nst) issue(it + S - 1);
-    const unsigned char* buf = smem + (size_t)(it % S) * STAGE;
+    const unsigned char* buf = ring + (size_t)(it % S) * STAGE;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int q = 4 * kk + g;  // 16-byte chunk of the row: k = 8q .. 8q + 7
@@ -353,6 +361,27 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(Slices<GemmSlice> t) {
 #pragma unroll
         for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
     }
+  }
+
+  if (G > 1) {
+    // Groups 1.. leave their sums in LDS (over the rings, now idle); group 0
+    // adds them in group order.
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    __syncthreads();
+    if (grp > 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) red[(((grp - 1) * 4 + wave) * NB * MB + b * MB + m) * 64 + lane] = acc[b][m];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int q = 1; q < G; ++q)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[b][m] += red[(((q - 1) * 4 + wave) * NB * MB + b * MB + m) * 64 + lane];
   }
 
   // The lane holds columns col0 + 16·NB·wave + 4·NB·g + [0, 4·NB) of row 16m + i16.
@@ -525,7 +554,19 @@ hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <typename T, int MB, int NB, int G, int S>
+hipError_t stream_launch(const Slices<GemmSlice>& t, hipStream_t s) {
+  constexpr size_t lds = (size_t)G * S * stream_stage_bytes<MB, NB>();
+  if constexpr (lds > GEMM_STREAM_MAX_LDS) {
+    return hipErrorInvalidValue;
+  } else {
+    hipLaunchKernelGGL((gemm_stream_kernel<T, MB, NB, G, S>), dim3((unsigned)t.first[t.count]), dim3(256 * G), lds,
+                       s, t);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int G, int S>
 hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
   const int mb = sl[0].g.n <= 16 ? 1 : sl[0].g.n <= 32 ? 2 : 4;
   Slices<GemmSlice> t{};
@@ -535,22 +576,27 @@ hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
     const BaseGemmArgs& a = sl[i].g;
     t.s[i] = sl[i];
     const int n_gemm = (a.d_out / (64 * nb)) * a.split;
-    const int n_side =
-        sl[i].has_side ? (int)(((long)sl[i].side.n * (sl[i].side.kmax / 4) + 255) / 256) : 0;
+    const int n_side = sl[i].has_side
+                           ? (int)(((long)sl[i].side.n * (sl[i].side.kmax / 4) + 256 * G - 1) / (256 * G))
+                           : 0;
     t.first[i + 1] = t.first[i] + n_gemm + n_side;
   }
   for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
-  const dim3 grid((unsigned)t.first[count]);
-#define TPA_ST(MBV, NBV)                                                                       \
-  if (mb == MBV && nb == NBV) {                                                               \
-    const size_t lds = STREAM_STAGES * stream_stage_bytes<MBV, NBV>();                        \
-    hipLaunchKernelGGL((gemm_stream_kernel<T, MBV, NBV>), grid, dim3(256), lds, s, t);        \
-    return hipGetLastError();                                                                 \
-  }
+#define TPA_ST(MBV, NBV) \
+  if (mb == MBV && nb == NBV) return stream_launch<T, MBV, NBV, G, S>(t, s);
   TPA_ST(1, 1) TPA_ST(2, 1) TPA_ST(4, 1)
   TPA_ST(1, 2) TPA_ST(2, 2) TPA_ST(4, 2)
   TPA_ST(1, 4) TPA_ST(2, 4) TPA_ST(4, 4)
 #undef TPA_ST
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t stream_dtype(int nb, int groups, int stages, const GemmSlice* sl, int count, hipStream_t s) {
+  if (groups == 1 && stages == 3) return stream_dispatch<T, 1, 3>(nb, sl, count, s);
+  if (groups == 1 && stages == 4) return stream_dispatch<T, 1, 4>(nb, sl, count, s);
+  if (groups == 1 && stages == 6) return stream_dispatch<T, 1, 6>(nb, sl, count, s);
+  if (groups == 2 && stages == 3) return stream_dispatch<T, 2, 3>(nb, sl, count, s);
   return hipErrorInvalidValue;
 }
 
@@ -582,7 +628,13 @@ hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* sl
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_stream(int dtype, int nb, const GemmSlice* slices, int count, hipStream_t s) {
+size_t gemm_stream_lds(int n, int nb, int groups, int stages) {
+  const int mb = n <= 16 ? 1 : n <= 32 ? 2 : 4;
+  return (size_t)groups * stages * (64 * nb + 16 * mb) * 128;
+}
+
+hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const GemmSlice* slices, int count,
+                              hipStream_t s) {
   if (count < 1 || count > MAX_SLICES || (nb != 1 && nb != 2 && nb != 4)) return hipErrorInvalidValue;
   for (int i = 0; i < count; ++i) {
     const BaseGemmArgs& a = slices[i].g;
@@ -592,8 +644,9 @@ hipError_t launch_gemm_stream(int dtype, int nb, const GemmSlice* slices, int co
         a.d_out % (64 * nb) || (long)a.split * a.kc < a.d_in)
       return hipErrorInvalidValue;
   }
-  if (dtype == 1) return stream_dispatch<f16>(nb, slices, count, s);
-  if (dtype == 2) return stream_dispatch<bf16>(nb, slices, count, s);
+  if (gemm_stream_lds(slices[0].g.n, nb, groups, stages) > GEMM_STREAM_MAX_LDS) return hipErrorInvalidValue;
+  if (dtype == 1) return stream_dtype<f16>(nb, groups, stages, slices, count, s);
+  if (dtype == 2) return stream_dtype<bf16>(nb, groups, stages, slices, count, s);
   return hipErrorInvalidValue;
 }
 

@@ -47,6 +47,8 @@ struct PlanArgs {
   int32_t* flag;       // layer's sticky invalid-slot flag
   int32_t* pinfo;      // [n]: (slot << 16) | row of plan position p
   int32_t max_tiles;   // tile lists are padded to this length with kind / slot -1
+  int32_t* sh_tiles;   // [4 * max_sh_tiles]: the shared-term tiles again, on their own
+  int32_t max_sh_tiles;  // ceil(n / tile_rows); padded like tiles
 };
 constexpr int PLAN_MAX_ROWS = 8192;
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
@@ -94,14 +96,17 @@ hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t strea
 struct ShrinkArgs {
   const void* x;
   const int32_t* pinfo;    // (slot << 16) | row by plan position
-  const int32_t* tiles;    // padded with kind -1 to max_tiles
+  const int32_t* tiles;    // plan tiles, owned-term tiles first, padded with kind -1
+  const int32_t* sh_tiles; // the shared-term tiles, padded with kind -1
   const SlotDev* slots;
   const void* vera_At;     // [r_v][d_in] or null
   int32_t r_v;
   int32_t n, d_in;
   int32_t kmax;            // row stride of part and v
-  int32_t max_tiles;
-  int32_t nblk;            // 16-column blocks per tile: kmax / 16
+  // Work items: own_tiles x own_nblk x split on the first own_tiles entries of
+  // tiles (bound on the owned-term tiles; 16-column blocks of the largest
+  // owned rank), then sh_ntiles x sh_nblk x split on sh_tiles (r_v / 16).
+  int32_t own_tiles, own_nblk, sh_ntiles, sh_nblk;
   int32_t split, kc;       // k ranges (kc a multiple of 32)
   float* part;
   void* v;
@@ -128,8 +133,12 @@ struct GemmSlice {
 hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* slices, int count,
                               hipStream_t stream);
 // The same GEMM with W and x streamed into LDS by direct loads (f16 / bf16;
-// d_in and kc multiples of 64).
-hipError_t launch_gemm_stream(int dtype, int nb, const GemmSlice* slices, int count, hipStream_t stream);
+// d_in and kc multiples of 64): `groups` k-groups of 4 waves per work-group
+// (1 or 2), `stages` LDS buffers per group (groups 1: 3, 4 or 6; groups 2: 3).
+constexpr size_t GEMM_STREAM_MAX_LDS = 160 * 1024;
+size_t gemm_stream_lds(int n, int nb, int groups, int stages);
+hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const GemmSlice* slices, int count,
+                              hipStream_t stream);
 // The shrink's split reduction on its own (when the GEMM cannot carry it).
 hipError_t launch_shrink_reduce(int dtype, const ShrinkArgs& a, hipStream_t stream);
 

@@ -13,7 +13,8 @@
 // workspace: perm, pinfo ((slot << 16) | row per position, so later kernels
 // get both with one load), row_slot, rot_pos (position of a row's rotated
 // copy, or -1), segments, tiles and OFT tiles (padded to max_tiles with
-// kind / slot -1, so later kernels need no counter), counters.
+// kind / slot -1, so later kernels need no counter), the shared-term tiles
+// again in a list of their own (padded to ceil(n / tile_rows)), counters.
 //
 // One work-group does the whole plan with everything in LDS: the only global
 // reads are slot_of_row and the slot records it points to, the rest are
@@ -209,12 +210,13 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
     const int p0 = s_cls[c], p1 = s_cls[c + 1];
     const int cnt = (p1 - p0 + TM - 1) / TM;
     for (int q = tid; q < cnt; q += T) {
-      int* t = a.tiles + 4 * (nt + q);
-      t[0] = p0 + q * TM;
-      t[1] = min(p0 + (q + 1) * TM, p1);
-      t[2] = c;
-      t[3] = -1;
+      const int4 tl = make_int4(p0 + q * TM, min(p0 + (q + 1) * TM, p1), c, -1);
+      *reinterpret_cast<int4*>(a.tiles + 4 * (nt + q)) = tl;
+      if (c == CLS_SHARED) *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = tl;
     }
+    if (c == CLS_SHARED)
+      for (int q = cnt + tid; q < a.max_sh_tiles; q += T)
+        *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = make_int4(0, 0, -1, -1);
     nt += cnt;
   }
   // Pad both tile lists to max_tiles so later kernels need no counter.

@@ -68,7 +68,7 @@ PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of) {
   ps.oft_bg = 1;
   if (sh) {
     ps.sh = *sh;
-    const long items = (long)sh->max_tiles * sh->nblk * sh->split;
+    const long items = ((long)sh->own_tiles * sh->own_nblk + (long)sh->sh_ntiles * sh->sh_nblk) * sh->split;
     ps.n_shrink_wg = (int)((items + THREADS / 64 - 1) / (THREADS / 64));
   }
   if (of) {

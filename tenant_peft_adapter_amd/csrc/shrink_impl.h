@@ -12,7 +12,7 @@
 namespace tpa {
 namespace shrink_impl {
 
-// // One wave per work item (plan tile, 16 factor columns, k range): factor
+// One wave per work item (plan tile, 16 factor columns, k range): factor
 // rows and the tile's x rows stream straight into MFMA registers (8 k steps
 // of loads issued together), no LDS and no barriers, so the whole GPU takes
 // part even when one tile (VeRA's shared factor) holds most of the work.
@@ -27,18 +27,30 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
   constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
   const int i16 = lane & 15, g = lane >> 4;
   const int ks = item % a.split;
-  const int rest = item / a.split;
-  const int cb = rest % a.nblk;
-  const int t = rest / a.nblk;
-  if (t >= a.max_tiles) return;
-  const int* tile = a.tiles + 4 * t;
-  const int kind = tile[2];
-  if (kind != CLS_OWNED && kind != CLS_SHARED) return;
-  const int p0 = tile[0], p1 = tile[1];
+  int rest = item / a.split;
+  const int own_items = a.own_tiles * a.own_nblk;
+  const int* tile;
+  int cb, want;
+  if (rest < own_items) {
+    cb = rest % a.own_nblk;
+    tile = a.tiles + 4 * (rest / a.own_nblk);
+    want = CLS_OWNED;
+  } else {
+    rest -= own_items;
+    const int t = rest / a.sh_nblk;
+    if (t >= a.sh_ntiles) return;
+    cb = rest % a.sh_nblk;
+    tile = a.sh_tiles + 4 * t;
+    want = CLS_SHARED;
+  }
+  const int4 tl = *reinterpret_cast<const int4*>(tile);
+  const int kind = tl.z;
+  if (kind != want) return;  // past the real tiles of that kind
+  const int p0 = tl.x, p1 = tl.y;
   const T* F;
   int N;
   if (kind == CLS_OWNED) {
-    const SlotDev& sd = a.slots[tile[3]];
+    const SlotDev& sd = a.slots[tl.w];
     F = static_cast<const T*>(sd.A);
     N = sd.rank;
   } else {
@@ -112,12 +124,12 @@ __device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx)
   for (; s + 8 <= a.split; s += 8) {
     f32x4 t[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(s + u) * stride);
+    for (int u = 0; u < 8; ++u) t[u] = gload<f32x4>(src + (size_t)(s + u) * stride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) v += t[u];
   }
-  for (; s < a.split; ++s) v += *reinterpret_cast<const f32x4*>(src + (size_t)s * stride);
-  if (cls == CLS_SHARED) v = v * *reinterpret_cast<const f32x4*>(sd.d + col);
+  for (; s < a.split; ++s) v += gload<f32x4>(src + (size_t)s * stride);
+  if (cls == CLS_SHARED) v = v * gload<f32x4>(sd.d + col);
   T* dst = static_cast<T*>(a.v) + (size_t)p * a.kmax + col;
 #pragma unroll
   for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(v[q]);

@@ -134,19 +134,21 @@ def make_projection(rng, name, d_in, d_out, dtype, n):
             "W": W, "x": x, "shared": None, "adapters": {}}
 
 
-def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False):
-    """Tiny single layer: W [256 x 256], n rows assigned uniformly at random
-    to five tenants, one per method (LoRA r8, DoRA r8, (IA)3, VeRA with a
-    shared rank-32 pair, OFT with blocks of 32).  Slots 1..5 in that order;
-    with_identity also draws rows onto slot 0 (base only)."""
+def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False, d_out=None):
+    """Tiny single layer: W [d x d] (d_out x d when d_out is given), n rows
+    assigned uniformly at random to five tenants, one per method (LoRA r8,
+    DoRA r8, (IA)3, VeRA with a shared rank-32 pair, OFT with blocks of 32).
+    Slots 1..5 in that order; with_identity also draws rows onto slot 0 (base
+    only)."""
     rng = np.random.default_rng(seed)
-    p = make_projection(rng, "tiny", d, d, dtype, n)
-    p["shared"] = _vera_shared(rng, d, d, 32, dtype)
+    do = d if d_out is None else d_out
+    p = make_projection(rng, "tiny", d, do, dtype, n)
+    p["shared"] = _vera_shared(rng, d, do, 32, dtype)
     p["adapters"] = {
-        1: _lora(rng, d, d, 8, dtype),
+        1: _lora(rng, d, do, 8, dtype),
         2: _dora(rng, p["W"], 8, dtype),
-        3: _ia3(rng, d),
-        4: _vera(rng, 32, d),
+        3: _ia3(rng, do),
+        4: _vera(rng, 32, do),
         5: _oft(rng, d, 32),
     }
     lo = 0 if with_identity else 1
