@@ -201,14 +201,14 @@ def calibrate(torch):
     return beta, lam
 
 
-PROFILE = os.path.join(ROOT, "profiles", "gemm_skinny_decoder_layer_mixed.md")
+PROFILE = os.path.join(ROOT, "profiles", "gemm_stream_decoder_layer_mixed.md")
 
 
-def profiled_traffic(kernel):
+def profiled_traffic(kernel, config):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC
-    summary, or None when the summary covers another kernel or the kernel's
-    sources changed since the counters were taken (sha256 over the files it
-    lists)."""
+    summary, or None when the summary covers another kernel or launch
+    configuration, or the kernel's sources changed since the counters were
+    taken (sha256 over the files it lists)."""
     import hashlib
     import re
     try:
@@ -216,10 +216,11 @@ def profiled_traffic(kernel):
     except OSError:
         return None
     k = re.search(r"^kernel: (\S+)", text, re.M)
+    c = re.search(r"^config: (.+)$", text, re.M)
     sha = re.search(r"^source_sha256: (\w+)", text, re.M)
     files = re.search(r"^\(sha256 over ([^;]+);", text, re.M)
     val = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
-    if not (k and sha and files and val) or k.group(1) != kernel:
+    if not (k and c and sha and files and val) or k.group(1) != kernel or c.group(1).strip() != config:
         return None
     h = hashlib.sha256()
     for f in files.group(1).split(", "):
@@ -301,10 +302,12 @@ def main():
     shapes = [bm.shape_of(n, p["d_in"], p["d_out"], wl["slot_of_row"], p["adapters"], q=2, r_v=256)
               for p in wl["projections"]]
     kb = [bm.kernel_bytes(s) for s in shapes]
-    # An event pair with no kernel between (stage 3 on this path) measures the
-    # pairs' own cost; it is taken off each kernel's interval.
+    # Kernel times are the raw event intervals, which agree with rocprofv3's
+    # per-dispatch durations.  An event pair with no kernel between (stage 3
+    # on this path) is reported for reference: its interval overlaps a
+    # kernel's start-up, so it is not taken off.
     pair_cost = sum(st[3] for st in stages) / len(stages) * 1e-6
-    gemm_t = [max(st[2] * 1e-6 - pair_cost, 1e-9) for st in stages]
+    gemm_t = [max(st[2] * 1e-6, 1e-9) for st in stages]
     # Dominant kernel: the base-GEMM launch with the most algorithmic bytes.
     # A unit's decode GEMM instance takes the column-block width of its
     # widest projection.
@@ -314,14 +317,15 @@ def main():
     widest = max(units[du], key=lambda i: wl["projections"][i]["d_out"])
     cfg = layers[widest].config(n)
     dom_name = {0: "gemm_skinny_kernel<f16,%d,%d,%d>" % (mb, cfg["gemm_nb"], cfg["gemm_groups"]),
-                2: "gemm_stream_kernel<f16,%d,%d>" % (mb, cfg["gemm_nb"])}.get(cfg["gemm_path"],
-                                                                             "gemm_tiled_kernel<f16>")
+                2: "gemm_stream_kernel<f16,%d,%d,%d,%d>" % (mb, cfg["gemm_nb"], cfg["gemm_groups"], cfg["gemm_stages"])
+                }.get(cfg["gemm_path"], "gemm_tiled_kernel<f16>")
+    dom_cfg = "nb=%d groups=%d stages=%d kc=%d split=%d" % (cfg["gemm_nb"], cfg["gemm_groups"], cfg["gemm_stages"],
+                                                             cfg["gemm_kc"], cfg["gemm_split"])
     dom_bytes, dom_time = gemm_bytes[du], gemm_t[du]
-    dom_time_raw = stages[du][2] * 1e-6
     gemm_bytes_all = sum(gemm_bytes)
     gemm_time_all = sum(gemm_t)
     adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes)
-    adapter_time = sum(st[1] + st[4] for st in stages) * 1e-6 - 2 * pair_cost * len(stages)
+    adapter_time = sum(st[1] + st[4] for st in stages) * 1e-6
     adapter_launches = len(step.plans) + 2 * len(units)
     predicted = bm.predict_time(gemm_time_all, adapter_bytes, adapter_launches, beta, lam)
 
@@ -365,9 +369,9 @@ def main():
         "roofline": {
             "kernel": "%s (base GEMM of %s in one launch)" % (dom_name, ", ".join(names[i] for i in units[du])),
             "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-            "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": profiled_traffic(dom_name),
+            "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": profiled_traffic(dom_name, dom_cfg),
             "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
-            "us_per_launch_raw_events": dom_time_raw * 1e6, "us_event_pair_cost": pair_cost * 1e6,
+            "us_event_pair_cost": pair_cost * 1e6, "config": dom_cfg,
         },
         "base_gemm": {"bytes_per_step": gemm_bytes_all, "us_per_step": gemm_time_all * 1e6,
                       "GBps": gemm_bytes_all / gemm_time_all / 1e9},
