@@ -7,10 +7,10 @@ rank-256 pair, OFT with blocks of 32 on q/k/v -- rows shuffled so segments
 are not contiguous.  Inputs are seeded synthetic data of those shapes.
 
 A step is one forward of all seven projections, captured in one HIP graph:
-the row plan of the batch (built once per group of projections whose slot
-classes agree: q, k, v and o, gate, up, down), then for each projection the
-shrink with OFT's rotation, the base GEMM (carrying the shrink's split
-reduction) and the expand.  `value` is adapted-
+the row plan of the batch (built once and used by every projection it
+accepts: here all seven), then for each projection the shrink with OFT's
+rotation, the base GEMM (carrying the shrink's split reduction) and the
+expand.  `value` is adapted-
 layer rows/s: rows through one adapted projection per second, i.e.
 7 · n / t_step.
 
@@ -65,19 +65,26 @@ def build_step(wl, torch):
         outs.append(torch.empty((n, p["d_out"]), dtype=torch.float16, device="cuda"))
         wss.append(L.workspace(n))
 
-    # Projections whose slot classes agree share one row plan per step (q, k
-    # and v here; o, gate, up and down), built by the first of them.  The
-    # projections of one fused layer -- q, k, v and gate, up, which read the
-    # same input in the model -- run as one group (one launch per kernel);
-    # o and down depend on earlier results in the model and run alone.
+    # One row plan per step serves every projection it accepts (same slot
+    # classes, and the builder's OFT flags or no rotation at all: here q's
+    # plan serves all seven, OFT adapting q, k and v only).  The projections
+    # of one fused layer -- q, k, v and gate, up, which read the same input in
+    # the model -- run as one group (one launch per kernel); o and down
+    # depend on earlier results in the model and run alone.
     from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
     names = [p["name"] for p in wl["projections"]]
     fused = [("q", "k", "v"), ("gate", "up")]
-    sig_groups = {}
+    owner = []   # (RowPlan, builder index, [layer indices])
     for i, L in enumerate(layers):
-        sig_groups.setdefault(L.plan_signature(), []).append(i)
+        for rp, b, idx in owner:
+            if rp.accepts(L):
+                idx.append(i)
+                break
+        else:
+            rp = RowPlan(L, n).build(L, sor)
+            owner.append((rp, i, [i]))
     plans = []
-    for idx in sig_groups.values():
+    for rp, b, idx in owner:
         launch_groups, seen = [], set()
         for i in idx:
             if i in seen:
@@ -89,11 +96,11 @@ def build_step(wl, torch):
             seen.update(members)
             launch_groups.append((members, LayerGroup([layers[j] for j in members], n) if len(members) > 1
                                   else None))
-        plans.append((RowPlan(layers[idx[0]], n), idx, launch_groups))
+        plans.append((rp, b, launch_groups))
 
     def step():
-        for plan, idx, launch_groups in plans:
-            plan.build(layers[idx[0]], sor)
+        for plan, b, launch_groups in plans:
+            plan.build(layers[b], sor)
             for members, grp in launch_groups:
                 if grp is None:
                     layers[members[0]].forward_planned(plan, xs[members[0]], out=outs[members[0]],

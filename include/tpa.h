@@ -187,14 +187,20 @@ tpa_status tpa_layer_forward(tpa_layer* layer, const void* x_dev, const int32_t*
  *     invalid slots;
  *   tpa_layer_forward_planned(layer, plan, x, out, ws, ws_bytes, s): as
  *     tpa_layer_forward for the plan's rows, without the plan kernel; -1 if
- *     layer's slot classes, slot count or tiling differ from the building
- *     layer's (any load or unload changes them).  ws as for
- *     tpa_layer_forward.
+ *     the plan does not accept the layer (below) or its tiling differs (any
+ *     load or unload can change that).  ws as for tpa_layer_forward;
+ *   tpa_plan_accepts(plan, layer, &ok): host only; ok = 1 when the plan is
+ *     built and layer's slots have the building layer's term classes and
+ *     either the same OFT flags or no OFT rotation at all (such a layer reads
+ *     neither the OFT tiles nor the rotated-row map), and the same slot
+ *     count.  In a decoder layer whose OFT tenants adapt q, k and v only, a
+ *     plan built by q serves all seven projections.
  * The tpa_plan handle is host memory (create/destroy); it holds no device
  * memory. */
 typedef struct tpa_plan tpa_plan;
 /* Layers whose signatures are equal can share a plan of the same rows. */
 tpa_status tpa_layer_plan_signature(const tpa_layer* layer, uint64_t* sig);
+tpa_status tpa_plan_accepts(const tpa_plan* plan, const tpa_layer* layer, int32_t* ok);
 tpa_status tpa_plan_create(tpa_plan** out);
 tpa_status tpa_plan_destroy(tpa_plan* plan);
 tpa_status tpa_plan_size(const tpa_layer* layer, int32_t n_max, size_t* bytes);
@@ -205,10 +211,10 @@ tpa_status tpa_layer_forward_planned(tpa_layer* layer, const tpa_plan* plan, con
 
 /* Projections of one fused layer (q, k and v; gate and up) forwarded in one
  * launch per kernel (P1 §5.2: one launch covers all slices of a layer), with
- * a plan built for their common slot classes.  count <= 4; layers[i] with
+ * a plan that accepts each of them.  count <= 4; layers[i] with
  * x[i] [n][d_in_i], out[i] [n][d_out_i], ws[i] of ws_bytes[i] bytes (at least
- * tpa_group_workspace_size's bytes[i] for this group; 256-byte aligned).  All
- * layers must have the plan's signature, one dtype and one device.  On the
+ * tpa_group_workspace_size's bytes[i] for this group; 256-byte aligned).  The
+ * plan must accept every layer; one dtype and one device.  On the
  * decode path (n <= 64) the group shares one base-GEMM configuration (column
  * blocks per work-group and k range), so results may differ from separate
  * forwards by the rounding of a different split-K order.  Stage events are

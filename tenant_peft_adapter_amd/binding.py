@@ -84,6 +84,7 @@ def _load():
         "tpa_layer_set_option": [vp, i32, i32],
         "tpa_layer_config": [vp, i32, P(tpa_config)],
         "tpa_layer_plan_signature": [vp, P(ctypes.c_uint64)],
+        "tpa_plan_accepts": [vp, vp, P(i32)],
         "tpa_plan_create": [P(vp)],
         "tpa_plan_destroy": [vp],
         "tpa_plan_size": [vp, i32, P(sz)],
@@ -201,6 +202,12 @@ def tpa_layer_plan_signature(layer):
     out = ctypes.c_uint64()
     _check(_lib.tpa_layer_plan_signature(layer, ctypes.byref(out)))
     return out.value
+
+
+def tpa_plan_accepts(plan, layer):
+    out = ctypes.c_int32()
+    _check(_lib.tpa_plan_accepts(plan, layer, ctypes.byref(out)))
+    return bool(out.value)
 
 
 def tpa_plan_create():

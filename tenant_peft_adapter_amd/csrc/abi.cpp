@@ -187,13 +187,15 @@ struct tpa_layer {
   int opt[9] = {-1, -1, -1, -1, -1, 0, -1, -1, -1};
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
-  uint64_t plan_sig = 0;  // hash of every slot's (term class, has R): what a row plan depends on
+  uint64_t plan_sig = 0;   // hash of every slot's (term class, has R): what a row plan depends on
+  uint64_t class_sig = 0;  // the same over term classes only
+  int n_rot = 0;           // loaded slots with an OFT rotation
 };
 
 // A row plan built by one layer and shared by the layers whose slot classes
 // match (same signature), so a batch is grouped once for all of them.
 struct tpa_plan {
-  uint64_t sig = 0;
+  uint64_t sig = 0, class_sig = 0;
   int max_slots = 0, n = 0, tile_rows = 0;
   const char* dev = nullptr;
   size_t bytes = 0;
@@ -399,21 +401,35 @@ tpa_status upload_slot(tpa_layer* L, int slot, hipStream_t s) {
 // FNV-1a over every slot's (term class, has R): the plan depends on nothing
 // else of the slot table.
 void update_plan_sig(tpa_layer* L) {
-  uint64_t h = 1469598103934665603ull;
-  auto mix = [&](uint64_t v) {
+  uint64_t h = 1469598103934665603ull, hc = h;
+  auto mix = [](uint64_t& x, uint64_t v) {
     for (int i = 0; i < 8; ++i) {
-      h ^= (v >> (8 * i)) & 0xFF;
-      h *= 1099511628211ull;
+      x ^= (v >> (8 * i)) & 0xFF;
+      x *= 1099511628211ull;
     }
   };
-  mix((uint64_t)L->max_slots);
-  int rmax = 0;
+  mix(h, (uint64_t)L->max_slots);
+  mix(hc, (uint64_t)L->max_slots);
+  int rmax = 0, nrot = 0;
   for (const SlotDev& sd : L->slots_host) {
-    mix((uint64_t)(uint32_t)sd.cls | ((uint64_t)sd.has_R << 32));
+    mix(h, (uint64_t)(uint32_t)sd.cls | ((uint64_t)sd.has_R << 32));
+    mix(hc, (uint64_t)(uint32_t)sd.cls);
     if (sd.cls == tpa::CLS_OWNED) rmax = std::max(rmax, (int)sd.rank);
+    if (sd.cls >= 0 && sd.has_R) ++nrot;
   }
   L->plan_sig = h;
+  L->class_sig = hc;
   L->max_owned_rank = rmax;
+  L->n_rot = nrot;
+}
+
+// A plan serves a layer whose slots have the builder's term classes and
+// rotation flags, or the builder's term classes and no rotation at all: the
+// order of rows and the tiles depend only on the classes, and a layer
+// without rotated slots reads neither the OFT tiles nor rot_pos.
+bool plan_accepts(const tpa_plan* plan, const tpa_layer* L) {
+  if (plan->max_slots != L->max_slots) return false;
+  return plan->sig == L->plan_sig || (plan->class_sig == L->class_sig && L->n_rot == 0);
 }
 
 // Bounds on what a plan of n rows holds for this layer's loaded slots (the
@@ -1086,6 +1102,13 @@ tpa_status tpa_layer_plan_signature(const tpa_layer* L, uint64_t* sig) {
   return TPA_OK;
 }
 
+tpa_status tpa_plan_accepts(const tpa_plan* plan, const tpa_layer* L, int32_t* ok) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!plan || !ok) return fail(TPA_ERR_INVALID, "null argument");
+  *ok = plan->built && plan_accepts(plan, L) ? 1 : 0;
+  return TPA_OK;
+}
+
 tpa_status tpa_plan_create(tpa_plan** out) {
   if (!out) return fail(TPA_ERR_INVALID, "null output");
   *out = new tpa_plan();
@@ -1124,6 +1147,7 @@ tpa_status tpa_plan_build(tpa_plan* plan, tpa_layer* L, const int32_t* sor, int3
     TPA_HIP(tpa::launch_plan(p, static_cast<hipStream_t>(stream)));
   }
   plan->sig = L->plan_sig;
+  plan->class_sig = L->class_sig;
   plan->max_slots = L->max_slots;
   plan->n = n;
   plan->tile_rows = c.tile_rows;
@@ -1143,7 +1167,7 @@ tpa_status tpa_layer_forward_planned(tpa_layer* L, const tpa_plan* plan, const v
   if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(TPA_ERR_INVALID, "workspace must be 256-byte aligned");
   if (x == out) return fail(TPA_ERR_INVALID, "out may not alias x");
   const Config c = choose_config(L, n);
-  if (plan->sig != L->plan_sig || plan->max_slots != L->max_slots || plan->tile_rows != c.tile_rows)
+  if (!plan_accepts(plan, L) || plan->tile_rows != c.tile_rows)
     return fail(TPA_ERR_INVALID, "plan was built for a layer with other slot classes or tiling");
   const Layout y = make_layout(L, n, c);
   if (ws_bytes < y.total) return fail(TPA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
@@ -1184,8 +1208,7 @@ tpa_status tpa_group_forward_planned(tpa_layer* const* layers, int32_t count, co
     if (tpa_status st = check_layer(L)) return st;
     if (L->dtype != layers[0]->dtype || L->device != layers[0]->device)
       return fail(TPA_ERR_INVALID, "group layers differ in dtype or device");
-    if (plan->sig != L->plan_sig || plan->max_slots != L->max_slots)
-      return fail(TPA_ERR_INVALID, "plan was built for a layer with other slot classes");
+    if (!plan_accepts(plan, L)) return fail(TPA_ERR_INVALID, "plan was built for a layer with other slot classes");
   }
   const int n = plan->n;
   if (n == 0) return TPA_OK;

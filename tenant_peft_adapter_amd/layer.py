@@ -131,6 +131,10 @@ class RowPlan:
         self.buf = torch.empty(max(size, 256), dtype=torch.uint8, device=layer.W.device)
         self.n = 0
 
+    def accepts(self, layer):
+        """Whether layer may forward this plan's rows (tpa_plan_accepts)."""
+        return B.tpa_plan_accepts(self.handle, layer.handle)
+
     def build(self, layer, slot_of_row):
         self.n = slot_of_row.numel()
         B.tpa_plan_build(self.handle, layer.handle, slot_of_row.data_ptr(), self.n, self.buf.data_ptr(),

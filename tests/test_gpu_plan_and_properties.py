@@ -260,8 +260,9 @@ def test_probes_copy_and_launch():
 def test_shared_plan_forward_matches_plain_forward():
     """A row plan built by one projection and reused by another with the same
     slot classes gives the same output, bit for bit, as each projection's own
-    forward; a projection with other slot classes, or one whose slot table
-    changed after the build, is refused."""
+    forward; so does a projection with the same classes and no OFT rotation
+    (OFT tenants are the identity on o); a projection with other slot
+    classes, or one whose slot table changed after the build, is refused."""
     from tenant_peft_adapter_amd import binding as B
     from tenant_peft_adapter_amd.layer import RowPlan
     wl = synth.decoder_layer_mixed(shapes=(("q", 4096, 4096), ("k", 4096, 1024), ("o", 4096, 4096)))
@@ -273,17 +274,29 @@ def test_shared_plan_forward_matches_plain_forward():
     sor = torch.tensor(wl["slot_of_row"]).cuda()
     n = sor.numel()
     plan = RowPlan(Lq, n).build(Lq, sor)
-    for L, p in ((Lq, pq), (Lk, pk)):
+    assert plan.accepts(Lq) and plan.accepts(Lk) and plan.accepts(Lo)
+    for L, p in ((Lq, pq), (Lk, pk), (Lo, po)):
         x = torch.tensor(p["x"]).half().cuda()
         want = L.forward(x, sor).clone()
         got = L.forward_planned(plan, x)
         torch.cuda.synchronize()
         assert torch.equal(got, want), p["name"]
-    xo = torch.tensor(po["x"]).half().cuda()
+    # o's plan has no rotation flags: q (which rotates) may not use it.
+    plan_o = RowPlan(Lo, n).build(Lo, sor)
+    assert plan_o.accepts(Lo) and not plan_o.accepts(Lq)
     with pytest.raises(B.TpaError) as e:
-        Lo.forward_planned(plan, xo)
+        Lq.forward_planned(plan_o, torch.tensor(pq["x"]).half().cuda())
+    assert e.value.code == -1
+    plan_o.close()
+    # A layer whose owned slot 1 is loaded as the identity has other classes.
+    owned = [s for s, ad in po["adapters"].items() if ad["method"] in ("lora", "dora")][0]
+    Lx = make_layer(po, max_slots=32, max_rank=256, skip=(owned,))
+    assert not plan.accepts(Lx)
+    with pytest.raises(B.TpaError) as e:
+        Lx.forward_planned(plan, torch.tensor(po["x"]).half().cuda())
     assert e.value.code == -1
     Lk.unload(1)
+    assert not plan.accepts(Lk)
     with pytest.raises(B.TpaError) as e:
         Lk.forward_planned(plan, torch.tensor(pk["x"]).half().cuda())
     assert e.value.code == -1
