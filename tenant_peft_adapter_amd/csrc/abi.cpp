@@ -165,6 +165,7 @@ struct Layout {
   int max_tiles;
   size_t sh_tiles;
   int max_sh_tiles;
+  size_t tile_rows_w, sh_rows_w, oft_rows_w;
 };
 
 }  // namespace
@@ -258,6 +259,16 @@ void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stage
   }
 }
 
+// Shrink: one wave per (tile, 16 factor columns, k range of ~256): short
+// waves, as its launch is on the critical path.
+void set_shrink_split(const tpa_layer* L, Config* c) {
+  int ssplit = L->opt[TPA_OPT_SHRINK_SPLIT];
+  if (ssplit <= 0) ssplit = std::max(1, std::min(28, L->d_in / 256));
+  ssplit = std::min(ssplit, L->d_in / 32);
+  c->shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
+  c->shrink_split = (L->d_in + c->shrink_kc - 1) / c->shrink_kc;
+}
+
 Config choose_config(const tpa_layer* L, int n) {
   Config c{};
   c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : (n <= 256 ? 16 : 64);
@@ -312,13 +323,8 @@ Config choose_config(const tpa_layer* L, int n) {
     c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
   }
-  // Shrink: one wave per (tile, 16 factor columns, k range of ~256-512).
-  int ssplit = L->opt[TPA_OPT_SHRINK_SPLIT];
-  if (ssplit <= 0) ssplit = std::max(1, std::min(28, L->d_in / 256));
-  ssplit = std::min(ssplit, L->d_in / 32);
-  c.shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
-  c.shrink_split = (L->d_in + c.shrink_kc - 1) / c.shrink_kc;
   c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];
+  set_shrink_split(L, &c);
   return c;
 }
 
@@ -346,6 +352,9 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.oft_tiles = take(16 * (size_t)y.max_tiles);
   y.max_sh_tiles = (n + c.tile_rows - 1) / c.tile_rows;
   y.sh_tiles = take(16 * (size_t)y.max_sh_tiles);
+  y.tile_rows_w = take(4 * (size_t)c.tile_rows * y.max_tiles);
+  y.sh_rows_w = take(4 * (size_t)c.tile_rows * y.max_sh_tiles);
+  y.oft_rows_w = take(4 * (size_t)c.tile_rows * y.max_tiles);
   y.counts = take(4 * tpa::CNT_WORDS);
   y.plan_end = off;
   y.x_rot = take((size_t)n * L->d_in * esz);
@@ -376,6 +385,9 @@ tpa::PlanArgs plan_args(tpa_layer* L, const int32_t* sor, int n, char* ws, const
   p.tiles = reinterpret_cast<int32_t*>(ws + y.tiles);
   p.oft_tiles = reinterpret_cast<int32_t*>(ws + y.oft_tiles);
   p.sh_tiles = reinterpret_cast<int32_t*>(ws + y.sh_tiles);
+  p.tile_rows_w = reinterpret_cast<int32_t*>(ws + y.tile_rows_w);
+  p.sh_rows_w = reinterpret_cast<int32_t*>(ws + y.sh_rows_w);
+  p.oft_rows_w = reinterpret_cast<int32_t*>(ws + y.oft_rows_w);
   p.max_sh_tiles = y.max_sh_tiles;
   p.counts = reinterpret_cast<int32_t*>(ws + y.counts);
   p.flag = L->flag_dev;
@@ -919,6 +931,8 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       sh[i].d_in = L->d_in;
       sh[i].kmax = L->kmax;
       sh[i].sh_tiles = p.sh_tiles;
+      sh[i].tile_rows_w = p.tile_rows_w;
+      sh[i].sh_rows_w = p.sh_rows_w;
       sh[i].own_tiles = owned_tile_bound(L, n, tile_rows, y.max_tiles);
       sh[i].own_nblk = std::max(1, (L->max_owned_rank + 15) / 16);
       sh[i].sh_ntiles = L->n_vera > 0 ? y.max_sh_tiles : 0;
@@ -930,8 +944,8 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     }
     of[i] = tpa::OftArgs{};
     of[i].x = sl[i].x;
-    of[i].perm = p.perm;
     of[i].oft_tiles = p.oft_tiles;
+    of[i].oft_rows_w = p.oft_rows_w;
     of[i].slots = L->slots_dev;
     of[i].x_rot = sl[i].w + y.x_rot;
     of[i].d_in = L->d_in;
@@ -1033,8 +1047,8 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     e[i].out = sl[i].out;
     e[i].hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart);
     e[i].hsplit = c.gemm_split;
-    e[i].pinfo = p.pinfo;
     e[i].tiles = p.tiles;
+    e[i].tile_rows_w = p.tile_rows_w;
     e[i].slots = L->slots_dev;
     e[i].vera_Bt = L->vera_Bt;
     e[i].r_v = L->r_v;

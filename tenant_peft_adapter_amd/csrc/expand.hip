@@ -112,11 +112,16 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   const ExpandArgs& a = t.s[si];
   const int local = (int)blockIdx.x - t.first[si];
   const int ncb = a.d_out / 64;
-  const int4 tl = *reinterpret_cast<const int4*>(a.tiles + 4 * (local / ncb));
-  const int p0 = tl.x, p1 = tl.y, kind = tl.z;
-  if (kind < 0) return;  // padding past the plan's last tile
   const int lane = threadIdx.x;
   const int i16 = lane & 15, g = lane >> 4;
+  // Tile header and the rows' words load side by side.
+  const int ti = local / ncb;
+  const int4 tl = *reinterpret_cast<const int4*>(a.tiles + 4 * ti);
+  int rw[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) rw[m] = a.tile_rows_w[(size_t)ti * 16 * MB + 16 * m + i16];
+  const int p0 = tl.x, kind = tl.z;
+  if (kind < 0) return;  // padding past the plan's last tile
   const int n0 = (local % ncb) * 64;
   const int col = n0 + 16 * g;
 
@@ -126,10 +131,8 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   const SlotDev* rsd[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    const int pi = p < p1 ? a.pinfo[p] : 0;
-    row[m] = p < p1 ? (pi & 0xFFFF) : -1;
-    rsd[m] = a.slots + (kind == CLS_OWNED ? tl.w : (pi >> 16));
+    row[m] = rw[m] >= 0 ? (rw[m] & 0xFFFF) : -1;
+    rsd[m] = a.slots + (kind == CLS_OWNED ? tl.w : rw[m] >= 0 ? (rw[m] >> 16) : 0);
   }
 
   // The rows' s, b and e pointers, then h of each row: their loads (h's the
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const int p = p0 + 16 * m + i16;
-      vv[m] = p < p1;
+      vv[m] = rw[m] >= 0;
       vp[m] = V + (size_t)(vv[m] ? p : 0) * a.kmax + 8 * g;
     }
     for (int k = 0; k < K; k += 32 * U) {

@@ -532,9 +532,7 @@ hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
     const BaseGemmArgs& a = sl[i].g;
     t.s[i] = sl[i];
     const int n_gemm = (a.d_out / (64 * nb)) * a.split;
-    const int n_side = sl[i].has_side
-                           ? (int)(((long)sl[i].side.n * (sl[i].side.kmax / 4) + 256 * G - 1) / (256 * G))
-                           : 0;
+    const int n_side = side_workgroups(sl[i], 256 * G);
     t.first[i + 1] = t.first[i] + n_gemm + n_side;
     const size_t stage = (size_t)16 * mb * (a.kc + 16 / sizeof(T)) * sizeof(T);
     const size_t red = G > 1 ? (size_t)4 * nb * mb * 64 * 16 : 0;
@@ -576,9 +574,7 @@ hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
     const BaseGemmArgs& a = sl[i].g;
     t.s[i] = sl[i];
     const int n_gemm = (a.d_out / (64 * nb)) * a.split;
-    const int n_side = sl[i].has_side
-                           ? (int)(((long)sl[i].side.n * (sl[i].side.kmax / 4) + 256 * G - 1) / (256 * G))
-                           : 0;
+    const int n_side = side_workgroups(sl[i], 256 * G);
     t.first[i + 1] = t.first[i] + n_gemm + n_side;
   }
   for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];

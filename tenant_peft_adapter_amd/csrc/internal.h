@@ -49,6 +49,13 @@ struct PlanArgs {
   int32_t max_tiles;   // tile lists are padded to this length with kind / slot -1
   int32_t* sh_tiles;   // [4 * max_sh_tiles]: the shared-term tiles again, on their own
   int32_t max_sh_tiles;  // ceil(n / tile_rows); padded like tiles
+  // Row words of each real tile of tiles / sh_tiles / oft_tiles: tile_rows
+  // entries per tile, pinfo of position p0 + j, or -1 past p1 (padding
+  // entries are left unwritten), so a kernel loads a tile's rows alongside
+  // its header instead of after it.
+  int32_t* tile_rows_w;      // [tile_rows * max_tiles]
+  int32_t* sh_rows_w;        // [tile_rows * max_sh_tiles]
+  int32_t* oft_rows_w;       // [tile_rows * max_tiles]
 };
 constexpr int PLAN_MAX_ROWS = 8192;
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
@@ -56,8 +63,8 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream);
 // ---------------------------------------------------------- OFT rotate ----
 struct OftArgs {
   const void* x;           // [n][d_in]
-  const int32_t* perm;
   const int32_t* oft_tiles;  // padded with slot -1 to max_tiles
+  const int32_t* oft_rows_w; // row words per OFT tile (16·MB each)
   const SlotDev* slots;
   void* x_rot;             // [n][d_in], row p = rotated row perm[p]
   int32_t d_in;
@@ -98,6 +105,8 @@ struct ShrinkArgs {
   const int32_t* pinfo;    // (slot << 16) | row by plan position
   const int32_t* tiles;    // plan tiles, owned-term tiles first, padded with kind -1
   const int32_t* sh_tiles; // the shared-term tiles, padded with kind -1
+  const int32_t* tile_rows_w;  // row words per tile (16·MB each)
+  const int32_t* sh_rows_w;    // row words per shared-term tile
   const SlotDev* slots;
   const void* vera_At;     // [r_v][d_in] or null
   int32_t r_v;
@@ -130,6 +139,10 @@ struct GemmSlice {
   ShrinkArgs side;
   int32_t has_side;
 };
+// Work-groups of `threads` threads that a slice's split reduction takes.
+inline int side_workgroups(const GemmSlice& sl, int threads) {
+  return sl.has_side ? (int)(((long)sl.side.n * (sl.side.kmax / 4) + threads - 1) / threads) : 0;
+}
 hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* slices, int count,
                               hipStream_t stream);
 // The same GEMM with W and x streamed into LDS by direct loads (f16 / bf16;
@@ -150,8 +163,8 @@ struct ExpandArgs {
   void* out;
   const float* hpart;      // null: read h from out
   int32_t hsplit;
-  const int32_t* pinfo;    // (slot << 16) | row by plan position
   const int32_t* tiles;    // padded with kind -1 to max_tiles
+  const int32_t* tile_rows_w;  // row words per tile (16·MB each)
   const SlotDev* slots;
   const void* vera_Bt;     // [d_out][r_v]
   int32_t r_v;

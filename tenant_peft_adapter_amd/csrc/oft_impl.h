@@ -22,24 +22,27 @@ template <typename T, int MB, int BS>
 __device__ __forceinline__ void oft_part(const OftArgs& a, int t, int bg, int wave, int lane) {
   constexpr int NB = BS / 16;
   constexpr int BLOCKS_PER_WG = 16;
-  const int* tile = a.oft_tiles + 4 * t;
-  if (tile[2] < 0) return;
-  const int p0 = tile[0], p1 = tile[1];
-  const SlotDev& sd = a.slots[tile[2]];
+  const int i16 = lane & 15, g = lane >> 4;
+  // Header and row words load side by side.
+  const int4 tile = *reinterpret_cast<const int4*>(a.oft_tiles + 4 * t);
+  int rw[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) rw[m] = a.oft_rows_w[(size_t)t * 16 * MB + 16 * m + i16];
+  if (tile.z < 0) return;
+  const int p0 = tile.x;
+  const SlotDev& sd = a.slots[tile.z];
   if (sd.oft_block != BS) return;
   const T* Rt = static_cast<const T*>(sd.Rt);
   const T* X = static_cast<const T*>(a.x);
   T* XR = static_cast<T*>(a.x_rot);
-  const int i16 = lane & 15, g = lane >> 4;
   const int nblocks = a.d_in / BS;
 
   const T* xp[MB];
   bool xv[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    xv[m] = p < p1;
-    xp[m] = X + (size_t)(xv[m] ? a.perm[p] : 0) * a.d_in + 8 * g;
+    xv[m] = rw[m] >= 0;
+    xp[m] = X + (size_t)(xv[m] ? (rw[m] & 0xFFFF) : 0) * a.d_in + 8 * g;
   }
 
   for (int j = 0; j < BLOCKS_PER_WG / 4; ++j) {
@@ -68,9 +71,8 @@ __device__ __forceinline__ void oft_part(const OftArgs& a, int t, int bg, int wa
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int p = p0 + 16 * m + i16;
-      if (p >= p1) continue;
-      T* dst = XR + (size_t)p * a.d_in + kb * BS + 4 * NB * g;
+      if (!xv[m]) continue;
+      T* dst = XR + (size_t)(p0 + 16 * m + i16) * a.d_in + kb * BS + 4 * NB * g;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll

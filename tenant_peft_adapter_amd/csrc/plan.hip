@@ -36,6 +36,20 @@ __device__ __forceinline__ int key_slot(uint32_t k) { return (int)((k >> 16) & 0
 __device__ __forceinline__ int key_rot(uint32_t k) { return (int)((k >> ROW_BITS) & 1); }
 __device__ __forceinline__ int key_row(uint32_t k) { return (int)(k & ((1u << ROW_BITS) - 1)); }
 
+// Row words (pinfo) of positions [q0, q0 + TM) of a tile ending at q1; -1 past
+// it.  TM is a multiple of 4.
+__device__ __forceinline__ void put_rows(int32_t* dst, const uint32_t* skeys, int q0, int q1, int TM) {
+  for (int j = 0; j < TM; j += 4) {
+    int w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = q0 + j + u;
+      w[u] = p < q1 ? (int)(((uint32_t)key_slot(skeys[p]) << 16) | (uint32_t)key_row(skeys[p])) : -1;
+    }
+    *reinterpret_cast<int4*>(dst + j) = make_int4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Exclusive prefix sum over a work-group of T threads; the total goes to
 // *total.  `scratch` holds T / 64 ints; callers may run scans back to back.
 template <int T>
@@ -190,18 +204,12 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
     for (int q = p0; q < p1; q += TM) {
       const int q1 = min(q + TM, p1);
       if (owned) {
-        int* t = a.tiles + 4 * own_off++;
-        t[0] = q;
-        t[1] = q1;
-        t[2] = CLS_OWNED;
-        t[3] = s;
+        put_rows(a.tile_rows_w + (size_t)own_off * TM, skeys, q, q1, TM);
+        *reinterpret_cast<int4*>(a.tiles + 4 * own_off++) = make_int4(q, q1, CLS_OWNED, s);
       }
       if (rot) {
-        int* t = a.oft_tiles + 4 * oft_off++;
-        t[0] = q;
-        t[1] = q1;
-        t[2] = s;
-        t[3] = 0;
+        put_rows(a.oft_rows_w + (size_t)oft_off * TM, skeys, q, q1, TM);
+        *reinterpret_cast<int4*>(a.oft_tiles + 4 * oft_off++) = make_int4(q, q1, s, 0);
       }
     }
   }
@@ -212,7 +220,11 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
     for (int q = tid; q < cnt; q += T) {
       const int4 tl = make_int4(p0 + q * TM, min(p0 + (q + 1) * TM, p1), c, -1);
       *reinterpret_cast<int4*>(a.tiles + 4 * (nt + q)) = tl;
-      if (c == CLS_SHARED) *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = tl;
+      put_rows(a.tile_rows_w + (size_t)(nt + q) * TM, skeys, tl.x, tl.y, TM);
+      if (c == CLS_SHARED) {
+        *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = tl;
+        put_rows(a.sh_rows_w + (size_t)q * TM, skeys, tl.x, tl.y, TM);
+      }
     }
     if (c == CLS_SHARED)
       for (int q = cnt + tid; q < a.max_sh_tiles; q += T)

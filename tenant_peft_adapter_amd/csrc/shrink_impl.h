@@ -25,15 +25,18 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
   // k steps whose loads are issued together (fp32 fragments are twice as
   // wide, so fewer fit in registers)
   constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
-  const int i16 = lane & 15, g = lane >> 4;
   const int ks = item % a.split;
   int rest = item / a.split;
   const int own_items = a.own_tiles * a.own_nblk;
   const int* tile;
+  const int* trow;  // the tile's row words
   int cb, want;
+  const int i16 = lane & 15, g = lane >> 4;
   if (rest < own_items) {
     cb = rest % a.own_nblk;
-    tile = a.tiles + 4 * (rest / a.own_nblk);
+    const int t = rest / a.own_nblk;
+    tile = a.tiles + 4 * t;
+    trow = a.tile_rows_w + (size_t)t * 16 * MB;
     want = CLS_OWNED;
   } else {
     rest -= own_items;
@@ -41,12 +44,18 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
     if (t >= a.sh_ntiles) return;
     cb = rest % a.sh_nblk;
     tile = a.sh_tiles + 4 * t;
+    trow = a.sh_rows_w + (size_t)t * 16 * MB;
     want = CLS_SHARED;
   }
+  // Header and row words load side by side (row words of a padding entry
+  // are never used).
   const int4 tl = *reinterpret_cast<const int4*>(tile);
+  int rw[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) rw[m] = trow[16 * m + i16];
   const int kind = tl.z;
   if (kind != want) return;  // past the real tiles of that kind
-  const int p0 = tl.x, p1 = tl.y;
+  const int p0 = tl.x;
   const T* F;
   int N;
   if (kind == CLS_OWNED) {
@@ -67,9 +76,8 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
   bool xv[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    xv[m] = p < p1;
-    xp[m] = X + (size_t)(xv[m] ? (a.pinfo[p] & 0xFFFF) : 0) * a.d_in + 8 * g;
+    xv[m] = rw[m] >= 0;
+    xp[m] = X + (size_t)(xv[m] ? (rw[m] & 0xFFFF) : 0) * a.d_in + 8 * g;
   }
   const T* fp = F + (size_t)(c0 + i16) * a.d_in + 8 * g;
 
@@ -98,7 +106,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int p = p0 + 16 * m + i16;
-    if (p < p1) *reinterpret_cast<f32x4*>(a.part + ((size_t)ks * a.n + p) * a.kmax + col) = acc[m];
+    if (xv[m]) *reinterpret_cast<f32x4*>(a.part + ((size_t)ks * a.n + p) * a.kmax + col) = acc[m];
   }
 }
 
