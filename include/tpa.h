@@ -259,8 +259,11 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *   TPA_OPT_GEMM_PATH    : n <= 64: 0 register-fed decode kernel, 2 decode
  *                          kernel fed by direct global-to-LDS loads (f16 /
  *                          bf16 with d_in % 64 == 0, else 0; the default
- *                          where it applies); 1 LDS-tiled kernel (always
- *                          used for n > 64)
+ *                          where it applies); any n: 1 LDS-tiled kernel
+ *                          with register-staged loads, 3 128 x 128 tiles fed
+ *                          by direct global-to-LDS loads (f16 / bf16, d_in
+ *                          % 64 == 0, d_out % 128 == 0, else 1; the default
+ *                          for n > 64)
  *   TPA_OPT_SCALE_ROUTE  : where s (and b) are applied (§4.3, appendix
  *                          "Routes"): 0 inside the expand (route one),
  *                          1 side kernel writing h⊙s before the expand,
@@ -285,7 +288,8 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no
  * device work): plan tile rows, base GEMM path (0 register-fed decode
- * kernel, 1 LDS-tiled kernel, 2 streamed decode kernel), its 64-column
+ * kernel, 1 LDS-tiled kernel, 2 streamed decode kernel, 3 direct-load
+ * 128 x 128 kernel), its 64-column
  * blocks per work-group (nb), split-K factor and k range, the shrink's split
  * and k range, the scale route, the decode GEMM's k-groups per work-group
  * and (streamed kernel, else 0) its LDS buffers per k-group.  For tests and

@@ -150,12 +150,16 @@ void cayley_transposed(const float* Q, int b, float* out) {
 
 struct Config {
   int tile_rows;
-  int gemm_path;  // 0 skinny, 1 tiled, 2 stream
+  int gemm_path;  // 0 skinny, 1 tiled, 2 stream, 3 wide
   int gemm_nb, gemm_groups, gemm_stages;
   int gemm_split, gemm_kc;
   int shrink_split, shrink_kc;
   int scale_route;
 };
+
+// The decode GEMMs (n <= 64) always write split partials; the others write
+// h into out when they do not split k.
+bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2; }
 
 struct Layout {
   size_t perm, pinfo, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
@@ -275,7 +279,17 @@ Config choose_config(const tpa_layer* L, int n) {
   // Decode (n <= 64): the LDS-streamed kernel for f16 / bf16 with d_in a
   // multiple of 64, else the register-fed one; larger batches: tiled.
   const bool stream_ok = L->dtype != TPA_F32 && L->d_in % 64 == 0;
-  c.gemm_path = (n > 64) ? 1 : (L->opt[TPA_OPT_GEMM_PATH] >= 0 ? L->opt[TPA_OPT_GEMM_PATH] : (stream_ok ? 2 : 0));
+  // n > 64: the direct-load 128 x 128 kernel (3) for f16 / bf16 with
+  // d_in % 64 == 0 and d_out % 128 == 0, else the register-staged one (1);
+  // options 1 and 3 pin those at any n.
+  const int path_opt = L->opt[TPA_OPT_GEMM_PATH];
+  if (path_opt == 1 || path_opt == 3)
+    c.gemm_path = path_opt;
+  else if (n > 64)
+    c.gemm_path = 3;
+  else
+    c.gemm_path = path_opt == 0 || path_opt == 2 ? path_opt : (stream_ok ? 2 : 0);
+  if (c.gemm_path == 3 && !(stream_ok && L->d_out % 128 == 0)) c.gemm_path = 1;
   if (c.gemm_path == 2 && !stream_ok) c.gemm_path = 0;
   if (c.gemm_path == 2) {
     // 64·nb columns per work-group; k-groups and k range from stream_pick.
@@ -358,7 +372,7 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.counts = take(4 * tpa::CNT_WORDS);
   y.plan_end = off;
   y.x_rot = take((size_t)n * L->d_in * esz);
-  const bool need_hpart = c.gemm_path != 1 || c.gemm_split > 1;
+  const bool need_hpart = decode_path(c) || c.gemm_split > 1;
   y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
   y.vpart = take((size_t)c.shrink_split * n * L->kmax * 4);
   y.v = take((size_t)n * L->kmax * esz);
@@ -862,7 +876,7 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
   for (int i = 0; i < count; ++i) cs[i] = choose_config(Ls[i], n);
   if (count < 2) return;
   for (int i = 0; i < count; ++i)
-    if (cs[i].gemm_path != cs[0].gemm_path || cs[i].gemm_path == 1) return;
+    if (cs[i].gemm_path != cs[0].gemm_path || !decode_path(cs[i])) return;
   const bool stream = cs[0].gemm_path == 2;
   int ref = 0;
   for (int i = 1; i < count; ++i)
@@ -998,7 +1012,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     g.out = sl[i].out;
     gs[i].side = sh[i];
     gs[i].has_side = term[i] ? 1 : 0;
-    if (c.gemm_path != sl[0].c.gemm_path || c.gemm_path == 1 || c.gemm_nb != sl[0].c.gemm_nb ||
+    if (c.gemm_path != sl[0].c.gemm_path || !decode_path(c) || c.gemm_nb != sl[0].c.gemm_nb ||
         c.gemm_groups != sl[0].c.gemm_groups || (c.gemm_path == 2 && c.gemm_stages != sl[0].c.gemm_stages))
       one_launch = false;
   }
@@ -1015,7 +1029,10 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
-        TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
+        if (c.gemm_path == 3)
+          TPA_HIP(tpa::launch_gemm_wide(dtype, gs[i].g, s));
+        else
+          TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
         if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
       }
     }
@@ -1028,7 +1045,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   for (int i = 0; i < count; ++i) {
     tpa_layer* L = sl[i].L;
     const Config& c = sl[i].c;
-    const bool hsplit = c.gemm_path != 1 || c.gemm_split > 1;
+    const bool hsplit = decode_path(c) || c.gemm_split > 1;
     sc[i] = tpa::ScaleArgs{};
     sc[i].y = sl[i].out;
     sc[i].hpart = hsplit ? reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart) : nullptr;
@@ -1308,7 +1325,7 @@ tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (key == TPA_OPT_GEMM_GROUPS && value > 2) return fail(TPA_ERR_INVALID, "gemm groups must be 1 or 2");
   if (key == TPA_OPT_TILE_ROWS && value > 0 && value != 16 && value != 64)
     return fail(TPA_ERR_INVALID, "tile rows must be 16 or 64");
-  if (key == TPA_OPT_GEMM_PATH && value > 2) return fail(TPA_ERR_INVALID, "gemm path must be 0, 1 or 2");
+  if (key == TPA_OPT_GEMM_PATH && value > 3) return fail(TPA_ERR_INVALID, "gemm path must be 0, 1, 2 or 3");
   if (key == TPA_OPT_SCALE_ROUTE) {
     if (value < 0) value = 0;
     if (value > 3) return fail(TPA_ERR_INVALID, "scale route must be 0..3");

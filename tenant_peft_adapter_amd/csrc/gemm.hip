@@ -521,6 +521,139 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- wide ----
+//
+// Base GEMM for n > 64 rows, f16/bf16, where MFMA throughput rather than the
+// single read of W sets the time.  Work-group = 4 waves; its tile is 128
+// rows of x by 128 output columns (wave (wr, wc) computes 64 x 64 as 4 x 4
+// MFMA tiles) by one k range.  Each 64-element k slice of the tile's x rows
+// and W rows (256 rows x 128 B) is loaded straight into one of S LDS
+// buffers with direct global-to-LDS loads (8 loads per wave per slice), the
+// chunks of a row permuted (c ^ swz(row)) so the fragment reads hit distinct
+// bank groups; S - 1 slices are in flight while one is multiplied.  S = 2
+// (64 KB) lets two work-groups share a CU, which measured faster than one
+// work-group with 3 or 4 buffers when the grid has work-groups to spare.  Per
+// slice each wave waits for its own loads, then the work-group meets at a
+// barrier.  Tiles are handed to work-groups so that each XCD (work-group i
+// runs on XCD i % 8) takes a contiguous run of column tiles over every row
+// tile: the slices of x and W its CUs read together stay in its L2.
+template <typename T, int S>
+__global__ __launch_bounds__(256) void gemm_wide_kernel(BaseGemmArgs a, int row_tiles, int col_tiles) {
+  typedef typename Frag<T>::V Vt;
+  constexpr int STAGE = 256 * 128;
+  constexpr int LI = 8;  // loads per wave per slice
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int ntile = row_tiles * col_tiles;
+  int t = (int)blockIdx.x;
+  if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+  const int rt = t % row_tiles, ct = t / row_tiles;
+  const int row0 = rt * 128, col0 = ct * 128;
+  const int ks = blockIdx.y;
+  const int kbeg = ks * a.kc;
+  const int nst = max(0, min(a.d_in - kbeg, a.kc)) / 64;
+  const T* X = static_cast<const T*>(a.x);
+  const T* XR = static_cast<const T*>(a.x_rot);
+  const T* W = static_cast<const T*>(a.W);
+
+  // Sources of this lane's loads: instruction j < 4 loads x rows
+  // 32·wave + 8j .. +8 of the tile, j >= 4 W rows 32·wave + 8(j - 4) .. +8;
+  // lane = 8 · (row within the instruction) + LDS chunk.
+  const int lr = lane >> 3, lc = lane & 7;
+  const T* src[LI];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + 8 * j + lr;
+    const int i = row0 + r;
+    const T* base = X;  // rows past n read row 0; their results are not stored
+    if (i < a.n) {
+      base = X + (size_t)i * a.d_in;
+      if (a.rot_pos) {
+        const int rp = a.rot_pos[i];
+        if (rp >= 0) base = XR + (size_t)rp * a.d_in;
+      }
+    }
+    src[j] = base + kbeg + 8 * (lc ^ swz<2>(r));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + 8 * j + lr;
+    src[4 + j] = W + (size_t)(col0 + r) * a.d_in + kbeg + 8 * (lc ^ swz<4>(r));
+  }
+  auto issue = [&](int st) {
+    unsigned char* buf = smem + (size_t)(st % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LI; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[j] + 64 * st),
+          (__attribute__((address_space(3))) void*)(buf + (j < 4 ? 0 : 128 * 128) + (size_t)(32 * wave + 8 * (j & 3)) * 128),
+          16, 0, 0);
+  };
+
+  int arow[4], brow[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) arow[b] = 64 * wc + perm_col<4>(i16, b);  // W rows (output columns)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) brow[m] = 64 * wr + 16 * m + i16;          // x rows
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nst) issue(st);
+  for (int it = 0; it < nst; ++it) {
+    const int younger = min(S - 2, nst - 1 - it);
+    __builtin_amdgcn_sched_barrier(0);
+    if (younger >= 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LI));
+    else if (younger == 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LI));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + S - 1 < nst) issue(it + S - 1);
+    const unsigned char* buf = smem + (size_t)(it % S) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int q = 4 * kk + g;
+      Vt af[4], bf[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        af[b] = *reinterpret_cast<const Vt*>(buf + 128 * 128 + arow[b] * 128 + 16 * (q ^ swz<4>(arow[b])));
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+    }
+  }
+
+  // Lane holds, for row block m, 16 consecutive output columns.
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = row0 + 64 * wr + 16 * m + i16;
+    if (row >= a.n) continue;
+    const int col = col0 + 64 * wc + 16 * g;
+    float v[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[4 * b + q] = acc[b][m][q];
+    if (a.split == 1)
+      store_run16<T>(static_cast<T*>(a.out) + (size_t)row * a.d_out + col, v);
+    else
+      store_run16<float>(a.part + ((size_t)ks * a.n + row) * a.d_out + col, v);
+  }
+}
+
 template <typename T, int G>
 hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
   const int mb = sl[0].g.n <= 16 ? 1 : sl[0].g.n <= 32 ? 2 : 4;
@@ -644,6 +777,21 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
   if (dtype == 1) return stream_dtype<f16>(nb, groups, stages, slices, count, s);
   if (dtype == 2) return stream_dtype<bf16>(nb, groups, stages, slices, count, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_wide(int dtype, const BaseGemmArgs& a, hipStream_t s) {
+  constexpr int S = 2;
+  if (a.n <= 0 || a.d_out % 128 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in)
+    return hipErrorInvalidValue;
+  const int row_tiles = (a.n + 127) / 128, col_tiles = a.d_out / 128;
+  const dim3 grid((unsigned)(row_tiles * col_tiles), (unsigned)a.split);
+  const size_t lds = (size_t)S * 256 * 128;
+  switch (dtype) {
+    case 1: hipLaunchKernelGGL((gemm_wide_kernel<f16, S>), grid, dim3(256), lds, s, a, row_tiles, col_tiles); break;
+    case 2: hipLaunchKernelGGL((gemm_wide_kernel<bf16, S>), grid, dim3(256), lds, s, a, row_tiles, col_tiles); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t s) {

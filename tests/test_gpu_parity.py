@@ -59,6 +59,21 @@ def test_ragged_batch_sizes(n):
     check(y_gpu, y, h, xw, label="ragged n=%d" % n)
 
 
+@pytest.mark.parametrize("n,path", [(100, 1), (300, 1), (40, 3), (129, 3)])
+def test_pinned_prefill_kernels(n, path):
+    """The register-staged tiled kernel (1) pinned at prefill sizes, and the
+    direct-load 128 x 128 kernel (3) pinned at a decode size and a ragged
+    prefill size."""
+    wl = synth.tiny_mixed(seed=50 + n, n=n, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    say("pinned path=%d n=%d" % (path, n))
+    L = make_layer(p, max_slots=8, max_rank=32, options={4: path})
+    assert L.config(n)["gemm_path"] == path
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="pinned path=%d n=%d" % (path, n))
+
+
 def test_prefill_lora_dora_q_proj():
     """q_proj 4096 -> 4096, 1024 rows in 16 segments of 64, 8 LoRA + 8 DoRA
     rank 16: every row checked."""

@@ -80,7 +80,7 @@ def test_identity_rows_equal_base_only_output_bitwise():
     assert np.array_equal(y_mixed[ident], y_base[ident])
 
 
-@pytest.mark.parametrize("n,path", [(20, 0), (20, 2), (64, 0), (64, 2), (200, 1)])
+@pytest.mark.parametrize("n,path", [(20, 0), (20, 2), (64, 0), (64, 2), (200, 1), (200, 3)])
 def test_batch_invariance_row_alone_vs_in_batch(n, path):
     """With the kernel configuration pinned, a row computed alone equals the
     same row inside a batch of other tenants, bit for bit."""
