@@ -18,10 +18,15 @@
 //
 // One work-group does the whole plan with everything in LDS: the only global
 // reads are slot_of_row and the slot records it points to, the rest are
-// writes.  A sort key packs (class, slot, has-R, row) into 32 bits; has-R is
-// a function of the slot, so it does not change the order.  Up to 1024 rows
-// are ranked directly (each thread counts the keys below its own, no
-// barriers inside the sort); larger batches use an LDS bitonic network.
+// writes.  A key packs (class, slot, has-R, row) into 32 bits; has-R is a
+// function of the slot.  Up to 256 rows, each key is ranked by counting the
+// keys below it.  Larger batches take a stable LSD radix sort on the bucket
+// class * max_slots + slot (4 bits a pass), which leaves rows of one bucket
+// in row order: the order of the keys.  Each thread owns a contiguous run of
+// at most 8 elements; a pass counts digits per thread, scans the packed
+// counts across the work-group and scatters in order.  Tiles are then
+// written position-parallel.  Barriers wait for LDS only: the plan never
+// reads its own global writes back.
 #include "internal.h"
 
 namespace tpa {
@@ -36,18 +41,8 @@ __device__ __forceinline__ int key_slot(uint32_t k) { return (int)((k >> 16) & 0
 __device__ __forceinline__ int key_rot(uint32_t k) { return (int)((k >> ROW_BITS) & 1); }
 __device__ __forceinline__ int key_row(uint32_t k) { return (int)(k & ((1u << ROW_BITS) - 1)); }
 
-// Row words (pinfo) of positions [q0, q0 + TM) of a tile ending at q1; -1 past
-// it.  TM is a multiple of 4.
-__device__ __forceinline__ void put_rows(int32_t* dst, const uint32_t* skeys, int q0, int q1, int TM) {
-  for (int j = 0; j < TM; j += 4) {
-    int w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = q0 + j + u;
-      w[u] = p < q1 ? (int)(((uint32_t)key_slot(skeys[p]) << 16) | (uint32_t)key_row(skeys[p])) : -1;
-    }
-    *reinterpret_cast<int4*>(dst + j) = make_int4(w[0], w[1], w[2], w[3]);
-  }
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Exclusive prefix sum over a work-group of T threads; the total goes to
@@ -68,7 +63,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     return incl - v;
   }
   if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int wave_off = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
@@ -76,72 +71,153 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     if (w < wave) wave_off += s;
     tot += s;
   }
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   return wave_off + incl - v;
 }
 
+// Exclusive scan across the work-group of eight packed words per thread
+// (sixteen 16-bit counters; no field ever exceeds n <= 8192, so no carry
+// crosses a field).  excl gets this thread's exclusive prefix, total the
+// work-group's sums.  scratch holds 8 words per wave.
+template <int T>
+__device__ __forceinline__ void block_scan8(const uint32_t (&v)[8], uint32_t (&excl)[8], uint32_t (&total)[8],
+                                            uint32_t* scratch) {
+  constexpr int W = T / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    incl[q] = v[q];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = (uint32_t)__shfl_up((int)incl[q], off, 64);
+      if (lane >= off) incl[q] += t;
+    }
+  }
+  if (lane == 63)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) scratch[8 * wave + q] = incl[q];
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t off = 0, tot = 0;
+    for (int w = 0; w < W; ++w) {
+      const uint32_t x = scratch[8 * w + q];
+      if (w < wave) off += x;
+      tot += x;
+    }
+    excl[q] = off + incl[q] - v[q];
+    total[q] = tot;
+  }
+  lds_barrier();
+}
+
 template <int T, bool RANK>
 __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
+  constexpr int EMAX = 8;  // elements per thread (n <= 8 T)
   extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
   __shared__ int scan_scratch[T / 64 > 0 ? T / 64 : 1];
+  __shared__ uint32_t scan8_scratch[8 * (T / 64)];
   __shared__ int s_cls[4];
+  __shared__ int s_bad;
   const int n = a.n;
   const int tid = threadIdx.x;
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  const int nkeys = RANK ? n : np2;
-  uint32_t* keys = sm;                               // [nkeys]
-  uint32_t* skeys = RANK ? sm + n : sm;              // sorted keys [n]
-  uint16_t* seg_start = reinterpret_cast<uint16_t*>(skeys + (RANK ? n : np2));  // [n + 1]
+  uint32_t* kbuf0 = sm;                                         // [n]
+  uint32_t* kbuf1 = sm + n;                                     // [n]
+  uint16_t* seg_start = reinterpret_cast<uint16_t*>(sm + 2 * n);  // [n + 1]
+  uint16_t* seg_of_pos = seg_start + (n + 2);                   // [n]
+  uint16_t* own_first = seg_of_pos + n;                         // [n]: first owned tile of a segment
+  uint16_t* oft_first = own_first + n;                          // [n]: first OFT tile of a segment
 
-  // 1. Effective slot and sort key per row (the only global reads).
+  // 1. Effective slot and key per row (the only global reads).
+  if (tid == 0) s_bad = 0;
+  lds_barrier();
   int bad = 0;
-  for (int i = tid; i < nkeys; i += T) {
-    uint32_t key = 0xFFFFFFFFu;
-    if (i < n) {
-      int s = a.slot_of_row[i];
-      if (!(s >= 0 && s < a.max_slots && a.slots[s].cls >= 0)) {
-        s = 0;
-        bad = 1;
-      }
-      const SlotDev& sd = a.slots[s];
-      const int cls = (s == 0) ? CLS_NONE : sd.cls;
-      const int rot = (s != 0 && sd.has_R) ? 1 : 0;
-      key = ((uint32_t)cls << 30) | ((uint32_t)s << 16) | ((uint32_t)rot << ROW_BITS) | (uint32_t)i;
-      a.row_slot[i] = s;
+  for (int i = tid; i < n; i += T) {
+    int s = a.slot_of_row[i];
+    if (!(s >= 0 && s < a.max_slots && a.slots[s].cls >= 0)) {
+      s = 0;
+      bad = 1;
     }
-    keys[i] = key;
+    const SlotDev& sd = a.slots[s];
+    const int cls = (s == 0) ? CLS_NONE : sd.cls;
+    const int rot = (s != 0 && sd.has_R) ? 1 : 0;
+    kbuf0[i] = ((uint32_t)cls << 30) | ((uint32_t)s << 16) | ((uint32_t)rot << ROW_BITS) | (uint32_t)i;
+    a.row_slot[i] = s;
   }
-  const int any_bad = __syncthreads_or(bad);
+  if (__any(bad) && (tid & 63) == 0) atomicOr(&s_bad, 1);
+  lds_barrier();
+  const int any_bad = s_bad;
 
-  // 2. Sort by key, ascending.
+  // 2. Sort.  Small batches: each key's rank is the count of smaller keys
+  //    (keys are distinct).  Otherwise a stable LSD radix sort on bucket =
+  //    class * max_slots + slot.
+  const int E = (n + T - 1) / T;
+  const int e_lo = min(n, tid * E), e_hi = min(n, e_lo + E);
+  const uint32_t nbucket = 3u * (uint32_t)a.max_slots;
+  int passes = 0;
+  while (!RANK && ((nbucket - 1) >> (4 * passes))) ++passes;
   if (RANK) {
     for (int i = tid; i < n; i += T) {
-      const uint32_t k = keys[i];
+      const uint32_t k = kbuf0[i];
       int r = 0;
-      for (int j = 0; j < n; ++j) r += keys[j] < k ? 1 : 0;
-      skeys[r] = k;
+      for (int j = 0; j < n; ++j) r += kbuf0[j] < k ? 1 : 0;
+      kbuf1[r] = k;
     }
-    __syncthreads();
-  } else {
-    for (int k = 2; k <= np2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < np2; i += T) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const uint32_t x = keys[i], y = keys[ixj];
-            const bool asc = (i & k) == 0;
-            if ((x > y) == asc) {
-              keys[i] = y;
-              keys[ixj] = x;
-            }
-          }
-        }
-        __syncthreads();
+    lds_barrier();
+  }
+  uint32_t* src = kbuf0;
+  uint32_t* dst = kbuf1;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int shift = 4 * pass;
+    uint32_t kv[EMAX];
+    int dg[EMAX];
+    uint32_t cnt[16];
+#pragma unroll
+    for (int d = 0; d < 16; ++d) cnt[d] = 0;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      dg[e] = -1;
+      if (e_lo + e < e_hi) {
+        kv[e] = src[e_lo + e];
+        const uint32_t bucket = (kv[e] >> 30) * (uint32_t)a.max_slots + ((kv[e] >> 16) & 0x3FFFu);
+        dg[e] = (int)((bucket >> shift) & 15u);
+#pragma unroll
+        for (int d = 0; d < 16; ++d) cnt[d] += dg[e] == d ? 1u : 0u;
       }
     }
+    uint32_t packed[8], excl[8], total[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) packed[q] = cnt[2 * q] | (cnt[2 * q + 1] << 16);
+    block_scan8<T>(packed, excl, total, scan8_scratch);
+    uint32_t pos[16];
+    uint32_t base = 0;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const uint32_t tot = (total[d >> 1] >> (16 * (d & 1))) & 0xFFFFu;
+      pos[d] = base + ((excl[d >> 1] >> (16 * (d & 1))) & 0xFFFFu);
+      base += tot;
+    }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (dg[e] < 0) continue;
+      uint32_t p = 0;
+#pragma unroll
+      for (int d = 0; d < 16; ++d)
+        if (dg[e] == d) p = pos[d]++;
+      dst[p] = kv[e];
+    }
+    lds_barrier();
+    uint32_t* t = src;
+    src = dst;
+    dst = t;
   }
+  if (RANK) {
+    src = kbuf1;
+    dst = kbuf0;
+  }
+  const uint32_t* skeys = src;  // sorted keys [n]
 
   // 3. Positions: perm, rot_pos, segment heads, class boundaries.  Each
   //    thread owns a contiguous chunk of positions, so a scan of per-thread
@@ -153,20 +229,27 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
     if (p == 0 || key_slot(skeys[p - 1]) != key_slot(skeys[p])) ++heads;
   int nseg = 0;
   int seg = block_exclusive_scan<T>(heads, scan_scratch, &nseg);
-  for (int p = p_lo; p < p_hi; ++p) {
+  // perm, pinfo (by position) and rot_pos (by row, through the LDS copy of
+  // the unsorted keys) are written with consecutive lanes on consecutive
+  // entries.
+  for (int p = tid; p < n; p += T) {
     const uint32_t k = skeys[p];
     const int row = key_row(k);
+    a.perm[p] = row;
+    a.pinfo[p] = (key_slot(k) << 16) | row;
+    dst[row] = key_rot(k) ? (uint32_t)p : 0xFFFFFFFFu;  // the spare key buffer
+  }
+  for (int p = p_lo; p < p_hi; ++p) {
+    const uint32_t k = skeys[p];
     const int s = key_slot(k);
     const int cls = key_cls(k);
-    a.perm[p] = row;
-    a.pinfo[p] = (s << 16) | row;
-    a.rot_pos[row] = key_rot(k) ? p : -1;
     if (p == 0 || key_slot(skeys[p - 1]) != s) {
       seg_start[seg] = (uint16_t)p;
       a.seg_ptr[seg] = p;
       a.seg_slot[seg] = s;
       ++seg;
     }
+    seg_of_pos[p] = (uint16_t)(seg - 1);
     const int prev_cls = (p == 0) ? -1 : key_cls(skeys[p - 1]);
     for (int c = prev_cls + 1; c <= cls; ++c) s_cls[c] = p;
     if (p == n - 1)
@@ -176,11 +259,15 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
     seg_start[nseg] = (uint16_t)n;
     a.seg_ptr[nseg] = n;
   }
-  __syncthreads();
+  lds_barrier();
+  for (int i = tid; i < n; i += T) a.rot_pos[i] = (int32_t)dst[i];
 
   // 4. Tiles: owned segments cut into pieces of tile_rows, then the shared-
   //    term and no-term ranges cut from their start; OFT tiles per segment
-  //    of a slot with R.
+  //    of a slot with R.  A scan over segments gives each segment its first
+  //    owned and OFT tile; then every position writes its own row word, and
+  //    the positions that start a tile write its header (and -1 over the
+  //    unused words of a short tile).
   const int TM = a.tile_rows;
   const int schunk = (nseg + T - 1) / T;
   const int j_lo = min(nseg, tid * schunk), j_hi = min(nseg, j_lo + schunk);
@@ -196,41 +283,52 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
   int own_off = block_exclusive_scan<T>(own, scan_scratch, &own_total);
   int oft_off = block_exclusive_scan<T>(oft, scan_scratch, &oft_total);
   for (int j = j_lo; j < j_hi; ++j) {
-    const int p0 = seg_start[j], p1 = seg_start[j + 1];
-    const uint32_t k = skeys[p0];
-    const int s = key_slot(k);
-    const bool owned = key_cls(k) == CLS_OWNED;
-    const bool rot = key_rot(k) != 0;
-    for (int q = p0; q < p1; q += TM) {
-      const int q1 = min(q + TM, p1);
-      if (owned) {
-        put_rows(a.tile_rows_w + (size_t)own_off * TM, skeys, q, q1, TM);
-        *reinterpret_cast<int4*>(a.tiles + 4 * own_off++) = make_int4(q, q1, CLS_OWNED, s);
+    const int len = (int)seg_start[j + 1] - (int)seg_start[j];
+    const uint32_t k = skeys[seg_start[j]];
+    const int nt = (len + TM - 1) / TM;
+    own_first[j] = (uint16_t)own_off;
+    oft_first[j] = (uint16_t)oft_off;
+    if (key_cls(k) == CLS_OWNED) own_off += nt;
+    if (key_rot(k)) oft_off += nt;
+  }
+  lds_barrier();
+  const int n_sh = (s_cls[CLS_SHARED + 1] - s_cls[CLS_SHARED] + TM - 1) / TM;
+  const int n_none = (s_cls[CLS_NONE + 1] - s_cls[CLS_NONE] + TM - 1) / TM;
+  const int nt = own_total + n_sh + n_none;
+  for (int p = tid; p < n; p += T) {
+    const uint32_t k = skeys[p];
+    const int word = (int)(((uint32_t)key_slot(k) << 16) | (uint32_t)key_row(k));
+    const int j = seg_of_pos[p];
+    const int s0 = seg_start[j], s1 = seg_start[j + 1];
+    const int off = p - s0;
+    const int cls = key_cls(k);
+    // (tile list, its row words, index in the list, start and end of the
+    // tile, header) for each list the position belongs to
+    auto put = [&](int* list, int* rows, int q, int q0, int q1, int4 hdr) {
+      rows[(size_t)q * TM + (p - q0)] = word;
+      if (p == q0) {
+        *reinterpret_cast<int4*>(list + 4 * q) = hdr;
+        for (int u = q1 - q0; u < TM; ++u) rows[(size_t)q * TM + u] = -1;
       }
-      if (rot) {
-        put_rows(a.oft_rows_w + (size_t)oft_off * TM, skeys, q, q1, TM);
-        *reinterpret_cast<int4*>(a.oft_tiles + 4 * oft_off++) = make_int4(q, q1, s, 0);
-      }
+    };
+    if (cls == CLS_OWNED) {
+      const int q0 = s0 + off / TM * TM, q1 = min(q0 + TM, s1);
+      put(a.tiles, a.tile_rows_w, own_first[j] + off / TM, q0, q1, make_int4(q0, q1, CLS_OWNED, key_slot(k)));
+    } else {
+      const int c0 = s_cls[cls], c1 = s_cls[cls + 1];
+      const int q = (p - c0) / TM;
+      const int q0 = c0 + q * TM, q1 = min(q0 + TM, c1);
+      const int4 hdr = make_int4(q0, q1, cls, -1);
+      put(a.tiles, a.tile_rows_w, own_total + (cls == CLS_NONE ? n_sh : 0) + q, q0, q1, hdr);
+      if (cls == CLS_SHARED) put(a.sh_tiles, a.sh_rows_w, q, q0, q1, hdr);
+    }
+    if (key_rot(k)) {
+      const int q0 = s0 + off / TM * TM, q1 = min(q0 + TM, s1);
+      put(a.oft_tiles, a.oft_rows_w, oft_first[j] + off / TM, q0, q1, make_int4(q0, q1, key_slot(k), 0));
     }
   }
-  int nt = own_total;
-  for (int c = CLS_SHARED; c <= CLS_NONE; ++c) {
-    const int p0 = s_cls[c], p1 = s_cls[c + 1];
-    const int cnt = (p1 - p0 + TM - 1) / TM;
-    for (int q = tid; q < cnt; q += T) {
-      const int4 tl = make_int4(p0 + q * TM, min(p0 + (q + 1) * TM, p1), c, -1);
-      *reinterpret_cast<int4*>(a.tiles + 4 * (nt + q)) = tl;
-      put_rows(a.tile_rows_w + (size_t)(nt + q) * TM, skeys, tl.x, tl.y, TM);
-      if (c == CLS_SHARED) {
-        *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = tl;
-        put_rows(a.sh_rows_w + (size_t)q * TM, skeys, tl.x, tl.y, TM);
-      }
-    }
-    if (c == CLS_SHARED)
-      for (int q = cnt + tid; q < a.max_sh_tiles; q += T)
-        *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = make_int4(0, 0, -1, -1);
-    nt += cnt;
-  }
+  for (int q = n_sh + tid; q < a.max_sh_tiles; q += T)
+    *reinterpret_cast<int4*>(a.sh_tiles + 4 * q) = make_int4(0, 0, -1, -1);
   // Pad both tile lists to max_tiles so later kernels need no counter.
   for (int q = nt + tid; q < a.max_tiles; q += T) {
     int* t = a.tiles + 4 * q;
@@ -259,10 +357,7 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
 
 template <int T, bool RANK>
 hipError_t plan_launch(const PlanArgs& a, hipStream_t stream) {
-  int np2 = 1;
-  while (np2 < a.n) np2 <<= 1;
-  const size_t keys = RANK ? 2 * (size_t)a.n : (size_t)np2;
-  const size_t lds = keys * sizeof(uint32_t) + ((size_t)a.n + 2) * sizeof(uint16_t);
+  const size_t lds = 2 * (size_t)a.n * sizeof(uint32_t) + (4 * (size_t)a.n + 2) * sizeof(uint16_t);
   hipLaunchKernelGGL((plan_kernel<T, RANK>), dim3(1), dim3(T), lds, stream, a);
   return hipGetLastError();
 }
@@ -271,9 +366,9 @@ hipError_t plan_launch(const PlanArgs& a, hipStream_t stream) {
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
   if (a.n <= 0 || a.n > PLAN_MAX_ROWS) return hipErrorInvalidValue;
+  if (a.max_slots < 1 || a.max_slots > 16383) return hipErrorInvalidValue;
   if (a.n <= 64) return plan_launch<64, true>(a, stream);
   if (a.n <= 256) return plan_launch<256, true>(a, stream);
-  if (a.n <= 1024) return plan_launch<1024, true>(a, stream);
   return plan_launch<1024, false>(a, stream);
 }
 
