@@ -274,8 +274,11 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *   TPA_OPT_GEMM_GROUPS  : decode GEMM, k-groups of 4 waves per work-group
  *                          (1 or 2; fp32 layers always use 1; the streamed
  *                          kernel takes 2 only with 3 stages)
- *   TPA_OPT_GEMM_STAGES  : streamed decode GEMM, LDS buffers per k-group
- *                          (3, 4 or 6; fewer where they do not fit) */
+ *   TPA_OPT_GEMM_STAGES  : LDS buffers of the direct-load GEMMs (2..6):
+ *                          streamed decode kernel, per k-group 3, 4 or 6
+ *                          (other values take 3; fewer where they do not
+ *                          fit); 128 x 128 kernel, 32 KB each, 2..5 (6
+ *                          takes the automatic choice) */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -292,8 +295,8 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
  * 128 x 128 kernel), its 64-column
  * blocks per work-group (nb), split-K factor and k range, the shrink's split
  * and k range, the scale route, the decode GEMM's k-groups per work-group
- * and (streamed kernel, else 0) its LDS buffers per k-group.  For tests and
- * measurement. */
+ * and (direct-load kernels, else 0) its LDS buffers (per k-group for the
+ * streamed kernel).  For tests and measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
       gemm_groups, gemm_stages;

@@ -295,7 +295,8 @@ Config choose_config(const tpa_layer* L, int n) {
     // 64·nb columns per work-group; k-groups and k range from stream_pick.
     c.gemm_nb = (L->d_out >= 2048 && L->d_out % 128 == 0) ? 2 : 1;
     if (L->opt[TPA_OPT_GEMM_NB] > 0 && L->d_out % (64 * L->opt[TPA_OPT_GEMM_NB]) == 0) c.gemm_nb = L->opt[TPA_OPT_GEMM_NB];
-    c.gemm_stages = L->opt[TPA_OPT_GEMM_STAGES] > 0 ? L->opt[TPA_OPT_GEMM_STAGES] : 3;
+    const int st = L->opt[TPA_OPT_GEMM_STAGES];
+    c.gemm_stages = st == 4 || st == 6 ? st : 3;
     while (c.gemm_stages > 3 && tpa::gemm_stream_lds(n, c.gemm_nb, 1, c.gemm_stages) > tpa::GEMM_STREAM_MAX_LDS)
       c.gemm_stages = c.gemm_stages == 6 ? 4 : 3;
     int kc;
@@ -336,6 +337,12 @@ Config choose_config(const tpa_layer* L, int n) {
     split = std::min(split, L->d_in / 64);
     c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
+    if (c.gemm_path == 3) {
+      // Two buffers (64 KB): the fastest ring depth measured at every
+      // prefill shape; deeper rings only by option.
+      const int st = L->opt[TPA_OPT_GEMM_STAGES];
+      c.gemm_stages = st >= 2 && st <= 5 ? st : 2;
+    }
   }
   c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];
   set_shrink_split(L, &c);
@@ -1030,7 +1037,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
         if (c.gemm_path == 3)
-          TPA_HIP(tpa::launch_gemm_wide(dtype, gs[i].g, s));
+          TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i].g, s));
         else
           TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
         if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
@@ -1318,8 +1325,8 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
   if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_GEMM_STAGES) return fail(TPA_ERR_INVALID, "unknown option %d", key);
-  if (key == TPA_OPT_GEMM_STAGES && value > 0 && value != 3 && value != 4 && value != 6)
-    return fail(TPA_ERR_INVALID, "gemm stages must be 3, 4 or 6");
+  if (key == TPA_OPT_GEMM_STAGES && value > 0 && (value < 2 || value > 6))
+    return fail(TPA_ERR_INVALID, "gemm stages must be 2..6");
   if (key == TPA_OPT_GEMM_NB && value > 0 && value != 1 && value != 2 && value != 4)
     return fail(TPA_ERR_INVALID, "gemm nb must be 1, 2 or 4");
   if (key == TPA_OPT_GEMM_GROUPS && value > 2) return fail(TPA_ERR_INVALID, "gemm groups must be 1 or 2");
@@ -1350,7 +1357,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   out->shrink_kc = c.shrink_kc;
   out->scale_route = c.scale_route;
   out->gemm_groups = c.gemm_groups;
-  out->gemm_stages = c.gemm_path == 2 ? c.gemm_stages : 0;
+  out->gemm_stages = c.gemm_path == 2 || c.gemm_path == 3 ? c.gemm_stages : 0;
   return TPA_OK;
 }
 

@@ -531,10 +531,11 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
 // buffers with direct global-to-LDS loads (8 loads per wave per slice), the
 // chunks of a row permuted (c ^ swz(row)) so the fragment reads hit distinct
 // bank groups; S - 1 slices are in flight while one is multiplied.  S = 2
-// (64 KB) lets two work-groups share a CU, which measured faster than one
-// work-group with 3 or 4 buffers when the grid has work-groups to spare.  Per
-// slice each wave waits for its own loads, then the work-group meets at a
-// barrier.  Tiles are handed to work-groups so that each XCD (work-group i
+// (64 KB) lets two work-groups share a CU; deeper rings (3..5 buffers, up to
+// the whole 160 KB) measured no faster even where a CU holds one
+// work-group: the slices' trip from L2 into LDS, not their latency, sets
+// the pace.  Per slice each wave waits for its own loads, then the
+// work-group meets at a barrier.  Tiles are handed to work-groups so that each XCD (work-group i
 // runs on XCD i % 8) takes a contiguous run of column tiles over every row
 // tile: the slices of x and W its CUs read together stay in its L2.
 template <typename T, int S>
@@ -607,9 +608,12 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(BaseGemmArgs a, int row_
   for (int st = 0; st < S - 1; ++st)
     if (st < nst) issue(st);
   for (int it = 0; it < nst; ++it) {
+    // Slices issued after this one that may still be in flight.
     const int younger = min(S - 2, nst - 1 - it);
     __builtin_amdgcn_sched_barrier(0);
-    if (younger >= 2)
+    if (S >= 5 && younger >= 3)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LI));
+    else if (S >= 4 && younger == 2)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LI));
     else if (younger == 1)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(LI));
@@ -779,18 +783,22 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_wide(int dtype, const BaseGemmArgs& a, hipStream_t s) {
-  constexpr int S = 2;
+hipError_t launch_gemm_wide(int dtype, int stages, const BaseGemmArgs& a, hipStream_t s) {
   if (a.n <= 0 || a.d_out % 128 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in)
     return hipErrorInvalidValue;
+  if (stages < 2 || stages > 5 || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
   const int row_tiles = (a.n + 127) / 128, col_tiles = a.d_out / 128;
   const dim3 grid((unsigned)(row_tiles * col_tiles), (unsigned)a.split);
-  const size_t lds = (size_t)S * 256 * 128;
-  switch (dtype) {
-    case 1: hipLaunchKernelGGL((gemm_wide_kernel<f16, S>), grid, dim3(256), lds, s, a, row_tiles, col_tiles); break;
-    case 2: hipLaunchKernelGGL((gemm_wide_kernel<bf16, S>), grid, dim3(256), lds, s, a, row_tiles, col_tiles); break;
-    default: return hipErrorInvalidValue;
+  const size_t lds = (size_t)stages * 256 * 128;
+#define TPA_WIDE(SV)                                                                                         \
+  if (stages == SV) {                                                                                        \
+    if (dtype == 1)                                                                                          \
+      hipLaunchKernelGGL((gemm_wide_kernel<f16, SV>), grid, dim3(256), lds, s, a, row_tiles, col_tiles);     \
+    else                                                                                                     \
+      hipLaunchKernelGGL((gemm_wide_kernel<bf16, SV>), grid, dim3(256), lds, s, a, row_tiles, col_tiles);    \
   }
+  TPA_WIDE(2) TPA_WIDE(3) TPA_WIDE(4) TPA_WIDE(5)
+#undef TPA_WIDE
   return hipGetLastError();
 }
 

@@ -94,8 +94,9 @@ constexpr size_t GEMM_SKINNY_MAX_LDS = 144 * 1024;
 size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc);
 // LDS-tiled 128x128 kernel; writes `out` when split == 1, else `part`.
 // n > 64, f16 / bf16: 128 x 128 tiles fed by direct global-to-LDS loads
-// (d_out % 128 == 0, d_in and kc multiples of 64).
-hipError_t launch_gemm_wide(int dtype, const BaseGemmArgs& a, hipStream_t stream);
+// (d_out % 128 == 0, d_in and kc multiples of 64) through a ring of `stages`
+// 32 KB LDS buffers (2..5).
+hipError_t launch_gemm_wide(int dtype, int stages, const BaseGemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t stream);
 
 // Shrink over the plan's tiles: owned-term tiles V[p] = x[perm[p]] A'ᵀ,

@@ -59,19 +59,28 @@ def test_ragged_batch_sizes(n):
     check(y_gpu, y, h, xw, label="ragged n=%d" % n)
 
 
-@pytest.mark.parametrize("n,path", [(100, 1), (300, 1), (40, 3), (129, 3)])
-def test_pinned_prefill_kernels(n, path):
+@pytest.mark.parametrize("n,path,stages,d", [
+    (100, 1, 0, 256), (300, 1, 0, 256),
+    (40, 3, 2, 256), (129, 3, 2, 256), (129, 3, 3, 640), (200, 3, 4, 640), (129, 3, 5, 640), (300, 3, 5, 256)])
+def test_pinned_prefill_kernels(n, path, stages, d):
     """The register-staged tiled kernel (1) pinned at prefill sizes, and the
-    direct-load 128 x 128 kernel (3) pinned at a decode size and a ragged
-    prefill size."""
-    wl = synth.tiny_mixed(seed=50 + n, n=n, dtype="f16", with_identity=True)
+    direct-load 128 x 128 kernel (3) pinned at a decode size and ragged
+    prefill sizes with each LDS ring depth (2..5 buffers; d_in = 256 gives
+    fewer k slices than a 5-deep ring holds, 640 more)."""
+    wl = synth.tiny_mixed(seed=50 + n + d, n=n, d=d, dtype="f16", with_identity=True)
     p = wl["projections"][0]
-    say("pinned path=%d n=%d" % (path, n))
-    L = make_layer(p, max_slots=8, max_rank=32, options={4: path})
-    assert L.config(n)["gemm_path"] == path
+    say("pinned path=%d stages=%d n=%d d=%d" % (path, stages, n, d))
+    opts = {4: path}
+    if stages:
+        opts[8] = stages
+    L = make_layer(p, max_slots=8, max_rank=32, options=opts)
+    cfg = L.config(n)
+    assert cfg["gemm_path"] == path
+    if stages:
+        assert cfg["gemm_stages"] == stages
     y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
     y, h, xw = reference(p, wl["slot_of_row"])
-    check(y_gpu, y, h, xw, label="pinned path=%d n=%d" % (path, n))
+    check(y_gpu, y, h, xw, label="pinned path=%d stages=%d n=%d d=%d" % (path, stages, n, d))
 
 
 def test_prefill_lora_dora_q_proj():
