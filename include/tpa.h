@@ -255,7 +255,8 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  * automatic choice.
  *   TPA_OPT_GEMM_SPLIT   : split-K factor of the base GEMM
  *   TPA_OPT_SHRINK_SPLIT : split-K factor of the shrink
- *   TPA_OPT_TILE_ROWS    : rows per tile of the plan (16 or 64)
+ *   TPA_OPT_TILE_ROWS    : rows per tile of the plan (16, the default, or
+ *                          64)
  *   TPA_OPT_GEMM_PATH    : n <= 64: 0 register-fed decode kernel, 2 decode
  *                          kernel fed by direct global-to-LDS loads (f16 /
  *                          bf16 with d_in % 64 == 0, else 0; the default

@@ -275,7 +275,9 @@ void set_shrink_split(const tpa_layer* L, Config* c) {
 
 Config choose_config(const tpa_layer* L, int n) {
   Config c{};
-  c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : (n <= 256 ? 16 : 64);
+  // 16-row tiles at every n: measured faster than 64 from 512 to 4096 rows
+  // (more work items for the shrink and expand), with identical results.
+  c.tile_rows = L->opt[TPA_OPT_TILE_ROWS] > 0 ? L->opt[TPA_OPT_TILE_ROWS] : 16;
   // Decode (n <= 64): the LDS-streamed kernel for f16 / bf16 with d_in a
   // multiple of 64, else the register-fed one; larger batches: tiled.
   const bool stream_ok = L->dtype != TPA_F32 && L->d_in % 64 == 0;

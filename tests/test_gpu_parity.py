@@ -83,6 +83,20 @@ def test_pinned_prefill_kernels(n, path, stages, d):
     check(y_gpu, y, h, xw, label="pinned path=%d stages=%d n=%d d=%d" % (path, stages, n, d))
 
 
+@pytest.mark.parametrize("n", [100, 300])
+def test_tile_rows_64_pinned(n):
+    """64-row plan tiles (four 16-row blocks per shrink and expand item)
+    against the oracle, ragged."""
+    wl = synth.tiny_mixed(seed=70 + n, n=n, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    say("tile_rows=64 n=%d" % n)
+    L = make_layer(p, max_slots=8, max_rank=32, options={3: 64})
+    assert L.config(n)["tile_rows"] == 64
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="tile_rows=64 n=%d" % n)
+
+
 def test_prefill_lora_dora_q_proj():
     """q_proj 4096 -> 4096, 1024 rows in 16 segments of 64, 8 LoRA + 8 DoRA
     rank 16: every row checked."""

@@ -27,7 +27,8 @@ def _tiny(seed=3, n=64, dtype="f16"):
 
 # ------------------------------------------------------------------ plan ---
 
-@pytest.mark.parametrize("n,tile_rows", [(1, 16), (64, 16), (300, 16), (1000, 64), (4096, 64), (8192, 64)])
+@pytest.mark.parametrize("n,tile_rows", [(1, 16), (64, 16), (300, 16), (1000, 16), (1000, 64), (4096, 16),
+                                         (4096, 64), (8192, 16), (8192, 64)])
 def test_plan_bit_exact_against_oracle(n, tile_rows):
     wl, p = _tiny()
     L = make_layer(p, max_slots=8, max_rank=32, options={3: tile_rows})
