@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--no-pure-lora", action="store_true", help="skip the pure-LoRA comparison batch")
     ap.add_argument("--stage-reps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
+    ap.add_argument("--workload", default="decoder_layer_mixed", choices=("decoder_layer_mixed", "stack"),
+                    help="stack: the 32-layer, 1024-tenant Zipf stack against the byte model")
+    ap.add_argument("--layers", type=int, default=32, help="stack: decoder layers")
+    ap.add_argument("--tenants", type=int, default=1024, help="stack: resident tenants")
+    ap.add_argument("--stack-n", default="16,256,4096", help="stack: batch sizes")
     return ap.parse_args()
 
 
@@ -264,6 +269,117 @@ def cpu_baseline(wl, min_seconds=10.0, chunk=4):
                       % (rows, wl["n"], chunk, len(wl["projections"]), dt)}
 
 
+def stack_main(args):
+    """The full adapter stack: `layers` decoder layers of the seven
+    Llama-3.1-8B projections with `tenants` resident tenants (methods in
+    turn, LoRA/DoRA at rank 64), batches of Zipf(1.1)-drawn rows.  A step is
+    one forward of every projection of every layer on the batch (one row
+    plan, q/k/v and gate/up as groups), captured in one graph.  Measured
+    step time is set beside the byte model (Scute paper §4.3: t0 + ΔQ/β +
+    ΔL·λ), with t0 the same step on identity rows (the base GEMMs and the
+    launches), ΔQ the adapter kernels' algorithmic bytes and ΔL = 0: the
+    identity batch launches the same kernels."""
+    import numpy as np
+    import torch
+    from tenant_peft_adapter_amd import binding as B
+    from tenant_peft_adapter_amd import bytemodel as bm
+    from tenant_peft_adapter_amd.layer import AdaptedLayer, LayerGroup, RowPlan
+    from workloads import stack, synth
+
+    torch.cuda.set_device(0)
+    shapes = synth.LLAMA8B_PROJECTIONS
+    names = [s[0] for s in shapes]
+    ns = [int(v) for v in args.stack_n.split(",")]
+    nmax, T, NL = max(ns), args.tenants, args.layers
+    protos = stack.prototypes()
+    xs = {name: stack.device_input(torch, nmax, d_in, name) for name, d_in, _ in shapes}
+    outs = {name: torch.empty((nmax, d_out), dtype=torch.float16, device="cuda") for name, _, d_out in shapes}
+    log("stack: loading %d tenants into %d layers x 7 projections" % (T, NL))
+    t_load = time.perf_counter()
+    layers = []
+    for li in range(NL):
+        row = []
+        for name, d_in, d_out in shapes:
+            W = stack.device_weight(torch, li, name, d_out, d_in)
+            L = AdaptedLayer(W, max_slots=T + 1, max_rank=256)
+            pr = protos[name]
+            L.set_vera_shared(pr["shared"]["A"], pr["shared"]["B"])
+            for t in range(T):
+                L.load(pr["records"][stack.method_of(t)])
+            row.append(L)
+        layers.append(row)
+        log("stack: layer %d loaded, %.0f s, %.1f GB in use" % (li, time.perf_counter() - t_load,
+                                                                  torch.cuda.mem_get_info()[1] / 1e9 -
+                                                                  torch.cuda.mem_get_info()[0] / 1e9))
+    t_load = time.perf_counter() - t_load
+
+    # Workspaces shared by every layer (one projection runs at a time).
+    qkv, gu = [0, 1, 2], [4, 5]
+    ws_qkv = [torch.empty(max(sz, 256), dtype=torch.uint8, device="cuda")
+              for sz in B.tpa_group_workspace_size([layers[0][i].handle for i in qkv], nmax)]
+    ws_gu = [torch.empty(max(sz, 256), dtype=torch.uint8, device="cuda")
+             for sz in B.tpa_group_workspace_size([layers[0][i].handle for i in gu], nmax)]
+    ws_o = torch.empty(B.tpa_workspace_size(layers[0][3].handle, nmax), dtype=torch.uint8, device="cuda")
+    ws_down = torch.empty(B.tpa_workspace_size(layers[0][6].handle, nmax), dtype=torch.uint8, device="cuda")
+    g_qkv = [LayerGroup([row[i] for i in qkv], nmax, ws=ws_qkv) for row in layers]
+    g_gu = [LayerGroup([row[i] for i in gu], nmax, ws=ws_gu) for row in layers]
+    plan = RowPlan(layers[0][0], nmax)
+
+    def make_step(sor):
+        n = sor.numel()
+        x = {k: v[:n] for k, v in xs.items()}
+        o = {k: v[:n] for k, v in outs.items()}
+
+        def step():
+            plan.build(layers[0][0], sor)
+            for li in range(NL):
+                g_qkv[li].forward(plan, [x["q"], x["k"], x["v"]], [o["q"], o["k"], o["v"]])
+                layers[li][3].forward_planned(plan, x["o"], out=o["o"], ws=ws_o)
+                g_gu[li].forward(plan, [x["gate"], x["up"]], [o["gate"], o["up"]])
+                layers[li][6].forward_planned(plan, x["down"], out=o["down"], ws=ws_down)
+        return step
+
+    beta, lam = calibrate(torch)
+    results = []
+    for n in ns:
+        sor_np = stack.zipf_rows(n, T)
+        sor = torch.tensor(sor_np).cuda()
+        base = torch.zeros(n, dtype=torch.int32, device="cuda")
+        plan.build(layers[0][0], sor)
+        torch.cuda.synchronize()
+        assert all(plan.accepts(L) for row in layers for L in row)
+        steps = max(3, min(50, int(2e6 / (n * NL))))
+        t = {}
+        for tag, rows in (("mixed", sor), ("base", base)):
+            g = capture(make_step(rows), torch)
+            t[tag] = time_graph(g, steps, 2, torch)
+            del g
+        q_ad = q_gemm = fl = 0
+        for name, d_in, d_out in shapes:
+            kb = bm.kernel_bytes(bm.shape_of(n, d_in, d_out, sor_np, stack.adapters_of(protos[name], T),
+                                             r_v=protos[name]["r_v"]))
+            q_gemm += NL * kb["gemm"]["bytes"]
+            fl += NL * kb["gemm"]["flops"]
+            q_ad += NL * sum(v["bytes"] for k, v in kb.items() if k != "gemm")
+        pred = t["base"] + q_ad / beta
+        res = {"n": n, "distinct_tenants": int(len(set(sor_np.tolist()))), "steps": steps,
+               "step_us": round(t["mixed"] * 1e6, 1), "base_step_us": round(t["base"] * 1e6, 1),
+               "adapter_bytes": int(q_ad), "gemm_bytes": int(q_gemm), "gemm_flops": int(fl),
+               "predicted_step_us": round(pred * 1e6, 1), "measured_over_predicted": round(t["mixed"] / pred, 3),
+               "adapter_GBps": round(q_ad / max(t["mixed"] - t["base"], 1e-9) / 1e9, 1),
+               "base_step_mfma_frac": round(fl / t["base"] / MFMA_F16_PEAK, 3),
+               "base_step_hbm_frac": round(q_gemm / t["base"] / HBM_PEAK, 3)}
+        log("stack n=%d: %s" % (n, res))
+        results.append(res)
+    print(json.dumps({
+        "metric": "full adapter stack: measured step time against the byte model",
+        "workload": "stack: %d Llama-3.1-8B decoder layers x 7 projections, fp16, %d resident tenants "
+                    "(LoRA r64, DoRA r64, (IA)3 k/v/up, VeRA r256, OFT b32 in turn), Zipf(1.1) rows" % (NL, T),
+        "data": "synthetic (seeded; raw parameters shared per projection and method, one device copy per tenant)",
+        "load_s": round(t_load, 1), "calibration": {"beta_hbm_GBps": beta / 1e9, "lambda_us": lam * 1e6},
+        "dL_launches": 0, "results": results}))
+
+
 def main():
     args = parse()
     ws = int(os.environ.get("WORLD_SIZE", "1"))
@@ -271,6 +387,8 @@ def main():
         print("bench.py measures one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "stack":
+        return stack_main(args)
     import numpy as np
     import torch
     from tenant_peft_adapter_amd import bytemodel as bm

@@ -210,7 +210,7 @@ tpa_status tpa_layer_forward_planned(tpa_layer* layer, const tpa_plan* plan, con
                                      void* out_dev, void* ws_dev, size_t ws_bytes, tpa_stream stream);
 
 /* Projections of one fused layer (q, k and v; gate and up) forwarded in one
- * launch per kernel (P1 §5.2: one launch covers all slices of a layer), with
+ * launch per kernel (Scute paper §5.2: one launch covers all slices of a layer), with
  * a plan that accepts each of them.  count <= 4; layers[i] with
  * x[i] [n][d_in_i], out[i] [n][d_out_i], ws[i] of ws_bytes[i] bytes (at least
  * tpa_group_workspace_size's bytes[i] for this group; 256-byte aligned).  The

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "internal.h"
@@ -56,7 +57,51 @@ struct DeviceGuard {
 struct HostSlot {
   bool used = false;
   tpa_adapter_info info{};
-  void* mem = nullptr;
+  void* mem = nullptr;  // block from the layer's slot arena
+  size_t bytes = 0;
+};
+
+// Device memory of a layer's slots.  Blocks are carved from chunks of 32
+// blocks' worth (16 MB to 256 MB) and go back to a free list of their exact
+// size on unload, so admitting a tenant mostly allocates nothing, and a
+// layer holding a thousand slots holds a few dozen allocations rather than
+// a thousand (the equal-sized blocks of one method and shape recycle into
+// each other).  A chunk left behind keeps a tail smaller than the block
+// that did not fit.
+struct SlotArena {
+  std::vector<void*> chunks;
+  char* cur = nullptr;
+  size_t left = 0;
+  std::unordered_map<size_t, std::vector<void*>> free_blocks;
+
+  hipError_t take(size_t bytes, void** out) {
+    auto it = free_blocks.find(bytes);
+    if (it != free_blocks.end() && !it->second.empty()) {
+      *out = it->second.back();
+      it->second.pop_back();
+      return hipSuccess;
+    }
+    if (bytes > left) {
+      const size_t sz = std::max(bytes, std::min(std::max(32 * bytes, size_t(16) << 20), size_t(256) << 20));
+      void* c = nullptr;
+      if (hipError_t e = hipMalloc(&c, sz)) return e;
+      chunks.push_back(c);
+      cur = static_cast<char*>(c);
+      left = sz;
+    }
+    *out = cur;
+    cur += bytes;
+    left -= bytes;
+    return hipSuccess;
+  }
+  void give(void* p, size_t bytes) { free_blocks[bytes].push_back(p); }
+  void release() {
+    for (void* c : chunks) (void)hipFree(c);
+    chunks.clear();
+    free_blocks.clear();
+    cur = nullptr;
+    left = 0;
+  }
 };
 
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -192,6 +237,10 @@ struct tpa_layer {
   int opt[9] = {-1, -1, -1, -1, -1, 0, -1, -1, -1};
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
+  SlotArena arena;
+  float* stage = nullptr;        // fp32 staging of an adapter's raw arrays during its load
+  size_t stage_floats = 0;
+  int32_t* status_dev = nullptr; // DoRA's norm check
   uint64_t plan_sig = 0;   // hash of every slot's (term class, has R): what a row plan depends on
   uint64_t class_sig = 0;  // the same over term classes only
   int n_rot = 0;           // loaded slots with an OFT rotation
@@ -484,25 +533,37 @@ int oft_tile_bound(const tpa_layer* L, int n, int tr, int max_tiles) {
   return std::min(max_tiles, (n + tr - 1) / tr + std::min(n, n_rot));
 }
 
-// A device float32 staging copy of a host array.
+// Device float32 staging of an adapter's raw arrays, carved from the
+// layer's staging buffer (grown to `floats` first; loads are serialized on
+// the caller's stream and synchronized before they return, so one buffer
+// serves every load of the layer).
 struct Staging {
-  std::vector<void*> bufs;
-  ~Staging() {
-    for (void* p : bufs) (void)hipFree(p);
-  }
-  tpa_status put(const float* host, size_t count, float** dev) {
+  tpa_layer* L;
+  size_t used = 0;
+  tpa_status reserve(size_t floats) {
+    if (floats <= L->stage_floats) return TPA_OK;
+    if (L->stage) {
+      TPA_HIP(hipDeviceSynchronize());
+      TPA_HIP(hipFree(L->stage));
+      L->stage = nullptr;
+      L->stage_floats = 0;
+    }
     void* p = nullptr;
-    TPA_HIP(hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(float)));
-    bufs.push_back(p);
-    if (count) TPA_HIP(hipMemcpy(p, host, count * sizeof(float), hipMemcpyHostToDevice));
-    *dev = static_cast<float*>(p);
+    TPA_HIP(hipMalloc(&p, floats * sizeof(float)));
+    L->stage = static_cast<float*>(p);
+    L->stage_floats = floats;
     return TPA_OK;
   }
   tpa_status alloc(size_t count, float** dev) {
-    void* p = nullptr;
-    TPA_HIP(hipMalloc(&p, std::max<size_t>(count, 1) * sizeof(float)));
-    bufs.push_back(p);
-    *dev = static_cast<float*>(p);
+    const size_t padded = (std::max<size_t>(count, 1) + 63) / 64 * 64;
+    if (used + padded > L->stage_floats) return fail(TPA_ERR_INVALID, "staging overflow");
+    *dev = L->stage + used;
+    used += padded;
+    return TPA_OK;
+  }
+  tpa_status put(const float* host, size_t count, float** dev, hipStream_t s) {
+    if (tpa_status e = alloc(count, dev)) return e;
+    if (count) TPA_HIP(hipMemcpyAsync(*dev, host, count * sizeof(float), hipMemcpyHostToDevice, s));
     return TPA_OK;
   }
 };
@@ -572,8 +633,9 @@ tpa_status tpa_layer_destroy(tpa_layer* L) {
   if (!L) return TPA_OK;
   DeviceGuard guard(L->device);
   (void)hipDeviceSynchronize();
-  for (auto& h : L->hs)
-    if (h.mem) (void)hipFree(h.mem);
+  L->arena.release();
+  if (L->stage) (void)hipFree(L->stage);
+  if (L->status_dev) (void)hipFree(L->status_dev);
   if (L->vera_mem) (void)hipFree(L->vera_mem);
   if (L->slots_dev) (void)hipFree(L->slots_dev);
   if (L->flag_dev) (void)hipFree(L->flag_dev);
@@ -601,10 +663,12 @@ tpa_status tpa_vera_shared_set(tpa_layer* L, int32_t r_v, const float* A, const 
   const size_t bt_bytes = align256((size_t)L->d_out * r_v * esz);
   TPA_HIP(hipMalloc(&L->vera_mem, at_bytes + bt_bytes));
   char* base = static_cast<char*>(L->vera_mem);
-  Staging st;
+  Staging st{L};
   float *a32, *b32;
-  if (tpa_status e = st.put(A, (size_t)L->d_in * r_v, &a32)) return e;
-  if (tpa_status e = st.put(B, (size_t)r_v * L->d_out, &b32)) return e;
+  if (tpa_status e = st.reserve(((size_t)L->d_in * r_v + 63) / 64 * 64 + ((size_t)r_v * L->d_out + 63) / 64 * 64))
+    return e;
+  if (tpa_status e = st.put(A, (size_t)L->d_in * r_v, &a32, s)) return e;
+  if (tpa_status e = st.put(B, (size_t)r_v * L->d_out, &b32, s)) return e;
   // A [d_in][r_v] -> [r_v][d_in];  B [r_v][d_out] -> [d_out][r_v].
   TPA_HIP(tpa::launch_pack_transpose(L->dtype, a32, L->d_in, r_v, 1.f, nullptr, base, r_v, L->d_in, s));
   TPA_HIP(tpa::launch_pack_transpose(L->dtype, b32, r_v, L->d_out, 1.f, nullptr, base + at_bytes, L->d_out, r_v, s));
@@ -693,16 +757,37 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
   }
   if (m == TPA_OFT) o_R = take((size_t)d_in * d->oft_block * esz);
   void* mem = nullptr;
-  if (off) TPA_HIP(hipMalloc(&mem, off));
+  if (off) TPA_HIP(L->arena.take(off, &mem));
   char* base = static_cast<char*>(mem);
-  Staging st;
-  int32_t* status_dev = nullptr;
+  Staging st{L};
+  {
+    // fp32 staging this load needs (each array padded to 64 floats)
+    auto pad = [](size_t c) { return (std::max<size_t>(c, 1) + 63) / 64 * 64; };
+    size_t need = 0;
+    if (m == TPA_LORA || m == TPA_DORA)
+      need = pad((size_t)d_in * d->rank) + pad((size_t)d->rank * d_out) + pad((size_t)r_pad * d_in) +
+             (m == TPA_DORA ? pad(d_out) : 0);
+    if (m == TPA_OFT) need = pad((size_t)d_in * d->oft_block);
+    if (tpa_status e = st.reserve(need)) {
+      if (mem) L->arena.give(mem, off);
+      return e;
+    }
+  }
+  if (m == TPA_DORA && !L->status_dev) {
+    void* p = nullptr;
+    if (hipError_t e = hipMalloc(&p, sizeof(int32_t))) {
+      if (mem) L->arena.give(mem, off);
+      return fail(TPA_ERR_HIP, "%s", hipGetErrorString(e));
+    }
+    L->status_dev = static_cast<int32_t*>(p);
+  }
+  int32_t* status_dev = m == TPA_DORA ? L->status_dev : nullptr;
   // Conversion to normal form; TPA_HIP returns from this lambda on error.
   auto convert = [&]() -> tpa_status {
     if (m == TPA_LORA || m == TPA_DORA) {
       float *a32, *b32, *at32;
-      if (tpa_status e = st.put(d->A, (size_t)d_in * d->rank, &a32)) return e;
-      if (tpa_status e = st.put(d->B, (size_t)d->rank * d_out, &b32)) return e;
+      if (tpa_status e = st.put(d->A, (size_t)d_in * d->rank, &a32, s)) return e;
+      if (tpa_status e = st.put(d->B, (size_t)d->rank * d_out, &b32, s)) return e;
       // A' = c·A stored [r_pad][d_in] (fold c -> A).
       if (tpa_status e = st.alloc((size_t)r_pad * d_in, &at32)) return e;
       TPA_HIP(tpa::launch_pack_transpose(0, a32, d_in, d->rank, d->c, nullptr, at32, r_pad, d_in, s));
@@ -714,8 +799,7 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
         TPA_HIP(tpa::launch_pack_transpose(L->dtype, b32, d->rank, d_out, 1.f, nullptr, base + o_Bt, d_out, r_pad, s));
       if (m == TPA_DORA) {
         float* m32;
-        if (tpa_status e = st.put(d->m, d_out, &m32)) return e;
-        TPA_HIP(hipMalloc(&status_dev, sizeof(int32_t)));
+        if (tpa_status e = st.put(d->m, d_out, &m32, s)) return e;
         TPA_HIP(hipMemsetAsync(status_dev, 0, sizeof(int32_t), s));
         // s = m ⊘ ‖W + cAB‖_c on the device from W; e = s folds into B
         // unless s is applied after the expand.
@@ -761,7 +845,7 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
       for (int j = 0; j < d_in / bs; ++j)
         cayley_transposed(d->Q + (size_t)j * bs * bs, bs, rt.data() + (size_t)j * bs * bs);
       float* r32;
-      if (tpa_status e = st.put(rt.data(), cnt, &r32)) return e;
+      if (tpa_status e = st.put(rt.data(), cnt, &r32, s)) return e;
       TPA_HIP(tpa::launch_convert(L->dtype, r32, base + o_R, cnt, 1.f, s));
       sd.Rt = base + o_R;
       sd.has_R = 1;
@@ -776,21 +860,22 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
     return TPA_OK;
   };
   tpa_status err = convert();
-  if (status_dev) (void)hipFree(status_dev);
   if (err) {
-    if (mem) (void)hipFree(mem);
+    (void)hipStreamSynchronize(s);
+    if (mem) L->arena.give(mem, off);
     return err;
   }
   L->slots_host[slot] = sd;
   if ((err = upload_slot(L, slot, s))) {
     L->slots_host[slot] = SlotDev{};
     L->slots_host[slot].cls = -1;
-    if (mem) (void)hipFree(mem);
+    if (mem) L->arena.give(mem, off);
     return err;
   }
   HostSlot& h = L->hs[slot];
   h.used = true;
   h.mem = mem;
+  h.bytes = off;
   h.info = tpa_adapter_info{};
   h.info.method = m;
   h.info.term_kind = term;
@@ -818,7 +903,7 @@ tpa_status tpa_adapter_unload(tpa_layer* L, int32_t slot, tpa_stream stream) {
   L->slots_host[slot] = SlotDev{};
   L->slots_host[slot].cls = -1;
   if (tpa_status e = upload_slot(L, slot, s)) return e;
-  if (L->hs[slot].mem) TPA_HIP(hipFree(L->hs[slot].mem));
+  if (L->hs[slot].mem) L->arena.give(L->hs[slot].mem, L->hs[slot].bytes);
   L->hs[slot] = HostSlot{};
   if (info.term_kind == 1) --L->n_owned;
   if (info.term_kind == 2) --L->n_vera;

@@ -157,11 +157,18 @@ class LayerGroup:
     """Projections of one fused layer (q, k, v or gate, up) that share a row
     plan, forwarded with one launch per kernel (tpa_group_forward_planned)."""
 
-    def __init__(self, layers, n_max):
+    def __init__(self, layers, n_max, ws=None):
+        """ws: optional per-projection workspaces to use instead of fresh
+        ones (groups that never run at the same time may share them)."""
         self.layers = list(layers)
         sizes = B.tpa_group_workspace_size([L.handle for L in self.layers], n_max)
-        self.ws = [torch.empty(max(sz, 256), dtype=torch.uint8, device=L.W.device)
-                   for L, sz in zip(self.layers, sizes)]
+        if ws is not None:
+            if len(ws) != len(self.layers) or any(w.numel() < sz for w, sz in zip(ws, sizes)):
+                raise ValueError("shared workspaces too small for this group")
+            self.ws = list(ws)
+        else:
+            self.ws = [torch.empty(max(sz, 256), dtype=torch.uint8, device=L.W.device)
+                       for L, sz in zip(self.layers, sizes)]
 
     def forward(self, plan, xs, outs=None):
         if outs is None:

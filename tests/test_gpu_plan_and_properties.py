@@ -198,6 +198,28 @@ def test_unload_and_reload():
     L.error_flag(clear=True)
 
 
+def test_slot_churn_recycles_blocks():
+    """Unloaded slots return their device block to the layer's arena and
+    later loads reuse it: repeated unload / load / extra-copy cycles leave
+    the outputs bitwise unchanged."""
+    wl, p = _tiny(seed=12)
+    L = make_layer(p, max_slots=12, max_rank=32)
+    sor = wl["slot_of_row"]
+    y0 = run(L, p["x"], sor, "f16")
+    for _ in range(3):
+        L.unload(2)
+        L.unload(1)
+        assert L.load(p["adapters"][1]) == 1
+        assert L.load(p["adapters"][2]) == 2
+        extra = [L.load(p["adapters"][k]) for k in (2, 1, 5)]
+        assert extra == [6, 7, 8]
+        for slot in extra:
+            L.unload(slot)
+    y1 = run(L, p["x"], sor, "f16")
+    assert np.array_equal(y0, y1)
+    assert L.error_flag(clear=True) == 0
+
+
 def test_error_codes():
     from tenant_peft_adapter_amd import binding as B
     wl, p = _tiny(seed=9)
