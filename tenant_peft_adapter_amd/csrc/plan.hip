@@ -45,6 +45,20 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave in registers: four
+// row shifts (within each 16-lane row), then the last lane of row 0 and 2
+// added into rows 1 and 3, then lane 31 into rows 2 and 3.  Lanes whose
+// source lies outside the row keep the identity (0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum over a work-group of T threads; the total goes to
 // *total.  `scratch` holds T / 64 ints; callers may run scans back to back.
 template <int T>
@@ -52,14 +66,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   constexpr int W = T / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
+  const int incl = (int)wave_incl_scan((uint32_t)v);
   if (W == 1) {
-    *total = __shfl(incl, 63, 64);
+    *total = __builtin_amdgcn_readlane(incl, 63);
     return incl - v;
   }
   if (lane == 63) scratch[wave] = incl;
@@ -79,7 +88,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 // Exclusive scan across the work-group of eight packed words per thread
 // (sixteen 16-bit counters; no field ever exceeds n <= 8192, so no carry
 // crosses a field).  excl gets this thread's exclusive prefix, total the
-// work-group's sums.  scratch holds 8 words per wave.
+// work-group's sums.  scratch holds 8 words per wave, 16-byte aligned.
 template <int T>
 __device__ __forceinline__ void block_scan8(const uint32_t (&v)[8], uint32_t (&excl)[8], uint32_t (&total)[8],
                                             uint32_t* scratch) {
@@ -87,38 +96,39 @@ __device__ __forceinline__ void block_scan8(const uint32_t (&v)[8], uint32_t (&e
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t incl[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    incl[q] = v[q];
+  for (int q = 0; q < 8; ++q) incl[q] = wave_incl_scan(v[q]);
+  if (lane == 63) {
+    uint4* d = reinterpret_cast<uint4*>(scratch + 8 * wave);
+    d[0] = make_uint4(incl[0], incl[1], incl[2], incl[3]);
+    d[1] = make_uint4(incl[4], incl[5], incl[6], incl[7]);
+  }
+  lds_barrier();
+  uint32_t off[8] = {}, tot[8] = {};
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t t = (uint32_t)__shfl_up((int)incl[q], off, 64);
-      if (lane >= off) incl[q] += t;
+  for (int w = 0; w < W; ++w) {
+    const uint4* sw = reinterpret_cast<const uint4*>(scratch + 8 * w);
+    const uint4 lo = sw[0], hi = sw[1];
+    const uint32_t x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (w < wave) off[q] += x[q];
+      tot[q] += x[q];
     }
   }
-  if (lane == 63)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) scratch[8 * wave + q] = incl[q];
-  lds_barrier();
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    uint32_t off = 0, tot = 0;
-    for (int w = 0; w < W; ++w) {
-      const uint32_t x = scratch[8 * w + q];
-      if (w < wave) off += x;
-      tot += x;
-    }
-    excl[q] = off + incl[q] - v[q];
-    total[q] = tot;
+    excl[q] = off[q] + incl[q] - v[q];
+    total[q] = tot[q];
   }
   lds_barrier();
 }
 
-template <int T, bool RANK>
+template <int T, bool RANK, int TM>
 __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
   constexpr int EMAX = 8;  // elements per thread (n <= 8 T)
   extern __shared__ __attribute__((aligned(16))) uint32_t sm[];
   __shared__ int scan_scratch[T / 64 > 0 ? T / 64 : 1];
-  __shared__ uint32_t scan8_scratch[8 * (T / 64)];
+  __shared__ __attribute__((aligned(16))) uint32_t scan8_scratch[8 * (T / 64)];
   __shared__ int s_cls[4];
   __shared__ int s_bad;
   const int n = a.n;
@@ -130,21 +140,46 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
   uint16_t* own_first = seg_of_pos + n;                         // [n]: first owned tile of a segment
   uint16_t* oft_first = own_first + n;                          // [n]: first OFT tile of a segment
 
-  // 1. Effective slot and key per row (the only global reads).
+  // 1. Effective slot and key per row (the only global reads).  Each thread
+  //    takes a contiguous run of at most EMAX rows; all its slot ids are
+  //    loaded before any slot record, so a thread waits for two round trips
+  //    whatever its run length.
   if (tid == 0) s_bad = 0;
   lds_barrier();
+  const int E = (n + T - 1) / T;
+  const int e_lo = min(n, tid * E), e_hi = min(n, e_lo + E);
   int bad = 0;
-  for (int i = tid; i < n; i += T) {
-    int s = a.slot_of_row[i];
-    if (!(s >= 0 && s < a.max_slots && a.slots[s].cls >= 0)) {
-      s = 0;
-      bad = 1;
+  {
+    int sv[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) sv[e] = e_lo + e < e_hi ? a.slot_of_row[e_lo + e] : 0;
+    // The record's first 16 bytes, as two 8-byte halves (records are 8-byte
+    // aligned): (cls, rank) and (has_R, oft_block).
+    int2 rec[EMAX], rot2[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      const bool in = e_lo + e < e_hi && sv[e] >= 0 && sv[e] < a.max_slots;
+      const int2* r = reinterpret_cast<const int2*>(a.slots + (in ? sv[e] : 0));
+      rec[e] = in ? r[0] : make_int2(-1, 0);
+      rot2[e] = in ? r[1] : make_int2(0, 0);
     }
-    const SlotDev& sd = a.slots[s];
-    const int cls = (s == 0) ? CLS_NONE : sd.cls;
-    const int rot = (s != 0 && sd.has_R) ? 1 : 0;
-    kbuf0[i] = ((uint32_t)cls << 30) | ((uint32_t)s << 16) | ((uint32_t)rot << ROW_BITS) | (uint32_t)i;
-    a.row_slot[i] = s;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      const int i = e_lo + e;
+      if (i >= e_hi) continue;
+      int s = sv[e];
+      int cls = rec[e].x, rot = rot2[e].x ? 1 : 0;
+      if (!(s >= 0 && s < a.max_slots && cls >= 0)) {
+        s = 0;
+        bad = 1;
+      }
+      if (s == 0) {
+        cls = CLS_NONE;
+        rot = 0;
+      }
+      kbuf0[i] = ((uint32_t)cls << 30) | ((uint32_t)s << 16) | ((uint32_t)rot << ROW_BITS) | (uint32_t)i;
+      a.row_slot[i] = s;
+    }
   }
   if (__any(bad) && (tid & 63) == 0) atomicOr(&s_bad, 1);
   lds_barrier();
@@ -153,8 +188,6 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
   // 2. Sort.  Small batches: each key's rank is the count of smaller keys
   //    (keys are distinct).  Otherwise a stable LSD radix sort on bucket =
   //    class * max_slots + slot.
-  const int E = (n + T - 1) / T;
-  const int e_lo = min(n, tid * E), e_hi = min(n, e_lo + E);
   const uint32_t nbucket = 3u * (uint32_t)a.max_slots;
   int passes = 0;
   while (!RANK && ((nbucket - 1) >> (4 * passes))) ++passes;
@@ -268,7 +301,6 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
   //    owned and OFT tile; then every position writes its own row word, and
   //    the positions that start a tile write its header (and -1 over the
   //    unused words of a short tile).
-  const int TM = a.tile_rows;
   const int schunk = (nseg + T - 1) / T;
   const int j_lo = min(nseg, tid * schunk), j_hi = min(nseg, j_lo + schunk);
   int own = 0, oft = 0;
@@ -355,10 +387,16 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
   }
 }
 
+// Tile rows are a template argument so the tile arithmetic is shifts.
 template <int T, bool RANK>
 hipError_t plan_launch(const PlanArgs& a, hipStream_t stream) {
   const size_t lds = 2 * (size_t)a.n * sizeof(uint32_t) + (4 * (size_t)a.n + 2) * sizeof(uint16_t);
-  hipLaunchKernelGGL((plan_kernel<T, RANK>), dim3(1), dim3(T), lds, stream, a);
+  if (a.tile_rows == 16)
+    hipLaunchKernelGGL((plan_kernel<T, RANK, 16>), dim3(1), dim3(T), lds, stream, a);
+  else if (a.tile_rows == 64)
+    hipLaunchKernelGGL((plan_kernel<T, RANK, 64>), dim3(1), dim3(T), lds, stream, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -369,6 +407,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
   if (a.max_slots < 1 || a.max_slots > 16383) return hipErrorInvalidValue;
   if (a.n <= 64) return plan_launch<64, true>(a, stream);
   if (a.n <= 256) return plan_launch<256, true>(a, stream);
+  if (a.n <= 2048) return plan_launch<256, false>(a, stream);
   return plan_launch<1024, false>(a, stream);
 }
 
