@@ -1123,11 +1123,12 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
-        if (c.gemm_path == 3)
-          TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i].g, s));
-        else
+        if (c.gemm_path == 3) {
+          TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i], s));  // carries the shrink's reduction
+        } else {
           TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
-        if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
+          if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
+        }
       }
     }
   }

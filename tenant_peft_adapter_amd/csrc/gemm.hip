@@ -535,19 +535,27 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
 // the whole 160 KB) measured no faster even where a CU holds one
 // work-group: the slices' trip from L2 into LDS, not their latency, sets
 // the pace.  Per slice each wave waits for its own loads, then the
-// work-group meets at a barrier.  Tiles are handed to work-groups so that each XCD (work-group i
-// runs on XCD i % 8) takes a contiguous run of column tiles over every row
-// tile: the slices of x and W its CUs read together stay in its L2.
+// work-group meets at a barrier.  Tiles are handed to work-groups so that
+// each XCD (work-group i runs on XCD i % 8) takes a contiguous run of column
+// tiles over every row tile: the slices of x and W its CUs read together
+// stay in its L2.  Work-groups past the tiles (first split only) run the
+// shrink's split reduction, which needs nothing from the GEMM: it fills the
+// room a CU has beside its tile instead of a launch of its own.
 template <typename T, int S>
-__global__ __launch_bounds__(256) void gemm_wide_kernel(BaseGemmArgs a, int row_tiles, int col_tiles) {
+__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_tiles, int col_tiles) {
   typedef typename Frag<T>::V Vt;
   constexpr int STAGE = 256 * 128;
   constexpr int LI = 8;  // loads per wave per slice
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const BaseGemmArgs& a = sl.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int wr = wave & 1, wc = wave >> 1;
   const int ntile = row_tiles * col_tiles;
+  if ((int)blockIdx.x >= ntile) {
+    if (blockIdx.y == 0) shrink_impl::shrink_reduce_item<T>(sl.side, ((int)blockIdx.x - ntile) * 256 + tid);
+    return;
+  }
   int t = (int)blockIdx.x;
   if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
   const int rt = t % row_tiles, ct = t / row_tiles;
@@ -783,19 +791,20 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_wide(int dtype, int stages, const BaseGemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& sl, hipStream_t s) {
+  const BaseGemmArgs& a = sl.g;
   if (a.n <= 0 || a.d_out % 128 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in)
     return hipErrorInvalidValue;
   if (stages < 2 || stages > 5 || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
   const int row_tiles = (a.n + 127) / 128, col_tiles = a.d_out / 128;
-  const dim3 grid((unsigned)(row_tiles * col_tiles), (unsigned)a.split);
+  const dim3 grid((unsigned)(row_tiles * col_tiles + side_workgroups(sl, 256)), (unsigned)a.split);
   const size_t lds = (size_t)stages * 256 * 128;
 #define TPA_WIDE(SV)                                                                                         \
   if (stages == SV) {                                                                                        \
     if (dtype == 1)                                                                                          \
-      hipLaunchKernelGGL((gemm_wide_kernel<f16, SV>), grid, dim3(256), lds, s, a, row_tiles, col_tiles);     \
+      hipLaunchKernelGGL((gemm_wide_kernel<f16, SV>), grid, dim3(256), lds, s, sl, row_tiles, col_tiles);    \
     else                                                                                                     \
-      hipLaunchKernelGGL((gemm_wide_kernel<bf16, SV>), grid, dim3(256), lds, s, a, row_tiles, col_tiles);    \
+      hipLaunchKernelGGL((gemm_wide_kernel<bf16, SV>), grid, dim3(256), lds, s, sl, row_tiles, col_tiles);   \
   }
   TPA_WIDE(2) TPA_WIDE(3) TPA_WIDE(4) TPA_WIDE(5)
 #undef TPA_WIDE

@@ -93,10 +93,6 @@ struct BaseGemmArgs {
 constexpr size_t GEMM_SKINNY_MAX_LDS = 144 * 1024;
 size_t gemm_skinny_lds(int dtype, int n, int nb, int groups, int kc);
 // LDS-tiled 128x128 kernel; writes `out` when split == 1, else `part`.
-// n > 64, f16 / bf16: 128 x 128 tiles fed by direct global-to-LDS loads
-// (d_out % 128 == 0, d_in and kc multiples of 64) through a ring of `stages`
-// 32 KB LDS buffers (2..5).
-hipError_t launch_gemm_wide(int dtype, int stages, const BaseGemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_tiled(int dtype, const BaseGemmArgs& a, hipStream_t stream);
 
 // Shrink over the plan's tiles: owned-term tiles V[p] = x[perm[p]] A'ᵀ,
@@ -154,6 +150,11 @@ hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* sl
 // (1 or 2), `stages` LDS buffers per group (groups 1: 3, 4 or 6; groups 2: 3).
 constexpr size_t GEMM_STREAM_MAX_LDS = 160 * 1024;
 size_t gemm_stream_lds(int n, int nb, int groups, int stages);
+// n > 64, f16 / bf16: 128 x 128 tiles fed by direct global-to-LDS loads
+// (d_out % 128 == 0, d_in and kc multiples of 64) through a ring of `stages`
+// 32 KB LDS buffers (2..5); writes `out` when split == 1, else `part`.  With
+// has_side, extra work-groups run the shrink's split reduction.
+hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& slice, hipStream_t stream);
 hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const GemmSlice* slices, int count,
                               hipStream_t stream);
 // The shrink's split reduction on its own (when the GEMM cannot carry it).
