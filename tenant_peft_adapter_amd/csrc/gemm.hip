@@ -536,9 +536,9 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
 // work-group: the slices' trip from L2 into LDS, not their latency, sets
 // the pace.  Per slice each wave waits for its own loads, then the
 // work-group meets at a barrier.  Tiles are handed to work-groups so that
-// each XCD (work-group i runs on XCD i % 8) takes a contiguous run of column
-// tiles over every row tile: the slices of x and W its CUs read together
-// stay in its L2.  Work-groups past the tiles (first split only) run the
+// each XCD (work-group i runs on XCD i % 8) takes a contiguous run of the
+// tile order below: the slices of x and W its CUs read together stay in its
+// L2.  Work-groups past the tiles (first split only) run the
 // shrink's split reduction, which needs nothing from the GEMM: it fills the
 // room a CU has beside its tile instead of a launch of its own.
 template <typename T, int S>
@@ -558,7 +558,12 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_ti
   }
   int t = (int)blockIdx.x;
   if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-  const int rt = t % row_tiles, ct = t / row_tiles;
+  // Tile order: strips of 8 row tiles, column by column, so the ~64 tiles
+  // an XCD runs at once form an 8 x 8 block reading 8 slices of x and 8 of
+  // W (each slice used 8 times from L2), not a column of every row tile.
+  const int strip = 8 * col_tiles;
+  const int r_first = (t / strip) * 8, r_rows = min(8, row_tiles - r_first);
+  const int rt = r_first + (t % strip) % r_rows, ct = (t % strip) / r_rows;
   const int row0 = rt * 128, col0 = ct * 128;
   const int ks = blockIdx.y;
   const int kbeg = ks * a.kc;
