@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=32, help="stack: decoder layers")
     ap.add_argument("--tenants", type=int, default=1024, help="stack: resident tenants")
     ap.add_argument("--stack-n", default="16,256,4096", help="stack: batch sizes")
+    ap.add_argument("--stack-eager", choices=("mixed", "base"), default=None,
+                    help="stack: two eager steps per batch size on Zipf (mixed) or identity (base) rows and the "
+                         "byte model's bytes per kernel class, no timing (for hardware counters)")
     return ap.parse_args()
 
 
@@ -338,6 +341,34 @@ def stack_main(args):
                 g_gu[li].forward(plan, [x["gate"], x["up"]], [o["gate"], o["up"]])
                 layers[li][6].forward_planned(plan, x["down"], out=o["down"], ws=ws_down)
         return step
+
+    if args.stack_eager:
+        # Two eager steps per batch size (the first warms caches and code);
+        # the byte model's algorithmic bytes per kernel class for one step.
+        # One 1 GiB device copy first: the reference that scales the
+        # hardware byte counters.
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        del src, dst
+        out = []
+        for n in ns:
+            sor_np = stack.zipf_rows(n, T) if args.stack_eager == "mixed" else np.zeros(n, np.int32)
+            step = make_step(torch.tensor(sor_np).cuda())
+            for _ in range(2):
+                step()
+            torch.cuda.synchronize()
+            per = {}
+            for name, d_in, d_out in shapes:
+                kb = bm.kernel_bytes(bm.shape_of(n, d_in, d_out, sor_np, stack.adapters_of(protos[name], T),
+                                                 r_v=protos[name]["r_v"]))
+                for k, v in kb.items():
+                    per[k] = per.get(k, 0) + NL * v["bytes"]
+            out.append({"n": n, "rows": args.stack_eager, "bytes_per_step": per})
+        print(json.dumps({"workload": "stack eager steps", "layers": NL, "tenants": T, "results": out}))
+        return
 
     beta, lam = calibrate(torch)
     results = []
