@@ -17,6 +17,12 @@ paperpeel.com):
              block-diagonal orthogonal R whose blocks are Cayley transforms
              of skew-symmetric matrices; the base layer is then unchanged.
   * SSF   -- §3.1 and Table 1: scale s and shift b on the output.
+  * Stack -- §3.2 (paragraph "Stacking") and the appendix paragraph of that
+             name: a second member applied at the same hook takes the first
+             member's output in place of its own base output xW; its terms
+             still read x.  Only the first member may transform the input
+             (OFT), since a later member's base path is the previous output,
+             not xW.
 
 All arithmetic is numpy float64.  Matrices use the paper's row convention:
 x [N, d_in], W [d_in, d_out], A [d_in, r], B [r, d_out].
@@ -30,10 +36,11 @@ Adapter records are plain dicts::
     {"method": "vera", "d": d, "e": e, "c": c}      # + shared {"A": Av, "B": Bv}
     {"method": "oft",  "Q": Q}                       # Q: [d_in / b, b, b] skew
     {"method": "ssf",  "s": s, "b": b}
+    {"method": "stack", "members": [rec1, rec2, ...]}   # applied in order
 """
 import numpy as np
 
-METHODS = ("identity", "lora", "dora", "ia3", "vera", "oft", "ssf")
+METHODS = ("identity", "lora", "dora", "ia3", "vera", "oft", "ssf", "stack")
 
 
 def _f64(a):
@@ -117,6 +124,41 @@ def direct_forward(x, W, adapter, shared=None):
     if meth == "oft":
         R = oft_rotation(adapter["Q"])
         return (x @ R) @ W
+    if meth == "stack":
+        members = adapter["members"]
+        y = direct_forward(x, W, members[0], shared)
+        for mem in members[1:]:
+            y = applied_to(y, x, W, mem, shared)
+        return y
+    raise ValueError("unknown method %r" % (meth,))
+
+
+def applied_to(y, x, W, adapter, shared=None):
+    """A member applied at a hook whose base output is already y (the
+    previous member's output) instead of xW: each method's definition with
+    xW replaced by y.  DoRA's magnitude still rescales the columns of its
+    own adapted weight W + cAB, so its scale comes from W as on its own."""
+    y = _f64(y)
+    x = _f64(x)
+    meth = adapter["method"]
+    if meth == "identity":
+        return y.copy()
+    if meth == "lora":
+        A, B, c = _f64(adapter["A"]), _f64(adapter["B"]), float(adapter["c"])
+        return y + c * ((x @ A) @ B)
+    if meth == "dora":
+        A, B, c = _f64(adapter["A"]), _f64(adapter["B"]), float(adapter["c"])
+        return (y + c * ((x @ A) @ B)) * dora_scale(W, A, B, c, adapter["m"])
+    if meth == "ia3":
+        return y * _f64(adapter["l"])
+    if meth == "ssf":
+        return y * _f64(adapter["s"]) + _f64(adapter["b"])
+    if meth == "vera":
+        Av, Bv = _f64(shared["A"]), _f64(shared["B"])
+        c = float(adapter.get("c", 1.0))
+        return y + c * ((((x @ Av) * _f64(adapter["d"])) @ Bv) * _f64(adapter["e"]))
+    if meth == "oft":
+        raise ValueError("only the first member of a stack may transform the input")
     raise ValueError("unknown method %r" % (meth,))
 
 
@@ -125,4 +167,6 @@ def input_transform(adapter, d_in):
     h = (xR)W that the parity bound is measured against."""
     if adapter["method"] == "oft":
         return oft_rotation(adapter["Q"])
+    if adapter["method"] == "stack":
+        return input_transform(adapter["members"][0], d_in)
     return np.eye(d_in)

@@ -67,6 +67,12 @@ def unfolded_slots(adapter, W, shared=None):
         out["R"] = oft_rotation(adapter["Q"])
         out["owned"] = {"R"}
         return out
+    if meth == "stack":
+        members = adapter["members"]
+        out = unfolded_slots(members[0], W, shared)
+        for mem in members[1:]:
+            out = stack(out, unfolded_slots(mem, W, shared))
+        return out
     raise ValueError("unknown method %r" % (meth,))
 
 

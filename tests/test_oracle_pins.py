@@ -462,7 +462,8 @@ def test_parity_metrics_simple():
 def test_pins_detect_planted_mistakes(monkeypatch):
     """Plant plausible mistakes in the oracle (on the CPU) and check that a
     pin fails for each: the other Cayley convention, the DoRA norm over the
-    wrong axis, a dropped c, a transposed shared factor."""
+    wrong axis, a dropped c, a transposed shared factor, a stacked scale
+    that skips the previous member's update."""
     gold = _load("hand_examples.json")
     x = np.array(gold["x"], dtype=np.float64)
     cases = {c["name"]: c for c in gold["cases"]}
@@ -503,3 +504,107 @@ def test_pins_detect_planted_mistakes(monkeypatch):
         return orig_dforward(x_, W_, ad, shared)
     monkeypatch.setattr(oracle, "direct_forward", bad_vera)
     assert not run("vera")
+    monkeypatch.setattr(oracle, "direct_forward", orig_dforward)
+    # 5. A stacked scale applied to the base output only, not to the
+    #    previous member's update (the order would then not matter).
+    st = gold["stacking"]
+    W2 = np.array(st["W"], dtype=np.float64)
+    rec = {"method": "stack", "members": [_arr(st["lora"]), _arr(st["ia3"])]}
+    assert np.array_equal(om.direct_forward(x, W2, rec), st["ia3_after_lora"])
+    orig_applied = om.applied_to
+
+    def bad_applied(y_, x_, W_, ad, shared=None):
+        if ad["method"] == "ia3":
+            return (x_ @ W_) * ad["l"] + (y_ - x_ @ W_)
+        return orig_applied(y_, x_, W_, ad, shared)
+    monkeypatch.setattr(om, "applied_to", bad_applied)
+    assert not np.array_equal(om.direct_forward(x, W2, rec), st["ia3_after_lora"])
+
+
+# ------------------------------------------------------ stacked records ----
+
+def _member(rng, meth, d_in, d_out, r=2, r_v=3, bs=2):
+    if meth == "lora":
+        return {"method": "lora", "A": rng.standard_normal((d_in, r)), "B": rng.standard_normal((r, d_out)), "c": 1.5}
+    if meth == "dora":
+        return {"method": "dora", "A": rng.standard_normal((d_in, r)), "B": rng.standard_normal((r, d_out)), "c": 0.5,
+                "m": rng.uniform(1, 2, d_out)}
+    if meth == "ia3":
+        return {"method": "ia3", "l": rng.uniform(0.5, 1.5, d_out)}
+    if meth == "ssf":
+        return {"method": "ssf", "s": rng.uniform(0.5, 1.5, d_out), "b": rng.standard_normal(d_out)}
+    if meth == "vera":
+        return {"method": "vera", "d": rng.uniform(0.5, 1.5, r_v), "e": rng.uniform(0.5, 1.5, d_out), "c": 2.0}
+    if meth == "oft":
+        return {"method": "oft", "Q": _skew(rng, d_in // bs, bs)}
+    return {"method": "identity"}
+
+
+STACKABLE = ("identity", "lora", "dora", "ia3", "ssf", "vera")
+
+
+@pytest.mark.parametrize("first", STACKABLE + ("oft",))
+def test_stack_record_equals_the_appendix_closed_form(first):
+    # Sequential application (each member's definition on the previous
+    # output) equals eq. (1) with the appendix's composed slots, for every
+    # pair and a triple: s1⊙s2, b1⊙s2 + b2, F1's terms times s2.
+    rng = np.random.default_rng(21)
+    d_in, d_out = 8, 6
+    x = rng.standard_normal((5, d_in))
+    W = rng.standard_normal((d_in, d_out))
+    shared = {"A": rng.standard_normal((d_in, 3)), "B": rng.standard_normal((3, d_out))}
+    for second in STACKABLE:
+        for third in (None, "ia3", "lora"):
+            members = [_member(rng, first, d_in, d_out), _member(rng, second, d_in, d_out)]
+            if third:
+                members.append(_member(rng, third, d_in, d_out))
+            rec = {"method": "stack", "members": members}
+            direct = om.direct_forward(x, W, rec, shared)
+            slots = nf.unfolded_slots(rec, W, shared)
+            composed = nf.normal_form_eval(x, W, slots)
+            scale = np.max(np.abs(direct))
+            np.testing.assert_allclose(direct, composed, rtol=0, atol=1e-12 * scale)
+            # folded slots (what a loader stores) give the same output
+            folded, _ = nf.fold(slots)
+            np.testing.assert_allclose(nf.normal_form_eval(x, W, folded), direct, rtol=0, atol=1e-12 * scale)
+
+
+def test_stack_record_hand_example():
+    gold = _load("hand_examples.json")
+    st = gold["stacking"]
+    x = np.array(gold["x"], dtype=np.float64)
+    W = np.array(st["W"], dtype=np.float64)
+    lora, ia3 = _arr(st["lora"]), _arr(st["ia3"])
+    np.testing.assert_array_equal(om.direct_forward(x, W, {"method": "stack", "members": [lora, ia3]}),
+                                  st["ia3_after_lora"])
+    np.testing.assert_array_equal(om.direct_forward(x, W, {"method": "stack", "members": [ia3, lora]}),
+                                  st["lora_after_ia3"])
+
+
+def test_stack_integer_inputs_exact():
+    # Integer values keep every product exact in float64: SSF then LoRA then
+    # (IA)3 must equal ((xW⊙s + b) + c(xA)B)⊙l written out by hand.
+    rng = np.random.default_rng(5)
+    d_in, d_out = 6, 4
+    ri = lambda *s: rng.integers(-3, 4, size=s).astype(np.float64)
+    x, W = ri(3, d_in), ri(d_in, d_out)
+    ssf = {"method": "ssf", "s": ri(d_out), "b": ri(d_out)}
+    lora = {"method": "lora", "A": ri(d_in, 2), "B": ri(2, d_out), "c": 2.0}
+    ia3 = {"method": "ia3", "l": ri(d_out)}
+    want = ((x @ W) * ssf["s"] + ssf["b"] + 2.0 * ((x @ lora["A"]) @ lora["B"])) * ia3["l"]
+    got = om.direct_forward(x, W, {"method": "stack", "members": [ssf, lora, ia3]})
+    np.testing.assert_array_equal(got, want)
+
+
+def test_stack_input_transform_only_first():
+    rng = np.random.default_rng(6)
+    d_in, d_out = 4, 3
+    x, W = rng.standard_normal((2, d_in)), rng.standard_normal((d_in, d_out))
+    oft = _member(rng, "oft", d_in, d_out)
+    ia3 = _member(rng, "ia3", d_in, d_out)
+    R = om.oft_rotation(oft["Q"])
+    got = om.direct_forward(x, W, {"method": "stack", "members": [oft, ia3]})
+    np.testing.assert_allclose(got, ((x @ R) @ W) * ia3["l"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(om.input_transform({"method": "stack", "members": [oft, ia3]}, d_in), R)
+    with pytest.raises(ValueError):
+        om.direct_forward(x, W, {"method": "stack", "members": [ia3, oft]})
