@@ -63,8 +63,12 @@ enum tpa_method {
   TPA_IA3 = 3,
   TPA_VERA = 4,
   TPA_OFT = 5,
-  TPA_SSF = 6
+  TPA_SSF = 6,
+  TPA_STACK = 7 /* reported by tpa_adapter_info_get for a stacked slot; not loadable by itself */
 };
+
+/* Most members in one stack (tpa_adapter_load_stack). */
+#define TPA_MAX_STACK 8
 
 /* Raw parameters of one adapter (host memory, float32, copied before
  * tpa_adapter_load returns).  Fields a method does not use are ignored.
@@ -149,6 +153,31 @@ tpa_status tpa_vera_shared_set(tpa_layer* layer, int32_t r_v, const float* A, co
  * skew-symmetric, a non-finite value, or a zero column norm. */
 tpa_status tpa_adapter_load(tpa_layer* layer, const tpa_adapter_desc* desc, int32_t* slot_out,
                             tpa_stream stream);
+
+/* Admit a stack of adapters at this hook as one slot (§3.2 paragraph
+ * "Stacking", appendix "Stacking"): members[0] is applied first, and each
+ * later member takes the previous member's output in place of its base
+ * output xW (its terms still read x).  The result is one member of eq. (1):
+ * scale s_1⊙…⊙s_K, shift folded through the later scales (b1⊙s2 + b2 for
+ * two members), and every member's term multiplied by the scales of the
+ * members after it through its outer vector e.  Order matters.
+ *   members: `count` raw descriptors (1 <= count <= TPA_MAX_STACK), each
+ *            valid for tpa_adapter_load; host memory, copied before return.
+ *            Only members[0] may be TPA_OFT (a later member's base path is
+ *            the previous output, so it cannot rotate the input).
+ * Storage: a stack whose only term is one VeRA term stays a shared-term
+ * slot (d' = c·d, e' = e ⊙ later scales); otherwise all terms become one
+ * owned term whose rank is the sum of the members' ranks (a VeRA term
+ * enters in its exact owned form A_v diag(c·d), B_v diag(e'), from the
+ * layer's stored pair), which must not exceed max_rank.  DoRA members get
+ * their scale from the device norm kernel as in tpa_adapter_load; the
+ * composition runs on the host in float64.  count == 1 is tpa_adapter_load.
+ * tpa_adapter_info_get reports method TPA_STACK.  Synchronizes `stream`.
+ * Errors: as tpa_adapter_load; -1 also for a count out of range, OFT after
+ * the first member, a stacked rank above max_rank, or a layer whose scale
+ * route applies s after the expand (TPA_OPT_SCALE_ROUTE >= 2). */
+tpa_status tpa_adapter_load_stack(tpa_layer* layer, const tpa_adapter_desc* members, int32_t count,
+                                  int32_t* slot_out, tpa_stream stream);
 
 /* Free a slot.  Synchronizes `stream` before releasing device memory, so
  * forwards enqueued on it earlier still see the adapter.  -4 if the slot is

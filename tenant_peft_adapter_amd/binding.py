@@ -26,7 +26,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tpa.h")
 
 TPA_F32, TPA_F16, TPA_BF16 = 0, 1, 2
 DTYPES = {"f32": TPA_F32, "f16": TPA_F16, "bf16": TPA_BF16}
-METHODS = {"identity": 0, "lora": 1, "dora": 2, "ia3": 3, "vera": 4, "oft": 5, "ssf": 6}
+METHODS = {"identity": 0, "lora": 1, "dora": 2, "ia3": 3, "vera": 4, "oft": 5, "ssf": 6, "stack": 7}
 (TPA_OPT_GEMM_SPLIT, TPA_OPT_SHRINK_SPLIT, TPA_OPT_TILE_ROWS, TPA_OPT_GEMM_PATH, TPA_OPT_SCALE_ROUTE,
  TPA_OPT_GEMM_NB, TPA_OPT_GEMM_GROUPS, TPA_OPT_GEMM_STAGES) = 1, 2, 3, 4, 5, 6, 7, 8
 LIVE_S, LIVE_B, LIVE_R, LIVE_D, LIVE_E = 1, 2, 4, 8, 16
@@ -74,6 +74,7 @@ def _load():
         "tpa_layer_destroy": [vp],
         "tpa_vera_shared_set": [vp, i32, vp, vp, vp],
         "tpa_adapter_load": [vp, P(tpa_adapter_desc), P(i32), vp],
+        "tpa_adapter_load_stack": [vp, P(tpa_adapter_desc), i32, P(i32), vp],
         "tpa_adapter_unload": [vp, i32, vp],
         "tpa_adapter_info_get": [vp, i32, P(tpa_adapter_info)],
         "tpa_workspace_size": [vp, i32, P(sz)],
@@ -168,13 +169,33 @@ def tpa_vera_shared_set(layer, r_v, A, B, stream=0):
     _check(_lib.tpa_vera_shared_set(layer, r_v, _ptr(A), _ptr(B), stream))
 
 
-def tpa_adapter_load(layer, method, rank=0, oft_block=0, c=1.0, A=None, B=None, m=None, l=None, d=None,
-                     e=None, Q=None, s=None, b=None, stream=0):
+def _desc(method, rank=0, oft_block=0, c=1.0, A=None, B=None, m=None, l=None, d=None, e=None, Q=None, s=None,
+          b=None):
+    """A tpa_adapter_desc and the float32 arrays it points into (keep both
+    alive until the call returns)."""
     keep = {k: _f32(v) for k, v in dict(A=A, B=B, m=m, l=l, d=d, e=e, Q=Q, s=s, b=b).items()}
     desc = tpa_adapter_desc(METHODS.get(method, method), rank, oft_block, c,
                             *[_ptr(keep[k]) for k in ("A", "B", "m", "l", "d", "e", "Q", "s", "b")])
+    return desc, keep
+
+
+def tpa_adapter_load(layer, method, rank=0, oft_block=0, c=1.0, A=None, B=None, m=None, l=None, d=None,
+                     e=None, Q=None, s=None, b=None, stream=0):
+    desc, keep = _desc(method, rank, oft_block, c, A, B, m, l, d, e, Q, s, b)
     slot = ctypes.c_int32()
     _check(_lib.tpa_adapter_load(layer, ctypes.byref(desc), ctypes.byref(slot), stream))
+    del keep
+    return slot.value
+
+
+def tpa_adapter_load_stack(layer, members, stream=0):
+    """members: list of keyword dicts of tpa_adapter_load (method, rank, ...),
+    applied in order."""
+    made = [_desc(**mem) for mem in members]
+    arr = (tpa_adapter_desc * len(made))(*[dsc for dsc, _ in made])
+    slot = ctypes.c_int32()
+    _check(_lib.tpa_adapter_load_stack(layer, arr, len(made), ctypes.byref(slot), stream))
+    del made
     return slot.value
 
 

@@ -231,7 +231,7 @@ struct tpa_layer {
   const void* vera_At = nullptr;
   const void* vera_Bt = nullptr;
   int r_v = 0;
-  int n_owned = 0, n_vera = 0, n_dora = 0;
+  int n_owned = 0, n_vera = 0, n_dora = 0, n_stack = 0;
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
   int opt[9] = {-1, -1, -1, -1, -1, 0, -1, -1, -1};
@@ -568,6 +568,153 @@ struct Staging {
   }
 };
 
+// Checks one raw adapter against the layer (shapes, ranks, finite values,
+// skew-symmetric Q).  Returns TPA_OK or the error with its message set.
+tpa_status validate_desc(const tpa_layer* L, const tpa_adapter_desc* d) {
+  const int d_in = L->d_in, d_out = L->d_out;
+  const int m = d->method;
+  if (m == TPA_LORA || m == TPA_DORA) {
+    if (d->rank < 1 || d->rank > L->max_rank)
+      return fail(TPA_ERR_INVALID, "rank %d outside [1, max_rank=%d]", d->rank, L->max_rank);
+    if (!d->A || !d->B) return fail(TPA_ERR_INVALID, "null A or B");
+    if (!std::isfinite(d->c) || !finite_all(d->A, (size_t)d_in * d->rank) || !finite_all(d->B, (size_t)d->rank * d_out))
+      return fail(TPA_ERR_VALUE, "non-finite LoRA/DoRA factor");
+    if (m == TPA_DORA && (!d->m || !finite_all(d->m, d_out))) return fail(TPA_ERR_VALUE, "missing or non-finite DoRA m");
+  } else if (m == TPA_IA3) {
+    if (!d->l) return fail(TPA_ERR_INVALID, "null l");
+    if (!finite_all(d->l, d_out)) return fail(TPA_ERR_VALUE, "non-finite l");
+  } else if (m == TPA_SSF) {
+    if (!d->s || !d->b) return fail(TPA_ERR_INVALID, "null s or b");
+    if (!finite_all(d->s, d_out) || !finite_all(d->b, d_out)) return fail(TPA_ERR_VALUE, "non-finite s or b");
+  } else if (m == TPA_VERA) {
+    if (L->r_v == 0) return fail(TPA_ERR_INVALID, "VeRA shared pair not set");
+    if (d->rank != 0 && d->rank != L->r_v) return fail(TPA_ERR_INVALID, "VeRA rank %d != shared rank %d", d->rank, L->r_v);
+    if (!d->d || !d->e) return fail(TPA_ERR_INVALID, "null d or e");
+    if (!std::isfinite(d->c) || !finite_all(d->d, L->r_v) || !finite_all(d->e, d_out))
+      return fail(TPA_ERR_VALUE, "non-finite VeRA vector");
+  } else if (m == TPA_OFT) {
+    const int bs = d->oft_block;
+    if (oft_bs_index(bs) < 0 || d_in % bs) return fail(TPA_ERR_INVALID, "OFT block %d must be 16, 32 or 64 and divide d_in", bs);
+    if (!d->Q) return fail(TPA_ERR_INVALID, "null Q");
+    const size_t cnt = (size_t)d_in * bs;
+    if (!finite_all(d->Q, cnt)) return fail(TPA_ERR_VALUE, "non-finite Q");
+    for (int j = 0; j < d_in / bs; ++j) {
+      const float* q = d->Q + (size_t)j * bs * bs;
+      float mx = 0.f;
+      for (int i = 0; i < bs * bs; ++i) mx = std::max(mx, std::fabs(q[i]));
+      for (int r = 0; r < bs; ++r)
+        for (int c = 0; c <= r; ++c)
+          if (std::fabs(q[r * bs + c] + q[c * bs + r]) > 1e-6f * (1.f + mx))
+            return fail(TPA_ERR_VALUE, "Q block %d is not skew-symmetric at (%d, %d)", j, r, c);
+    }
+  }
+  return TPA_OK;
+}
+
+struct StackTerm {
+  bool shared = false;          // VeRA term (c·d, e on the layer's pair)
+  int r = 0;
+  std::vector<double> A;        // owned: c·A as [d_in][r]
+  std::vector<double> B;        // owned: B as [r][d_out]
+  std::vector<double> dv;       // shared: c·d [r_v]
+  std::vector<double> e;        // outer vector [d_out]
+};
+
+float half_bits_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  int exp = (h >> 10) & 0x1F;
+  uint32_t man = h & 0x3FF;
+  uint32_t bits;
+  if (exp == 0x1F) {
+    bits = sign | 0x7F800000u | (man << 13);
+  } else if (exp == 0) {
+    if (man == 0) {
+      bits = sign;
+    } else {  // subnormal: normalise
+      int e = -1;
+      do {
+        man <<= 1;
+        ++e;
+      } while (!(man & 0x400));
+      bits = sign | ((uint32_t)(127 - 15 - e) << 23) | ((man & 0x3FF) << 13);
+    }
+  } else {
+    bits = sign | ((uint32_t)(exp - 15 + 127) << 23) | (man << 13);
+  }
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return f;
+}
+
+// Device matrix in the layer type -> host float64.
+tpa_status fetch_matrix(const tpa_layer* L, const void* dev, size_t count, std::vector<double>* out) {
+  out->resize(count);
+  if (L->dtype == TPA_F32) {
+    std::vector<float> h(count);
+    TPA_HIP(hipMemcpy(h.data(), dev, count * 4, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < count; ++i) (*out)[i] = h[i];
+  } else {
+    std::vector<uint16_t> h(count);
+    TPA_HIP(hipMemcpy(h.data(), dev, count * 2, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < count; ++i) {
+      float f;
+      if (L->dtype == TPA_BF16) {
+        const uint32_t bits = (uint32_t)h[i] << 16;
+        std::memcpy(&f, &bits, 4);
+      } else {
+        f = half_bits_to_float(h[i]);
+      }
+      (*out)[i] = f;
+    }
+  }
+  return TPA_OK;
+}
+
+// DoRA's scale m ⊘ ‖W + cAB‖_c of one member, by the load-time norm kernel.
+tpa_status dora_scale_host(tpa_layer* L, const tpa_adapter_desc* d, hipStream_t s, std::vector<double>* out) {
+  const int d_in = L->d_in, d_out = L->d_out, r_pad = round_up(d->rank, 16);
+  auto pad = [](size_t c) { return (std::max<size_t>(c, 1) + 63) / 64 * 64; };
+  Staging st{L};
+  if (tpa_status e = st.reserve(pad((size_t)d_in * d->rank) + pad((size_t)d->rank * d_out) +
+                                pad((size_t)r_pad * d_in) + 2 * pad(d_out)))
+    return e;
+  if (!L->status_dev) {
+    void* p = nullptr;
+    TPA_HIP(hipMalloc(&p, sizeof(int32_t)));
+    L->status_dev = static_cast<int32_t*>(p);
+  }
+  float *a32, *b32, *at32, *m32, *s32;
+  if (tpa_status e = st.put(d->A, (size_t)d_in * d->rank, &a32, s)) return e;
+  if (tpa_status e = st.put(d->B, (size_t)d->rank * d_out, &b32, s)) return e;
+  if (tpa_status e = st.alloc((size_t)r_pad * d_in, &at32)) return e;
+  if (tpa_status e = st.put(d->m, d_out, &m32, s)) return e;
+  if (tpa_status e = st.alloc(d_out, &s32)) return e;
+  TPA_HIP(tpa::launch_pack_transpose(0, a32, d_in, d->rank, d->c, nullptr, at32, r_pad, d_in, s));
+  TPA_HIP(hipMemsetAsync(L->status_dev, 0, sizeof(int32_t), s));
+  tpa::DoraArgs da{};
+  da.W = L->W;
+  da.At = at32;
+  da.B = b32;
+  da.m = m32;
+  da.d_in = d_in;
+  da.d_out = d_out;
+  da.r = d->rank;
+  da.r_pad = r_pad;
+  da.s = s32;
+  da.Bt = nullptr;
+  da.fold_e = 0;
+  da.status = L->status_dev;
+  TPA_HIP(tpa::launch_dora_norm(L->dtype, da, s));
+  std::vector<float> sv(d_out);
+  int32_t status = 0;
+  TPA_HIP(hipMemcpyAsync(sv.data(), s32, (size_t)d_out * 4, hipMemcpyDeviceToHost, s));
+  TPA_HIP(hipMemcpyAsync(&status, L->status_dev, sizeof status, hipMemcpyDeviceToHost, s));
+  TPA_HIP(hipStreamSynchronize(s));
+  if (status) return fail(TPA_ERR_VALUE, "DoRA: zero or non-finite column norm");
+  out->assign(sv.begin(), sv.end());
+  return TPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -686,42 +833,7 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
   if (!method_shape(d->method, &owned, &present, &term)) return fail(TPA_ERR_METHOD, "unknown method %d", d->method);
   const int d_in = L->d_in, d_out = L->d_out;
   const int m = d->method;
-  // Validation.
-  if (m == TPA_LORA || m == TPA_DORA) {
-    if (d->rank < 1 || d->rank > L->max_rank)
-      return fail(TPA_ERR_INVALID, "rank %d outside [1, max_rank=%d]", d->rank, L->max_rank);
-    if (!d->A || !d->B) return fail(TPA_ERR_INVALID, "null A or B");
-    if (!std::isfinite(d->c) || !finite_all(d->A, (size_t)d_in * d->rank) || !finite_all(d->B, (size_t)d->rank * d_out))
-      return fail(TPA_ERR_VALUE, "non-finite LoRA/DoRA factor");
-    if (m == TPA_DORA && (!d->m || !finite_all(d->m, d_out))) return fail(TPA_ERR_VALUE, "missing or non-finite DoRA m");
-  } else if (m == TPA_IA3) {
-    if (!d->l) return fail(TPA_ERR_INVALID, "null l");
-    if (!finite_all(d->l, d_out)) return fail(TPA_ERR_VALUE, "non-finite l");
-  } else if (m == TPA_SSF) {
-    if (!d->s || !d->b) return fail(TPA_ERR_INVALID, "null s or b");
-    if (!finite_all(d->s, d_out) || !finite_all(d->b, d_out)) return fail(TPA_ERR_VALUE, "non-finite s or b");
-  } else if (m == TPA_VERA) {
-    if (L->r_v == 0) return fail(TPA_ERR_INVALID, "VeRA shared pair not set");
-    if (d->rank != 0 && d->rank != L->r_v) return fail(TPA_ERR_INVALID, "VeRA rank %d != shared rank %d", d->rank, L->r_v);
-    if (!d->d || !d->e) return fail(TPA_ERR_INVALID, "null d or e");
-    if (!std::isfinite(d->c) || !finite_all(d->d, L->r_v) || !finite_all(d->e, d_out))
-      return fail(TPA_ERR_VALUE, "non-finite VeRA vector");
-  } else if (m == TPA_OFT) {
-    const int bs = d->oft_block;
-    if (oft_bs_index(bs) < 0 || d_in % bs) return fail(TPA_ERR_INVALID, "OFT block %d must be 16, 32 or 64 and divide d_in", bs);
-    if (!d->Q) return fail(TPA_ERR_INVALID, "null Q");
-    const size_t cnt = (size_t)d_in * bs;
-    if (!finite_all(d->Q, cnt)) return fail(TPA_ERR_VALUE, "non-finite Q");
-    for (int j = 0; j < d_in / bs; ++j) {
-      const float* q = d->Q + (size_t)j * bs * bs;
-      float mx = 0.f;
-      for (int i = 0; i < bs * bs; ++i) mx = std::max(mx, std::fabs(q[i]));
-      for (int r = 0; r < bs; ++r)
-        for (int c = 0; c <= r; ++c)
-          if (std::fabs(q[r * bs + c] + q[c * bs + r]) > 1e-6f * (1.f + mx))
-            return fail(TPA_ERR_VALUE, "Q block %d is not skew-symmetric at (%d, %d)", j, r, c);
-    }
-  }
+  if (tpa_status e = validate_desc(L, d)) return e;
   int slot = -1;
   for (int i = 1; i < L->max_slots; ++i)
     if (!L->hs[i].used) {
@@ -893,6 +1005,245 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
   return TPA_OK;
 }
 
+// A stack (§3.2 "Stacking", appendix "Stacking"): members applied in order
+// at one hook, each to the previous member's output.  The composition is
+// again one member of eq. (1): scale Π s_j, shift folded through the later
+// scales (b1⊙s2 + b2), and every member's term, each multiplied by the
+// scales of the members after it through its outer vector e.  The members'
+// own folds are made on the host in float64 (DoRA's scale comes from the
+// device norm kernel, as for a single DoRA load); then the terms are stored
+// as one slot:
+//   * one shared (VeRA) term and nothing else: a shared-term slot (d' = c·d,
+//     e' = e ⊙ later scales);
+//   * otherwise every term becomes part of one owned term whose rank is the
+//     sum of the members' ranks (a shared term enters through its exact
+//     owned form A_v diag(c·d), B_v diag(e'), from the layer's stored pair),
+//     so the stack runs as one segment of the same kernels.
+// Only the first member may hold an input transform R (OFT).
+tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members, int32_t count, int32_t* slot_out,
+                                  tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (!members || !slot_out) return fail(TPA_ERR_INVALID, "null argument");
+  if (count < 1 || count > TPA_MAX_STACK) return fail(TPA_ERR_INVALID, "a stack holds 1..%d members (got %d)",
+                                                      TPA_MAX_STACK, count);
+  if (count == 1) return tpa_adapter_load(L, members, slot_out, stream);
+  if (L->opt[TPA_OPT_SCALE_ROUTE] >= 2)
+    return fail(TPA_ERR_INVALID, "stacks fold later scales into the terms; use a scale route inside the expand");
+  for (int j = 0; j < count; ++j) {
+    int owned, present, term;
+    if (!method_shape(members[j].method, &owned, &present, &term))
+      return fail(TPA_ERR_METHOD, "member %d: unknown method %d", j, members[j].method);
+    if (j > 0 && members[j].method == TPA_OFT)
+      return fail(TPA_ERR_INVALID, "member %d: only the first member of a stack may rotate the input", j);
+    if (tpa_status e = validate_desc(L, &members[j])) return e;
+  }
+  int slot = -1;
+  for (int i = 1; i < L->max_slots; ++i)
+    if (!L->hs[i].used) {
+      slot = i;
+      break;
+    }
+  if (slot < 0) return fail(TPA_ERR_NO_SLOT, "all %d slots in use", L->max_slots);
+
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TPA_HIP(hipStreamSynchronize(s));
+  const int d_in = L->d_in, d_out = L->d_out;
+  // Compose on the host: y <- y ⊙ s_j + b_j + (terms of member j).
+  std::vector<double> S, Bsh;
+  std::vector<StackTerm> terms;
+  int fold_mask = 0;
+  for (int j = 0; j < count; ++j) {
+    const tpa_adapter_desc& d = members[j];
+    std::vector<double> sj, bj;
+    if (d.method == TPA_DORA) {
+      if (tpa_status e = dora_scale_host(L, &d, s, &sj)) return e;
+    } else if (d.method == TPA_IA3) {
+      sj.assign(d.l, d.l + d_out);
+    } else if (d.method == TPA_SSF) {
+      sj.assign(d.s, d.s + d_out);
+      bj.assign(d.b, d.b + d_out);
+    }
+    if (!sj.empty()) {
+      if (S.empty()) S.assign(d_out, 1.0);
+      for (int c = 0; c < d_out; ++c) S[c] *= sj[c];
+      if (!Bsh.empty())
+        for (int c = 0; c < d_out; ++c) Bsh[c] *= sj[c];
+      for (StackTerm& tm : terms)
+        for (int c = 0; c < d_out; ++c) tm.e[c] *= sj[c];
+    }
+    if (!bj.empty()) {
+      if (Bsh.empty()) Bsh.assign(d_out, 0.0);
+      for (int c = 0; c < d_out; ++c) Bsh[c] += bj[c];
+    }
+    if (d.method == TPA_LORA || d.method == TPA_DORA) {
+      StackTerm tm;
+      tm.r = d.rank;
+      tm.A.resize((size_t)d_in * d.rank);
+      for (size_t i = 0; i < tm.A.size(); ++i) tm.A[i] = (double)d.c * d.A[i];
+      tm.B.assign(d.B, d.B + (size_t)d.rank * d_out);
+      tm.e = d.method == TPA_DORA ? sj : std::vector<double>(d_out, 1.0);
+      terms.push_back(std::move(tm));
+      fold_mask |= TPA_FOLD_C_A;
+    } else if (d.method == TPA_VERA) {
+      StackTerm tm;
+      tm.shared = true;
+      tm.r = L->r_v;
+      tm.dv.resize(L->r_v);
+      for (int k = 0; k < L->r_v; ++k) tm.dv[k] = (double)d.c * d.d[k];
+      tm.e.assign(d.e, d.e + d_out);
+      terms.push_back(std::move(tm));
+    }
+  }
+  const bool has_R = members[0].method == TPA_OFT;
+  const bool one_shared = terms.size() == 1 && terms[0].shared;
+  int r_tot = 0;
+  for (const StackTerm& tm : terms) r_tot += tm.r;
+  const int r_pad = one_shared ? 0 : round_up(r_tot, 16);
+  if (!one_shared && r_tot > L->max_rank)
+    return fail(TPA_ERR_INVALID, "stacked rank %d exceeds max_rank=%d", r_tot, L->max_rank);
+  const int cls = terms.empty() ? tpa::CLS_NONE : one_shared ? tpa::CLS_SHARED : tpa::CLS_OWNED;
+
+  // Owned form of every term: A_all [d_in][r_tot] and B_all [r_tot][d_out]
+  // with e folded into B (a shared term through A_v diag(c·d), B_v).
+  std::vector<float> A_all, B_all;
+  if (cls == tpa::CLS_OWNED) {
+    std::vector<double> Av, Bv;  // the layer's pair as stored: [r_v][d_in], [d_out][r_v]
+    for (const StackTerm& tm : terms)
+      if (tm.shared && Av.empty()) {
+        if (tpa_status e = fetch_matrix(L, L->vera_At, (size_t)L->r_v * d_in, &Av)) return e;
+        if (tpa_status e = fetch_matrix(L, L->vera_Bt, (size_t)d_out * L->r_v, &Bv)) return e;
+      }
+    A_all.assign((size_t)d_in * r_tot, 0.f);
+    B_all.assign((size_t)r_tot * d_out, 0.f);
+    int k0 = 0;
+    for (const StackTerm& tm : terms) {
+      for (int i = 0; i < d_in; ++i)
+        for (int k = 0; k < tm.r; ++k)
+          A_all[(size_t)i * r_tot + k0 + k] =
+              (float)(tm.shared ? Av[(size_t)k * d_in + i] * tm.dv[k] : tm.A[(size_t)i * tm.r + k]);
+      for (int k = 0; k < tm.r; ++k)
+        for (int c = 0; c < d_out; ++c)
+          B_all[(size_t)(k0 + k) * d_out + c] =
+              (float)((tm.shared ? Bv[(size_t)c * L->r_v + k] : tm.B[(size_t)k * d_out + c]) * tm.e[c]);
+      if (tm.shared) fold_mask |= TPA_FOLD_D_A;
+      fold_mask |= TPA_FOLD_E_B;
+      k0 += tm.r;
+    }
+  } else if (cls == tpa::CLS_SHARED) {
+    fold_mask |= TPA_FOLD_C_D;
+  }
+
+  const size_t esz = tpa::dtype_size(L->dtype);
+  size_t off = 0;
+  size_t o_At = 0, o_Bt = 0, o_s = 0, o_b = 0, o_d = 0, o_e = 0, o_R = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  if (cls == tpa::CLS_OWNED) {
+    o_At = take((size_t)r_pad * d_in * esz);
+    o_Bt = take((size_t)d_out * r_pad * esz);
+  }
+  if (!S.empty()) o_s = take((size_t)d_out * 4);
+  if (!Bsh.empty()) o_b = take((size_t)d_out * 4);
+  if (cls == tpa::CLS_SHARED) {
+    o_d = take((size_t)L->r_v * 4);
+    o_e = take((size_t)d_out * 4);
+  }
+  const int bs = has_R ? members[0].oft_block : 0;
+  if (has_R) o_R = take((size_t)d_in * bs * esz);
+  void* mem = nullptr;
+  if (off) TPA_HIP(L->arena.take(off, &mem));
+  char* base = static_cast<char*>(mem);
+  SlotDev sd{};
+  sd.cls = cls;
+  auto upload = [&]() -> tpa_status {
+    auto pad = [](size_t c) { return (std::max<size_t>(c, 1) + 63) / 64 * 64; };
+    Staging st{L};
+    size_t need = has_R ? pad((size_t)d_in * bs) : 0;
+    if (cls == tpa::CLS_OWNED) need += pad(A_all.size()) + pad(B_all.size());
+    if (tpa_status e = st.reserve(need)) return e;
+    auto to_f32 = [](const std::vector<double>& v) { return std::vector<float>(v.begin(), v.end()); };
+    std::vector<float> s32 = to_f32(S), b32 = to_f32(Bsh), dd, ee;
+    if (cls == tpa::CLS_OWNED) {
+      float *a32, *bb32;
+      if (tpa_status e = st.put(A_all.data(), A_all.size(), &a32, s)) return e;
+      if (tpa_status e = st.put(B_all.data(), B_all.size(), &bb32, s)) return e;
+      // A_all [d_in][r_tot] -> [r_pad][d_in];  B_all [r_tot][d_out] -> [d_out][r_pad].
+      TPA_HIP(tpa::launch_pack_transpose(L->dtype, a32, d_in, r_tot, 1.f, nullptr, base + o_At, r_pad, d_in, s));
+      TPA_HIP(tpa::launch_pack_transpose(L->dtype, bb32, r_tot, d_out, 1.f, nullptr, base + o_Bt, d_out, r_pad, s));
+      sd.A = base + o_At;
+      sd.Bt = base + o_Bt;
+      sd.rank = r_pad;
+    } else if (cls == tpa::CLS_SHARED) {
+      dd = to_f32(terms[0].dv);
+      ee = to_f32(terms[0].e);
+      TPA_HIP(hipMemcpyAsync(base + o_d, dd.data(), dd.size() * 4, hipMemcpyHostToDevice, s));
+      TPA_HIP(hipMemcpyAsync(base + o_e, ee.data(), ee.size() * 4, hipMemcpyHostToDevice, s));
+      sd.d = reinterpret_cast<float*>(base + o_d);
+      sd.e = reinterpret_cast<float*>(base + o_e);
+      sd.rank = L->r_v;
+    }
+    if (!S.empty()) {
+      TPA_HIP(hipMemcpyAsync(base + o_s, s32.data(), s32.size() * 4, hipMemcpyHostToDevice, s));
+      sd.s = reinterpret_cast<float*>(base + o_s);
+    }
+    if (!Bsh.empty()) {
+      TPA_HIP(hipMemcpyAsync(base + o_b, b32.data(), b32.size() * 4, hipMemcpyHostToDevice, s));
+      sd.b = reinterpret_cast<float*>(base + o_b);
+    }
+    if (has_R) {
+      const size_t cnt = (size_t)d_in * bs;
+      std::vector<float> rt(cnt);
+      for (int j = 0; j < d_in / bs; ++j)
+        cayley_transposed(members[0].Q + (size_t)j * bs * bs, bs, rt.data() + (size_t)j * bs * bs);
+      float* r32;
+      if (tpa_status e = st.put(rt.data(), cnt, &r32, s)) return e;
+      TPA_HIP(tpa::launch_convert(L->dtype, r32, base + o_R, cnt, 1.f, s));
+      sd.Rt = base + o_R;
+      sd.has_R = 1;
+      sd.oft_block = bs;
+    }
+    TPA_HIP(hipStreamSynchronize(s));  // host vectors above must outlive the copies
+    return TPA_OK;
+  };
+  tpa_status err = upload();
+  if (!err) {
+    L->slots_host[slot] = sd;
+    err = upload_slot(L, slot, s);
+    if (err) {
+      L->slots_host[slot] = SlotDev{};
+      L->slots_host[slot].cls = -1;
+    }
+  }
+  if (err) {
+    (void)hipStreamSynchronize(s);
+    if (mem) L->arena.give(mem, off);
+    return err;
+  }
+  HostSlot& h = L->hs[slot];
+  h.used = true;
+  h.mem = mem;
+  h.bytes = off;
+  h.info = tpa_adapter_info{};
+  h.info.method = TPA_STACK;
+  h.info.term_kind = cls == tpa::CLS_OWNED ? 1 : cls == tpa::CLS_SHARED ? 2 : 0;
+  h.info.rank = cls == tpa::CLS_OWNED ? r_tot : cls == tpa::CLS_SHARED ? L->r_v : 0;
+  h.info.oft_block = bs;
+  h.info.fold_mask = fold_mask;
+  h.info.live_mask = (S.empty() ? 0 : TPA_LIVE_S) | (Bsh.empty() ? 0 : TPA_LIVE_B) | (has_R ? TPA_LIVE_R : 0) |
+                     (cls == tpa::CLS_SHARED ? TPA_LIVE_D | TPA_LIVE_E : 0);
+  if (cls == tpa::CLS_OWNED) ++L->n_owned;
+  if (cls == tpa::CLS_SHARED) ++L->n_vera;
+  ++L->n_stack;
+  if (has_R) ++L->n_oft_bs[oft_bs_index(bs)];
+  update_plan_sig(L);
+  *slot_out = slot;
+  return TPA_OK;
+}
+
 tpa_status tpa_adapter_unload(tpa_layer* L, int32_t slot, tpa_stream stream) {
   if (tpa_status st = check_layer(L)) return st;
   if (slot <= 0 || slot >= L->max_slots || !L->hs[slot].used) return fail(TPA_ERR_UNKNOWN_SLOT, "slot %d is not loaded", slot);
@@ -908,7 +1259,8 @@ tpa_status tpa_adapter_unload(tpa_layer* L, int32_t slot, tpa_stream stream) {
   if (info.term_kind == 1) --L->n_owned;
   if (info.term_kind == 2) --L->n_vera;
   if (info.method == TPA_DORA) --L->n_dora;
-  if (info.method == TPA_OFT) --L->n_oft_bs[oft_bs_index(info.oft_block)];
+  if (info.method == TPA_STACK) --L->n_stack;
+  if (info.live_mask & TPA_LIVE_R) --L->n_oft_bs[oft_bs_index(info.oft_block)];
   update_plan_sig(L);
   return TPA_OK;
 }
@@ -1425,8 +1777,8 @@ tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
     if (value < 0) value = 0;
     if (value > 3) return fail(TPA_ERR_INVALID, "scale route must be 0..3");
     const bool was_post = L->opt[TPA_OPT_SCALE_ROUTE] >= 2, post = value >= 2;
-    if (was_post != post && L->n_dora > 0)
-      return fail(TPA_ERR_INVALID, "DoRA slots are folded for the current route; unload them first");
+    if (was_post != post && (L->n_dora > 0 || L->n_stack > 0))
+      return fail(TPA_ERR_INVALID, "DoRA or stacked slots are folded for the current route; unload them first");
   }
   L->opt[key] = value;
   return TPA_OK;

@@ -47,9 +47,8 @@ class AdaptedLayer:
         A = np.asarray(A, np.float32)
         B.tpa_vera_shared_set(self.handle, A.shape[1], A, Bm, _stream())
 
-    def load(self, rec):
-        """Admit an adapter given as a raw-parameter record (method name and
-        numpy arrays in the paper's math layout); returns its slot."""
+    @staticmethod
+    def _kwargs(rec):
         meth = rec["method"]
         kw = {}
         if meth in ("lora", "dora"):
@@ -62,7 +61,17 @@ class AdaptedLayer:
             kw = dict(c=rec.get("c", 1.0), d=rec["d"], e=rec["e"])
         elif meth == "oft":
             kw = dict(oft_block=rec["Q"].shape[1], Q=rec["Q"])
-        return B.tpa_adapter_load(self.handle, meth, stream=_stream(), **kw)
+        kw["method"] = meth
+        return kw
+
+    def load(self, rec):
+        """Admit an adapter given as a raw-parameter record (method name and
+        numpy arrays in the paper's math layout); returns its slot.  A record
+        {"method": "stack", "members": [...]} admits the members as one
+        stacked slot, applied in list order."""
+        if rec["method"] == "stack":
+            return B.tpa_adapter_load_stack(self.handle, [self._kwargs(m) for m in rec["members"]], _stream())
+        return B.tpa_adapter_load(self.handle, stream=_stream(), **self._kwargs(rec))
 
     def unload(self, slot):
         B.tpa_adapter_unload(self.handle, slot, _stream())

@@ -1,0 +1,82 @@
+"""GPU parity of stacked adapters (§3.2 paragraph "Stacking", appendix
+"Stacking"): several members applied in order at one hook, loaded through
+tpa_adapter_load_stack as one slot, against the oracle's sequential
+application of each member's own definition.  Same tolerances as the other
+parity tests: fp32 layers 1e-4 (mean relative) and 2e-5 · max|h| (max);
+f16 layers 1% and 2e-3 · max|h|."""
+import numpy as np
+import pytest
+
+from gpu_util import check, make_layer, reference, run, say
+from tenant_peft_adapter_amd import binding as B
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(mean_tol=1e-4, max_tol=2e-5), "f16": dict(mean_tol=0.01, max_tol=2e-3)}
+
+
+@pytest.mark.parametrize("dtype,n", [("f32", 64), ("f16", 64), ("f16", 17), ("f16", 300)])
+def test_stacks_match_oracle(dtype, n):
+    wl = synth.tiny_stacks(seed=5000 + n, n=n, dtype=dtype)
+    p = wl["projections"][0]
+    say("tiny_stacks %s n=%d" % (dtype, n))
+    L = make_layer(p, max_slots=16, max_rank=64)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="stacks %s n=%d" % (dtype, n), **TOL[dtype])
+    # every slot on its own rows too (a stack's error must not hide in the mean)
+    for slot in range(1, 12):
+        rows = np.nonzero(wl["slot_of_row"] == slot)[0]
+        if len(rows):
+            check(y_gpu[rows], y[rows], h[rows], xw[rows], label="slot %d" % slot, **TOL[dtype])
+    L.close()
+
+
+def test_stack_metadata():
+    wl = synth.tiny_stacks(n=8, dtype="f16")
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=16, max_rank=64)
+    want = {  # slot: (term_kind, rank, live bits)
+        1: (1, 8, B.LIVE_S), 2: (1, 8, B.LIVE_S), 3: (1, 8, B.LIVE_S | B.LIVE_B), 4: (1, 8, B.LIVE_R),
+        5: (2, 32, B.LIVE_S | B.LIVE_D | B.LIVE_E), 6: (1, 40, 0),
+        7: (2, 32, B.LIVE_S | B.LIVE_B | B.LIVE_R | B.LIVE_D | B.LIVE_E), 8: (0, 0, B.LIVE_S | B.LIVE_B),
+        11: (1, 16, B.LIVE_S),
+    }
+    for slot, (kind, rank, live) in want.items():
+        info = L.info(slot)
+        say(slot, info)
+        assert info["method"] == B.METHODS["stack"], (slot, info)
+        assert (info["term_kind"], info["rank"], info["live_mask"]) == (kind, rank, live), (slot, info)
+    assert L.info(9)["method"] == B.METHODS["lora"]
+    assert L.info(6)["fold_mask"] & B.FOLD_D_A  # the VeRA term entered in owned form
+    L.close()
+
+
+def test_stack_rejections_and_reload():
+    wl = synth.tiny_stacks(n=64, dtype="f16")
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=16, max_rank=64)
+    ads = p["adapters"]
+    oft = ads[4]["members"][0]
+    lora = ads[9]
+    with pytest.raises(B.TpaError) as ei:  # OFT after the first member
+        L.load({"method": "stack", "members": [lora, oft]})
+    assert ei.value.code == -1
+    small = make_layer({**p, "adapters": {}}, max_slots=16, max_rank=32)
+    with pytest.raises(B.TpaError) as ei:  # rank 8 + 32 above max_rank 32
+        small.load(ads[6])
+    assert ei.value.code == -1
+    small.close()
+    # unload the rotated stacks and load them again: same outputs
+    before = run(L, p["x"], wl["slot_of_row"], "f16")
+    for slot in (4, 7):
+        L.unload(slot)
+    assert L.load(ads[4]) == 4
+    assert L.load(ads[7]) == 7
+    after = run(L, p["x"], wl["slot_of_row"], "f16")
+    np.testing.assert_array_equal(before, after)
+    # a one-member stack is the plain load
+    s1 = L.load({"method": "stack", "members": [lora]})
+    assert L.info(s1)["method"] == B.METHODS["lora"]
+    L.close()

@@ -121,6 +121,11 @@ def _oft(rng, d_in, block=32, std=0.1):
     return {"method": "oft", "Q": Q.astype(np.float32), "block": block}
 
 
+def _ssf(rng, d_out):
+    return {"method": "ssf", "s": (1.0 + 0.3 * rng.standard_normal(d_out)).astype(np.float32),
+            "b": (0.3 * rng.standard_normal(d_out)).astype(np.float32)}
+
+
 def _vera_shared(rng, d_in, d_out, r_v, dtype):
     return {"A": round_to(_normal(rng, (d_in, r_v), 1.0 / np.sqrt(d_in)), dtype),
             "B": round_to(_normal(rng, (r_v, d_out), 1.0 / np.sqrt(r_v)), dtype)}
@@ -154,6 +159,37 @@ def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False, d_out=None
     lo = 0 if with_identity else 1
     slot_of_row = rng.integers(lo, 6, size=n).astype(np.int32)
     return {"name": "tiny_mixed", "dtype": dtype, "n": n,
+            "slot_of_row": slot_of_row, "projections": [p]}
+
+
+def tiny_stacks(seed=5000, n=64, d=256, dtype="f32", r=8, r_v=32):
+    """Tiny single layer with stacked adapters (several members applied in
+    order at one hook) beside single ones, rows uniform over slots 0..11.
+    SSF (absent from the other workloads) draws s = 1 + 0.3 z, b = 0.3 z.
+      1 LoRA then (IA)3        2 (IA)3 then LoRA        3 SSF, DoRA, (IA)3
+      4 OFT then LoRA          5 VeRA then (IA)3        6 LoRA then VeRA
+      7 OFT, VeRA, SSF         8 (IA)3 then SSF         9 LoRA alone
+     10 VeRA alone            11 DoRA then LoRA"""
+    rng = np.random.default_rng(seed)
+    p = make_projection(rng, "tiny", d, d, dtype, n)
+    p["shared"] = _vera_shared(rng, d, d, r_v, dtype)
+    W = p["W"]
+    st = lambda *m: {"method": "stack", "members": list(m)}
+    p["adapters"] = {
+        1: st(_lora(rng, d, d, r, dtype), _ia3(rng, d)),
+        2: st(_ia3(rng, d), _lora(rng, d, d, r, dtype)),
+        3: st(_ssf(rng, d), _dora(rng, W, r, dtype), _ia3(rng, d)),
+        4: st(_oft(rng, d, 32), _lora(rng, d, d, r, dtype)),
+        5: st(_vera(rng, r_v, d), _ia3(rng, d)),
+        6: st(_lora(rng, d, d, r, dtype), _vera(rng, r_v, d)),
+        7: st(_oft(rng, d, 32), _vera(rng, r_v, d), _ssf(rng, d)),
+        8: st(_ia3(rng, d), _ssf(rng, d)),
+        9: _lora(rng, d, d, r, dtype),
+        10: _vera(rng, r_v, d),
+        11: st(_dora(rng, W, r, dtype), _lora(rng, d, d, r, dtype)),
+    }
+    slot_of_row = rng.integers(0, 12, size=n).astype(np.int32)
+    return {"name": "tiny_stacks", "dtype": dtype, "n": n,
             "slot_of_row": slot_of_row, "projections": [p]}
 
 
