@@ -17,6 +17,13 @@ paperpeel.com):
              block-diagonal orthogonal R whose blocks are Cayley transforms
              of skew-symmetric matrices; the base layer is then unchanged.
   * SSF   -- §3.1 and Table 1: scale s and shift b on the output.
+  * LoHa  -- §3.1 ("Other methods fit as well"): the update is built from
+             products of small factors.  Reading: LoHa's own definition, the
+             elementwise product of two low-rank products,
+             ΔW = c · (A1 B1) ⊙ (A2 B2).
+  * LoKr  -- same passage.  Reading: LoKr's own definition, a Kronecker
+             product of a small matrix with a low-rank product,
+             ΔW = c · (C ⊗ (A B)), C [p, q], A [d_in/p, r], B [r, d_out/q].
   * Stack -- §3.2 (paragraph "Stacking") and the appendix paragraph of that
              name: a second member applied at the same hook takes the first
              member's output in place of its own base output xW; its terms
@@ -36,11 +43,13 @@ Adapter records are plain dicts::
     {"method": "vera", "d": d, "e": e, "c": c}      # + shared {"A": Av, "B": Bv}
     {"method": "oft",  "Q": Q}                       # Q: [d_in / b, b, b] skew
     {"method": "ssf",  "s": s, "b": b}
+    {"method": "loha", "A": A1, "B": B1, "A2": A2, "B2": B2, "c": c}
+    {"method": "lokr", "C": C, "A": A, "B": B, "c": c}
     {"method": "stack", "members": [rec1, rec2, ...]}   # applied in order
 """
 import numpy as np
 
-METHODS = ("identity", "lora", "dora", "ia3", "vera", "oft", "ssf", "stack")
+METHODS = ("identity", "lora", "dora", "ia3", "vera", "oft", "ssf", "loha", "lokr", "stack")
 
 
 def _f64(a):
@@ -124,6 +133,8 @@ def direct_forward(x, W, adapter, shared=None):
     if meth == "oft":
         R = oft_rotation(adapter["Q"])
         return (x @ R) @ W
+    if meth in ("loha", "lokr"):
+        return x @ W + x @ product_update(adapter)
     if meth == "stack":
         members = adapter["members"]
         y = direct_forward(x, W, members[0], shared)
@@ -131,6 +142,16 @@ def direct_forward(x, W, adapter, shared=None):
             y = applied_to(y, x, W, mem, shared)
         return y
     raise ValueError("unknown method %r" % (meth,))
+
+
+def product_update(adapter):
+    """ΔW [d_in, d_out] of LoHa or LoKr, formed densely from its factors."""
+    c = float(adapter["c"])
+    if adapter["method"] == "loha":
+        return c * ((_f64(adapter["A"]) @ _f64(adapter["B"])) * (_f64(adapter["A2"]) @ _f64(adapter["B2"])))
+    if adapter["method"] == "lokr":
+        return c * np.kron(_f64(adapter["C"]), _f64(adapter["A"]) @ _f64(adapter["B"]))
+    raise ValueError("not a product method: %r" % (adapter["method"],))
 
 
 def applied_to(y, x, W, adapter, shared=None):
@@ -157,6 +178,8 @@ def applied_to(y, x, W, adapter, shared=None):
         Av, Bv = _f64(shared["A"]), _f64(shared["B"])
         c = float(adapter.get("c", 1.0))
         return y + c * ((((x @ Av) * _f64(adapter["d"])) @ Bv) * _f64(adapter["e"]))
+    if meth in ("loha", "lokr"):
+        return y + x @ product_update(adapter)
     if meth == "oft":
         raise ValueError("only the first member of a stack may transform the input")
     raise ValueError("unknown method %r" % (meth,))

@@ -67,6 +67,13 @@ def unfolded_slots(adapter, W, shared=None):
         out["R"] = oft_rotation(adapter["Q"])
         out["owned"] = {"R"}
         return out
+    if meth in ("loha", "lokr"):
+        # Expanded at load into one low-rank term (§3.1, "Other methods fit
+        # as well"); see expand_product for the factors.
+        A, B = expand_product(adapter)
+        out["terms"].append({"c": float(adapter["c"]), "A": A, "d": None, "B": B, "e": None})
+        out["owned"] = {"A", "B"}
+        return out
     if meth == "stack":
         members = adapter["members"]
         out = unfolded_slots(members[0], W, shared)
@@ -74,6 +81,29 @@ def unfolded_slots(adapter, W, shared=None):
             out = stack(out, unfolded_slots(mem, W, shared))
         return out
     raise ValueError("unknown method %r" % (meth,))
+
+
+def expand_product(adapter):
+    """Low-rank factors (A [d_in, R], B [R, d_out]) with A B equal to the
+    update of LoHa or LoKr without c.
+      LoHa: (A1 B1) ⊙ (A2 B2) = Σ_{k,l} (A1[:,k] ⊙ A2[:,l]) (B1[k] ⊙ B2[l]),
+            so column (k, l) of A is A1[:,k] ⊙ A2[:,l] and row (k, l) of B is
+            B1[k] ⊙ B2[l]; R = r1 · r2.
+      LoKr: C ⊗ (A B) = (C ⊗ A)(I_q ⊗ B) (mixed products), R = q · r, or
+            (I_p ⊗ A)(C ⊗ B), R = p · r; the smaller R is taken."""
+    if adapter["method"] == "loha":
+        A1, B1 = _f64(adapter["A"]), _f64(adapter["B"])
+        A2, B2 = _f64(adapter["A2"]), _f64(adapter["B2"])
+        A = (A1[:, :, None] * A2[:, None, :]).reshape(A1.shape[0], -1)
+        B = (B1[:, None, :] * B2[None, :, :]).reshape(-1, B1.shape[1])
+        return A, B
+    if adapter["method"] == "lokr":
+        C, A0, B0 = _f64(adapter["C"]), _f64(adapter["A"]), _f64(adapter["B"])
+        p, q = C.shape
+        if q <= p:
+            return np.kron(C, A0), np.kron(np.eye(q), B0)
+        return np.kron(np.eye(p), A0), np.kron(C, B0)
+    raise ValueError("not a product method: %r" % (adapter["method"],))
 
 
 def normal_form_eval(x, W, slots):

@@ -608,3 +608,82 @@ def test_stack_input_transform_only_first():
     np.testing.assert_allclose(om.input_transform({"method": "stack", "members": [oft, ia3]}, d_in), R)
     with pytest.raises(ValueError):
         om.direct_forward(x, W, {"method": "stack", "members": [ia3, oft]})
+
+
+# ------------------------------------------------------- LoHa and LoKr ----
+
+def _loha(rng, d_in, d_out, r1=2, r2=3, c=0.75, ints=False):
+    f = (lambda *s: rng.integers(-2, 3, size=s).astype(np.float64)) if ints else (lambda *s: rng.standard_normal(s))
+    return {"method": "loha", "A": f(d_in, r1), "B": f(r1, d_out), "A2": f(d_in, r2), "B2": f(r2, d_out), "c": c}
+
+
+def _lokr(rng, d_in, d_out, p=2, q=3, r=2, c=0.75, ints=False):
+    f = (lambda *s: rng.integers(-2, 3, size=s).astype(np.float64)) if ints else (lambda *s: rng.standard_normal(s))
+    return {"method": "lokr", "C": f(p, q), "A": f(d_in // p, r), "B": f(r, d_out // q), "c": c}
+
+
+def _py_delta(ad, d_in, d_out):
+    """Pure-Python ΔW by each method's elementwise definition."""
+    c = ad["c"]
+    if ad["method"] == "loha":
+        A1, B1, A2, B2 = (ad[k].tolist() for k in ("A", "B", "A2", "B2"))
+        return [[c * sum(A1[i][k] * B1[k][j] for k in range(len(B1))) *
+                 sum(A2[i][l] * B2[l][j] for l in range(len(B2))) for j in range(d_out)] for i in range(d_in)]
+    C, A, B = (ad[k].tolist() for k in ("C", "A", "B"))
+    p2, q2 = len(A), len(B[0])
+    return [[c * C[i // p2][j // q2] * sum(A[i % p2][k] * B[k][j % q2] for k in range(len(B)))
+             for j in range(d_out)] for i in range(d_in)]
+
+
+@pytest.mark.parametrize("meth,shape", [("loha", {}), ("lokr", dict(p=2, q=3)), ("lokr", dict(p=3, q=2)),
+                                        ("lokr", dict(p=1, q=1))])
+def test_product_methods_brute_force(meth, shape):
+    rng = np.random.default_rng(31)
+    d_in, d_out = 6, 6
+    ad = _loha(rng, d_in, d_out) if meth == "loha" else _lokr(rng, d_in, d_out, **shape)
+    x, W = rng.standard_normal((3, d_in)), rng.standard_normal((d_in, d_out))
+    dW = np.array(_py_delta(ad, d_in, d_out))
+    np.testing.assert_allclose(om.product_update(ad), dW, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(om.direct_forward(x, W, ad), x @ W + x @ dW, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("meth", ["loha", "lokr"])
+def test_product_expansion_exact_and_rank(meth):
+    # The load-time expansion into one low-rank term reproduces the update
+    # exactly on integer inputs; its rank is r1·r2 (LoHa) or min(p, q)·r
+    # (LoKr), above the adapter's own rank.
+    rng = np.random.default_rng(32)
+    d_in, d_out = 12, 12
+    ad = _loha(rng, d_in, d_out, ints=True, c=2.0) if meth == "loha" else _lokr(rng, d_in, d_out, p=3, q=2, r=2,
+                                                                              ints=True, c=2.0)
+    x = rng.integers(-3, 4, size=(4, d_in)).astype(np.float64)
+    W = rng.integers(-3, 4, size=(d_in, d_out)).astype(np.float64)
+    A, B = nf.expand_product(ad)
+    assert A.shape[1] == (6 if meth == "loha" else 4)
+    direct = om.direct_forward(x, W, ad)
+    np.testing.assert_array_equal(nf.normal_form_eval(x, W, nf.unfolded_slots(ad, W)), direct)
+    folded, made = nf.fold(nf.unfolded_slots(ad, W))
+    assert made == ["c->A"]
+    np.testing.assert_array_equal(nf.normal_form_eval(x, W, folded), direct)
+    g = np.random.default_rng(33)
+    gen = _loha(g, d_in, d_out) if meth == "loha" else _lokr(g, d_in, d_out, p=3, q=2, r=2)
+    assert np.linalg.matrix_rank(om.product_update(gen)) == A.shape[1]
+
+
+def test_product_methods_reduce_to_lora():
+    rng = np.random.default_rng(34)
+    d_in, d_out = 8, 6
+    x, W = rng.standard_normal((3, d_in)), rng.standard_normal((d_in, d_out))
+    lora = {"method": "lora", "A": rng.standard_normal((d_in, 2)), "B": rng.standard_normal((2, d_out)), "c": 1.5}
+    want = om.direct_forward(x, W, lora)
+    loha = {"method": "loha", "A": lora["A"], "B": lora["B"], "A2": np.ones((d_in, 1)), "B2": np.ones((1, d_out)),
+            "c": 1.5}
+    lokr = {"method": "lokr", "C": np.ones((1, 1)), "A": lora["A"], "B": lora["B"], "c": 1.5}
+    np.testing.assert_allclose(om.direct_forward(x, W, loha), want, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(om.direct_forward(x, W, lokr), want, rtol=0, atol=1e-13)
+    # C = I: block-diagonal update, each block of d_in/p inputs feeds its own outputs
+    eye = {"method": "lokr", "C": np.eye(2), "A": rng.standard_normal((4, 2)), "B": rng.standard_normal((2, 3)),
+           "c": 1.0}
+    D = eye["A"] @ eye["B"]
+    blocks = np.concatenate([x[:, :4] @ D, x[:, 4:] @ D], axis=1)
+    np.testing.assert_allclose(om.direct_forward(x, W, eye) - x @ W, blocks, rtol=0, atol=1e-13)
