@@ -64,7 +64,9 @@ enum tpa_method {
   TPA_VERA = 4,
   TPA_OFT = 5,
   TPA_SSF = 6,
-  TPA_STACK = 7 /* reported by tpa_adapter_info_get for a stacked slot; not loadable by itself */
+  TPA_STACK = 7, /* reported by tpa_adapter_info_get for a stacked slot; not loadable by itself */
+  TPA_LOHA = 8,
+  TPA_LOKR = 9
 };
 
 /* Most members in one stack (tpa_adapter_load_stack). */
@@ -78,7 +80,16 @@ enum tpa_method {
  *   VeRA : d [r_v], e [d_out], c; the shared pair is set per layer with
  *          tpa_vera_shared_set; rank must be 0 or r_v
  *   OFT  : Q [d_in / oft_block][oft_block][oft_block], skew-symmetric
- *   SSF  : s [d_out], b [d_out]                                           */
+ *   SSF  : s [d_out], b [d_out]
+ *   LoHa : ΔW = c · (A B) ⊙ (A2 B2) (§3.1 "Other methods fit as well": a
+ *          product of small factors, expanded at load).  A [d_in][rank],
+ *          B [rank][d_out], A2 [d_in][rank2], B2 [rank2][d_out]
+ *          (rank2 = 0: rank2 = rank); stored as one owned term of rank
+ *          rank · rank2, which must not exceed max_rank.
+ *   LoKr : ΔW = c · (C ⊗ (A B)), C [kron_p][kron_q], A [d_in / kron_p][rank],
+ *          B [rank][d_out / kron_q]; kron_p divides d_in and kron_q d_out.
+ *          Stored as one owned term of rank min(kron_p, kron_q) · rank
+ *          (C ⊗ AB = (C ⊗ A)(I ⊗ B) or (I ⊗ A)(C ⊗ B)), at most max_rank.  */
 typedef struct {
   int32_t method;
   int32_t rank;
@@ -93,6 +104,13 @@ typedef struct {
   const float* Q;
   const float* s;
   const float* b;
+  int32_t rank2;   /* LoHa */
+  int32_t kron_p;  /* LoKr */
+  int32_t kron_q;  /* LoKr */
+  int32_t reserved;
+  const float* A2; /* LoHa */
+  const float* B2; /* LoHa */
+  const float* C;  /* LoKr */
 } tpa_adapter_desc;
 
 /* Merged-slot metadata (Table 1 and the fold rule of §3.2).

@@ -26,7 +26,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tpa.h")
 
 TPA_F32, TPA_F16, TPA_BF16 = 0, 1, 2
 DTYPES = {"f32": TPA_F32, "f16": TPA_F16, "bf16": TPA_BF16}
-METHODS = {"identity": 0, "lora": 1, "dora": 2, "ia3": 3, "vera": 4, "oft": 5, "ssf": 6, "stack": 7}
+METHODS = {"identity": 0, "lora": 1, "dora": 2, "ia3": 3, "vera": 4, "oft": 5, "ssf": 6, "stack": 7, "loha": 8, "lokr": 9}
 (TPA_OPT_GEMM_SPLIT, TPA_OPT_SHRINK_SPLIT, TPA_OPT_TILE_ROWS, TPA_OPT_GEMM_PATH, TPA_OPT_SCALE_ROUTE,
  TPA_OPT_GEMM_NB, TPA_OPT_GEMM_GROUPS, TPA_OPT_GEMM_STAGES) = 1, 2, 3, 4, 5, 6, 7, 8
 LIVE_S, LIVE_B, LIVE_R, LIVE_D, LIVE_E = 1, 2, 4, 8, 16
@@ -42,8 +42,10 @@ class TpaError(RuntimeError):
 
 
 class tpa_adapter_desc(ctypes.Structure):
-    _fields_ = [("method", ctypes.c_int32), ("rank", ctypes.c_int32), ("oft_block", ctypes.c_int32),
-                ("c", ctypes.c_float)] + [(k, ctypes.c_void_p) for k in ("A", "B", "m", "l", "d", "e", "Q", "s", "b")]
+    _fields_ = ([("method", ctypes.c_int32), ("rank", ctypes.c_int32), ("oft_block", ctypes.c_int32),
+                 ("c", ctypes.c_float)] + [(k, ctypes.c_void_p) for k in ("A", "B", "m", "l", "d", "e", "Q", "s", "b")]
+                + [(k, ctypes.c_int32) for k in ("rank2", "kron_p", "kron_q", "reserved")]
+                + [(k, ctypes.c_void_p) for k in ("A2", "B2", "C")])
 
 
 class tpa_adapter_info(ctypes.Structure):
@@ -170,18 +172,19 @@ def tpa_vera_shared_set(layer, r_v, A, B, stream=0):
 
 
 def _desc(method, rank=0, oft_block=0, c=1.0, A=None, B=None, m=None, l=None, d=None, e=None, Q=None, s=None,
-          b=None):
+          b=None, rank2=0, kron_p=0, kron_q=0, A2=None, B2=None, C=None):
     """A tpa_adapter_desc and the float32 arrays it points into (keep both
     alive until the call returns)."""
-    keep = {k: _f32(v) for k, v in dict(A=A, B=B, m=m, l=l, d=d, e=e, Q=Q, s=s, b=b).items()}
+    keep = {k: _f32(v) for k, v in dict(A=A, B=B, m=m, l=l, d=d, e=e, Q=Q, s=s, b=b, A2=A2, B2=B2, C=C).items()}
     desc = tpa_adapter_desc(METHODS.get(method, method), rank, oft_block, c,
-                            *[_ptr(keep[k]) for k in ("A", "B", "m", "l", "d", "e", "Q", "s", "b")])
+                            *[_ptr(keep[k]) for k in ("A", "B", "m", "l", "d", "e", "Q", "s", "b")],
+                            rank2, kron_p, kron_q, 0, *[_ptr(keep[k]) for k in ("A2", "B2", "C")])
     return desc, keep
 
 
-def tpa_adapter_load(layer, method, rank=0, oft_block=0, c=1.0, A=None, B=None, m=None, l=None, d=None,
-                     e=None, Q=None, s=None, b=None, stream=0):
-    desc, keep = _desc(method, rank, oft_block, c, A, B, m, l, d, e, Q, s, b)
+def tpa_adapter_load(layer, method, stream=0, **fields):
+    """fields: the tpa_adapter_desc members the method uses (rank, c, A, ...)."""
+    desc, keep = _desc(method, **fields)
     slot = ctypes.c_int32()
     _check(_lib.tpa_adapter_load(layer, ctypes.byref(desc), ctypes.byref(slot), stream))
     del keep

@@ -158,6 +158,9 @@ bool method_shape(int method, int* owned, int* present, int* term) {
     case TPA_VERA: *owned = OWN_D | OWN_E; *present = PR_C | PR_D | PR_E; *term = 2; return true;
     case TPA_OFT: *owned = OWN_R; *present = PR_R; *term = 0; return true;
     case TPA_SSF: *owned = 0; *present = PR_S | PR_B; *term = 0; return true;
+    // LoHa and LoKr once expanded into one low-rank term (§3.1): like LoRA.
+    case TPA_LOHA: *owned = OWN_A | OWN_B; *present = PR_C; *term = 1; return true;
+    case TPA_LOKR: *owned = OWN_A | OWN_B; *present = PR_C; *term = 1; return true;
   }
   return false;
 }
@@ -592,6 +595,26 @@ tpa_status validate_desc(const tpa_layer* L, const tpa_adapter_desc* d) {
     if (!d->d || !d->e) return fail(TPA_ERR_INVALID, "null d or e");
     if (!std::isfinite(d->c) || !finite_all(d->d, L->r_v) || !finite_all(d->e, d_out))
       return fail(TPA_ERR_VALUE, "non-finite VeRA vector");
+  } else if (m == TPA_LOHA) {
+    const int r2 = d->rank2 ? d->rank2 : d->rank;
+    if (d->rank < 1 || r2 < 1 || (long)d->rank * r2 > L->max_rank)
+      return fail(TPA_ERR_INVALID, "LoHa ranks %d x %d must be >= 1 with a product <= max_rank=%d", d->rank, r2,
+                  L->max_rank);
+    if (!d->A || !d->B || !d->A2 || !d->B2) return fail(TPA_ERR_INVALID, "null LoHa factor");
+    if (!std::isfinite(d->c) || !finite_all(d->A, (size_t)d_in * d->rank) ||
+        !finite_all(d->B, (size_t)d->rank * d_out) || !finite_all(d->A2, (size_t)d_in * r2) ||
+        !finite_all(d->B2, (size_t)r2 * d_out))
+      return fail(TPA_ERR_VALUE, "non-finite LoHa factor");
+  } else if (m == TPA_LOKR) {
+    const int p = d->kron_p, q = d->kron_q;
+    if (p < 1 || q < 1 || d_in % p || d_out % q)
+      return fail(TPA_ERR_INVALID, "LoKr factor shape %d x %d must divide %d x %d", p, q, d_in, d_out);
+    if (d->rank < 1 || (long)std::min(p, q) * d->rank > L->max_rank)
+      return fail(TPA_ERR_INVALID, "LoKr rank %d x min(%d, %d) outside [1, max_rank=%d]", d->rank, p, q, L->max_rank);
+    if (!d->C || !d->A || !d->B) return fail(TPA_ERR_INVALID, "null LoKr factor");
+    if (!std::isfinite(d->c) || !finite_all(d->C, (size_t)p * q) ||
+        !finite_all(d->A, (size_t)(d_in / p) * d->rank) || !finite_all(d->B, (size_t)d->rank * (d_out / q)))
+      return fail(TPA_ERR_VALUE, "non-finite LoKr factor");
   } else if (m == TPA_OFT) {
     const int bs = d->oft_block;
     if (oft_bs_index(bs) < 0 || d_in % bs) return fail(TPA_ERR_INVALID, "OFT block %d must be 16, 32 or 64 and divide d_in", bs);
@@ -618,7 +641,55 @@ struct StackTerm {
   std::vector<double> B;        // owned: B as [r][d_out]
   std::vector<double> dv;       // shared: c·d [r_v]
   std::vector<double> e;        // outer vector [d_out]
+  bool e_unit = true;           // e is all ones (nothing to fold into B)
 };
+
+// LoHa / LoKr update as one low-rank term without c (§3.1, "Other methods
+// fit as well"): A [d_in][R], B [R][d_out] with A B = ΔW / c.
+//   LoHa: column (k, l) of A is A1[:,k] ⊙ A2[:,l], row (k, l) of B is
+//         B1[k] ⊙ B2[l] (R = r1 · r2).
+//   LoKr: C ⊗ (A0 B0) = (C ⊗ A0)(I_q ⊗ B0) when q <= p (R = q · r), else
+//         (I_p ⊗ A0)(C ⊗ B0) (R = p · r).
+void expand_product(const tpa_layer* L, const tpa_adapter_desc& d, StackTerm* tm) {
+  const int d_in = L->d_in, d_out = L->d_out;
+  if (d.method == TPA_LOHA) {
+    const int r1 = d.rank, r2 = d.rank2 ? d.rank2 : d.rank, R = r1 * r2;
+    tm->r = R;
+    tm->A.assign((size_t)d_in * R, 0.0);
+    tm->B.assign((size_t)R * d_out, 0.0);
+    for (int i = 0; i < d_in; ++i)
+      for (int k = 0; k < r1; ++k)
+        for (int l = 0; l < r2; ++l)
+          tm->A[(size_t)i * R + k * r2 + l] = (double)d.A[(size_t)i * r1 + k] * d.A2[(size_t)i * r2 + l];
+    for (int k = 0; k < r1; ++k)
+      for (int l = 0; l < r2; ++l)
+        for (int j = 0; j < d_out; ++j)
+          tm->B[(size_t)(k * r2 + l) * d_out + j] = (double)d.B[(size_t)k * d_out + j] * d.B2[(size_t)l * d_out + j];
+    return;
+  }
+  const int p = d.kron_p, q = d.kron_q, r = d.rank, p2 = d_in / p, q2 = d_out / q;
+  const bool left_c = q <= p;  // C rides with A (R = q·r), else with B (R = p·r)
+  const int R = (left_c ? q : p) * r;
+  tm->r = R;
+  tm->A.assign((size_t)d_in * R, 0.0);
+  tm->B.assign((size_t)R * d_out, 0.0);
+  for (int i1 = 0; i1 < p; ++i1)
+    for (int i2 = 0; i2 < p2; ++i2)
+      for (int k1 = 0; k1 < (left_c ? q : p); ++k1) {
+        const double f = left_c ? (double)d.C[(size_t)i1 * q + k1] : (i1 == k1 ? 1.0 : 0.0);
+        if (f == 0.0) continue;
+        for (int k = 0; k < r; ++k)
+          tm->A[(size_t)(i1 * p2 + i2) * R + k1 * r + k] = f * d.A[(size_t)i2 * r + k];
+      }
+  for (int k1 = 0; k1 < (left_c ? q : p); ++k1)
+    for (int k = 0; k < r; ++k)
+      for (int j1 = 0; j1 < q; ++j1) {
+        const double f = left_c ? (k1 == j1 ? 1.0 : 0.0) : (double)d.C[(size_t)k1 * q + j1];
+        if (f == 0.0) continue;
+        for (int j2 = 0; j2 < q2; ++j2)
+          tm->B[(size_t)(k1 * r + k) * d_out + j1 * q2 + j2] = f * d.B[(size_t)k * q2 + j2];
+      }
+}
 
 float half_bits_to_float(uint16_t h) {
   const uint32_t sign = (uint32_t)(h >> 15) << 31;
@@ -833,6 +904,7 @@ tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* sl
   if (!method_shape(d->method, &owned, &present, &term)) return fail(TPA_ERR_METHOD, "unknown method %d", d->method);
   const int d_in = L->d_in, d_out = L->d_out;
   const int m = d->method;
+  if (d->method == TPA_LOHA || d->method == TPA_LOKR) return tpa_adapter_load_stack(L, d, 1, slot_out, stream);
   if (tpa_status e = validate_desc(L, d)) return e;
   int slot = -1;
   for (int i = 1; i < L->max_slots; ++i)
@@ -1026,7 +1098,8 @@ tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members,
   if (!members || !slot_out) return fail(TPA_ERR_INVALID, "null argument");
   if (count < 1 || count > TPA_MAX_STACK) return fail(TPA_ERR_INVALID, "a stack holds 1..%d members (got %d)",
                                                       TPA_MAX_STACK, count);
-  if (count == 1) return tpa_adapter_load(L, members, slot_out, stream);
+  const bool product1 = count == 1 && (members[0].method == TPA_LOHA || members[0].method == TPA_LOKR);
+  if (count == 1 && !product1) return tpa_adapter_load(L, members, slot_out, stream);
   if (L->opt[TPA_OPT_SCALE_ROUTE] >= 2)
     return fail(TPA_ERR_INVALID, "stacks fold later scales into the terms; use a scale route inside the expand");
   for (int j = 0; j < count; ++j) {
@@ -1069,8 +1142,10 @@ tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members,
       for (int c = 0; c < d_out; ++c) S[c] *= sj[c];
       if (!Bsh.empty())
         for (int c = 0; c < d_out; ++c) Bsh[c] *= sj[c];
-      for (StackTerm& tm : terms)
+      for (StackTerm& tm : terms) {
         for (int c = 0; c < d_out; ++c) tm.e[c] *= sj[c];
+        tm.e_unit = false;
+      }
     }
     if (!bj.empty()) {
       if (Bsh.empty()) Bsh.assign(d_out, 0.0);
@@ -1083,11 +1158,20 @@ tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members,
       for (size_t i = 0; i < tm.A.size(); ++i) tm.A[i] = (double)d.c * d.A[i];
       tm.B.assign(d.B, d.B + (size_t)d.rank * d_out);
       tm.e = d.method == TPA_DORA ? sj : std::vector<double>(d_out, 1.0);
+      tm.e_unit = d.method != TPA_DORA;
+      terms.push_back(std::move(tm));
+      fold_mask |= TPA_FOLD_C_A;
+    } else if (d.method == TPA_LOHA || d.method == TPA_LOKR) {
+      StackTerm tm;
+      expand_product(L, d, &tm);
+      for (double& v : tm.A) v *= (double)d.c;
+      tm.e.assign(d_out, 1.0);
       terms.push_back(std::move(tm));
       fold_mask |= TPA_FOLD_C_A;
     } else if (d.method == TPA_VERA) {
       StackTerm tm;
       tm.shared = true;
+      tm.e_unit = false;
       tm.r = L->r_v;
       tm.dv.resize(L->r_v);
       for (int k = 0; k < L->r_v; ++k) tm.dv[k] = (double)d.c * d.d[k];
@@ -1127,7 +1211,7 @@ tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members,
           B_all[(size_t)(k0 + k) * d_out + c] =
               (float)((tm.shared ? Bv[(size_t)c * L->r_v + k] : tm.B[(size_t)k * d_out + c]) * tm.e[c]);
       if (tm.shared) fold_mask |= TPA_FOLD_D_A;
-      fold_mask |= TPA_FOLD_E_B;
+      if (!tm.e_unit) fold_mask |= TPA_FOLD_E_B;
       k0 += tm.r;
     }
   } else if (cls == tpa::CLS_SHARED) {
@@ -1228,7 +1312,7 @@ tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members,
   h.mem = mem;
   h.bytes = off;
   h.info = tpa_adapter_info{};
-  h.info.method = TPA_STACK;
+  h.info.method = count == 1 ? members[0].method : TPA_STACK;
   h.info.term_kind = cls == tpa::CLS_OWNED ? 1 : cls == tpa::CLS_SHARED ? 2 : 0;
   h.info.rank = cls == tpa::CLS_OWNED ? r_tot : cls == tpa::CLS_SHARED ? L->r_v : 0;
   h.info.oft_block = bs;
@@ -1237,7 +1321,7 @@ tpa_status tpa_adapter_load_stack(tpa_layer* L, const tpa_adapter_desc* members,
                      (cls == tpa::CLS_SHARED ? TPA_LIVE_D | TPA_LIVE_E : 0);
   if (cls == tpa::CLS_OWNED) ++L->n_owned;
   if (cls == tpa::CLS_SHARED) ++L->n_vera;
-  ++L->n_stack;
+  if (count > 1) ++L->n_stack;
   if (has_R) ++L->n_oft_bs[oft_bs_index(bs)];
   update_plan_sig(L);
   *slot_out = slot;

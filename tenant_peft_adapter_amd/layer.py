@@ -61,6 +61,12 @@ class AdaptedLayer:
             kw = dict(c=rec.get("c", 1.0), d=rec["d"], e=rec["e"])
         elif meth == "oft":
             kw = dict(oft_block=rec["Q"].shape[1], Q=rec["Q"])
+        elif meth == "loha":
+            kw = dict(rank=rec["A"].shape[1], rank2=rec["A2"].shape[1], c=rec["c"], A=rec["A"], B=rec["B"],
+                      A2=rec["A2"], B2=rec["B2"])
+        elif meth == "lokr":
+            kw = dict(rank=rec["A"].shape[1], kron_p=rec["C"].shape[0], kron_q=rec["C"].shape[1], c=rec["c"],
+                      C=rec["C"], A=rec["A"], B=rec["B"])
         kw["method"] = meth
         return kw
 

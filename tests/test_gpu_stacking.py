@@ -1,7 +1,9 @@
 """GPU parity of stacked adapters (§3.2 paragraph "Stacking", appendix
 "Stacking"): several members applied in order at one hook, loaded through
 tpa_adapter_load_stack as one slot, against the oracle's sequential
-application of each member's own definition.  Same tolerances as the other
+application of each member's own definition; and of LoHa and LoKr, expanded
+at load into one low-rank term (§3.1, "Other methods fit as well"), against
+their own definitions.  Same tolerances as the other
 parity tests: fp32 layers 1e-4 (mean relative) and 2e-5 · max|h| (max);
 f16 layers 1% and 2e-3 · max|h|."""
 import numpy as np
@@ -21,12 +23,12 @@ def test_stacks_match_oracle(dtype, n):
     wl = synth.tiny_stacks(seed=5000 + n, n=n, dtype=dtype)
     p = wl["projections"][0]
     say("tiny_stacks %s n=%d" % (dtype, n))
-    L = make_layer(p, max_slots=16, max_rank=64)
+    L = make_layer(p, max_slots=24, max_rank=64)
     y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
     y, h, xw = reference(p, wl["slot_of_row"])
     check(y_gpu, y, h, xw, label="stacks %s n=%d" % (dtype, n), **TOL[dtype])
     # every slot on its own rows too (a stack's error must not hide in the mean)
-    for slot in range(1, 12):
+    for slot in range(1, 17):
         rows = np.nonzero(wl["slot_of_row"] == slot)[0]
         if len(rows):
             check(y_gpu[rows], y[rows], h[rows], xw[rows], label="slot %d" % slot, **TOL[dtype])
@@ -36,7 +38,7 @@ def test_stacks_match_oracle(dtype, n):
 def test_stack_metadata():
     wl = synth.tiny_stacks(n=8, dtype="f16")
     p = wl["projections"][0]
-    L = make_layer(p, max_slots=16, max_rank=64)
+    L = make_layer(p, max_slots=24, max_rank=64)
     want = {  # slot: (term_kind, rank, live bits)
         1: (1, 8, B.LIVE_S), 2: (1, 8, B.LIVE_S), 3: (1, 8, B.LIVE_S | B.LIVE_B), 4: (1, 8, B.LIVE_R),
         5: (2, 32, B.LIVE_S | B.LIVE_D | B.LIVE_E), 6: (1, 40, 0),
@@ -49,6 +51,14 @@ def test_stack_metadata():
         assert info["method"] == B.METHODS["stack"], (slot, info)
         assert (info["term_kind"], info["rank"], info["live_mask"]) == (kind, rank, live), (slot, info)
     assert L.info(9)["method"] == B.METHODS["lora"]
+    # LoHa and LoKr: one owned term of the expanded rank, c folded into A
+    for slot, meth, rank in ((12, "loha", 16), (13, "lokr", 16), (14, "lokr", 8)):
+        info = L.info(slot)
+        assert (info["method"], info["term_kind"], info["rank"]) == (B.METHODS[meth], 1, rank), (slot, info)
+        assert (info["fold_mask"], info["live_mask"]) == (B.FOLD_C_A, 0), (slot, info)
+    info = L.info(15)
+    assert (info["method"], info["rank"], info["live_mask"]) == (B.METHODS["stack"], 8, B.LIVE_S), info
+    assert L.info(16)["method"] == B.METHODS["ssf"]
     assert L.info(6)["fold_mask"] & B.FOLD_D_A  # the VeRA term entered in owned form
     L.close()
 
@@ -56,7 +66,7 @@ def test_stack_metadata():
 def test_stack_rejections_and_reload():
     wl = synth.tiny_stacks(n=64, dtype="f16")
     p = wl["projections"][0]
-    L = make_layer(p, max_slots=16, max_rank=64)
+    L = make_layer(p, max_slots=24, max_rank=64)
     ads = p["adapters"]
     oft = ads[4]["members"][0]
     lora = ads[9]
@@ -64,9 +74,13 @@ def test_stack_rejections_and_reload():
         L.load({"method": "stack", "members": [lora, oft]})
     assert ei.value.code == -1
     small = make_layer({**p, "adapters": {}}, max_slots=16, max_rank=32)
-    with pytest.raises(B.TpaError) as ei:  # rank 8 + 32 above max_rank 32
-        small.load(ads[6])
-    assert ei.value.code == -1
+    rng = np.random.default_rng(3)
+    big = (ads[6],  # stacked rank 8 + 32, LoHa 8 x 8, LoKr 16 x 4: all above max_rank 32
+           synth._loha(rng, 256, 256, 8, 8, "f16"), synth._lokr(rng, 256, 256, 16, 16, 4, "f16"))
+    for rec in big:
+        with pytest.raises(B.TpaError) as ei:
+            small.load(rec)
+        assert ei.value.code == -1
     small.close()
     # unload the rotated stacks and load them again: same outputs
     before = run(L, p["x"], wl["slot_of_row"], "f16")

@@ -126,6 +126,28 @@ def _ssf(rng, d_out):
             "b": (0.3 * rng.standard_normal(d_out)).astype(np.float32)}
 
 
+def _loha(rng, d_in, d_out, r1, r2, dtype, c=1.0):
+    """LoHa factors with A ~ N(0, 1/sqrt(d_in)), B ~ N(0, 1/r): each of the
+    two products has entries of variance d_in^-1/2, so their elementwise
+    product has the size of a LoRA update's entries."""
+    return {"method": "loha",
+            "A": round_to(_normal(rng, (d_in, r1), d_in ** -0.25), dtype),
+            "B": round_to(_normal(rng, (r1, d_out), 1.0 / np.sqrt(r1)), dtype),
+            "A2": round_to(_normal(rng, (d_in, r2), d_in ** -0.25), dtype),
+            "B2": round_to(_normal(rng, (r2, d_out), 1.0 / np.sqrt(r2)), dtype),
+            "c": float(c)}
+
+
+def _lokr(rng, d_in, d_out, p, q, r, dtype, c=1.0):
+    """LoKr factors: C [p, q] ~ N(0, 1), A [d_in/p, r] ~ N(0, 1/d_in),
+    B [r, d_out/q] ~ N(0, 1/r) (update entries of a LoRA update's size)."""
+    return {"method": "lokr",
+            "C": round_to(rng.standard_normal((p, q)), dtype),
+            "A": round_to(_normal(rng, (d_in // p, r), 1.0 / np.sqrt(d_in)), dtype),
+            "B": round_to(_normal(rng, (r, d_out // q), 1.0 / np.sqrt(r)), dtype),
+            "c": float(c)}
+
+
 def _vera_shared(rng, d_in, d_out, r_v, dtype):
     return {"A": round_to(_normal(rng, (d_in, r_v), 1.0 / np.sqrt(d_in)), dtype),
             "B": round_to(_normal(rng, (r_v, d_out), 1.0 / np.sqrt(r_v)), dtype)}
@@ -164,12 +186,15 @@ def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False, d_out=None
 
 def tiny_stacks(seed=5000, n=64, d=256, dtype="f32", r=8, r_v=32):
     """Tiny single layer with stacked adapters (several members applied in
-    order at one hook) beside single ones, rows uniform over slots 0..11.
+    order at one hook) beside single ones.
     SSF (absent from the other workloads) draws s = 1 + 0.3 z, b = 0.3 z.
       1 LoRA then (IA)3        2 (IA)3 then LoRA        3 SSF, DoRA, (IA)3
       4 OFT then LoRA          5 VeRA then (IA)3        6 LoRA then VeRA
       7 OFT, VeRA, SSF         8 (IA)3 then SSF         9 LoRA alone
-     10 VeRA alone            11 DoRA then LoRA"""
+     10 VeRA alone            11 DoRA then LoRA
+    and the members expanded at load: 12 LoHa (ranks 4 x 4), 13 LoKr with
+    C 4 x 4 and rank 4, 14 LoKr with C 2 x 8 and rank 4, 15 LoKr then (IA)3,
+    16 SSF alone; rows uniform over slots 0..16."""
     rng = np.random.default_rng(seed)
     p = make_projection(rng, "tiny", d, d, dtype, n)
     p["shared"] = _vera_shared(rng, d, d, r_v, dtype)
@@ -187,8 +212,13 @@ def tiny_stacks(seed=5000, n=64, d=256, dtype="f32", r=8, r_v=32):
         9: _lora(rng, d, d, r, dtype),
         10: _vera(rng, r_v, d),
         11: st(_dora(rng, W, r, dtype), _lora(rng, d, d, r, dtype)),
+        12: _loha(rng, d, d, 4, 4, dtype),
+        13: _lokr(rng, d, d, 4, 4, 4, dtype),
+        14: _lokr(rng, d, d, 2, 8, 4, dtype),
+        15: st(_lokr(rng, d, d, 8, 4, 2, dtype), _ia3(rng, d)),
+        16: _ssf(rng, d),
     }
-    slot_of_row = rng.integers(0, 12, size=n).astype(np.int32)
+    slot_of_row = rng.integers(0, 17, size=n).astype(np.int32)
     return {"name": "tiny_stacks", "dtype": dtype, "n": n,
             "slot_of_row": slot_of_row, "projections": [p]}
 
