@@ -326,7 +326,19 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          streamed decode kernel, per k-group 3, 4 or 6
  *                          (other values take 3; fewer where they do not
  *                          fit); 128 x 128 kernel, 32 KB each, 2..5 (6
- *                          takes the automatic choice) */
+ *                          takes the automatic choice)
+ *   TPA_OPT_OVERLAP      : 1 runs the shrink and its split
+ *                          reduction on a second stream of the layer
+ *                          (default priority) beside OFT's rotation and
+ *                          the base GEMM, forked from and joined to the
+ *                          caller's stream with events, so the forward
+ *                          still behaves as one ordered call on `stream`
+ *                          (and is captured whole into a HIP graph); 0 runs
+ *                          every step on `stream` (the default: measured
+ *                          faster, the fork and join of a graph-replayed
+ *                          decode step cost more than the launch they
+ *                          hide).  The group forward uses the first layer's
+ *                          setting. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -335,6 +347,7 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_GEMM_NB 6
 #define TPA_OPT_GEMM_GROUPS 7
 #define TPA_OPT_GEMM_STAGES 8
+#define TPA_OPT_OVERLAP 9
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no

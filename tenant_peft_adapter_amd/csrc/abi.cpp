@@ -237,7 +237,12 @@ struct tpa_layer {
   int n_owned = 0, n_vera = 0, n_dora = 0, n_stack = 0;
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
-  int opt[9] = {-1, -1, -1, -1, -1, 0, -1, -1, -1};
+  int opt[10] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1};
+  // Second stream (default priority) on which the shrink runs beside the
+  // base GEMM, and the events that fork it from and join it to the caller's
+  // stream; created at the first forward that uses them.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
   SlotArena arena;
@@ -852,6 +857,9 @@ tpa_status tpa_layer_destroy(tpa_layer* L) {
   DeviceGuard guard(L->device);
   (void)hipDeviceSynchronize();
   L->arena.release();
+  if (L->ev_fork) (void)hipEventDestroy(L->ev_fork);
+  if (L->ev_join) (void)hipEventDestroy(L->ev_join);
+  if (L->side) (void)hipStreamDestroy(L->side);
   if (L->stage) (void)hipFree(L->stage);
   if (L->status_dev) (void)hipFree(L->status_dev);
   if (L->vera_mem) (void)hipFree(L->vera_mem);
@@ -1497,10 +1505,29 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   }
 
   // 2. The shrink and OFT's rotation: one launch per OFT block size present
-  //    (the shrink rides in the first), or one for the shrink alone.
+  //    (the shrink rides in the first), or one for the shrink alone.  With
+  //    overlap on, the shrink and its split reduction run on the layer's
+  //    second stream beside OFT's rotation and the base GEMM (neither reads
+  //    V or U), and the expand waits for them.  Off by default: in a graph-
+  //    replayed decode step the fork and join cost more than the launch
+  //    they hide (222 vs 202 µs per decoder layer).
+  const bool overlap = any_term_all && L0->opt[TPA_OPT_OVERLAP] == 1;
+  if (overlap) {
+    if (!L0->side) TPA_HIP(hipStreamCreateWithFlags(&L0->side, hipStreamNonBlocking));
+    if (!L0->ev_fork) TPA_HIP(hipEventCreateWithFlags(&L0->ev_fork, hipEventDisableTiming));
+    if (!L0->ev_join) TPA_HIP(hipEventCreateWithFlags(&L0->ev_join, hipEventDisableTiming));
+    TPA_HIP(hipEventRecord(L0->ev_fork, s));
+    TPA_HIP(hipStreamWaitEvent(L0->side, L0->ev_fork, 0));
+    tpa::PreSlice ps[tpa::MAX_SLICES];
+    for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr);
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, L0->side));
+    for (int i = 0; i < count; ++i)
+      if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], L0->side));
+    TPA_HIP(hipEventRecord(L0->ev_join, L0->side));
+  }
   static const int kBs[3] = {16, 32, 64};
   tpa::PreSlice ps[tpa::MAX_SLICES];
-  bool sh_done = false;
+  bool sh_done = overlap;
   for (int b = 0; b < 3; ++b) {
     bool any = false;
     for (int i = 0; i < count; ++i) any = any || sl[i].L->n_oft_bs[b] > 0;
@@ -1541,7 +1568,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     g.part = reinterpret_cast<float*>(sl[i].w + sl[i].y.hpart);
     g.out = sl[i].out;
     gs[i].side = sh[i];
-    gs[i].has_side = term[i] ? 1 : 0;
+    gs[i].has_side = term[i] && !overlap ? 1 : 0;
     if (c.gemm_path != sl[0].c.gemm_path || !decode_path(c) || c.gemm_nb != sl[0].c.gemm_nb ||
         c.gemm_groups != sl[0].c.gemm_groups || (c.gemm_path == 2 && c.gemm_stages != sl[0].c.gemm_stages))
       one_launch = false;
@@ -1563,7 +1590,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
           TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i], s));  // carries the shrink's reduction
         } else {
           TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
-          if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
+          if (term[i] && !overlap) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
         }
       }
     }
@@ -1608,6 +1635,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     e[i].apply_scale = c.scale_route == 0;
   }
   if (tpa_status st = stage(L0, 4, s)) return st;
+  if (overlap) TPA_HIP(hipStreamWaitEvent(s, L0->ev_join, 0));
   bool same_h = true;
   for (int i = 0; i < count; ++i) same_h = same_h && ((e[i].hpart != nullptr) == (e[0].hpart != nullptr));
   if (same_h) {
@@ -1848,7 +1876,8 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
-  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_GEMM_STAGES) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_OVERLAP) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_OVERLAP && value > 1) return fail(TPA_ERR_INVALID, "overlap must be 0 or 1");
   if (key == TPA_OPT_GEMM_STAGES && value > 0 && (value < 2 || value > 6))
     return fail(TPA_ERR_INVALID, "gemm stages must be 2..6");
   if (key == TPA_OPT_GEMM_NB && value > 0 && value != 1 && value != 2 && value != 4)

@@ -324,3 +324,54 @@ def test_shared_plan_forward_matches_plain_forward():
         Lk.forward_planned(plan, torch.tensor(pk["x"]).half().cuda())
     assert e.value.code == -1
     plan.close()
+
+
+@pytest.mark.parametrize("n,path", [(64, 2), (64, 0), (17, 2), (300, 3), (300, 1)])
+def test_overlap_matches_one_stream(n, path):
+    """The shrink on the layer's second stream (option) gives the same bits
+    as every step on the caller's stream: same kernels, same order of the
+    split sums."""
+    wl = synth.tiny_mixed(seed=70 + n, n=n, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    say("overlap n=%d path=%d" % (n, path))
+    outs = []
+    for ov in (1, 0):
+        L = make_layer(p, max_slots=8, max_rank=32, options={4: path, 9: ov})
+        outs.append(run(L, p["x"], wl["slot_of_row"], "f16"))
+        L.close()
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_graph_capture_group_with_overlap():
+    """A captured plan + group forward (q, k, v with OFT rows: rotation on
+    the caller's stream, shrink on the second stream) replays to the eager
+    result, with eager work between replays."""
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    shapes = (("q", 512, 512), ("k", 512, 256), ("v", 512, 256))
+    wl = synth.decoder_layer_mixed(shapes=shapes, r_v=64)
+    Ls = [make_layer(p, max_slots=32, max_rank=64, options={9: 1}) for p in wl["projections"]]
+    xs = [torch.tensor(p["x"]).half().cuda() for p in wl["projections"]]
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    plan = RowPlan(Ls[0], wl["n"])
+    grp = LayerGroup(Ls, wl["n"])
+    outs = [torch.empty((wl["n"], L.d_out), dtype=torch.float16, device="cuda") for L in Ls]
+    grp.forward(plan.build(Ls[0], sor), xs, outs)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            grp.forward(plan.build(Ls[0], sor), xs, outs)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), rep
+        grp.forward(plan.build(Ls[0], sor), xs)
+        torch.cuda.synchronize()
+
