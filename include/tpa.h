@@ -338,7 +338,11 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          faster, the fork and join of a graph-replayed
  *                          decode step cost more than the launch they
  *                          hide).  The group forward uses the first layer's
- *                          setting. */
+ *                          setting.
+ *   TPA_OPT_WIDE_TILE    : direct-load kernel for n > 64: 256 (256 x 256
+ *                          tiles, 8 waves; needs d_out % 256 == 0) or 128;
+ *                          by default 256 when that gives at least 256
+ *                          tiles, else 128. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -348,19 +352,21 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_GEMM_GROUPS 7
 #define TPA_OPT_GEMM_STAGES 8
 #define TPA_OPT_OVERLAP 9
+#define TPA_OPT_WIDE_TILE 10
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no
  * device work): plan tile rows, base GEMM path (0 register-fed decode
  * kernel, 1 LDS-tiled kernel, 2 streamed decode kernel, 3 direct-load
- * 128 x 128 kernel), its 64-column
+ * tiled kernel), its 64-column
  * blocks per work-group (nb), split-K factor and k range, the shrink's split
  * and k range, the scale route, the decode GEMM's k-groups per work-group
  * and (direct-load kernels, else 0) its LDS buffers (per k-group for the
- * streamed kernel).  For tests and measurement. */
+ * streamed kernel), and path 3's tile edge (128 or 256; else 0).  For tests
+ * and measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
-      gemm_groups, gemm_stages;
+      gemm_groups, gemm_stages, gemm_tile;
 } tpa_config;
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
 

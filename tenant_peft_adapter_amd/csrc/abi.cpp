@@ -203,6 +203,7 @@ struct Config {
   int gemm_split, gemm_kc;
   int shrink_split, shrink_kc;
   int scale_route;
+  int gemm_tile;  // path 3: 128 (128 x 128 tiles) or 256 (256 x 256 tiles)
 };
 
 // The decode GEMMs (n <= 64) always write split partials; the others write
@@ -237,7 +238,7 @@ struct tpa_layer {
   int n_owned = 0, n_vera = 0, n_dora = 0, n_stack = 0;
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
-  int opt[10] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1};
+  int opt[11] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1};
   // Second stream (default priority) on which the shrink runs beside the
   // base GEMM, and the events that fork it from and join it to the caller's
   // stream; created at the first forward that uses them.
@@ -390,7 +391,15 @@ Config choose_config(const tpa_layer* L, int n) {
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
   } else {
     c.gemm_nb = 4;
-    const int tiles = ((n + 127) / 128) * (L->d_out / 128);
+    // Path 3: 256 x 256 tiles once they give every CU one (their waves read
+    // LDS and L2 at the MFMA rate with room to spare), else 128 x 128.
+    c.gemm_tile = 128;
+    if (c.gemm_path == 3 && L->d_out % 256 == 0) {
+      const int pin = L->opt[TPA_OPT_WIDE_TILE];
+      const bool fill = (long)((n + 255) / 256) * (L->d_out / 256) >= 256;
+      if (pin == 256 || (pin != 128 && fill)) c.gemm_tile = 256;
+    }
+    const int tiles = ((n + c.gemm_tile - 1) / c.gemm_tile) * (L->d_out / c.gemm_tile);
     int split = L->opt[TPA_OPT_GEMM_SPLIT];
     if (split <= 0) split = std::max(1, std::min(L->d_in / 512, (256 + tiles - 1) / tiles));
     split = std::min(split, L->d_in / 64);
@@ -1586,7 +1595,9 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
-        if (c.gemm_path == 3) {
+        if (c.gemm_path == 3 && c.gemm_tile == 256) {
+          TPA_HIP(tpa::launch_gemm_big(dtype, gs[i], s));  // carries the shrink's reduction
+        } else if (c.gemm_path == 3) {
           TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i], s));  // carries the shrink's reduction
         } else {
           TPA_HIP(tpa::launch_gemm_tiled(dtype, gs[i].g, s));
@@ -1876,7 +1887,9 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
-  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_OVERLAP) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_WIDE_TILE) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_WIDE_TILE && value > 0 && value != 128 && value != 256)
+    return fail(TPA_ERR_INVALID, "wide tile must be 128 or 256");
   if (key == TPA_OPT_OVERLAP && value > 1) return fail(TPA_ERR_INVALID, "overlap must be 0 or 1");
   if (key == TPA_OPT_GEMM_STAGES && value > 0 && (value < 2 || value > 6))
     return fail(TPA_ERR_INVALID, "gemm stages must be 2..6");
@@ -1911,6 +1924,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   out->scale_route = c.scale_route;
   out->gemm_groups = c.gemm_groups;
   out->gemm_stages = c.gemm_path == 2 || c.gemm_path == 3 ? c.gemm_stages : 0;
+  out->gemm_tile = c.gemm_path == 3 ? c.gemm_tile : 0;
   return TPA_OK;
 }
 

@@ -671,6 +671,136 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_ti
   }
 }
 
+// ----------------------------------------------------------------- big ----
+//
+// The same direct-load GEMM with 256 x 256 tiles, for batches large enough
+// to give every CU a tile.  Work-group = 8 waves; wave (wr, wc) computes 128
+// rows of x by 64 output columns (8 x 4 MFMA tiles, 128 fp32 accumulators
+// per lane).  Per 64-element k slice the tile's 256 x rows and 256 W rows
+// (64 KB) go straight into one of two LDS buffers (8 loads per wave).  Per
+// 32-element k step a wave reads 12 fragments from LDS for 32 MFMAs (the
+// 128 x 128 tile's waves read 8 for 16): with two waves per SIMD that is
+// 96 B per clock of LDS reads per CU at the MFMA rate, below the 128 B a CU
+// delivers, and the slices' trip from L2 into LDS is 32 B per clock instead
+// of 64.  Tile order, split partials and the shrink's reduction in extra
+// work-groups as in the 128 x 128 kernel.
+template <typename T>
+__global__ __launch_bounds__(512) void gemm_big_kernel(GemmSlice sl, int row_tiles, int col_tiles) {
+  typedef typename Frag<T>::V Vt;
+  constexpr int S = 2;
+  constexpr int STAGE = 512 * 128;  // 256 x rows + 256 W rows, 128 B each
+  constexpr int LI = 8;             // loads per wave per slice
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const BaseGemmArgs& a = sl.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int ntile = row_tiles * col_tiles;
+  if ((int)blockIdx.x >= ntile) {
+    if (blockIdx.y == 0) shrink_impl::shrink_reduce_item<T>(sl.side, ((int)blockIdx.x - ntile) * 512 + tid);
+    return;
+  }
+  int t = (int)blockIdx.x;
+  if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+  const int strip = 8 * col_tiles;
+  const int r_first = (t / strip) * 8, r_rows = min(8, row_tiles - r_first);
+  const int rt = r_first + (t % strip) % r_rows, ct = (t % strip) / r_rows;
+  const int row0 = rt * 256, col0 = ct * 256;
+  const int ks = blockIdx.y;
+  const int kbeg = ks * a.kc;
+  const int nst = max(0, min(a.d_in - kbeg, a.kc)) / 64;
+  const T* X = static_cast<const T*>(a.x);
+  const T* XR = static_cast<const T*>(a.x_rot);
+  const T* W = static_cast<const T*>(a.W);
+
+  // Instruction j < 4 loads x rows 32·wave + 8j .. +8 of the tile, j >= 4
+  // W rows 32·wave + 8(j - 4) .. +8; lane = 8 · (row in the instruction) +
+  // LDS chunk.
+  const int lr = lane >> 3, lc = lane & 7;
+  const T* src[LI];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + 8 * j + lr;
+    const int i = row0 + r;
+    const T* base = X;  // rows past n read row 0; their results are not stored
+    if (i < a.n) {
+      base = X + (size_t)i * a.d_in;
+      if (a.rot_pos) {
+        const int rp = a.rot_pos[i];
+        if (rp >= 0) base = XR + (size_t)rp * a.d_in;
+      }
+    }
+    src[j] = base + kbeg + 8 * (lc ^ swz<2>(r));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * wave + 8 * j + lr;
+    src[4 + j] = W + (size_t)(col0 + r) * a.d_in + kbeg + 8 * (lc ^ swz<4>(r));
+  }
+  auto issue = [&](int st) {
+    unsigned char* buf = smem + (size_t)(st % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LI; ++j)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[j] + 64 * st),
+          (__attribute__((address_space(3))) void*)(buf + (j < 4 ? 0 : 256 * 128) +
+                                                    (size_t)(32 * wave + 8 * (j & 3)) * 128),
+          16, 0, 0);
+  };
+
+  int arow[4], brow[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) arow[b] = 64 * wc + perm_col<4>(i16, b);  // W rows (output columns)
+#pragma unroll
+  for (int m = 0; m < 8; ++m) brow[m] = 128 * wr + 16 * m + i16;         // x rows
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nst > 0) issue(0);
+  for (int it = 0; it < nst; ++it) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < nst) issue(it + 1);
+    const unsigned char* buf = smem + (size_t)(it % S) * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int q = 4 * kk + g;
+      Vt af[4], bf[8];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        af[b] = *reinterpret_cast<const Vt*>(buf + 256 * 128 + arow[b] * 128 + 16 * (q ^ swz<4>(arow[b])));
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int row = row0 + 128 * wr + 16 * m + i16;
+    if (row >= a.n) continue;
+    const int col = col0 + 64 * wc + 16 * g;
+    float v[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[4 * b + q] = acc[b][m][q];
+    if (a.split == 1)
+      store_run16<T>(static_cast<T*>(a.out) + (size_t)row * a.d_out + col, v);
+    else
+      store_run16<float>(a.part + ((size_t)ks * a.n + row) * a.d_out + col, v);
+  }
+}
+
 template <typename T, int G>
 hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
   const int mb = sl[0].g.n <= 16 ? 1 : sl[0].g.n <= 32 ? 2 : 4;
@@ -813,6 +943,21 @@ hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& sl, hipStrea
   }
   TPA_WIDE(2) TPA_WIDE(3) TPA_WIDE(4) TPA_WIDE(5)
 #undef TPA_WIDE
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_big(int dtype, const GemmSlice& sl, hipStream_t s) {
+  const BaseGemmArgs& a = sl.g;
+  if (a.n <= 0 || a.d_out % 256 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in)
+    return hipErrorInvalidValue;
+  if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
+  const int row_tiles = (a.n + 255) / 256, col_tiles = a.d_out / 256;
+  const dim3 grid((unsigned)(row_tiles * col_tiles + side_workgroups(sl, 512)), (unsigned)a.split);
+  const size_t lds = (size_t)2 * 512 * 128;
+  if (dtype == 1)
+    hipLaunchKernelGGL((gemm_big_kernel<f16>), grid, dim3(512), lds, s, sl, row_tiles, col_tiles);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<bf16>), grid, dim3(512), lds, s, sl, row_tiles, col_tiles);
   return hipGetLastError();
 }
 

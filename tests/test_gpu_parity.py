@@ -209,3 +209,40 @@ def test_group_forward_gate_up_matches_separate_forwards():
                                                                          device="cuda")])
     assert e.value.code == -1
     plan.close()
+
+
+@pytest.mark.parametrize("n,d,d_out,split", [(300, 256, 256, 0), (513, 640, 512, 0), (200, 256, 768, 2),
+                                             (1024, 512, 256, 3)])
+def test_big_tile_kernel(n, d, d_out, split):
+    """The 256 x 256-tile direct-load kernel pinned at small shapes with
+    ragged row tiles, several column tiles, split-K partials and the
+    shrink's reduction in its grid; against the oracle and bitwise against
+    itself across runs."""
+    wl = synth.tiny_mixed(seed=130 + n + d, n=n, d=d, dtype="f16", with_identity=True, d_out=d_out)
+    p = wl["projections"][0]
+    say("big tile n=%d d=%d d_out=%d split=%d" % (n, d, d_out, split))
+    opts = {4: 3, 10: 256}
+    if split:
+        opts[1] = split
+    L = make_layer(p, max_slots=8, max_rank=32, options=opts)
+    cfg = L.config(n)
+    assert (cfg["gemm_path"], cfg["gemm_tile"]) == (3, 256), cfg
+    if split:
+        assert cfg["gemm_split"] == split, cfg
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y_again = run(L, p["x"], wl["slot_of_row"], "f16")
+    np.testing.assert_array_equal(y_gpu, y_again)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="big n=%d" % n)
+
+
+def test_big_tile_chosen_at_prefill_sizes():
+    """At 4096 rows of a 4096 x 4096 projection the 256 x 256 tiles give one
+    per CU and are chosen; at 1024 rows the 128 x 128 tiles are."""
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    W = torch.zeros((4096, 4096), dtype=torch.float16, device="cuda")
+    L = AdaptedLayer(W, max_slots=4, max_rank=16)
+    assert L.config(4096)["gemm_tile"] == 256
+    assert L.config(1024)["gemm_tile"] == 128
+    assert L.config(64)["gemm_tile"] == 0
+    L.close()
