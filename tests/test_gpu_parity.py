@@ -246,3 +246,66 @@ def test_big_tile_chosen_at_prefill_sizes():
     assert L.config(1024)["gemm_tile"] == 128
     assert L.config(64)["gemm_tile"] == 0
     L.close()
+
+
+@pytest.mark.parametrize("d_out,tenants", [(4096, 1), (4096, 16), (4096, 1024), (14336, 16), (14336, 1024)])
+def test_vera_sweep_full_size(d_out, tenants):
+    """The VeRA tenant sweep at its own sizes (4096 -> 4096 / 14336, 256
+    rows, shared rank-256 pair): sampled rows against the oracle, and the
+    shared-factor path against the same tenants stored as their exact
+    rank-256 LoRA conversion through the owned-factor path (§4.2 equates
+    the two; the conversion rounds its scaled factors to f16 once more)."""
+    wl = synth.vera_sweep(d_out=d_out, tenants=tenants)
+    p = wl["projections"][0]
+    say("vera sweep d_out=%d tenants=%d" % (d_out, tenants))
+    L = make_layer(p, max_slots=tenants + 1, max_rank=256)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    L.close()
+    rows = np.arange(0, wl["n"], 7)
+    y, h, xw = reference(p, wl["slot_of_row"], rows)
+    check(y_gpu[rows], y, h, xw, label="vera sweep")
+    if tenants > 16:
+        return  # the conversion arm of 1024 tenants is 9.6 GB of factors; the smaller sweeps cover it
+    wl2 = synth.vera_sweep(d_out=d_out, tenants=tenants, as_lora=True)
+    p2 = wl2["projections"][0]
+    assert np.array_equal(wl2["slot_of_row"], wl["slot_of_row"])
+    L2 = make_layer(p2, max_slots=tenants + 1, max_rank=256)
+    y_lora = run(L2, p2["x"], wl2["slot_of_row"], "f16")
+    L2.close()
+    check(y_lora[rows], y, h, xw, label="rank-256 LoRA arm")
+    eff = np.linalg.norm(y - xw, axis=1)
+    gap = np.linalg.norm(y_gpu[rows] - y_lora[rows], axis=1)
+    assert np.mean(gap / eff) <= 0.01
+
+
+def test_largest_batch():
+    """The largest batch the plan takes (8192 rows) through every kernel."""
+    wl = synth.tiny_mixed(seed=8192, n=8192, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    say("n=8192")
+    L = make_layer(p, max_slots=8, max_rank=32)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="n=8192")
+
+
+def test_empty_batch_through_the_abi():
+    """n = 0 is a valid call that launches nothing and leaves out alone;
+    n above the plan's limit is rejected before any launch."""
+    from tenant_peft_adapter_amd import binding as B
+    wl = synth.tiny_mixed(seed=3, n=4, dtype="f16")
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=8, max_rank=32)
+    out = torch.full((4, p["d_out"]), 7.0, dtype=torch.float16, device="cuda")
+    x = torch.tensor(p["x"]).half().cuda()
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    ws = L.workspace(4)
+    st = torch.cuda.current_stream().cuda_stream
+    B.tpa_layer_forward(L.handle, x.data_ptr(), sor.data_ptr(), 0, out.data_ptr(), ws.data_ptr(), ws.numel(), st)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    with pytest.raises(B.TpaError) as ei:
+        B.tpa_layer_forward(L.handle, x.data_ptr(), sor.data_ptr(), 8193, out.data_ptr(), ws.data_ptr(),
+                            ws.numel(), st)
+    assert ei.value.code == -1
+    L.close()
