@@ -73,3 +73,46 @@ def test_null_layer_calls_fail_cleanly():
     assert lib.tpa_layer_destroy(None) == 0
     out = ctypes.c_size_t()
     assert lib.tpa_workspace_size(None, 4, ctypes.byref(out)) == -1
+
+
+C_CONSUMER = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "tpa.h"
+int main(void) {
+  tpa_adapter_info info;
+  if (tpa_method_info(TPA_LOHA, &info) != TPA_OK) return 2;
+  printf("%zu %zu %zu %zu %zu %zu %zu %d %d\n", sizeof(tpa_adapter_desc), offsetof(tpa_adapter_desc, b),
+         offsetof(tpa_adapter_desc, rank2), offsetof(tpa_adapter_desc, A2), offsetof(tpa_adapter_desc, C),
+         sizeof(tpa_config), sizeof(tpa_adapter_info), info.fold_mask, info.term_kind);
+  return tpa_method_info(42, &info) == TPA_ERR_METHOD ? 0 : 3;
+}
+"""
+
+
+def test_plain_c_consumer_and_struct_layouts(tmp_path):
+    """The header is plain C: a C99 program compiled with gcc includes it,
+    links libtpa.so and calls a host-only entry point; the structs it sees
+    have the layout the ctypes binding declares."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "consumer.c"
+    src.write_text(C_CONSUMER)
+    exe = tmp_path / "consumer"
+    libdir = os.path.dirname(B.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(B.HEADER), str(src), "-o", str(exe),
+                    "-L", libdir, "-ltpa", "-Wl,-rpath," + libdir], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    size, off_b, off_rank2, off_a2, off_c, cfg, info, fold, term = map(int, res.stdout.split())
+    assert size == ctypes.sizeof(B.tpa_adapter_desc)
+    assert off_b == B.tpa_adapter_desc.b.offset
+    assert off_rank2 == B.tpa_adapter_desc.rank2.offset
+    assert off_a2 == B.tpa_adapter_desc.A2.offset
+    assert off_c == B.tpa_adapter_desc.C.offset
+    assert cfg == ctypes.sizeof(B.tpa_config)
+    assert info == ctypes.sizeof(B.tpa_adapter_info)
+    assert (fold, term) == (B.FOLD_C_A, 1)
