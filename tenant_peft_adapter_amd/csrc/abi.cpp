@@ -206,9 +206,10 @@ struct Config {
   int gemm_tile;  // path 3: 128 (128 x 128 tiles) or 256 (256 x 256 tiles)
 };
 
-// The decode GEMMs (n <= 64) always write split partials; the others write
-// h into out when they do not split k.
 bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2; }
+// The register-fed decode GEMM always writes split partials; the others
+// write h into out (in the layer type) when they do not split k.
+bool h_partials(const Config& c) { return c.gemm_path == 0 || c.gemm_split > 1; }
 
 struct Layout {
   size_t perm, pinfo, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
@@ -272,6 +273,9 @@ int oft_bs_index(int bs) { return bs == 16 ? 0 : bs == 32 ? 1 : bs == 64 ? 2 : -
 // k range of the streamed decode GEMM for a grid of `col_tiles` column tiles
 // (summed over the projections of one launch) over d_in: the largest power
 // of two with at most 16 slices of 64 per k-group and >= 192 work-groups.
+// (Whole-d_in ranges for gate + up, whose 224 column tiles alone fill the
+// grid, write h once in the layer type but made the decode step slower:
+// 208 against 200-204 µs.)
 int stream_kc(long col_tiles, int d_in, int groups) {
   int kc = 64 * groups;
   for (int cand = 4096; cand >= 64 * groups; cand /= 2) {
@@ -447,7 +451,7 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.counts = take(4 * tpa::CNT_WORDS);
   y.plan_end = off;
   y.x_rot = take((size_t)n * L->d_in * esz);
-  const bool need_hpart = decode_path(c) || c.gemm_split > 1;
+  const bool need_hpart = h_partials(c);
   y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
   y.vpart = take((size_t)c.shrink_split * n * L->kmax * 4);
   y.v = take((size_t)n * L->kmax * esz);
@@ -1614,7 +1618,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   for (int i = 0; i < count; ++i) {
     tpa_layer* L = sl[i].L;
     const Config& c = sl[i].c;
-    const bool hsplit = decode_path(c) || c.gemm_split > 1;
+    const bool hsplit = h_partials(c);
     sc[i] = tpa::ScaleArgs{};
     sc[i].y = sl[i].out;
     sc[i].hpart = hsplit ? reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart) : nullptr;

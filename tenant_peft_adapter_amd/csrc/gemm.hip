@@ -384,14 +384,25 @@ __global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> 
         for (int m = 0; m < MB; ++m) acc[b][m] += red[(((q - 1) * 4 + wave) * NB * MB + b * MB + m) * 64 + lane];
   }
 
-  // The lane holds columns col0 + 16·NB·wave + 4·NB·g + [0, 4·NB) of row 16m + i16.
+  // The lane holds columns col0 + 16·NB·wave + 4·NB·g + [0, 4·NB) of row
+  // 16m + i16: fp32 partials when k is split, else h in the layer type.
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int row = 16 * m + i16;
     if (row >= a.n) continue;
-    float* dst = a.part + ((size_t)ks * a.n + row) * a.d_out + col0 + 16 * NB * wave + 4 * NB * g;
+    const size_t col = (size_t)col0 + 16 * NB * wave + 4 * NB * g;
+    if (a.split == 1) {
+      typedef T T4 __attribute__((ext_vector_type(4)));
+      T* dst = static_cast<T*>(a.out) + (size_t)row * a.d_out + col;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = acc[b][m];
+      for (int b = 0; b < NB; ++b)
+        *reinterpret_cast<T4*>(dst + 4 * b) =
+            T4{to_t<T>(acc[b][m][0]), to_t<T>(acc[b][m][1]), to_t<T>(acc[b][m][2]), to_t<T>(acc[b][m][3])};
+    } else {
+      float* dst = a.part + ((size_t)ks * a.n + row) * a.d_out + col;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = acc[b][m];
+    }
   }
 }
 
