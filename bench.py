@@ -181,11 +181,10 @@ def stage_times(layers, step, reps, torch):
     return [[v / reps for v in row] for row in acc]
 
 
-def calibrate(torch):
-    """β_HBM: a 2 GiB device copy (larger than the 256 MB MALL); λ: 200 chained
-    one-block kernels in one graph (appendix "Constants")."""
+def _copy_rate(torch, nbytes, reps):
+    """Bytes read plus written per second by the library's copy probe over a
+    buffer pair of `nbytes`, timed over `reps` back-to-back copies."""
     from tenant_peft_adapter_amd import binding as B
-    nbytes = 1 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     st = torch.cuda.current_stream().cuda_stream
@@ -193,13 +192,24 @@ def calibrate(torch):
         B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    reps = 10
     for _ in range(reps):
         B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, st)
     e1.record()
     torch.cuda.synchronize()
-    beta = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
+    rate = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
     del src, dst
+    return rate
+
+
+def calibrate(torch):
+    """β_HBM: a 2 GiB device copy (1 GiB read + 1 GiB written, larger than the
+    256 MB MALL); β_MALL: the fastest of copies of 16, 32 and 64 MB (1/16 to
+    1/4 of the MALL, read and written back from it); λ: 200 chained one-block
+    kernels in one graph (appendix "Constants", sizes rescaled to this
+    chip's caches).  Returns (β_HBM, λ, β_MALL)."""
+    from tenant_peft_adapter_amd import binding as B
+    beta = _copy_rate(torch, 1 << 30, 10)
+    beta_mall = max(_copy_rate(torch, mb << 20, 200) for mb in (16, 32, 64))
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
@@ -213,7 +223,7 @@ def calibrate(torch):
         g.replay()
     torch.cuda.synchronize()
     lam = (time.perf_counter() - t0) / 20 / 200
-    return beta, lam
+    return beta, lam, beta_mall
 
 
 PROFILE = os.path.join(ROOT, "profiles", "gemm_stream_decoder_layer_mixed.md")
@@ -370,7 +380,7 @@ def stack_main(args):
         print(json.dumps({"workload": "stack eager steps", "layers": NL, "tenants": T, "results": out}))
         return
 
-    beta, lam = calibrate(torch)
+    beta, lam, beta_mall = calibrate(torch)
     results = []
     for n in ns:
         sor_np = stack.zipf_rows(n, T)
@@ -407,7 +417,8 @@ def stack_main(args):
         "workload": "stack: %d Llama-3.1-8B decoder layers x 7 projections, fp16, %d resident tenants "
                     "(LoRA r64, DoRA r64, (IA)3 k/v/up, VeRA r256, OFT b32 in turn), Zipf(1.1) rows" % (NL, T),
         "data": "synthetic (seeded; raw parameters shared per projection and method, one device copy per tenant)",
-        "load_s": round(t_load, 1), "calibration": {"beta_hbm_GBps": beta / 1e9, "lambda_us": lam * 1e6},
+        "load_s": round(t_load, 1), "calibration": {"beta_hbm_GBps": beta / 1e9, "beta_mall_GBps": beta_mall / 1e9,
+                        "lambda_us": lam * 1e6},
         "dL_launches": 0, "results": results}))
 
 
@@ -449,7 +460,7 @@ def main():
     log("per-stage event timing")
     stages = stage_times([layers[m[0]] for m in units], step, args.stage_reps, torch)
     log("calibration")
-    beta, lam = calibrate(torch)
+    beta, lam, beta_mall = calibrate(torch)
 
     # Byte model per projection; measured times per launch unit (a fused
     # group or a single projection), each kernel one launch per unit.
@@ -526,6 +537,7 @@ def main():
             "kernel": "%s (base GEMM of %s in one launch)" % (dom_name, ", ".join(names[i] for i in units[du])),
             "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
             "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": profiled_traffic(dom_name, dom_cfg),
+            "frac_of_copy_rate": dom_bytes / dom_time / beta,
             "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
             "us_event_pair_cost": pair_cost * 1e6, "config": dom_cfg,
         },
@@ -534,7 +546,8 @@ def main():
         "adapter_path": {"bytes_per_step": adapter_bytes, "us_per_step_shrink_oft_expand": adapter_time * 1e6,
                          "GBps": adapter_bytes / adapter_time / 1e9, "launches": adapter_launches,
                          "predicted_step_us": predicted * 1e6},
-        "calibration": {"beta_hbm_GBps": beta / 1e9, "lambda_us": lam * 1e6},
+        "calibration": {"beta_hbm_GBps": beta / 1e9, "beta_mall_GBps": beta_mall / 1e9,
+                        "lambda_us": lam * 1e6},
         "stages_us_raw_events": {nm: dict(zip(("plan", "shrink+oft", "gemm+reduce", "pre-expand", "expand"),
                                               [round(v, 2) for v in st]))
                                  for nm, st in zip(unit_names, stages)},
