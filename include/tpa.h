@@ -342,7 +342,14 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *   TPA_OPT_WIDE_TILE    : direct-load kernel for n > 64: 256 (256 x 256
  *                          tiles, 8 waves; needs d_out % 256 == 0) or 128;
  *                          by default 256 when that gives at least 256
- *                          tiles, else 128. */
+ *                          tiles, else 128.
+ *   TPA_OPT_FUSE_EXPAND  : 128 x 128 direct-load kernel with k whole: 1 runs
+ *                          the expand in the GEMM's epilogue (the GEMM
+ *                          takes the rows in the plan's tile order, 16 row
+ *                          slots per tile, keeps h in fp32 and writes out
+ *                          once; the shrink's reduction becomes a launch
+ *                          before it); 0 (default) a separate expand, which
+ *                          measured faster. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -353,6 +360,7 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_GEMM_STAGES 8
 #define TPA_OPT_OVERLAP 9
 #define TPA_OPT_WIDE_TILE 10
+#define TPA_OPT_FUSE_EXPAND 11
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no
@@ -362,11 +370,11 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
  * blocks per work-group (nb), split-K factor and k range, the shrink's split
  * and k range, the scale route, the decode GEMM's k-groups per work-group
  * and (direct-load kernels, else 0) its LDS buffers (per k-group for the
- * streamed kernel), and path 3's tile edge (128 or 256; else 0).  For tests
- * and measurement. */
+ * streamed kernel), path 3's tile edge (128 or 256; else 0), and whether
+ * the expand runs in the GEMM's epilogue.  For tests and measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
-      gemm_groups, gemm_stages, gemm_tile;
+      gemm_groups, gemm_stages, gemm_tile, fused_expand;
 } tpa_config;
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtpa.so")
-SOURCES = ("abi.cpp", "plan.hip", "pre.hip", "gemm.hip", "expand.hip", "load.hip")
+SOURCES = ("abi.cpp", "plan.hip", "pre.hip", "gemm.hip", "fused.hip", "expand.hip", "load.hip")
 ARCH = "gfx950"
 
 

@@ -204,6 +204,7 @@ struct Config {
   int shrink_split, shrink_kc;
   int scale_route;
   int gemm_tile;  // path 3: 128 (128 x 128 tiles) or 256 (256 x 256 tiles)
+  int fused;      // path 3, 128 x 128 tiles: the expand runs in the GEMM's epilogue
 };
 
 bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2; }
@@ -239,7 +240,7 @@ struct tpa_layer {
   int n_owned = 0, n_vera = 0, n_dora = 0, n_stack = 0;
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
-  int opt[11] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1};
+  int opt[12] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1, -1};
   // Second stream (default priority) on which the shrink runs beside the
   // base GEMM, and the events that fork it from and join it to the caller's
   // stream; created at the first forward that uses them.
@@ -417,6 +418,14 @@ Config choose_config(const tpa_layer* L, int n) {
     }
   }
   c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];
+  // Expand in the GEMM's epilogue (by option only): needs the 128 x 128
+  // prefill kernel with k whole, 16-row plan tiles and s applied in the
+  // expand.  Measured slower than the separate expand (prefill q_proj, 1024
+  // rows: 90 against 77 µs per layer): one work-group per CU runs its
+  // epilogue's dependent loads after its GEMM with nothing to overlap them,
+  // where the separate expand spreads them over thousands of waves.
+  c.fused = c.gemm_path == 3 && c.gemm_tile == 128 && c.gemm_split == 1 && c.tile_rows == 16 &&
+            c.scale_route == 0 && L->dtype != TPA_F32 && L->opt[TPA_OPT_FUSE_EXPAND] == 1;
   set_shrink_split(L, &c);
   return c;
 }
@@ -1599,7 +1608,9 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
-        if (c.gemm_path == 3 && c.gemm_tile == 256) {
+        if (c.fused) {
+          // launched with the expand's arguments below
+        } else if (c.gemm_path == 3 && c.gemm_tile == 256) {
           TPA_HIP(tpa::launch_gemm_big(dtype, gs[i], s));  // carries the shrink's reduction
         } else if (c.gemm_path == 3) {
           TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i], s));  // carries the shrink's reduction
@@ -1648,15 +1659,32 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     e[i].d_out = L->d_out;
     e[i].max_tiles = all_tile_bound(L, n, tile_rows, sl[i].y.max_tiles);
     e[i].apply_scale = c.scale_route == 0;
+    if (c.fused) {
+      // The shrink's reduction as a launch of its own (V / U must be final
+      // before the GEMM's epilogue reads them), then the GEMM with the
+      // expand in its epilogue over the plan's tiles.
+      if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], s));
+      tpa::FusedArgs f{};
+      f.g = gs[i].g;
+      f.e = e[i];
+      f.list_tiles = p.max_tiles;
+      f.row_tiles = (std::min(e[i].max_tiles, p.max_tiles) + 7) / 8;
+      f.col_tiles = L->d_out / 128;
+      TPA_HIP(tpa::launch_gemm_fused(dtype, c.gemm_stages, f, s));
+    }
   }
   if (tpa_status st = stage(L0, 4, s)) return st;
   if (overlap) TPA_HIP(hipStreamWaitEvent(s, L0->ev_join, 0));
-  bool same_h = true;
-  for (int i = 0; i < count; ++i) same_h = same_h && ((e[i].hpart != nullptr) == (e[0].hpart != nullptr));
-  if (same_h) {
+  bool same_h = true, any_fused = false;
+  for (int i = 0; i < count; ++i) {
+    same_h = same_h && ((e[i].hpart != nullptr) == (e[0].hpart != nullptr));
+    any_fused = any_fused || sl[i].c.fused;
+  }
+  if (same_h && !any_fused) {
     TPA_HIP(tpa::launch_expand(dtype, tile_rows, e, count, s));
   } else {
-    for (int i = 0; i < count; ++i) TPA_HIP(tpa::launch_expand(dtype, tile_rows, &e[i], 1, s));
+    for (int i = 0; i < count; ++i)
+      if (!sl[i].c.fused) TPA_HIP(tpa::launch_expand(dtype, tile_rows, &e[i], 1, s));
   }
   for (int i = 0; i < count; ++i) {
     sc[i].hpart = nullptr;
@@ -1891,7 +1919,8 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
-  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_WIDE_TILE) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_FUSE_EXPAND) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_FUSE_EXPAND && value > 1) return fail(TPA_ERR_INVALID, "fused expand must be 0 or 1");
   if (key == TPA_OPT_WIDE_TILE && value > 0 && value != 128 && value != 256)
     return fail(TPA_ERR_INVALID, "wide tile must be 128 or 256");
   if (key == TPA_OPT_OVERLAP && value > 1) return fail(TPA_ERR_INVALID, "overlap must be 0 or 1");
@@ -1929,6 +1958,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   out->gemm_groups = c.gemm_groups;
   out->gemm_stages = c.gemm_path == 2 || c.gemm_path == 3 ? c.gemm_stages : 0;
   out->gemm_tile = c.gemm_path == 3 ? c.gemm_tile : 0;
+  out->fused_expand = c.fused;
   return TPA_OK;
 }
 

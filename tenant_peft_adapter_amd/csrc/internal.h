@@ -185,6 +185,19 @@ struct ExpandArgs {
 // Every slice must have hpart set, or every slice must have it null.
 hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int count, hipStream_t stream);
 
+// Prefill base GEMM (n > 64, f16 / bf16, k not split) whose epilogue is the
+// expand: rows taken in the plan's tile order (16 row slots per tile of
+// tile_rows 16), out written once.  g.x / x_rot / rot_pos / W / n / d_in /
+// d_out as for the other GEMMs; e as for the expand (h comes from the GEMM,
+// hpart unused, apply_scale must be set).  row_tiles: 128-slot tiles over
+// the plan's tile bound; list_tiles: length of the padded tile list.
+struct FusedArgs {
+  BaseGemmArgs g;
+  ExpandArgs e;
+  int32_t row_tiles, col_tiles, list_tiles;
+};
+hipError_t launch_gemm_fused(int dtype, int stages, const FusedArgs& f, hipStream_t stream);
+
 // Separate scale passes, for the route comparison of the appendix "Routes".
 //   mode 1 side kernel:  h ← h ⊙ s + b        (before the expand)
 //   mode 2 gathered:     out ← out ⊙ s + b    (after the expand)

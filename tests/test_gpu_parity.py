@@ -309,3 +309,60 @@ def test_empty_batch_through_the_abi():
                             ws.numel(), st)
     assert ei.value.code == -1
     L.close()
+
+
+@pytest.mark.parametrize("wl_name,n,d,dtype", [("tiny_mixed", 65, 256, "f16"), ("tiny_mixed", 300, 640, "f16"),
+                                               ("tiny_mixed", 1024, 256, "f16"), ("tiny_mixed", 300, 256, "bf16"),
+                                               ("tiny_stacks", 300, 256, "f16")])
+def test_fused_expand_epilogue(wl_name, n, d, dtype):
+    """The expand in the prefill GEMM's epilogue (rows in plan-tile order)
+    against the oracle, and against the same layer with the expand as a
+    launch of its own (which reads h back rounded to the layer type, so the
+    two differ by that rounding times s)."""
+    if wl_name == "tiny_mixed":
+        wl = synth.tiny_mixed(seed=170 + n + d, n=n, d=d, dtype=dtype, with_identity=True)
+    else:
+        wl = synth.tiny_stacks(seed=170 + n, n=n, dtype=dtype)
+    p = wl["projections"][0]
+    sor = wl["slot_of_row"].copy()
+    sor[::37] = 99  # rows of an unknown slot: computed as the identity, flag raised
+    say("fused expand %s n=%d d=%d %s" % (wl_name, n, d, dtype))
+    outs = []
+    for fuse in (1, 0):
+        L = make_layer(p, max_slots=24, max_rank=64, options={4: 3, 10: 128, 1: 1, 11: fuse})
+        cfg = L.config(n)
+        assert (cfg["gemm_path"], cfg["gemm_tile"], cfg["gemm_split"], cfg["fused_expand"]) == (3, 128, 1, fuse), cfg
+        outs.append(run(L, p["x"], sor, dtype))
+        assert L.error_flag(clear=True) == 1
+        L.close()
+    ref_sor = np.where(sor == 99, 0, sor)
+    y, h, xw = reference(p, ref_sor)
+    tol = dict(mean_tol=0.01, max_tol=2e-3) if dtype == "f16" else dict(mean_tol=0.05, max_tol=1.6e-2)
+    check(outs[0], y, h, xw, label="fused", **tol)
+    # The separate expand reads h back rounded to the layer type, which adds
+    # up to |s| · u · |h| per element (u the type's unit roundoff); stacked
+    # members multiply their scales, so there only the mean criterion is a
+    # fixed bound for it.
+    check(outs[1], y, h, xw, label="separate", mean_tol=tol["mean_tol"], max_tol=1.0)
+    diff = np.abs(outs[0] - outs[1]).max()
+    say("fused vs separate expand: max diff", diff)
+    if wl_name == "tiny_mixed":
+        assert diff <= tol["max_tol"] * np.abs(h).max()
+
+
+def test_fused_expand_at_prefill():
+    """At the prefill workload (16 segments of 64 rows, 1024 rows) the fused
+    epilogue (an option; the separate expand is the default) matches the
+    oracle."""
+    wl = synth.prefill_lora_dora(n=1024, tenants=16)
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=32, max_rank=16)
+    assert L.config(1024)["fused_expand"] == 0
+    L.set_option(11, 1)
+    cfg = L.config(1024)
+    assert cfg["fused_expand"] == 1, cfg
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    rows = np.arange(0, 1024, 9)
+    y, h, xw = reference(p, wl["slot_of_row"], rows)
+    check(y_gpu[rows], y, h, xw, label="fused prefill")
+    L.close()
