@@ -205,12 +205,13 @@ struct Config {
   int scale_route;
   int gemm_tile;  // path 3: 128 (128 x 128 tiles) or 256 (256 x 256 tiles)
   int fused;      // path 3, 128 x 128 tiles: the expand runs in the GEMM's epilogue
+  int h_fp32;     // h goes to the expand in fp32 even when k is not split
 };
 
 bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2; }
 // The register-fed decode GEMM always writes split partials; the others
 // write h into out (in the layer type) when they do not split k.
-bool h_partials(const Config& c) { return c.gemm_path == 0 || c.gemm_split > 1; }
+bool h_partials(const Config& c) { return c.gemm_path == 0 || c.gemm_split > 1 || c.h_fp32; }
 
 struct Layout {
   size_t perm, pinfo, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
@@ -426,6 +427,10 @@ Config choose_config(const tpa_layer* L, int n) {
   // where the separate expand spreads them over thousands of waves.
   c.fused = c.gemm_path == 3 && c.gemm_tile == 128 && c.gemm_split == 1 && c.tile_rows == 16 &&
             c.scale_route == 0 && L->dtype != TPA_F32 && L->opt[TPA_OPT_FUSE_EXPAND] == 1;
+  // A stacked slot's scale is the product of its members' scales, so h
+  // rounded to the layer type before the expand would carry |s|·u·|h| of
+  // error: such layers keep h in fp32 between the GEMM and the expand.
+  c.h_fp32 = L->n_stack > 0 && !c.fused;
   set_shrink_split(L, &c);
   return c;
 }
@@ -1586,6 +1591,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     g.d_in = L->d_in;
     g.d_out = L->d_out;
     g.split = c.gemm_split;
+    g.h_fp32 = c.h_fp32;
     g.kc = c.gemm_kc;
     g.part = reinterpret_cast<float*>(sl[i].w + sl[i].y.hpart);
     g.out = sl[i].out;

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> 
     const int row = 16 * m + i16;
     if (row >= a.n) continue;
     const size_t col = (size_t)col0 + 16 * NB * wave + 4 * NB * g;
-    if (a.split == 1) {
+    if (a.split == 1 && !a.h_fp32) {
       typedef T T4 __attribute__((ext_vector_type(4)));
       T* dst = static_cast<T*>(a.out) + (size_t)row * a.d_out + col;
 #pragma unroll
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[4 * b + q] = acc[b][m][q];
-    if (a.split == 1) {
+    if (a.split == 1 && !a.h_fp32) {
       store_run16<T>(static_cast<T*>(a.out) + (size_t)row * a.d_out + col, v);
     } else {
       store_run16<float>(a.part + ((size_t)ks * a.n + row) * a.d_out + col, v);
@@ -675,7 +675,7 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_ti
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[4 * b + q] = acc[b][m][q];
-    if (a.split == 1)
+    if (a.split == 1 && !a.h_fp32)
       store_run16<T>(static_cast<T*>(a.out) + (size_t)row * a.d_out + col, v);
     else
       store_run16<float>(a.part + ((size_t)ks * a.n + row) * a.d_out + col, v);
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmSlice sl, int row_til
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[4 * b + q] = acc[b][m][q];
-    if (a.split == 1)
+    if (a.split == 1 && !a.h_fp32)
       store_run16<T>(static_cast<T*>(a.out) + (size_t)row * a.d_out + col, v);
     else
       store_run16<float>(a.part + ((size_t)ks * a.n + row) * a.d_out + col, v);

@@ -83,8 +83,9 @@ struct BaseGemmArgs {
   int32_t n, d_in, d_out;
   int32_t split;           // split-K factor
   int32_t kc;              // k range per split (multiple of 32)
-  float* part;             // [split][n][d_out] fp32 partials (split path)
+  float* part;             // [split][n][d_out] fp32 partials (split path, or h_fp32)
   void* out;               // [n][d_out] in the layer type (split == 1, tiled)
+  int32_t h_fp32;          // split == 1: h to part in fp32 rather than to out
 };
 // Skinny kernel: n <= 64 rows; 64·nb output columns per work-group (nb = 1,
 // 2 or 4; d_out % (64·nb) == 0), kc a multiple of 64 whose staged x fits

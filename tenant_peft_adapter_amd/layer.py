@@ -30,7 +30,8 @@ class AdaptedLayer:
         self.handle = B.tpa_layer_create(self.device, self.d_in, self.d_out, self.dtype, self.W.data_ptr(),
                                          max_slots, max_rank)
         self._ws = None
-        self._ws_n = 0
+        self._ws_n = 0     # rows the current workspace was checked for (0: check again)
+        self._ws_max = 0   # most rows asked for so far
 
     def close(self):
         if self.handle:
@@ -75,11 +76,13 @@ class AdaptedLayer:
         numpy arrays in the paper's math layout); returns its slot.  A record
         {"method": "stack", "members": [...]} admits the members as one
         stacked slot, applied in list order."""
+        self._ws_n = 0
         if rec["method"] == "stack":
             return B.tpa_adapter_load_stack(self.handle, [self._kwargs(m) for m in rec["members"]], _stream())
         return B.tpa_adapter_load(self.handle, stream=_stream(), **self._kwargs(rec))
 
     def unload(self, slot):
+        self._ws_n = 0
         B.tpa_adapter_unload(self.handle, slot, _stream())
 
     def info(self, slot):
@@ -93,10 +96,14 @@ class AdaptedLayer:
         return B.tpa_layer_config(self.handle, n)
 
     def workspace(self, n):
+        """A workspace for up to n rows.  Its size also depends on the loaded
+        slots, so loads and unloads make the next call check it again."""
         if self._ws is None or self._ws_n < n:
-            size = B.tpa_workspace_size(self.handle, n)
-            self._ws = torch.empty(max(size, 256), dtype=torch.uint8, device=self.W.device)
-            self._ws_n = n
+            size = B.tpa_workspace_size(self.handle, max(n, self._ws_max))
+            if self._ws is None or self._ws.numel() < size:
+                self._ws = torch.empty(max(size, 256), dtype=torch.uint8, device=self.W.device)
+            self._ws_max = max(n, self._ws_max)
+            self._ws_n = self._ws_max
         return self._ws
 
     def forward(self, x, slot_of_row, out=None, ws=None):

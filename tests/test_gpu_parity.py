@@ -339,15 +339,14 @@ def test_fused_expand_epilogue(wl_name, n, d, dtype):
     y, h, xw = reference(p, ref_sor)
     tol = dict(mean_tol=0.01, max_tol=2e-3) if dtype == "f16" else dict(mean_tol=0.05, max_tol=1.6e-2)
     check(outs[0], y, h, xw, label="fused", **tol)
-    # The separate expand reads h back rounded to the layer type, which adds
-    # up to |s| · u · |h| per element (u the type's unit roundoff); stacked
-    # members multiply their scales, so there only the mean criterion is a
-    # fixed bound for it.
-    check(outs[1], y, h, xw, label="separate", mean_tol=tol["mean_tol"], max_tol=1.0)
+    # The separate expand reads h back rounded to the layer type (adding up
+    # to |s| · u · |h|), except on layers with stacked slots, whose scales
+    # multiply: those keep h in fp32 (this seed's stacks exceeded the max
+    # bound with a rounded h).
+    check(outs[1], y, h, xw, label="separate", **tol)
     diff = np.abs(outs[0] - outs[1]).max()
     say("fused vs separate expand: max diff", diff)
-    if wl_name == "tiny_mixed":
-        assert diff <= tol["max_tol"] * np.abs(h).max()
+    assert diff <= tol["max_tol"] * np.abs(h).max()
 
 
 def test_fused_expand_at_prefill():
