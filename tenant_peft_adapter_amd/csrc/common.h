@@ -97,6 +97,62 @@ __device__ __forceinline__ float to_f(T v) {
   return (float)v;
 }
 
+// s_waitcnt operand that waits for vmcnt <= n and nothing else (gfx9 layout:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at
+// their maxima).  The direct global-to-LDS loads count as vector loads.
+constexpr unsigned waitcnt_vm(int n) { return (unsigned)((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14)); }
+
+// Chunk permutation of the direct-load kernels' 128-byte LDS rows: chunk c
+// of row r is stored at c ^ swz<SH>(r), so that the fragment reads (16 rows,
+// one chunk each) hit distinct bank groups: with l = r & 3 and h = bits SH,
+// SH+1 of the row (the lane's i >> 2 under perm_col), any 8 lanes differ in
+// (row * 128 + 16 * chunk) mod 128 and any 16 lanes in that mod 256.
+template <int SH>
+__device__ __forceinline__ int swz(int r) {
+  const int l = r & 3, h = (r >> SH) & 3;
+  return ((l >> 1) & 1) | ((h & 1) << 1) | ((((h >> 1) ^ l) & 1) << 2);
+}
+
+// 16 consecutive elements of one row, to or from fp32 registers.
+template <typename T>
+__device__ __forceinline__ void load_run16(const T* src, float* v) {
+  typename Frag<T>::V lo = *reinterpret_cast<const typename Frag<T>::V*>(src);
+  typename Frag<T>::V hi = *reinterpret_cast<const typename Frag<T>::V*>(src + 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = to_f<T>(lo[j]);
+    v[8 + j] = to_f<T>(hi[j]);
+  }
+}
+template <>
+__device__ __forceinline__ void load_run16<float>(const float* src, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * q);
+    v[4 * q] = x[0];
+    v[4 * q + 1] = x[1];
+    v[4 * q + 2] = x[2];
+    v[4 * q + 3] = x[3];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store_run16(T* dst, const float* v) {
+  typename Frag<T>::V lo, hi;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    lo[j] = to_t<T>(v[j]);
+    hi[j] = to_t<T>(v[8 + j]);
+  }
+  *reinterpret_cast<typename Frag<T>::V*>(dst) = lo;
+  *reinterpret_cast<typename Frag<T>::V*>(dst + 8) = hi;
+}
+template <>
+__device__ __forceinline__ void store_run16<float>(float* dst, const float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(dst + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+
 // Output column, within a wave's group of 16*NB columns, of a-row i of
 // column block b (see the file comment).
 template <int NB>

@@ -26,46 +26,6 @@ namespace {
 
 constexpr int THREADS = 256;
 
-template <typename T>
-__device__ __forceinline__ void load_run16(const T* src, float* v) {
-  typename Frag<T>::V lo = *reinterpret_cast<const typename Frag<T>::V*>(src);
-  typename Frag<T>::V hi = *reinterpret_cast<const typename Frag<T>::V*>(src + 8);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    v[j] = to_f<T>(lo[j]);
-    v[8 + j] = to_f<T>(hi[j]);
-  }
-}
-template <>
-__device__ __forceinline__ void load_run16<float>(const float* src, float* v) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * q);
-    v[4 * q] = x[0];
-    v[4 * q + 1] = x[1];
-    v[4 * q + 2] = x[2];
-    v[4 * q + 3] = x[3];
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_run16(T* dst, const float* v) {
-  typename Frag<T>::V lo, hi;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    lo[j] = to_t<T>(v[j]);
-    hi[j] = to_t<T>(v[8 + j]);
-  }
-  *reinterpret_cast<typename Frag<T>::V*>(dst) = lo;
-  *reinterpret_cast<typename Frag<T>::V*>(dst + 8) = hi;
-}
-template <>
-__device__ __forceinline__ void store_run16<float>(float* dst, const float* v) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<f32x4*>(dst + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-}
-
 // h of one row segment of 16 columns: the split partials added in split
 // order, their loads issued 4 splits (16 loads) at a time.
 __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size_t split_stride,

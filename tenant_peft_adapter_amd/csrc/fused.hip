@@ -25,28 +25,6 @@ namespace tpa {
 
 namespace {
 
-// s_waitcnt immediate for "at most n vector-memory loads outstanding" (the
-// LDS and export counters left at their maximum).
-constexpr unsigned fwait_vm(int n) { return (unsigned)((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14)); }
-
-template <int SH>
-__device__ __forceinline__ int fswz(int r) {
-  const int l = r & 3, h = (r >> SH) & 3;
-  return ((l >> 1) & 1) | ((h & 1) << 1) | ((((h >> 1) ^ l) & 1) << 2);
-}
-
-template <typename T>
-__device__ __forceinline__ void store16(T* dst, const float* v) {
-  typename Frag<T>::V lo, hi;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    lo[j] = to_t<T>(v[j]);
-    hi[j] = to_t<T>(v[8 + j]);
-  }
-  *reinterpret_cast<typename Frag<T>::V*>(dst) = lo;
-  *reinterpret_cast<typename Frag<T>::V*>(dst + 8) = hi;
-}
-
 template <typename T, int S>
 __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
   typedef typename Frag<T>::V Vt;
@@ -96,12 +74,12 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
         if (rp >= 0) base = XR + (size_t)rp * a.d_in;
       }
     }
-    src[j] = base + 8 * (lc ^ fswz<2>(r));
+    src[j] = base + 8 * (lc ^ swz<2>(r));
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 32 * wave + 8 * j + lr;
-    src[4 + j] = W + (size_t)(col0 + r) * a.d_in + 8 * (lc ^ fswz<4>(r));
+    src[4 + j] = W + (size_t)(col0 + r) * a.d_in + 8 * (lc ^ swz<4>(r));
   }
   auto issue = [&](int st) {
     unsigned char* buf = smem + (size_t)(st % S) * STAGE;
@@ -131,11 +109,11 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
     const int younger = min(S - 2, nst - 1 - it);
     __builtin_amdgcn_sched_barrier(0);
     if (S >= 4 && younger == 2)
-      __builtin_amdgcn_s_waitcnt(fwait_vm(2 * LI));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LI));
     else if (younger == 1)
-      __builtin_amdgcn_s_waitcnt(fwait_vm(LI));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LI));
     else
-      __builtin_amdgcn_s_waitcnt(fwait_vm(0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (it + S - 1 < nst) issue(it + S - 1);
@@ -146,10 +124,10 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
       Vt af[4], bf[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        af[b] = *reinterpret_cast<const Vt*>(buf + 128 * 128 + arow[b] * 128 + 16 * (q ^ fswz<4>(arow[b])));
+        af[b] = *reinterpret_cast<const Vt*>(buf + 128 * 128 + arow[b] * 128 + 16 * (q ^ swz<4>(arow[b])));
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ fswz<2>(brow[m])));
+        bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -227,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
         v[4 * q + j] = r;
       }
     }
-    store16<T>(out + (size_t)row * a.d_out + col, v);
+    store_run16<T>(out + (size_t)row * a.d_out + col, v);
   }
 }
 

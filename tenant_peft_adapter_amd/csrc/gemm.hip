@@ -26,10 +26,6 @@ namespace {
 
 constexpr int THREADS = 256;
 
-// s_waitcnt operand that waits for vmcnt <= n and nothing else (gfx9 layout:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt and lgkmcnt at
-// their maxima).
-constexpr unsigned waitcnt_vm(int n) { return (unsigned)((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14)); }
 
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::V lds_frag(const T* p) {
@@ -216,17 +212,8 @@ __global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(Slices<GemmSlice> 
 // while halving the partials written and read back.  Work-groups past the
 // GEMM's own run the shrink's split reduction, as in gemm_skinny_kernel.
 //
-// Within a 128-byte LDS row the eight 16-byte chunks are permuted, chunk c
-// stored at c ^ swz(row), so that the fragment reads (16 rows, one chunk
-// each) hit distinct bank groups: with l = row & 3 and h = bits SH, SH+1 of
-// the row (the lane's i >> 2 under perm_col), swz mixes l and h so that any
-// 8 lanes differ in (row * 128 + 16 * chunk) mod 128 and any 16 lanes in
-// that mod 256.
-template <int SH>
-__device__ __forceinline__ int swz(int r) {
-  const int l = r & 3, h = (r >> SH) & 3;
-  return ((l >> 1) & 1) | ((h & 1) << 1) | ((((h >> 1) ^ l) & 1) << 2);
-}
+// Within a 128-byte LDS row the eight 16-byte chunks are permuted (swz in
+// common.h) so that the fragment reads hit distinct bank groups.
 
 template <int NB>
 constexpr int log2_nb() {
@@ -407,26 +394,6 @@ __global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> 
 }
 
 // --------------------------------------------------------------- tiled ----
-
-template <typename T>
-__device__ __forceinline__ void store_run16(T* dst, const float* v);
-template <>
-__device__ __forceinline__ void store_run16<float>(float* dst, const float* v) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<f32x4*>(dst + 4 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-}
-template <typename T>
-__device__ __forceinline__ void store_run16(T* dst, const float* v) {
-  typename Frag<T>::V lo, hi;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    lo[j] = to_t<T>(v[j]);
-    hi[j] = to_t<T>(v[8 + j]);
-  }
-  *reinterpret_cast<typename Frag<T>::V*>(dst) = lo;
-  *reinterpret_cast<typename Frag<T>::V*>(dst + 8) = hi;
-}
 
 template <typename T>
 __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
