@@ -348,8 +348,9 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          takes the rows in the plan's tile order, 16 row
  *                          slots per tile, keeps h in fp32 and writes out
  *                          once; the shrink's reduction becomes a launch
- *                          before it); 0 (default) a separate expand, which
- *                          measured faster. */
+ *                          before it); 0 a separate expand; by default
+ *                          the epilogue when the plan's tile bound keeps the
+ *                          row slots within 1.5x the rows. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3

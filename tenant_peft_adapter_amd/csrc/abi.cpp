@@ -419,14 +419,19 @@ Config choose_config(const tpa_layer* L, int n) {
     }
   }
   c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];
-  // Expand in the GEMM's epilogue (by option only): needs the 128 x 128
-  // prefill kernel with k whole, 16-row plan tiles and s applied in the
-  // expand.  Measured slower than the separate expand (prefill q_proj, 1024
-  // rows: 90 against 77 µs per layer): one work-group per CU runs its
-  // epilogue's dependent loads after its GEMM with nothing to overlap them,
-  // where the separate expand spreads them over thousands of waves.
-  c.fused = c.gemm_path == 3 && c.gemm_tile == 128 && c.gemm_split == 1 && c.tile_rows == 16 &&
-            c.scale_route == 0 && L->dtype != TPA_F32 && L->opt[TPA_OPT_FUSE_EXPAND] == 1;
+  // Expand in the GEMM's epilogue: needs the 128 x 128 prefill kernel with
+  // k whole, 16-row plan tiles and s applied in the expand.  The GEMM then
+  // runs over plan tiles (16 row slots each, a short tile's unused slots
+  // computed for nothing), so by default it is taken only when the plan's
+  // tile bound keeps the row slots within 1.5x the rows (prefill q_proj:
+  // 1024 rows 75.8-77.1 against 76.7-78.3 µs per layer, 2048 rows 107-109
+  // against 111-112).
+  c.fused = 0;
+  if (c.gemm_path == 3 && c.gemm_tile == 128 && c.gemm_split == 1 && c.tile_rows == 16 && c.scale_route == 0 &&
+      L->dtype != TPA_F32 && L->opt[TPA_OPT_FUSE_EXPAND] != 0) {
+    const long slots = 16L * ((n + 15) / 16 + std::min(n, L->n_owned) + 2);  // the plan's tile bound
+    c.fused = L->opt[TPA_OPT_FUSE_EXPAND] == 1 || 2 * slots <= 3L * n;
+  }
   // A stacked slot's scale is the product of its members' scales, so h
   // rounded to the layer type before the expand would carry |s|·u·|h| of
   // error: such layers keep h in fp32 between the GEMM and the expand.

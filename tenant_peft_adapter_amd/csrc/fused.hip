@@ -38,11 +38,12 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
   const int wr = wave & 1, wc = wave >> 1;
   const int row_tiles = f.row_tiles, col_tiles = f.col_tiles;
   const int ntile = row_tiles * col_tiles;
-  int t = (int)blockIdx.x;
-  if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-  const int strip = 8 * col_tiles;
-  const int r_first = (t / strip) * 8, r_rows = min(8, row_tiles - r_first);
-  const int rt = r_first + (t % strip) % r_rows, ct = (t % strip) / r_rows;
+  // Row-major tile order: consecutive work-groups go to different XCDs, so
+  // the trailing row tiles (past the plan's real tiles when the tile bound
+  // is loose) are spread over every XCD instead of idling the last ones.
+  const int t = (int)blockIdx.x;
+  (void)ntile;
+  const int rt = t / col_tiles, ct = t % col_tiles;
   const int row0 = rt * 128, col0 = ct * 128;  // row0: row slot (16 per plan tile)
   // Real tiles come first in the plan's list: a work-group whose first
   // tile is padding has nothing to do (the same for all its threads).
@@ -90,6 +91,46 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
           (__attribute__((address_space(3))) void*)(buf + (j < 4 ? 0 : 128 * 128) + (size_t)(32 * wave + 8 * (j & 3)) * 128),
           16, 0, 0);
   };
+
+  // The epilogue's metadata, loaded now so that its chain of dependent
+  // loads (tile header -> slot record -> vector pointers) is in flight while
+  // the GEMM runs: per row block m of this wave, the plan tile, the lane's
+  // row word, the term's rank and factor, and the row's s, b and e.
+  int ekind[4], erow[4], ep0[4], eK[4];
+  const T* eBt[4];
+  const float* esp[4];
+  const float* ebq[4];
+  const float* eep[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int tq = (row0 + 64 * wr + 16 * m) >> 4;
+    int4 tl = make_int4(0, 0, -1, -1);
+    if (tq < f.list_tiles) tl = *reinterpret_cast<const int4*>(e.tiles + 4 * tq);
+    ekind[m] = tl.z;
+    ep0[m] = tl.x;
+    const int w = tl.z >= 0 ? e.tile_rows_w[tq * 16 + i16] : -1;
+    erow[m] = w >= 0 ? (w & 0xFFFF) : -1;
+    const SlotDev* rsd = e.slots + (tl.z == CLS_OWNED ? tl.w : (w >= 0 ? (w >> 16) : 0));
+    esp[m] = nullptr;
+    ebq[m] = nullptr;
+    eep[m] = nullptr;
+    if (w >= 0) {
+      if (e.apply_scale) {
+        esp[m] = gload<const float*>(&rsd->s);
+        ebq[m] = gload<const float*>(&rsd->b);
+      }
+      if (tl.z == CLS_SHARED) eep[m] = gload<const float*>(&rsd->e);
+    }
+    eK[m] = 0;
+    eBt[m] = nullptr;
+    if (tl.z == CLS_OWNED) {
+      eK[m] = e.slots[tl.w].rank;
+      eBt[m] = static_cast<const T*>(e.slots[tl.w].Bt);
+    } else if (tl.z == CLS_SHARED) {
+      eK[m] = e.r_v;
+      eBt[m] = static_cast<const T*>(e.vera_Bt);
+    }
+  }
 
   int arow[4], brow[4];
 #pragma unroll
@@ -143,33 +184,13 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
   const int col = n0 + 16 * g;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int tq = (row0 + 64 * wr + 16 * m) >> 4;
-    if (tq >= f.list_tiles) continue;
-    const int4 tl = *reinterpret_cast<const int4*>(e.tiles + 4 * tq);
-    const int kind = tl.z;
-    if (kind < 0) continue;  // padding tile: the same for the whole wave
-    const int w = e.tile_rows_w[tq * 16 + i16];
-    const int row = w >= 0 ? (w & 0xFFFF) : -1;
-    const SlotDev* rsd = e.slots + (kind == CLS_OWNED ? tl.w : (w >= 0 ? (w >> 16) : 0));
-    const float* sp = nullptr;
-    const float* bq = nullptr;
-    const float* ep = nullptr;
-    if (row >= 0) {
-      if (e.apply_scale) {
-        sp = gload<const float*>(&rsd->s);
-        bq = gload<const float*>(&rsd->b);
-      }
-      if (kind == CLS_SHARED) ep = gload<const float*>(&rsd->e);
-    }
-    int K = 0;
-    const T* Bt = nullptr;
-    if (kind == CLS_OWNED) {
-      K = e.slots[tl.w].rank;
-      Bt = static_cast<const T*>(e.slots[tl.w].Bt);
-    } else if (kind == CLS_SHARED) {
-      K = e.r_v;
-      Bt = static_cast<const T*>(e.vera_Bt);
-    }
+    if (ekind[m] < 0) continue;  // padding tile: the same for the whole wave
+    const int row = erow[m];
+    const float* sp = esp[m];
+    const float* bq = ebq[m];
+    const float* ep = eep[m];
+    const int K = eK[m];
+    const T* Bt = eBt[m];
     f32x4 tac[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) tac[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -177,7 +198,7 @@ __global__ __launch_bounds__(256) void gemm_fused_kernel(FusedArgs f) {
       const T* bp[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) bp[b] = Bt + (size_t)(n0 + perm_col<4>(i16, b)) * K + 8 * g;
-      const T* vp = V + (size_t)(row >= 0 ? tl.x + i16 : 0) * e.kmax + 8 * g;
+      const T* vp = V + (size_t)(row >= 0 ? ep0[m] + i16 : 0) * e.kmax + 8 * g;
       for (int k = 0; k < K; k += 32) {
         const bool ok = k + 8 * g < K;
         Vt af[4];

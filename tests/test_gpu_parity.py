@@ -349,17 +349,16 @@ def test_fused_expand_epilogue(wl_name, n, d, dtype):
     assert diff <= tol["max_tol"] * np.abs(h).max()
 
 
-def test_fused_expand_at_prefill():
+def test_fused_expand_default_at_prefill():
     """At the prefill workload (16 segments of 64 rows, 1024 rows) the fused
-    epilogue (an option; the separate expand is the default) matches the
-    oracle."""
+    epilogue is the default and matches the oracle; with many loaded owned
+    slots the tile bound is loose and the separate expand is kept."""
     wl = synth.prefill_lora_dora(n=1024, tenants=16)
     p = wl["projections"][0]
     L = make_layer(p, max_slots=32, max_rank=16)
-    assert L.config(1024)["fused_expand"] == 0
-    L.set_option(11, 1)
     cfg = L.config(1024)
     assert cfg["fused_expand"] == 1, cfg
+    assert L.config(128)["fused_expand"] == 0  # k is split at 128 rows
     y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
     rows = np.arange(0, 1024, 9)
     y, h, xw = reference(p, wl["slot_of_row"], rows)
