@@ -14,6 +14,11 @@ expand.  `value` is adapted-
 layer rows/s: rows through one adapted projection per second, i.e.
 7 · n / t_step.
 
+The same run also times two other workloads of the layer (`side_targets`):
+the prefill q_proj (1024 rows in 16 segments of LoRA / DoRA r16), with its
+FLOPs over the fp16 MFMA peak, and VeRA's layer time at 1 and 1024 tenants
+(256 rows, 4096 -> 14336, shared rank 256).
+
 Prints one JSON line.  `python bench.py --gpus N` with N > 1 exits: this
 build measures one GPU.
 """
@@ -43,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pure-lora", action="store_true", help="skip the pure-LoRA comparison batch")
+    ap.add_argument("--no-side-targets", action="store_true",
+                    help="skip the prefill q_proj layer and the VeRA tenant sweep")
     ap.add_argument("--stage-reps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
     ap.add_argument("--workload", default="decoder_layer_mixed", choices=("decoder_layer_mixed", "stack"),
@@ -422,6 +429,48 @@ def stack_main(args):
         "dL_launches": 0, "results": results}))
 
 
+def single_layer_time(wl, torch, reps=200, warmup=20, max_rank=256):
+    """Graph-replayed time of one forward of a single-projection workload."""
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    p = wl["projections"][0]
+    n = wl["n"]
+    L = AdaptedLayer(torch.tensor(p["W"]).half().cuda(), max_slots=len(p["adapters"]) + 1, max_rank=max_rank)
+    if p["shared"] is not None:
+        L.set_vera_shared(p["shared"]["A"], p["shared"]["B"])
+    for slot in sorted(p["adapters"]):
+        assert L.load(p["adapters"][slot]) == slot
+    x = torch.tensor(p["x"]).half().cuda()
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    out = torch.empty((n, p["d_out"]), dtype=torch.float16, device="cuda")
+    ws = L.workspace(n)
+    g = capture(lambda: L.forward(x, sor, out=out, ws=ws), torch)
+    t = time_graph(g, reps, warmup, torch)
+    cfg = L.config(n)
+    del g
+    L.close()
+    return t, cfg
+
+
+def side_targets(torch):
+    """The other targets on their own workloads, in the same run: the
+    prefill q_proj layer (1024 rows, 16 segments of LoRA / DoRA r16) with
+    its base GEMM's share of the fp16 MFMA peak, and VeRA's step time from 1
+    to 1024 tenants (256 rows, 4096 -> 14336, shared rank 256)."""
+    from workloads import synth
+    t_pre, cfg = single_layer_time(synth.prefill_lora_dora(n=1024, tenants=16), torch)
+    flops = 2.0 * 1024 * 4096 * 4096
+    vera = {}
+    for T in (1, 1024):
+        vera[T], _ = single_layer_time(synth.vera_sweep(d_out=14336, tenants=T), torch)
+    return {
+        "prefill_q_proj_n1024": {"us_per_layer": t_pre * 1e6, "rows_per_s": 1024 / t_pre,
+                                 "layer_flops_over_mfma_peak": flops / t_pre / MFMA_F16_PEAK,
+                                 "fused_expand": bool(cfg["fused_expand"]), "gemm_tile": cfg["gemm_tile"]},
+        "vera_4096x14336_n256": {"us_T1": vera[1] * 1e6, "us_T1024": vera[1024] * 1e6,
+                                 "growth": vera[1024] / vera[1] - 1.0},
+    }
+
+
 def main():
     args = parse()
     ws = int(os.environ.get("WORLD_SIZE", "1"))
@@ -512,6 +561,11 @@ def main():
             L.close()
         del gp
 
+    side = None
+    if not args.no_side_targets:
+        log("prefill and VeRA-sweep layers")
+        side = side_targets(torch)
+
     out = {
         "metric": METRIC,
         "value": 7 * n / t_step,
@@ -548,6 +602,7 @@ def main():
                          "predicted_step_us": predicted * 1e6},
         "calibration": {"beta_hbm_GBps": beta / 1e9, "beta_mall_GBps": beta_mall / 1e9,
                         "lambda_us": lam * 1e6},
+        "side_targets": side,
         "stages_us_raw_events": {nm: dict(zip(("plan", "shrink+oft", "gemm+reduce", "pre-expand", "expand"),
                                               [round(v, 2) for v in st]))
                                  for nm, st in zip(unit_names, stages)},
