@@ -8,8 +8,9 @@ path never calls it and it never calls the HIP path; the two share no code.
 What it computes (Scute paper, arXiv 2611.01089, "§3.1 The Normal Form",
 eq. (1) and Table 1): each row of a batch belongs to one tenant, and the
 tenant's adapter is applied to the shared base weight W by the plain
-definition of its PEFT method (LoRA, DoRA, (IA)3, VeRA, OFT, SSF), evaluated
-from the adapter's own raw parameters in numpy float64.  A second path
+definition of its PEFT method (LoRA, DoRA, (IA)3, VeRA, OFT, SSF, LoHa,
+LoKr, or a stack of members applied in order), evaluated from the adapter's
+own raw parameters in numpy float64.  A second path
 evaluates eq. (1) literally from the adapter's slots, unfolded and folded.
 
 Conventions (the paper's): rows are tokens, ``x`` is ``[N, d_in]``, the
@@ -23,6 +24,8 @@ unpinned".
 """
 from .methods import (  # noqa: F401
     METHODS,
+    applied_to,
+    product_update,
     cayley,
     oft_rotation,
     dora_column_norm,
@@ -38,5 +41,6 @@ from .normal_form import (  # noqa: F401
     member_table,
     fold_rule,
     stack,
+    expand_product,
 )
 from .layer import layer_forward, plan, parity_metrics  # noqa: F401
