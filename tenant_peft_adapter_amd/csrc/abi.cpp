@@ -1606,7 +1606,16 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
         c.gemm_groups != sl[0].c.gemm_groups || (c.gemm_path == 2 && c.gemm_stages != sl[0].c.gemm_stages))
       one_launch = false;
   }
-  if (one_launch) {
+  // Prefill projections on 256 x 256 tiles (gate and up) share one launch:
+  // their tiles fill whole rounds of the grid together where each alone
+  // leaves the last round half empty.
+  bool big_group = count > 1;
+  for (int i = 0; i < count; ++i)
+    big_group = big_group && sl[i].c.gemm_path == 3 && sl[i].c.gemm_tile == 256 && !sl[i].c.fused &&
+                sl[i].c.gemm_split == sl[0].c.gemm_split;
+  if (big_group) {
+    TPA_HIP(tpa::launch_gemm_big(dtype, gs, count, s));  // carries the shrinks' reductions
+  } else if (one_launch) {
     if (sl[0].c.gemm_path == 2)
       TPA_HIP(tpa::launch_gemm_stream(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, sl[0].c.gemm_stages, gs, count, s));
     else
@@ -1622,7 +1631,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
         if (c.fused) {
           // launched with the expand's arguments below
         } else if (c.gemm_path == 3 && c.gemm_tile == 256) {
-          TPA_HIP(tpa::launch_gemm_big(dtype, gs[i], s));  // carries the shrink's reduction
+          TPA_HIP(tpa::launch_gemm_big(dtype, &gs[i], 1, s));  // carries the shrink's reduction
         } else if (c.gemm_path == 3) {
           TPA_HIP(tpa::launch_gemm_wide(dtype, c.gemm_stages, gs[i], s));  // carries the shrink's reduction
         } else {

@@ -663,22 +663,28 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_ti
 // of 64.  Tile order, split partials and the shrink's reduction in extra
 // work-groups as in the 128 x 128 kernel.
 template <typename T>
-__global__ __launch_bounds__(512) void gemm_big_kernel(GemmSlice sl, int row_tiles, int col_tiles) {
+__global__ __launch_bounds__(512) void gemm_big_kernel(Slices<GemmSlice> ts) {
   typedef typename Frag<T>::V Vt;
   constexpr int S = 2;
   constexpr int STAGE = 512 * 128;  // 256 x rows + 256 W rows, 128 B each
   constexpr int LI = 8;             // loads per wave per slice
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  // Several projections of one input (gate and up) may share the launch:
+  // work-group ranges per projection, each its tiles then its side work.
+  const int si = slice_of(ts, (int)blockIdx.x);
+  const GemmSlice& sl = ts.s[si];
+  const int local = (int)blockIdx.x - ts.first[si];
   const BaseGemmArgs& a = sl.g;
+  const int row_tiles = (a.n + 255) / 256, col_tiles = a.d_out / 256;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int wr = wave & 1, wc = wave >> 1;
   const int ntile = row_tiles * col_tiles;
-  if ((int)blockIdx.x >= ntile) {
-    if (blockIdx.y == 0) shrink_impl::shrink_reduce_item<T>(sl.side, ((int)blockIdx.x - ntile) * 512 + tid);
+  if (local >= ntile) {
+    if (blockIdx.y == 0) shrink_impl::shrink_reduce_item<T>(sl.side, (local - ntile) * 512 + tid);
     return;
   }
-  int t = (int)blockIdx.x;
+  int t = local;
   if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
   const int strip = 8 * col_tiles;
   const int r_first = (t / strip) * 8, r_rows = min(8, row_tiles - r_first);
@@ -924,18 +930,29 @@ hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& sl, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_big(int dtype, const GemmSlice& sl, hipStream_t s) {
-  const BaseGemmArgs& a = sl.g;
-  if (a.n <= 0 || a.d_out % 256 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in)
-    return hipErrorInvalidValue;
-  if (dtype != 1 && dtype != 2) return hipErrorInvalidValue;
-  const int row_tiles = (a.n + 255) / 256, col_tiles = a.d_out / 256;
-  const dim3 grid((unsigned)(row_tiles * col_tiles + side_workgroups(sl, 512)), (unsigned)a.split);
+hipError_t launch_gemm_big(int dtype, const GemmSlice* slices, int count, hipStream_t s) {
+  if (count < 1 || count > MAX_SLICES || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
+  Slices<GemmSlice> t{};
+  t.count = count;
+  t.first[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    const BaseGemmArgs& a = slices[i].g;
+    if (a.n <= 0 || a.n != slices[0].g.n || a.d_out % 256 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 ||
+        (long)a.split * a.kc < a.d_in || a.split != slices[0].g.split)
+      return hipErrorInvalidValue;
+    t.s[i] = slices[i];
+    // Each projection's range starts on a multiple of 8 work-groups, so its
+    // tile order keeps the XCD mapping (work-group i runs on XCD i % 8).
+    const int n_wg = ((a.n + 255) / 256) * (a.d_out / 256) + side_workgroups(slices[i], 512);
+    t.first[i + 1] = t.first[i] + (i + 1 < count ? (n_wg + 7) / 8 * 8 : n_wg);
+  }
+  for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
+  const dim3 grid((unsigned)t.first[count], (unsigned)slices[0].g.split);
   const size_t lds = (size_t)2 * 512 * 128;
   if (dtype == 1)
-    hipLaunchKernelGGL((gemm_big_kernel<f16>), grid, dim3(512), lds, s, sl, row_tiles, col_tiles);
+    hipLaunchKernelGGL((gemm_big_kernel<f16>), grid, dim3(512), lds, s, t);
   else
-    hipLaunchKernelGGL((gemm_big_kernel<bf16>), grid, dim3(512), lds, s, sl, row_tiles, col_tiles);
+    hipLaunchKernelGGL((gemm_big_kernel<bf16>), grid, dim3(512), lds, s, t);
   return hipGetLastError();
 }
 

@@ -158,7 +158,9 @@ size_t gemm_stream_lds(int n, int nb, int groups, int stages);
 hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& slice, hipStream_t stream);
 // The direct-load GEMM with 256 x 256 tiles (8 waves, two 64 KB LDS
 // buffers): d_out % 256 == 0, f16 / bf16; same outputs and side work.
-hipError_t launch_gemm_big(int dtype, const GemmSlice& slice, hipStream_t stream);
+// Several slices (projections of one input, same n and split) may share
+// the launch.
+hipError_t launch_gemm_big(int dtype, const GemmSlice* slices, int count, hipStream_t stream);
 hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const GemmSlice* slices, int count,
                               hipStream_t stream);
 // The shrink's split reduction on its own (when the GEMM cannot carry it).

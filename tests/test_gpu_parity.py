@@ -364,3 +364,30 @@ def test_fused_expand_default_at_prefill():
     y, h, xw = reference(p, wl["slot_of_row"], rows)
     check(y_gpu[rows], y, h, xw, label="fused prefill")
     L.close()
+
+
+@pytest.mark.parametrize("n", [300, 600])
+def test_group_big_tiles_one_launch(n):
+    """Two projections on 256 x 256 tiles as a group run in one launch (the
+    projections' work-group ranges side by side) and give the separate
+    forwards' bits, each matching the oracle."""
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    wa = synth.tiny_mixed(seed=400 + n, n=n, d=256, dtype="f16", with_identity=True, d_out=512)
+    wb = synth.tiny_mixed(seed=401 + n, n=n, d=256, dtype="f16", with_identity=True, d_out=768)
+    wb["slot_of_row"] = wa["slot_of_row"]
+    pa, pb = wa["projections"][0], wb["projections"][0]
+    say("big-tile group n=%d" % n)
+    La = make_layer(pa, max_slots=8, max_rank=32, options={4: 3, 10: 256})
+    Lb = make_layer(pb, max_slots=8, max_rank=32, options={4: 3, 10: 256})
+    assert La.config(n)["gemm_tile"] == 256 and La.config(n)["fused_expand"] == 0
+    sor = torch.tensor(wa["slot_of_row"]).cuda()
+    xs = [torch.tensor(p["x"]).half().cuda() for p in (pa, pb)]
+    sep = [La.forward(xs[0], sor).float().cpu().numpy(), Lb.forward(xs[1], sor).float().cpu().numpy()]
+    plan = RowPlan(La, n).build(La, sor)
+    outs = LayerGroup([La, Lb], n).forward(plan, xs)
+    torch.cuda.synchronize()
+    for o, s_, p in zip(outs, sep, (pa, pb)):
+        np.testing.assert_array_equal(o.float().cpu().numpy(), s_)
+        y, h, xw = reference(p, wa["slot_of_row"])
+        check(s_.astype(np.float64), y, h, xw, label="big group")
+    plan.close()
