@@ -304,10 +304,11 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *   TPA_OPT_SHRINK_SPLIT : split-K factor of the shrink
  *   TPA_OPT_TILE_ROWS    : rows per tile of the plan (16, the default, or
  *                          64)
- *   TPA_OPT_GEMM_PATH    : n <= 64: 0 register-fed decode kernel, 2 decode
- *                          kernel fed by direct global-to-LDS loads (f16 /
- *                          bf16 with d_in % 64 == 0, else 0; the default
- *                          where it applies); any n: 1 LDS-tiled kernel
+ *   TPA_OPT_GEMM_PATH    : n <= 64: 0 register-fed decode kernel; n <= 256:
+ *                          2 decode kernel fed by direct global-to-LDS
+ *                          loads (f16 / bf16 with d_in % 64 == 0, else 0;
+ *                          the default where it applies up to 64 rows, by
+ *                          option up to 256); any n: 1 LDS-tiled kernel
  *                          with register-staged loads, 3 128 x 128 tiles fed
  *                          by direct global-to-LDS loads (f16 / bf16, d_in
  *                          % 64 == 0, d_out % 128 == 0, else 1; the default

@@ -351,6 +351,8 @@ Config choose_config(const tpa_layer* L, int n) {
   const int path_opt = L->opt[TPA_OPT_GEMM_PATH];
   if (path_opt == 1 || path_opt == 3)
     c.gemm_path = path_opt;
+  else if (path_opt == 2 && n <= 256)
+    c.gemm_path = 2;
   else if (n > 64)
     c.gemm_path = 3;
   else

@@ -828,9 +828,12 @@ hipError_t stream_launch(const Slices<GemmSlice>& t, hipStream_t s) {
   }
 }
 
+// 16-row blocks of x per work-group of the streamed GEMM for n rows.
+int stream_mb(int n) { return n <= 16 ? 1 : n <= 32 ? 2 : n <= 64 ? 4 : n <= 128 ? 8 : 16; }
+
 template <typename T, int G, int S>
 hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
-  const int mb = sl[0].g.n <= 16 ? 1 : sl[0].g.n <= 32 ? 2 : 4;
+  const int mb = stream_mb(sl[0].g.n);
   Slices<GemmSlice> t{};
   t.count = count;
   t.first[0] = 0;
@@ -844,8 +847,8 @@ hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
   for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
 #define TPA_ST(MBV, NBV) \
   if (mb == MBV && nb == NBV) return stream_launch<T, MBV, NBV, G, S>(t, s);
-  TPA_ST(1, 1) TPA_ST(2, 1) TPA_ST(4, 1)
-  TPA_ST(1, 2) TPA_ST(2, 2) TPA_ST(4, 2)
+  TPA_ST(1, 1) TPA_ST(2, 1) TPA_ST(4, 1) TPA_ST(8, 1) TPA_ST(16, 1)
+  TPA_ST(1, 2) TPA_ST(2, 2) TPA_ST(4, 2) TPA_ST(8, 2) TPA_ST(16, 2)
   TPA_ST(1, 4) TPA_ST(2, 4) TPA_ST(4, 4)
 #undef TPA_ST
   return hipErrorInvalidValue;
@@ -889,7 +892,7 @@ hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* sl
 }
 
 size_t gemm_stream_lds(int n, int nb, int groups, int stages) {
-  const int mb = n <= 16 ? 1 : n <= 32 ? 2 : 4;
+  const int mb = stream_mb(n);
   return (size_t)groups * stages * (64 * nb + 16 * mb) * 128;
 }
 
@@ -900,7 +903,7 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
     const BaseGemmArgs& a = slices[i].g;
     // Whole 64-element slices in every k range, whole column tiles, rows
     // 64-byte aligned for the 16-byte loads.
-    if (a.n <= 0 || a.n > 64 || a.n != slices[0].g.n || a.kc <= 0 || a.kc % 64 || a.d_in % 64 ||
+    if (a.n <= 0 || a.n > 256 || a.n != slices[0].g.n || a.kc <= 0 || a.kc % 64 || a.d_in % 64 ||
         a.d_out % (64 * nb) || (long)a.split * a.kc < a.d_in)
       return hipErrorInvalidValue;
   }

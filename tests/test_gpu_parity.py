@@ -391,3 +391,19 @@ def test_group_big_tiles_one_launch(n):
         y, h, xw = reference(p, wa["slot_of_row"])
         check(s_.astype(np.float64), y, h, xw, label="big group")
     plan.close()
+
+
+@pytest.mark.parametrize("n", [65, 100, 128, 200, 256])
+@pytest.mark.parametrize("d", [256, 640])
+def test_stream_gemm_up_to_256_rows(n, d):
+    """The streamed GEMM (W read once, all rows of x in each work-group) at
+    65 to 256 rows: 8 or 16 row blocks per work-group, ragged tails."""
+    wl = synth.tiny_mixed(seed=500 + n + d, n=n, d=d, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    say("stream n=%d d=%d" % (n, d))
+    L = make_layer(p, max_slots=8, max_rank=32, options={4: 2})
+    assert L.config(n)["gemm_path"] == 2
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="stream n=%d" % n)
+    L.close()
