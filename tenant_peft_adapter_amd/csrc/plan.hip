@@ -407,7 +407,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t stream) {
   if (a.max_slots < 1 || a.max_slots > 16383) return hipErrorInvalidValue;
   if (a.n <= 64) return plan_launch<64, true>(a, stream);
   if (a.n <= 256) return plan_launch<256, true>(a, stream);
-  if (a.n <= 1024) return plan_launch<256, false>(a, stream);  // 1024 threads from 2048 rows: 20.4 -> 16.3 µs
+  // Thread counts measured per range (graph-replayed plan): 512 threads
+  // from 257 to 1024 rows (1024 rows: 11.7 -> 11.1 µs against 256), 1024
+  // above (2048 rows: 20.4 -> 16.3 µs against 256).
+  if (a.n <= 1024) return plan_launch<512, false>(a, stream);
   return plan_launch<1024, false>(a, stream);
 }
 
