@@ -8,6 +8,7 @@ parity tests: fp32 layers 1e-4 (mean relative) and 2e-5 · max|h| (max);
 f16 layers 1% and 2e-3 · max|h|."""
 import numpy as np
 import pytest
+import torch
 
 from gpu_util import check, make_layer, reference, run, say
 from tenant_peft_adapter_amd import binding as B
@@ -98,3 +99,47 @@ def test_stack_rejections_and_reload():
     s1 = L.load({"method": "stack", "members": [lora]})
     assert L.info(s1)["method"] == B.METHODS["lora"]
     L.close()
+
+
+def test_stack_argument_errors():
+    """Counts outside 1..TPA_MAX_STACK and null pointers are rejected
+    before anything is uploaded; the layer keeps working."""
+    import ctypes
+    wl = synth.tiny_stacks(n=16, dtype="f16")
+    p = wl["projections"][0]
+    L = make_layer({**p, "adapters": {}}, max_slots=8, max_rank=64)
+    lib = B.library()
+    slot = ctypes.c_int32()
+    descs = (B.tpa_adapter_desc * 9)()
+    for count in (0, 9, -1):
+        assert lib.tpa_adapter_load_stack(L.handle, descs, count, ctypes.byref(slot), None) == -1
+    assert lib.tpa_adapter_load_stack(L.handle, None, 2, ctypes.byref(slot), None) == -1
+    assert lib.tpa_adapter_load_stack(L.handle, descs, 2, None, None) == -1
+    descs[0].method, descs[1].method = 42, 1
+    assert lib.tpa_adapter_load_stack(L.handle, descs, 2, ctypes.byref(slot), None) == -2
+    assert L.load(p["adapters"][1]) == 1
+    L.close()
+
+
+@pytest.mark.parametrize("n", [16, 300])
+def test_stacks_and_products_in_a_group(n):
+    """Stacked, LoHa and LoKr slots through a fused group forward (one
+    launch per kernel over three projections sharing the plan) match the
+    separate forwards' outputs within the parity bound and the oracle."""
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    wls = [synth.tiny_stacks(seed=700 + 10 * i + n, n=n, dtype="f16") for i in range(3)]
+    for w in wls[1:]:
+        w["slot_of_row"] = wls[0]["slot_of_row"]
+    ps = [w["projections"][0] for w in wls]
+    Ls = [make_layer(p, max_slots=24, max_rank=64) for p in ps]
+    sor = torch.tensor(wls[0]["slot_of_row"]).cuda()
+    xs = [torch.tensor(p["x"]).half().cuda() for p in ps]
+    plan = RowPlan(Ls[0], n).build(Ls[0], sor)
+    outs = LayerGroup(Ls, n).forward(plan, xs)
+    torch.cuda.synchronize()
+    for o, p in zip(outs, ps):
+        y, h, xw = reference(p, wls[0]["slot_of_row"])
+        check(o.float().cpu().numpy().astype(np.float64), y, h, xw, label="group n=%d" % n, **TOL["f16"])
+    plan.close()
+    for L in Ls:
+        L.close()
