@@ -328,10 +328,15 @@ void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stage
 }
 
 // Shrink: one wave per (tile, 16 factor columns, k range of ~256): short
-// waves, as its launch is on the critical path.
-void set_shrink_split(const tpa_layer* L, Config* c) {
+// waves, as its launch is on the critical path.  From 2048 rows there are
+// enough tiles to fill the chip with longer k ranges (~512, at most 8
+// splits), which halve the fp32 partials written and summed again (2-layer
+// cut of the 1024-tenant Zipf stack at 4096 rows: 2999 -> 2902 µs per
+// layer; at 1024 rows the short ranges stay ahead, 1218 vs 1235).
+void set_shrink_split(const tpa_layer* L, int n, Config* c) {
   int ssplit = L->opt[TPA_OPT_SHRINK_SPLIT];
-  if (ssplit <= 0) ssplit = std::max(1, std::min(28, L->d_in / 256));
+  if (ssplit <= 0)
+    ssplit = n >= 2048 ? std::max(1, std::min(8, L->d_in / 512)) : std::max(1, std::min(28, L->d_in / 256));
   ssplit = std::min(ssplit, L->d_in / 32);
   c->shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
   c->shrink_split = (L->d_in + c->shrink_kc - 1) / c->shrink_kc;
@@ -438,7 +443,7 @@ Config choose_config(const tpa_layer* L, int n) {
   // rounded to the layer type before the expand would carry |s|·u·|h| of
   // error: such layers keep h in fp32 between the GEMM and the expand.
   c.h_fp32 = L->n_stack > 0 && !c.fused;
-  set_shrink_split(L, &c);
+  set_shrink_split(L, n, &c);
   return c;
 }
 
