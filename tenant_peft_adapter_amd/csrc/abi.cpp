@@ -419,10 +419,17 @@ Config choose_config(const tpa_layer* L, int n) {
     c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
     if (c.gemm_path == 3) {
-      // Two buffers (64 KB): the fastest ring depth measured at every
-      // prefill shape; deeper rings only by option.
+      // Two buffers (64 KB) let two work-groups share a CU.  Where the
+      // split grid has at most one per CU and each runs a long k range,
+      // four buffers (three slices in flight) cover more of HBM's latency
+      // (the 14336 -> 4096 down projection, cold weights: 128 rows 40.2 ->
+      // 35.8 µs, 256 rows 63.4 -> 55.2, 512 rows 110 -> 95);
+      // with more work-groups than CUs the deeper ring halves residency
+      // and loses (14336 outputs at 256 rows: 53.6 -> 65.2).
       const int st = L->opt[TPA_OPT_GEMM_STAGES];
-      c.gemm_stages = st >= 2 && st <= 5 ? st : 2;
+      const bool deep = c.gemm_tile == 128 && c.gemm_split > 1 && (long)tiles * c.gemm_split <= 256 &&
+                        c.gemm_kc >= 1536;
+      c.gemm_stages = st >= 2 && st <= 5 ? st : (deep ? 4 : 2);
     }
   }
   c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];

@@ -289,6 +289,21 @@ def test_largest_batch():
     check(y_gpu, y, h, xw, label="n=8192")
 
 
+@pytest.mark.parametrize("n,splits", [(2047, 8), (2048, 4)])
+def test_shrink_split_either_side_of_2048_rows(n, splits):
+    """d_in = 2048: below 2048 rows the shrink takes k ranges of 256 (8
+    splits), from 2048 rows ranges of 512 (4 splits); both against the
+    oracle, every row."""
+    wl = synth.tiny_mixed(seed=2040 + n, n=n, d=2048, dtype="f16", with_identity=True, d_out=512)
+    p = wl["projections"][0]
+    say("shrink split boundary n=%d" % n)
+    L = make_layer(p, max_slots=8, max_rank=32)
+    assert L.config(n)["shrink_split"] == splits
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="shrink split n=%d" % n)
+
+
 def test_empty_batch_through_the_abi():
     """n = 0 is a valid call that launches nothing and leaves out alone;
     n above the plan's limit is rejected before any launch."""
