@@ -337,11 +337,17 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          caller's stream with events, so the forward
  *                          still behaves as one ordered call on `stream`
  *                          (and is captured whole into a HIP graph); 0 runs
- *                          every step on `stream` (the default: measured
- *                          faster, the fork and join of a graph-replayed
- *                          decode step cost more than the launch they
- *                          hide).  The group forward uses the first layer's
- *                          setting.
+ *                          every step on `stream`; the automatic choice
+ *                          overlaps above 64 rows only (the fork and join of a
+ *                          graph-replayed decode step cost more than the
+ *                          launch they hide).  Never where the expand runs
+ *                          in the GEMM's epilogue (that GEMM reads the
+ *                          shrink's output).  The second stream and its two
+ *                          events are created on the first forward that
+ *                          overlaps outside graph capture; a captured
+ *                          forward before then runs on `stream` alone.
+ *                          Both ways give the same bits.  The group
+ *                          forward uses the first layer's setting.
  *   TPA_OPT_WIDE_TILE    : direct-load kernel for n > 64: 256 (256 x 256
  *                          tiles, 8 waves; needs d_out % 256 == 0) or 128;
  *                          by default 256 when that gives at least 256

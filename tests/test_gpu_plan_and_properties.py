@@ -326,20 +326,64 @@ def test_shared_plan_forward_matches_plain_forward():
     plan.close()
 
 
-@pytest.mark.parametrize("n,path", [(64, 2), (64, 0), (17, 2), (300, 3), (300, 1)])
-def test_overlap_matches_one_stream(n, path):
-    """The shrink on the layer's second stream (option) gives the same bits
-    as every step on the caller's stream: same kernels, same order of the
-    split sums."""
+@pytest.mark.parametrize("n,path,fuse", [(64, 2, 0), (64, 0, 0), (17, 2, 0), (100, 3, 0), (300, 3, 0),
+                                         (300, 3, 1), (300, 1, 0)])
+def test_overlap_matches_one_stream(n, path, fuse):
+    """The shrink on the layer's second stream gives the same bits as every
+    step on the caller's stream (option 0): same kernels, same order of the
+    split sums; forced on (1), automatic (-1, on above 64 rows), and with the
+    expand in the GEMM's epilogue (fuse 1), where overlap does not apply."""
     wl = synth.tiny_mixed(seed=70 + n, n=n, dtype="f16", with_identity=True)
     p = wl["projections"][0]
-    say("overlap n=%d path=%d" % (n, path))
+    say("overlap n=%d path=%d fuse=%d" % (n, path, fuse))
     outs = []
-    for ov in (1, 0):
-        L = make_layer(p, max_slots=8, max_rank=32, options={4: path, 9: ov})
+    for ov in (1, -1, 0):
+        opts = {4: path, 9: ov}
+        if fuse >= 0:
+            opts[11] = fuse
+        L = make_layer(p, max_slots=8, max_rank=32, options=opts)
+        assert L.config(n)["fused_expand"] == fuse
         outs.append(run(L, p["x"], wl["slot_of_row"], "f16"))
         L.close()
-    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+    np.testing.assert_array_equal(outs[1], outs[2])
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(outs[0], y, h, xw, label="overlap n=%d" % n)
+
+
+def test_first_forward_inside_graph_capture_with_automatic_overlap():
+    """A fresh layer whose first forward above 64 rows is captured runs that
+    forward on the capturing stream alone (no stream is made during
+    capture); eager forwards afterwards overlap; replays and eager calls
+    give the same bits."""
+    n = 200
+    wl = synth.tiny_mixed(seed=777, n=n, dtype="f16", with_identity=True)
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=8, max_rank=32, options={11: 0})
+    x = torch.tensor(p["x"]).half().cuda()
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    out = torch.empty((n, L.d_out), dtype=torch.float16, device="cuda")
+    L.workspace(n)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            L.forward(x, sor, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = L.forward(x, sor).clone()   # overlapped: the side stream is made now
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        L.forward(x, sor)
+    torch.cuda.synchronize()
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(eager.float().cpu().numpy().astype(np.float64), y, h, xw, label="captured first forward")
 
 
 def test_graph_capture_group_with_overlap():
