@@ -304,6 +304,43 @@ def test_shrink_split_either_side_of_2048_rows(n, splits):
     check(y_gpu, y, h, xw, label="shrink split n=%d" % n)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_large_batch_defaults_every_type(dtype):
+    """2100 rows, d_in 1024 -> 512, default configuration in each layer
+    type: the shrink's long k ranges (2 splits from 2048 rows), the shrink
+    on the second stream (automatic above 64 rows), the tiled GEMM of the
+    type (register-staged for fp32, direct loads for 16-bit types)."""
+    n = 2100
+    wl = synth.tiny_mixed(seed=2100, n=n, d=1024, dtype=dtype, with_identity=True, d_out=512)
+    p = wl["projections"][0]
+    say("large batch defaults", dtype)
+    L = make_layer(p, max_slots=8, max_rank=32)
+    cfg = L.config(n)
+    assert cfg["shrink_split"] == 2 and cfg["gemm_path"] == (1 if dtype == "f32" else 3)
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    tol = F32_TOL if dtype == "f32" else dict(max_tol=2e-3, mean_tol=0.01) if dtype == "f16" else \
+        dict(max_tol=1.6e-2, mean_tol=0.05)
+    check(y_gpu, y, h, xw, label="large batch " + dtype, **tol)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_deep_ring_default_for_long_split_k(dtype):
+    """128 rows of a 14336 -> 4096 projection: 32 tiles x split 8, k ranges
+    of 1792, so the 128 x 128 kernel takes four LDS buffers by default."""
+    n = 128
+    wl = synth.tiny_mixed(seed=1280, n=n, d=14336, dtype=dtype, with_identity=True, d_out=4096)
+    p = wl["projections"][0]
+    say("deep ring", dtype)
+    L = make_layer(p, max_slots=8, max_rank=32)
+    cfg = L.config(n)
+    assert (cfg["gemm_path"], cfg["gemm_split"], cfg["gemm_stages"]) == (3, 8, 4), cfg
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    tol = dict(max_tol=2e-3, mean_tol=0.01) if dtype == "f16" else dict(max_tol=1.6e-2, mean_tol=0.05)
+    check(y_gpu, y, h, xw, label="deep ring " + dtype, **tol)
+
+
 def test_empty_batch_through_the_abi():
     """n = 0 is a valid call that launches nothing and leaves out alone;
     n above the plan's limit is rejected before any launch."""
