@@ -63,11 +63,18 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
   }
 }
 
-template <typename T, int MB, bool HPART>
+// FEW: two k steps in flight instead of four (16-bit types, 16-row tiles):
+// 118 registers instead of 158, so four waves per SIMD instead of three.
+// Above 256 rows there are enough work-groups for the extra waves to pay
+// (2-layer cut of the 1024-tenant Zipf stack: 1024 rows 1211 -> 1198 µs per
+// layer, 4096 rows 2876 -> 2847); at decode sizes the longer dependent
+// chain of a rank-256 VeRA tile costs more (decoder layer 203.7 -> 206.2
+// µs per step), so small batches keep four.
+template <typename T, int MB, bool HPART, bool FEW>
 __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fewer for wide fragments)
-  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 2 : 1) : (MB == 1 ? 4 : 2);
+  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 2 : 1) : (MB == 1 && !FEW ? 4 : 2);
   const int si = slice_of(t, (int)blockIdx.x);
   const ExpandArgs& a = t.s[si];
   const int local = (int)blockIdx.x - t.first[si];
@@ -239,10 +246,18 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
 template <typename T, int MB>
 hipError_t expand_launch(const Slices<ExpandArgs>& t, hipStream_t s) {
   const dim3 grid((unsigned)t.first[t.count]);
-  if (t.s[0].hpart)
-    hipLaunchKernelGGL((expand_kernel<T, MB, true>), grid, dim3(64), 0, s, t);
-  else
-    hipLaunchKernelGGL((expand_kernel<T, MB, false>), grid, dim3(64), 0, s, t);
+  const bool few = sizeof(T) == 2 && MB == 1 && t.s[0].n > 256;
+  if (t.s[0].hpart) {
+    if (few)
+      hipLaunchKernelGGL((expand_kernel<T, MB, true, true>), grid, dim3(64), 0, s, t);
+    else
+      hipLaunchKernelGGL((expand_kernel<T, MB, true, false>), grid, dim3(64), 0, s, t);
+  } else {
+    if (few)
+      hipLaunchKernelGGL((expand_kernel<T, MB, false, true>), grid, dim3(64), 0, s, t);
+    else
+      hipLaunchKernelGGL((expand_kernel<T, MB, false, false>), grid, dim3(64), 0, s, t);
+  }
   return hipGetLastError();
 }
 

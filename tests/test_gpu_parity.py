@@ -158,13 +158,14 @@ def test_stream_gemm_tiny(dtype, n, d, nb, split, groups):
           label="stream " + dtype)
 
 
-@pytest.mark.parametrize("path", [0, 2])
-def test_group_forward_qkv_against_oracle(path):
+@pytest.mark.parametrize("path,n", [(0, 64), (2, 64), (-1, 300)])
+def test_group_forward_qkv_against_oracle(path, n):
     """q, k and v of the decoder-layer workload forwarded as one group (one
     launch per kernel, a shared plan): every row of every projection against
-    the oracle."""
+    the oracle.  At 300 rows the default configuration: 128 x 128 tiles, OFT's
+    rotation on the caller's stream and the shrink on the second stream."""
     from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
-    wl = synth.decoder_layer_mixed(shapes=(("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024)))
+    wl = synth.decoder_layer_mixed(n=n, shapes=(("q", 4096, 4096), ("k", 4096, 1024), ("v", 4096, 1024)))
     projs = wl["projections"]
     Ls = [make_layer(p, max_slots=32, max_rank=256, options={4: path}) for p in projs]
     say("group q+k+v n=%d path=%d" % (wl["n"], path))
