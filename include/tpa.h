@@ -338,7 +338,7 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          still behaves as one ordered call on `stream`
  *                          (and is captured whole into a HIP graph); 0 runs
  *                          every step on `stream`; the automatic choice
- *                          overlaps above 64 rows only (the fork and join of a
+ *                          overlaps above 128 rows only (the fork and join of a
  *                          graph-replayed decode step cost more than the
  *                          launch they hide).  Never where the expand runs
  *                          in the GEMM's epilogue (that GEMM reads the

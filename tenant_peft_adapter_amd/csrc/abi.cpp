@@ -1554,13 +1554,14 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   //    (the shrink rides in the first), or one for the shrink alone.  With
   //    overlap on, the shrink and its split reduction run on the layer's
   //    second stream beside OFT's rotation and the base GEMM (neither reads
-  //    V or U), and the expand waits for them.  By default only above 64
+  //    V or U), and the expand waits for them.  By default only above 128
   //    rows: in a graph-replayed decode step the fork and join cost more
-  //    than the launch they hide (222 vs 202 µs per decoder layer), while
-  //    the 2-layer cut of the 1024-tenant Zipf stack gains at 256 rows
-  //    (508-524 -> 499 µs per layer), 1024 (1203-1219 -> 1156-1159) and
-  //    4096 (2890 -> 2876-2879), the shrink's waves filling CUs the split
-  //    GEMM leaves short of work.  Never where the expand rides in the
+  //    than the launch they hide (222 vs 202 µs per decoder layer; on the
+  //    2-layer cut of the 1024-tenant Zipf stack 96 rows 314-315 -> 318-322
+  //    µs per layer, 128 rows 378 -> 385), while that cut gains at 192 rows
+  //    (442.5 -> 436-437), 1024 (1203-1219 -> 1156-1159) and 4096 (2890 ->
+  //    2876-2879), the shrink's waves filling CUs the split GEMM leaves
+  //    short of work.  Never where the expand rides in the
   //    GEMM's epilogue: that GEMM reads V and U, so nothing could overlap.
   //    The second stream and its events are made on first use, outside
   //    graph capture (a captured forward before then runs on one stream;
@@ -1568,7 +1569,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   bool any_fused_cfg = false;
   for (int i = 0; i < count; ++i) any_fused_cfg = any_fused_cfg || sl[i].c.fused;
   const int ov_opt = L0->opt[TPA_OPT_OVERLAP];
-  bool overlap = any_term_all && !any_fused_cfg && (ov_opt == 1 || (ov_opt < 0 && n > 64));
+  bool overlap = any_term_all && !any_fused_cfg && (ov_opt == 1 || (ov_opt < 0 && n > 128));
   if (overlap && !(L0->side && L0->ev_fork && L0->ev_join)) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) {

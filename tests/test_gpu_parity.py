@@ -309,7 +309,7 @@ def test_shrink_split_either_side_of_2048_rows(n, splits):
 def test_large_batch_defaults_every_type(dtype):
     """2100 rows, d_in 1024 -> 512, default configuration in each layer
     type: the shrink's long k ranges (2 splits from 2048 rows), the shrink
-    on the second stream (automatic above 64 rows), the tiled GEMM of the
+    on the second stream (automatic above 128 rows), the tiled GEMM of the
     type (register-staged for fp32, direct loads for 16-bit types)."""
     n = 2100
     wl = synth.tiny_mixed(seed=2100, n=n, d=1024, dtype=dtype, with_identity=True, d_out=512)

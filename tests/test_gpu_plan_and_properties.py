@@ -331,7 +331,7 @@ def test_shared_plan_forward_matches_plain_forward():
 def test_overlap_matches_one_stream(n, path, fuse):
     """The shrink on the layer's second stream gives the same bits as every
     step on the caller's stream (option 0): same kernels, same order of the
-    split sums; forced on (1), automatic (-1, on above 64 rows), and with the
+    split sums; forced on (1), automatic (-1, on above 128 rows), and with the
     expand in the GEMM's epilogue (fuse 1), where overlap does not apply."""
     wl = synth.tiny_mixed(seed=70 + n, n=n, dtype="f16", with_identity=True)
     p = wl["projections"][0]
@@ -352,7 +352,7 @@ def test_overlap_matches_one_stream(n, path, fuse):
 
 
 def test_first_forward_inside_graph_capture_with_automatic_overlap():
-    """A fresh layer whose first forward above 64 rows is captured runs that
+    """A fresh layer whose first forward above 128 rows is captured runs that
     forward on the capturing stream alone (no stream is made during
     capture); eager forwards afterwards overlap; replays and eager calls
     give the same bits."""
