@@ -265,26 +265,31 @@ def cpu_baseline(wl, min_seconds=10.0, chunk=4):
     """The oracle, untuned, on a bounded sample of the same batch: chunks of
     `chunk` rows (in batch order) through all seven projections until at
     least `min_seconds` have passed."""
+    import contextlib
+
     import numpy as np
     import oracle
+    # The cores this process may run on; BLAS gets one thread per core.
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
     except Exception:  # pragma: no cover
-        threads = 1
+        limit = contextlib.nullcontext()
     rows = 0
-    t0 = time.perf_counter()
-    while rows < wl["n"]:
-        sel = np.arange(rows, min(rows + chunk, wl["n"]))
-        for p in wl["projections"]:
-            x = p["x"][sel].astype(np.float64)
-            oracle.layer_forward(x, p["W"].astype(np.float64).T, wl["slot_of_row"][sel], p["adapters"],
-                                 p["shared"])
-        rows += len(sel)
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": rows * len(wl["projections"]) / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+    with limit:
+        t0 = time.perf_counter()
+        while rows < wl["n"]:
+            sel = np.arange(rows, min(rows + chunk, wl["n"]))
+            for p in wl["projections"]:
+                x = p["x"][sel].astype(np.float64)
+                oracle.layer_forward(x, p["W"].astype(np.float64).T, wl["slot_of_row"][sel], p["adapters"],
+                                     p["shared"])
+            rows += len(sel)
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": rows * len(wl["projections"]) / dt, "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": "first %d of the %d rows, in calls of %d rows, through all %d projections (%.1f s)"
                       % (rows, wl["n"], chunk, len(wl["projections"]), dt)}
 
@@ -325,7 +330,7 @@ def stack_main(args):
             pr = protos[name]
             L.set_vera_shared(pr["shared"]["A"], pr["shared"]["B"])
             for t in range(T):
-                L.load(pr["records"][stack.method_of(t)])
+                L.load(stack.tenant_record(pr, t))
             row.append(L)
         layers.append(row)
         log("stack: layer %d loaded, %.0f s, %.1f GB in use" % (li, time.perf_counter() - t_load,

@@ -149,9 +149,13 @@ tpa_status tpa_method_info(int32_t method, tpa_adapter_info* out);
  *              workspace.
  * Requires d_in a multiple of 64, d_out a multiple of 128, 2 <= max_slots <= 16384,
  * 1 <= max_rank <= 512. */
+/* Per-layer slot storage: Scute paper §5.2 (each adapted layer keeps one
+ * buffer per slot for s, d, e and R beside the LoRA factors). */
 tpa_status tpa_layer_create(int32_t device, int32_t d_in, int32_t d_out, int32_t dtype,
                             const void* W_dev, int32_t max_slots, int32_t max_rank,
                             tpa_layer** out);
+/* Frees the layer's slot storage (§5.2); W stays the caller's.  A null
+ * layer is a no-op. */
 tpa_status tpa_layer_destroy(tpa_layer* layer);
 
 /* Set VeRA's frozen pair shared by every VeRA slot of this layer
@@ -197,15 +201,22 @@ tpa_status tpa_adapter_load(tpa_layer* layer, const tpa_adapter_desc* desc, int3
 tpa_status tpa_adapter_load_stack(tpa_layer* layer, const tpa_adapter_desc* members, int32_t count,
                                   int32_t* slot_out, tpa_stream stream);
 
-/* Free a slot.  Synchronizes `stream` before releasing device memory, so
- * forwards enqueued on it earlier still see the adapter.  -4 if the slot is
- * not loaded. */
+/* Free a slot (admission of §5.1 undone).  Synchronizes `stream` before
+ * releasing device memory, so forwards enqueued on it earlier still see the
+ * adapter (faangrind "multi-lora-serving" page, failure mode "Adapter
+ * evicted while in use").  -4 if the slot is not loaded. */
 tpa_status tpa_adapter_unload(tpa_layer* layer, int32_t slot, tpa_stream stream);
 
+/* The slot's metadata (Table 1; the fold rule of §3.2): method, the slots
+ * that stay live, the folds made, term kind, rank and OFT block.  Host only.
+ * -4 if the slot is not loaded (slot 0 reports the identity). */
 tpa_status tpa_adapter_info_get(const tpa_layer* layer, int32_t slot, tpa_adapter_info* out);
 
 /* Bytes of device workspace a forward of any n <= n_max rows needs under
- * the layer's current options; n_max <= 8192. */
+ * the layer's current options; n_max <= 8192.  The workspace holds the row
+ * plan (§2 "The LoRA schedule"), the rotated rows of OFT tenants (§4.1
+ * route three), the shrink's V and U between the two halves of the term
+ * (§2), and the base GEMM's split partials.  Host only. */
 tpa_status tpa_workspace_size(const tpa_layer* layer, int32_t n_max, size_t* bytes);
 
 /* out[i] = F_{slot_of_row[i]}(x[i]) for i < n (eq. (1)).
@@ -245,14 +256,22 @@ tpa_status tpa_layer_forward(tpa_layer* layer, const void* x_dev, const int32_t*
  * The tpa_plan handle is host memory (create/destroy); it holds no device
  * memory. */
 typedef struct tpa_plan tpa_plan;
-/* Layers whose signatures are equal can share a plan of the same rows. */
+/* Layers whose signatures are equal can share a plan of the same rows
+ * (§2 "The LoRA schedule"; appendix "CUDA graphs": the row mapping is built
+ * once per step for every layer). */
 tpa_status tpa_layer_plan_signature(const tpa_layer* layer, uint64_t* sig);
+/* §2 "The LoRA schedule": whether a plan's grouping serves this layer. */
 tpa_status tpa_plan_accepts(const tpa_plan* plan, const tpa_layer* layer, int32_t* ok);
+/* Host handle of a shared row plan (§2 "The LoRA schedule"). */
 tpa_status tpa_plan_create(tpa_plan** out);
-tpa_status tpa_plan_destroy(tpa_plan* plan);
+tpa_status tpa_plan_destroy(tpa_plan* plan); /* §2 "The LoRA schedule" */
+/* Device bytes of a plan of n_max rows (§2 "The LoRA schedule"). */
 tpa_status tpa_plan_size(const tpa_layer* layer, int32_t n_max, size_t* bytes);
+/* Groups the rows once per step (§2 "The LoRA schedule"; appendix "CUDA
+ * graphs"). */
 tpa_status tpa_plan_build(tpa_plan* plan, tpa_layer* layer, const int32_t* slot_of_row_dev, int32_t n,
                           void* plan_dev, size_t plan_bytes, tpa_stream stream);
+/* eq. (1) for the plan's rows, steps after the plan (§2, §4.1). */
 tpa_status tpa_layer_forward_planned(tpa_layer* layer, const tpa_plan* plan, const void* x_dev,
                                      void* out_dev, void* ws_dev, size_t ws_bytes, tpa_stream stream);
 
@@ -266,13 +285,19 @@ tpa_status tpa_layer_forward_planned(tpa_layer* layer, const tpa_plan* plan, con
  * blocks per work-group and k range), so results may differ from separate
  * forwards by the rounding of a different split-K order.  Stage events are
  * those of layers[0]. */
+/* Workspace bytes of each projection of a group (§5.2, one launch per
+ * kernel for every slice); bytes[count]. */
 tpa_status tpa_group_workspace_size(tpa_layer* const* layers, int32_t count, int32_t n_max, size_t* bytes);
+/* eq. (1) for every projection of the group, one launch per kernel (§5.2). */
 tpa_status tpa_group_forward_planned(tpa_layer* const* layers, int32_t count, const tpa_plan* plan,
                                      const void* const* x_dev, void* const* out_dev, void* const* ws_dev,
                                      const size_t* ws_bytes, tpa_stream stream);
 
-/* Read (and optionally clear) the layer's sticky invalid-slot flag.
- * Synchronizes `stream`. */
+/* Read (and optionally clear) the layer's sticky invalid-slot flag: set by
+ * any forward or plan whose slot_of_row names a slot that is out of range
+ * or not loaded (such rows are computed as the identity, never with another
+ * tenant's weights: faangrind "multi-lora-serving" page, failure mode
+ * "Wrong adapter applied").  Synchronizes `stream`. */
 tpa_status tpa_error_flag(tpa_layer* layer, int32_t* flag_host, int32_t clear, tpa_stream stream);
 
 /* The row plan a forward of these rows uses, copied to host arrays
@@ -293,8 +318,11 @@ typedef struct {
   int32_t* oft_tiles;
   int32_t* counts;
 } tpa_plan_host;
+/* Padded tile-list length and rows per tile of a plan of n rows (§2 "The
+ * LoRA schedule": one adapter per tile).  Host only. */
 tpa_status tpa_plan_max_tiles(const tpa_layer* layer, int32_t n, int32_t* max_tiles,
                               int32_t* tile_rows);
+/* Runs the plan kernel (§2 "The LoRA schedule") and copies the plan out. */
 tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int32_t n,
                           void* ws_dev, size_t ws_bytes, tpa_plan_host* out, tpa_stream stream);
 
@@ -331,8 +359,9 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          leaves at most 256 work-groups, each with a k
  *                          range of at least 1536, else 2)
  *   TPA_OPT_OVERLAP      : 1 runs the shrink and its split
- *                          reduction on a second stream of the layer
- *                          (default priority) beside OFT's rotation and
+ *                          reduction on a second stream (one per device,
+ *                          shared by every layer; default priority)
+ *                          beside OFT's rotation and
  *                          the base GEMM, forked from and joined to the
  *                          caller's stream with events, so the forward
  *                          still behaves as one ordered call on `stream`
@@ -342,12 +371,15 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          graph-replayed decode step cost more than the
  *                          launch they hide).  Never where the expand runs
  *                          in the GEMM's epilogue (that GEMM reads the
- *                          shrink's output).  The second stream and its two
- *                          events are created on the first forward that
- *                          overlaps outside graph capture; a captured
- *                          forward before then runs on `stream` alone.
- *                          Both ways give the same bits.  The group
- *                          forward uses the first layer's setting.
+ *                          shrink's output).  The second stream (once per
+ *                          device) and the layer's two events are created
+ *                          on the first forward that overlaps outside graph
+ *                          capture; a captured forward before then runs on
+ *                          `stream` alone.  Both ways give the same bits.
+ *                          Stage event 3 (after the GEMM) is recorded after
+ *                          the join, so it covers the overlapped shrink.
+ *                          The group forward uses the first layer's
+ *                          setting.
  *   TPA_OPT_WIDE_TILE    : direct-load kernel for n > 64: 256 (256 x 256
  *                          tiles, 8 waves; needs d_out % 256 == 0) or 128;
  *                          by default 256 when that gives at least 256
@@ -371,6 +403,8 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_OVERLAP 9
 #define TPA_OPT_WIDE_TILE 10
 #define TPA_OPT_FUSE_EXPAND 11
+/* Scale routes of §4.3 and the appendix "Routes"; the other keys pin the
+ * kernel configuration the appendix "Tuned kernels" would tune. */
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
 
 /* The kernel configuration a forward of n rows would use (host only, no
@@ -386,6 +420,7 @@ typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
       gemm_groups, gemm_stages, gemm_tile, fused_expand;
 } tpa_config;
+/* Appendix "Tuned kernels": the configuration in force for n rows. */
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
 
 /* Stage timing: when `events` is non-null, each forward records events[0]
@@ -395,6 +430,7 @@ tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
  * expand, and the expand (with any scale pass after it), all on its stream.
  * `events` are hipEvent_t handles owned by the caller; count must be 6 (or 0
  * with null to stop).  For profiling only. */
+/* Appendix "Kernel timing": per-kernel times of one forward. */
 tpa_status tpa_layer_set_stage_events(tpa_layer* layer, void* const* events, int32_t count);
 
 /* Events for tpa_layer_set_stage_events.  A default HIP event performs a
@@ -402,9 +438,9 @@ tpa_status tpa_layer_set_stage_events(tpa_layer* layer, void* const* events, int
  * which costs microseconds and lands inside the interval being timed; these
  * are created without it, so an event pair around one kernel measures that
  * kernel.  elapsed waits for `end` and returns milliseconds. */
-tpa_status tpa_timing_event_create(void** event);
-tpa_status tpa_timing_event_destroy(void* event);
-tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms);
+tpa_status tpa_timing_event_create(void** event);          /* appendix "Kernel timing" */
+tpa_status tpa_timing_event_destroy(void* event);          /* appendix "Kernel timing" */
+tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms); /* appendix "Kernel timing" */
 
 /* Calibration probes (appendix "Constants"): a plain device copy of `bytes`
  * (a multiple of 16, 16-byte aligned pointers) by a streaming kernel, and
@@ -413,11 +449,14 @@ tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms);
  * of the device's constant-rate clock and touches no memory: work queued
  * behind it on the stream starts back to back once it ends, so host launch
  * gaps drop out of event timings. */
-tpa_status tpa_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, tpa_stream stream);
-tpa_status tpa_probe_empty(int32_t count, tpa_stream stream);
-tpa_status tpa_probe_delay(int32_t microseconds, tpa_stream stream);
+tpa_status tpa_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, tpa_stream stream); /* β, appendix "Constants" */
+tpa_status tpa_probe_empty(int32_t count, tpa_stream stream);    /* λ, appendix "Constants" */
+tpa_status tpa_probe_delay(int32_t microseconds, tpa_stream stream); /* appendix "Kernel timing" */
 
-/* Message of the last error on this thread ("" if none). */
+/* Message of the last error on this thread ("" if none): why an adapter
+ * was refused at admission (shape, rank or value checks: faangrind
+ * "multi-lora-serving" page, failure mode "Corrupt or untrusted adapter
+ * file") or why a call failed. */
 const char* tpa_last_error(void);
 
 #ifdef __cplusplus

@@ -111,8 +111,10 @@ class BatchShape:
     q: int = 2                       # bytes per element of x, W, out, factors
     f_v: int = 4                     # bytes per element of s, b, d, e (fp32)
     owned_ranks: list = field(default_factory=list)   # rank of each distinct owned-term tenant
+    owned_ranks_stored: list = field(default_factory=list)  # the same, padded to 16 as stored
     n_owned: int = 0                 # rows with an owned term
-    v_elems: int = 0                 # Σ over owned rows of the row's (padded) rank
+    v_elems: int = 0                 # Σ over owned rows of the row's rank
+    f_uv: int = 0                    # bytes per element of V and U between shrink and expand (0: q)
     r_v: int = 0
     n_vera: int = 0
     k_vera: int = 0
@@ -134,8 +136,8 @@ def shape_of(n, d_in, d_out, slot_of_row, adapters, q=2, r_v=0):
         m = ad["method"]
         if m in ("lora", "dora"):
             r = ad["A"].shape[1]
-            r += (-r) % 16                           # stored padded to 16
             bs.owned_ranks.append(r)
+            bs.owned_ranks_stored.append(r + (-r) % 16)
             bs.n_owned += rows
             bs.v_elems += rows * r
         if m == "dora" or m == "ia3" or m == "ssf":
@@ -153,19 +155,24 @@ def shape_of(n, d_in, d_out, slot_of_row, adapters, q=2, r_v=0):
 
 
 def kernel_bytes(b):
-    """Algorithmic bytes (what each kernel must read and write) and flops."""
+    """Algorithmic bytes (what each kernel must read and write) and flops.
+
+    Factors count at their true rank (the stored copy is padded to 16 rows;
+    stored_factor_bytes gives that), and V and U once written by the shrink
+    and once read by the expand, in the layer type (as stored)."""
     sum_r = sum(b.owned_ranks)
+    fuv = b.f_uv or b.q
     out = {}
     out["oft"] = {"bytes": b.q * (2 * b.n_oft * b.d_in + b.k_oft * b.d_in * b.oft_block),
                   "flops": 2 * b.oft_block * b.n_oft * b.d_in, "launches": 1 if b.k_oft else 0}
     out["gemm"] = {"bytes": b.q * (b.n * b.d_in + b.d_in * b.d_out + b.n * b.d_out),
                    "flops": 2 * b.n * b.d_in * b.d_out, "launches": 1}
-    sh = b.q * (b.n_owned * b.d_in + sum_r * b.d_in) + 4 * b.v_elems
+    sh = b.q * (b.n_owned * b.d_in + sum_r * b.d_in) + fuv * b.v_elems
     if b.k_vera:
-        sh += b.q * (b.n_vera * b.d_in + b.r_v * b.d_in) + 4 * b.n_vera * b.r_v + b.f_v * b.k_vera * b.r_v
+        sh += b.q * (b.n_vera * b.d_in + b.r_v * b.d_in) + fuv * b.n_vera * b.r_v + b.f_v * b.k_vera * b.r_v
     out["shrink"] = {"bytes": sh, "flops": 2 * b.d_in * (b.v_elems + b.n_vera * b.r_v),
                      "launches": 1 if (b.owned_ranks or b.k_vera) else 0}
-    ex = b.q * (2 * b.n * b.d_out + sum_r * b.d_out) + 4 * (b.v_elems + b.n_vera * b.r_v)
+    ex = b.q * (2 * b.n * b.d_out + sum_r * b.d_out) + fuv * (b.v_elems + b.n_vera * b.r_v)
     ex += b.f_v * (b.k_s + b.k_b + b.k_vera) * b.d_out
     if b.k_vera:
         ex += b.q * b.r_v * b.d_out
@@ -173,6 +180,12 @@ def kernel_bytes(b):
                      "launches": 1}
     out["plan"] = {"bytes": 4 * b.n * 7, "flops": 0, "launches": 1}
     return out
+
+
+def stored_factor_bytes(b):
+    """Bytes of the owned factors as stored (rank padded to 16), read once by
+    the shrink (A') and once by the expand (B')."""
+    return b.q * sum(b.owned_ranks_stored) * (b.d_in + b.d_out)
 
 
 def adapter_path_bytes(b):

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -242,10 +243,11 @@ struct tpa_layer {
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
   int opt[12] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1, -1};
-  // Second stream (default priority) on which the shrink runs beside the
+  // Events that fork the shrink onto the device's side stream (below) from
+  // the caller's stream and join it back; made at the first forward that
+  // uses them.
   // base GEMM, and the events that fork it from and join it to the caller's
   // stream; created at the first forward that uses them.
-  hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
@@ -271,6 +273,21 @@ struct tpa_plan {
 namespace {
 
 int oft_bs_index(int bs) { return bs == 16 ? 0 : bs == 32 ? 1 : bs == 64 ? 2 : -1; }
+
+// One second stream per device (default priority) on which overlapping
+// forwards run the shrink beside the base GEMM: every layer shares it, so a
+// stack of layers does not spread over more streams than the hardware has
+// queues.  Made at the first forward that overlaps outside graph capture,
+// kept until the process ends.  Forwards on different caller streams that
+// overlap at once serialize their shrinks on it (their events keep each
+// forward ordered).
+std::mutex g_side_mu;
+std::unordered_map<int, hipStream_t> g_side;
+hipStream_t side_stream(int device) {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  auto it = g_side.find(device);
+  return it == g_side.end() ? nullptr : it->second;
+}
 
 // k range of the streamed decode GEMM for a grid of `col_tiles` column tiles
 // (summed over the projections of one launch) over d_in: the largest power
@@ -905,7 +922,6 @@ tpa_status tpa_layer_destroy(tpa_layer* L) {
   L->arena.release();
   if (L->ev_fork) (void)hipEventDestroy(L->ev_fork);
   if (L->ev_join) (void)hipEventDestroy(L->ev_join);
-  if (L->side) (void)hipStreamDestroy(L->side);
   if (L->stage) (void)hipFree(L->stage);
   if (L->status_dev) (void)hipFree(L->status_dev);
   if (L->vera_mem) (void)hipFree(L->vera_mem);
@@ -1570,7 +1586,8 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   for (int i = 0; i < count; ++i) any_fused_cfg = any_fused_cfg || sl[i].c.fused;
   const int ov_opt = L0->opt[TPA_OPT_OVERLAP];
   bool overlap = any_term_all && !any_fused_cfg && (ov_opt == 1 || (ov_opt < 0 && n > 128));
-  if (overlap && !(L0->side && L0->ev_fork && L0->ev_join)) {
+  hipStream_t side = overlap ? side_stream(L0->device) : nullptr;
+  if (overlap && !(side && L0->ev_fork && L0->ev_join)) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
       (void)hipGetLastError();
@@ -1579,17 +1596,21 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     overlap = cap == hipStreamCaptureStatusNone;
   }
   if (overlap) {
-    if (!L0->side) TPA_HIP(hipStreamCreateWithFlags(&L0->side, hipStreamNonBlocking));
+    if (!side) {
+      std::lock_guard<std::mutex> lock(g_side_mu);
+      if (!g_side[L0->device]) TPA_HIP(hipStreamCreateWithFlags(&g_side[L0->device], hipStreamNonBlocking));
+      side = g_side[L0->device];
+    }
     if (!L0->ev_fork) TPA_HIP(hipEventCreateWithFlags(&L0->ev_fork, hipEventDisableTiming));
     if (!L0->ev_join) TPA_HIP(hipEventCreateWithFlags(&L0->ev_join, hipEventDisableTiming));
     TPA_HIP(hipEventRecord(L0->ev_fork, s));
-    TPA_HIP(hipStreamWaitEvent(L0->side, L0->ev_fork, 0));
+    TPA_HIP(hipStreamWaitEvent(side, L0->ev_fork, 0));
     tpa::PreSlice ps[tpa::MAX_SLICES];
     for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr);
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, L0->side));
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, side));
     for (int i = 0; i < count; ++i)
-      if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], L0->side));
-    TPA_HIP(hipEventRecord(L0->ev_join, L0->side));
+      if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], side));
+    TPA_HIP(hipEventRecord(L0->ev_join, side));
   }
   static const int kBs[3] = {16, 32, 64};
   tpa::PreSlice ps[tpa::MAX_SLICES];
@@ -1675,6 +1696,9 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       }
     }
   }
+  // Join the side stream here, so the stage event after the GEMM also
+  // covers the shrink that ran beside it (only the expand reads V and U).
+  if (overlap) TPA_HIP(hipStreamWaitEvent(s, L0->ev_join, 0));
   if (tpa_status st = stage(L0, 3, s)) return st;
 
   // 4. Expand (with the comparison routes' separate scale passes).
@@ -1728,7 +1752,6 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     }
   }
   if (tpa_status st = stage(L0, 4, s)) return st;
-  if (overlap) TPA_HIP(hipStreamWaitEvent(s, L0->ev_join, 0));
   bool same_h = true, any_fused = false;
   for (int i = 0; i < count; ++i) {
     same_h = same_h && ((e[i].hpart != nullptr) == (e[0].hpart != nullptr));

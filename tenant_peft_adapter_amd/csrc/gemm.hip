@@ -509,10 +509,13 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
 // buffers with direct global-to-LDS loads (8 loads per wave per slice), the
 // chunks of a row permuted (c ^ swz(row)) so the fragment reads hit distinct
 // bank groups; S - 1 slices are in flight while one is multiplied.  S = 2
-// (64 KB) lets two work-groups share a CU; deeper rings (3..5 buffers, up to
-// the whole 160 KB) measured no faster even where a CU holds one
-// work-group: the slices' trip from L2 into LDS, not their latency, sets
-// the pace.  Per slice each wave waits for its own loads, then the
+// (64 KB) lets two work-groups share a CU and is the default.  Four buffers
+// (three slices in flight) are chosen for split-K grids of at most 256
+// work-groups (one per CU) whose k ranges hold at least 1536 elements: such
+// long loops read their slices from HBM rather than L2, and the deeper ring
+// covers that latency (14336 -> 4096 at 128-512 rows: 10-13% faster); where
+// two work-groups would share a CU, or the loop is short, two buffers stay
+// ahead.  Per slice each wave waits for its own loads, then the
 // work-group meets at a barrier.  Tiles are handed to work-groups so that
 // each XCD (work-group i runs on XCD i % 8) takes a contiguous run of the
 // tile order below: the slices of x and W its CUs read together stay in its

@@ -16,6 +16,45 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _check_rows(name, t, n, width, dtype, device):
+    """t must be a contiguous [n, width] tensor of `dtype` on `device`; the
+    kernels read and write exactly that many elements from its data pointer."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, the layer's weight on %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, the layer computes in %s" % (name, t.dtype, dtype))
+    if t.dim() != 2 or tuple(t.shape) != (n, width):
+        raise ValueError("%s has shape %s, expected (%d, %d)" % (name, tuple(t.shape), n, width))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_slots(slot_of_row, n, device):
+    """slot_of_row must be a contiguous int32 vector of n entries on `device`
+    (an int64 vector would be read as twice as many int32 slots)."""
+    if not isinstance(slot_of_row, torch.Tensor):
+        raise ValueError("slot_of_row must be a torch tensor")
+    if slot_of_row.device != device:
+        raise ValueError("slot_of_row is on %s, the layer's weight on %s" % (slot_of_row.device, device))
+    if slot_of_row.dtype != torch.int32:
+        raise ValueError("slot_of_row has dtype %s, expected torch.int32" % slot_of_row.dtype)
+    if slot_of_row.dim() != 1 or slot_of_row.numel() != n:
+        raise ValueError("slot_of_row has shape %s, expected (%d,)" % (tuple(slot_of_row.shape), n))
+    if not slot_of_row.is_contiguous():
+        raise ValueError("slot_of_row must be contiguous")
+
+
+def _check_ws(ws, need, device):
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("workspace of %d bytes, the forward needs %d" % (ws.numel() * ws.element_size(), need))
+    if ws.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+
+
 class AdaptedLayer:
     """One projection y = F_{slot_of_row[i]}(x[i]) over a shared weight W
     ([d_out, d_in], an nn.Linear weight on the GPU)."""
@@ -106,15 +145,34 @@ class AdaptedLayer:
             self._ws_n = self._ws_max
         return self._ws
 
+    def check_forward_args(self, x, slot_of_row=None, out=None, n=None):
+        """Raise ValueError unless x ([n, d_in]), slot_of_row (int32 [n]) and
+        out ([n, d_out]) are contiguous tensors of the layer's dtype (int32
+        for the slots) on the weight's device, and out does not alias x."""
+        if not isinstance(x, torch.Tensor) or x.dim() != 2:
+            raise ValueError("x must be a 2-D tensor [n, d_in]")
+        n = x.shape[0] if n is None else n
+        _check_rows("x", x, n, self.d_in, self.W.dtype, self.W.device)
+        if slot_of_row is not None:
+            _check_slots(slot_of_row, n, self.W.device)
+        if out is not None:
+            _check_rows("out", out, n, self.d_out, self.W.dtype, self.W.device)
+            if n > 0 and out.data_ptr() == x.data_ptr():
+                raise ValueError("out may not alias x")
+        return n
+
     def forward(self, x, slot_of_row, out=None, ws=None):
-        n = x.shape[0]
+        n = self.check_forward_args(x, slot_of_row, out)
         if out is None:
             out = torch.empty((n, self.d_out), dtype=self.W.dtype, device=self.W.device)
         if n == 0:
             return out
-        ws = self.workspace(n) if ws is None else ws
+        if ws is None:
+            ws = self.workspace(n)
+        else:
+            _check_ws(ws, B.tpa_workspace_size(self.handle, n), self.W.device)
         B.tpa_layer_forward(self.handle, x.data_ptr(), slot_of_row.data_ptr(), n, out.data_ptr(), ws.data_ptr(),
-                            ws.numel(), _stream())
+                            ws.numel() * ws.element_size(), _stream())
         return out
 
     def plan_signature(self):
@@ -125,17 +183,22 @@ class AdaptedLayer:
         """Forward of the rows of a RowPlan built by a layer with the same
         slot classes (the plan kernel is not run again)."""
         n = plan.n
+        self.check_forward_args(x, None, out, n=n)
         if out is None:
             out = torch.empty((n, self.d_out), dtype=self.W.dtype, device=self.W.device)
         if n == 0:
             return out
-        ws = self.workspace(n) if ws is None else ws
+        if ws is None:
+            ws = self.workspace(n)
+        else:
+            _check_ws(ws, B.tpa_workspace_size(self.handle, n), self.W.device)
         B.tpa_layer_forward_planned(self.handle, plan.handle, x.data_ptr(), out.data_ptr(), ws.data_ptr(),
-                                    ws.numel(), _stream())
+                                    ws.numel() * ws.element_size(), _stream())
         return out
 
     def plan(self, slot_of_row):
         n = slot_of_row.numel()
+        _check_slots(slot_of_row, n, self.W.device)
         ws = self.workspace(max(n, 1))
         return B.tpa_plan_debug(self.handle, slot_of_row.data_ptr(), n, ws.data_ptr(), ws.numel(), _stream())
 
@@ -152,13 +215,18 @@ class RowPlan:
         size = B.tpa_plan_size(layer.handle, n_max)
         self.buf = torch.empty(max(size, 256), dtype=torch.uint8, device=layer.W.device)
         self.n = 0
+        self.n_max = n_max
 
     def accepts(self, layer):
         """Whether layer may forward this plan's rows (tpa_plan_accepts)."""
         return B.tpa_plan_accepts(self.handle, layer.handle)
 
     def build(self, layer, slot_of_row):
-        self.n = slot_of_row.numel()
+        n = slot_of_row.numel() if isinstance(slot_of_row, torch.Tensor) else -1
+        _check_slots(slot_of_row, n, layer.W.device)
+        if n > self.n_max:
+            raise ValueError("plan buffer sized for %d rows, got %d" % (self.n_max, n))
+        self.n = n
         B.tpa_plan_build(self.handle, layer.handle, slot_of_row.data_ptr(), self.n, self.buf.data_ptr(),
                          self.buf.numel(), _stream())
         return self
@@ -193,6 +261,10 @@ class LayerGroup:
                        for L, sz in zip(self.layers, sizes)]
 
     def forward(self, plan, xs, outs=None):
+        if len(xs) != len(self.layers) or (outs is not None and len(outs) != len(self.layers)):
+            raise ValueError("one input (and output) per projection of the group")
+        for i, L in enumerate(self.layers):
+            L.check_forward_args(xs[i], None, None if outs is None else outs[i], n=plan.n)
         if outs is None:
             outs = [torch.empty((plan.n, L.d_out), dtype=L.W.dtype, device=L.W.device) for L in self.layers]
         B.tpa_group_forward_planned([L.handle for L in self.layers], plan.handle, [x.data_ptr() for x in xs],

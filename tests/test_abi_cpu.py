@@ -116,3 +116,99 @@ def test_plain_c_consumer_and_struct_layouts(tmp_path):
     assert cfg == ctypes.sizeof(B.tpa_config)
     assert info == ctypes.sizeof(B.tpa_adapter_info)
     assert (fold, term) == (B.FOLD_C_A, 1)
+
+
+def _fake_layer(d_in=64, d_out=128, dtype=None):
+    """An AdaptedLayer shell over a CPU weight (no library handle): enough to
+    exercise the wrapper's argument checks, which run before any C-ABI call."""
+    import torch
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    L = object.__new__(AdaptedLayer)
+    L.W = torch.zeros((d_out, d_in), dtype=dtype or torch.float16)
+    L.d_out, L.d_in = d_out, d_in
+    L.handle = None
+    return L
+
+
+def test_wrapper_accepts_well_formed_arguments():
+    import torch
+    L = _fake_layer()
+    x = torch.zeros((5, 64), dtype=torch.float16)
+    sor = torch.zeros(5, dtype=torch.int32)
+    out = torch.zeros((5, 128), dtype=torch.float16)
+    assert L.check_forward_args(x, sor, out) == 5
+    assert L.check_forward_args(x[:0], sor[:0]) == 0
+
+
+@pytest.mark.parametrize("case", ["x_narrow", "x_dtype", "x_strided", "x_1d", "sor_int64", "sor_short",
+                                  "sor_strided", "out_shape", "out_dtype", "out_alias", "x_not_tensor"])
+def test_wrapper_rejects_mismatched_tensors_before_any_launch(case):
+    """A narrower or wider x, another dtype, a non-contiguous view, int64 slot
+    ids or a wrong-size output would make the kernels read or write past the
+    tensors (or pick wrong slots): the wrapper raises ValueError first.  The
+    layer shell has no library handle, so reaching the C ABI would fail with
+    another error."""
+    import torch
+    L = _fake_layer()
+    x = torch.zeros((5, 64), dtype=torch.float16)
+    sor = torch.zeros(5, dtype=torch.int32)
+    out = torch.zeros((5, 128), dtype=torch.float16)
+    if case == "x_narrow":
+        x = torch.zeros((5, 32), dtype=torch.float16)
+    elif case == "x_dtype":
+        x = torch.zeros((5, 64), dtype=torch.float32)
+    elif case == "x_strided":
+        x = torch.zeros((5, 128), dtype=torch.float16)[:, ::2]
+    elif case == "x_1d":
+        x = torch.zeros(64, dtype=torch.float16)
+    elif case == "sor_int64":
+        sor = torch.zeros(5, dtype=torch.int64)
+    elif case == "sor_short":
+        sor = torch.zeros(4, dtype=torch.int32)
+    elif case == "sor_strided":
+        sor = torch.zeros(10, dtype=torch.int32)[::2]
+    elif case == "out_shape":
+        out = torch.zeros((5, 64), dtype=torch.float16)
+    elif case == "out_dtype":
+        out = torch.zeros((5, 128), dtype=torch.bfloat16)
+    elif case == "out_alias":
+        L = _fake_layer(d_in=128)
+        x = torch.zeros((5, 128), dtype=torch.float16)
+        out = x
+    elif case == "x_not_tensor":
+        x = [[0.0] * 64] * 5
+    with pytest.raises(ValueError):
+        L.forward(x, sor, out=out)
+
+
+def _decl_comments():
+    """(name, text) per function declared in include/tpa.h: the declaration
+    with the comment lines directly above it."""
+    import re
+    lines = open(B.HEADER).read().split("\n")
+    out = []
+    for i, l in enumerate(lines):
+        m = re.match(r"^(?:tpa_status|const char\*)\s+(tpa_\w+)\s*\(", l)
+        if not m:
+            continue
+        block = []
+        k = i
+        while True:                                   # the declaration itself
+            block.append(lines[k])
+            if lines[k].rstrip().endswith(";") or "; /*" in lines[k]:
+                break
+            k += 1
+        j = i - 1
+        while j >= 0 and re.match(r"^\s*(/\*|\*|//)", lines[j]):   # its comment
+            block.append(lines[j])
+            j -= 1
+        out.append((m.group(1), "\n".join(block)))
+    return out
+
+
+def test_every_header_declaration_cites_a_passage():
+    import re
+    decls = _decl_comments()
+    assert len(decls) == len(B.header_symbols())
+    missing = [n for n, t in decls if not re.search(r"§|Table|[Aa]ppendix|eq\. \(|\"multi-lora-serving\" page", t)]
+    assert not missing, missing

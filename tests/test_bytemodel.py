@@ -60,4 +60,14 @@ def test_kernel_bytes_counts():
     kb = bm.kernel_bytes(b)
     assert kb["gemm"]["bytes"] == 2 * (8 * 64 + 64 * 128 + 8 * 128)
     assert kb["oft"]["bytes"] == 2 * (2 * 64 + 64 * 32)
-    assert kb["shrink"]["bytes"] == 2 * (2 * 64 + 16 * 64) + 4 * 32 + 2 * (3 * 64 + 32 * 64) + 4 * 3 * 32 + 4 * 32
+    assert kb["shrink"]["bytes"] == 2 * (2 * 64 + 16 * 64) + 2 * 32 + 2 * (3 * 64 + 32 * 64) + 2 * 3 * 32 + 4 * 32
+    assert kb["expand"]["bytes"] == 2 * (2 * 8 * 128 + 16 * 128) + 2 * (32 + 3 * 32) + 4 * (1 + 1) * 128 + 2 * 32 * 128
+
+
+def test_true_rank_counts_and_stored_padding():
+    import numpy as np
+    ad = {1: {"method": "lora", "A": np.zeros((64, 8)), "B": np.zeros((8, 128)), "c": 2.0}}
+    b = bm.shape_of(4, 64, 128, [1, 1, 1, 1], ad, q=2)
+    assert b.owned_ranks == [8] and b.owned_ranks_stored == [16] and b.v_elems == 32
+    assert bm.kernel_bytes(b)["shrink"]["bytes"] == 2 * (4 * 64 + 8 * 64) + 2 * 32
+    assert bm.stored_factor_bytes(b) == 2 * 16 * (64 + 128)

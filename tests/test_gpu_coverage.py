@@ -1,0 +1,141 @@
+"""GPU tests that widen the parity cases to the sizes the workloads reach:
+
+  * the row plan, bit for bit against the oracle's canonical plan, on slot
+    tables of 1025 slots (1024 tenants and the identity: the full stack) and
+    16383 (the largest the plan's key holds), with Zipf and uniform rows, at
+    batch sizes that take the rank sort (n <= 256) and the radix sort with
+    three and four digit passes (Scute paper, §2 "The LoRA schedule":
+    rows grouped into one segment per adapter);
+  * OFT's rotation with blocks of 16, 32 and 64 (§4.1 route three), on a
+    tiny layer and on a 4096-wide one, on the decode and the prefill
+    kernels, against the oracle's direct definition y = (x R) W."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import check, make_layer, reference, run, say
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+# ------------------------------------------------------------------ plan ---
+
+# Method of slot k (k >= 1) by k mod 6; every term class and the rotation
+# flag occur across the whole slot range.
+_CYCLE = ("identity", "lora", "vera", "ia3", "oft", "dora")
+_HOLES = (7, 1000, 1024)   # unloaded again after the fill: rows naming them are invalid
+
+
+def _slot_record(rng_recs, k):
+    return rng_recs[_CYCLE[k % len(_CYCLE)]]
+
+
+@pytest.fixture(scope="module", params=[1025, 16383])
+def big_table(request):
+    """A 64 -> 128 f16 layer whose slots 1 .. max_slots-1 are all loaded
+    (method by slot, see _CYCLE), then a few unloaded again."""
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    max_slots = request.param
+    d_in, d_out = 64, 128
+    rng = np.random.default_rng(7000 + max_slots)
+    W = synth.round_to(synth._normal(rng, (d_out, d_in), 1.0 / np.sqrt(d_in)), "f16")
+    shared = synth._vera_shared(rng, d_in, d_out, 16, "f16")
+    recs = {"identity": {"method": "identity"}, "lora": synth._lora(rng, d_in, d_out, 1, "f16"),
+            "vera": synth._vera(rng, 16, d_out), "ia3": synth._ia3(rng, d_out), "oft": synth._oft(rng, d_in, 32),
+            "dora": synth._dora(rng, W, 1, "f16")}
+    L = AdaptedLayer(torch.tensor(W).half().cuda(), max_slots=max_slots, max_rank=16)
+    L.set_vera_shared(shared["A"], shared["B"])
+    say("big slot table: loading %d slots" % (max_slots - 1))
+    for k in range(1, max_slots):
+        assert L.load(_slot_record(recs, k)) == k
+    holes = [h for h in _HOLES if h < max_slots]
+    for h in holes:
+        L.unload(h)
+    cls = [-1] * max_slots
+    has_R = [0] * max_slots
+    cls[0] = 2
+    for k in range(1, max_slots):
+        m = _CYCLE[k % len(_CYCLE)]
+        cls[k] = 0 if m in ("lora", "dora") else 1 if m == "vera" else 2
+        has_R[k] = 1 if m == "oft" else 0
+    for h in holes:
+        cls[h] = -1
+        has_R[h] = 0
+    say("big slot table: %d slots loaded, holes %s" % (max_slots - 1 - len(holes), holes))
+    yield L, max_slots, cls, has_R, holes
+    L.close()
+
+
+def _rows(kind, n, max_slots, holes, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "zipf":
+        p = np.arange(1, max_slots, dtype=np.float64) ** -1.1
+        p /= p.sum()
+        sor = rng.choice(np.arange(1, max_slots), size=n, p=p)
+    else:
+        sor = rng.integers(0, max_slots, size=n)
+    sor = sor.astype(np.int32)
+    # A few invalid ids: unloaded slots, out of range on both sides.
+    if n >= 8:
+        bad = [holes[0] if holes else -1, -1, max_slots, max_slots + 5]
+        idx = rng.choice(n, size=len(bad), replace=False)
+        sor[idx] = bad
+    return sor
+
+
+@pytest.mark.parametrize("kind", ["zipf", "uniform"])
+@pytest.mark.parametrize("n", [1, 256, 257, 4096, 8192])
+def test_plan_bit_exact_large_slot_tables(big_table, kind, n):
+    L, max_slots, cls, has_R, holes = big_table
+    sor = _rows(kind, n, max_slots, holes, seed=n * 31 + max_slots)
+    say("plan max_slots=%d n=%d rows=%s distinct=%d" % (max_slots, n, kind, len(set(sor.tolist()))))
+    got = L.plan(torch.tensor(sor).cuda())
+    want = oracle.plan(sor.tolist(), cls, 16, has_R)
+    for k in ("perm", "row_slot", "seg_ptr", "seg_slot", "class_ptr", "tiles", "oft_tiles", "invalid"):
+        assert got[k] == (list(want[k]) if isinstance(want[k], list) else want[k]), k
+    if n >= 8:
+        assert got["invalid"] == 1
+
+
+def test_plan_large_table_64_row_tiles(big_table):
+    L, max_slots, cls, has_R, holes = big_table
+    L.set_option(3, 64)
+    try:
+        sor = _rows("zipf", 4096, max_slots, holes, seed=99)
+        got = L.plan(torch.tensor(sor).cuda())
+        want = oracle.plan(sor.tolist(), cls, 64, has_R)
+        for k in ("perm", "seg_ptr", "seg_slot", "class_ptr", "tiles", "oft_tiles", "invalid"):
+            assert got[k] == (list(want[k]) if isinstance(want[k], list) else want[k]), k
+    finally:
+        L.set_option(3, -1)
+
+
+# ------------------------------------------------------------ OFT blocks ---
+
+@pytest.mark.parametrize("dtype,n", [("f32", 64), ("f16", 64), ("f16", 300), ("bf16", 64)])
+def test_oft_block_sizes_tiny(dtype, n):
+    wl = synth.oft_blocks(n=n, dtype=dtype)
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=16, max_rank=16)
+    for slot, b in ((1, 16), (3, 32), (5, 64)):
+        assert L.info(slot)["oft_block"] == b
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    tol = {"f32": (1e-4, 2e-5), "f16": (0.01, 2e-3), "bf16": (0.05, 1.6e-2)}[dtype]
+    check(y_gpu, y, h, xw, mean_tol=tol[0], max_tol=tol[1], label="oft blocks %s n=%d" % (dtype, n))
+    L.close()
+
+
+@pytest.mark.parametrize("n", [64, 300])
+def test_oft_block_sizes_4096_wide(n):
+    """4096 -> 4096 f16 (a q projection's shape): the decode kernels at 64
+    rows, the prefill kernels at 300 rows."""
+    wl = synth.oft_blocks(seed=6100 + n, n=n, d_in=4096, d_out=4096, dtype="f16")
+    p = wl["projections"][0]
+    L = make_layer(p, max_slots=16, max_rank=16)
+    say("oft 4096 n=%d config %s" % (n, L.config(n)))
+    y_gpu = run(L, p["x"], wl["slot_of_row"], "f16")
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(y_gpu, y, h, xw, label="oft blocks 4096 n=%d" % n)
+    L.close()

@@ -2,7 +2,10 @@
 stack (seven Llama-3.1-8B projections, 1024 resident tenants, LoRA/DoRA at
 rank 64, VeRA r256, (IA)3, OFT b32), a Zipf(1.1) batch run as the stack
 benchmark runs it (one row plan, q/k/v and gate/up as groups), sampled rows
-of every method against the oracle row by row."""
+against the oracle row by row.  Every tenant holds values of its own
+(workloads.stack.tenant_record), and the sample takes one row from each of
+at least 64 distinct tenants, several of every method, so a row sent to
+another tenant of its own method fails the check."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +30,7 @@ def stack_layer():
         L = AdaptedLayer(W, max_slots=T + 1, max_rank=256)
         L.set_vera_shared(protos[name]["shared"]["A"], protos[name]["shared"]["B"])
         for t in range(T):
-            assert L.load(protos[name]["records"][stack.method_of(t)]) == t + 1
+            assert L.load(stack.tenant_record(protos[name], t)) == t + 1
         layers.append(L)
     yield protos, layers
     for L in layers:
@@ -49,18 +52,25 @@ def test_stack_layer_sampled_rows(stack_layer, n):
     outs += LayerGroup(layers[4:6], n).forward(plan, xs[4:6])
     outs.append(layers[6].forward_planned(plan, xs[6]))
     torch.cuda.synchronize()
-    # Two rows of two distinct tenants per method.
+    # One row of each of up to `per` distinct tenants per method: the most
+    # popular tenants first, then the rarest present, so rows of tenants far
+    # apart in slot order (and in the plan's sort) are both checked.
+    per = 14 if n >= 4096 else 3
     rows = []
     for m in stack.METHODS:
-        seen = set()
+        first = {}
         for i, s in enumerate(sor_np.tolist()):
-            if stack.method_of(s - 1) == m and s not in seen:
-                rows.append(i)
-                seen.add(s)
-            if len(seen) == 2:
-                break
+            if stack.method_of(s - 1) == m and s not in first:
+                first[s] = i
+        ids = sorted(first)
+        pick = ids if len(ids) <= per else ids[:per // 2] + ids[-(per - per // 2):]
+        rows += [first[s] for s in pick]
     rows = np.array(sorted(rows))
-    say("stack layer n=%d: %d sampled rows over %d distinct tenants" % (n, len(rows), len(set(sor_np.tolist()))))
+    tenants = sorted(set(sor_np[rows].tolist()))
+    say("stack layer n=%d: %d sampled rows of %d tenants (%d distinct in the batch)"
+        % (n, len(rows), len(tenants), len(set(sor_np.tolist()))))
+    if n >= 4096:
+        assert len(tenants) >= 64
     for (name, d_in, d_out), L, x, o in zip(shapes, layers, xs, outs):
         p = {"name": name, "d_in": d_in, "d_out": d_out, "dtype": "f16",
              "W": L.W.float().cpu().numpy(), "x": x.float().cpu().numpy(),

@@ -687,3 +687,27 @@ def test_product_methods_reduce_to_lora():
     D = eye["A"] @ eye["B"]
     blocks = np.concatenate([x[:, :4] @ D, x[:, 4:] @ D], axis=1)
     np.testing.assert_allclose(om.direct_forward(x, W, eye) - x @ W, blocks, rtol=0, atol=1e-13)
+
+
+def test_dora_magnitude_recipe_matches_the_oracle_norm():
+    """The input generator forms DoRA's magnitude by the workload recipe
+    m = ‖W + cAB‖_c · (1 + 0.1 z) (its own expansion of the norm over the
+    rank-r term, so it stays cheap at 4096 x 14336).  Replaying its seeded
+    draws, m must equal the oracle's column norm times 1 + 0.1 z: the
+    recipe is pinned to the oracle's pinned norm, and the scale the oracle
+    derives from it is exactly the drawn gain."""
+    from workloads import synth
+    for d_in, d_out, r, dt in ((64, 96, 4, "f16"), (256, 128, 8, "bf16"), (128, 64, 3, "f32")):
+        rng = np.random.default_rng(d_in + d_out)
+        W = synth.round_to(synth._normal(rng, (d_out, d_in), 1.0 / np.sqrt(d_in)), dt)
+        state = rng.bit_generator.state
+        rec = synth._dora(rng, W, r, dt)
+        rng2 = np.random.default_rng()
+        rng2.bit_generator.state = state
+        lo = synth._lora(rng2, d_in, d_out, r, dt)
+        g = 1.0 + 0.1 * rng2.standard_normal(d_out)
+        assert np.array_equal(lo["A"], rec["A"]) and np.array_equal(lo["B"], rec["B"])
+        norm = oracle.dora_column_norm(W.T.astype(np.float64), rec["A"], rec["B"], rec["c"])
+        np.testing.assert_allclose(rec["m"], norm * g, rtol=2e-7)
+        s = oracle.dora_scale(W.T.astype(np.float64), rec["A"], rec["B"], rec["c"], rec["m"])
+        np.testing.assert_allclose(s, g, rtol=2e-7)

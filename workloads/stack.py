@@ -12,10 +12,16 @@ Readings (where the workload description leaves a step open):
     LoRA, DoRA, VeRA on all seven, (IA)3 on k, v, up, OFT on q, k, v);
   * LoRA and DoRA at rank 64, VeRA's shared pair at rank 256, OFT blocks of
     32, with the value distributions of the other workloads;
-  * only the bytes a step moves matter here, so the raw parameters are drawn
-    once per (projection, method) and every tenant of that method loads its
-    own copy of them (distinct device memory, equal values); the base
-    weights and inputs are drawn per layer and projection on the device;
+  * raw parameters are drawn once per (projection, method); tenant t's own
+    record is that prototype with a factor f_t in [0.75, 1.25) of its own
+    (a golden-ratio sequence, so no two tenants share one) applied to its
+    adapter's deviation from the identity and rounded to the layer type
+    again: LoRA and DoRA A·f_t (DoRA also m·f_t), (IA)3 1 + (l − 1)·f_t,
+    VeRA 1 + (d − 1)·f_t and 1 + (e − 1)·f_t, OFT Q·f_t.  So every tenant
+    has distinct values (a row routed to another tenant of the same method
+    gives another output) while drawing 1024 full records stays cheap; the
+    base weights and inputs are drawn per layer and projection on the
+    device;
   * DoRA's magnitude is m = 1 + 0.1 z per column: with these weights the
     column norms of W + cAB are close to 1, so the scale stays near 1 ± 0.1
     without forming the norms on the host for all 32 layers.
@@ -65,9 +71,70 @@ def prototypes(seed=4000, r=64, r_v=256, dtype="f16", shapes=synth.LLAMA8B_PROJE
     return out
 
 
+def tenant_factor(t):
+    """f_t in [0.75, 1.25): 0.75 + 0.5 · frac(t · φ), distinct for every t."""
+    return 0.75 + 0.5 * ((t * 0.6180339887498949) % 1.0)
+
+
+def tenant_record(proto, t, dtype="f16"):
+    """Raw-parameter record of tenant t (0-based) for one projection: the
+    method's prototype with the tenant's factor applied (module docstring)."""
+    rec = proto["records"][method_of(t)]
+    f = np.float64(tenant_factor(t))
+    m = rec["method"]
+    if m in ("lora", "dora"):
+        out = dict(rec)
+        out["A"] = synth.round_to(rec["A"].astype(np.float64) * f, dtype)
+        if m == "dora":
+            out["m"] = (rec["m"].astype(np.float64) * f).astype(np.float32)
+        return out
+    if m == "ia3":
+        return {"method": "ia3", "l": (1.0 + (rec["l"].astype(np.float64) - 1.0) * f).astype(np.float32)}
+    if m == "vera":
+        return {"method": "vera", "c": rec["c"],
+                "d": (1.0 + (rec["d"].astype(np.float64) - 1.0) * f).astype(np.float32),
+                "e": (1.0 + (rec["e"].astype(np.float64) - 1.0) * f).astype(np.float32)}
+    if m == "oft":
+        return {"method": "oft", "block": rec["block"], "Q": (rec["Q"].astype(np.float64) * f).astype(np.float32)}
+    return rec
+
+
+class TenantRecords:
+    """slot -> raw-parameter record (slot t + 1 holds tenant t), made on
+    access: only the tenants a check touches are materialized."""
+
+    def __init__(self, proto, tenants=1024):
+        self.proto, self.tenants = proto, tenants
+        self._memo = {}
+
+    def __len__(self):
+        return self.tenants
+
+    def __contains__(self, slot):
+        return 1 <= int(slot) <= self.tenants
+
+    def __iter__(self):
+        return iter(range(1, self.tenants + 1))
+
+    def __getitem__(self, slot):
+        slot = int(slot)
+        if slot not in self:
+            raise KeyError(slot)
+        if slot not in self._memo:
+            self._memo[slot] = tenant_record(self.proto, slot - 1)
+        return self._memo[slot]
+
+    def get(self, slot, default=None):
+        return self[slot] if slot in self else default
+
+    def items(self):
+        return ((s, self[s]) for s in self)
+
+
 def adapters_of(proto, tenants=1024):
-    """slot -> raw-parameter record for one projection of the stack."""
-    return {t + 1: proto["records"][method_of(t)] for t in range(tenants)}
+    """slot -> raw-parameter record for one projection of the stack (made on
+    access)."""
+    return TenantRecords(proto, tenants)
 
 
 def device_weight(torch, layer, name, d_out, d_in, seed=4200):

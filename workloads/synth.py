@@ -184,6 +184,27 @@ def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False, d_out=None
             "slot_of_row": slot_of_row, "projections": [p]}
 
 
+def oft_blocks(seed=6000, n=64, d_in=256, d_out=256, dtype="f32", blocks=(16, 32, 64)):
+    """One layer with OFT tenants of every block size the rotation accepts
+    (appendix "Training" names 32; 16 and 64 are the other sizes a d_in that
+    is a multiple of 64 divides into), two per size, beside a LoRA r8 tenant
+    and identity rows.  Slots 1, 2: blocks[0]; 3, 4: blocks[1]; 5, 6:
+    blocks[2]; 7 LoRA; rows uniform over slots 0..7."""
+    rng = np.random.default_rng(seed)
+    p = make_projection(rng, "oft_blocks", d_in, d_out, dtype, n)
+    p["shared"] = None
+    p["adapters"] = {}
+    slot = 1
+    for b in blocks:
+        for _ in range(2):
+            p["adapters"][slot] = _oft(rng, d_in, b)
+            slot += 1
+    p["adapters"][slot] = _lora(rng, d_in, d_out, 8, dtype)
+    slot_of_row = rng.integers(0, slot + 1, size=n).astype(np.int32)
+    return {"name": "oft_blocks", "dtype": dtype, "n": n,
+            "slot_of_row": slot_of_row, "projections": [p]}
+
+
 def tiny_stacks(seed=5000, n=64, d=256, dtype="f32", r=8, r_v=32):
     """Tiny single layer with stacked adapters (several members applied in
     order at one hook) beside single ones.
