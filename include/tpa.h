@@ -232,6 +232,25 @@ tpa_status tpa_layer_forward(tpa_layer* layer, const void* x_dev, const int32_t*
                              int32_t n, void* out_dev, void* ws_dev, size_t ws_bytes,
                              tpa_stream stream);
 
+/* Bytes of scratch each GPU holds for tpa_layer_forward_noalloc. */
+#define TPA_NOALLOC_SCRATCH_BYTES (64u << 20)
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as tpa_layer_forward, same kernels and same bits, with its
+ * workspace in a scratch array the library holds, one copy per GPU, of
+ * TPA_NOALLOC_SCRATCH_BYTES, kept until the process ends.  The call
+ * allocates nothing (no hipMalloc or hipFree, no stream or event is
+ * created: the shrink runs on `stream`, never on a second stream).
+ *   x_dev, slot_of_row_dev, out_dev: as for tpa_layer_forward.
+ * Errors: as tpa_layer_forward; -6 when a forward of n rows on this layer
+ * needs more workspace than the scratch holds (tpa_workspace_size(layer, n)
+ * gives the bytes; nothing is launched then).  Every call on one GPU uses
+ * that GPU's one scratch array: calls whose work may overlap on a GPU
+ * (other streams, other threads, other layers) race and must be
+ * serialized by the caller; calls queued on one stream are ordered. */
+tpa_status tpa_layer_forward_noalloc(tpa_layer* layer, const void* x_dev, const int32_t* slot_of_row_dev,
+                                     int32_t n, void* out_dev, tpa_stream stream);
+
 /* Shared row plans.  The plan of a batch (rows grouped by term class and
  * slot, tiles, OFT tiles; §2 "The LoRA schedule") depends only on
  * slot_of_row and on each slot's term class and whether it holds an OFT

@@ -82,6 +82,7 @@ def _load():
         "tpa_adapter_info_get": [vp, i32, P(tpa_adapter_info)],
         "tpa_workspace_size": [vp, i32, P(sz)],
         "tpa_layer_forward": [vp, vp, vp, i32, vp, vp, sz, vp],
+        "tpa_layer_forward_noalloc": [vp, vp, vp, i32, vp, vp],
         "tpa_error_flag": [vp, P(i32), i32, vp],
         "tpa_plan_max_tiles": [vp, i32, P(i32), P(i32)],
         "tpa_plan_debug": [vp, vp, i32, vp, sz, P(tpa_plan_host), vp],
@@ -221,6 +222,13 @@ def tpa_workspace_size(layer, n_max):
 
 def tpa_layer_forward(layer, x_ptr, slot_of_row_ptr, n, out_ptr, ws_ptr, ws_bytes, stream=0):
     _check(_lib.tpa_layer_forward(layer, x_ptr, slot_of_row_ptr, n, out_ptr, ws_ptr, ws_bytes, stream))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TPA_NOALLOC_SCRATCH_BYTES
+
+
+def tpa_layer_forward_noalloc(layer, x_ptr, slot_of_row_ptr, n, out_ptr, stream=0):
+    _check(_lib.tpa_layer_forward_noalloc(layer, x_ptr, slot_of_row_ptr, n, out_ptr, stream))
 
 
 def tpa_layer_plan_signature(layer):

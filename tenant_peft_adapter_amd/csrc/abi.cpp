@@ -289,6 +289,34 @@ hipStream_t side_stream(int device) {
   return it == g_side.end() ? nullptr : it->second;
 }
 
+// Scratch memory of tpa_layer_forward_noalloc (for callers that cannot
+// allocate): the workspace of one forward, in a file-scope device array of
+// which each GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not a device
+// address: host code only ever passes the address hipGetSymbolAddress
+// returns for the current device (kept per device in g_scratch).
+static __device__ __align__(256) unsigned char scratch[TPA_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch;
+
+// Device address of `device`'s scratch array, looked up once per device with
+// that device current (the caller holds a DeviceGuard for it).
+tpa_status scratch_address(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch.find(device);
+  if (it != g_scratch.end()) {
+    *out = it->second;
+    return TPA_OK;
+  }
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr)
+    return fail(TPA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", device, hipGetErrorString(e));
+  g_scratch[device] = ptr;
+  *out = ptr;
+  return TPA_OK;
+}
+
 // k range of the streamed decode GEMM for a grid of `col_tiles` column tiles
 // (summed over the projections of one launch) over d_in: the largest power
 // of two with at most 16 slices of 64 per k-group and >= 192 work-groups.
@@ -911,6 +939,12 @@ tpa_status tpa_layer_create(int32_t device, int32_t d_in, int32_t d_out, int32_t
     return fail(TPA_ERR_HIP, "layer allocation: %s", hipGetErrorString(e));
   }
   update_plan_sig(L);
+  // Set-up of the no-allocation forward: this device's scratch address.
+  void* scratch_ptr = nullptr;
+  if (tpa_status st = scratch_address(device, &scratch_ptr)) {
+    tpa_layer_destroy(L);
+    return st;
+  }
   *out = L;
   return TPA_OK;
 }
@@ -1518,7 +1552,8 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
 // reduction), the expand (and any separate scale pass).  Each kernel is one
 // launch over all projections whose configurations allow it.  Stage events
 // are those of the first projection's layer.
-tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs& p, int n, hipStream_t s) {
+tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs& p, int n, hipStream_t s,
+                                    bool allow_side = true) {
   tpa_layer* L0 = sl[0].L;
   const int dtype = L0->dtype;
   const int tile_rows = sl[0].c.tile_rows;
@@ -1585,7 +1620,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   bool any_fused_cfg = false;
   for (int i = 0; i < count; ++i) any_fused_cfg = any_fused_cfg || sl[i].c.fused;
   const int ov_opt = L0->opt[TPA_OPT_OVERLAP];
-  bool overlap = any_term_all && !any_fused_cfg && (ov_opt == 1 || (ov_opt < 0 && n > 128));
+  bool overlap = allow_side && any_term_all && !any_fused_cfg && (ov_opt == 1 || (ov_opt < 0 && n > 128));
   hipStream_t side = overlap ? side_stream(L0->device) : nullptr;
   if (overlap && !(side && L0->ev_fork && L0->ev_join)) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
@@ -1775,9 +1810,9 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
 }
 
 tpa_status forward_after_plan(tpa_layer* L, const tpa::PlanArgs& p, const void* x, int n, void* out, char* w,
-                              const Layout& y, const Config& c, hipStream_t s) {
+                              const Layout& y, const Config& c, hipStream_t s, bool allow_side = true) {
   SliceCtx one{L, x, out, w, y, c};
-  return forward_group_after_plan(&one, 1, p, n, s);
+  return forward_group_after_plan(&one, 1, p, n, s, allow_side);
 }
 
 }  // namespace
@@ -1803,6 +1838,34 @@ tpa_status tpa_layer_forward(tpa_layer* L, const void* x, const int32_t* sor, in
   TPA_HIP(tpa::launch_plan(p, s));
   if (tpa_status st = stage(L, 1, s)) return st;
   return forward_after_plan(L, p, x, n, out, w, y, c, s);
+}
+
+tpa_status tpa_layer_forward_noalloc(tpa_layer* L, const void* x, const int32_t* sor, int32_t n, void* out,
+                                     tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (n < 0 || n > tpa::PLAN_MAX_ROWS) return fail(TPA_ERR_INVALID, "n=%d outside [0, %d]", n, tpa::PLAN_MAX_ROWS);
+  if (n == 0) return TPA_OK;
+  if (!x || !sor || !out) return fail(TPA_ERR_INVALID, "null pointer");
+  if (x == out) return fail(TPA_ERR_INVALID, "out may not alias x");
+  const Config c = choose_config(L, n);
+  const Layout y = make_layout(L, n, c);
+  if (y.total > (size_t)TPA_NOALLOC_SCRATCH_BYTES)
+    return fail(TPA_ERR_WORKSPACE, "a forward of %d rows on this layer needs %zu bytes of workspace, more than the "
+                "%zu bytes of scratch the no-allocation forward holds", n, y.total, (size_t)TPA_NOALLOC_SCRATCH_BYTES);
+  DeviceGuard guard(L->device);
+  void* ws = nullptr;
+  if (tpa_status st = scratch_address(L->device, &ws)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  // Nothing in the workspace needs clearing: the plan kernel writes every
+  // entry later kernels read, and the GEMM and shrink write their partials
+  // before they are summed.  The shrink stays on `stream` (no second stream
+  // or event is created), which gives the same bits as the overlapped order.
+  const tpa::PlanArgs p = plan_args(L, sor, n, w, y, c);
+  if (tpa_status st = stage(L, 0, s)) return st;
+  TPA_HIP(tpa::launch_plan(p, s));
+  if (tpa_status st = stage(L, 1, s)) return st;
+  return forward_after_plan(L, p, x, n, out, w, y, c, s, false);
 }
 
 tpa_status tpa_layer_plan_signature(const tpa_layer* L, uint64_t* sig) {

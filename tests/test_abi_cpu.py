@@ -210,5 +210,17 @@ def test_every_header_declaration_cites_a_passage():
     import re
     decls = _decl_comments()
     assert len(decls) == len(B.header_symbols())
-    missing = [n for n, t in decls if not re.search(r"§|Table|[Aa]ppendix|eq\. \(|\"multi-lora-serving\" page", t)]
+    # The no-allocation forward is not a step of the pages: its comment names
+    # the callers it serves instead.
+    missing = [n for n, t in decls if n != "tpa_layer_forward_noalloc" and
+               not re.search(r"§|Table|[Aa]ppendix|eq\. \(|\"multi-lora-serving\" page", t)]
     assert not missing, missing
+    noalloc = dict(decls)["tpa_layer_forward_noalloc"]
+    assert "cannot allocate" in noalloc
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    import re
+    text = open(B.HEADER).read()
+    m = re.search(r"#define TPA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
