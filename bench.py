@@ -12,12 +12,19 @@ accepts: here all seven), then for each projection the shrink with OFT's
 rotation, the base GEMM (carrying the shrink's split reduction) and the
 expand.  `value` is adapted-
 layer rows/s: rows through one adapted projection per second, i.e.
-7 · n / t_step.
+7 · n / t_step, with t_step the mean over exactly `--steps` graph replays
+whose buffer sets rotate (`--sets` copies of the layer's weights, inputs
+and adapters), so every step reads its weights from HBM as consecutive
+decoder layers do.  `timing` adds the appendix "Kernel timing" protocol
+(graph chains of at least 2 ms, rebuilt five times, median), cold and warm.
 
-The same run also times two other workloads of the layer (`side_targets`):
-the prefill q_proj (1024 rows in 16 segments of LoRA / DoRA r16), with its
-FLOPs over the fp16 MFMA peak, and VeRA's layer time at 1 and 1024 tenants
-(256 rows, 4096 -> 14336, shared rank 256).
+The same run also times other workloads of the layer (`side_targets`):
+the prefill q_proj (1024 rows in 16 segments of LoRA / DoRA r16) warm and
+cold, with its base GEMM against the fp16 MFMA peak; DoRA's expand against
+an equal-shape LoRA expand (§4.3 "DoRA in vLLM"); VeRA's layer time at 1
+and 1024 tenants (256 rows, 4096 -> 14336, shared rank 256); and
+(`routes_vs_byte_model`) the routes of the appendix "Routes" against the
+byte model, Table A7's medians.
 
 Prints one JSON line.  `python bench.py --gpus N` with N > 1 exits: this
 build measures one GPU.
@@ -51,9 +58,16 @@ def parse():
     ap.add_argument("--no-side-targets", action="store_true",
                     help="skip the prefill q_proj layer and the VeRA tenant sweep")
     ap.add_argument("--stage-reps", type=int, default=30)
+    ap.add_argument("--sets", type=int, default=4,
+                    help="buffer sets the timed chain rotates over (cold weights; 4 sets hold 1.8 GB of W)")
+    ap.add_argument("--routes", action="store_true",
+                    help="also measure the routes-against-the-byte-model table (off by default: its first run "
+                         "ended in a segmentation fault of this process whose cause is not yet shown)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
-    ap.add_argument("--workload", default="decoder_layer_mixed", choices=("decoder_layer_mixed", "stack"),
-                    help="stack: the 32-layer, 1024-tenant Zipf stack against the byte model")
+    ap.add_argument("--workload", default="decoder_layer_mixed",
+                    choices=("decoder_layer_mixed", "stack", "prefill_q_proj"),
+                    help="stack: the 32-layer, 1024-tenant Zipf stack against the byte model; prefill_q_proj: "
+                         "only the 1024-row q_proj layer (8 LoRA + 8 DoRA r16), for profiling")
     ap.add_argument("--layers", type=int, default=32, help="stack: decoder layers")
     ap.add_argument("--tenants", type=int, default=1024, help="stack: resident tenants")
     ap.add_argument("--stack-n", default="16,256,4096", help="stack: batch sizes")
@@ -127,9 +141,10 @@ def build_step(wl, torch):
     return layers, step, units
 
 
-def capture(step, torch):
-    step()
-    torch.cuda.synchronize()
+def capture(step, torch, warm=True):
+    if warm:
+        step()
+        torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -139,6 +154,41 @@ def capture(step, torch):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     return g
+
+
+def capture_chain(call, count, torch):
+    """One graph holding `count` calls call(0) .. call(count - 1) (each call
+    runs once eagerly first, which also warms caches and code)."""
+    for i in range(min(count, 8)):
+        call(i)
+    torch.cuda.synchronize()
+    return capture(lambda: [call(i) for i in range(count)], torch, warm=False)
+
+
+def time_chain(call, torch, min_s=2e-3, rebuilds=5):
+    """Appendix "Kernel timing": enough copies of a call chained into one
+    graph that the timed interval reaches `min_s`, divided by the copies;
+    the graph rebuilt `rebuilds` times and the median of the per-call times
+    taken.  call(i) is the i-th copy (callers rotate buffer sets with i for
+    cold measurements).  Returns (median seconds per call, samples, copies)."""
+    import statistics
+    g = capture_chain(call, 1, torch)
+    t1 = time_graph(g, 10, 2, torch)
+    del g
+    copies = max(1, int(min_s / max(t1, 1e-7)) + 1)
+    samples = []
+    for _ in range(rebuilds):
+        g = capture_chain(call, copies, torch)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e-3 / copies)
+        del g
+    return statistics.median(samples), samples, copies
 
 
 def time_graph(g, steps, warmup, torch):
@@ -208,12 +258,63 @@ def _copy_rate(torch, nbytes, reps):
     return rate
 
 
-def calibrate(torch):
+def _read_rate(torch, nbytes, reps):
+    """Bytes read per second by the library's read probe over `nbytes`."""
+    from tenant_peft_adapter_amd import binding as B
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(B.PROBE_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        B.tpa_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), st)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        B.tpa_probe_read(src.data_ptr(), nbytes, sink.data_ptr(), st)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = nbytes * reps / (e0.elapsed_time(e1) * 1e-3)
+    del src, sink
+    return rate
+
+
+def _copy_rate_graph(torch, nbytes, copies=400):
+    """Copy rate of `copies` chained copies of one small buffer pair inside a
+    graph (read + written bytes per second)."""
+    from tenant_peft_adapter_amd import binding as B
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(copies):
+                B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, s.cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * copies / (e0.elapsed_time(e1) * 1e-3)
+    del g, src, dst
+    return rate
+
+
+L2_BYTES = 8 * (4 << 20)     # MI355X: 4 MB of L2 in each of the 8 XCDs
+MALL_BYTES = 256 << 20       # Infinity Cache
+
+
+def calibrate(torch, full=False):
     """β_HBM: a 2 GiB device copy (1 GiB read + 1 GiB written, larger than the
     256 MB MALL); β_MALL: the fastest of copies of 16, 32 and 64 MB (1/16 to
     1/4 of the MALL, read and written back from it); λ: 200 chained one-block
     kernels in one graph (appendix "Constants", sizes rescaled to this
-    chip's caches).  Returns (β_HBM, λ, β_MALL)."""
+    chip's caches).  Returns (β_HBM, λ, β_MALL), or with full=True a dict
+    that also holds β_L2 (the fastest of copies of 1/16, 1/8 and 1/4 of the
+    chip's L2, each XCD's share in its own L2, chained in a graph) and the
+    read ceiling (a 1 GiB read-only stream)."""
     from tenant_peft_adapter_amd import binding as B
     beta = _copy_rate(torch, 1 << 30, 10)
     beta_mall = max(_copy_rate(torch, mb << 20, 200) for mb in (16, 32, 64))
@@ -230,7 +331,11 @@ def calibrate(torch):
         g.replay()
     torch.cuda.synchronize()
     lam = (time.perf_counter() - t0) / 20 / 200
-    return beta, lam, beta_mall
+    if not full:
+        return beta, lam, beta_mall
+    beta_l2 = max(_copy_rate_graph(torch, L2_BYTES // f) for f in (16, 8, 4))
+    read = _read_rate(torch, 1 << 30, 10)
+    return {"beta_hbm": beta, "lambda": lam, "beta_mall": beta_mall, "beta_l2": beta_l2, "read_hbm": read}
 
 
 PROFILE = os.path.join(ROOT, "profiles", "gemm_stream_decoder_layer_mixed.md")
@@ -434,46 +539,262 @@ def stack_main(args):
         "dL_launches": 0, "results": results}))
 
 
-def single_layer_time(wl, torch, reps=200, warmup=20, max_rank=256):
-    """Graph-replayed time of one forward of a single-projection workload."""
+def load_layer(p, torch, max_rank=256, options=None, copies=1):
+    """A layer (or `copies` layers, each with its own W and adapters) of a
+    single-projection workload."""
     from tenant_peft_adapter_amd.layer import AdaptedLayer
+    out = []
+    for _ in range(copies):
+        L = AdaptedLayer(torch.tensor(p["W"]).half().cuda(), max_slots=max(2, len(p["adapters"]) + 1), max_rank=max_rank)
+        for k, v in (options or {}).items():
+            L.set_option(k, v)
+        if p["shared"] is not None:
+            L.set_vera_shared(p["shared"]["A"], p["shared"]["B"])
+        for slot in sorted(p["adapters"]):
+            assert L.load(p["adapters"][slot]) == slot
+        out.append(L)
+    return out if copies > 1 else out[0]
+
+
+def layer_call(Ls, xs, sor, torch):
+    """call(i): the forward of buffer set i mod len(Ls)."""
+    n = sor.numel()
+    outs = [torch.empty((n, L.d_out), dtype=torch.float16, device="cuda") for L in Ls]
+    wss = [L.workspace(n) for L in Ls]
+
+    def call(i):
+        k = i % len(Ls)
+        Ls[k].forward(xs[k], sor, out=outs[k], ws=wss[k])
+    return call
+
+
+def single_layer_time(wl, torch, copies=1, max_rank=256, options=None):
+    """Chained-graph time of one forward of a single-projection workload;
+    with copies > 1 the chain rotates over that many layers (own W, adapters,
+    input and output: a cold measurement)."""
     p = wl["projections"][0]
-    n = wl["n"]
-    L = AdaptedLayer(torch.tensor(p["W"]).half().cuda(), max_slots=len(p["adapters"]) + 1, max_rank=max_rank)
-    if p["shared"] is not None:
-        L.set_vera_shared(p["shared"]["A"], p["shared"]["B"])
-    for slot in sorted(p["adapters"]):
-        assert L.load(p["adapters"][slot]) == slot
-    x = torch.tensor(p["x"]).half().cuda()
+    Ls = load_layer(p, torch, max_rank=max_rank, options=options, copies=copies)
+    Ls = Ls if copies > 1 else [Ls]
+    xs = [torch.tensor(p["x"]).half().cuda() for _ in Ls]
     sor = torch.tensor(wl["slot_of_row"]).cuda()
-    out = torch.empty((n, p["d_out"]), dtype=torch.float16, device="cuda")
-    ws = L.workspace(n)
-    g = capture(lambda: L.forward(x, sor, out=out, ws=ws), torch)
-    t = time_graph(g, reps, warmup, torch)
-    cfg = L.config(n)
-    del g
-    L.close()
+    t, samples, chained = time_chain(layer_call(Ls, xs, sor, torch), torch)
+    cfg = Ls[0].config(wl["n"])
+    for L in Ls:
+        L.close()
     return t, cfg
 
 
-def side_targets(torch):
+def prefill_targets(torch, cold_sets=12, stage_reps=20):
+    """The prefill q_proj workload (1024 rows in 16 segments, 8 LoRA + 8
+    DoRA r16): layer time warm and cold (the chain rotating over
+    `cold_sets` layers, > 512 MB in all), the kernel stages of the default
+    path, and the base GEMM alone (a layer without adapters, expand apart)
+    against the fp16 MFMA peak."""
+    import numpy as np
+    from tenant_peft_adapter_amd import binding as B
+    from workloads import synth
+    n = 1024
+    wl = synth.prefill_lora_dora(n=n, tenants=16)
+    p = wl["projections"][0]
+    t_warm, cfg = single_layer_time(wl, torch)
+    t_cold, _ = single_layer_time(wl, torch, copies=cold_sets)
+    L = load_layer(p, torch)
+    x = torch.tensor(p["x"]).half().cuda()
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    call = layer_call([L], [x], sor, torch)
+    st = stage_times([L], lambda: call(0), stage_reps, torch)[0]
+    L.close()
+    # Base GEMM alone: no adapters, identity rows, the expand in its own launch.
+    Lb = load_layer({**p, "adapters": {}, "shared": None}, torch, options={B.TPA_OPT_FUSE_EXPAND: 0})
+    callb = layer_call([Lb], [x], torch.zeros(n, dtype=torch.int32, device="cuda"), torch)
+    stb = stage_times([Lb], lambda: callb(0), stage_reps, torch)[0]
+    cfgb = Lb.config(n)
+    Lb.close()
+    flops = 2.0 * n * 4096 * 4096
+    t_gemm = stb[2] * 1e-6
+    kern = "gemm_%s_kernel<f16%s>" % ("big" if cfgb["gemm_tile"] == 256 else "wide",
+                                      "" if cfgb["gemm_tile"] == 256 else ",%d" % cfgb["gemm_stages"])
+    return {
+        "us_per_layer": t_warm * 1e6, "us_per_layer_cold": t_cold * 1e6, "cold_sets": cold_sets,
+        "rows_per_s": n / t_warm, "layer_flops_over_mfma_peak": flops / t_warm / MFMA_F16_PEAK,
+        "fused_expand": bool(cfg["fused_expand"]), "gemm_tile": cfg["gemm_tile"],
+        "stages_us": dict(zip(("plan", "shrink", "gemm", "reduce+fused gemm", "expand"), [round(v, 2) for v in st])),
+        "roofline_base_gemm": {"kernel": kern + " (1024 x 4096 x 4096, no adapters)", "bound": "mfma",
+                               "achieved": flops / t_gemm / 1e12, "peak": MFMA_F16_PEAK / 1e12,
+                               "unit": "TFLOP/s", "frac": flops / t_gemm / MFMA_F16_PEAK,
+                               "us_per_launch": t_gemm * 1e6,
+                               "config": "tile=%d stages=%d split=%d" % (cfgb["gemm_tile"], cfgb["gemm_stages"],
+                                                                         cfgb["gemm_split"])},
+    }
+
+
+def dora_expand_ratio(torch, ns=(1024, 4096), stage_reps=20):
+    """§4.3 "DoRA in vLLM": the expand of a DoRA batch (s inside the expand,
+    route one) against the expand of an equal-shape LoRA batch (16 segments
+    of rank 16, q_proj 4096 -> 4096), and the same DoRA batch with s
+    applied after the expand by the index-scale route (a per-row copy of s,
+    then a multiply).  Expand stages from the library's timing events; the
+    expand runs in its own launch here."""
+    from tenant_peft_adapter_amd import binding as B
+    from workloads import synth
+    out = {}
+    for n in ns:
+        t = {}
+        for methods, route in (("lora", 0), ("dora", 0), ("dora", 3)):
+            wl = synth.prefill_lora_dora(n=n, tenants=16, methods=methods)
+            p = wl["projections"][0]
+            opts = {B.TPA_OPT_FUSE_EXPAND: 0}
+            if route:
+                opts[B.TPA_OPT_SCALE_ROUTE] = route
+            L = load_layer(p, torch, options=opts)
+            call = layer_call([L], [torch.tensor(p["x"]).half().cuda()], torch.tensor(wl["slot_of_row"]).cuda(),
+                              torch)
+            t[(methods, route)] = stage_times([L], lambda: call(0), stage_reps, torch)[0][4]
+            L.close()
+        out["n%d" % n] = {"lora_expand_us": t[("lora", 0)], "dora_expand_us": t[("dora", 0)],
+                          "dora_over_lora": t[("dora", 0)] / t[("lora", 0)],
+                          "index_scale_expand_and_passes_us": t[("dora", 3)],
+                          "index_scale_over_lora": t[("dora", 3)] / t[("lora", 0)]}
+    return out
+
+
+def route_table(torch, cal, ns=(256, 1024, 4096), d_outs=(4096, 14336), oft_k=(1, 4, 16)):
+    """Appendix "Routes" and Table A7, on this chip: measured layer time of
+    each route that applies DoRA's s outside the expand (side kernel,
+    gathered scale, index scale) and of OFT's input transform, against the
+    byte model t0 + ΔQ/β + ΔL·λ (§4.3), t0 the same batch without the extra
+    pass.  β is β_L2 when the extra bytes fit the L2, β_MALL when they fit
+    the MALL, else β_HBM (§4.3: the cache's rate when the extra read and
+    write fit in it).  Cells: 16 DoRA r16 segments, d_in 4096, n rows x
+    d_out; OFT: k tenants (b = 32) over n rows, d_in 4096 and 14336.
+    Returns the cells and, per route, the median absolute error of the
+    increment and of the total over bandwidth-regime cells (ΔQ/β > λ) and of
+    the total over the launch-bound rest."""
+    import statistics
+
+    import numpy as np
+    from tenant_peft_adapter_amd import binding as B
+    from tenant_peft_adapter_amd import bytemodel as bm
+    from workloads import synth
+    lam = cal["lambda"]
+
+    def beta_for(dq):
+        if dq <= L2_BYTES:
+            return cal["beta_l2"], "l2"
+        if dq <= MALL_BYTES:
+            return cal["beta_mall"], "mall"
+        return cal["beta_hbm"], "hbm"
+
+    cells = []
+
+    def add(route, n, d, t0, t, dq, dl):
+        beta, where = beta_for(dq)
+        extra = dq / beta + dl * lam
+        inc = t - t0
+        cells.append({"route": route, "n": n, "d": d, "t0_us": round(t0 * 1e6, 2), "t_us": round(t * 1e6, 2),
+                      "pred_us": round((t0 + extra) * 1e6, 2), "beta": where, "dq_bytes": int(dq),
+                      "bandwidth_regime": dq / beta > lam,
+                      "inc_err": abs(inc - extra) / max(abs(inc), 1e-9), "total_err": abs(t - t0 - extra) / t})
+
+    names = {1: "side kernel", 2: "gathered scale", 3: "index scale"}
+    nmax = max(ns)
+    for d_out in d_outs:
+        wl = synth.prefill_lora_dora(seed=7000 + d_out, n=nmax, tenants=16, d_out=d_out, methods="dora")
+        p = wl["projections"][0]
+        La = load_layer(p, torch, options={B.TPA_OPT_FUSE_EXPAND: 0})
+        Lb = load_layer(p, torch, options={B.TPA_OPT_FUSE_EXPAND: 0, B.TPA_OPT_SCALE_ROUTE: 2})
+        x_all = torch.tensor(p["x"]).half().cuda()
+        for n in ns:
+            sor = torch.tensor(np.minimum(np.arange(n) // max(1, n // 16) + 1, 16).astype(np.int32)).cuda()
+            x = x_all[:n].contiguous()
+            t = {}
+            for route in (0, 1, 2, 3):
+                L = La if route < 2 else Lb
+                L.set_option(B.TPA_OPT_SCALE_ROUTE, route)
+                log("routes: cell d_out=%d n=%d route=%d" % (d_out, n, route))
+                t[route] = time_chain(layer_call([L], [x], sor, torch), torch)[0]
+            for route in (1, 2, 3):
+                dq, dl = bm.scale_route_extra(n, d_out, route)
+                add(names[route], n, d_out, t[0], t[route], dq, dl)
+        La.close()
+        Lb.close()
+        log("routes: d_out %d done" % d_out)
+    for d_in in (4096, 14336):
+        rng = np.random.default_rng(7100 + d_in)
+        p = synth.make_projection(rng, "oft", d_in, 4096, "f16", 1)
+        p["adapters"] = {t + 1: synth._oft(rng, d_in, 32) for t in range(max(oft_k))}
+        L = load_layer(p, torch, options={B.TPA_OPT_FUSE_EXPAND: 0})
+        x_all = torch.randn((nmax, d_in), device="cuda").half()
+        for n in ns:
+            x = x_all[:n].contiguous()
+            t0 = time_chain(layer_call([L], [x], torch.zeros(n, dtype=torch.int32, device="cuda"), torch), torch)[0]
+            for k in oft_k:
+                log("routes: OFT cell d_in=%d n=%d k=%d" % (d_in, n, k))
+                sor = torch.tensor((np.arange(n) * k // n + 1).astype(np.int32)).cuda()
+                t = time_chain(layer_call([L], [x], sor, torch), torch)[0]
+                add("OFT transform", n, d_in, t0, t, 2 * (2 * n * d_in + k * d_in * 32), 1)
+        L.close()
+        log("routes: OFT d_in %d done" % d_in)
+    summary = {}
+    for route in list(names.values()) + ["OFT transform"]:
+        bw = [c for c in cells if c["route"] == route and c["bandwidth_regime"]]
+        lb = [c for c in cells if c["route"] == route and not c["bandwidth_regime"]]
+        summary[route] = {
+            "cells": len(bw) + len(lb), "bandwidth_cells": len(bw),
+            "increment_median_err": statistics.median([c["inc_err"] for c in bw]) if bw else None,
+            "total_median_err": statistics.median([c["total_err"] for c in bw]) if bw else None,
+            "launch_median_err": statistics.median([c["total_err"] for c in lb]) if lb else None}
+    return {"summary": summary, "cells": cells}
+
+
+def side_targets(torch, args):
     """The other targets on their own workloads, in the same run: the
     prefill q_proj layer (1024 rows, 16 segments of LoRA / DoRA r16) with
-    its base GEMM's share of the fp16 MFMA peak, and VeRA's step time from 1
-    to 1024 tenants (256 rows, 4096 -> 14336, shared rank 256)."""
+    its base GEMM's share of the fp16 MFMA peak, DoRA's expand against
+    LoRA's, and VeRA's step time from 1 to 1024 tenants (256 rows, 4096 ->
+    14336, shared rank 256)."""
     from workloads import synth
-    t_pre, cfg = single_layer_time(synth.prefill_lora_dora(n=1024, tenants=16), torch)
-    flops = 2.0 * 1024 * 4096 * 4096
+    pre = prefill_targets(torch, stage_reps=args.stage_reps)
+    log("prefill q_proj: %.1f us warm, %.1f us cold" % (pre["us_per_layer"], pre["us_per_layer_cold"]))
+    dora = dora_expand_ratio(torch, stage_reps=args.stage_reps)
     vera = {}
     for T in (1, 1024):
         vera[T], _ = single_layer_time(synth.vera_sweep(d_out=14336, tenants=T), torch)
     return {
-        "prefill_q_proj_n1024": {"us_per_layer": t_pre * 1e6, "rows_per_s": 1024 / t_pre,
-                                 "layer_flops_over_mfma_peak": flops / t_pre / MFMA_F16_PEAK,
-                                 "fused_expand": bool(cfg["fused_expand"]), "gemm_tile": cfg["gemm_tile"]},
+        "prefill_q_proj_n1024": pre,
+        "dora_expand_over_lora_expand": dora,
         "vera_4096x14336_n256": {"us_T1": vera[1] * 1e6, "us_T1024": vera[1024] * 1e6,
                                  "growth": vera[1024] / vera[1] - 1.0},
     }
+
+
+def prefill_main(args):
+    """The prefill q_proj layer alone (1024 rows, 16 segments of LoRA / DoRA
+    r16, 4096 -> 4096, f16): `warmup` then `steps` graph-replayed forwards
+    with the default kernels, then the same number of forwards of the same
+    layer without adapters and with the expand in its own launch (the base
+    GEMM alone).  One JSON line with both times."""
+    import torch
+    from tenant_peft_adapter_amd import binding as B
+    from workloads import synth
+    torch.cuda.set_device(0)
+    n = 1024
+    wl = synth.prefill_lora_dora(n=n, tenants=16)
+    p = wl["projections"][0]
+    x = torch.tensor(p["x"]).half().cuda()
+    res = {"workload": "prefill_q_proj: 4096 -> 4096, n=1024 in 16 segments, 8 LoRA + 8 DoRA r16, f16"}
+    for tag, pp, rows, opts in (("mixed", p, torch.tensor(wl["slot_of_row"]).cuda(), None),
+                                ("base_gemm", {**p, "adapters": {}, "shared": None},
+                                 torch.zeros(n, dtype=torch.int32, device="cuda"), {B.TPA_OPT_FUSE_EXPAND: 0})):
+        L = load_layer(pp, torch, options=opts)
+        call = layer_call([L], [x], rows, torch)
+        g = capture(lambda: call(0), torch)
+        t = time_graph(g, args.steps, args.warmup, torch)
+        res[tag] = {"us_per_layer": t * 1e6, "config": L.config(n)}
+        del g
+        L.close()
+        log("%s: %.1f us" % (tag, t * 1e6))
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -485,6 +806,8 @@ def main():
         sys.exit(2)
     if args.workload == "stack":
         return stack_main(args)
+    if args.workload == "prefill_q_proj":
+        return prefill_main(args)
     import numpy as np
     import torch
     from tenant_peft_adapter_amd import bytemodel as bm
@@ -494,12 +817,30 @@ def main():
     log("generating the mixed decoder-layer workload")
     wl = synth.decoder_layer_mixed()
     n = wl["n"]
-    log("loading 20 tenants into 7 projections")
-    layers, step, units = build_step(wl, torch)
-    g = capture(step, torch)
+    log("loading 20 tenants into 7 projections, %d buffer sets" % args.sets)
+    sets = [build_step(wl, torch) for _ in range(args.sets)]
+    layers, step, units = sets[0]
+    # Warm-up steps, then the driver's timed region: exactly `steps` steps of
+    # the captured graph, the chain rotating over the buffer sets (every
+    # step reads W from HBM, as consecutive decoder layers do).
+    chain = [st for _, st, _ in sets]
+    graphs = [capture(c, torch) for c in chain]
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
     log("timing %d graph-replayed steps" % args.steps)
-    t_step = time_graph(g, args.steps, args.warmup, torch)
-    log("%.1f us per step" % (t_step * 1e6))
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    del graphs
+    log("%.1f us per step (driver region)" % (t_step * 1e6))
+    # Appendix "Kernel timing": chains of >= 2 ms, five rebuilds, median;
+    # cold (rotating the buffer sets) and warm (one set).
+    t_cold, cold_samples, cold_copies = time_chain(lambda i: chain[i % len(chain)](), torch)
+    t_warm, warm_samples, warm_copies = time_chain(lambda i: step(), torch)
+    log("%.1f us per step cold, %.1f warm (chained graphs)" % (t_cold * 1e6, t_warm * 1e6))
 
     # Eager (no graph) for reference.
     for _ in range(3):
@@ -514,7 +855,8 @@ def main():
     log("per-stage event timing")
     stages = stage_times([layers[m[0]] for m in units], step, args.stage_reps, torch)
     log("calibration")
-    beta, lam, beta_mall = calibrate(torch)
+    cal = calibrate(torch, full=True)
+    beta, lam, beta_mall = cal["beta_hbm"], cal["lambda"], cal["beta_mall"]
 
     # Byte model per projection; measured times per launch unit (a fused
     # group or a single projection), each kernel one launch per unit.
@@ -550,26 +892,33 @@ def main():
     adapter_launches = len(step.plans) + 2 * len(units)
     predicted = bm.predict_time(gemm_time_all, adapter_bytes, adapter_launches, beta, lam)
 
-    ratio = None
+    ratio = t_pure = None
     if not args.no_pure_lora:
         log("pure-LoRA batch")
         wl_pure = synth.decoder_layer_mixed(pure_lora=True)
-        for L in layers:
-            L.close()
-        del g
+        for ls, _, _ in sets:
+            for L in ls:
+                L.close()
+        sets = chain = None
         torch.cuda.empty_cache()
-        layers_p, step_p, _ = build_step(wl_pure, torch)
-        gp = capture(step_p, torch)
-        t_pure = time_graph(gp, args.steps, args.warmup, torch)
-        ratio = t_step / t_pure
-        for L in layers_p:
-            L.close()
-        del gp
+        sets_p = [build_step(wl_pure, torch) for _ in range(args.sets)]
+        chain_p = [st for _, st, _ in sets_p]
+        t_pure = time_chain(lambda i: chain_p[i % len(chain_p)](), torch)[0]
+        ratio = t_cold / t_pure
+        for ls, _, _ in sets_p:
+            for L in ls:
+                L.close()
+        sets_p = chain_p = None
+        torch.cuda.empty_cache()
 
     side = None
     if not args.no_side_targets:
-        log("prefill and VeRA-sweep layers")
-        side = side_targets(torch)
+        log("prefill, DoRA-expand and VeRA-sweep layers")
+        side = side_targets(torch, args)
+    routes = None
+    if args.routes:
+        log("routes against the byte model")
+        routes = route_table(torch, cal)
 
     out = {
         "metric": METRIC,
@@ -590,13 +939,21 @@ def main():
                    "n": n, "projections": names, "graph": True},
         "us_per_adapted_layer": t_step * 1e6 / 7,
         "decoder_layer_rows_per_s": n / t_step,
+        "timing": {"driver_region_us_per_step": t_step * 1e6, "buffer_sets": args.sets,
+                   "cold_us_per_step": t_cold * 1e6, "cold_samples_us": [round(v * 1e6, 2) for v in cold_samples],
+                   "warm_us_per_step": t_warm * 1e6, "warm_samples_us": [round(v * 1e6, 2) for v in warm_samples],
+                   "steps_per_chain": [cold_copies, warm_copies],
+                   "protocol": "graph chains of >= 2 ms, 5 rebuilds, median; cold rotates %d buffer sets "
+                               "(%.0f MB of weights)" % (args.sets, args.sets * gemm_bytes_all / 1e6)},
         "eager_ms_per_step": t_eager * 1e3,
         "mixed_over_pure_lora": ratio,
+        "pure_lora_us_per_step_cold": None if t_pure is None else t_pure * 1e6,
         "roofline": {
             "kernel": "%s (base GEMM of %s in one launch)" % (dom_name, ", ".join(names[i] for i in units[du])),
             "bound": "hbm", "achieved": dom_bytes / dom_time / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
             "frac": dom_bytes / dom_time / HBM_PEAK, "traffic": profiled_traffic(dom_name, dom_cfg),
             "frac_of_copy_rate": dom_bytes / dom_time / beta,
+            "frac_of_read_rate": dom_bytes / dom_time / cal["read_hbm"],
             "bytes_per_launch": dom_bytes, "us_per_launch": dom_time * 1e6,
             "us_event_pair_cost": pair_cost * 1e6, "config": dom_cfg,
         },
@@ -606,8 +963,10 @@ def main():
                          "GBps": adapter_bytes / adapter_time / 1e9, "launches": adapter_launches,
                          "predicted_step_us": predicted * 1e6},
         "calibration": {"beta_hbm_GBps": beta / 1e9, "beta_mall_GBps": beta_mall / 1e9,
+                        "beta_l2_GBps": cal["beta_l2"] / 1e9, "read_hbm_GBps": cal["read_hbm"] / 1e9,
                         "lambda_us": lam * 1e6},
         "side_targets": side,
+        "routes_vs_byte_model": routes,
         "stages_us_raw_events": {nm: dict(zip(("plan", "shrink+oft", "gemm+reduce", "pre-expand", "expand"),
                                               [round(v, 2) for v in st]))
                                  for nm, st in zip(unit_names, stages)},

@@ -469,6 +469,12 @@ tpa_status tpa_timing_event_elapsed(void* start, void* end, float* ms); /* appen
  * behind it on the stream starts back to back once it ends, so host launch
  * gaps drop out of event timings. */
 tpa_status tpa_probe_copy(void* dst_dev, const void* src_dev, size_t bytes, tpa_stream stream); /* β, appendix "Constants" */
+/* Read ceiling beside β (appendix "Constants" measures copies; a kernel
+ * that mostly reads, like the decode GEMM streaming W, is also set against
+ * a plain read): streams `bytes` (a multiple of 16, 16-byte aligned) from
+ * src_dev and writes one 4-byte word per work-group to sink_dev, which
+ * must hold 8192 words. */
+tpa_status tpa_probe_read(const void* src_dev, size_t bytes, void* sink_dev, tpa_stream stream);
 tpa_status tpa_probe_empty(int32_t count, tpa_stream stream);    /* λ, appendix "Constants" */
 tpa_status tpa_probe_delay(int32_t microseconds, tpa_stream stream); /* appendix "Kernel timing" */
 

@@ -102,6 +102,7 @@ def _load():
         "tpa_timing_event_destroy": [vp],
         "tpa_timing_event_elapsed": [vp, vp, P(ctypes.c_float)],
         "tpa_probe_copy": [vp, vp, sz, vp],
+        "tpa_probe_read": [vp, sz, vp, vp],
         "tpa_probe_empty": [i32, vp],
         "tpa_probe_delay": [i32, vp],
     }
@@ -348,6 +349,13 @@ def tpa_timing_event_elapsed(start, end):
 
 def tpa_probe_copy(dst_ptr, src_ptr, nbytes, stream=0):
     _check(_lib.tpa_probe_copy(dst_ptr, src_ptr, nbytes, stream))
+
+
+PROBE_READ_SINK_WORDS = 8192
+
+
+def tpa_probe_read(src_ptr, nbytes, sink_ptr, stream=0):
+    _check(_lib.tpa_probe_read(src_ptr, nbytes, sink_ptr, stream))
 
 
 def tpa_probe_empty(count, stream=0):

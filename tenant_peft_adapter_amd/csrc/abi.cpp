@@ -2144,6 +2144,13 @@ tpa_status tpa_probe_copy(void* dst, const void* src, size_t bytes, tpa_stream s
   return TPA_OK;
 }
 
+tpa_status tpa_probe_read(const void* src, size_t bytes, void* sink, tpa_stream stream) {
+  if (!src || !sink || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(TPA_ERR_INVALID, "read probe needs a 16-byte aligned source, a multiple of 16 bytes and a sink");
+  TPA_HIP(tpa::launch_read(src, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)));
+  return TPA_OK;
+}
+
 tpa_status tpa_probe_empty(int32_t count, tpa_stream stream) {
   if (count < 0) return fail(TPA_ERR_INVALID, "negative count");
   TPA_HIP(tpa::launch_empty(count, static_cast<hipStream_t>(stream)));

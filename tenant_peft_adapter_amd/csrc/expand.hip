@@ -129,6 +129,15 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
     else
       load_run16<T>(out + (size_t)row[m] * a.d_out + col, v[m]);
   }
+  // The rows' s values load now, beside h, so they arrive while the term is
+  // computed rather than after it (a tenant with a live s then costs about
+  // what one without does); b and e, rarer, load in the epilogue.
+  f32x4 s4[MB][4];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s4[m][q] = (row[m] >= 0 && sp[m]) ? gload<f32x4>(sp[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
 
   int K = 0;
   const T* Bt = nullptr;
@@ -184,14 +193,13 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   }
 
   // Epilogue: lane holds 16 consecutive columns of one row of the tile.
-  // The s, b and e values of all rows are loaded together, then combined.
+  // h ⊙ s + b, plus the term (times e for a shared-term row).
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     if (row[m] < 0) continue;
-    f32x4 s4[4], b4[4], e4[4];
+    f32x4 b4[4], e4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      s4[q] = sp[m] ? gload<f32x4>(sp[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
       b4[q] = bq[m] ? gload<f32x4>(bq[m] + col + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
       e4[q] = ep[m] ? gload<f32x4>(ep[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
     }
@@ -199,7 +207,7 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float h = v[m][4 * q + j] * s4[q][j] + b4[q][j];
+        float h = v[m][4 * q + j] * s4[m][q][j] + b4[q][j];
         if (K > 0) h += acc[q][m][j] * e4[q][j];
         v[m][4 * q + j] = h;
       }
@@ -207,7 +215,8 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   }
 }
 
-// Separate scale passes (route comparison).  One thread per 16 columns.
+// Separate scale passes (route comparison).  One thread per 16 columns;
+// every vector moves in 16-byte loads and stores.
 template <typename T>
 __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mode) {
   const size_t idx = (size_t)blockIdx.x * THREADS + threadIdx.x;
@@ -216,12 +225,17 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
   const int row = (int)(idx / runs);
   const int col = 16 * (int)(idx % runs);
   const SlotDev& sd = a.slots[a.row_slot[row]];
+  const float* sv = gload<const float*>(&sd.s);
+  const float* bv = gload<const float*>(&sd.b);
   T* y = static_cast<T*>(a.y) + (size_t)row * a.d_out + col;
-  float v[16];
+  float v[16], f[16];
   if (mode == 3) {  // index scale, step one: a per-row copy of the scale
-    float* sr = a.srow + (size_t)row * a.d_out + col;
+    if (sv)
+      load_run16<float>(sv + col, f);
+    else
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sr[j] = sd.s ? sd.s[col + j] : 1.f;
+      for (int j = 0; j < 16; ++j) f[j] = 1.f;
+    store_run16<float>(a.srow + (size_t)row * a.d_out + col, f);
     return;
   }
   if (mode == 1 && a.hpart)
@@ -229,16 +243,18 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
   else
     load_run16<T>(y, v);
   if (mode == 4) {  // index scale, step two: multiply by the per-row copy
-    const float* sr = a.srow + (size_t)row * a.d_out + col;
+    load_run16<float>(a.srow + (size_t)row * a.d_out + col, f);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] *= sr[j];
-  } else if (sd.s) {
+    for (int j = 0; j < 16; ++j) v[j] *= f[j];
+  } else if (sv) {
+    load_run16<float>(sv + col, f);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] *= sd.s[col + j];
+    for (int j = 0; j < 16; ++j) v[j] *= f[j];
   }
-  if (sd.b) {
+  if (bv) {
+    load_run16<float>(bv + col, f);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] += sd.b[col + j];
+    for (int j = 0; j < 16; ++j) v[j] += f[j];
   }
   store_run16<T>(y, v);
 }

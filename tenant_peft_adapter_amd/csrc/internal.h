@@ -245,6 +245,10 @@ hipError_t launch_pack_transpose(int dtype, const float* src, int rows, int cols
 
 // -------------------------------------------------------------- probes ----
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+// Read-only probe: one 4-byte word per work-group (at most
+// PROBE_READ_BLOCKS) goes to sink.
+constexpr int PROBE_READ_BLOCKS = 8192;
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_empty(int count, hipStream_t stream);
 hipError_t launch_delay(int microseconds, hipStream_t stream);
 

@@ -78,6 +78,32 @@ __global__ __launch_bounds__(THREADS) void copy_kernel(uint4* dst, const uint4* 
     dst[i] = src[i];
 }
 
+// Read-only streaming probe: each thread folds its 16-byte loads (four in
+// flight per iteration) into one word; one word per work-group is written,
+// so the kernel's traffic is the read.
+__global__ __launch_bounds__(THREADS) void read_kernel(const uint4* src, size_t n16, uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * THREADS;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * THREADS + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  __shared__ uint32_t red[THREADS / 64];
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < THREADS / 64; ++w) t ^= red[w];
+    sink[blockIdx.x] = t;
+  }
+}
+
 __global__ void empty_kernel() {}
 
 // One wave that idles for `ticks` of the constant-rate device clock; the
@@ -151,6 +177,15 @@ hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) 
   if (g > 8192) g = 8192;
   if (g == 0) g = 1;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)g), dim3(THREADS), 0, s, (uint4*)dst, (const uint4*)src, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  size_t g = (n16 + THREADS * 4 - 1) / (THREADS * 4);
+  if (g > PROBE_READ_BLOCKS) g = PROBE_READ_BLOCKS;
+  if (g == 0) g = 1;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)g), dim3(THREADS), 0, s, (const uint4*)src, n16, sink);
   return hipGetLastError();
 }
 

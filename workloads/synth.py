@@ -244,17 +244,20 @@ def tiny_stacks(seed=5000, n=64, d=256, dtype="f32", r=8, r_v=32):
             "slot_of_row": slot_of_row, "projections": [p]}
 
 
-def prefill_lora_dora(seed=1000, n=1024, d=4096, r=16, dtype="f16", tenants=16):
-    """q_proj 4096 -> 4096, n prefill rows in `tenants` contiguous segments
-    of n / tenants rows; even segments LoRA, odd segments DoRA, rank r."""
+def prefill_lora_dora(seed=1000, n=1024, d=4096, r=16, dtype="f16", tenants=16, d_out=None, methods="mixed"):
+    """q_proj 4096 -> 4096 (d_out x d when d_out is given), n prefill rows in
+    `tenants` contiguous segments of n / tenants rows; even segments LoRA,
+    odd segments DoRA, rank r (methods "lora" or "dora": every segment)."""
     rng = np.random.default_rng(seed)
-    p = make_projection(rng, "q", d, d, dtype, n)
+    do = d if d_out is None else d_out
+    p = make_projection(rng, "q", d, do, dtype, n)
     stats = _BaseStats(p["W"])
     for t in range(tenants):
-        p["adapters"][t + 1] = (_lora(rng, d, d, r, dtype) if t % 2 == 0
-                                else _dora(rng, p["W"], r, dtype, stats=stats))
-    seg = n // tenants
-    slot_of_row = (np.arange(n) // seg + 1).astype(np.int32)
+        dora = methods == "dora" or (methods == "mixed" and t % 2 == 1)
+        p["adapters"][t + 1] = (_dora(rng, p["W"], r, dtype, stats=stats) if dora
+                                else _lora(rng, d, do, r, dtype))
+    seg = max(1, n // tenants)
+    slot_of_row = np.minimum(np.arange(n) // seg + 1, tenants).astype(np.int32)
     return {"name": "prefill_lora_dora", "dtype": dtype, "n": n,
             "slot_of_row": slot_of_row, "projections": [p]}
 
