@@ -82,15 +82,23 @@ def build_step(wl, torch):
     n = wl["n"]
     sor = torch.tensor(wl["slot_of_row"]).cuda()
     layers, xs, outs, wss = [], [], [], []
+    by_name, x_dev = {}, {}
     for p in wl["projections"]:
         W = torch.tensor(p["W"]).half().cuda()
         L = AdaptedLayer(W, max_slots=32, max_rank=256)
         if p["shared"] is not None:
-            L.set_vera_shared(p["shared"]["A"], p["shared"]["B"])
+            if p["shared"].get("a_from") in by_name:   # VeRA's A stored once per fused input
+                L.set_vera_shared_from(by_name[p["shared"]["a_from"]], p["shared"]["B"])
+            else:
+                L.set_vera_shared(p["shared"]["A"], p["shared"]["B"])
         for slot in sorted(p["adapters"]):
             assert L.load(p["adapters"][slot]) == slot
         layers.append(L)
-        xs.append(torch.tensor(p["x"]).half().cuda())
+        by_name[p["name"]] = L
+        # Projections of one fused input read the same device rows.
+        if id(p["x"]) not in x_dev:
+            x_dev[id(p["x"])] = torch.tensor(p["x"]).half().cuda()
+        xs.append(x_dev[id(p["x"])])
         outs.append(torch.empty((n, p["d_out"]), dtype=torch.float16, device="cuda"))
         wss.append(L.workspace(n))
 
@@ -862,7 +870,8 @@ def main():
     # group or a single projection), each kernel one launch per unit.
     names = [p["name"] for p in wl["projections"]]
     unit_names = ["+".join(names[i] for i in m) for m in units]
-    shapes = [bm.shape_of(n, p["d_in"], p["d_out"], wl["slot_of_row"], p["adapters"], q=2, r_v=256)
+    shapes = [bm.shape_of(n, p["d_in"], p["d_out"], wl["slot_of_row"], p["adapters"], q=2, r_v=256,
+                          vera_a_read=not (p["shared"] or {}).get("a_from"))
               for p in wl["projections"]]
     kb = [bm.kernel_bytes(s) for s in shapes]
     # Kernel times are the raw event intervals, which agree with rocprofv3's

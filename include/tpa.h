@@ -165,6 +165,17 @@ tpa_status tpa_layer_destroy(tpa_layer* layer);
 tpa_status tpa_vera_shared_set(tpa_layer* layer, int32_t r_v, const float* A, const float* B,
                                tpa_stream stream);
 
+/* VeRA's A read once per fused input (Table 2's route-two count; appendix
+ * "Byte counts": the shared A once per input a fused layer reads, B once
+ * per slice): `layer` takes `from`'s stored A_v (the same device copy, held
+ * until both layers drop it; r_v from `from`) and its own B [r_v][d_out]
+ * (float32 host).  `from` must have a VeRA pair and the same device, dtype
+ * and d_in.  A group forward (tpa_group_forward_planned) whose projections
+ * hold one A_v and read one input pointer computes x·A_vᵀ once for all of
+ * them; each applies its own d' and B_v.  Same rules as
+ * tpa_vera_shared_set otherwise (no VeRA slot loaded; synchronizes). */
+tpa_status tpa_vera_shared_set_from(tpa_layer* layer, tpa_layer* from, const float* B, tpa_stream stream);
+
 /* Admit one adapter (§5.1): validate, convert to normal form and fold what
  * the fold rule allows, upload to the device, and return its slot (the
  * lowest free slot >= 1).  Runs on `stream` and synchronizes it before
@@ -378,27 +389,23 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          leaves at most 256 work-groups, each with a k
  *                          range of at least 1536, else 2)
  *   TPA_OPT_OVERLAP      : 1 runs the shrink and its split
- *                          reduction on a second stream (one per device,
- *                          shared by every layer; default priority)
- *                          beside OFT's rotation and
+ *                          reduction on a second stream of the layer
+ *                          (default priority) beside OFT's rotation and
  *                          the base GEMM, forked from and joined to the
  *                          caller's stream with events, so the forward
  *                          still behaves as one ordered call on `stream`
- *                          (and is captured whole into a HIP graph); 0 runs
- *                          every step on `stream`; the automatic choice
- *                          overlaps above 128 rows only (the fork and join of a
- *                          graph-replayed decode step cost more than the
- *                          launch they hide).  Never where the expand runs
- *                          in the GEMM's epilogue (that GEMM reads the
- *                          shrink's output).  The second stream (once per
- *                          device) and the layer's two events are created
- *                          on the first forward that overlaps outside graph
- *                          capture; a captured forward before then runs on
- *                          `stream` alone.  Both ways give the same bits.
- *                          Stage event 3 (after the GEMM) is recorded after
- *                          the join, so it covers the overlapped shrink.
- *                          The group forward uses the first layer's
- *                          setting.
+ *                          (and is captured whole into a HIP graph); 0 or
+ *                          < 0 (the default) runs every step on `stream`.
+ *                          Never where the expand runs in the GEMM's
+ *                          epilogue (that GEMM reads the shrink's output).
+ *                          The second stream and its two events are
+ *                          created on the first forward that overlaps
+ *                          outside graph capture; a captured forward
+ *                          before then runs on `stream` alone.  Both ways
+ *                          give the same bits.  Stage event 3 (after the
+ *                          GEMM) is recorded after the join, so it covers
+ *                          the overlapped shrink.  The group forward uses
+ *                          the first layer's setting.
  *   TPA_OPT_WIDE_TILE    : direct-load kernel for n > 64: 256 (256 x 256
  *                          tiles, 8 waves; needs d_out % 256 == 0) or 128;
  *                          by default 256 when that gives at least 256

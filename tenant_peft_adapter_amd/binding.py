@@ -76,6 +76,7 @@ def _load():
         "tpa_layer_create": [i32, i32, i32, i32, vp, i32, i32, P(vp)],
         "tpa_layer_destroy": [vp],
         "tpa_vera_shared_set": [vp, i32, vp, vp, vp],
+        "tpa_vera_shared_set_from": [vp, vp, vp, vp],
         "tpa_adapter_load": [vp, P(tpa_adapter_desc), P(i32), vp],
         "tpa_adapter_load_stack": [vp, P(tpa_adapter_desc), i32, P(i32), vp],
         "tpa_adapter_unload": [vp, i32, vp],
@@ -172,6 +173,11 @@ def tpa_layer_destroy(layer):
 def tpa_vera_shared_set(layer, r_v, A, B, stream=0):
     A, B = _f32(A), _f32(B)
     _check(_lib.tpa_vera_shared_set(layer, r_v, _ptr(A), _ptr(B), stream))
+
+
+def tpa_vera_shared_set_from(layer, from_layer, B, stream=0):
+    B = _f32(B)
+    _check(_lib.tpa_vera_shared_set_from(layer, from_layer, _ptr(B), stream))
 
 
 def _desc(method, rank=0, oft_block=0, c=1.0, A=None, B=None, m=None, l=None, d=None, e=None, Q=None, s=None,

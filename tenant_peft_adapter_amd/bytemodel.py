@@ -123,14 +123,18 @@ class BatchShape:
     n_oft: int = 0
     k_oft: int = 0
     oft_block: int = 32
+    vera_a_read: bool = True         # False: another projection of the fused input reads A_v
 
 
-def shape_of(n, d_in, d_out, slot_of_row, adapters, q=2, r_v=0):
-    """BatchShape from per-row slots and raw adapter records."""
+def shape_of(n, d_in, d_out, slot_of_row, adapters, q=2, r_v=0, vera_a_read=True):
+    """BatchShape from per-row slots and raw adapter records.  vera_a_read
+    False: the projection shares its input and VeRA's A with an earlier one
+    of its fused layer, which reads A_v and computes x·A_vᵀ for both
+    (appendix "Byte counts")."""
     present = {}
     for s in slot_of_row:
         present[int(s)] = present.get(int(s), 0) + 1
-    bs = BatchShape(n=n, d_in=d_in, d_out=d_out, q=q, r_v=r_v)
+    bs = BatchShape(n=n, d_in=d_in, d_out=d_out, q=q, r_v=r_v, vera_a_read=vera_a_read)
     for s, rows in present.items():
         ad = adapters.get(s, {"method": "identity"})
         m = ad["method"]
@@ -169,7 +173,11 @@ def kernel_bytes(b):
                    "flops": 2 * b.n * b.d_in * b.d_out, "launches": 1}
     sh = b.q * (b.n_owned * b.d_in + sum_r * b.d_in) + fuv * b.v_elems
     if b.k_vera:
-        sh += b.q * (b.n_vera * b.d_in + b.r_v * b.d_in) + fuv * b.n_vera * b.r_v + b.f_v * b.k_vera * b.r_v
+        if b.vera_a_read:
+            sh += b.q * (b.n_vera * b.d_in + b.r_v * b.d_in)
+        else:                        # reads the fused input's x·A_v instead of x and A_v
+            sh += fuv * b.n_vera * b.r_v
+        sh += fuv * b.n_vera * b.r_v + b.f_v * b.k_vera * b.r_v
     out["shrink"] = {"bytes": sh, "flops": 2 * b.d_in * (b.v_elems + b.n_vera * b.r_v),
                      "launches": 1 if (b.owned_ranks or b.k_vera) else 0}
     ex = b.q * (2 * b.n * b.d_out + sum_r * b.d_out) + fuv * (b.v_elems + b.n_vera * b.r_v)

@@ -214,6 +214,15 @@ bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2;
 // write h into out (in the layer type) when they do not split k.
 bool h_partials(const Config& c) { return c.gemm_path == 0 || c.gemm_split > 1 || c.h_fp32; }
 
+// VeRA's shared A_v on the device ([r_v][d_in] in the layer type), held by
+// every layer that reads it (one per fused input group: q, k and v share
+// one; gate and up another) and freed with its last holder.
+struct VeraA {
+  void* mem = nullptr;
+  int device = 0, dtype = 0, d_in = 0, r_v = 0;
+  int refs = 0;
+};
+
 struct Layout {
   size_t perm, pinfo, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
   size_t plan_end;  // the plan arrays come first; a shared plan buffer holds [0, plan_end)
@@ -235,6 +244,9 @@ struct tpa_layer {
   std::vector<SlotDev> slots_host;
   std::vector<HostSlot> hs;
   int32_t* flag_dev = nullptr;
+  // VeRA's pair: A_v in a block that layers reading the same input may
+  // share (reference-counted, freed with its last holder), B_v in vera_mem.
+  VeraA* vera_a = nullptr;
   void* vera_mem = nullptr;
   const void* vera_At = nullptr;
   const void* vera_Bt = nullptr;
@@ -243,11 +255,11 @@ struct tpa_layer {
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
   int opt[12] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1, -1};
-  // Events that fork the shrink onto the device's side stream (below) from
-  // the caller's stream and join it back; made at the first forward that
+  // Second stream (default priority) on which the shrink runs beside the
+  // base GEMM when overlap is asked for, and the events that fork it from
+  // and join it to the caller's stream; created at the first forward that
   // uses them.
-  // base GEMM, and the events that fork it from and join it to the caller's
-  // stream; created at the first forward that uses them.
+  hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   hipEvent_t stage_ev[6] = {};
   bool stage_on = false;
@@ -274,20 +286,18 @@ namespace {
 
 int oft_bs_index(int bs) { return bs == 16 ? 0 : bs == 32 ? 1 : bs == 64 ? 2 : -1; }
 
-// One second stream per device (default priority) on which overlapping
-// forwards run the shrink beside the base GEMM: every layer shares it, so a
-// stack of layers does not spread over more streams than the hardware has
-// queues.  Made at the first forward that overlaps outside graph capture,
-// kept until the process ends.  Forwards on different caller streams that
-// overlap at once serialize their shrinks on it (their events keep each
-// forward ordered).
-std::mutex g_side_mu;
-std::unordered_map<int, hipStream_t> g_side;
-hipStream_t side_stream(int device) {
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  auto it = g_side.find(device);
-  return it == g_side.end() ? nullptr : it->second;
+// Drops the layer's hold on its VeRA A (freeing it with the last holder).
+void release_vera_a(tpa_layer* L) {
+  if (!L->vera_a) return;
+  if (--L->vera_a->refs == 0) {
+    DeviceGuard guard(L->vera_a->device);
+    (void)hipFree(L->vera_a->mem);
+    delete L->vera_a;
+  }
+  L->vera_a = nullptr;
+  L->vera_At = nullptr;
 }
+
 
 // Scratch memory of tpa_layer_forward_noalloc (for callers that cannot
 // allocate): the workspace of one forward, in a file-scope device array of
@@ -882,6 +892,41 @@ tpa_status dora_scale_host(tpa_layer* L, const tpa_adapter_desc* d, hipStream_t 
   return TPA_OK;
 }
 
+
+// Installs the layer's VeRA pair: A_v from `va` (taking a hold on it and
+// dropping the one on its previous A), B_v [d_out][r_v] uploaded from the
+// float32 host array B [r_v][d_out].  Synchronizes s.
+tpa_status set_vera_b(tpa_layer* L, VeraA* va, const float* B, hipStream_t s) {
+  const size_t esz = tpa::dtype_size(L->dtype);
+  const int r_v = va->r_v;
+  void* bmem = nullptr;
+  TPA_HIP(hipMalloc(&bmem, (size_t)L->d_out * r_v * esz));
+  Staging st{L};
+  float* b32;
+  tpa_status e = st.reserve(((size_t)r_v * L->d_out + 63) / 64 * 64);
+  if (!e) e = st.put(B, (size_t)r_v * L->d_out, &b32, s);
+  if (e) {
+    (void)hipFree(bmem);
+    return e;
+  }
+  // B [r_v][d_out] -> [d_out][r_v].
+  hipError_t he = tpa::launch_pack_transpose(L->dtype, b32, r_v, L->d_out, 1.f, nullptr, bmem, L->d_out, r_v, s);
+  if (he == hipSuccess) he = hipStreamSynchronize(s);
+  if (he != hipSuccess) {
+    (void)hipFree(bmem);
+    return fail(TPA_ERR_HIP, "%s", hipGetErrorString(he));
+  }
+  ++va->refs;
+  release_vera_a(L);
+  if (L->vera_mem) (void)hipFree(L->vera_mem);
+  L->vera_a = va;
+  L->vera_mem = bmem;
+  L->vera_At = va->mem;
+  L->vera_Bt = bmem;
+  L->r_v = r_v;
+  return TPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -956,9 +1001,11 @@ tpa_status tpa_layer_destroy(tpa_layer* L) {
   L->arena.release();
   if (L->ev_fork) (void)hipEventDestroy(L->ev_fork);
   if (L->ev_join) (void)hipEventDestroy(L->ev_join);
+  if (L->side) (void)hipStreamDestroy(L->side);
   if (L->stage) (void)hipFree(L->stage);
   if (L->status_dev) (void)hipFree(L->status_dev);
   if (L->vera_mem) (void)hipFree(L->vera_mem);
+  release_vera_a(L);
   if (L->slots_dev) (void)hipFree(L->slots_dev);
   if (L->flag_dev) (void)hipFree(L->flag_dev);
   delete L;
@@ -976,29 +1023,62 @@ tpa_status tpa_vera_shared_set(tpa_layer* L, int32_t r_v, const float* A, const 
   DeviceGuard guard(L->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   TPA_HIP(hipStreamSynchronize(s));
-  if (L->vera_mem) {
-    TPA_HIP(hipFree(L->vera_mem));
-    L->vera_mem = nullptr;
-  }
   const size_t esz = tpa::dtype_size(L->dtype);
-  const size_t at_bytes = align256((size_t)r_v * L->d_in * esz);
-  const size_t bt_bytes = align256((size_t)L->d_out * r_v * esz);
-  TPA_HIP(hipMalloc(&L->vera_mem, at_bytes + bt_bytes));
-  char* base = static_cast<char*>(L->vera_mem);
+  VeraA* va = new VeraA();
+  va->device = L->device;
+  va->dtype = L->dtype;
+  va->d_in = L->d_in;
+  va->r_v = r_v;
+  if (hipError_t e = hipMalloc(&va->mem, (size_t)r_v * L->d_in * esz)) {
+    delete va;
+    return fail(TPA_ERR_HIP, "%s", hipGetErrorString(e));
+  }
   Staging st{L};
-  float *a32, *b32;
-  if (tpa_status e = st.reserve(((size_t)L->d_in * r_v + 63) / 64 * 64 + ((size_t)r_v * L->d_out + 63) / 64 * 64))
+  float* a32;
+  if (tpa_status e = st.reserve(((size_t)L->d_in * r_v + 63) / 64 * 64)) {
+    (void)hipFree(va->mem);
+    delete va;
     return e;
-  if (tpa_status e = st.put(A, (size_t)L->d_in * r_v, &a32, s)) return e;
-  if (tpa_status e = st.put(B, (size_t)r_v * L->d_out, &b32, s)) return e;
-  // A [d_in][r_v] -> [r_v][d_in];  B [r_v][d_out] -> [d_out][r_v].
-  TPA_HIP(tpa::launch_pack_transpose(L->dtype, a32, L->d_in, r_v, 1.f, nullptr, base, r_v, L->d_in, s));
-  TPA_HIP(tpa::launch_pack_transpose(L->dtype, b32, r_v, L->d_out, 1.f, nullptr, base + at_bytes, L->d_out, r_v, s));
-  TPA_HIP(hipStreamSynchronize(s));
-  L->vera_At = base;
-  L->vera_Bt = base + at_bytes;
-  L->r_v = r_v;
+  }
+  if (tpa_status e = st.put(A, (size_t)L->d_in * r_v, &a32, s)) {
+    (void)hipFree(va->mem);
+    delete va;
+    return e;
+  }
+  // A [d_in][r_v] -> [r_v][d_in].
+  hipError_t e = tpa::launch_pack_transpose(L->dtype, a32, L->d_in, r_v, 1.f, nullptr, va->mem, r_v, L->d_in, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipFree(va->mem);
+    delete va;
+    return fail(TPA_ERR_HIP, "%s", hipGetErrorString(e));
+  }
+  if (tpa_status st2 = set_vera_b(L, va, B, s)) {
+    (void)hipFree(va->mem);
+    delete va;
+    return st2;
+  }
   return TPA_OK;
+}
+
+tpa_status tpa_vera_shared_set_from(tpa_layer* L, tpa_layer* from, const float* B, tpa_stream stream) {
+  if (tpa_status st = check_layer(L)) return st;
+  if (tpa_status st = check_layer(from)) return st;
+  if (!B) return fail(TPA_ERR_INVALID, "null VeRA factor");
+  if (!from->vera_a) return fail(TPA_ERR_INVALID, "the source layer has no VeRA pair");
+  if (from->device != L->device || from->dtype != L->dtype || from->d_in != L->d_in)
+    return fail(TPA_ERR_INVALID, "the source layer differs in device, dtype or d_in");
+  if (from->r_v > L->max_rank) return fail(TPA_ERR_INVALID, "r_v %d above max_rank %d", from->r_v, L->max_rank);
+  if (L->n_vera > 0) return fail(TPA_ERR_INVALID, "VeRA slots are loaded; unload them first");
+  if (!finite_all(B, (size_t)from->r_v * L->d_out)) return fail(TPA_ERR_VALUE, "non-finite VeRA factor");
+  DeviceGuard guard(L->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TPA_HIP(hipStreamSynchronize(s));
+  VeraA* va = from->vera_a;
+  ++va->refs;  // held across set_vera_b, which releases the layer's old A
+  const tpa_status st = set_vera_b(L, va, B, s);
+  --va->refs;
+  return st;
 }
 
 tpa_status tpa_adapter_load(tpa_layer* L, const tpa_adapter_desc* d, int32_t* slot_out, tpa_stream stream) {
@@ -1591,6 +1671,8 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       sh[i].part = reinterpret_cast<float*>(sl[i].w + y.vpart);
       sh[i].v = sl[i].w + y.v;
     }
+    sh[i].part_shared = nullptr;
+    sh[i].kmax_shared = 0;
     of[i] = tpa::OftArgs{};
     of[i].x = sl[i].x;
     of[i].oft_tiles = p.oft_tiles;
@@ -1601,28 +1683,40 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     of[i].max_tiles = oft_tile_bound(L, n, tile_rows, y.max_tiles);
   }
 
+  // VeRA's A_v read once per fused input (Table 2's route-two count; the
+  // appendix "Byte counts"): a projection of the group whose layer holds the
+  // first projection's A_v and reads the same input computes no x·A_vᵀ of
+  // its own; its reduction takes the first projection's partials and
+  // applies its own d'.  Same bits as computing them again.
+  for (int i = 1; i < count; ++i) {
+    const tpa_layer* L = sl[i].L;
+    if (term[i] && term[0] && L->n_vera > 0 && L0->n_vera > 0 && L->vera_At && L->vera_At == L0->vera_At &&
+        sl[i].x == sl[0].x && L->r_v == L0->r_v && sh[i].split == sh[0].split && sh[i].kc == sh[0].kc) {
+      sh[i].sh_ntiles = 0;
+      sh[i].part_shared = sh[0].part;
+      sh[i].kmax_shared = sh[0].kmax;
+    }
+  }
+
   // 2. The shrink and OFT's rotation: one launch per OFT block size present
   //    (the shrink rides in the first), or one for the shrink alone.  With
   //    overlap on, the shrink and its split reduction run on the layer's
   //    second stream beside OFT's rotation and the base GEMM (neither reads
-  //    V or U), and the expand waits for them.  By default only above 128
-  //    rows: in a graph-replayed decode step the fork and join cost more
-  //    than the launch they hide (222 vs 202 µs per decoder layer; on the
-  //    2-layer cut of the 1024-tenant Zipf stack 96 rows 314-315 -> 318-322
-  //    µs per layer, 128 rows 378 -> 385), while that cut gains at 192 rows
-  //    (442.5 -> 436-437), 1024 (1203-1219 -> 1156-1159) and 4096 (2890 ->
-  //    2876-2879), the shrink's waves filling CUs the split GEMM leaves
-  //    short of work.  Never where the expand rides in the
-  //    GEMM's epilogue: that GEMM reads V and U, so nothing could overlap.
-  //    The second stream and its events are made on first use, outside
-  //    graph capture (a captured forward before then runs on one stream;
-  //    both orders give the same bits).
+  //    V or U), and the expand waits for them.  Only when asked for
+  //    (TPA_OPT_OVERLAP = 1): in a graph-replayed decode step the fork and
+  //    join cost more than the launch they hide (222 vs 202 µs per decoder
+  //    layer), and larger batches gain 1-4% (2-layer cut of the
+  //    1024-tenant Zipf stack: 192 rows 442.5 -> 436-437 µs per layer,
+  //    1024 rows 1203-1219 -> 1156-1159, 4096 rows 2890 -> 2876-2879).
+  //    Never where the expand rides in the GEMM's epilogue: that GEMM reads
+  //    V and U, so nothing could overlap.  The second stream and its events
+  //    are made on first use, outside graph capture (a captured forward
+  //    before then runs on one stream; both orders give the same bits).
   bool any_fused_cfg = false;
   for (int i = 0; i < count; ++i) any_fused_cfg = any_fused_cfg || sl[i].c.fused;
   const int ov_opt = L0->opt[TPA_OPT_OVERLAP];
-  bool overlap = allow_side && any_term_all && !any_fused_cfg && (ov_opt == 1 || (ov_opt < 0 && n > 128));
-  hipStream_t side = overlap ? side_stream(L0->device) : nullptr;
-  if (overlap && !(side && L0->ev_fork && L0->ev_join)) {
+  bool overlap = allow_side && any_term_all && !any_fused_cfg && ov_opt == 1;
+  if (overlap && !(L0->side && L0->ev_fork && L0->ev_join)) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
       (void)hipGetLastError();
@@ -1631,21 +1725,17 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     overlap = cap == hipStreamCaptureStatusNone;
   }
   if (overlap) {
-    if (!side) {
-      std::lock_guard<std::mutex> lock(g_side_mu);
-      if (!g_side[L0->device]) TPA_HIP(hipStreamCreateWithFlags(&g_side[L0->device], hipStreamNonBlocking));
-      side = g_side[L0->device];
-    }
+    if (!L0->side) TPA_HIP(hipStreamCreateWithFlags(&L0->side, hipStreamNonBlocking));
     if (!L0->ev_fork) TPA_HIP(hipEventCreateWithFlags(&L0->ev_fork, hipEventDisableTiming));
     if (!L0->ev_join) TPA_HIP(hipEventCreateWithFlags(&L0->ev_join, hipEventDisableTiming));
     TPA_HIP(hipEventRecord(L0->ev_fork, s));
-    TPA_HIP(hipStreamWaitEvent(side, L0->ev_fork, 0));
+    TPA_HIP(hipStreamWaitEvent(L0->side, L0->ev_fork, 0));
     tpa::PreSlice ps[tpa::MAX_SLICES];
     for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr);
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, side));
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, L0->side));
     for (int i = 0; i < count; ++i)
-      if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], side));
-    TPA_HIP(hipEventRecord(L0->ev_join, side));
+      if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], L0->side));
+    TPA_HIP(hipEventRecord(L0->ev_join, L0->side));
   }
   static const int kBs[3] = {16, 32, 64};
   tpa::PreSlice ps[tpa::MAX_SLICES];

@@ -120,6 +120,11 @@ struct ShrinkArgs {
   int32_t split, kc;       // k ranges (kc a multiple of 32)
   float* part;
   void* v;
+  // Shared-term rows read their x·A_vᵀ partials from here when set (the
+  // first projection of a group that shares A_v and the input computed
+  // them; row stride kmax_shared), else from part.
+  const float* part_shared;
+  int32_t kmax_shared;
 };
 // One slice of the launch before the base GEMM: the shrink's items and/or
 // OFT's rotation of its tiles for the launch's block size.

@@ -112,7 +112,10 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
 
 // Reduce pass: V[p][c] = Σ_s part[s][p][c] in split order (times d'[c] for
 // a shared-term row), stored in the layer type; one thread per 4 columns of
-// one plan position, only for columns below the row's rank.
+// one plan position, only for columns below the row's rank.  A shared-term
+// row's partials may come from another projection of the group
+// (part_shared): x·A_vᵀ is the same for every projection that reads the
+// same input with the same A_v, only d' differs.
 template <typename T>
 __device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx) {
   const int q4 = a.kmax / 4;
@@ -125,8 +128,10 @@ __device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx)
   const int N = cls == CLS_OWNED ? sd.rank : a.r_v;
   if (col >= N) return;
   // Splits added in order; their loads go out 8 at a time.
-  const float* src = a.part + (size_t)p * a.kmax + col;
-  const size_t stride = (size_t)a.n * a.kmax;
+  const bool borrowed = cls == CLS_SHARED && a.part_shared;
+  const int ld = borrowed ? a.kmax_shared : a.kmax;
+  const float* src = (borrowed ? a.part_shared : a.part) + (size_t)p * ld + col;
+  const size_t stride = (size_t)a.n * ld;
   f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = 0;
   for (; s + 8 <= a.split; s += 8) {

@@ -88,6 +88,11 @@ class AdaptedLayer:
         A = np.asarray(A, np.float32)
         B.tpa_vera_shared_set(self.handle, A.shape[1], A, Bm, _stream())
 
+    def set_vera_shared_from(self, other, Bm):
+        """VeRA's pair with other's stored A (read once by a group forward
+        over projections of one input) and this layer's own B."""
+        B.tpa_vera_shared_set_from(self.handle, other.handle, Bm, _stream())
+
     @staticmethod
     def _kwargs(rec):
         meth = rec["method"]

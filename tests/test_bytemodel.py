@@ -71,3 +71,15 @@ def test_true_rank_counts_and_stored_padding():
     assert b.owned_ranks == [8] and b.owned_ranks_stored == [16] and b.v_elems == 32
     assert bm.kernel_bytes(b)["shrink"]["bytes"] == 2 * (4 * 64 + 8 * 64) + 2 * 32
     assert bm.stored_factor_bytes(b) == 2 * 16 * (64 + 128)
+
+
+def test_vera_a_read_once_per_fused_input():
+    """A projection that shares its input and VeRA's A with an earlier one of
+    its fused layer reads neither x nor A_v for the VeRA rows: it reads the
+    shared x·A_v product instead (appendix "Byte counts")."""
+    import numpy as np
+    ad = {1: {"method": "vera", "d": np.zeros(256), "e": np.zeros(1024)}}
+    own = bm.kernel_bytes(bm.shape_of(8, 4096, 1024, [1] * 8, ad, q=2, r_v=256))["shrink"]["bytes"]
+    shared = bm.kernel_bytes(bm.shape_of(8, 4096, 1024, [1] * 8, ad, q=2, r_v=256,
+                                         vera_a_read=False))["shrink"]["bytes"]
+    assert own - shared == 2 * (8 * 4096 + 256 * 4096) - 2 * 8 * 256

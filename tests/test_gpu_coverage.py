@@ -8,7 +8,9 @@
     rows grouped into one segment per adapter);
   * OFT's rotation with blocks of 16, 32 and 64 (§4.1 route three), on a
     tiny layer and on a 4096-wide one, on the decode and the prefill
-    kernels, against the oracle's direct definition y = (x R) W."""
+    kernels, against the oracle's direct definition y = (x R) W;
+  * VeRA's A stored and read once per fused input (q/k/v, gate/up), against
+    the same group with a copy per projection and the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -139,3 +141,62 @@ def test_oft_block_sizes_4096_wide(n):
     y, h, xw = reference(p, wl["slot_of_row"])
     check(y_gpu, y, h, xw, label="oft blocks 4096 n=%d" % n)
     L.close()
+
+
+# ------------------------------------------------ VeRA's A once per group ---
+
+def _borrowing_layers(projs, max_slots=32, max_rank=256):
+    """Layers of one fused input: the first stores VeRA's pair, the others
+    take its A (tpa_vera_shared_set_from) with their own B."""
+    from tenant_peft_adapter_amd.layer import AdaptedLayer
+    Ls = []
+    for i, p in enumerate(projs):
+        if i == 0:
+            Ls.append(make_layer(p, max_slots=max_slots, max_rank=max_rank))
+            continue
+        assert p["shared"]["A"] is projs[0]["shared"]["A"]
+        L = AdaptedLayer(torch.tensor(p["W"]).half().cuda(), max_slots=max_slots, max_rank=max_rank)
+        L.set_vera_shared_from(Ls[0], p["shared"]["B"])
+        for slot in sorted(p["adapters"]):
+            assert L.load(p["adapters"][slot]) == slot
+        Ls.append(L)
+    return Ls
+
+
+@pytest.mark.parametrize("names,n", [(("q", "k", "v"), 64), (("q", "k", "v"), 300), (("gate", "up"), 64)])
+def test_vera_a_read_once_per_fused_group(names, n):
+    """Appendix "Byte counts": VeRA's A is read once per fused input.  The
+    group forward over projections that hold one A_v and read one input
+    computes x·A_vᵀ once; its outputs equal, bit for bit, those of the same
+    group with a copy of A per projection and an input tensor per
+    projection, and match the oracle.  Closing the layer that stored A
+    leaves the others working (the A block is held by all of them)."""
+    from tenant_peft_adapter_amd.layer import LayerGroup, RowPlan
+    shapes = tuple(s for s in synth.LLAMA8B_PROJECTIONS if s[0] in names)
+    wl = synth.decoder_layer_mixed(n=n, shapes=shapes)
+    projs = wl["projections"]
+    sor = torch.tensor(wl["slot_of_row"]).cuda()
+    say("shared A group %s n=%d" % ("+".join(names), n))
+    Ls = _borrowing_layers(projs)
+    x = torch.tensor(projs[0]["x"]).half().cuda()
+    plan = RowPlan(Ls[0], n).build(Ls[0], sor)
+    got = [o.clone() for o in LayerGroup(Ls, n).forward(plan, [x] * len(Ls))]
+    Lo = [make_layer(p, max_slots=32, max_rank=256) for p in projs]
+    xs = [torch.tensor(p["x"]).half().cuda() for p in projs]
+    plan2 = RowPlan(Lo[0], n).build(Lo[0], sor)
+    want = LayerGroup(Lo, n).forward(plan2, xs)
+    torch.cuda.synchronize()
+    for nm, g, w, p in zip(names, got, want, projs):
+        assert torch.equal(g, w), nm
+        rows = np.arange(0, n, max(1, n // 64))
+        y, h, xw = reference(p, wl["slot_of_row"], rows)
+        check(g.float().cpu().numpy().astype(np.float64)[rows], y, h, xw, label="shared A %s n=%d" % (nm, n))
+    Ls[0].close()
+    y1 = Ls[1].forward(x, sor)
+    w1 = Lo[1].forward(xs[1], sor)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, w1)
+    plan.close()
+    plan2.close()
+    for L in Ls[1:] + Lo:
+        L.close()

@@ -331,7 +331,7 @@ def test_shared_plan_forward_matches_plain_forward():
 def test_overlap_matches_one_stream(n, path, fuse):
     """The shrink on the layer's second stream gives the same bits as every
     step on the caller's stream (option 0): same kernels, same order of the
-    split sums; forced on (1), automatic (-1, on above 128 rows), and with the
+    split sums; forced on (1), automatic (-1, one stream), and with the
     expand in the GEMM's epilogue (fuse 1), where overlap does not apply."""
     wl = synth.tiny_mixed(seed=70 + n, n=n, dtype="f16", with_identity=True)
     p = wl["projections"][0]
@@ -351,15 +351,15 @@ def test_overlap_matches_one_stream(n, path, fuse):
     check(outs[0], y, h, xw, label="overlap n=%d" % n)
 
 
-def test_first_forward_inside_graph_capture_with_automatic_overlap():
-    """A fresh layer whose first forward above 128 rows is captured runs that
-    forward on the capturing stream alone (no stream is made during
+def test_first_forward_inside_graph_capture_with_overlap():
+    """A fresh layer with overlap on whose first forward is captured runs
+    that forward on the capturing stream alone (no stream is made during
     capture); eager forwards afterwards overlap; replays and eager calls
     give the same bits."""
     n = 200
     wl = synth.tiny_mixed(seed=777, n=n, dtype="f16", with_identity=True)
     p = wl["projections"][0]
-    L = make_layer(p, max_slots=8, max_rank=32, options={11: 0})
+    L = make_layer(p, max_slots=8, max_rank=32, options={11: 0, 9: 1})
     x = torch.tensor(p["x"]).half().cuda()
     sor = torch.tensor(wl["slot_of_row"]).cuda()
     out = torch.empty((n, L.d_out), dtype=torch.float16, device="cuda")

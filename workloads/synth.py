@@ -262,6 +262,12 @@ def prefill_lora_dora(seed=1000, n=1024, d=4096, r=16, dtype="f16", tenants=16, 
             "slot_of_row": slot_of_row, "projections": [p]}
 
 
+# Projections that read one input in the model (the fused layers q/k/v and
+# gate/up): they share the input rows and VeRA's A (appendix "Byte counts":
+# the shared A is read once per fused input, B once per slice).
+FUSED_INPUT_OF = {"q": "q", "k": "q", "v": "q", "o": "o", "gate": "gate", "up": "gate", "down": "down"}
+
+
 def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=256,
                         oft_block=32, shapes=LLAMA8B_PROJECTIONS, pure_lora=False):
     """One decoder layer's seven projections with 5 * per_method tenants:
@@ -270,7 +276,11 @@ def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=25
     has slot t + 1 in every projection; where its method does not adapt a
     projection the slot holds the identity.  Row j belongs to tenant
     j mod (5 * per_method), then the rows are shuffled so segments are not
-    contiguous.  Inputs per projection are independent N(0, 1) rows.
+    contiguous.  Inputs are N(0, 1) rows, one draw per fused input (q, k and
+    v read the same rows, gate and up the same rows, o and down their own),
+    and VeRA's A is drawn once per fused input (B per projection); a
+    projection that takes them from an earlier one records its name in
+    p["input_of"] and p["shared"]["a_from"].
 
     pure_lora: the same rows and slots, every tenant a rank-r LoRA (the
     equal-size pure-LoRA batch)."""
@@ -279,11 +289,19 @@ def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=25
     order = ["lora", "dora", "ia3", "vera", "oft"]
     methods = [order[t // per_method] for t in range(T)]
     projs = []
+    by_name = {}
     for name, d_in, d_out in shapes:
         p = make_projection(rng, name, d_in, d_out, dtype, n)
+        src = by_name.get(FUSED_INPUT_OF.get(name, name))
+        if src is not None and src["d_in"] == d_in:
+            p["x"] = src["x"]
+            p["input_of"] = src["name"]
         stats = None
         if not pure_lora:
             p["shared"] = _vera_shared(rng, d_in, d_out, r_v, dtype)
+            if src is not None and src["d_in"] == d_in:
+                p["shared"]["A"] = src["shared"]["A"]
+                p["shared"]["a_from"] = src["name"]
             stats = _BaseStats(p["W"])
         for t, m in enumerate(methods):
             slot = t + 1
@@ -300,6 +318,7 @@ def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=25
                 p["adapters"][slot] = (_oft(rng, d_in, oft_block) if name in ("q", "k", "v")
                                        else {"method": "identity"})
         projs.append(p)
+        by_name.setdefault(name, p)
     slot_of_row = (np.arange(n) % T + 1).astype(np.int32)
     slot_of_row = slot_of_row[rng.permutation(n)]
     return {"name": "decoder_layer_mixed" + ("_pure_lora" if pure_lora else ""),
