@@ -786,6 +786,14 @@ def prefill_main(args):
     from tenant_peft_adapter_amd import binding as B
     from workloads import synth
     torch.cuda.set_device(0)
+    # One 1 GiB device copy first: the reference that scales the hardware
+    # byte counters of a profiled run.
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    B.tpa_probe_copy(dst.data_ptr(), src.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del src, dst
     n = 1024
     wl = synth.prefill_lora_dora(n=n, tenants=16)
     p = wl["projections"][0]
