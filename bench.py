@@ -61,8 +61,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4,
                     help="buffer sets the timed chain rotates over (cold weights; 4 sets hold 1.8 GB of W)")
     ap.add_argument("--routes", action="store_true",
-                    help="also measure the routes-against-the-byte-model table (off by default: its first run "
-                         "ended in a segmentation fault of this process whose cause is not yet shown)")
+                    help="also measure the routes-against-the-byte-model table (eager, event-timed forwards)")
+    ap.add_argument("--only-routes", action="store_true", help="calibrate and measure the routes table only")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time in the CPU sample")
     ap.add_argument("--workload", default="decoder_layer_mixed",
                     choices=("decoder_layer_mixed", "stack", "prefill_q_proj"),
@@ -666,18 +666,21 @@ def dora_expand_ratio(torch, ns=(1024, 4096), stage_reps=20):
     return out
 
 
-def route_table(torch, cal, ns=(256, 1024, 4096), d_outs=(4096, 14336), oft_k=(1, 4, 16)):
+def route_table(torch, cal, ns=(256, 512, 1024, 2048, 4096), d_outs=(1024, 4096, 14336), oft_k=(1, 4, 16), reps=10):
     """Appendix "Routes" and Table A7, on this chip: measured layer time of
     each route that applies DoRA's s outside the expand (side kernel,
     gathered scale, index scale) and of OFT's input transform, against the
     byte model t0 + ΔQ/β + ΔL·λ (§4.3), t0 the same batch without the extra
-    pass.  β is β_L2 when the extra bytes fit the L2, β_MALL when they fit
-    the MALL, else β_HBM (§4.3: the cache's rate when the extra read and
-    write fit in it).  Cells: 16 DoRA r16 segments, d_in 4096, n rows x
-    d_out; OFT: k tenants (b = 32) over n rows, d_in 4096 and 14336.
-    Returns the cells and, per route, the median absolute error of the
-    increment and of the total over bandwidth-regime cells (ΔQ/β > λ) and of
-    the total over the launch-bound rest."""
+    pass.  Times are the library's timing events around each forward, run
+    eagerly behind an idle wave (as `stage_times`), first event to last,
+    mean of `reps`.  β is β_L2 when the extra bytes fit the L2, β_MALL when
+    they fit the MALL, else β_HBM (§4.3: the cache's rate when the extra
+    read and write fit in it).  Cells: 16 DoRA r16 segments, d_in 4096, n
+    rows x d_out; OFT: k tenants (b = 32) over n rows, d_in 4096 and 14336,
+    against the same weight without adapters (one launch fewer).  Returns
+    the cells and, per route, the median absolute error of the increment and
+    of the total over bandwidth-regime cells (ΔQ/β > λ) and of the total
+    over the launch-bound rest."""
     import statistics
 
     import numpy as np
@@ -692,6 +695,10 @@ def route_table(torch, cal, ns=(256, 1024, 4096), d_outs=(4096, 14336), oft_k=(1
         if dq <= MALL_BYTES:
             return cal["beta_mall"], "mall"
         return cal["beta_hbm"], "hbm"
+
+    def layer_time(L, x, sor):
+        call = layer_call([L], [x], sor, torch)
+        return sum(stage_times([L], lambda: call(0), reps, torch)[0]) * 1e-6
 
     cells = []
 
@@ -720,29 +727,30 @@ def route_table(torch, cal, ns=(256, 1024, 4096), d_outs=(4096, 14336), oft_k=(1
                 L = La if route < 2 else Lb
                 L.set_option(B.TPA_OPT_SCALE_ROUTE, route)
                 log("routes: cell d_out=%d n=%d route=%d" % (d_out, n, route))
-                t[route] = time_chain(layer_call([L], [x], sor, torch), torch)[0]
+                t[route] = layer_time(L, x, sor)
             for route in (1, 2, 3):
                 dq, dl = bm.scale_route_extra(n, d_out, route)
                 add(names[route], n, d_out, t[0], t[route], dq, dl)
         La.close()
         Lb.close()
-        log("routes: d_out %d done" % d_out)
     for d_in in (4096, 14336):
         rng = np.random.default_rng(7100 + d_in)
         p = synth.make_projection(rng, "oft", d_in, 4096, "f16", 1)
         p["adapters"] = {t + 1: synth._oft(rng, d_in, 32) for t in range(max(oft_k))}
         L = load_layer(p, torch, options={B.TPA_OPT_FUSE_EXPAND: 0})
+        L0 = load_layer({**p, "adapters": {}}, torch, options={B.TPA_OPT_FUSE_EXPAND: 0})
         x_all = torch.randn((nmax, d_in), device="cuda").half()
         for n in ns:
             x = x_all[:n].contiguous()
-            t0 = time_chain(layer_call([L], [x], torch.zeros(n, dtype=torch.int32, device="cuda"), torch), torch)[0]
+            log("routes: OFT base d_in=%d n=%d" % (d_in, n))
+            t0 = layer_time(L0, x, torch.zeros(n, dtype=torch.int32, device="cuda"))
             for k in oft_k:
                 log("routes: OFT cell d_in=%d n=%d k=%d" % (d_in, n, k))
                 sor = torch.tensor((np.arange(n) * k // n + 1).astype(np.int32)).cuda()
-                t = time_chain(layer_call([L], [x], sor, torch), torch)[0]
+                t = layer_time(L, x, sor)
                 add("OFT transform", n, d_in, t0, t, 2 * (2 * n * d_in + k * d_in * 32), 1)
         L.close()
-        log("routes: OFT d_in %d done" % d_in)
+        L0.close()
     summary = {}
     for route in list(names.values()) + ["OFT transform"]:
         bw = [c for c in cells if c["route"] == route and c["bandwidth_regime"]]
@@ -830,6 +838,12 @@ def main():
     from workloads import synth
 
     torch.cuda.set_device(0)
+    if args.only_routes:
+        cal = calibrate(torch, full=True)
+        out = {"workload": "routes against the byte model", "calibration": {k: v for k, v in cal.items()},
+               "routes_vs_byte_model": route_table(torch, cal)}
+        print(json.dumps(out), flush=True)
+        return
     log("generating the mixed decoder-layer workload")
     wl = synth.decoder_layer_mixed()
     n = wl["n"]
