@@ -227,7 +227,9 @@ tpa_status tpa_adapter_info_get(const tpa_layer* layer, int32_t slot, tpa_adapte
  * the layer's current options; n_max <= 8192.  The workspace holds the row
  * plan (§2 "The LoRA schedule"), the rotated rows of OFT tenants (§4.1
  * route three), the shrink's V and U between the two halves of the term
- * (§2), and the base GEMM's split partials.  Host only. */
+ * (§2), the base GEMM's split partials and, when the decode GEMM carries
+ * the expand, its arrival counters (one word per column tile, cleared on
+ * every forward by the launch before the GEMM).  Host only. */
 tpa_status tpa_workspace_size(const tpa_layer* layer, int32_t n_max, size_t* bytes);
 
 /* out[i] = F_{slot_of_row[i]}(x[i]) for i < n (eq. (1)).
@@ -410,14 +412,29 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          tiles, 8 waves; needs d_out % 256 == 0) or 128;
  *                          by default 256 when that gives at least 256
  *                          tiles, else 128.
- *   TPA_OPT_FUSE_EXPAND  : 128 x 128 direct-load kernel with k whole: 1 runs
- *                          the expand in the GEMM's epilogue (the GEMM
+ *   TPA_OPT_FUSE_EXPAND  : the expand in the base GEMM's epilogue (§2 "The
+ *                          LoRA schedule"; §5.2).  128 x 128 direct-load
+ *                          kernel with k whole: 1 runs it there (the GEMM
  *                          takes the rows in the plan's tile order, 16 row
  *                          slots per tile, keeps h in fp32 and writes out
  *                          once; the shrink's reduction becomes a launch
- *                          before it); 0 a separate expand; by default
- *                          the epilogue when the plan's tile bound keeps the
- *                          row slots within 1.5x the rows. */
+ *                          before it); by default when the plan's tile
+ *                          bound keeps the row slots within 1.5x the rows.
+ *                          Streamed decode kernel (n <= 64, 3 stages,
+ *                          16-row tiles, route 0, shrink split <= 16): by
+ *                          default (1 or < 0) the work-group that completes
+ *                          a column tile (the last of its split work-groups
+ *                          to arrive, counted on counters in the workspace
+ *                          that the launch before the GEMM clears) adds the
+ *                          splits, applies s and b and adds the term; the
+ *                          shrink then adds its k ranges inside one
+ *                          work-group, so two launches per forward instead
+ *                          of three.  It needs a launch before the GEMM (a
+ *                          term or an OFT rotation on the layer) unless k
+ *                          is whole, and rounds the last sum to the layer
+ *                          type once, so it may differ from the separate
+ *                          expand by one unit in the last place.  0: a
+ *                          separate expand everywhere. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -441,7 +458,8 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
  * and k range, the scale route, the decode GEMM's k-groups per work-group
  * and (direct-load kernels, else 0) its LDS buffers (per k-group for the
  * streamed kernel), path 3's tile edge (128 or 256; else 0), and whether
- * the expand runs in the GEMM's epilogue.  For tests and measurement. */
+ * the expand runs in the GEMM's epilogue (prefill or decode kernel).  For
+ * tests and measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
       gemm_groups, gemm_stages, gemm_tile, fused_expand;

@@ -207,6 +207,7 @@ struct Config {
   int gemm_tile;  // path 3: 128 (128 x 128 tiles) or 256 (256 x 256 tiles)
   int fused;      // path 3, 128 x 128 tiles: the expand runs in the GEMM's epilogue
   int h_fp32;     // h goes to the expand in fp32 even when k is not split
+  int fused_dec;  // path 2: the expand runs in the streamed GEMM's epilogue, after a whole-k shrink
 };
 
 bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2; }
@@ -227,6 +228,7 @@ struct Layout {
   size_t perm, pinfo, row_slot, rot_pos, seg_ptr, seg_slot, tiles, oft_tiles, counts;
   size_t plan_end;  // the plan arrays come first; a shared plan buffer holds [0, plan_end)
   size_t x_rot, hpart, vpart, v, srow;
+  size_t cnt;  // fused decode epilogue: one arrival counter per column tile
   size_t total;
   int max_tiles;
   size_t sh_tiles;
@@ -388,13 +390,33 @@ void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stage
 // splits), which halve the fp32 partials written and summed again (2-layer
 // cut of the 1024-tenant Zipf stack at 4096 rows: 2999 -> 2902 µs per
 // layer; at 1024 rows the short ranges stay ahead, 1218 vs 1235).
+// With the expand in the decode GEMM's epilogue the shrink runs whole-k
+// (one work-group per item adds the k ranges itself), so at most
+// PRE_WHOLE_WAVES ranges.
 void set_shrink_split(const tpa_layer* L, int n, Config* c) {
   int ssplit = L->opt[TPA_OPT_SHRINK_SPLIT];
-  if (ssplit <= 0)
+  if (ssplit <= 0) {
     ssplit = n >= 2048 ? std::max(1, std::min(8, L->d_in / 512)) : std::max(1, std::min(28, L->d_in / 256));
+    if (c->fused_dec) ssplit = std::min(ssplit, tpa::PRE_WHOLE_WAVES);
+  }
   ssplit = std::min(ssplit, L->d_in / 32);
   c->shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
   c->shrink_split = (L->d_in + c->shrink_kc - 1) / c->shrink_kc;
+}
+
+int max_tiles_for(const tpa_layer* L, int n, int tile_rows);
+int all_tile_bound(const tpa_layer* L, int n, int tr, int max_tiles);
+
+// Whether the streamed decode GEMM can carry the expand for n rows at the
+// configuration's column blocks and k-groups: one thread per entry of the
+// tile list and the epilogue's tables within LDS beside the rings.
+bool fused_dec_fits(const tpa_layer* L, int n, const Config& c) {
+  const int mt = all_tile_bound(L, n, c.tile_rows, max_tiles_for(L, n, c.tile_rows));
+  const int kcap = std::max(L->kmax, L->r_v);
+  const size_t lds = tpa::gemm_stream_lds(n, c.gemm_nb, c.gemm_groups, c.gemm_stages) +
+                     tpa::gemm_stream_epi_lds(n, mt, mt * ((kcap + 31) / 32));
+  return mt <= 256 * c.gemm_groups && lds <= tpa::GEMM_STREAM_MAX_LDS &&
+         tpa::gemm_stream_epi_ok(n, c.gemm_nb, c.gemm_groups, c.gemm_stages);
 }
 
 Config choose_config(const tpa_layer* L, int n) {
@@ -501,10 +523,20 @@ Config choose_config(const tpa_layer* L, int n) {
     const long slots = 16L * ((n + 15) / 16 + std::min(n, L->n_owned) + 2);  // the plan's tile bound
     c.fused = L->opt[TPA_OPT_FUSE_EXPAND] == 1 || 2 * slots <= 3L * n;
   }
+  // Decode: the expand in the streamed GEMM's epilogue (the column tile's
+  // last split work-group finishes it), after a whole-k shrink, so the
+  // four launches of a projection group become two (decoder layer,
+  // graph-replayed step: see the measurements kept with the bench).  Needs
+  // the 3-stage streamed kernel, 16-row tiles, s inside the expand, a
+  // shrink of at most PRE_WHOLE_WAVES k ranges, and the tables in LDS.
+  c.fused_dec = 0;
+  if (c.gemm_path == 2 && n <= 64 && c.gemm_stages == 3 && c.tile_rows == 16 && c.scale_route == 0 &&
+      L->opt[TPA_OPT_FUSE_EXPAND] != 0 && L->opt[TPA_OPT_SHRINK_SPLIT] <= tpa::PRE_WHOLE_WAVES)
+    c.fused_dec = fused_dec_fits(L, n, c);
   // A stacked slot's scale is the product of its members' scales, so h
   // rounded to the layer type before the expand would carry |s|·u·|h| of
   // error: such layers keep h in fp32 between the GEMM and the expand.
-  c.h_fp32 = L->n_stack > 0 && !c.fused;
+  c.h_fp32 = L->n_stack > 0 && !c.fused && !c.fused_dec;
   set_shrink_split(L, n, &c);
   return c;
 }
@@ -541,9 +573,10 @@ Layout make_layout(const tpa_layer* L, int n, const Config& c) {
   y.x_rot = take((size_t)n * L->d_in * esz);
   const bool need_hpart = h_partials(c);
   y.hpart = take(need_hpart ? (size_t)c.gemm_split * n * L->d_out * 4 : 0);
-  y.vpart = take((size_t)c.shrink_split * n * L->kmax * 4);
+  y.vpart = take(c.fused_dec ? 0 : (size_t)c.shrink_split * n * L->kmax * 4);
   y.v = take((size_t)n * L->kmax * esz);
   y.srow = take(c.scale_route == 3 ? (size_t)n * L->d_out * 4 : 0);
+  y.cnt = take(c.fused_dec ? 4 * (size_t)(L->d_out / 64) : 0);
   y.total = off;
   return y;
 }
@@ -1586,11 +1619,25 @@ struct SliceCtx {
 // width (that of the widest projection, when it divides every d_out), one
 // k-group count and one k range, chosen as for one projection but over the
 // combined grid (a split pinned on the first projection is kept).
+// The fused decode epilogue is a property of the group's launches (the
+// shrink's mode and the GEMM's): all projections take it or none does.
+void uniform_fused_dec(tpa_layer* const* Ls, int count, Config* cs, bool allowed) {
+  bool all = allowed;
+  for (int i = 0; i < count; ++i) all = all && cs[i].fused_dec;
+  for (int i = 0; i < count; ++i) {
+    cs[i].fused_dec = all ? 1 : 0;
+    cs[i].h_fp32 = Ls[i]->n_stack > 0 && !cs[i].fused && !cs[i].fused_dec;
+  }
+}
+
 void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
   for (int i = 0; i < count; ++i) cs[i] = choose_config(Ls[i], n);
   if (count < 2) return;
   for (int i = 0; i < count; ++i)
-    if (cs[i].gemm_path != cs[0].gemm_path || !decode_path(cs[i])) return;
+    if (cs[i].gemm_path != cs[0].gemm_path || !decode_path(cs[i])) {
+      uniform_fused_dec(Ls, count, cs, false);
+      return;
+    }
   const bool stream = cs[0].gemm_path == 2;
   int ref = 0;
   for (int i = 1; i < count; ++i)
@@ -1618,13 +1665,17 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
       if (wgs >= 200) break;
     }
   }
+  bool fits = stream && S == 3;
   for (int i = 0; i < count; ++i) {
     cs[i].gemm_nb = nb;
     cs[i].gemm_groups = G;
     cs[i].gemm_stages = S;
     cs[i].gemm_kc = std::min(kc, round_up(Ls[i]->d_in, 64 * (stream ? G : 1)));
     cs[i].gemm_split = (Ls[i]->d_in + cs[i].gemm_kc - 1) / cs[i].gemm_kc;
+    fits = fits && fused_dec_fits(Ls[i], n, cs[i]);
   }
+  // (a shrink capped for the fused epilogue stays valid without it)
+  uniform_fused_dec(Ls, count, cs, fits);
 }
 
 // Everything after the plan, for `count` projections that share it: the
@@ -1673,6 +1724,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     }
     sh[i].part_shared = nullptr;
     sh[i].kmax_shared = 0;
+    sh[i].borrows = 0;
     of[i] = tpa::OftArgs{};
     of[i].x = sl[i].x;
     of[i].oft_tiles = p.oft_tiles;
@@ -1688,15 +1740,41 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   // first projection's A_v and reads the same input computes no x·A_vᵀ of
   // its own; its reduction takes the first projection's partials and
   // applies its own d'.  Same bits as computing them again.
+  // The expand in the decode GEMM's epilogue (all projections of the group
+  // or none, by their configurations): the shrink then runs whole-k, and a
+  // launch before the GEMM clears its arrival counters (the shrink's or
+  // OFT's; with k whole in the GEMM no counter is read).
+  bool any_oft = false, all_unsplit = true;
+  for (int i = 0; i < count; ++i) {
+    any_oft = any_oft || oft[i];
+    all_unsplit = all_unsplit && sl[i].c.gemm_split == 1;
+  }
+  const bool fdec = sl[0].c.fused_dec && (any_term_all || any_oft || all_unsplit);
   for (int i = 1; i < count; ++i) {
     const tpa_layer* L = sl[i].L;
     if (term[i] && term[0] && L->n_vera > 0 && L0->n_vera > 0 && L->vera_At && L->vera_At == L0->vera_At &&
         sl[i].x == sl[0].x && L->r_v == L0->r_v && sh[i].split == sh[0].split && sh[i].kc == sh[0].kc) {
       sh[i].sh_ntiles = 0;
-      sh[i].part_shared = sh[0].part;
-      sh[i].kmax_shared = sh[0].kmax;
+      if (fdec) {
+        sh[i].borrows = 1;
+      } else {
+        sh[i].part_shared = sh[0].part;
+        sh[i].kmax_shared = sh[0].kmax;
+      }
     }
   }
+  int32_t* cnt[tpa::MAX_SLICES];
+  for (int i = 0; i < count; ++i)
+    cnt[i] = fdec && sl[i].c.gemm_split > 1 ? reinterpret_cast<int32_t*>(sl[i].w + sl[i].y.cnt) : nullptr;
+  bool cnt_cleared = false;
+  auto clear_counters = [&](tpa::PreSlice* ps) {
+    if (cnt_cleared) return;
+    for (int i = 0; i < count; ++i) {
+      ps[i].zero = cnt[i];
+      ps[i].zero_n = cnt[i] ? sl[i].L->d_out / (64 * sl[i].c.gemm_nb) : 0;
+    }
+    cnt_cleared = true;
+  };
 
   // 2. The shrink and OFT's rotation: one launch per OFT block size present
   //    (the shrink rides in the first), or one for the shrink alone.  With
@@ -1712,7 +1790,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   //    V and U, so nothing could overlap.  The second stream and its events
   //    are made on first use, outside graph capture (a captured forward
   //    before then runs on one stream; both orders give the same bits).
-  bool any_fused_cfg = false;
+  bool any_fused_cfg = fdec;
   for (int i = 0; i < count; ++i) any_fused_cfg = any_fused_cfg || sl[i].c.fused;
   const int ov_opt = L0->opt[TPA_OPT_OVERLAP];
   bool overlap = allow_side && any_term_all && !any_fused_cfg && ov_opt == 1;
@@ -1747,16 +1825,39 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     for (int i = 0; i < count; ++i) {
       of[i].block = kBs[b];
       ps[i] = tpa::make_pre_slice(!sh_done && term[i] ? &sh[i] : nullptr,
-                                  sl[i].L->n_oft_bs[b] ? &of[i] : nullptr);
+                                  sl[i].L->n_oft_bs[b] ? &of[i] : nullptr, fdec);
     }
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, kBs[b], ps, count, s));
+    if (fdec) clear_counters(ps);
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, kBs[b], ps, count, s, fdec));
     sh_done = true;
   }
   if (!sh_done && any_term_all) {
-    for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr);
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, s));
+    for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr, fdec);
+    if (fdec) clear_counters(ps);
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, s, fdec));
   }
   if (tpa_status st = stage(L0, 2, s)) return st;
+
+  auto expand_args = [&](int i) {
+    tpa_layer* L = sl[i].L;
+    const Config& c = sl[i].c;
+    tpa::ExpandArgs ea{};
+    ea.out = sl[i].out;
+    ea.hpart = nullptr;
+    ea.hsplit = c.gemm_split;
+    ea.tiles = p.tiles;
+    ea.tile_rows_w = p.tile_rows_w;
+    ea.slots = L->slots_dev;
+    ea.vera_Bt = L->vera_Bt;
+    ea.r_v = L->r_v;
+    ea.v = sl[i].w + sl[i].y.v;
+    ea.kmax = L->kmax;
+    ea.n = n;
+    ea.d_out = L->d_out;
+    ea.max_tiles = all_tile_bound(L, n, tile_rows, sl[i].y.max_tiles);
+    ea.apply_scale = c.scale_route == 0;
+    return ea;
+  };
 
   // 3. Base GEMM.  Decode path: one launch over the projections (they share
   //    the column-block width and k-groups), the shrink's split reduction
@@ -1781,7 +1882,15 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     g.part = reinterpret_cast<float*>(sl[i].w + sl[i].y.hpart);
     g.out = sl[i].out;
     gs[i].side = sh[i];
-    gs[i].has_side = term[i] && !overlap ? 1 : 0;
+    gs[i].has_side = term[i] && !overlap && !fdec ? 1 : 0;
+    gs[i].e = tpa::ExpandArgs{};
+    gs[i].pinfo = nullptr;
+    gs[i].cnt = nullptr;
+    if (fdec) {
+      gs[i].e = expand_args(i);
+      gs[i].pinfo = p.pinfo;
+      gs[i].cnt = cnt[i];
+    }
     if (c.gemm_path != sl[0].c.gemm_path || !decode_path(c) || c.gemm_nb != sl[0].c.gemm_nb ||
         c.gemm_groups != sl[0].c.gemm_groups || (c.gemm_path == 2 && c.gemm_stages != sl[0].c.gemm_stages))
       one_launch = false;
@@ -1797,14 +1906,15 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     TPA_HIP(tpa::launch_gemm_big(dtype, gs, count, s));  // carries the shrinks' reductions
   } else if (one_launch) {
     if (sl[0].c.gemm_path == 2)
-      TPA_HIP(tpa::launch_gemm_stream(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, sl[0].c.gemm_stages, gs, count, s));
+      TPA_HIP(tpa::launch_gemm_stream(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, sl[0].c.gemm_stages, gs, count, s,
+                                      fdec));
     else
       TPA_HIP(tpa::launch_gemm_skinny(dtype, sl[0].c.gemm_nb, sl[0].c.gemm_groups, gs, count, s));
   } else {
     for (int i = 0; i < count; ++i) {
       const Config& c = sl[i].c;
       if (c.gemm_path == 2) {
-        TPA_HIP(tpa::launch_gemm_stream(dtype, c.gemm_nb, c.gemm_groups, c.gemm_stages, &gs[i], 1, s));
+        TPA_HIP(tpa::launch_gemm_stream(dtype, c.gemm_nb, c.gemm_groups, c.gemm_stages, &gs[i], 1, s, fdec));
       } else if (c.gemm_path == 0) {
         TPA_HIP(tpa::launch_gemm_skinny(dtype, c.gemm_nb, c.gemm_groups, &gs[i], 1, s));
       } else {
@@ -1826,7 +1936,12 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   if (overlap) TPA_HIP(hipStreamWaitEvent(s, L0->ev_join, 0));
   if (tpa_status st = stage(L0, 3, s)) return st;
 
-  // 4. Expand (with the comparison routes' separate scale passes).
+  // 4. Expand (with the comparison routes' separate scale passes), unless
+  //    the GEMM's epilogue ran it.
+  if (fdec) {
+    if (tpa_status st = stage(L0, 4, s)) return st;
+    return stage(L0, 5, s);
+  }
   tpa::ExpandArgs e[tpa::MAX_SLICES];
   tpa::ScaleArgs sc[tpa::MAX_SLICES];
   for (int i = 0; i < count; ++i) {
@@ -1847,21 +1962,8 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       TPA_HIP(tpa::launch_scale_pass(dtype, 1, sc[i], s));
       h_in_out = true;
     }
-    e[i] = tpa::ExpandArgs{};
-    e[i].out = sl[i].out;
+    e[i] = expand_args(i);
     e[i].hpart = h_in_out ? nullptr : reinterpret_cast<const float*>(sl[i].w + sl[i].y.hpart);
-    e[i].hsplit = c.gemm_split;
-    e[i].tiles = p.tiles;
-    e[i].tile_rows_w = p.tile_rows_w;
-    e[i].slots = L->slots_dev;
-    e[i].vera_Bt = L->vera_Bt;
-    e[i].r_v = L->r_v;
-    e[i].v = sl[i].w + sl[i].y.v;
-    e[i].kmax = L->kmax;
-    e[i].n = n;
-    e[i].d_out = L->d_out;
-    e[i].max_tiles = all_tile_bound(L, n, tile_rows, sl[i].y.max_tiles);
-    e[i].apply_scale = c.scale_route == 0;
     if (c.fused) {
       // The shrink's reduction as a launch of its own (V / U must be final
       // before the GEMM's epilogue reads them), then the GEMM with the
@@ -2188,7 +2290,10 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   out->gemm_groups = c.gemm_groups;
   out->gemm_stages = c.gemm_path == 2 || c.gemm_path == 3 ? c.gemm_stages : 0;
   out->gemm_tile = c.gemm_path == 3 ? c.gemm_tile : 0;
-  out->fused_expand = c.fused;
+  // The decode epilogue also needs a launch before the GEMM to clear its
+  // counters: a term, an OFT rotation, or k not split.
+  const bool pre = L->n_owned > 0 || L->n_vera > 0 || L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
+  out->fused_expand = c.fused || (c.fused_dec && (pre || c.gemm_split == 1));
   return TPA_OK;
 }
 

@@ -160,6 +160,26 @@ __device__ __forceinline__ int perm_col(int i, int b) {
   return 4 * NB * (i >> 2) + 4 * b + (i & 3);
 }
 
+// Barrier that waits for this wave's LDS operations only (the callers
+// exchange data through LDS, never through global memory).
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave in registers: four
+// row shifts (within each 16-lane row), then the last lane of row 0 and 2
+// added into rows 1 and 3, then lane 31 into rows 2 and 3.  Lanes whose
+// source lies outside the row keep the identity (0).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Term class of a slot, as ordered by the row plan.
 enum { CLS_OWNED = 0, CLS_SHARED = 1, CLS_NONE = 2 };
 

@@ -215,6 +215,280 @@ __global__ __launch_bounds__(256 * G) void gemm_skinny_kernel(Slices<GemmSlice> 
 // Within a 128-byte LDS row the eight 16-byte chunks are permuted (swz in
 // common.h) so that the fragment reads hit distinct bank groups.
 
+// Fused epilogue of the streamed decode GEMM: the expand (Scute paper,
+// §2 "The LoRA schedule": the expand reads h, adds V B and writes the
+// tile; §4.1 route one and §5.2: s applied as the tile finishes; route two:
+// the shared factor's term over rows of any tenant, times e) run by the
+// work-group that completes a column tile, while h is still on chip.
+//
+// With k split, each work-group writes its split's fp32 sum, makes it
+// visible at device scope (release fence) and counts itself in on the
+// tile's counter; the one that brings the count to the split count
+// (acquire fence) finishes the tile.  Nobody waits on anybody: the others
+// have nothing left to do.  The finishing work-group builds tables in LDS
+// (each row's plan position, class and s / b / e; each term tile's rows,
+// rank and factor; the MFMA k steps over all term tiles), parks its own
+// split in LDS, and then every thread takes runs of 4 columns of one row:
+// the splits added in split order (its own from LDS), times s, plus b,
+// exactly as the expand adds them, back into LDS with e beside it.  Group 0
+// computes the term in the GEMM's register layout: for each k step of a
+// tile, a = the factor's rows at the wave's output columns (B' or B_v,
+// stored [d_out][K]), b = V (or U) of those of the wave's rows that lie in
+// the tile, zero for the others, so a row collects its own tile's products
+// in k order and exact zeros from every other tile (the expand's sums), and
+// y = (h ⊙ s + b) + term ⊙ e is written once.
+struct EpiLds {
+  int wsum, rpos, rs, rb, re, tinfo, tbt, steps, end;
+};
+// Bytes of the rings the epilogue uses: the k-groups' sums, then h and e
+// (16·MB rows of 64·NB + 4 floats each).
+__host__ __device__ constexpr size_t epi_ring_bytes(int mb, int nb, int g) {
+  return (size_t)(g - 1) * 4 * nb * mb * 1024 + (size_t)2 * 16 * mb * (64 * nb + 4) * 4;
+}
+__host__ __device__ inline EpiLds epi_lds_layout(int nrows, int max_tiles, int steps) {
+  EpiLds o;
+  o.wsum = 16;  // after the arrival flag; one word per wave (at most 16)
+  o.rpos = 80;
+  o.rs = o.rpos + ((4 * nrows + 15) & ~15);
+  o.rb = o.rs + 8 * nrows;
+  o.re = o.rb + 8 * nrows;
+  o.tinfo = (o.re + 8 * nrows + 15) & ~15;
+  o.tbt = o.tinfo + 16 * max_tiles;
+  o.steps = o.tbt + 8 * max_tiles;
+  o.end = o.steps + 4 * steps;
+  return o;
+}
+
+// ring: the work-group's LDS rings (free once the k loop is done); its
+// first red_bytes hold the k-groups' sums until group 0 has added them.
+// tab: the tables, after the rings.
+template <typename T, int MB, int NB, int G>
+__device__ __forceinline__ void stream_epilogue(const GemmSlice& sl, const f32x4 (&acc)[NB][MB], int ks,
+                                                int col_tile, int col0, unsigned char* ring, unsigned char* tab,
+                                                int grp, int wave, int lane) {
+  typedef typename Frag<T>::V Vt;
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  constexpr int NT = 256 * G;
+  constexpr int UE = 4;                      // k steps whose loads are issued together
+  constexpr int PITCH = 64 * NB + 4;         // floats per LDS row of h (padded against bank conflicts)
+  constexpr int UNITS = 16 * MB * 16 * NB;   // runs of 4 columns in the tile
+  constexpr int UPT = (UNITS + NT - 1) / NT; // per thread
+  // splits whose loads are issued together: 16 loads of 16 bytes per thread
+  constexpr int SPB = UPT >= 16 ? 1 : (16 / UPT > 8 ? 8 : 16 / UPT);
+  const BaseGemmArgs& a = sl.g;
+  const ExpandArgs& e = sl.e;
+  const int tid = (int)threadIdx.x;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int n = a.n;
+  int* flag = reinterpret_cast<int*>(tab);
+  float* hs = reinterpret_cast<float*>(ring + (size_t)(G - 1) * 4 * NB * MB * 1024);  // [16·MB][PITCH]
+  float* es = hs + 16 * MB * PITCH;                                                    // [16·MB][PITCH]
+
+  // 1. Split sum out, arrival in.
+  if (a.split > 1) {
+    if (grp == 0) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int row = 16 * m + i16;
+        if (row >= n) continue;
+        float* dst = a.part + ((size_t)ks * n + row) * a.d_out + col0 + 16 * NB * wave + 4 * NB * g;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(dst + 4 * b) = acc[b][m];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0)
+      *flag = __hip_atomic_fetch_add(sl.cnt + col_tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+              a.split - 1;
+    __syncthreads();
+    if (!*flag) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+
+  // 2. Tables in LDS, and this split's sum parked beside them.
+  const EpiLds o = epi_lds_layout(16 * MB, e.max_tiles, 0);
+  int* wsum = reinterpret_cast<int*>(tab + o.wsum);
+  int* rpos = reinterpret_cast<int*>(tab + o.rpos);
+  const float** rs = reinterpret_cast<const float**>(tab + o.rs);
+  const float** rb = reinterpret_cast<const float**>(tab + o.rb);
+  const float** re = reinterpret_cast<const float**>(tab + o.re);
+  int4* tinfo = reinterpret_cast<int4*>(tab + o.tinfo);
+  const void** tbt = reinterpret_cast<const void**>(tab + o.tbt);
+  int* steps = reinterpret_cast<int*>(tab + o.steps);
+  for (int p = tid; p < n; p += NT) {
+    const int w = gload<int>(sl.pinfo + p);
+    const int row = w & 0xFFFF;
+    const SlotDev* sd = e.slots + ((unsigned)w >> 16);
+    rpos[row] = p | (gload<int>(&sd->cls) << 16);
+    rs[row] = gload<const float*>(&sd->s);
+    rb[row] = gload<const float*>(&sd->b);
+    re[row] = gload<const float*>(&sd->e);
+  }
+  int nst = 0;
+  if (tid < e.max_tiles) {
+    const int4 hd = *reinterpret_cast<const int4*>(e.tiles + 4 * tid);
+    int K = 0;
+    const void* bt = nullptr;
+    if (hd.z == CLS_OWNED) {
+      K = gload<int>(&e.slots[hd.w].rank);
+      bt = gload<const void*>(&e.slots[hd.w].Bt);
+    } else if (hd.z == CLS_SHARED) {
+      K = e.r_v;
+      bt = e.vera_Bt;
+    }
+    tinfo[tid] = make_int4(hd.x, hd.y, K, 0);
+    tbt[tid] = bt;
+    nst = (K + 31) / 32;
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        *reinterpret_cast<f32x4*>(hs + (16 * m + i16) * PITCH + 16 * NB * wave + 4 * NB * g + 4 * b) = acc[b][m];
+  }
+  const int incl = (int)wave_incl_scan((uint32_t)nst);
+  if (lane == 63) wsum[tid >> 6] = incl;
+  lds_barrier();
+  int off = incl - nst, total = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int sw = wsum[w];
+    if (w < (tid >> 6)) off += sw;
+    total += sw;
+  }
+  for (int j = 0; j < nst; ++j) steps[off + j] = (tid << 8) | j;
+
+  // 3. Every thread: runs of 4 columns, h = the splits in split order, then
+  //    h ⊙ s + b into hs and e (1 for rows without a shared term) into es.
+  f32x4 hv[UPT], sv[UPT], bv[UPT], ev[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int unit = tid + u * NT;
+    const int row = unit / (16 * NB), c4 = unit % (16 * NB);
+    hv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sv[u] = f32x4{1.f, 1.f, 1.f, 1.f};
+    bv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ev[u] = f32x4{1.f, 1.f, 1.f, 1.f};
+    if (unit < UNITS && row < n) {
+      const int colg = col0 + 4 * c4;
+      const float* sp = rs[row];
+      const float* bq = rb[row];
+      const float* ep = re[row];
+      if (sp) sv[u] = gload<f32x4>(sp + colg);
+      if (bq) bv[u] = gload<f32x4>(bq + colg);
+      if ((rpos[row] >> 16) == CLS_SHARED && ep) ev[u] = gload<f32x4>(ep + colg);
+    }
+  }
+  for (int s0 = 0; s0 < a.split; s0 += SPB) {
+    f32x4 ld[SPB][UPT];
+#pragma unroll
+    for (int q = 0; q < SPB; ++q)
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int unit = tid + u * NT;
+        const int row = unit / (16 * NB), c4 = unit % (16 * NB);
+        const int sp = s0 + q;
+        ld[q][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (unit < UNITS && row < n && sp < a.split) {
+          if (sp == ks)
+            ld[q][u] = *reinterpret_cast<const f32x4*>(hs + row * PITCH + 4 * c4);
+          else
+            ld[q][u] = gload<f32x4>(a.part + ((size_t)sp * n + row) * a.d_out + col0 + 4 * c4);
+        }
+      }
+#pragma unroll
+    for (int q = 0; q < SPB; ++q) {
+      if (s0 + q >= a.split) break;
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) hv[u] += ld[q][u];
+    }
+  }
+  lds_barrier();  // every read of the parked split is done
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    const int unit = tid + u * NT;
+    if (unit >= UNITS) continue;
+    const int row = unit / (16 * NB), c4 = unit % (16 * NB);
+    f32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = hv[u][j] * sv[u][j] + bv[u][j];
+    *reinterpret_cast<f32x4*>(hs + row * PITCH + 4 * c4) = y;
+    *reinterpret_cast<f32x4*>(es + row * PITCH + 4 * c4) = ev[u];
+  }
+  lds_barrier();
+  if (grp != 0) return;
+
+  // 4. Group 0: the term over every k step of every term tile, in the
+  //    GEMM's layout (lane: columns colw .. colw + 4·NB of rows 16m + i16).
+  int pos[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int row = 16 * m + i16;
+    pos[m] = row < n ? (rpos[row] & 0xFFFF) : -1;
+  }
+  f32x4 tacc[NB][MB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) tacc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const T* V = static_cast<const T*>(e.v);
+  int acol[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acol[b] = col0 + 16 * NB * wave + perm_col<NB>(i16, b);
+  for (int j0 = 0; j0 < total; j0 += UE) {
+    Vt af[UE][NB], bf[UE][MB];
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int j = j0 + u;
+      int4 ti = make_int4(0, 0, 0, 0);
+      const T* bt = nullptr;
+      int kk = 0;
+      if (j < total) {
+        const int sw = steps[j];
+        ti = tinfo[sw >> 8];
+        bt = static_cast<const T*>(tbt[sw >> 8]);
+        kk = 32 * (sw & 255) + 8 * g;
+      }
+      const bool ok = kk < ti.z;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) af[u][b] = ok ? load_frag<T>(bt + (size_t)acol[b] * ti.z + kk) : zero_frag<T>();
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        bf[u][m] = (ok && pos[m] >= ti.x && pos[m] < ti.y) ? load_frag<T>(V + (size_t)pos[m] * e.kmax + kk)
+                                                            : zero_frag<T>();
+    }
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      if (j0 + u >= total) break;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int m = 0; m < MB; ++m) tacc[b][m] = mma(tacc[b][m], af[u][b], bf[u][m]);
+    }
+  }
+
+  // 5. y = (h ⊙ s + b) + term ⊙ e, written once.
+  T* out = static_cast<T*>(e.out);
+  const int cl = 16 * NB * wave + 4 * NB * g;  // column within the tile
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int row = 16 * m + i16;
+    if (row >= n) continue;
+    T* dst = out + (size_t)row * e.d_out + col0 + cl;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const f32x4 hsb = *reinterpret_cast<const f32x4*>(hs + row * PITCH + cl + 4 * b);
+      const f32x4 e4 = *reinterpret_cast<const f32x4*>(es + row * PITCH + cl + 4 * b);
+      f32x4 y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = hsb[j] + tacc[b][m][j] * e4[j];
+      *reinterpret_cast<T4*>(dst + 4 * b) = T4{to_t<T>(y[0]), to_t<T>(y[1]), to_t<T>(y[2]), to_t<T>(y[3])};
+    }
+  }
+}
+
 template <int NB>
 constexpr int log2_nb() {
   return NB == 1 ? 0 : NB == 2 ? 1 : 2;
@@ -225,7 +499,7 @@ constexpr size_t stream_stage_bytes() {
   return (size_t)(64 * NB + 16 * MB) * 128;
 }
 
-template <typename T, int MB, int NB, int G, int S>
+template <typename T, int MB, int NB, int G, int S, bool EPI>
 __global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> t) {
   typedef typename Frag<T>::V Vt;
   constexpr int WROWS = 64 * NB;             // W rows (output columns) per work-group
@@ -362,13 +636,23 @@ __global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> 
         for (int m = 0; m < MB; ++m) red[(((grp - 1) * 4 + wave) * NB * MB + b * MB + m) * 64 + lane] = acc[b][m];
     }
     __syncthreads();
-    if (grp > 0) return;
+    if (!EPI && grp > 0) return;  // with the fused epilogue every wave stays for its barriers
+    if (grp == 0) {
 #pragma unroll
-    for (int q = 1; q < G; ++q)
+      for (int q = 1; q < G; ++q)
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int m = 0; m < MB; ++m) acc[b][m] += red[(((q - 1) * 4 + wave) * NB * MB + b * MB + m) * 64 + lane];
+          for (int m = 0; m < MB; ++m)
+            acc[b][m] += red[(((q - 1) * 4 + wave) * NB * MB + b * MB + m) * 64 + lane];
+    }
+  }
+  if constexpr (EPI) {
+    static_assert(epi_ring_bytes(MB, NB, G) <= (size_t)G * S * STAGE,
+                  "the epilogue's h and e fit in the rings beside the k-groups' sums");
+    stream_epilogue<T, MB, NB, G>(t.s[si], acc, ks, local % col_tiles, col0, smem, smem + (size_t)G * S * STAGE,
+                                  grp, wave, lane);
+    return;
   }
 
   // The lane holds columns col0 + 16·NB·wave + 4·NB·g + [0, 4·NB) of row
@@ -820,13 +1104,23 @@ hipError_t skinny_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
 }
 
 template <typename T, int MB, int NB, int G, int S>
-hipError_t stream_launch(const Slices<GemmSlice>& t, hipStream_t s) {
+hipError_t stream_launch(const Slices<GemmSlice>& t, hipStream_t s, size_t epi_bytes) {
   constexpr size_t lds = (size_t)G * S * stream_stage_bytes<MB, NB>();
   if constexpr (lds > GEMM_STREAM_MAX_LDS) {
     return hipErrorInvalidValue;
   } else {
-    hipLaunchKernelGGL((gemm_stream_kernel<T, MB, NB, G, S>), dim3((unsigned)t.first[t.count]), dim3(256 * G), lds,
-                       s, t);
+    if (epi_bytes) {
+      if constexpr (S == 3 && MB <= 4 && epi_ring_bytes(MB, NB, G) <= lds) {
+        if (lds + epi_bytes > GEMM_STREAM_MAX_LDS) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_stream_kernel<T, MB, NB, G, S, true>), dim3((unsigned)t.first[t.count]),
+                           dim3(256 * G), lds + epi_bytes, s, t);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
+    hipLaunchKernelGGL((gemm_stream_kernel<T, MB, NB, G, S, false>), dim3((unsigned)t.first[t.count]), dim3(256 * G),
+                       lds, s, t);
     return hipGetLastError();
   }
 }
@@ -835,7 +1129,7 @@ hipError_t stream_launch(const Slices<GemmSlice>& t, hipStream_t s) {
 int stream_mb(int n) { return n <= 16 ? 1 : n <= 32 ? 2 : n <= 64 ? 4 : n <= 128 ? 8 : 16; }
 
 template <typename T, int G, int S>
-hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s) {
+hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s, size_t epi_bytes) {
   const int mb = stream_mb(sl[0].g.n);
   Slices<GemmSlice> t{};
   t.count = count;
@@ -849,7 +1143,7 @@ hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
   }
   for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
 #define TPA_ST(MBV, NBV) \
-  if (mb == MBV && nb == NBV) return stream_launch<T, MBV, NBV, G, S>(t, s);
+  if (mb == MBV && nb == NBV) return stream_launch<T, MBV, NBV, G, S>(t, s, epi_bytes);
   TPA_ST(1, 1) TPA_ST(2, 1) TPA_ST(4, 1) TPA_ST(8, 1) TPA_ST(16, 1)
   TPA_ST(1, 2) TPA_ST(2, 2) TPA_ST(4, 2) TPA_ST(8, 2) TPA_ST(16, 2)
   TPA_ST(1, 4) TPA_ST(2, 4) TPA_ST(4, 4)
@@ -858,11 +1152,12 @@ hipError_t stream_dispatch(int nb, const GemmSlice* sl, int count, hipStream_t s
 }
 
 template <typename T>
-hipError_t stream_dtype(int nb, int groups, int stages, const GemmSlice* sl, int count, hipStream_t s) {
-  if (groups == 1 && stages == 3) return stream_dispatch<T, 1, 3>(nb, sl, count, s);
-  if (groups == 1 && stages == 4) return stream_dispatch<T, 1, 4>(nb, sl, count, s);
-  if (groups == 1 && stages == 6) return stream_dispatch<T, 1, 6>(nb, sl, count, s);
-  if (groups == 2 && stages == 3) return stream_dispatch<T, 2, 3>(nb, sl, count, s);
+hipError_t stream_dtype(int nb, int groups, int stages, const GemmSlice* sl, int count, hipStream_t s,
+                        size_t epi_bytes) {
+  if (groups == 1 && stages == 3) return stream_dispatch<T, 1, 3>(nb, sl, count, s, epi_bytes);
+  if (groups == 1 && stages == 4) return stream_dispatch<T, 1, 4>(nb, sl, count, s, epi_bytes);
+  if (groups == 1 && stages == 6) return stream_dispatch<T, 1, 6>(nb, sl, count, s, epi_bytes);
+  if (groups == 2 && stages == 3) return stream_dispatch<T, 2, 3>(nb, sl, count, s, epi_bytes);
   return hipErrorInvalidValue;
 }
 
@@ -899,9 +1194,19 @@ size_t gemm_stream_lds(int n, int nb, int groups, int stages) {
   return (size_t)groups * stages * (64 * nb + 16 * mb) * 128;
 }
 
+size_t gemm_stream_epi_lds(int n, int max_tiles, int steps) {
+  return (size_t)epi_lds_layout(16 * stream_mb(n), max_tiles, steps).end;
+}
+
+bool gemm_stream_epi_ok(int n, int nb, int groups, int stages) {
+  const int mb = stream_mb(n);
+  return n <= 64 && stages == 3 && epi_ring_bytes(mb, nb, groups) <= gemm_stream_lds(n, nb, groups, stages);
+}
+
 hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const GemmSlice* slices, int count,
-                              hipStream_t s) {
+                              hipStream_t s, bool epi) {
   if (count < 1 || count > MAX_SLICES || (nb != 1 && nb != 2 && nb != 4)) return hipErrorInvalidValue;
+  size_t epi_bytes = 0;
   for (int i = 0; i < count; ++i) {
     const BaseGemmArgs& a = slices[i].g;
     // Whole 64-element slices in every k range, whole column tiles, rows
@@ -909,10 +1214,23 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
     if (a.n <= 0 || a.n > 256 || a.n != slices[0].g.n || a.kc <= 0 || a.kc % 64 || a.d_in % 64 ||
         a.d_out % (64 * nb) || (long)a.split * a.kc < a.d_in)
       return hipErrorInvalidValue;
+    if (epi) {
+      // The epilogue's tables: every row, every entry of the tile list (one
+      // thread each) and the k steps of the largest factor per entry.
+      const ExpandArgs& e = slices[i].e;
+      if (!gemm_stream_epi_ok(a.n, nb, groups, stages) || slices[i].has_side || !slices[i].pinfo || !e.out || !e.tiles ||
+          !e.slots || !e.apply_scale || e.n != a.n || e.d_out != a.d_out || e.max_tiles < 0 ||
+          e.max_tiles > 256 * groups || (a.split > 1 && (!slices[i].cnt || !a.part)))
+        return hipErrorInvalidValue;
+      const int kcap = std::max(e.kmax, e.r_v);
+      if (kcap > 32 * 255) return hipErrorInvalidValue;  // a step names its k step in 8 bits
+      epi_bytes = std::max(epi_bytes, gemm_stream_epi_lds(a.n, e.max_tiles, e.max_tiles * ((kcap + 31) / 32)));
+    }
   }
-  if (gemm_stream_lds(slices[0].g.n, nb, groups, stages) > GEMM_STREAM_MAX_LDS) return hipErrorInvalidValue;
-  if (dtype == 1) return stream_dtype<f16>(nb, groups, stages, slices, count, s);
-  if (dtype == 2) return stream_dtype<bf16>(nb, groups, stages, slices, count, s);
+  if (gemm_stream_lds(slices[0].g.n, nb, groups, stages) + epi_bytes > GEMM_STREAM_MAX_LDS)
+    return hipErrorInvalidValue;
+  if (dtype == 1) return stream_dtype<f16>(nb, groups, stages, slices, count, s, epi_bytes);
+  if (dtype == 2) return stream_dtype<bf16>(nb, groups, stages, slices, count, s, epi_bytes);
   return hipErrorInvalidValue;
 }
 

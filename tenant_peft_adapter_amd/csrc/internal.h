@@ -125,6 +125,10 @@ struct ShrinkArgs {
   // them; row stride kmax_shared), else from part.
   const float* part_shared;
   int32_t kmax_shared;
+  // Whole-k shrink (launch_pre with whole): this slice takes its shared-term
+  // rows' x·A_vᵀ from the launch's first slice, whose work-groups write
+  // this slice's U with this slice's d'.
+  int32_t borrows;
 };
 // One slice of the launch before the base GEMM: the shrink's items and/or
 // OFT's rotation of its tiles for the launch's block size.
@@ -132,11 +136,42 @@ struct PreSlice {
   ShrinkArgs sh;
   OftArgs of;
   int32_t n_shrink_wg, n_oft_wg, oft_bg;
+  // Arrival counters of the fused decode GEMM that follows (one word per
+  // column tile), cleared by the launch's first work-group; may be null.
+  int32_t* zero;
+  int32_t zero_n;
 };
 // Fills a PreSlice; sh / of may be null (that part gets no work-groups).
-PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of);
+// whole: the shrink's layout for launch_pre's whole-k mode.
+PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of, bool whole = false);
 // bs: OFT block size of the slices' OFT parts (0 when no slice has one).
-hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t stream);
+// whole (f16 / bf16, 16-row tiles, sh.split <= PRE_WHOLE_WAVES): one
+// work-group of PRE_WHOLE_WAVES waves per shrink item (plan tile, 16 factor
+// columns), wave w on the w-th k range of kc; the waves' sums meet in LDS
+// and are added in wave order (the order the reduce pass adds splits in),
+// so V and U are final when the launch ends and no partials are written.
+constexpr int PRE_WHOLE_WAVES = 16;
+hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t stream,
+                      bool whole = false);
+
+// out[row] = h[row] ⊙ s + b + V[p] B'ᵀ (owned tile) or (U[p] B_vᵀ) ⊙ e
+// (shared tile), for row = perm[p].  h is read from `out` (in place, layer
+// type) or summed from `hpart` (fp32 split-K partials, fixed order).
+struct ExpandArgs {
+  void* out;
+  const float* hpart;      // null: read h from out
+  int32_t hsplit;
+  const int32_t* tiles;    // padded with kind -1 to max_tiles
+  const int32_t* tile_rows_w;  // row words per tile (16·MB each)
+  const SlotDev* slots;
+  const void* vera_Bt;     // [d_out][r_v]
+  int32_t r_v;
+  const void* v;           // shrink output [n][kmax], layer type, by plan position
+  int32_t kmax;
+  int32_t n, d_out;
+  int32_t max_tiles;
+  int32_t apply_scale;     // 0: leave s and b to a separate pass
+};
 
 // One slice of a decode base-GEMM launch; with has_side, work-groups after
 // the slice's GEMM work-groups run the shrink's split reduction.
@@ -144,6 +179,14 @@ struct GemmSlice {
   BaseGemmArgs g;
   ShrinkArgs side;
   int32_t has_side;
+  // Streamed decode GEMM with the expand in its epilogue (launch_gemm_stream
+  // with epi): the expand's arguments (out, tiles, slots, vera_Bt, r_v, v,
+  // kmax, n, d_out; max_tiles entries of the tile list are read), the
+  // plan's pinfo, and one arrival counter per column tile (zero at launch;
+  // the last of a tile's split work-groups to arrive finishes it).
+  ExpandArgs e;
+  const int32_t* pinfo;
+  int32_t* cnt;
 };
 // Work-groups of `threads` threads that a slice's split reduction takes.
 inline int side_workgroups(const GemmSlice& sl, int threads) {
@@ -166,30 +209,22 @@ hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& slice, hipSt
 // Several slices (projections of one input, same n and split) may share
 // the launch.
 hipError_t launch_gemm_big(int dtype, const GemmSlice* slices, int count, hipStream_t stream);
+// epi: the expand runs in the epilogue (every slice's e, pinfo and cnt set;
+// n <= 64, 3 stages, V and U final before the launch, s applied there: the
+// e.apply_scale route); out is then written once and no partials are read
+// back by another launch.
 hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const GemmSlice* slices, int count,
-                              hipStream_t stream);
+                              hipStream_t stream, bool epi = false);
+// Bytes of LDS the fused epilogue adds after the rings, for n rows, a tile
+// list of max_tiles entries and at most `steps` MFMA k steps over it.
+size_t gemm_stream_epi_lds(int n, int max_tiles, int steps);
+// Whether the fused epilogue exists for this shape (n <= 64, 3 stages, its
+// h and e fit in the rings).
+bool gemm_stream_epi_ok(int n, int nb, int groups, int stages);
 // The shrink's split reduction on its own (when the GEMM cannot carry it).
 hipError_t launch_shrink_reduce(int dtype, const ShrinkArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- expand --
-// out[row] = h[row] ⊙ s + b + V[p] B'ᵀ (owned tile) or (U[p] B_vᵀ) ⊙ e
-// (shared tile), for row = perm[p].  h is read from `out` (in place, layer
-// type) or summed from `hpart` (fp32 split-K partials, fixed order).
-struct ExpandArgs {
-  void* out;
-  const float* hpart;      // null: read h from out
-  int32_t hsplit;
-  const int32_t* tiles;    // padded with kind -1 to max_tiles
-  const int32_t* tile_rows_w;  // row words per tile (16·MB each)
-  const SlotDev* slots;
-  const void* vera_Bt;     // [d_out][r_v]
-  int32_t r_v;
-  const void* v;           // shrink output [n][kmax], layer type, by plan position
-  int32_t kmax;
-  int32_t n, d_out;
-  int32_t max_tiles;
-  int32_t apply_scale;     // 0: leave s and b to a separate pass
-};
 // Every slice must have hpart set, or every slice must have it null.
 hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int count, hipStream_t stream);
 

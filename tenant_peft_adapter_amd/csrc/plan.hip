@@ -41,24 +41,6 @@ __device__ __forceinline__ int key_slot(uint32_t k) { return (int)((k >> 16) & 0
 __device__ __forceinline__ int key_rot(uint32_t k) { return (int)((k >> ROW_BITS) & 1); }
 __device__ __forceinline__ int key_row(uint32_t k) { return (int)(k & ((1u << ROW_BITS) - 1)); }
 
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave in registers: four
-// row shifts (within each 16-lane row), then the last lane of row 0 and 2
-// added into rows 1 and 3, then lane 31 into rows 2 and 3.  Lanes whose
-// source lies outside the row keep the identity (0).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
-
 // Exclusive prefix sum over a work-group of T threads; the total goes to
 // *total.  `scratch` holds T / 64 ints; callers may run scans back to back.
 template <int T>

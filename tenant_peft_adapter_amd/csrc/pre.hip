@@ -8,7 +8,9 @@
 // three (input transform in a pass of its own before the shared GEMM).
 //
 // Grid: first the shrink's work-groups (4 independent waves each, one item
-// per wave), then OFT's (one OFT tile x 16 blocks per work-group).
+// per wave; or, in whole-k mode, one item per work-group of 16 waves that
+// also adds the k ranges' sums), then OFT's (one OFT tile x 16 blocks per
+// work-group).
 #include "oft_impl.h"
 #include "shrink_impl.h"
 
@@ -33,6 +35,49 @@ __global__ __launch_bounds__(THREADS) void pre_kernel(Slices<PreSlice> t) {
     const int o = local - ps.n_shrink_wg;
     oft_impl::oft_part<T, MB, (BS == 0 ? 16 : BS)>(ps.of, o / ps.oft_bg, o % ps.oft_bg, wave, lane);
   }
+}
+
+// Whole-k mode (16-row tiles): one work-group of PRE_WHOLE_WAVES waves per
+// shrink item, then OFT's work-groups (one block per wave).  The launch's
+// first work-group also clears the arrival counters of the fused GEMM that
+// follows it on the stream.
+template <typename T, int BS>
+__global__ __launch_bounds__(64 * PRE_WHOLE_WAVES) void pre_whole_kernel(Slices<PreSlice> t) {
+  __shared__ f32x4 red[PRE_WHOLE_WAVES * 64];
+  if (blockIdx.x == 0) {
+    for (int j = 0; j < t.count; ++j) {
+      int32_t* z = t.s[j].zero;
+      if (!z) continue;
+      for (int i = (int)threadIdx.x; i < t.s[j].zero_n; i += 64 * PRE_WHOLE_WAVES) z[i] = 0;
+    }
+  }
+  const int si = slice_of(t, (int)blockIdx.x);
+  const PreSlice& ps = t.s[si];
+  const int local = (int)blockIdx.x - t.first[si];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (local < ps.n_shrink_wg) {
+    shrink_impl::shrink_whole<T, PRE_WHOLE_WAVES>(t, si, local, wave, lane, red);
+    return;
+  }
+  if (BS != 0) {
+    const int o = local - ps.n_shrink_wg;
+    oft_impl::oft_part<T, 1, (BS == 0 ? 16 : BS), PRE_WHOLE_WAVES>(ps.of, o / ps.oft_bg, o % ps.oft_bg, wave, lane);
+  }
+}
+
+template <typename T>
+hipError_t pre_whole_bs(int bs, const Slices<PreSlice>& t, hipStream_t s) {
+  const dim3 grid((unsigned)t.first[t.count]);
+  if (grid.x == 0) return hipSuccess;
+  const dim3 block(64 * PRE_WHOLE_WAVES);
+  switch (bs) {
+    case 0: hipLaunchKernelGGL((pre_whole_kernel<T, 0>), grid, block, 0, s, t); break;
+    case 16: hipLaunchKernelGGL((pre_whole_kernel<T, 16>), grid, block, 0, s, t); break;
+    case 32: hipLaunchKernelGGL((pre_whole_kernel<T, 32>), grid, block, 0, s, t); break;
+    case 64: hipLaunchKernelGGL((pre_whole_kernel<T, 64>), grid, block, 0, s, t); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename T, int MB>
@@ -63,13 +108,18 @@ __global__ __launch_bounds__(THREADS) void shrink_reduce_kernel(ShrinkArgs a) {
 
 }  // namespace
 
-PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of) {
+PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of, bool whole) {
   PreSlice ps{};
   ps.oft_bg = 1;
   if (sh) {
     ps.sh = *sh;
-    const long items = ((long)sh->own_tiles * sh->own_nblk + (long)sh->sh_ntiles * sh->sh_nblk) * sh->split;
-    ps.n_shrink_wg = (int)((items + THREADS / 64 - 1) / (THREADS / 64));
+    const long tiles_x_blocks = (long)sh->own_tiles * sh->own_nblk + (long)sh->sh_ntiles * sh->sh_nblk;
+    if (whole) {
+      ps.n_shrink_wg = (int)tiles_x_blocks;
+    } else {
+      const long items = tiles_x_blocks * sh->split;
+      ps.n_shrink_wg = (int)((items + THREADS / 64 - 1) / (THREADS / 64));
+    }
   }
   if (of) {
     ps.of = *of;
@@ -79,8 +129,16 @@ PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of) {
   return ps;
 }
 
-hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t s) {
+hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t s,
+                      bool whole) {
   if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
+  if (whole) {
+    if (tile_rows != 16 || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
+    for (int i = 0; i < count; ++i)
+      if (slices[i].n_shrink_wg > 0 &&
+          (slices[i].sh.split > PRE_WHOLE_WAVES || (long)slices[i].sh.split * slices[i].sh.kc < slices[i].sh.d_in))
+        return hipErrorInvalidValue;
+  }
   Slices<PreSlice> t{};
   t.count = count;
   t.first[0] = 0;
@@ -89,6 +147,7 @@ hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, 
     t.first[i + 1] = t.first[i] + slices[i].n_shrink_wg + slices[i].n_oft_wg;
   }
   for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
+  if (whole) return dtype == 1 ? pre_whole_bs<f16>(bs, t, s) : pre_whole_bs<bf16>(bs, t, s);
   switch (dtype) {
     case 0: return pre_tm<float>(tile_rows, bs, t, s);
     case 1: return pre_tm<f16>(tile_rows, bs, t, s);

@@ -148,5 +148,100 @@ __device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx)
   for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(v[q]);
 }
 
+// Whole-k shrink: one work-group of Q waves per work item of slice si
+// (plan tile, 16 factor columns).  Wave w runs the w-th k range of kc with
+// the split items' loop (waves past the split add nothing), leaves its fp32
+// sum in LDS, and wave 0 adds the Q sums in wave order: the same additions
+// as the reduce pass over the splits.  Shared-term rows are then scaled by
+// d' and written for this slice and, from the first slice, for every slice
+// that borrows its x·A_vᵀ (each with its own d').  Every early return
+// depends only on the item, so the work-group takes it together and the
+// barrier is met by all of its waves.
+template <typename T, int Q>
+__device__ __forceinline__ void shrink_whole(const Slices<PreSlice>& t, int si, int item, int wave, int lane,
+                                             f32x4* red) {
+  typedef typename Frag<T>::V Vt;
+  constexpr int U = 8;
+  const ShrinkArgs& a = t.s[si].sh;
+  const int own_items = a.own_tiles * a.own_nblk;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int* tile;
+  const int* trow;
+  int cb, want;
+  int rest = item;
+  if (rest < own_items) {
+    cb = rest % a.own_nblk;
+    const int tt = rest / a.own_nblk;
+    tile = a.tiles + 4 * tt;
+    trow = a.tile_rows_w + (size_t)tt * 16;
+    want = CLS_OWNED;
+  } else {
+    rest -= own_items;
+    const int tt = rest / a.sh_nblk;
+    if (tt >= a.sh_ntiles) return;
+    cb = rest % a.sh_nblk;
+    tile = a.sh_tiles + 4 * tt;
+    trow = a.sh_rows_w + (size_t)tt * 16;
+    want = CLS_SHARED;
+  }
+  const int4 tl = *reinterpret_cast<const int4*>(tile);
+  const int rw = trow[i16];
+  if (tl.z != want) return;
+  const T* F;
+  int N;
+  if (want == CLS_OWNED) {
+    const SlotDev& sd = a.slots[tl.w];
+    F = static_cast<const T*>(sd.A);
+    N = sd.rank;
+  } else {
+    F = static_cast<const T*>(a.vera_At);
+    N = a.r_v;
+  }
+  const int c0 = 16 * cb;
+  if (c0 >= N) return;
+  const int kbeg = wave * a.kc;
+  const int kend = wave < a.split ? min(a.d_in, kbeg + a.kc) : kbeg;
+  const bool xv = rw >= 0;
+  const T* xp = static_cast<const T*>(a.x) + (size_t)(xv ? (rw & 0xFFFF) : 0) * a.d_in + 8 * g;
+  const T* fp = F + (size_t)(c0 + i16) * a.d_in + 8 * g;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = kbeg; k < kend; k += 32 * U) {
+    Vt ff[U], xf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + 32 * u;
+      const bool ok = kk < kend;
+      ff[u] = ok ? load_frag<T>(fp + kk) : zero_frag<T>();
+      xf[u] = (ok && xv) ? load_frag<T>(xp + kk) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k + 32 * u >= kend) break;
+      acc = mma(acc, ff[u], xf[u]);
+    }
+  }
+  red[wave * 64 + lane] = acc;
+  lds_barrier();
+  if (wave != 0 || !xv) return;
+  // Lane holds columns c0 + 4g .. + 3 of plan position p0 + i16.
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < Q; ++w) v += red[w * 64 + lane];
+  const int col = c0 + 4 * g;
+  if (col >= N) return;
+  const int p = tl.x + i16;
+  const int slot = (int)((unsigned)rw >> 16);
+  for (int j = 0; j < t.count; ++j) {
+    const ShrinkArgs& b = t.s[j].sh;
+    const bool mine = j == si;
+    if (!mine && !(want == CLS_SHARED && si == 0 && b.borrows)) continue;
+    f32x4 o = v;
+    if (want == CLS_SHARED) o = v * gload<f32x4>(b.slots[slot].d + col);
+    T* dst = static_cast<T*>(b.v) + (size_t)p * b.kmax + col;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(o[q]);
+  }
+}
+
 }  // namespace shrink_impl
 }  // namespace tpa

@@ -326,8 +326,8 @@ def test_shared_plan_forward_matches_plain_forward():
     plan.close()
 
 
-@pytest.mark.parametrize("n,path,fuse", [(64, 2, 0), (64, 0, 0), (17, 2, 0), (100, 3, 0), (300, 3, 0),
-                                         (300, 3, 1), (300, 1, 0)])
+@pytest.mark.parametrize("n,path,fuse", [(64, 2, 0), (64, 2, 1), (64, 0, 0), (17, 2, 0), (17, 2, 1), (100, 3, 0),
+                                         (300, 3, 0), (300, 3, 1), (300, 1, 0)])
 def test_overlap_matches_one_stream(n, path, fuse):
     """The shrink on the layer's second stream gives the same bits as every
     step on the caller's stream (option 0): same kernels, same order of the
