@@ -421,20 +421,22 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          before it); by default when the plan's tile
  *                          bound keeps the row slots within 1.5x the rows.
  *                          Streamed decode kernel (n <= 64, 3 stages,
- *                          16-row tiles, route 0, shrink split <= 16): by
- *                          default (1 or < 0) the work-group that completes
- *                          a column tile (the last of its split work-groups
+ *                          16-row tiles, route 0, shrink split <= 16): 1
+ *                          runs it in the work-group that completes a
+ *                          column tile (the last of its split work-groups
  *                          to arrive, counted on counters in the workspace
- *                          that the launch before the GEMM clears) adds the
- *                          splits, applies s and b and adds the term; the
- *                          shrink then adds its k ranges inside one
- *                          work-group, so two launches per forward instead
- *                          of three.  It needs a launch before the GEMM (a
- *                          term or an OFT rotation on the layer) unless k
- *                          is whole, and rounds the last sum to the layer
- *                          type once, so it may differ from the separate
- *                          expand by one unit in the last place.  0: a
- *                          separate expand everywhere. */
+ *                          that the launch before the GEMM clears), which
+ *                          adds the splits, applies s and b and adds the
+ *                          term; the shrink then adds its k ranges inside
+ *                          one work-group, so two launches per forward
+ *                          instead of three, but slower on MI355X (each
+ *                          split's device-scope release writes back an L2).
+ *                          It needs a launch before the GEMM (a term or an
+ *                          OFT rotation on the layer) unless k is whole,
+ *                          and rounds the last sum to the layer type once,
+ *                          so it may differ from the separate expand by one
+ *                          unit in the last place.  Default (< 0) at
+ *                          decode and 0 everywhere: the separate expand. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3

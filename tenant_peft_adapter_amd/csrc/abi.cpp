@@ -523,15 +523,22 @@ Config choose_config(const tpa_layer* L, int n) {
     const long slots = 16L * ((n + 15) / 16 + std::min(n, L->n_owned) + 2);  // the plan's tile bound
     c.fused = L->opt[TPA_OPT_FUSE_EXPAND] == 1 || 2 * slots <= 3L * n;
   }
-  // Decode: the expand in the streamed GEMM's epilogue (the column tile's
-  // last split work-group finishes it), after a whole-k shrink, so the
-  // four launches of a projection group become two (decoder layer,
-  // graph-replayed step: see the measurements kept with the bench).  Needs
-  // the 3-stage streamed kernel, 16-row tiles, s inside the expand, a
-  // shrink of at most PRE_WHOLE_WAVES k ranges, and the tables in LDS.
+  // Decode, by option only: the expand in the streamed GEMM's epilogue
+  // (the column tile's last split work-group finishes it) after a whole-k
+  // shrink: three launches of a projection group become two, but measured
+  // slower (decoder layer, graph-replayed step: 555 µs against 200 with
+  // the separate expand).  Each split work-group's release at device scope
+  // writes back its XCD's L2 (gate + up GEMM 55 -> 224 µs; 84 µs with the
+  // fences left out), the finishing work-group's chain of dependent loads
+  // (tables, partials, s / b / e, the term's k steps) is longer than the
+  // separate expand, whose thousands of waves overlap theirs, and 16-wave
+  // whole-k work-groups leave most CUs idle in the shrink (7-10 -> 13-31
+  // µs).  Needs the 3-stage streamed kernel, 16-row tiles, s inside the
+  // expand, a shrink of at most PRE_WHOLE_WAVES k ranges and the tables in
+  // LDS.
   c.fused_dec = 0;
   if (c.gemm_path == 2 && n <= 64 && c.gemm_stages == 3 && c.tile_rows == 16 && c.scale_route == 0 &&
-      L->opt[TPA_OPT_FUSE_EXPAND] != 0 && L->opt[TPA_OPT_SHRINK_SPLIT] <= tpa::PRE_WHOLE_WAVES)
+      L->opt[TPA_OPT_FUSE_EXPAND] == 1 && L->opt[TPA_OPT_SHRINK_SPLIT] <= tpa::PRE_WHOLE_WAVES)
     c.fused_dec = fused_dec_fits(L, n, c);
   // A stacked slot's scale is the product of its members' scales, so h
   // rounded to the layer type before the expand would carry |s|·u·|h| of

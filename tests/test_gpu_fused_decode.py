@@ -1,7 +1,8 @@
 """GPU tests of the decode path whose expand runs in the streamed GEMM's
-epilogue (Scute paper, §2 "The LoRA schedule": the expand finishes each
-tile of h; §4.1 route one and §5.2: s applied as the tile finishes; route
-two: the shared factor's term times e), after a whole-k shrink:
+epilogue (option 1 of the fused-expand key; Scute paper, §2 "The LoRA
+schedule": the expand finishes each tile of h; §4.1 route one and §5.2: s
+applied as the tile finishes; route two: the shared factor's term times e),
+after a whole-k shrink:
 
   * the decoder-layer workload, every projection, against the oracle and
     against the same layer with the expand as a launch of its own and the
@@ -47,10 +48,10 @@ def _one_ulp(a, b, dtype):
 
 
 def _pair(p, n, sor, dtype="f16", opts=None, max_slots=32, max_rank=256):
-    """Outputs of the layer with the fused epilogue (default) and with the
-    separate expand, both on 16 shrink k ranges."""
+    """Outputs of the layer with the fused epilogue (option 1) and with the
+    separate expand (the default at decode), both on 16 shrink k ranges."""
     outs = []
-    for fuse in (-1, 0):
+    for fuse in (1, -1):
         o = {SHRINK_SPLIT: 16, FUSE: fuse}
         o.update(opts or {})
         L = make_layer(p, max_slots=max_slots, max_rank=max_rank, options=o)
@@ -144,8 +145,8 @@ def test_fused_group_forward(names, borrow):
     wl = synth.decoder_layer_mixed(n=64, shapes=shapes)
     projs = wl["projections"]
     say("fused group %s borrow=%d" % ("+".join(names), borrow))
-    cf, got = _group(projs, wl["n"], wl["slot_of_row"], -1, borrow)
-    cs, want = _group(projs, wl["n"], wl["slot_of_row"], 0, borrow)
+    cf, got = _group(projs, wl["n"], wl["slot_of_row"], 1, borrow)
+    cs, want = _group(projs, wl["n"], wl["slot_of_row"], -1, borrow)
     assert cf["fused_expand"] == 1 and cs["fused_expand"] == 0
     for nm, g, w, p in zip(names, got, want, projs):
         _one_ulp(g, w, "f16")
@@ -162,7 +163,7 @@ def test_fused_repeated_calls_and_graph_replays():
     wl = _decoder()
     p = [q for q in wl["projections"] if q["name"] == "down"][0]
     n = wl["n"]
-    L = make_layer(p, max_slots=32, max_rank=256)
+    L = make_layer(p, max_slots=32, max_rank=256, options={FUSE: 1})
     assert L.config(n)["fused_expand"] == 1 and L.config(n)["gemm_split"] > 1
     x = torch.tensor(p["x"]).half().cuda()
     sor = torch.tensor(wl["slot_of_row"]).cuda()
@@ -202,7 +203,7 @@ def test_fused_unknown_slots():
     p = wl["projections"][0]
     sor = wl["slot_of_row"].copy()
     sor[::9] = 99
-    L = make_layer(p, max_slots=24, max_rank=64, options={PATH: 2})
+    L = make_layer(p, max_slots=24, max_rank=64, options={PATH: 2, FUSE: 1})
     assert L.config(64)["fused_expand"] == 1
     y_gpu = run(L, p["x"], sor, "f16")
     assert L.error_flag(clear=True) == 1
@@ -226,13 +227,13 @@ def test_fused_fallbacks():
     sor = np.array([s if s in ia3 else 0 for s in wl["slot_of_row"]], dtype=np.int32)
     y, h, xw = reference(pi, sor)
     for split, fused in ((2, 0), (1, 1)):
-        L = make_layer(pi, max_slots=24, max_rank=64, options={PATH: 2, GEMM_SPLIT: split})
+        L = make_layer(pi, max_slots=24, max_rank=64, options={PATH: 2, GEMM_SPLIT: split, FUSE: 1})
         assert L.config(64)["fused_expand"] == fused, (split, L.config(64))
         check(run(L, pi["x"], sor, "f16"), y, h, xw, label="ia3 only split=%d" % split)
         L.close()
     y, h, xw = reference(p, wl["slot_of_row"])
     for route in (1, 2, 3):
-        L = make_layer(p, max_slots=24, max_rank=64, options={PATH: 2, ROUTE: route})
+        L = make_layer(p, max_slots=24, max_rank=64, options={PATH: 2, ROUTE: route, FUSE: 1})
         assert L.config(64)["fused_expand"] == 0
         check(run(L, p["x"], wl["slot_of_row"], "f16"), y, h, xw, label="route %d" % route)
         L.close()
