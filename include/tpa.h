@@ -436,7 +436,13 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          and rounds the last sum to the layer type once,
  *                          so it may differ from the separate expand by one
  *                          unit in the last place.  Default (< 0) at
- *                          decode and 0 everywhere: the separate expand. */
+ *                          decode and 0 everywhere: the separate expand.
+ *   TPA_OPT_SHRINK_COLS  : factor columns per shrink work item, 16 or 64
+ *                          (f16 / bf16, 16-row tiles, split-k shrink): 64
+ *                          reads a tile's x rows once for four column
+ *                          blocks instead of once per block; the same
+ *                          bits.  By default 64 from 512 rows, else 16.
+ *                          The group forward uses the first layer's. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2
 #define TPA_OPT_TILE_ROWS 3
@@ -448,6 +454,7 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
 #define TPA_OPT_OVERLAP 9
 #define TPA_OPT_WIDE_TILE 10
 #define TPA_OPT_FUSE_EXPAND 11
+#define TPA_OPT_SHRINK_COLS 12
 /* Scale routes of §4.3 and the appendix "Routes"; the other keys pin the
  * kernel configuration the appendix "Tuned kernels" would tune. */
 tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
@@ -460,11 +467,11 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
  * and k range, the scale route, the decode GEMM's k-groups per work-group
  * and (direct-load kernels, else 0) its LDS buffers (per k-group for the
  * streamed kernel), path 3's tile edge (128 or 256; else 0), and whether
- * the expand runs in the GEMM's epilogue (prefill or decode kernel).  For
- * tests and measurement. */
+ * the expand runs in the GEMM's epilogue (prefill or decode kernel), and the
+ * factor columns per shrink item.  For tests and measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
-      gemm_groups, gemm_stages, gemm_tile, fused_expand;
+      gemm_groups, gemm_stages, gemm_tile, fused_expand, shrink_cols;
 } tpa_config;
 /* Appendix "Tuned kernels": the configuration in force for n rows. */
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);

@@ -29,7 +29,7 @@ DTYPES = {"f32": TPA_F32, "f16": TPA_F16, "bf16": TPA_BF16}
 METHODS = {"identity": 0, "lora": 1, "dora": 2, "ia3": 3, "vera": 4, "oft": 5, "ssf": 6, "stack": 7, "loha": 8, "lokr": 9}
 (TPA_OPT_GEMM_SPLIT, TPA_OPT_SHRINK_SPLIT, TPA_OPT_TILE_ROWS, TPA_OPT_GEMM_PATH, TPA_OPT_SCALE_ROUTE,
  TPA_OPT_GEMM_NB, TPA_OPT_GEMM_GROUPS, TPA_OPT_GEMM_STAGES, TPA_OPT_OVERLAP, TPA_OPT_WIDE_TILE,
- TPA_OPT_FUSE_EXPAND) = (1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11)
+ TPA_OPT_FUSE_EXPAND, TPA_OPT_SHRINK_COLS) = (1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12)
 LIVE_S, LIVE_B, LIVE_R, LIVE_D, LIVE_E = 1, 2, 4, 8, 16
 FOLD_C_A, FOLD_E_B, FOLD_C_D, FOLD_D_A = 1, 2, 4, 8
 STATUS = {0: "OK", -1: "INVALID", -2: "METHOD", -3: "NO_SLOT", -4: "UNKNOWN_SLOT",
@@ -56,7 +56,7 @@ class tpa_adapter_info(ctypes.Structure):
 class tpa_config(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in ("tile_rows", "gemm_path", "gemm_nb", "gemm_split", "gemm_kc",
                                               "shrink_split", "shrink_kc", "scale_route", "gemm_groups",
-                                              "gemm_stages", "gemm_tile", "fused_expand")]
+                                              "gemm_stages", "gemm_tile", "fused_expand", "shrink_cols")]
 
 
 class tpa_plan_host(ctypes.Structure):

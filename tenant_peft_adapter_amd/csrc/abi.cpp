@@ -208,6 +208,7 @@ struct Config {
   int fused;      // path 3, 128 x 128 tiles: the expand runs in the GEMM's epilogue
   int h_fp32;     // h goes to the expand in fp32 even when k is not split
   int fused_dec;  // path 2: the expand runs in the streamed GEMM's epilogue, after a whole-k shrink
+  int shrink_ncb; // 16-column blocks per shrink item (1 or 4)
 };
 
 bool decode_path(const Config& c) { return c.gemm_path == 0 || c.gemm_path == 2; }
@@ -256,7 +257,7 @@ struct tpa_layer {
   int n_owned = 0, n_vera = 0, n_dora = 0, n_stack = 0;
   int max_owned_rank = 0;  // largest rank among loaded owned-term slots
   int n_oft_bs[3] = {0, 0, 0};  // loaded OFT slots with block 16, 32, 64
-  int opt[12] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1, -1};
+  int opt[13] = {-1, -1, -1, -1, -1, 0, -1, -1, -1, -1, -1, -1, -1};
   // Second stream (default priority) on which the shrink runs beside the
   // base GEMM when overlap is asked for, and the events that fork it from
   // and join it to the caller's stream; created at the first forward that
@@ -407,6 +408,9 @@ void set_shrink_split(const tpa_layer* L, int n, Config* c) {
 int max_tiles_for(const tpa_layer* L, int n, int tile_rows);
 int all_tile_bound(const tpa_layer* L, int n, int tr, int max_tiles);
 
+// Rows from which shrink items take 64 factor columns by default.
+constexpr int SHRINK_WIDE_ROWS = 512;
+
 // Whether the streamed decode GEMM can carry the expand for n rows at the
 // configuration's column blocks and k-groups: one thread per entry of the
 // tile list and the epilogue's tables within LDS beside the rings.
@@ -545,6 +549,12 @@ Config choose_config(const tpa_layer* L, int n) {
   // error: such layers keep h in fp32 between the GEMM and the expand.
   c.h_fp32 = L->n_stack > 0 && !c.fused && !c.fused_dec;
   set_shrink_split(L, n, &c);
+  // Shrink items of 64 factor columns (one read of the tile's x rows for
+  // four column blocks) where there are items enough to fill the chip
+  // without them; decode keeps 16 for the shorter chains.  Same bits.
+  const int cols = L->opt[TPA_OPT_SHRINK_COLS];
+  const bool wide_ok = L->dtype != TPA_F32 && c.tile_rows == 16 && !c.fused_dec;
+  c.shrink_ncb = wide_ok && (cols == 64 || (cols <= 0 && n >= SHRINK_WIDE_ROWS)) ? 4 : 1;
   return c;
 }
 
@@ -1695,6 +1705,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
   tpa_layer* L0 = sl[0].L;
   const int dtype = L0->dtype;
   const int tile_rows = sl[0].c.tile_rows;
+  const int ncb = sl[0].c.shrink_ncb;  // one shrink launch: the first projection's item width for all
   tpa::ShrinkArgs sh[tpa::MAX_SLICES];
   tpa::OftArgs of[tpa::MAX_SLICES];
   bool term[tpa::MAX_SLICES], oft[tpa::MAX_SLICES];
@@ -1721,9 +1732,9 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
       sh[i].tile_rows_w = p.tile_rows_w;
       sh[i].sh_rows_w = p.sh_rows_w;
       sh[i].own_tiles = owned_tile_bound(L, n, tile_rows, y.max_tiles);
-      sh[i].own_nblk = std::max(1, (L->max_owned_rank + 15) / 16);
+      sh[i].own_nblk = std::max(1, (L->max_owned_rank + 16 * ncb - 1) / (16 * ncb));
       sh[i].sh_ntiles = L->n_vera > 0 ? y.max_sh_tiles : 0;
-      sh[i].sh_nblk = std::max(1, L->r_v / 16);
+      sh[i].sh_nblk = std::max(1, (L->r_v + 16 * ncb - 1) / (16 * ncb));
       sh[i].split = c.shrink_split;
       sh[i].kc = c.shrink_kc;
       sh[i].part = reinterpret_cast<float*>(sl[i].w + y.vpart);
@@ -1817,7 +1828,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     TPA_HIP(hipStreamWaitEvent(L0->side, L0->ev_fork, 0));
     tpa::PreSlice ps[tpa::MAX_SLICES];
     for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr);
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, L0->side));
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, L0->side, false, ncb));
     for (int i = 0; i < count; ++i)
       if (term[i]) TPA_HIP(tpa::launch_shrink_reduce(dtype, sh[i], L0->side));
     TPA_HIP(hipEventRecord(L0->ev_join, L0->side));
@@ -1835,13 +1846,13 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
                                   sl[i].L->n_oft_bs[b] ? &of[i] : nullptr, fdec);
     }
     if (fdec) clear_counters(ps);
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, kBs[b], ps, count, s, fdec));
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, kBs[b], ps, count, s, fdec, ncb));
     sh_done = true;
   }
   if (!sh_done && any_term_all) {
     for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr, fdec);
     if (fdec) clear_counters(ps);
-    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, s, fdec));
+    TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, s, fdec, ncb));
   }
   if (tpa_status st = stage(L0, 2, s)) return st;
 
@@ -2258,7 +2269,9 @@ tpa_status tpa_plan_debug(tpa_layer* L, const int32_t* sor, int32_t n, void* ws,
 
 tpa_status tpa_layer_set_option(tpa_layer* L, int32_t key, int32_t value) {
   if (tpa_status st = check_layer(L)) return st;
-  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_FUSE_EXPAND) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key < TPA_OPT_GEMM_SPLIT || key > TPA_OPT_SHRINK_COLS) return fail(TPA_ERR_INVALID, "unknown option %d", key);
+  if (key == TPA_OPT_SHRINK_COLS && value > 0 && value != 16 && value != 64)
+    return fail(TPA_ERR_INVALID, "shrink columns must be 16 or 64");
   if (key == TPA_OPT_FUSE_EXPAND && value > 1) return fail(TPA_ERR_INVALID, "fused expand must be 0 or 1");
   if (key == TPA_OPT_WIDE_TILE && value > 0 && value != 128 && value != 256)
     return fail(TPA_ERR_INVALID, "wide tile must be 128 or 256");
@@ -2301,6 +2314,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   // counters: a term, an OFT rotation, or k not split.
   const bool pre = L->n_owned > 0 || L->n_vera > 0 || L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
   out->fused_expand = c.fused || (c.fused_dec && (pre || c.gemm_split == 1));
+  out->shrink_cols = 16 * c.shrink_ncb;
   return TPA_OK;
 }
 

@@ -114,8 +114,9 @@ struct ShrinkArgs {
   int32_t n, d_in;
   int32_t kmax;            // row stride of part and v
   // Work items: own_tiles x own_nblk x split on the first own_tiles entries of
-  // tiles (bound on the owned-term tiles; 16-column blocks of the largest
-  // owned rank), then sh_ntiles x sh_nblk x split on sh_tiles (r_v / 16).
+  // tiles (bound on the owned-term tiles; column blocks of 16·ncb of the
+  // largest owned rank), then sh_ntiles x sh_nblk x split on sh_tiles
+  // (r_v / (16·ncb)); ncb is the launch's (launch_pre).
   int32_t own_tiles, own_nblk, sh_ntiles, sh_nblk;
   int32_t split, kc;       // k ranges (kc a multiple of 32)
   float* part;
@@ -151,8 +152,11 @@ PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of, bool whole = fa
 // and are added in wave order (the order the reduce pass adds splits in),
 // so V and U are final when the launch ends and no partials are written.
 constexpr int PRE_WHOLE_WAVES = 16;
+// ncb: 16-column blocks per shrink item (1, or 4 for f16 / bf16 with
+// 16-row tiles in split mode); the slices' own_nblk and sh_nblk count
+// blocks of 16·ncb columns.
 hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t stream,
-                      bool whole = false);
+                      bool whole = false, int ncb = 1);
 
 // out[row] = h[row] ⊙ s + b + V[p] B'ᵀ (owned tile) or (U[p] B_vᵀ) ⊙ e
 // (shared tile), for row = perm[p].  h is read from `out` (in place, layer

@@ -21,14 +21,14 @@ namespace {
 constexpr int THREADS = 256;
 constexpr int OFT_BLOCKS_PER_WG = 16;
 
-template <typename T, int MB, int BS>
+template <typename T, int MB, int BS, int NCB>
 __global__ __launch_bounds__(THREADS) void pre_kernel(Slices<PreSlice> t) {
   const int si = slice_of(t, (int)blockIdx.x);
   const PreSlice& ps = t.s[si];
   const int local = (int)blockIdx.x - t.first[si];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (local < ps.n_shrink_wg) {
-    shrink_impl::shrink_item<T, MB>(ps.sh, local * (THREADS / 64) + wave, lane);
+    shrink_impl::shrink_item<T, MB, NCB>(ps.sh, local * (THREADS / 64) + wave, lane);
     return;
   }
   if (BS != 0) {
@@ -80,24 +80,31 @@ hipError_t pre_whole_bs(int bs, const Slices<PreSlice>& t, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int MB>
+template <typename T, int MB, int NCB>
 hipError_t pre_bs(int bs, const Slices<PreSlice>& t, hipStream_t s) {
   const dim3 grid((unsigned)t.first[t.count]);
   if (grid.x == 0) return hipSuccess;
   switch (bs) {
-    case 0: hipLaunchKernelGGL((pre_kernel<T, MB, 0>), grid, dim3(THREADS), 0, s, t); break;
-    case 16: hipLaunchKernelGGL((pre_kernel<T, MB, 16>), grid, dim3(THREADS), 0, s, t); break;
-    case 32: hipLaunchKernelGGL((pre_kernel<T, MB, 32>), grid, dim3(THREADS), 0, s, t); break;
-    case 64: hipLaunchKernelGGL((pre_kernel<T, MB, 64>), grid, dim3(THREADS), 0, s, t); break;
+    case 0: hipLaunchKernelGGL((pre_kernel<T, MB, 0, NCB>), grid, dim3(THREADS), 0, s, t); break;
+    case 16: hipLaunchKernelGGL((pre_kernel<T, MB, 16, NCB>), grid, dim3(THREADS), 0, s, t); break;
+    case 32: hipLaunchKernelGGL((pre_kernel<T, MB, 32, NCB>), grid, dim3(THREADS), 0, s, t); break;
+    case 64: hipLaunchKernelGGL((pre_kernel<T, MB, 64, NCB>), grid, dim3(THREADS), 0, s, t); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t pre_tm(int tile_rows, int bs, const Slices<PreSlice>& t, hipStream_t s) {
-  if (tile_rows == 16) return pre_bs<T, 1>(bs, t, s);
-  if (tile_rows == 64) return pre_bs<T, 4>(bs, t, s);
+hipError_t pre_tm(int tile_rows, int bs, int ncb, const Slices<PreSlice>& t, hipStream_t s) {
+  if (ncb == 4) {
+    if constexpr (sizeof(T) == 2) {
+      if (tile_rows == 16) return pre_bs<T, 1, 4>(bs, t, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (ncb != 1) return hipErrorInvalidValue;
+  if (tile_rows == 16) return pre_bs<T, 1, 1>(bs, t, s);
+  if (tile_rows == 64) return pre_bs<T, 4, 1>(bs, t, s);
   return hipErrorInvalidValue;
 }
 
@@ -130,8 +137,9 @@ PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of, bool whole) {
 }
 
 hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, int count, hipStream_t s,
-                      bool whole) {
+                      bool whole, int ncb) {
   if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
+  if (whole && ncb != 1) return hipErrorInvalidValue;
   if (whole) {
     if (tile_rows != 16 || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
     for (int i = 0; i < count; ++i)
@@ -149,9 +157,9 @@ hipError_t launch_pre(int dtype, int tile_rows, int bs, const PreSlice* slices, 
   for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
   if (whole) return dtype == 1 ? pre_whole_bs<f16>(bs, t, s) : pre_whole_bs<bf16>(bs, t, s);
   switch (dtype) {
-    case 0: return pre_tm<float>(tile_rows, bs, t, s);
-    case 1: return pre_tm<f16>(tile_rows, bs, t, s);
-    case 2: return pre_tm<bf16>(tile_rows, bs, t, s);
+    case 0: return pre_tm<float>(tile_rows, bs, ncb, t, s);
+    case 1: return pre_tm<f16>(tile_rows, bs, ncb, t, s);
+    case 2: return pre_tm<bf16>(tile_rows, bs, ncb, t, s);
   }
   return hipErrorInvalidValue;
 }

@@ -12,19 +12,23 @@
 namespace tpa {
 namespace shrink_impl {
 
-// One wave per work item (plan tile, 16 factor columns, k range): factor
-// rows and the tile's x rows stream straight into MFMA registers (8 k steps
-// of loads issued together), no LDS and no barriers, so the whole GPU takes
-// part even when one tile (VeRA's shared factor) holds most of the work.
-// Each item writes its fp32 partial [split][n][kmax] by plan position; the
-// reduce pass below adds the splits in split order.
+// One wave per work item (plan tile, 16·NCB factor columns, k range):
+// factor rows and the tile's x rows stream straight into MFMA registers
+// (up to 8 k steps of loads issued together), no LDS and no barriers, so
+// the whole GPU takes part even when one tile (VeRA's shared factor) holds
+// most of the work.  Each item writes its fp32 partial [split][n][kmax] by
+// plan position; the reduce pass below adds the splits in split order.
+// With NCB = 4 an item reads its x rows once for 64 factor columns instead
+// of once per 16 (blocks past the factor's rank load nothing); each block's
+// products are the same MFMA steps in the same k order, so the partials
+// are the same bits.
 
-template <typename T, int MB>
+template <typename T, int MB, int NCB = 1>
 __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int lane) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fp32 fragments are twice as
-  // wide, so fewer fit in registers)
-  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? 8 : 4);
+  // wide, and wide items load four factor fragments a step, so fewer fit)
+  constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 4 : 2) : (MB == 1 ? (NCB == 1 ? 8 : 4) : 4);
   const int ks = item % a.split;
   int rest = item / a.split;
   const int own_items = a.own_tiles * a.own_nblk;
@@ -66,7 +70,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
     F = static_cast<const T*>(a.vera_At);
     N = a.r_v;
   }
-  const int c0 = 16 * cb;
+  const int c0 = 16 * NCB * cb;
   if (c0 >= N) return;
   const int kbeg = ks * a.kc;
   const int kend = min(a.d_in, kbeg + a.kc);
@@ -79,18 +83,28 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
     xv[m] = rw[m] >= 0;
     xp[m] = X + (size_t)(xv[m] ? (rw[m] & 0xFFFF) : 0) * a.d_in + 8 * g;
   }
-  const T* fp = F + (size_t)(c0 + i16) * a.d_in + 8 * g;
-
-  f32x4 acc[MB];
+  // Column blocks of this item within the factor's rank (a multiple of 16).
+  const T* fp[NCB];
+  bool fv[NCB];
 #pragma unroll
-  for (int m = 0; m < MB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NCB; ++j) {
+    fv[j] = c0 + 16 * j < N;
+    fp[j] = F + (size_t)(fv[j] ? c0 + 16 * j + i16 : 0) * a.d_in + 8 * g;
+  }
+
+  f32x4 acc[NCB][MB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j)
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[j][m] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = kbeg; k < kend; k += 32 * U) {
-    Vt ff[U], xf[U][MB];
+    Vt ff[U][NCB], xf[U][MB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kk = k + 32 * u;
       const bool ok = kk < kend;
-      ff[u] = ok ? load_frag<T>(fp + kk) : zero_frag<T>();
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) ff[u][j] = (ok && fv[j]) ? load_frag<T>(fp[j] + kk) : zero_frag<T>();
 #pragma unroll
       for (int m = 0; m < MB; ++m) xf[u][m] = (ok && xv[m]) ? load_frag<T>(xp[m] + kk) : zero_frag<T>();
     }
@@ -98,15 +112,23 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, int item, int l
     for (int u = 0; u < U; ++u) {
       if (k + 32 * u >= kend) break;
 #pragma unroll
-      for (int m = 0; m < MB; ++m) acc[m] = mma(acc[m], ff[u], xf[u][m]);
+      for (int j = 0; j < NCB; ++j) {
+        if (!fv[j]) continue;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[j][m] = mma(acc[j][m], ff[u][j], xf[u][m]);
+      }
     }
   }
-  // Lane holds V[p0 + 16m + i16][c0 + 4g + v], v = 0..3.
-  const int col = c0 + 4 * g;
+  // Lane holds V[p0 + 16m + i16][c0 + 16j + 4g + v], v = 0..3.
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int p = p0 + 16 * m + i16;
-    if (xv[m]) *reinterpret_cast<f32x4*>(a.part + ((size_t)ks * a.n + p) * a.kmax + col) = acc[m];
+  for (int j = 0; j < NCB; ++j) {
+    if (!fv[j]) continue;
+    const int col = c0 + 16 * j + 4 * g;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int p = p0 + 16 * m + i16;
+      if (xv[m]) *reinterpret_cast<f32x4*>(a.part + ((size_t)ks * a.n + p) * a.kmax + col) = acc[j][m];
+    }
   }
 }
 

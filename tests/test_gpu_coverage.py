@@ -200,3 +200,37 @@ def test_vera_a_read_once_per_fused_group(names, n):
     plan2.close()
     for L in Ls[1:] + Lo:
         L.close()
+
+
+# ------------------------------------------------- shrink item widths ---
+
+@pytest.mark.parametrize("n", [65, 300, 1024])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_shrink_items_of_64_columns_same_bits(n, dtype):
+    """§2 "The LoRA schedule", shrink: work items of 64 factor columns (the
+    tile's x rows read once for four column blocks) give the same V and U,
+    hence the same outputs, as items of 16: each block's products are the
+    same MFMA steps in the same k order.  Ranks 16, 48 and 64 and VeRA's
+    shared r_v = 64 leave some of an item's blocks past the rank (masked),
+    and the layer matches the oracle."""
+    rng = np.random.default_rng(7100 + n)
+    d_in, d_out = 256, 256
+    W = synth.round_to(synth._normal(rng, (d_out, d_in), 1.0 / np.sqrt(d_in)), dtype)
+    shared = synth._vera_shared(rng, d_in, d_out, 64, dtype)
+    adapters = {1: synth._lora(rng, d_in, d_out, 16, dtype), 2: synth._lora(rng, d_in, d_out, 48, dtype),
+                3: synth._lora(rng, d_in, d_out, 64, dtype), 4: synth._vera(rng, 64, d_out),
+                5: synth._dora(rng, W, 16, dtype), 6: synth._ia3(rng, d_out)}
+    x = synth.round_to(synth._normal(rng, (n, d_in), 1.0), dtype)
+    sor = rng.integers(0, 7, size=n).astype(np.int32)
+    p = {"W": W, "x": x, "adapters": adapters, "shared": shared, "dtype": dtype, "d_in": d_in, "d_out": d_out}
+    outs = []
+    for cols in (16, 64):
+        L = make_layer(p, max_slots=8, max_rank=64, options={12: cols})
+        assert L.config(n)["shrink_cols"] == cols
+        outs.append(run(L, x, sor, dtype))
+        L.close()
+    say("shrink items of 16 / 64 columns n=%d %s: max diff %g" % (n, dtype, np.abs(outs[0] - outs[1]).max()))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    y, h, xw = reference(p, sor)
+    tol = {"f16": (0.01, 2e-3), "bf16": (0.05, 1.6e-2)}[dtype]
+    check(outs[1], y, h, xw, mean_tol=tol[0], max_tol=tol[1], label="shrink 64 columns n=%d" % n)
