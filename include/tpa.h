@@ -441,7 +441,8 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          (f16 / bf16, 16-row tiles, split-k shrink): 64
  *                          reads a tile's x rows once for four column
  *                          blocks instead of once per block; the same
- *                          bits.  By default 64 from 512 rows, else 16.
+ *                          bits.  By default 64 from 512 rows when an
+ *                          owned rank or VeRA's r_v exceeds 16, else 16.
  *                          The group forward uses the first layer's. */
 #define TPA_OPT_GEMM_SPLIT 1
 #define TPA_OPT_SHRINK_SPLIT 2

@@ -551,10 +551,13 @@ Config choose_config(const tpa_layer* L, int n) {
   set_shrink_split(L, n, &c);
   // Shrink items of 64 factor columns (one read of the tile's x rows for
   // four column blocks) where there are items enough to fill the chip
-  // without them; decode keeps 16 for the shorter chains.  Same bits.
+  // without them and a factor wider than 16 columns to share the read;
+  // decode and rank-16 layers keep 16, whose items issue twice the k steps
+  // at once (1024-row q_proj, rank 16: 6.5 against 7.9 µs).  Same bits.
   const int cols = L->opt[TPA_OPT_SHRINK_COLS];
   const bool wide_ok = L->dtype != TPA_F32 && c.tile_rows == 16 && !c.fused_dec;
-  c.shrink_ncb = wide_ok && (cols == 64 || (cols <= 0 && n >= SHRINK_WIDE_ROWS)) ? 4 : 1;
+  const bool wide_pays = L->max_owned_rank > 16 || (L->n_vera > 0 && L->r_v > 16);
+  c.shrink_ncb = wide_ok && (cols == 64 || (cols <= 0 && n >= SHRINK_WIDE_ROWS && wide_pays)) ? 4 : 1;
   return c;
 }
 
