@@ -387,9 +387,7 @@ tpa_status tpa_plan_debug(tpa_layer* layer, const int32_t* slot_of_row_dev, int3
  *                          streamed decode kernel, per k-group 3, 4 or 6
  *                          (other values take 3; fewer where they do not
  *                          fit); 128 x 128 kernel, 32 KB each, 2..5 (6
- *                          takes the automatic choice: 4 when split-K
- *                          leaves at most 256 work-groups, each with a k
- *                          range of at least 1536, else 2)
+ *                          takes the automatic choice, 4)
  *   TPA_OPT_OVERLAP      : 1 runs the shrink and its split
  *                          reduction on a second stream of the layer
  *                          (default priority) beside OFT's rotation and

@@ -500,17 +500,11 @@ Config choose_config(const tpa_layer* L, int n) {
     c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
     if (c.gemm_path == 3) {
-      // Two buffers (64 KB) let two work-groups share a CU.  Where the
-      // split grid has at most one per CU and each runs a long k range,
-      // four buffers (three slices in flight) cover more of HBM's latency
-      // (the 14336 -> 4096 down projection, cold weights: 128 rows 40.2 ->
-      // 35.8 µs, 256 rows 63.4 -> 55.2, 512 rows 110 -> 95);
-      // with more work-groups than CUs the deeper ring halves residency
-      // and loses (14336 outputs at 256 rows: 53.6 -> 65.2).
+      // The 128 x 128 kernel runs one work-group of 12 waves per CU, so its
+      // ring may take 128 KB: four buffers keep three slices in flight (five
+      // measured no better: 1024 x 4096 x 4096 44.6 against 42.5 µs).
       const int st = L->opt[TPA_OPT_GEMM_STAGES];
-      const bool deep = c.gemm_tile == 128 && c.gemm_split > 1 && (long)tiles * c.gemm_split <= 256 &&
-                        c.gemm_kc >= 1536;
-      c.gemm_stages = st >= 2 && st <= 5 ? st : (deep ? 4 : 2);
+      c.gemm_stages = st >= 2 && st <= 5 ? st : 4;
     }
   }
   c.scale_route = L->opt[TPA_OPT_SCALE_ROUTE];

@@ -19,6 +19,7 @@
 
 #include "internal.h"
 #include "shrink_impl.h"
+#include "wide_impl.h"
 
 namespace tpa {
 
@@ -786,46 +787,35 @@ __global__ __launch_bounds__(THREADS) void gemm_tiled_kernel(BaseGemmArgs a) {
 // ---------------------------------------------------------------- wide ----
 //
 // Base GEMM for n > 64 rows, f16/bf16, where MFMA throughput rather than the
-// single read of W sets the time.  Work-group = 4 waves; its tile is 128
-// rows of x by 128 output columns (wave (wr, wc) computes 64 x 64 as 4 x 4
-// MFMA tiles) by one k range.  Each 64-element k slice of the tile's x rows
-// and W rows (256 rows x 128 B) is loaded straight into one of S LDS
-// buffers with direct global-to-LDS loads (8 loads per wave per slice), the
-// chunks of a row permuted (c ^ swz(row)) so the fragment reads hit distinct
-// bank groups; S - 1 slices are in flight while one is multiplied.  S = 2
-// (64 KB) lets two work-groups share a CU and is the default.  Four buffers
-// (three slices in flight) are chosen for split-K grids of at most 256
-// work-groups (one per CU) whose k ranges hold at least 1536 elements: such
-// long loops read their slices from HBM rather than L2, and the deeper ring
-// covers that latency (14336 -> 4096 at 128-512 rows: 10-13% faster); where
-// two work-groups would share a CU, or the loop is short, two buffers stay
-// ahead.  Per slice each wave waits for its own loads, then the
-// work-group meets at a barrier.  Tiles are handed to work-groups so that
-// each XCD (work-group i runs on XCD i % 8) takes a contiguous run of the
-// tile order below: the slices of x and W its CUs read together stay in its
-// L2.  Work-groups past the tiles (first split only) run the
-// shrink's split reduction, which needs nothing from the GEMM: it fills the
-// room a CU has beside its tile instead of a launch of its own.
+// single read of W sets the time.  Work-group = one tile of 128 rows of x by
+// 128 output columns by one k range, 12 waves: the k loop of wide_impl.h
+// (4 producer waves stream each 64-element slice of the tile's x and W rows
+// into a ring of S 32 KB LDS buffers by direct loads; two groups of 4 waves,
+// each wave 64 x 64 as 4 x 4 MFMA tiles, take the two 32-element halves of
+// every slice one phase apart), then each of those waves stores two 16-row
+// blocks of its 64 x 64 block.  One work-group per CU
+// (12 waves and 128 KB of LDS at S = 4).  Tiles are handed to work-groups so
+// that each XCD (work-group i runs on XCD i % 8) takes a contiguous run of
+// the tile order below: the slices of x and W its CUs read together stay in
+// its L2.  Work-groups past the tiles (first split only) run the shrink's
+// split reduction, which needs nothing from the GEMM: it fills the room a CU
+// has beside its tile instead of a launch of its own.
 template <typename T, int S>
-__global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_tiles, int col_tiles) {
-  typedef typename Frag<T>::V Vt;
-  constexpr int STAGE = 256 * 128;
-  constexpr int LI = 8;  // loads per wave per slice
+__global__ __launch_bounds__(wide_impl::THREADS) void gemm_wide_kernel(GemmSlice sl, int row_tiles, int col_tiles) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const BaseGemmArgs& a = sl.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i16 = lane & 15, g = lane >> 4;
-  const int wr = wave & 1, wc = wave >> 1;
+  const wide_impl::Role ro = wide_impl::role();
   const int ntile = row_tiles * col_tiles;
   if ((int)blockIdx.x >= ntile) {
-    if (blockIdx.y == 0) shrink_impl::shrink_reduce_item<T>(sl.side, ((int)blockIdx.x - ntile) * 256 + tid);
+    if (blockIdx.y == 0)
+      shrink_impl::shrink_reduce_item<T>(sl.side, ((int)blockIdx.x - ntile) * wide_impl::THREADS + (int)threadIdx.x);
     return;
   }
   int t = (int)blockIdx.x;
   if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-  // Tile order: strips of 8 row tiles, column by column, so the ~64 tiles
-  // an XCD runs at once form an 8 x 8 block reading 8 slices of x and 8 of
-  // W (each slice used 8 times from L2), not a column of every row tile.
+  // Tile order: strips of 8 row tiles, column by column, so the ~32 tiles
+  // an XCD runs at once form an 8 x 4 block reading 8 slices of x and 4 of
+  // W (each used 4 or 8 times from L2), not a column of every row tile.
   const int strip = 8 * col_tiles;
   const int r_first = (t / strip) * 8, r_rows = min(8, row_tiles - r_first);
   const int rt = r_first + (t % strip) % r_rows, ct = (t % strip) / r_rows;
@@ -833,102 +823,54 @@ __global__ __launch_bounds__(256) void gemm_wide_kernel(GemmSlice sl, int row_ti
   const int ks = blockIdx.y;
   const int kbeg = ks * a.kc;
   const int nst = max(0, min(a.d_in - kbeg, a.kc)) / 64;
-  const T* X = static_cast<const T*>(a.x);
-  const T* XR = static_cast<const T*>(a.x_rot);
-  const T* W = static_cast<const T*>(a.W);
 
-  // Sources of this lane's loads: instruction j < 4 loads x rows
-  // 32·wave + 8j .. +8 of the tile, j >= 4 W rows 32·wave + 8(j - 4) .. +8;
-  // lane = 8 · (row within the instruction) + LDS chunk.
-  const int lr = lane >> 3, lc = lane & 7;
-  const T* src[LI];
+  const T* src[wide_impl::LI] = {};
+  if (ro.prod) {
+    const T* X = static_cast<const T*>(a.x);
+    const T* XR = static_cast<const T*>(a.x_rot);
+    const T* W = static_cast<const T*>(a.W);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 32 * wave + 8 * j + lr;
-    const int i = row0 + r;
-    const T* base = X;  // rows past n read row 0; their results are not stored
-    if (i < a.n) {
-      base = X + (size_t)i * a.d_in;
-      if (a.rot_pos) {
-        const int rp = a.rot_pos[i];
-        if (rp >= 0) base = XR + (size_t)rp * a.d_in;
+    for (int j = 0; j < wide_impl::LI; ++j) {
+      const int r = wide_impl::producer_row(ro, j);
+      const T* base;
+      if (r < 128) {
+        const int i = row0 + r;
+        base = X;  // rows past n read row 0; their results are not stored
+        if (i < a.n) {
+          base = X + (size_t)i * a.d_in;
+          if (a.rot_pos) {
+            const int rp = a.rot_pos[i];
+            if (rp >= 0) base = XR + (size_t)rp * a.d_in;
+          }
+        }
+      } else {
+        base = W + (size_t)(col0 + r - 128) * a.d_in;
       }
+      src[j] = base + kbeg + wide_impl::producer_chunk_elems(ro, r);
     }
-    src[j] = base + kbeg + 8 * (lc ^ swz<2>(r));
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 32 * wave + 8 * j + lr;
-    src[4 + j] = W + (size_t)(col0 + r) * a.d_in + kbeg + 8 * (lc ^ swz<4>(r));
-  }
-  auto issue = [&](int st) {
-    unsigned char* buf = smem + (size_t)(st % S) * STAGE;
-#pragma unroll
-    for (int j = 0; j < LI; ++j)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src[j] + 64 * st),
-          (__attribute__((address_space(3))) void*)(buf + (j < 4 ? 0 : 128 * 128) + (size_t)(32 * wave + 8 * (j & 3)) * 128),
-          16, 0, 0);
-  };
-
-  int arow[4], brow[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) arow[b] = 64 * wc + perm_col<4>(i16, b);  // W rows (output columns)
-#pragma unroll
-  for (int m = 0; m < 4; ++m) brow[m] = 64 * wr + 16 * m + i16;          // x rows
   f32x4 acc[4][4];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  wide_impl::k_loop<T, S>(ro, src, nst, smem, acc);
+  wide_impl::exchange(ro, smem, acc);
+  if (ro.prod) return;
 
+  // Lane holds, for row block 2 grp + mm, 16 consecutive output columns.
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (st < nst) issue(st);
-  for (int it = 0; it < nst; ++it) {
-    // Slices issued after this one that may still be in flight.
-    const int younger = min(S - 2, nst - 1 - it);
-    __builtin_amdgcn_sched_barrier(0);
-    if (S >= 5 && younger >= 3)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LI));
-    else if (S >= 4 && younger == 2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LI));
-    else if (younger == 1)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(LI));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    if (it + S - 1 < nst) issue(it + S - 1);
-    const unsigned char* buf = smem + (size_t)(it % S) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int q = 4 * kk + g;
-      Vt af[4], bf[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        af[b] = *reinterpret_cast<const Vt*>(buf + 128 * 128 + arow[b] * 128 + 16 * (q ^ swz<4>(arow[b])));
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
-    }
-  }
-
-  // Lane holds, for row block m, 16 consecutive output columns.
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int row = row0 + 64 * wr + 16 * m + i16;
+  for (int mm = 0; mm < 2; ++mm) {
+    const int row = row0 + 64 * ro.wr + 16 * (2 * ro.grp + mm) + ro.i16;
     if (row >= a.n) continue;
-    const int col = col0 + 64 * wc + 16 * g;
+    const int col = col0 + 64 * ro.wc + 16 * ro.g;
     float v[16];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b) {
+      const f32x4 h4 = acc[b][mm];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[4 * b + q] = acc[b][m][q];
+      for (int q = 0; q < 4; ++q) v[4 * b + q] = h4[q];
+    }
     if (a.split == 1 && !a.h_fp32)
       store_run16<T>(static_cast<T*>(a.out) + (size_t)row * a.d_out + col, v);
     else
@@ -1240,14 +1182,15 @@ hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& sl, hipStrea
     return hipErrorInvalidValue;
   if (stages < 2 || stages > 5 || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
   const int row_tiles = (a.n + 127) / 128, col_tiles = a.d_out / 128;
-  const dim3 grid((unsigned)(row_tiles * col_tiles + side_workgroups(sl, 256)), (unsigned)a.split);
-  const size_t lds = (size_t)stages * 256 * 128;
-#define TPA_WIDE(SV)                                                                                         \
-  if (stages == SV) {                                                                                        \
-    if (dtype == 1)                                                                                          \
-      hipLaunchKernelGGL((gemm_wide_kernel<f16, SV>), grid, dim3(256), lds, s, sl, row_tiles, col_tiles);    \
-    else                                                                                                     \
-      hipLaunchKernelGGL((gemm_wide_kernel<bf16, SV>), grid, dim3(256), lds, s, sl, row_tiles, col_tiles);   \
+  const dim3 grid((unsigned)(row_tiles * col_tiles + side_workgroups(sl, wide_impl::THREADS)), (unsigned)a.split);
+  const dim3 block(wide_impl::THREADS);
+  const size_t lds = (size_t)stages * wide_impl::STAGE;
+#define TPA_WIDE(SV)                                                                                      \
+  if (stages == SV) {                                                                                     \
+    if (dtype == 1)                                                                                       \
+      hipLaunchKernelGGL((gemm_wide_kernel<f16, SV>), grid, block, lds, s, sl, row_tiles, col_tiles);     \
+    else                                                                                                  \
+      hipLaunchKernelGGL((gemm_wide_kernel<bf16, SV>), grid, block, lds, s, sl, row_tiles, col_tiles);    \
   }
   TPA_WIDE(2) TPA_WIDE(3) TPA_WIDE(4) TPA_WIDE(5)
 #undef TPA_WIDE

@@ -328,7 +328,8 @@ def test_large_batch_defaults_every_type(dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_deep_ring_default_for_long_split_k(dtype):
     """128 rows of a 14336 -> 4096 projection: 32 tiles x split 8, k ranges
-    of 1792, so the 128 x 128 kernel takes four LDS buffers by default."""
+    of 1792, through the 128 x 128 kernel with its default ring of four LDS
+    buffers."""
     n = 128
     wl = synth.tiny_mixed(seed=1280, n=n, d=14336, dtype=dtype, with_identity=True, d_out=4096)
     p = wl["projections"][0]
