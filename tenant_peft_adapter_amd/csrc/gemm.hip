@@ -885,12 +885,13 @@ __global__ __launch_bounds__(wide_impl::THREADS) void gemm_wide_kernel(GemmSlice
 // rows of x by 64 output columns (8 x 4 MFMA tiles, 128 fp32 accumulators
 // per lane).  Per 64-element k slice the tile's 256 x rows and 256 W rows
 // (64 KB) go straight into one of two LDS buffers (8 loads per wave).  Per
-// 32-element k step a wave reads 12 fragments from LDS for 32 MFMAs (the
-// 128 x 128 tile's waves read 8 for 16): with two waves per SIMD that is
-// 96 B per clock of LDS reads per CU at the MFMA rate, below the 128 B a CU
-// delivers, and the slices' trip from L2 into LDS is 32 B per clock instead
-// of 64.  Tile order, split partials and the shrink's reduction in extra
-// work-groups as in the 128 x 128 kernel.
+// 32-element k step a wave reads 12 fragments from LDS for 32 MFMAs, and
+// the slices' trip from L2 into LDS is 32 B per clock at the MFMA rate
+// instead of the 128 x 128 tile's 64.  The two waves of a SIMD work one
+// phase apart (below), so one reads fragments while the other multiplies:
+// a wave alone reads LDS at about 21 B per clock, its 12 KB per step take
+// about as long as its 32 MFMAs.  Tile order, split partials and the
+// shrink's reduction in extra work-groups as in the 128 x 128 kernel.
 template <typename T>
 __global__ __launch_bounds__(512) void gemm_big_kernel(Slices<GemmSlice> ts) {
   typedef typename Frag<T>::V Vt;
@@ -908,6 +909,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(Slices<GemmSlice> ts) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   const int wr = wave & 1, wc = wave >> 1;
+  const int grp = wave >> 2;
   const int ntile = row_tiles * col_tiles;
   if (local >= ntile) {
     if (blockIdx.y == 0) shrink_impl::shrink_reduce_item<T>(sl.side, (local - ntile) * 512 + tid);
@@ -971,31 +973,54 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(Slices<GemmSlice> ts) {
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (nst > 0) issue(0);
-  for (int it = 0; it < nst; ++it) {
+  Vt af[4], bf[8];
+  auto R = [&](int st, int kk) {
+    const unsigned char* buf = smem + (size_t)(st % S) * STAGE;
+    const int q = 4 * kk + g;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      af[b] = *reinterpret_cast<const Vt*>(buf + 256 * 128 + arow[b] * 128 + 16 * (q ^ swz<4>(arow[b])));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+  auto M = [&]() {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
+  };
+  auto bar = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Ping-pong: waves 0..3 and 4..7 (one of each per SIMD) run one phase
+  // apart, a phase being one k step's fragment reads or its 32 MFMAs, with a
+  // barrier between phases; group 1 enters one barrier later and group 0
+  // leaves through one more.  Each wave loads its share of slice it + 1 at
+  // the start of its first read phase of slice it (every read of that
+  // buffer, slice it - 1, is behind the barrier before it), and has it
+  // landed before the barrier that precedes group 0's reads of slice it + 1.
+  if (nst > 0) issue(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  bar();
+  if (grp == 1) bar();
+  for (int it = 0; it < nst; ++it) {
     if (it + 1 < nst) issue(it + 1);
-    const unsigned char* buf = smem + (size_t)(it % S) * STAGE;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int q = 4 * kk + g;
-      Vt af[4], bf[8];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        af[b] = *reinterpret_cast<const Vt*>(buf + 256 * 128 + arow[b] * 128 + 16 * (q ^ swz<4>(arow[b])));
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        bf[m] = *reinterpret_cast<const Vt*>(buf + brow[m] * 128 + 16 * (q ^ swz<2>(brow[m])));
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[b][m] = mma(acc[b][m], af[b], bf[m]);
-    }
+    R(it, 0);
+    bar();
+    M();
+    bar();
+    R(it, 1);
+    if (grp == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    bar();
+    M();
+    if (grp == 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    bar();
   }
+  if (grp == 0) bar();
 
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
