@@ -495,7 +495,17 @@ Config choose_config(const tpa_layer* L, int n) {
     }
     const int tiles = ((n + c.gemm_tile - 1) / c.gemm_tile) * (L->d_out / c.gemm_tile);
     int split = L->opt[TPA_OPT_GEMM_SPLIT];
-    if (split <= 0) split = std::max(1, std::min(L->d_in / 512, (256 + tiles - 1) / tiles));
+    if (split <= 0) {
+      // The direct-load kernels hold a CU per work-group: split k so that
+      // the grid fills at most one round (tiles x split <= 256).  A second,
+      // partial round of split work-groups costs more than the CUs it
+      // fills (base layer, 256 rows, 14336 outputs, 224 tiles: split 2
+      // 75.4 µs against 56.4 with 1; 768 rows, 14336 -> 4096, 192 tiles:
+      // 150.1 against 133.7).  The register-staged kernel's small
+      // work-groups share CUs: there the grid may overfill.
+      const int fill = c.gemm_path == 3 ? std::max(1, 256 / tiles) : (256 + tiles - 1) / tiles;
+      split = std::max(1, std::min(L->d_in / 512, fill));
+    }
     split = std::min(split, L->d_in / 64);
     c.gemm_kc = round_up((L->d_in + split - 1) / split, 64);
     c.gemm_split = (L->d_in + c.gemm_kc - 1) / c.gemm_kc;
