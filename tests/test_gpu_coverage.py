@@ -234,3 +234,44 @@ def test_shrink_items_of_64_columns_same_bits(n, dtype):
     y, h, xw = reference(p, sor)
     tol = {"f16": (0.01, 2e-3), "bf16": (0.05, 1.6e-2)}[dtype]
     check(outs[1], y, h, xw, mean_tol=tol[0], max_tol=tol[1], label="shrink 64 columns n=%d" % n)
+
+
+# ------------------------------------------------ short k in the prefill GEMMs ---
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,d_in,d_out,tile,split,stages,dtype", [
+    (65, 64, 128, 128, 0, 4, "f16"),     # one slice: the ring holds fewer slices than it could
+    (130, 128, 256, 128, 2, 4, "f16"),   # one slice per split, the shrink's reduction in the grid
+    (300, 192, 256, 128, 0, 5, "bf16"),  # three slices, a ring of five
+    (257, 192, 384, 128, 3, 2, "f16"),   # split 3 of one slice each, two buffers, ragged rows
+    (257, 64, 256, 256, 0, 0, "f16"),    # 256 x 256 tiles over one slice
+    (300, 128, 512, 256, 2, 0, "bf16"),  # 256 x 256 tiles, one slice per split
+])
+def test_direct_load_gemms_short_k(n, d_in, d_out, tile, split, stages, dtype):
+    """§2 "The LoRA schedule", base GEMM h = (xR)W: the direct-load prefill
+    kernels where the k range is shorter than their LDS ring (one to three
+    64-element slices per work-group, split or not), with ragged row tiles,
+    against the oracle.  The producer waves of the 128 x 128 kernel then
+    issue fewer slices before the loop than the ring holds, and the 256 x
+    256 kernel's two phases per slice run over a single slice."""
+    wl = synth.tiny_mixed(seed=7300 + n + d_in, n=n, d=d_in, dtype=dtype, with_identity=True, d_out=d_out)
+    p = wl["projections"][0]
+    opts = {4: 3, 10: tile, 11: 0}
+    if split:
+        opts[1] = split
+    if stages:
+        opts[8] = stages
+    L = make_layer(p, max_slots=8, max_rank=32, options=opts)
+    cfg = L.config(n)
+    assert (cfg["gemm_path"], cfg["gemm_tile"]) == (3, tile), cfg
+    if split:
+        assert cfg["gemm_split"] == split, cfg
+    if stages:
+        assert cfg["gemm_stages"] == stages, cfg
+    say("short k n=%d d_in=%d d_out=%d tile=%d split=%d stages=%d %s" % (n, d_in, d_out, tile, cfg["gemm_split"],
+                                                                        cfg["gemm_stages"], dtype))
+    y_gpu = run(L, p["x"], wl["slot_of_row"], dtype)
+    L.close()
+    y, h, xw = reference(p, wl["slot_of_row"])
+    tol = dict(mean_tol=0.01, max_tol=2e-3) if dtype == "f16" else dict(mean_tol=0.05, max_tol=1.6e-2)
+    check(y_gpu, y, h, xw, label="short k %d/%d/%d" % (n, d_in, d_out), **tol)
