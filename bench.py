@@ -904,23 +904,28 @@ def main():
     gemm_t = [max(st[2] * 1e-6, 1e-9) for st in stages]
     # Dominant kernel: the base-GEMM launch with the most algorithmic bytes.
     # A unit's decode GEMM instance takes the column-block width of its
-    # widest projection.
+    # widest projection.  A unit with no OFT tenant runs its shrink in the
+    # GEMM's own launch (no launch before it): that launch's bytes and time
+    # then include the shrink's, which leave the adapter path's.
     mb = 1 if n <= 16 else 2 if n <= 32 else 4
+    sg = [all(layers[i].config(n)["shrink_in_gemm"] for i in m) for m in units]
     gemm_bytes = [sum(kb[i]["gemm"]["bytes"] for i in m) for m in units]
-    du = max(range(len(units)), key=lambda u: gemm_bytes[u])
+    side_bytes = [sum(kb[i]["shrink"]["bytes"] for i in m) if sg[u] else 0 for u, m in enumerate(units)]
+    launch_bytes = [g + b for g, b in zip(gemm_bytes, side_bytes)]
+    du = max(range(len(units)), key=lambda u: launch_bytes[u])
     widest = max(units[du], key=lambda i: wl["projections"][i]["d_out"])
     cfg = layers[widest].config(n)
     dom_name = {0: "gemm_skinny_kernel<f16,%d,%d,%d>" % (mb, cfg["gemm_nb"], cfg["gemm_groups"]),
                 2: "gemm_stream_kernel<f16,%d,%d,%d,%d>" % (mb, cfg["gemm_nb"], cfg["gemm_groups"], cfg["gemm_stages"])
                 }.get(cfg["gemm_path"], "gemm_tiled_kernel<f16>")
-    dom_cfg = "nb=%d groups=%d stages=%d kc=%d split=%d" % (cfg["gemm_nb"], cfg["gemm_groups"], cfg["gemm_stages"],
-                                                             cfg["gemm_kc"], cfg["gemm_split"])
-    dom_bytes, dom_time = gemm_bytes[du], gemm_t[du]
-    gemm_bytes_all = sum(gemm_bytes)
+    dom_cfg = "nb=%d groups=%d stages=%d kc=%d split=%d shrink_in_launch=%d" % (
+        cfg["gemm_nb"], cfg["gemm_groups"], cfg["gemm_stages"], cfg["gemm_kc"], cfg["gemm_split"], int(sg[du]))
+    dom_bytes, dom_time = launch_bytes[du], gemm_t[du]
+    gemm_bytes_all = sum(launch_bytes)
     gemm_time_all = sum(gemm_t)
-    adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes)
-    adapter_time = sum(st[1] + st[4] for st in stages) * 1e-6
-    adapter_launches = len(step.plans) + 2 * len(units)
+    adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes) - sum(side_bytes)
+    adapter_time = sum((0.0 if sg[u] else st[1]) + st[4] for u, st in enumerate(stages)) * 1e-6
+    adapter_launches = len(step.plans) + sum(1 for g in sg if not g) + len(units)
     predicted = bm.predict_time(gemm_time_all, adapter_bytes, adapter_launches, beta, lam)
 
     ratio = t_pure = None
@@ -975,7 +980,7 @@ def main():
                    "warm_us_per_step": t_warm * 1e6, "warm_samples_us": [round(v * 1e6, 2) for v in warm_samples],
                    "steps_per_chain": [cold_copies, warm_copies],
                    "protocol": "graph chains of >= 2 ms, 5 rebuilds, median; cold rotates %d buffer sets "
-                               "(%.0f MB of weights)" % (args.sets, args.sets * gemm_bytes_all / 1e6)},
+                               "(%.0f MB of weights)" % (args.sets, args.sets * sum(gemm_bytes) / 1e6)},
         "eager_ms_per_step": t_eager * 1e3,
         "mixed_over_pure_lora": ratio,
         "pure_lora_us_per_step_cold": None if t_pure is None else t_pure * 1e6,
@@ -989,7 +994,8 @@ def main():
             "us_event_pair_cost": pair_cost * 1e6, "config": dom_cfg,
         },
         "base_gemm": {"bytes_per_step": gemm_bytes_all, "us_per_step": gemm_time_all * 1e6,
-                      "GBps": gemm_bytes_all / gemm_time_all / 1e9},
+                      "GBps": gemm_bytes_all / gemm_time_all / 1e9, "shrink_bytes_in_gemm_launches": sum(side_bytes),
+                      "units_with_shrink_in_gemm": [unit_names[u] for u in range(len(units)) if sg[u]]},
         "adapter_path": {"bytes_per_step": adapter_bytes, "us_per_step_shrink_oft_expand": adapter_time * 1e6,
                          "GBps": adapter_bytes / adapter_time / 1e9, "launches": adapter_launches,
                          "predicted_step_us": predicted * 1e6},

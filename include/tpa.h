@@ -466,11 +466,14 @@ tpa_status tpa_layer_set_option(tpa_layer* layer, int32_t key, int32_t value);
  * and k range, the scale route, the decode GEMM's k-groups per work-group
  * and (direct-load kernels, else 0) its LDS buffers (per k-group for the
  * streamed kernel), path 3's tile edge (128 or 256; else 0), and whether
- * the expand runs in the GEMM's epilogue (prefill or decode kernel), and the
- * factor columns per shrink item.  For tests and measurement. */
+ * the expand runs in the GEMM's epilogue (prefill or decode kernel), the
+ * factor columns per shrink item, and whether the shrink runs in the decode
+ * GEMM's own launch (one whole-k item per side work-group; a group forward
+ * does so only when every layer of the group can).  For tests and
+ * measurement. */
 typedef struct {
   int32_t tile_rows, gemm_path, gemm_nb, gemm_split, gemm_kc, shrink_split, shrink_kc, scale_route,
-      gemm_groups, gemm_stages, gemm_tile, fused_expand, shrink_cols;
+      gemm_groups, gemm_stages, gemm_tile, fused_expand, shrink_cols, shrink_in_gemm;
 } tpa_config;
 /* Appendix "Tuned kernels": the configuration in force for n rows. */
 tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);

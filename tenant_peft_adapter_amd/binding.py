@@ -56,7 +56,8 @@ class tpa_adapter_info(ctypes.Structure):
 class tpa_config(ctypes.Structure):
     _fields_ = [(k, ctypes.c_int32) for k in ("tile_rows", "gemm_path", "gemm_nb", "gemm_split", "gemm_kc",
                                               "shrink_split", "shrink_kc", "scale_route", "gemm_groups",
-                                              "gemm_stages", "gemm_tile", "fused_expand", "shrink_cols")]
+                                              "gemm_stages", "gemm_tile", "fused_expand", "shrink_cols",
+                                              "shrink_in_gemm")]
 
 
 class tpa_plan_host(ctypes.Structure):

@@ -208,6 +208,7 @@ struct Config {
   int fused;      // path 3, 128 x 128 tiles: the expand runs in the GEMM's epilogue
   int h_fp32;     // h goes to the expand in fp32 even when k is not split
   int fused_dec;  // path 2: the expand runs in the streamed GEMM's epilogue, after a whole-k shrink
+  int shrink_in_gemm;  // path 2, no OFT: the shrink runs whole-k in the GEMM's side work-groups
   int shrink_ncb; // 16-column blocks per shrink item (1 or 4)
 };
 
@@ -399,6 +400,7 @@ void set_shrink_split(const tpa_layer* L, int n, Config* c) {
   if (ssplit <= 0) {
     ssplit = n >= 2048 ? std::max(1, std::min(8, L->d_in / 512)) : std::max(1, std::min(28, L->d_in / 256));
     if (c->fused_dec) ssplit = std::min(ssplit, tpa::PRE_WHOLE_WAVES);
+    if (c->shrink_in_gemm) ssplit = 4 * c->gemm_groups;  // one k range per wave of a GEMM work-group
   }
   ssplit = std::min(ssplit, L->d_in / 32);
   c->shrink_kc = round_up((L->d_in + ssplit - 1) / ssplit, 32);
@@ -552,6 +554,15 @@ Config choose_config(const tpa_layer* L, int n) {
   // rounded to the layer type before the expand would carry |s|·u·|h| of
   // error: such layers keep h in fp32 between the GEMM and the expand.
   c.h_fp32 = L->n_stack > 0 && !c.fused && !c.fused_dec;
+  // Decode on the streamed GEMM with no OFT tenant on the layer: nothing
+  // has to run before the GEMM, so the shrink runs in the GEMM's own grid
+  // (side work-groups, one whole-k item each, V and U final when the GEMM
+  // ends), and the launch before it goes.  Not with a pinned shrink split
+  // or the second stream.
+  c.shrink_in_gemm = c.gemm_path == 2 && !c.fused_dec && L->dtype != TPA_F32 && c.tile_rows == 16 &&
+                     L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] == 0 && (L->n_owned > 0 || L->n_vera > 0) &&
+                     L->opt[TPA_OPT_SHRINK_SPLIT] <= 0 && L->opt[TPA_OPT_OVERLAP] != 1 &&
+                     L->opt[TPA_OPT_SHRINK_COLS] != 64;
   set_shrink_split(L, n, &c);
   // Shrink items of 64 factor columns (one read of the tile's x rows for
   // four column blocks) where there are items enough to fill the chip
@@ -1696,6 +1707,7 @@ void group_configs(tpa_layer* const* Ls, int count, int n, Config* cs) {
     cs[i].gemm_stages = S;
     cs[i].gemm_kc = std::min(kc, round_up(Ls[i]->d_in, 64 * (stream ? G : 1)));
     cs[i].gemm_split = (Ls[i]->d_in + cs[i].gemm_kc - 1) / cs[i].gemm_kc;
+    if (cs[i].shrink_in_gemm) set_shrink_split(Ls[i], n, &cs[i]);  // one k range per wave of the launch's groups
     fits = fits && fused_dec_fits(Ls[i], n, cs[i]);
   }
   // (a shrink capped for the fused epilogue stays valid without it)
@@ -1775,12 +1787,17 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     all_unsplit = all_unsplit && sl[i].c.gemm_split == 1;
   }
   const bool fdec = sl[0].c.fused_dec && (any_term_all || any_oft || all_unsplit);
+  // Decode projections without OFT: the shrink runs in the GEMM's side
+  // work-groups (every projection of the group or none).
+  bool sgemm = !fdec && any_term_all;
+  for (int i = 0; i < count; ++i)
+    sgemm = sgemm && sl[i].c.shrink_in_gemm && !oft[i] && sl[i].c.shrink_ncb == 1 && sl[i].c.gemm_path == 2;
   for (int i = 1; i < count; ++i) {
     const tpa_layer* L = sl[i].L;
     if (term[i] && term[0] && L->n_vera > 0 && L0->n_vera > 0 && L->vera_At && L->vera_At == L0->vera_At &&
         sl[i].x == sl[0].x && L->r_v == L0->r_v && sh[i].split == sh[0].split && sh[i].kc == sh[0].kc) {
       sh[i].sh_ntiles = 0;
-      if (fdec) {
+      if (fdec || sgemm) {
         sh[i].borrows = 1;
       } else {
         sh[i].part_shared = sh[0].part;
@@ -1856,7 +1873,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     TPA_HIP(tpa::launch_pre(dtype, tile_rows, kBs[b], ps, count, s, fdec, ncb));
     sh_done = true;
   }
-  if (!sh_done && any_term_all) {
+  if (!sh_done && any_term_all && !sgemm) {
     for (int i = 0; i < count; ++i) ps[i] = tpa::make_pre_slice(term[i] ? &sh[i] : nullptr, nullptr, fdec);
     if (fdec) clear_counters(ps);
     TPA_HIP(tpa::launch_pre(dtype, tile_rows, 0, ps, count, s, fdec, ncb));
@@ -1908,6 +1925,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     g.out = sl[i].out;
     gs[i].side = sh[i];
     gs[i].has_side = term[i] && !overlap && !fdec ? 1 : 0;
+    gs[i].side_whole = sgemm ? 1 : 0;
     gs[i].e = tpa::ExpandArgs{};
     gs[i].pinfo = nullptr;
     gs[i].cnt = nullptr;
@@ -2322,6 +2340,7 @@ tpa_status tpa_layer_config(const tpa_layer* L, int32_t n, tpa_config* out) {
   const bool pre = L->n_owned > 0 || L->n_vera > 0 || L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] > 0;
   out->fused_expand = c.fused || (c.fused_dec && (pre || c.gemm_split == 1));
   out->shrink_cols = 16 * c.shrink_ncb;
+  out->shrink_in_gemm = c.shrink_in_gemm;
   return TPA_OK;
 }
 

@@ -518,7 +518,11 @@ __global__ __launch_bounds__(256 * G) void gemm_stream_kernel(Slices<GemmSlice> 
   const int col_tiles = a.d_out / WROWS;
   const int n_gemm = col_tiles * a.split;
   if (local >= n_gemm) {
-    shrink_impl::shrink_reduce_item<T>(t.s[si].side, (local - n_gemm) * 256 * G + tid);
+    if (t.s[si].side_whole)
+      shrink_impl::shrink_whole_item<T, 4 * G>([&](int j) -> const ShrinkArgs& { return t.s[j].side; }, t.count, si,
+                                               local - n_gemm, tid >> 6, lane, reinterpret_cast<f32x4*>(smem));
+    else
+      shrink_impl::shrink_reduce_item<T>(t.s[si].side, (local - n_gemm) * 256 * G + tid);
     return;
   }
   const int col0 = (local % col_tiles) * WROWS;
@@ -1142,7 +1146,7 @@ hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* sl
   if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
   for (int i = 0; i < count; ++i) {
     const BaseGemmArgs& a = slices[i].g;
-    if (a.n <= 0 || a.n > 64 || a.n != slices[0].g.n || a.kc % 64 || a.d_out % (64 * nb))
+    if (a.n <= 0 || a.n > 64 || a.n != slices[0].g.n || a.kc % 64 || a.d_out % (64 * nb) || slices[i].side_whole)
       return hipErrorInvalidValue;
     if (gemm_skinny_lds(dtype, a.n, nb, dtype == 0 ? 1 : groups, a.kc) > GEMM_SKINNY_MAX_LDS)
       return hipErrorInvalidValue;
@@ -1181,6 +1185,12 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
     if (a.n <= 0 || a.n > 256 || a.n != slices[0].g.n || a.kc <= 0 || a.kc % 64 || a.d_in % 64 ||
         a.d_out % (64 * nb) || (long)a.split * a.kc < a.d_in)
       return hipErrorInvalidValue;
+    // Whole-k shrink items in the side work-groups: one k range per wave
+    // of a work-group, covering d_in; not beside the fused epilogue.
+    const ShrinkArgs& sh = slices[i].side;
+    if (slices[i].has_side && slices[i].side_whole &&
+        (epi || sh.split < 1 || sh.split > 4 * groups || sh.kc <= 0 || sh.kc % 32 || (long)sh.split * sh.kc < sh.d_in))
+      return hipErrorInvalidValue;
     if (epi) {
       // The epilogue's tables: every row, every entry of the tile list (one
       // thread each) and the k steps of the largest factor per entry.
@@ -1203,7 +1213,8 @@ hipError_t launch_gemm_stream(int dtype, int nb, int groups, int stages, const G
 
 hipError_t launch_gemm_wide(int dtype, int stages, const GemmSlice& sl, hipStream_t s) {
   const BaseGemmArgs& a = sl.g;
-  if (a.n <= 0 || a.d_out % 128 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in)
+  if (a.n <= 0 || a.d_out % 128 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 || (long)a.split * a.kc < a.d_in ||
+      sl.side_whole)
     return hipErrorInvalidValue;
   if (stages < 2 || stages > 5 || (dtype != 1 && dtype != 2)) return hipErrorInvalidValue;
   const int row_tiles = (a.n + 127) / 128, col_tiles = a.d_out / 128;
@@ -1230,7 +1241,7 @@ hipError_t launch_gemm_big(int dtype, const GemmSlice* slices, int count, hipStr
   for (int i = 0; i < count; ++i) {
     const BaseGemmArgs& a = slices[i].g;
     if (a.n <= 0 || a.n != slices[0].g.n || a.d_out % 256 || a.d_in % 64 || a.kc <= 0 || a.kc % 64 ||
-        (long)a.split * a.kc < a.d_in || a.split != slices[0].g.split)
+        (long)a.split * a.kc < a.d_in || a.split != slices[0].g.split || slices[i].side_whole)
       return hipErrorInvalidValue;
     t.s[i] = slices[i];
     // Each projection's range starts on a multiple of 8 work-groups, so its

@@ -183,6 +183,11 @@ struct GemmSlice {
   BaseGemmArgs g;
   ShrinkArgs side;
   int32_t has_side;
+  // Streamed decode GEMM only: the side work-groups run the shrink itself,
+  // one whole-k item each (its k ranges on the work-group's waves, added in
+  // LDS in wave order), instead of adding split partials of a launch
+  // before; nothing before the GEMM writes V or U.
+  int32_t side_whole;
   // Streamed decode GEMM with the expand in its epilogue (launch_gemm_stream
   // with epi): the expand's arguments (out, tiles, slots, vera_Bt, r_v, v,
   // kmax, n, d_out; max_tiles entries of the tile list are read), the
@@ -192,9 +197,12 @@ struct GemmSlice {
   const int32_t* pinfo;
   int32_t* cnt;
 };
-// Work-groups of `threads` threads that a slice's split reduction takes.
+// Work-groups of `threads` threads that a slice's split reduction takes,
+// or, with side_whole, one per whole-k shrink item.
 inline int side_workgroups(const GemmSlice& sl, int threads) {
-  return sl.has_side ? (int)(((long)sl.side.n * (sl.side.kmax / 4) + threads - 1) / threads) : 0;
+  if (!sl.has_side) return 0;
+  if (sl.side_whole) return sl.side.own_tiles * sl.side.own_nblk + sl.side.sh_ntiles * sl.side.sh_nblk;
+  return (int)(((long)sl.side.n * (sl.side.kmax / 4) + threads - 1) / threads);
 }
 hipError_t launch_gemm_skinny(int dtype, int nb, int groups, const GemmSlice* slices, int count,
                               hipStream_t stream);

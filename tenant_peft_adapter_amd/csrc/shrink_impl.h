@@ -179,12 +179,15 @@ __device__ __forceinline__ void shrink_reduce_item(const ShrinkArgs& a, int idx)
 // that borrows its x·A_vᵀ (each with its own d').  Every early return
 // depends only on the item, so the work-group takes it together and the
 // barrier is met by all of its waves.
-template <typename T, int Q>
-__device__ __forceinline__ void shrink_whole(const Slices<PreSlice>& t, int si, int item, int wave, int lane,
-                                             f32x4* red) {
+// The item reaches the launch's slices through sh_of(j) (the ShrinkArgs of
+// slice j, j < count): the launch before the GEMM and the decode GEMM's
+// side work-groups both run it.
+template <typename T, int Q, typename ShOf>
+__device__ __forceinline__ void shrink_whole_item(ShOf sh_of, int count, int si, int item, int wave, int lane,
+                                                  f32x4* red) {
   typedef typename Frag<T>::V Vt;
   constexpr int U = 8;
-  const ShrinkArgs& a = t.s[si].sh;
+  const ShrinkArgs& a = sh_of(si);
   const int own_items = a.own_tiles * a.own_nblk;
   const int i16 = lane & 15, g = lane >> 4;
   const int* tile;
@@ -253,8 +256,8 @@ __device__ __forceinline__ void shrink_whole(const Slices<PreSlice>& t, int si, 
   if (col >= N) return;
   const int p = tl.x + i16;
   const int slot = (int)((unsigned)rw >> 16);
-  for (int j = 0; j < t.count; ++j) {
-    const ShrinkArgs& b = t.s[j].sh;
+  for (int j = 0; j < count; ++j) {
+    const ShrinkArgs& b = sh_of(j);
     const bool mine = j == si;
     if (!mine && !(want == CLS_SHARED && si == 0 && b.borrows)) continue;
     f32x4 o = v;
@@ -263,6 +266,12 @@ __device__ __forceinline__ void shrink_whole(const Slices<PreSlice>& t, int si, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) dst[q] = to_t<T>(o[q]);
   }
+}
+
+template <typename T, int Q>
+__device__ __forceinline__ void shrink_whole(const Slices<PreSlice>& t, int si, int item, int wave, int lane,
+                                             f32x4* red) {
+  shrink_whole_item<T, Q>([&](int j) -> const ShrinkArgs& { return t.s[j].sh; }, t.count, si, item, wave, lane, red);
 }
 
 }  // namespace shrink_impl
