@@ -333,17 +333,32 @@ tpa_status scratch_address(int device, void** out) {
 
 // k range of the streamed decode GEMM for a grid of `col_tiles` column tiles
 // (summed over the projections of one launch) over d_in: the largest power
-// of two with at most 16 slices of 64 per k-group and >= 192 work-groups.
+// of two with at most 16 slices of 64 per k-group and >= 192 work-groups,
+// or >= 128 where the launch also carries the whole shrink (its items keep
+// the other CUs busy, and half the split partials are written and read
+// again: o, 4096 -> 4096 at 64 rows, 23.3 -> 18.8 µs for GEMM + expand).
 // (Whole-d_in ranges for gate + up, whose 224 column tiles alone fill the
 // grid, write h once in the layer type but made the decode step slower:
 // 208 against 200-204 µs.)
-int stream_kc(long col_tiles, int d_in, int groups) {
+int stream_kc(long col_tiles, int d_in, int groups, bool side_shrink) {
+  const long min_wgs = side_shrink ? 128 : 192;
   int kc = 64 * groups;
   for (int cand = 4096; cand >= 64 * groups; cand /= 2) {
     if (cand > 1024 * groups) continue;
-    if (col_tiles * ((d_in + cand - 1) / cand) >= 192) return cand;
+    if (col_tiles * ((d_in + cand - 1) / cand) >= min_wgs) return cand;
   }
   return kc;
+}
+
+// The conditions, other than the GEMM path, for a decode shrink to run in the
+// streamed GEMM's own launch: nothing else has to run before the GEMM (no OFT
+// tenant), a term to compute, 16-row tiles of a 16-bit type, 16-column items,
+// and no option that keeps the launch before (a pinned shrink split, the
+// second stream, the opt-in fused epilogue).
+bool shrink_in_gemm_ok(const tpa_layer* L, int tile_rows) {
+  return L->dtype != TPA_F32 && tile_rows == 16 && L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] == 0 &&
+         (L->n_owned > 0 || L->n_vera > 0) && L->opt[TPA_OPT_SHRINK_SPLIT] <= 0 && L->opt[TPA_OPT_OVERLAP] != 1 &&
+         L->opt[TPA_OPT_SHRINK_COLS] != 64 && L->opt[TPA_OPT_FUSE_EXPAND] != 1;
 }
 
 // k-groups and k range of one streamed decode-GEMM launch over `count`
@@ -355,9 +370,11 @@ void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stage
                  int* kc_out) {
   long col_tiles = 0;
   int d_in = 0;
+  bool side_shrink = true;
   for (int i = 0; i < count; ++i) {
     col_tiles += Ls[i]->d_out / (64 * nb);
     d_in = std::max(d_in, Ls[i]->d_in);
+    side_shrink = side_shrink && shrink_in_gemm_ok(Ls[i], Ls[i]->opt[TPA_OPT_TILE_ROWS] > 0 ? Ls[i]->opt[TPA_OPT_TILE_ROWS] : 16);
   }
   long best_rounds = 0;
   *groups = 0;
@@ -366,7 +383,7 @@ void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stage
     if (G > 1 && stages != 3) continue;
     const size_t lds = tpa::gemm_stream_lds(n, nb, G, stages);
     if (lds > tpa::GEMM_STREAM_MAX_LDS) continue;
-    const int kc = stream_kc(col_tiles, d_in, G);
+    const int kc = stream_kc(col_tiles, d_in, G, side_shrink);
     long total = 0;
     for (int i = 0; i < count; ++i) {
       total += (long)(Ls[i]->d_out / (64 * nb)) * ((Ls[i]->d_in + kc - 1) / kc);
@@ -382,7 +399,7 @@ void stream_pick(const tpa_layer* const* Ls, int count, int n, int nb, int stage
   }
   if (*groups == 0) {  // nothing fits the options: one group, three stages
     *groups = 1;
-    *kc_out = stream_kc(col_tiles, d_in, 1);
+    *kc_out = stream_kc(col_tiles, d_in, 1, side_shrink);
   }
 }
 
@@ -559,10 +576,7 @@ Config choose_config(const tpa_layer* L, int n) {
   // (side work-groups, one whole-k item each, V and U final when the GEMM
   // ends), and the launch before it goes.  Not with a pinned shrink split
   // or the second stream.
-  c.shrink_in_gemm = c.gemm_path == 2 && !c.fused_dec && L->dtype != TPA_F32 && c.tile_rows == 16 &&
-                     L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] == 0 && (L->n_owned > 0 || L->n_vera > 0) &&
-                     L->opt[TPA_OPT_SHRINK_SPLIT] <= 0 && L->opt[TPA_OPT_OVERLAP] != 1 &&
-                     L->opt[TPA_OPT_SHRINK_COLS] != 64;
+  c.shrink_in_gemm = c.gemm_path == 2 && !c.fused_dec && shrink_in_gemm_ok(L, c.tile_rows);
   set_shrink_split(L, n, &c);
   // Shrink items of 64 factor columns (one read of the tile's x rows for
   // four column blocks) where there are items enough to fill the chip

@@ -27,7 +27,7 @@ from workloads import synth
 
 pytestmark = pytest.mark.gpu
 
-SHRINK_SPLIT, GROUPS = 2, 7
+SHRINK_SPLIT, GROUPS, GEMM_SPLIT = 2, 7, 1
 
 _WL = {}
 
@@ -65,9 +65,13 @@ def test_shrink_in_gemm_matches_split_shrink(dtype, name, n):
     again = run(L, x, sor, dtype)
     L.close()
     assert np.array_equal(got, again)
-    Lp = make_layer(p, max_slots=32, max_rank=256, options={SHRINK_SPLIT: 4 * groups})
+    # (the GEMM's k-groups and split pinned too: a launch that carries the
+    # shrink may take longer k ranges)
+    Lp = make_layer(p, max_slots=32, max_rank=256,
+                    options={SHRINK_SPLIT: 4 * groups, GROUPS: groups, GEMM_SPLIT: cfg["gemm_split"]})
     cp = Lp.config(n)
     assert cp["shrink_in_gemm"] == 0 and cp["shrink_kc"] == cfg["shrink_kc"], (cp, cfg)
+    assert (cp["gemm_kc"], cp["gemm_groups"]) == (cfg["gemm_kc"], groups), (cp, cfg)
     want = run(Lp, x, sor, dtype)
     Lp.close()
     assert np.array_equal(got, want), float(np.abs(got - want).max())
