@@ -480,8 +480,9 @@ tpa_status tpa_layer_config(const tpa_layer* layer, int32_t n, tpa_config* out);
 
 /* Stage timing: when `events` is non-null, each forward records events[0]
  * before its first kernel and events[1..5] after the plan, the launch of the
- * shrink with OFT's rotation, the base GEMM (which also carries the shrink's
- * split reduction on the decode path), any scale pass that runs before the
+ * shrink with OFT's rotation (none where the decode GEMM carries the whole
+ * shrink), the base GEMM (which also carries the shrink's split reduction,
+ * or the whole shrink, on the decode path), any scale pass that runs before the
  * expand, and the expand (with any scale pass after it), all on its stream.
  * `events` are hipEvent_t handles owned by the caller; count must be 6 (or 0
  * with null to stop).  For profiling only. */
