@@ -904,9 +904,8 @@ def main():
     gemm_t = [max(st[2] * 1e-6, 1e-9) for st in stages]
     # Dominant kernel: the base-GEMM launch with the most algorithmic bytes.
     # A unit's decode GEMM instance takes the column-block width of its
-    # widest projection.  A unit with no OFT tenant runs its shrink in the
-    # GEMM's own launch (no launch before it): that launch's bytes and time
-    # then include the shrink's, which leave the adapter path's.
+    # widest projection.  A unit whose shrink runs in the GEMM's own launch
+    # counts the shrink's bytes and time there, not in the adapter path.
     mb = 1 if n <= 16 else 2 if n <= 32 else 4
     sg = [all(layers[i].config(n)["shrink_in_gemm"] for i in m) for m in units]
     gemm_bytes = [sum(kb[i]["gemm"]["bytes"] for i in m) for m in units]
@@ -923,9 +922,12 @@ def main():
     dom_bytes, dom_time = launch_bytes[du], gemm_t[du]
     gemm_bytes_all = sum(launch_bytes)
     gemm_time_all = sum(gemm_t)
+    # A launch before the GEMM remains where the shrink runs there or OFT
+    # tenants need their rotation.
+    pre = [not sg[u] or any(kb[i]["oft"]["launches"] for i in m) for u, m in enumerate(units)]
     adapter_bytes = sum(bm.adapter_path_bytes(s) for s in shapes) - sum(side_bytes)
-    adapter_time = sum((0.0 if sg[u] else st[1]) + st[4] for u, st in enumerate(stages)) * 1e-6
-    adapter_launches = len(step.plans) + sum(1 for g in sg if not g) + len(units)
+    adapter_time = sum((st[1] if pre[u] else 0.0) + st[4] for u, st in enumerate(stages)) * 1e-6
+    adapter_launches = len(step.plans) + sum(pre) + len(units)
     predicted = bm.predict_time(gemm_time_all, adapter_bytes, adapter_launches, beta, lam)
 
     ratio = t_pure = None

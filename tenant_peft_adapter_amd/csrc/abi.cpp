@@ -351,14 +351,14 @@ int stream_kc(long col_tiles, int d_in, int groups, bool side_shrink) {
 }
 
 // The conditions, other than the GEMM path, for a decode shrink to run in the
-// streamed GEMM's own launch: nothing else has to run before the GEMM (no OFT
-// tenant), a term to compute, 16-row tiles of a 16-bit type, 16-column items,
-// and no option that keeps the launch before (a pinned shrink split, the
-// second stream, the opt-in fused epilogue).
+// streamed GEMM's own launch: a term to compute, 16-row tiles of a 16-bit
+// type, 16-column items, and no option that keeps it in the launch before
+// (a pinned shrink split, the second stream, the opt-in fused epilogue).
+// OFT's rotation, which the GEMM reads, still runs before it.
 bool shrink_in_gemm_ok(const tpa_layer* L, int tile_rows) {
-  return L->dtype != TPA_F32 && tile_rows == 16 && L->n_oft_bs[0] + L->n_oft_bs[1] + L->n_oft_bs[2] == 0 &&
-         (L->n_owned > 0 || L->n_vera > 0) && L->opt[TPA_OPT_SHRINK_SPLIT] <= 0 && L->opt[TPA_OPT_OVERLAP] != 1 &&
-         L->opt[TPA_OPT_SHRINK_COLS] != 64 && L->opt[TPA_OPT_FUSE_EXPAND] != 1;
+  return L->dtype != TPA_F32 && tile_rows == 16 && (L->n_owned > 0 || L->n_vera > 0) &&
+         L->opt[TPA_OPT_SHRINK_SPLIT] <= 0 && L->opt[TPA_OPT_OVERLAP] != 1 && L->opt[TPA_OPT_SHRINK_COLS] != 64 &&
+         L->opt[TPA_OPT_FUSE_EXPAND] != 1;
 }
 
 // k-groups and k range of one streamed decode-GEMM launch over `count`
@@ -571,11 +571,11 @@ Config choose_config(const tpa_layer* L, int n) {
   // rounded to the layer type before the expand would carry |s|·u·|h| of
   // error: such layers keep h in fp32 between the GEMM and the expand.
   c.h_fp32 = L->n_stack > 0 && !c.fused && !c.fused_dec;
-  // Decode on the streamed GEMM with no OFT tenant on the layer: nothing
-  // has to run before the GEMM, so the shrink runs in the GEMM's own grid
-  // (side work-groups, one whole-k item each, V and U final when the GEMM
-  // ends), and the launch before it goes.  Not with a pinned shrink split
-  // or the second stream.
+  // Decode on the streamed GEMM: the shrink needs nothing the GEMM makes,
+  // so it runs in the GEMM's own grid (side work-groups, one whole-k item
+  // each, V and U final when the GEMM ends); the launch before the GEMM
+  // goes, or keeps only OFT's rotation.  Not with a pinned shrink split or
+  // the second stream.
   c.shrink_in_gemm = c.gemm_path == 2 && !c.fused_dec && shrink_in_gemm_ok(L, c.tile_rows);
   set_shrink_split(L, n, &c);
   // Shrink items of 64 factor columns (one read of the tile's x rows for
@@ -1801,11 +1801,12 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     all_unsplit = all_unsplit && sl[i].c.gemm_split == 1;
   }
   const bool fdec = sl[0].c.fused_dec && (any_term_all || any_oft || all_unsplit);
-  // Decode projections without OFT: the shrink runs in the GEMM's side
-  // work-groups (every projection of the group or none).
+  // Decode projections on the streamed GEMM: the shrink runs in the GEMM's
+  // side work-groups (every projection of the group or none); OFT's
+  // rotation keeps its launch before the GEMM.
   bool sgemm = !fdec && any_term_all;
   for (int i = 0; i < count; ++i)
-    sgemm = sgemm && sl[i].c.shrink_in_gemm && !oft[i] && sl[i].c.shrink_ncb == 1 && sl[i].c.gemm_path == 2;
+    sgemm = sgemm && sl[i].c.shrink_in_gemm && sl[i].c.shrink_ncb == 1 && sl[i].c.gemm_path == 2;
   for (int i = 1; i < count; ++i) {
     const tpa_layer* L = sl[i].L;
     if (term[i] && term[0] && L->n_vera > 0 && L0->n_vera > 0 && L->vera_At && L->vera_At == L0->vera_At &&
@@ -1880,7 +1881,7 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     if (!any) continue;
     for (int i = 0; i < count; ++i) {
       of[i].block = kBs[b];
-      ps[i] = tpa::make_pre_slice(!sh_done && term[i] ? &sh[i] : nullptr,
+      ps[i] = tpa::make_pre_slice(!sh_done && !sgemm && term[i] ? &sh[i] : nullptr,
                                   sl[i].L->n_oft_bs[b] ? &of[i] : nullptr, fdec);
     }
     if (fdec) clear_counters(ps);

@@ -2,21 +2,21 @@
 launch (Scute paper, §2 "The LoRA schedule": the shrink V = x A of each
 tile; §4.1: the base product and the terms of one layer in one pass).
 
-With no OFT tenant on a projection nothing has to run before its base
-GEMM, so the work-groups past the GEMM's tiles each take one (tile, 16
-factor columns) item of the shrink over the whole of k: one k range per
-wave, added in wave order.  The launch before the GEMM is gone, and V comes
-out with the bits the split shrink and its reduction give on the same k
-ranges (a pinned shrink split of 4 ranges per k-group keeps the separate
-launch).  Checked here:
+The shrink needs nothing the base GEMM makes, so the work-groups past the
+GEMM's tiles each take one (tile, 16 factor columns) item of the shrink
+over the whole of k: one k range per wave, added in wave order.  The launch
+before the GEMM is gone (or, on a projection with OFT tenants, keeps only
+their rotation), and V comes out with the bits the split shrink and its
+reduction give on the same k ranges (a pinned shrink split of 4 ranges per
+k-group keeps the separate launch).  Checked here:
 
-  * o, gate, up and down of the decoder-layer workload, f16 and bf16, at
-    64, 17 (a ragged last tile) and 1 row: the same bits as the pinned split
-    and the oracle's bar;
+  * every projection of the decoder-layer workload (q, k and v with OFT
+    tenants), f16 and bf16, at 64, 17 (a ragged last tile) and 1 row: the
+    same bits as the pinned split and the oracle's bar;
   * the gate / up group, whose up projection borrows VeRA's x A_v from gate
-    (one item writes both projections' scaled columns), and an o / down
-    group with two inputs;
-  * a projection with OFT tenants (q) keeps the launch before the GEMM;
+    (one item writes both projections' scaled columns), the q / k / v group
+    (OFT rotation before the GEMM, VeRA's x A_v borrowed by k and v), and
+    an o / down group with two inputs;
   * repeated calls give the same bits (every item overwrites its V)."""
 import numpy as np
 import pytest
@@ -47,7 +47,7 @@ def _tol(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("name", ["o", "gate", "up", "down"])
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
 @pytest.mark.parametrize("n", [64, 17, 1])
 def test_shrink_in_gemm_matches_split_shrink(dtype, name, n):
     wl = _workload(dtype)
@@ -105,7 +105,7 @@ def _group_outputs(projs, n, sor, opts, borrow):
     return cfgs, outs
 
 
-@pytest.mark.parametrize("names,borrow", [(("gate", "up"), True), (("o", "down"), False)])
+@pytest.mark.parametrize("names,borrow", [(("gate", "up"), True), (("q", "k", "v"), True), (("o", "down"), False)])
 def test_shrink_in_gemm_group(names, borrow):
     wl = _workload("f16")
     projs = [_proj(wl, nm) for nm in names]
@@ -122,15 +122,3 @@ def test_shrink_in_gemm_group(names, borrow):
         assert np.array_equal(g, w), (nm, float(np.abs(g - w).max()))
         y, h, xw = reference({**p, "x": projs[0]["x"]} if borrow else p, wl["slot_of_row"])
         check(g, y, h, xw, label="shrink in GEMM group " + nm)
-
-
-def test_oft_projection_keeps_launch_before_gemm():
-    wl = _workload("f16")
-    p = _proj(wl, "q")
-    L = make_layer(p, max_slots=32, max_rank=256)
-    cfg = L.config(wl["n"])
-    assert cfg["gemm_path"] == 2 and cfg["shrink_in_gemm"] == 0, cfg
-    got = run(L, p["x"], wl["slot_of_row"], "f16")
-    L.close()
-    y, h, xw = reference(p, wl["slot_of_row"])
-    check(got, y, h, xw, label="q with OFT")
