@@ -1913,6 +1913,9 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     ea.d_out = L->d_out;
     ea.max_tiles = all_tile_bound(L, n, tile_rows, sl[i].y.max_tiles);
     ea.apply_scale = c.scale_route == 0;
+    ea.sh_tiles = L->n_vera > 0 ? p.sh_tiles : nullptr;
+    ea.sh_rows_w = L->n_vera > 0 ? p.sh_rows_w : nullptr;
+    ea.max_sh_tiles = L->n_vera > 0 ? p.max_sh_tiles : 0;
     return ea;
   };
 

@@ -70,8 +70,11 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
 // layer, 4096 rows 2876 -> 2847); at decode sizes the longer dependent
 // chain of a rank-256 VeRA tile costs more (decoder layer 203.7 -> 206.2
 // µs per step), so small batches keep four.
+// Up to two ranges per projection: its shared-term tiles, then the rest.
+typedef Slices<ExpandArgs, 2 * MAX_SLICES> ExpandSlices;
+
 template <typename T, int MB, bool HPART, bool FEW>
-__global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
+__global__ __launch_bounds__(64) void expand_kernel(ExpandSlices t) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fewer for wide fragments)
   constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 2 : 1) : (MB == 1 && !FEW ? 4 : 2);
@@ -89,6 +92,7 @@ __global__ __launch_bounds__(64) void expand_kernel(Slices<ExpandArgs> t) {
   for (int m = 0; m < MB; ++m) rw[m] = a.tile_rows_w[(size_t)ti * 16 * MB + 16 * m + i16];
   const int p0 = tl.x, kind = tl.z;
   if (kind < 0) return;  // padding past the plan's last tile
+  if (a.part == 2 && kind == CLS_SHARED) return;  // done in the projection's first range
   const int n0 = (local % ncb) * 64;
   const int col = n0 + 16 * g;
 
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
 }
 
 template <typename T, int MB>
-hipError_t expand_launch(const Slices<ExpandArgs>& t, hipStream_t s) {
+hipError_t expand_launch(const ExpandSlices& t, hipStream_t s) {
   const dim3 grid((unsigned)t.first[t.count]);
   const bool few = sizeof(T) == 2 && MB == 1 && t.s[0].n > 256;
   if (t.s[0].hpart) {
@@ -278,7 +282,7 @@ hipError_t expand_launch(const Slices<ExpandArgs>& t, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t expand_tm(int tile_rows, const Slices<ExpandArgs>& t, hipStream_t s) {
+hipError_t expand_tm(int tile_rows, const ExpandSlices& t, hipStream_t s) {
   if (tile_rows == 16) return expand_launch<T, 1>(t, s);
   if (tile_rows == 64) return expand_launch<T, 4>(t, s);
   return hipErrorInvalidValue;
@@ -286,18 +290,38 @@ hipError_t expand_tm(int tile_rows, const Slices<ExpandArgs>& t, hipStream_t s) 
 
 }  // namespace
 
+// Work-groups are dispatched in index order.  At decode sizes a shared-term
+// (VeRA) tile's rank-r_v product is the launch's longest chain of dependent
+// loads, while most work-groups take owned tiles of a few rows; with the
+// shared-term tiles first (their own ranges, from the plan's separate list)
+// their chains start in the first wave of dispatch instead of behind every
+// owned tile of the launch.  Each work-group's result is unchanged.
 hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int count, hipStream_t s) {
   if (count < 1 || count > MAX_SLICES) return hipErrorInvalidValue;
-  Slices<ExpandArgs> t{};
-  t.count = count;
-  t.first[0] = 0;
+  ExpandSlices t{};
+  int m = 0;
+  bool sh_first[MAX_SLICES];
   for (int i = 0; i < count; ++i) {
-    if ((slices[i].hpart != nullptr) != (slices[0].hpart != nullptr) || slices[i].d_out % 64)
-      return hipErrorInvalidValue;
-    t.s[i] = slices[i];
-    t.first[i + 1] = t.first[i] + slices[i].max_tiles * (slices[i].d_out / 64);
+    const ExpandArgs& a = slices[i];
+    if ((a.hpart != nullptr) != (slices[0].hpart != nullptr) || a.d_out % 64) return hipErrorInvalidValue;
+    sh_first[i] = a.n <= 64 && a.sh_tiles && a.sh_rows_w && a.max_sh_tiles > 0 && a.vera_Bt && a.r_v > 0;
+    if (!sh_first[i]) continue;
+    t.s[m] = a;
+    t.s[m].tiles = a.sh_tiles;
+    t.s[m].tile_rows_w = a.sh_rows_w;
+    t.s[m].max_tiles = a.max_sh_tiles;
+    t.s[m].part = 0;
+    ++m;
   }
-  for (int i = count; i < MAX_SLICES; ++i) t.first[i + 1] = t.first[count];
+  for (int i = 0; i < count; ++i) {
+    t.s[m] = slices[i];
+    t.s[m].part = sh_first[i] ? 2 : 0;
+    ++m;
+  }
+  t.count = m;
+  t.first[0] = 0;
+  for (int i = 0; i < m; ++i) t.first[i + 1] = t.first[i] + t.s[i].max_tiles * (t.s[i].d_out / 64);
+  for (int i = m; i < 2 * MAX_SLICES; ++i) t.first[i + 1] = t.first[m];
   switch (dtype) {
     case 0: return expand_tm<float>(tile_rows, t, s);
     case 1: return expand_tm<f16>(tile_rows, t, s);

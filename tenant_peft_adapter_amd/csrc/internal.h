@@ -14,17 +14,17 @@ namespace tpa {
 // v; gate, up) that share one row plan: the kernel argument holds one record
 // per slice and the work-group ranges [first[i], first[i + 1]) of each.
 constexpr int MAX_SLICES = 4;
-template <typename A>
+template <typename A, int N = MAX_SLICES>
 struct Slices {
-  A s[MAX_SLICES];
-  int32_t first[MAX_SLICES + 1];
+  A s[N];
+  int32_t first[N + 1];
   int32_t count;
 };
-template <typename A>
-__device__ __forceinline__ int slice_of(const Slices<A>& t, int bid) {
+template <typename A, int N>
+__device__ __forceinline__ int slice_of(const Slices<A, N>& t, int bid) {
   int i = 0;
 #pragma unroll
-  for (int j = 1; j < MAX_SLICES; ++j)
+  for (int j = 1; j < N; ++j)
     if (j < t.count && bid >= t.first[j]) i = j;
   return i;
 }
@@ -175,6 +175,14 @@ struct ExpandArgs {
   int32_t n, d_out;
   int32_t max_tiles;
   int32_t apply_scale;     // 0: leave s and b to a separate pass
+  // The plan's shared-term tiles on their own (padded with kind -1 to
+  // max_sh_tiles; null or 0 where the layer has no shared term).  At decode
+  // sizes launch_expand runs them first, as ranges of their own, and skips
+  // them in the full list.
+  const int32_t* sh_tiles;
+  const int32_t* sh_rows_w;
+  int32_t max_sh_tiles;
+  int32_t part;            // set by launch_expand: 0 every tile, 2 every tile but shared-term ones
 };
 
 // One slice of a decode base-GEMM launch; with has_side, work-groups after
