@@ -27,21 +27,26 @@ namespace {
 constexpr int THREADS = 256;
 
 // h of one row segment of 16 columns: the split partials added in split
-// order, their loads issued 4 splits (16 loads) at a time.
+// order, their loads issued 4 splits (16 loads) at a time.  TAIL: the last
+// group short of 4 too (2 splits: one round trip, not two; 7: two, not
+// four); else the splits past the last full group one at a time, which
+// needs fewer registers.
+template <bool TAIL>
 __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size_t split_stride,
                                             float* v) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = 0.f;
   int s = 0;
-  for (; s + 4 <= hsplit; s += 4) {
-    f32x4 x[4][4];
+  for (; TAIL ? s < hsplit : s + 4 <= hsplit; s += 4) {
+    f32x4 x[4][4];  // (entries past the last split are neither loaded nor added)
 #pragma unroll
     for (int u = 0; u < 4; ++u)
+      if (s + u < hsplit)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        x[u][q] = gload<f32x4>(hpart + (size_t)(s + u) * split_stride + 4 * q);
+        for (int q = 0; q < 4; ++q) x[u][q] = gload<f32x4>(hpart + (size_t)(s + u) * split_stride + 4 * q);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 4; ++u) {
+      if (s + u >= hsplit) break;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[4 * q] += x[u][q][0];
@@ -49,6 +54,7 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
         v[4 * q + 2] += x[u][q][2];
         v[4 * q + 3] += x[u][q][3];
       }
+    }
   }
   for (; s < hsplit; ++s) {
     const float* src = hpart + (size_t)s * split_stride;
@@ -74,7 +80,8 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
 typedef Slices<ExpandArgs, 2 * MAX_SLICES> ExpandSlices;
 
 template <typename T, int MB, bool HPART, bool FEW>
-__global__ __launch_bounds__(64) void expand_kernel(ExpandSlices t) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MB == 1 && !FEW ? 3 : 1))) void expand_kernel(
+    ExpandSlices t) {
   typedef typename Frag<T>::V Vt;
   // k steps whose loads are issued together (fewer for wide fragments)
   constexpr int U = sizeof(T) == 4 ? (MB == 1 ? 2 : 1) : (MB == 1 && !FEW ? 4 : 2);
@@ -106,8 +113,19 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandSlices t) {
     rsd[m] = a.slots + (kind == CLS_OWNED ? tl.w : rw[m] >= 0 ? (rw[m] >> 16) : 0);
   }
 
-  // The rows' s, b and e pointers, then h of each row: their loads (h's the
-  // largest) go out as soon as the rows are known, ahead of the term's.
+  // The term's factor (stored [d_out][K]) and rank: kernel arguments for a
+  // shared-term tile; an owned tile's come from its slot's record, read
+  // beside the rows' pointers.
+  int K = 0;
+  const T* Bt = nullptr;
+  if (kind == CLS_OWNED) {
+    K = a.slots[tl.w].rank;
+    Bt = static_cast<const T*>(a.slots[tl.w].Bt);
+  } else if (kind == CLS_SHARED) {
+    K = a.r_v;
+    Bt = static_cast<const T*>(a.vera_Bt);
+  }
+  // The rows' s, b and e pointers.
   const float* sp[MB];
   const float* bq[MB];
   const float* ep[MB];
@@ -125,55 +143,65 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandSlices t) {
   }
   T* out = static_cast<T*>(a.out);
   float v[MB][16];
+  f32x4 s4[MB][4], e4[MB][4];
+  // h of each row (its split partials summed in order), then the rows' s
+  // values (so that a tenant with a live s costs about what one without
+  // does); b, rarer, loads in the epilogue.
+  auto load_h_s = [&]() {
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    if (row[m] < 0) continue;
-    if (HPART)
-      sum_parts16(a.hpart + (size_t)row[m] * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v[m]);
-    else
-      load_run16<T>(out + (size_t)row[m] * a.d_out + col, v[m]);
-  }
-  // The rows' s values load now, beside h, so they arrive while the term is
-  // computed rather than after it (a tenant with a live s then costs about
-  // what one without does); b and e, rarer, load in the epilogue.
-  f32x4 s4[MB][4];
+    for (int m = 0; m < MB; ++m) {
+      if (row[m] < 0) continue;
+      if (HPART)
+        sum_parts16<!FEW>(a.hpart + (size_t)row[m] * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v[m]);
+      else
+        load_run16<T>(out + (size_t)row[m] * a.d_out + col, v[m]);
+    }
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      s4[m][q] = (row[m] >= 0 && sp[m]) ? gload<f32x4>(sp[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+      for (int q = 0; q < 4; ++q)
+        s4[m][q] = (row[m] >= 0 && sp[m]) ? gload<f32x4>(sp[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+  };
+  auto load_e = [&]() {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        e4[m][q] = (row[m] >= 0 && ep[m]) ? gload<f32x4>(ep[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+  };
 
-  int K = 0;
-  const T* Bt = nullptr;
-  if (kind == CLS_OWNED) {
-    K = a.slots[tl.w].rank;
-    Bt = static_cast<const T*>(a.slots[tl.w].Bt);
-  } else if (kind == CLS_SHARED) {
-    K = a.r_v;
-    Bt = static_cast<const T*>(a.vera_Bt);
-  }
-
+  // term = V[p] · B'ᵀ over this wave's 64 columns: a = B' rows (output
+  // columns), b = V rows of the tile (plan positions).
   f32x4 acc[4][MB];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  if (K > 0) {
-    // term = V[p] · B'ᵀ over this wave's 64 columns: a = B' rows (output
-    // columns), b = V rows of the tile (plan positions).
-    const T* V = static_cast<const T*>(a.v);
-    const T* bp[4];
+  const T* V = static_cast<const T*>(a.v);
+  const T* bp[4];
+  const T* vp[MB];
+  bool vv[MB];
+  auto point = [&]() {
 #pragma unroll
     for (int b = 0; b < 4; ++b) bp[b] = Bt + (size_t)(n0 + perm_col<4>(i16, b)) * K + 8 * g;
-    const T* vp[MB];
-    bool vv[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const int p = p0 + 16 * m + i16;
       vv[m] = rw[m] >= 0;
       vp[m] = V + (size_t)(vv[m] ? p : 0) * a.kmax + 8 * g;
     }
+  };
+  // At decode sizes (!FEW) a term of more than one k step (VeRA's shared
+  // rank, owned ranks above 32) goes first: its loads need only the tile and
+  // the factor, so the first U k steps go out beside the rows' pointers; h,
+  // s and e load after it, when the fragments' registers are free again.
+  // Its chain of round trips is the launch's longest, and few waves share
+  // the chip with it.  Above 256 rows every tile takes h first (stack cut
+  // at 4096 rows: 5472-5476 µs per step with h first, 5497-5505 with the
+  // term first).
+  const bool long_term = !FEW && K > 32;
+  if (long_term) {
+    point();
     for (int k = 0; k < K; k += 32 * U) {
       Vt af[U][4], bf[U][MB];
 #pragma unroll
@@ -194,6 +222,37 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandSlices t) {
           for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[u][b], bf[u][m]);
       }
     }
+    load_h_s();
+    load_e();
+  } else {
+    // h and s first, then the term's loads: at decode sizes no term or one
+    // k step, one step's fragments; above 256 rows any rank, U steps at a
+    // time.
+    load_h_s();
+    if (K > 0) {
+      point();
+      constexpr int U2 = FEW ? U : 1;
+      for (int k = 0; k < K; k += 32 * U2) {
+        Vt af[U2][4], bf[U2][MB];
+#pragma unroll
+        for (int u = 0; u < U2; ++u) {
+          const int kk = k + 32 * u;
+          const bool ok = kk + 8 * g < K;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) af[u][b] = ok ? load_frag<T>(bp[b] + kk) : zero_frag<T>();
+#pragma unroll
+          for (int m = 0; m < MB; ++m) bf[u][m] = (ok && vv[m]) ? load_frag<T>(vp[m] + kk) : zero_frag<T>();
+        }
+#pragma unroll
+        for (int u = 0; u < U2; ++u) {
+          if (k + 32 * u >= K) break;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[b][m] = mma(acc[b][m], af[u][b], bf[u][m]);
+        }
+      }
+    }
   }
 
   // Epilogue: lane holds 16 consecutive columns of one row of the tile.
@@ -201,18 +260,18 @@ __global__ __launch_bounds__(64) void expand_kernel(ExpandSlices t) {
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     if (row[m] < 0) continue;
-    f32x4 b4[4], e4[4];
+    f32x4 b4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       b4[q] = bq[m] ? gload<f32x4>(bq[m] + col + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
-      e4[q] = ep[m] ? gload<f32x4>(ep[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+      if (!long_term) e4[m][q] = ep[m] ? gload<f32x4>(ep[m] + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float h = v[m][4 * q + j] * s4[m][q][j] + b4[q][j];
-        if (K > 0) h += acc[q][m][j] * e4[q][j];
+        if (K > 0) h += acc[q][m][j] * e4[m][q][j];
         v[m][4 * q + j] = h;
       }
     store_run16<T>(out + (size_t)row[m] * a.d_out + col, v[m]);
@@ -243,7 +302,7 @@ __global__ __launch_bounds__(THREADS) void scale_pass_kernel(ScaleArgs a, int mo
     return;
   }
   if (mode == 1 && a.hpart)
-    sum_parts16(a.hpart + (size_t)row * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
+    sum_parts16<false>(a.hpart + (size_t)row * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
   else
     load_run16<T>(y, v);
   if (mode == 4) {  // index scale, step two: multiply by the per-row copy
