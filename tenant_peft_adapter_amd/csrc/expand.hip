@@ -69,15 +69,19 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
   }
 }
 
-// FEW: two k steps in flight instead of four (16-bit types, 16-row tiles):
-// 118 registers instead of 158, so four waves per SIMD instead of three.
-// Above 256 rows there are enough work-groups for the extra waves to pay
-// (2-layer cut of the 1024-tenant Zipf stack: 1024 rows 1211 -> 1198 µs per
-// layer, 4096 rows 2876 -> 2847); at decode sizes the longer dependent
-// chain of a rank-256 VeRA tile costs more (decoder layer 203.7 -> 206.2
-// µs per step), so small batches keep four.
 // Up to two ranges per projection: its shared-term tiles, then the rest.
 typedef Slices<ExpandArgs, 2 * MAX_SLICES> ExpandSlices;
+
+// FEW (16-bit types, 16-row tiles, above 256 rows): two k steps of loads in
+// flight instead of four, h and s loaded before the term at any rank, the
+// split partials past the last full group of four one at a time: about 128
+// registers, four waves per SIMD (2-layer cut of the 1024-tenant Zipf stack
+// against four k steps at 158 registers: 1024 rows 1211 -> 1198 µs per
+// layer, 4096 rows 2876 -> 2847).  At decode sizes (!FEW) a long term runs
+// first, four k steps at a time (two steps per round trip made a rank-256
+// VeRA tile's chain longer: decoder layer 203.7 -> 206.2 µs per step), and a
+// short one loads one step's fragments; with the occupancy hint that is
+// 119 registers, four waves per SIMD as well.
 
 template <typename T, int MB, bool HPART, bool FEW>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MB == 1 && !FEW ? 3 : 1))) void expand_kernel(
