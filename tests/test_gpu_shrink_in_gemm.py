@@ -122,3 +122,28 @@ def test_shrink_in_gemm_group(names, borrow):
         assert np.array_equal(g, w), (nm, float(np.abs(g - w).max()))
         y, h, xw = reference({**p, "x": projs[0]["x"]} if borrow else p, wl["slot_of_row"])
         check(g, y, h, xw, label="shrink in GEMM group " + nm)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("n", [64, 17, 1])
+@pytest.mark.parametrize("r_v", [96, 256])
+def test_decode_terms_of_several_k_steps(dtype, n, r_v):
+    """Owned ranks of one (16), two (48, 64) and five (160: a full group of
+    four steps and one more) 32-wide k steps and VeRA ranks 96 and 256 at
+    decode sizes: the expand runs a term of more than one step first (its
+    shared-term tiles in a range of their own, ahead of the rest) and a
+    one-step term after h; the shrink rides in the GEMM's launch.  Against
+    the oracle, and bitwise against a second call."""
+    wl = synth.decode_ranks(seed=7000 + n + r_v, n=n, dtype=dtype, r_v=r_v)
+    p = wl["projections"][0]
+    say("decode ranks %s n=%d r_v=%d" % (dtype, n, r_v))
+    L = make_layer(p, max_slots=8, max_rank=256)
+    cfg = L.config(n)
+    assert cfg["gemm_path"] == 2 and cfg["shrink_in_gemm"] == 1, cfg
+    got = run(L, p["x"], wl["slot_of_row"], dtype)
+    again = run(L, p["x"], wl["slot_of_row"], dtype)
+    L.close()
+    assert np.array_equal(got, again)
+    y, h, xw = reference(p, wl["slot_of_row"])
+    check(got, y, h, xw, label="decode ranks %s n=%d r_v=%d" % (dtype, n, r_v), **_tol(dtype))
+

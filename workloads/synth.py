@@ -184,6 +184,27 @@ def tiny_mixed(seed=0, n=64, d=256, dtype="f32", with_identity=False, d_out=None
             "slot_of_row": slot_of_row, "projections": [p]}
 
 
+def decode_ranks(seed=7000, n=64, d_in=512, d_out=384, dtype="f16", r_v=96):
+    """Decode-size layer whose terms span one, several and a partial group of
+    32-wide k steps: LoRA r16, LoRA r48, DoRA r64, LoRA r160, VeRA with a
+    shared rank-r_v pair, (IA)3, and identity rows.  Slots 1..6 in that
+    order; rows uniform over slots 0..6."""
+    rng = np.random.default_rng(seed)
+    p = make_projection(rng, "decode_ranks", d_in, d_out, dtype, n)
+    p["shared"] = _vera_shared(rng, d_in, d_out, r_v, dtype)
+    p["adapters"] = {
+        1: _lora(rng, d_in, d_out, 16, dtype),
+        2: _lora(rng, d_in, d_out, 48, dtype),
+        3: _dora(rng, p["W"], 64, dtype),
+        4: _lora(rng, d_in, d_out, 160, dtype),
+        5: _vera(rng, r_v, d_out),
+        6: _ia3(rng, d_out),
+    }
+    slot_of_row = rng.integers(0, 7, size=n).astype(np.int32)
+    return {"name": "decode_ranks", "dtype": dtype, "n": n,
+            "slot_of_row": slot_of_row, "projections": [p]}
+
+
 def oft_blocks(seed=6000, n=64, d_in=256, d_out=256, dtype="f32", blocks=(16, 32, 64)):
     """One layer with OFT tenants of every block size the rotation accepts
     (appendix "Training" names 32; 16 and 64 are the other sizes a d_in that
