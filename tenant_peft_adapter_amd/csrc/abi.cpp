@@ -1784,6 +1784,11 @@ tpa_status forward_group_after_plan(SliceCtx* sl, int count, const tpa::PlanArgs
     of[i].x_rot = sl[i].w + y.x_rot;
     of[i].d_in = L->d_in;
     of[i].max_tiles = oft_tile_bound(L, n, tile_rows, y.max_tiles);
+    // One block per wave at decode sizes, where the launch is a chain of
+    // round trips (q/k/v of the decoder layer at 64 rows: 180.3 -> 178.5 µs
+    // per step); four per wave above, where more, smaller work-groups lost
+    // more than they overlapped (2-layer stack cut at 4096 rows +0.9%).
+    of[i].bpw = n <= 64 ? 4 : 16;
   }
 
   // VeRA's A_v read once per fused input (Table 2's route-two count; the

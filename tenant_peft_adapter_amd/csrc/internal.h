@@ -70,6 +70,9 @@ struct OftArgs {
   int32_t d_in;
   int32_t block;           // OFT block size of this launch (16, 32 or 64)
   int32_t max_tiles;
+  // Blocks per work-group of the split launch (4: one per wave, 16: four
+  // per wave); the whole-k launch takes one per wave of its work-groups.
+  int32_t bpw;
 };
 
 // ---------------------------------------------------------------- GEMMs ---

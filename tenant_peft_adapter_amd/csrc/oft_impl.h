@@ -5,8 +5,9 @@
 // [rows, d_in] once plus each tenant's d_in / b blocks of b x b.
 //
 // Work-group = one OFT tile of the plan (rows of one tenant, so each R
-// block is read once per tile) x 16 consecutive blocks (shared out among
-// its waves).  A
+// block is read once per tile) x a.bpw consecutive blocks shared out among
+// its waves (a wave's blocks run one after another, each a round trip of
+// loads).  A
 // block is an MFMA product with K = b: D = Rᵀ · x_blockᵀ, so each lane ends
 // with 4·(b/16) consecutive columns of one row.  R blocks are stored
 // transposed ([c][t] = R[t][c]).  The rotated row p (plan order) is written
@@ -18,12 +19,12 @@
 namespace tpa {
 namespace oft_impl {
 
-// Work-group part `bg` (16 consecutive blocks, 16 / NW per wave for a
-// work-group of NW waves) of OFT tile t.
-template <typename T, int MB, int BS, int NW = 4>
+// Work-group part `bg` (a.bpw consecutive blocks, a.bpw / NW per wave for
+// a work-group of NW waves; a.bpw a multiple of NW) of OFT tile t.
+template <typename T, int MB, int BS, int NW>
 __device__ __forceinline__ void oft_part(const OftArgs& a, int t, int bg, int wave, int lane) {
   constexpr int NB = BS / 16;
-  constexpr int BLOCKS_PER_WG = 16;
+  const int bpw = a.bpw;
   const int i16 = lane & 15, g = lane >> 4;
   // Header and row words load side by side.
   const int4 tile = *reinterpret_cast<const int4*>(a.oft_tiles + 4 * t);
@@ -47,9 +48,8 @@ __device__ __forceinline__ void oft_part(const OftArgs& a, int t, int bg, int wa
     xp[m] = X + (size_t)(xv[m] ? (rw[m] & 0xFFFF) : 0) * a.d_in + 8 * g;
   }
 
-  static_assert(BLOCKS_PER_WG % NW == 0, "blocks per work-group must divide among its waves");
-  for (int j = 0; j < BLOCKS_PER_WG / NW; ++j) {
-    const int kb = bg * BLOCKS_PER_WG + NW * j + wave;
+  for (int j = 0; j < bpw / NW; ++j) {
+    const int kb = bg * bpw + NW * j + wave;
     if (kb >= nblocks) break;
     f32x4 acc[NB][MB];
 #pragma unroll

@@ -19,7 +19,6 @@ namespace tpa {
 namespace {
 
 constexpr int THREADS = 256;
-constexpr int OFT_BLOCKS_PER_WG = 16;
 
 template <typename T, int MB, int BS, int NCB>
 __global__ __launch_bounds__(THREADS) void pre_kernel(Slices<PreSlice> t) {
@@ -33,7 +32,7 @@ __global__ __launch_bounds__(THREADS) void pre_kernel(Slices<PreSlice> t) {
   }
   if (BS != 0) {
     const int o = local - ps.n_shrink_wg;
-    oft_impl::oft_part<T, MB, (BS == 0 ? 16 : BS)>(ps.of, o / ps.oft_bg, o % ps.oft_bg, wave, lane);
+    oft_impl::oft_part<T, MB, (BS == 0 ? 16 : BS), THREADS / 64>(ps.of, o / ps.oft_bg, o % ps.oft_bg, wave, lane);
   }
 }
 
@@ -130,7 +129,10 @@ PreSlice make_pre_slice(const ShrinkArgs* sh, const OftArgs* of, bool whole) {
   }
   if (of) {
     ps.of = *of;
-    ps.oft_bg = (of->d_in / of->block + OFT_BLOCKS_PER_WG - 1) / OFT_BLOCKS_PER_WG;
+    // Blocks per work-group: a multiple of its waves (4 in the split launch,
+    // PRE_WHOLE_WAVES, one per wave, in the whole-k one).
+    if (whole || ps.of.bpw < THREADS / 64 || ps.of.bpw % (THREADS / 64)) ps.of.bpw = whole ? PRE_WHOLE_WAVES : 16;
+    ps.oft_bg = (of->d_in / of->block + ps.of.bpw - 1) / ps.of.bpw;
     ps.n_oft_wg = of->max_tiles * ps.oft_bg;
   }
   return ps;
