@@ -69,6 +69,118 @@ __device__ __forceinline__ void sum_parts16(const float* hpart, int hsplit, size
   }
 }
 
+// h of one row segment of 8 columns: the split partials added in split
+// order, 4 splits (8 loads) at a time, the last group short of 4 included.
+__device__ __forceinline__ void sum_parts8(const float* hpart, int hsplit, size_t split_stride, float* v) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  for (int s = 0; s < hsplit; s += 4) {
+    f32x4 x[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s + u < hsplit)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) x[u][q] = gload<f32x4>(hpart + (size_t)(s + u) * split_stride + 4 * q);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (s + u >= hsplit) break;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        v[4 * q] += x[u][q][0];
+        v[4 * q + 1] += x[u][q][1];
+        v[4 * q + 2] += x[u][q][2];
+        v[4 * q + 3] += x[u][q][3];
+      }
+    }
+  }
+}
+
+// A shared-term tile at decode sizes (16-bit types, 16-row tiles): work-
+// group = one wave = the tile x 32 output columns, so that the term's whole
+// rank (up to 8 k steps of 32: VeRA's 256) loads in one round trip, where
+// 64 columns take two (their fragments would need twice the registers).
+// The same products and sums as the 64-column wave, in the same order; lane
+// holds 8 consecutive columns of one row.
+template <typename T, bool HPART>
+__device__ __forceinline__ void shared_tile32(const ExpandArgs& a, int local, int lane) {
+  typedef typename Frag<T>::V Vt;
+  constexpr int U = 8;
+  const int ncb = a.d_out / 32;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int ti = local / ncb;
+  const int n0 = (local % ncb) * 32;
+  const int col = n0 + 8 * g;
+  const int4 tl = *reinterpret_cast<const int4*>(a.tiles + 4 * ti);
+  const int rw = a.tile_rows_w[(size_t)ti * 16 + i16];
+  if (tl.z != CLS_SHARED) return;  // padding past the last shared-term tile
+  const int row = rw >= 0 ? (rw & 0xFFFF) : -1;
+  const SlotDev* rsd = a.slots + (rw >= 0 ? (rw >> 16) : 0);
+  const int K = a.r_v;
+  const float* sp = nullptr;
+  const float* bq = nullptr;
+  const float* ep = nullptr;
+  if (row >= 0) {
+    if (a.apply_scale) {
+      sp = gload<const float*>(&rsd->s);
+      bq = gload<const float*>(&rsd->b);
+    }
+    ep = gload<const float*>(&rsd->e);
+  }
+  // term = U[p] · B_vᵀ over the 32 columns: a = B_v rows (output columns),
+  // b = the tile's U rows.
+  const T* bp[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+    bp[b] = static_cast<const T*>(a.vera_Bt) + (size_t)(n0 + perm_col<2>(i16, b)) * K + 8 * g;
+  const bool vv = rw >= 0;
+  const T* vp = static_cast<const T*>(a.v) + (size_t)(vv ? tl.x + i16 : 0) * a.kmax + 8 * g;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int k = 0; k < K; k += 32 * U) {
+    Vt af[U][2], bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + 32 * u;
+      const bool ok = kk + 8 * g < K;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) af[u][b] = ok ? load_frag<T>(bp[b] + kk) : zero_frag<T>();
+      bf[u] = (ok && vv) ? load_frag<T>(vp + kk) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k + 32 * u >= K) break;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) acc[b] = mma(acc[b], af[u][b], bf[u]);
+    }
+  }
+  if (row < 0) return;
+  T* out = static_cast<T*>(a.out);
+  float v[8];
+  if (HPART) {
+    sum_parts8(a.hpart + (size_t)row * a.d_out + col, a.hsplit, (size_t)a.n * a.d_out, v);
+  } else {
+    const Vt h8 = *reinterpret_cast<const Vt*>(out + (size_t)row * a.d_out + col);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = to_f<T>(h8[j]);
+  }
+  f32x4 s4[2], b4[2], e4[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    s4[q] = sp ? gload<f32x4>(sp + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+    b4[q] = bq ? gload<f32x4>(bq + col + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+    e4[q] = ep ? gload<f32x4>(ep + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
+  }
+  Vt o8;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float h = v[4 * q + j] * s4[q][j] + b4[q][j];
+      h += acc[q][j] * e4[q][j];
+      o8[4 * q + j] = to_t<T>(h);
+    }
+  *reinterpret_cast<Vt*>(out + (size_t)row * a.d_out + col) = o8;
+}
+
 // Up to two ranges per projection: its shared-term tiles, then the rest.
 typedef Slices<ExpandArgs, 2 * MAX_SLICES> ExpandSlices;
 
@@ -92,6 +204,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MB == 1 && !
   const int si = slice_of(t, (int)blockIdx.x);
   const ExpandArgs& a = t.s[si];
   const int local = (int)blockIdx.x - t.first[si];
+  if constexpr (sizeof(T) == 2 && MB == 1 && !FEW) {
+    if (a.part == 1) {
+      shared_tile32<T, HPART>(a, local, (int)threadIdx.x);
+      return;
+    }
+  }
   const int ncb = a.d_out / 64;
   const int lane = threadIdx.x;
   const int i16 = lane & 15, g = lane >> 4;
@@ -373,7 +491,7 @@ hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int
     t.s[m].tiles = a.sh_tiles;
     t.s[m].tile_rows_w = a.sh_rows_w;
     t.s[m].max_tiles = a.max_sh_tiles;
-    t.s[m].part = 0;
+    t.s[m].part = 1;
     ++m;
   }
   for (int i = 0; i < count; ++i) {
@@ -383,7 +501,11 @@ hipError_t launch_expand(int dtype, int tile_rows, const ExpandArgs* slices, int
   }
   t.count = m;
   t.first[0] = 0;
-  for (int i = 0; i < m; ++i) t.first[i + 1] = t.first[i] + t.s[i].max_tiles * (t.s[i].d_out / 64);
+  // (a shared-term range of 16-bit types on 16-row tiles runs 32 columns
+  // per work-group: shared_tile32)
+  const bool narrow = dtype != 0 && tile_rows == 16;
+  for (int i = 0; i < m; ++i)
+    t.first[i + 1] = t.first[i] + t.s[i].max_tiles * (t.s[i].d_out / (t.s[i].part == 1 && narrow ? 32 : 64));
   for (int i = m; i < 2 * MAX_SLICES; ++i) t.first[i + 1] = t.first[m];
   switch (dtype) {
     case 0: return expand_tm<float>(tile_rows, t, s);
