@@ -136,14 +136,18 @@ __global__ __launch_bounds__(T) void plan_kernel(PlanArgs a) {
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) sv[e] = e_lo + e < e_hi ? a.slot_of_row[e_lo + e] : 0;
     // The record's first 16 bytes, as two 8-byte halves (records are 8-byte
-    // aligned): (cls, rank) and (has_R, oft_block).
+    // aligned): (cls, rank) and (has_R, oft_block).  Every entry loads (slot
+    // 0's record where the entry is past the run or its slot out of range)
+    // so that all of them go out at once: loaded under a condition, each
+    // became a round trip of its own.
     int2 rec[EMAX], rot2[EMAX];
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
       const bool in = e_lo + e < e_hi && sv[e] >= 0 && sv[e] < a.max_slots;
       const int2* r = reinterpret_cast<const int2*>(a.slots + (in ? sv[e] : 0));
-      rec[e] = in ? r[0] : make_int2(-1, 0);
-      rot2[e] = in ? r[1] : make_int2(0, 0);
+      const int2 r0 = r[0], r1 = r[1];
+      rec[e] = make_int2(in ? r0.x : -1, r0.y);
+      rot2[e] = make_int2(in ? r1.x : 0, r1.y);
     }
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
