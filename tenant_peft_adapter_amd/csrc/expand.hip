@@ -169,13 +169,18 @@ __device__ __forceinline__ void shared_tile32(const ExpandArgs& a, int local, in
     b4[q] = bq ? gload<f32x4>(bq + col + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
     e4[q] = ep ? gload<f32x4>(ep + col + 4 * q) : f32x4{1.f, 1.f, 1.f, 1.f};
   }
+  // (written as the 64-column wave writes it: h rounded to fp32, then to
+  // the layer type.  With the term added unconditionally the compiler fuses
+  // the last multiply-add and the conversion into one mixed-precision FMA,
+  // a single rounding, and the result differs from the other waves' in the
+  // last place now and then.)
   Vt o8;
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float h = v[4 * q + j] * s4[q][j] + b4[q][j];
-      h += acc[q][j] * e4[q][j];
+      if (K > 0) h += acc[q][j] * e4[q][j];
       o8[4 * q + j] = to_t<T>(h);
     }
   *reinterpret_cast<Vt*>(out + (size_t)row * a.d_out + col) = o8;

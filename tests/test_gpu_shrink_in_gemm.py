@@ -27,7 +27,7 @@ from workloads import synth
 
 pytestmark = pytest.mark.gpu
 
-SHRINK_SPLIT, GROUPS, GEMM_SPLIT = 2, 7, 1
+SHRINK_SPLIT, GROUPS, GEMM_SPLIT, TILE_ROWS = 2, 7, 1, 3
 
 _WL = {}
 
@@ -147,3 +147,30 @@ def test_decode_terms_of_several_k_steps(dtype, n, r_v):
     y, h, xw = reference(p, wl["slot_of_row"])
     check(got, y, h, xw, label="decode ranks %s n=%d r_v=%d" % (dtype, n, r_v), **_tol(dtype))
 
+
+
+@pytest.mark.parametrize("name,n", [("gate", 64), ("gate", 17), ("down", 64)])
+def test_vera_narrow_waves_match_wide_tiles(name, n):
+    """The decode expand's VeRA tiles on 32-column waves (16-row tiles)
+    against the same layer on 64-row tiles (64-column waves, another code
+    path) with the GEMM's split and k-groups and the shrink's k ranges
+    pinned alike: every output element is the same sum in the same order,
+    so the outputs agree bit for bit."""
+    wl = _workload("f16")
+    p = _proj(wl, name)
+    sor = np.asarray(wl["slot_of_row"])[:n]
+    x = p["x"][:n]
+    L = make_layer(p, max_slots=32, max_rank=256)
+    cfg = L.config(n)
+    assert cfg["tile_rows"] == 16 and cfg["shrink_in_gemm"] == 1, cfg
+    got = run(L, x, sor, "f16")
+    L.close()
+    opts = {TILE_ROWS: 64, GEMM_SPLIT: cfg["gemm_split"], GROUPS: cfg["gemm_groups"],
+            SHRINK_SPLIT: cfg["shrink_split"]}
+    Lw = make_layer(p, max_slots=32, max_rank=256, options=opts)
+    cw = Lw.config(n)
+    assert (cw["tile_rows"], cw["gemm_kc"], cw["shrink_kc"]) == (64, cfg["gemm_kc"], cfg["shrink_kc"]), (cw, cfg)
+    want = run(Lw, x, sor, "f16")
+    Lw.close()
+    say("narrow vs wide %s n=%d: max |diff| %g" % (name, n, float(np.abs(got - want).max())))
+    assert np.array_equal(got, want)
