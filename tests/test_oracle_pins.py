@@ -689,15 +689,17 @@ def test_product_methods_reduce_to_lora():
     np.testing.assert_allclose(om.direct_forward(x, W, eye) - x @ W, blocks, rtol=0, atol=1e-13)
 
 
-def test_dora_magnitude_recipe_matches_the_oracle_norm():
-    """The input generator forms DoRA's magnitude by the workload recipe
-    m = ‖W + cAB‖_c · (1 + 0.1 z) (its own expansion of the norm over the
-    rank-r term, so it stays cheap at 4096 x 14336).  Replaying its seeded
-    draws, m must equal the oracle's column norm times 1 + 0.1 z: the
-    recipe is pinned to the oracle's pinned norm, and the scale the oracle
-    derives from it is exactly the drawn gain."""
+def test_dora_magnitude_recipe_is_the_expected_norm():
+    """The input generator sets DoRA's magnitude to m = sqrt(1 + c²) ·
+    (1 + 0.1 z), a constant of its draws and no norm of the drawn values
+    (it does none of the method's arithmetic).  Replaying its seeded draws
+    gives exactly that m; and sqrt(1 + c²) is the expected column norm of
+    W + cAB under the draws (W ~ N(0, 1/d_in), A ~ N(0, 1/d_in),
+    B ~ N(0, 1/r)): the mean of the oracle's squared column norms over
+    1024 columns is 1 + c² within a few standard errors, so the scale the
+    oracle derives from m stays near the drawn gain on average."""
     from workloads import synth
-    for d_in, d_out, r, dt in ((64, 96, 4, "f16"), (256, 128, 8, "bf16"), (128, 64, 3, "f32")):
+    for d_in, d_out, r, dt in ((64, 96, 4, "f16"), (1024, 1024, 16, "f32")):
         rng = np.random.default_rng(d_in + d_out)
         W = synth.round_to(synth._normal(rng, (d_out, d_in), 1.0 / np.sqrt(d_in)), dt)
         state = rng.bit_generator.state
@@ -706,8 +708,14 @@ def test_dora_magnitude_recipe_matches_the_oracle_norm():
         rng2.bit_generator.state = state
         lo = synth._lora(rng2, d_in, d_out, r, dt)
         g = 1.0 + 0.1 * rng2.standard_normal(d_out)
+        c = rec["c"]
+        assert c == 2.0
         assert np.array_equal(lo["A"], rec["A"]) and np.array_equal(lo["B"], rec["B"])
-        norm = oracle.dora_column_norm(W.T.astype(np.float64), rec["A"], rec["B"], rec["c"])
-        np.testing.assert_allclose(rec["m"], norm * g, rtol=2e-7)
-        s = oracle.dora_scale(W.T.astype(np.float64), rec["A"], rec["B"], rec["c"], rec["m"])
-        np.testing.assert_allclose(s, g, rtol=2e-7)
+        assert np.array_equal(rec["m"], (np.sqrt(1.0 + c * c) * g).astype(np.float32))
+        if d_in < 1024:
+            continue
+        norm = oracle.dora_column_norm(W.T.astype(np.float64), rec["A"], rec["B"], c)
+        assert abs(np.mean(norm ** 2) / (1.0 + c * c) - 1.0) < 0.04
+        s = oracle.dora_scale(W.T.astype(np.float64), rec["A"], rec["B"], c, rec["m"])
+        assert abs(np.mean(s / g) - 1.0) < 0.06
+

@@ -16,13 +16,16 @@ B [r, d_out], Q [d_in / b, b, b].
 Distributions (one reading of the workload descriptions, used everywhere):
   W ~ N(0, 1/d_in); x ~ N(0, 1); LoRA and DoRA A ~ N(0, 1/d_in),
   B ~ N(0, 1/r), c = 2 (alpha 32 over rank 16); DoRA magnitude
-  m = ‖Wᵀ + cAB‖_c · (1 + 0.1 z); (IA)3 l = 1 + 0.3 z; VeRA shared
+  m = sqrt(1 + c²) · (1 + 0.1 z); (IA)3 l = 1 + 0.3 z; VeRA shared
   A ~ N(0, 1/d_in), B ~ N(0, 1/r_v), d, e = 1 + 0.3 z, c = 1; OFT skew Q
   with upper entries 0.1 z, blocks of 32.
 
-The DoRA magnitude is an input recipe: it is formed here once from the
-rounded W, A, B, so that the adapter's scale is 1 + 0.1 z; both sides then
-receive m and compute the scale from it on their own.
+The DoRA magnitude's sqrt(1 + c²) is the expected column norm of the
+adapted weight under these draws (a column of W has expected squared norm
+1, one of cAB has c², and the cross term has mean 0), a constant of the
+recipe, not a norm formed from the drawn values: the scale that both sides
+compute from m on their own is then about 1 + 0.1 z.  This module does none
+of the methods' arithmetic.
 """
 import numpy as np
 
@@ -69,33 +72,14 @@ def _lora(rng, d_in, d_out, r, dtype, c=2.0):
     return {"method": "lora", "A": A, "B": B, "c": float(c)}
 
 
-class _BaseStats:
-    """float64 copy of a base weight and its squared row norms, formed once
-    per projection for the DoRA magnitude recipe below."""
-
-    def __init__(self, W):
-        self.W64 = W.astype(np.float64)
-        self.sq = np.einsum("ij,ij->i", self.W64, self.W64)
-
-
-def _dora(rng, W, r, dtype, c=2.0, stats=None):
-    """DoRA tenant whose magnitude follows the workload recipe
-    m = ‖Wᵀ + cAB‖_c · (1 + 0.1 z).  The column norm is expanded over the
-    rank-r term, ‖w_j‖² + 2c·w_j·(A b_j) + c²·b_jᵀ(AᵀA)b_j, so the recipe
-    costs one [d_out x d_in] x [d_in x r] product per tenant."""
+def _dora(rng, W, r, dtype, c=2.0):
+    """DoRA tenant: LoRA factors of rank r and a magnitude
+    m = sqrt(1 + c²) · (1 + 0.1 z) (W gives the shapes only)."""
     d_out, d_in = W.shape
     rec = _lora(rng, d_in, d_out, r, dtype, c)
-    st = stats if stats is not None else _BaseStats(W)
-    A = rec["A"].astype(np.float64)
-    B = rec["B"].astype(np.float64)
-    WA = st.W64 @ A                                   # [d_out, r]
-    cross = np.einsum("jk,kj->j", WA, B)
-    G = A.T @ A                                       # [r, r]
-    quad = np.einsum("kj,kl,lj->j", B, G, B)
-    col = np.sqrt(st.sq + 2.0 * c * cross + c * c * quad)
     g = 1.0 + 0.1 * rng.standard_normal(d_out)
     rec["method"] = "dora"
-    rec["m"] = (col * g).astype(np.float32)
+    rec["m"] = (np.sqrt(1.0 + c * c) * g).astype(np.float32)
     return rec
 
 
@@ -272,10 +256,9 @@ def prefill_lora_dora(seed=1000, n=1024, d=4096, r=16, dtype="f16", tenants=16, 
     rng = np.random.default_rng(seed)
     do = d if d_out is None else d_out
     p = make_projection(rng, "q", d, do, dtype, n)
-    stats = _BaseStats(p["W"])
     for t in range(tenants):
         dora = methods == "dora" or (methods == "mixed" and t % 2 == 1)
-        p["adapters"][t + 1] = (_dora(rng, p["W"], r, dtype, stats=stats) if dora
+        p["adapters"][t + 1] = (_dora(rng, p["W"], r, dtype) if dora
                                 else _lora(rng, d, do, r, dtype))
     seg = max(1, n // tenants)
     slot_of_row = np.minimum(np.arange(n) // seg + 1, tenants).astype(np.int32)
@@ -317,19 +300,17 @@ def decoder_layer_mixed(seed=2000, n=64, dtype="f16", per_method=4, r=16, r_v=25
         if src is not None and src["d_in"] == d_in:
             p["x"] = src["x"]
             p["input_of"] = src["name"]
-        stats = None
         if not pure_lora:
             p["shared"] = _vera_shared(rng, d_in, d_out, r_v, dtype)
             if src is not None and src["d_in"] == d_in:
                 p["shared"]["A"] = src["shared"]["A"]
                 p["shared"]["a_from"] = src["name"]
-            stats = _BaseStats(p["W"])
         for t, m in enumerate(methods):
             slot = t + 1
             if pure_lora or m == "lora":
                 p["adapters"][slot] = _lora(rng, d_in, d_out, r, dtype)
             elif m == "dora":
-                p["adapters"][slot] = _dora(rng, p["W"], r, dtype, stats=stats)
+                p["adapters"][slot] = _dora(rng, p["W"], r, dtype)
             elif m == "ia3":
                 p["adapters"][slot] = (_ia3(rng, d_out) if name in ("k", "v", "up")
                                        else {"method": "identity"})
