@@ -148,7 +148,6 @@ def test_decode_terms_of_several_k_steps(dtype, n, r_v):
     check(got, y, h, xw, label="decode ranks %s n=%d r_v=%d" % (dtype, n, r_v), **_tol(dtype))
 
 
-
 @pytest.mark.parametrize("name,n", [("gate", 64), ("gate", 17), ("down", 64)])
 def test_vera_narrow_waves_match_wide_tiles(name, n):
     """The decode expand's VeRA tiles on 32-column waves (16-row tiles)
