@@ -11,7 +11,8 @@ reduction give on the same k ranges (a pinned shrink split of 4 ranges per
 k-group keeps the separate launch).  Checked here:
 
   * every projection of the decoder-layer workload (q, k and v with OFT
-    tenants), f16 and bf16, at 64, 17 (a ragged last tile) and 1 row: the
+    tenants), f16 and bf16, at 64, 17 (a ragged last tile), 16 (one full
+    tile) and 1 row: the
     same bits as the pinned split and the oracle's bar;
   * the gate / up group, whose up projection borrows VeRA's x A_v from gate
     (one item writes both projections' scaled columns), the q / k / v group
@@ -48,7 +49,7 @@ def _tol(dtype):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
-@pytest.mark.parametrize("n", [64, 17, 1])
+@pytest.mark.parametrize("n", [64, 17, 16, 1])
 def test_shrink_in_gemm_matches_split_shrink(dtype, name, n):
     wl = _workload(dtype)
     p = _proj(wl, name)
@@ -125,7 +126,7 @@ def test_shrink_in_gemm_group(names, borrow):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("n", [64, 17, 1])
+@pytest.mark.parametrize("n", [64, 33, 17, 16, 1])
 @pytest.mark.parametrize("r_v", [96, 256])
 def test_decode_terms_of_several_k_steps(dtype, n, r_v):
     """Owned ranks of one (16), two (48, 64) and five (160: a full group of
