@@ -825,7 +825,7 @@ def main():
     args = parse()
     ws = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or ws != 1:
-        print("bench.py measures one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
+        print("bench.py measures one GPU only (the library has no multi-GPU path); got --gpus %d" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     if args.workload == "stack":
