@@ -850,7 +850,7 @@ def main():
     log("loading 20 tenants into 7 projections, %d buffer sets" % args.sets)
     sets = [build_step(wl, torch) for _ in range(args.sets)]
     layers, step, units = sets[0]
-    # Warm-up steps, then the driver's timed region: exactly `steps` steps of
+    # Warm-up steps, then the timed region: exactly `steps` steps of
     # the captured graph, the chain rotating over the buffer sets (every
     # step reads W from HBM, as consecutive decoder layers do).
     chain = [st for _, st, _ in sets]
@@ -865,7 +865,7 @@ def main():
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
     del graphs
-    log("%.1f us per step (driver region)" % (t_step * 1e6))
+    log("%.1f us per step (timed region)" % (t_step * 1e6))
     # Appendix "Kernel timing": chains of >= 2 ms, five rebuilds, median;
     # cold (rotating the buffer sets) and warm (one set).
     t_cold, cold_samples, cold_copies = time_chain(lambda i: chain[i % len(chain)](), torch)
@@ -977,7 +977,7 @@ def main():
                    "n": n, "projections": names, "graph": True},
         "us_per_adapted_layer": t_step * 1e6 / 7,
         "decoder_layer_rows_per_s": n / t_step,
-        "timing": {"driver_region_us_per_step": t_step * 1e6, "buffer_sets": args.sets,
+        "timing": {"timed_region_us_per_step": t_step * 1e6, "buffer_sets": args.sets,
                    "cold_us_per_step": t_cold * 1e6, "cold_samples_us": [round(v * 1e6, 2) for v in cold_samples],
                    "warm_us_per_step": t_warm * 1e6, "warm_samples_us": [round(v * 1e6, 2) for v in warm_samples],
                    "steps_per_chain": [cold_copies, warm_copies],
